@@ -1,0 +1,432 @@
+"""Plain numpy oracle of the sparse ternary BitLinear forward (test infrastructure only).
+
+Sources (pages; cited by title and section):
+  [SB]  "Sparse-BitNet: 1.58-bit LLMs are Naturally Friendly to Semi-Structured
+        Sparsity" -- abstract (newx.sg page) and the technical summary
+        (gist.science page, section 2 "Methodologie", Kerncomponenten:
+        Sparse-BitLinear, Maskering, Forward Pass; Training Strategie:
+        Dynamisch Masker).
+  [B158] "BitNet b1.58: Ternary Weights for 1.58-bit LLMs" (fanout blog page) --
+        section "The mechanism" (absmean weight quantization, Eqs. 1-3 of the
+        paper; activations scaled per token to [-Qb, Qb]) and "Algorithm /
+        figure walkthrough" steps 3-5.
+  [SS]  SlideSparse abstract on the page "Is 2:4 Sparsity Still Worth It?
+        Semi-Structured Sparsity versus Quantization in LLM Inference" --
+        Sliding Window Decomposition of (2N-2):2N blocks into N-1 overlapping
+        2:4 windows, and Activation Lifting.
+
+Readings taken where the pages are silent or garbled (the page [B158] lost the
+formulas of Eqs. 1-3 in extraction):
+  * gamma = mean |W| over the whole dense master matrix (per tensor), computed
+    exactly and rounded once to fp32 (round half to even).  No epsilon.
+    gamma == 0 gives an all-zero ternary matrix.
+  * W~ = clip(rint(fl32(W / gamma)), -1, 1) with rint = round half to even.
+  * N:M mask: per row, per contiguous group of M along K starting at k = 0,
+    keep the N largest |w| of the continuous master; ties go to the lower
+    index; exactly N positions are kept even when their ternary code is 0.
+    The mask multiplies the ternary matrix (quantize first, then mask; gamma
+    comes from the dense master).
+  * Activations: absmax_t = max_k |x_tk|; s_t = fl32(127 / absmax_t);
+    q = clamp(rint(fl32(x * s_t)), -127, 127); scale_t = fl32(absmax_t / 127);
+    absmax_t == 0 gives q = 0 and scale_t = 0.
+  * 6:8 windows: window w in {0,1,2} covers positions 2w..2w+3 of an 8-group;
+    greedy assignment in ascending position order (w0 takes kept positions in
+    0..3, at most 2; w1 takes the remaining kept positions in 2..5, at most 2;
+    w2 takes the rest).  Lifted activations: x'[12g + 4w + j] = x[8g + 2w + j].
+  * Output: y = acc * gamma * scale_t evaluated in fp64, rounded to fp32.
+
+Packed layout (layout id 1), the format of the library's packed buffers:
+  A *slot* is one kept weight.  SPARSE layout (2:4, or 6:8 lifted into 2:4
+  windows): each 4-wide window j of a row's (lifted) K axis holds slots 2j and
+  2j+1 -- the kept positions in ascending order -- with a 2-bit ternary code
+  (00 = 0, 01 = +1, 11 = -1) and a 2-bit position index 0..3 within the window.
+  DENSE2 layout: every position is a slot with a 2-bit code and no index.
+  A *unit* is 16 consecutive slots of one row (row r, unit c) and is stored as
+  one little-endian code dword -- slot i at bits 8*(i%4) + 2*(i//4) -- and,
+  for SPARSE, one meta dword -- slot i's index at bits 2*i.  Units are tiled
+  for 64-lane fragments: rows are padded to a multiple of 32 (padded rows:
+  codes 0, every window's indices (0, 1)), and unit (r, c) lives at dword
+  ((r // 32) * (U // 2) + c // 2) * 64 + (c % 2) * 32 + r % 32, where U is the
+  number of units per row (K_eff / 32 for SPARSE, K / 16 for DENSE2).
+
+Pinned functions (tests/test_oracle_*.py) and what pins them:
+  absmean_gamma      rational brute force, closed forms, permutation and 2^k
+                     scaling invariance, ties at fp32 midpoints, subnormals
+  round_ratio_to_f32 numpy's correctly rounded fp64 -> fp32 cast
+  nm_mask            exhaustive subset search on tie-heavy groups
+  ternarize          worked example with an exact half, the closed-form
+                     threshold |w| * 2^25 > gamma * (2^24 + 1), sign symmetry
+  window_table_68    the worked example; every valid 6:8 mask reconstructs
+  pack / unpack      hand-encoded dwords (tests/golden), round trip
+  act_quant          worked example with exact halves, invariants
+  acc_dense          brute-force Python loops on tiny inputs; agrees with the
+                     add/sub form acc_addsub; 6:8 lifted == dense
+  rescale            zero case and exact small products
+"""
+from __future__ import annotations
+
+import math
+from fractions import Fraction
+from typing import Dict, List, Tuple
+
+import numpy as np
+
+LAYOUT_SPARSE = 0
+LAYOUT_DENSE2 = 1
+QB = 127                  # activation range [-Qb, Qb]
+PANEL = 32                # rows per tile panel
+PAD_META = 0x44444444     # meta dword of a padded row: every window (0, 1)
+
+__all__ = [
+    "LAYOUT_SPARSE", "LAYOUT_DENSE2", "QB", "PAD_META",
+    "round_ratio_to_f32", "absmean_gamma", "nm_mask", "ternarize", "effective_weights",
+    "window_table_68", "k_eff", "packed_dwords", "weight_slots", "pack", "unpack_slots",
+    "slots_to_dense", "act_quant", "lift_68", "acc_dense", "acc_addsub", "rescale", "forward",
+]
+
+
+# ----------------------------------------------------------------------------------------------
+# gamma: absmean scale ([B158] "The mechanism", absmean weight quantization; [SB] 2, the scale
+# is taken from the dense master before the mask is applied)
+# ----------------------------------------------------------------------------------------------
+
+def round_ratio_to_f32(num: int, den: int) -> np.float32:
+    """Round the nonnegative rational num/den to the nearest fp32, ties to even (exact)."""
+    assert num >= 0 and den > 0
+    if num == 0:
+        return np.float32(0.0)
+    # binary exponent E with 2^E <= num/den < 2^(E+1)
+    E = num.bit_length() - den.bit_length()
+    if E >= 0:
+        if num < (den << E):
+            E -= 1
+    else:
+        if (num << -E) < den:
+            E -= 1
+    # quantum of the fp32 grid at that exponent (subnormals share 2^-149)
+    qe = max(E, -126) - 23
+    if qe >= 0:
+        q, r = divmod(num, den << qe)
+        d = den << qe
+    else:
+        q, r = divmod(num << -qe, den)
+        d = den
+    if 2 * r > d or (2 * r == d and (q & 1)):
+        q += 1
+    val = math.ldexp(float(q), qe)
+    out = np.float32(val)
+    assert float(out) == val, "value out of fp32 range"
+    return out
+
+
+def absmean_gamma(W: np.ndarray) -> np.float32:
+    """gamma = mean |W| over every entry of the dense fp32 master, exact then rounded once.
+
+    Every finite fp32 magnitude is m * 2^(max(e,1) - 150) with integer significand m < 2^24
+    and biased exponent e, i.e. an integer multiple of 2^-149.  The sum of all magnitudes is
+    therefore an exact integer S in units of 2^-149 and gamma = RNE_fp32(S / (count * 2^149)).
+    """
+    a = np.abs(np.asarray(W, dtype=np.float32)).ravel()
+    count = a.size
+    assert count > 0
+    bits = a.view(np.uint32)
+    e = (bits >> 23).astype(np.int64)
+    assert np.all(e < 255), "non-finite weights are outside the contract"
+    m = (bits & 0x7FFFFF).astype(np.int64)
+    m = np.where(e > 0, m | (1 << 23), m)
+    shift = np.maximum(e, 1) - 1
+    S = 0
+    for s in np.unique(shift):
+        S += int(m[shift == s].sum(dtype=np.int64)) << int(s)
+    return round_ratio_to_f32(S, count << 149)
+
+
+# ----------------------------------------------------------------------------------------------
+# N:M mask on the continuous master ([SB] 2, Maskering; Dynamisch Masker)
+# ----------------------------------------------------------------------------------------------
+
+def nm_mask(W: np.ndarray, N: int, M: int) -> np.ndarray:
+    """Boolean keep-mask: per row, per contiguous M-group along K, the N largest |w|.
+
+    Ties are broken toward the lower index (a stable sort of -|w|).  |-0.0| == |+0.0|.
+    """
+    W = np.asarray(W, dtype=np.float32)
+    n, K = W.shape
+    assert K % M == 0 and 0 < N <= M
+    g = np.abs(W).reshape(n, K // M, M)
+    order = np.argsort(-g, axis=-1, kind="stable")
+    keep = np.zeros(g.shape, dtype=bool)
+    np.put_along_axis(keep, order[..., :N], True, axis=-1)
+    return keep.reshape(n, K)
+
+
+# ----------------------------------------------------------------------------------------------
+# ternarization ([B158] "The mechanism": divide by gamma, round, clip to [-1, 1])
+# ----------------------------------------------------------------------------------------------
+
+def ternarize(W: np.ndarray, gamma: np.float32) -> np.ndarray:
+    """W~ = clip(rint(fl32(W / gamma)), -1, 1), rint = round half to even; all zero if gamma == 0."""
+    W = np.asarray(W, dtype=np.float32)
+    if float(gamma) == 0.0:
+        return np.zeros(W.shape, dtype=np.int8)
+    q = W / np.float32(gamma)            # IEEE fp32 division
+    assert q.dtype == np.float32
+    return np.clip(np.rint(q), -1, 1).astype(np.int8)
+
+
+def effective_weights(W: np.ndarray, N: int, M: int) -> Tuple[np.ndarray, np.float32, np.ndarray]:
+    """W_eff = mask * ternary(W) ([SB] 2, Forward Pass: quantize, then apply the mask).
+
+    Returns (W_eff int8 [n][K], gamma, keep mask).
+    """
+    gamma = absmean_gamma(W)
+    t = ternarize(W, gamma)
+    keep = nm_mask(W, N, M)
+    return np.where(keep, t, 0).astype(np.int8), gamma, keep
+
+
+# ----------------------------------------------------------------------------------------------
+# 6:8 sliding windows ([SS] Sliding Window Decomposition)
+# ----------------------------------------------------------------------------------------------
+
+def _assign_windows_68(kept: List[int]) -> List[List[int]]:
+    """Greedy assignment of the 6 kept positions of an 8-group to windows 0..3, 2..5, 4..7."""
+    assert len(kept) == 6
+    kept = sorted(kept)
+    w0 = [p for p in kept if p <= 3][:2]
+    rest = [p for p in kept if p not in w0]
+    w1 = [p for p in rest if 2 <= p <= 5][:2]
+    w2 = [p for p in rest if p not in w1]
+    assert len(w0) == 2 and len(w1) == 2 and len(w2) == 2, kept
+    assert all(4 <= p <= 7 for p in w2)
+    return [w0, w1, w2]
+
+
+def window_table_68() -> Dict[int, List[List[int]]]:
+    """keep-bitmask of an 8-group (bit p = position p kept) -> positions per window."""
+    table = {}
+    for drop in range(8):
+        for drop2 in range(drop + 1, 8):
+            kept = [p for p in range(8) if p not in (drop, drop2)]
+            mask = sum(1 << p for p in kept)
+            table[mask] = _assign_windows_68(kept)
+    return table
+
+
+# ----------------------------------------------------------------------------------------------
+# slots and the packed layout
+# ----------------------------------------------------------------------------------------------
+
+def k_eff(K: int, N: int, M: int, layout: int) -> int:
+    """Length of the packed K axis: K for 2:4 and DENSE2, 3K/2 for 6:8 windows."""
+    if layout == LAYOUT_DENSE2:
+        return K
+    if (N, M) == (2, 4):
+        return K
+    if (N, M) == (6, 8):
+        return K * 3 // 2
+    raise ValueError("SPARSE layout supports 2:4 and 6:8")
+
+
+def packed_dwords(n: int, K: int, N: int, M: int, layout: int) -> Tuple[int, int, int]:
+    """(code dwords, meta dwords, n_pad) of a packed matrix."""
+    n_pad = -(-n // PANEL) * PANEL
+    ke = k_eff(K, N, M, layout)
+    if layout == LAYOUT_DENSE2:
+        assert K % 32 == 0
+        return n_pad * K // 16, 0, n_pad
+    assert ke % 64 == 0
+    return n_pad * ke // 32, n_pad * ke // 32, n_pad
+
+
+def weight_slots(W_eff: np.ndarray, keep: np.ndarray, N: int, M: int, layout: int):
+    """Per-row slot codes (int8 in {-1,0,1}) and window indices (uint8 0..3, SPARSE only)."""
+    n, K = W_eff.shape
+    if layout == LAYOUT_DENSE2:
+        return W_eff.astype(np.int8).copy(), None
+    if (N, M) == (2, 4):
+        kg = keep.reshape(n, K // 4, 4)
+        pos = np.argsort(~kg, axis=-1, kind="stable")[..., :2]          # kept positions, ascending
+        vals = np.take_along_axis(W_eff.reshape(n, K // 4, 4), pos, axis=-1)
+        return vals.reshape(n, K // 2).astype(np.int8), pos.reshape(n, K // 2).astype(np.uint8)
+    if (N, M) == (6, 8):
+        table = window_table_68()
+        G = K // 8
+        kg = keep.reshape(n, G, 8)
+        bitmask = (kg.astype(np.int64) << np.arange(8)).sum(axis=-1)
+        # dense position (0..7) of each of the 6 slots per group, for every valid bitmask
+        lut = np.zeros((256, 6), dtype=np.int64)
+        for msk, wins in table.items():
+            lut[msk] = [p for w in wins for p in w]
+        assert np.all(np.isin(bitmask, list(table.keys())))
+        pos = lut[bitmask]                                                # [n][G][6]
+        vals = np.take_along_axis(W_eff.reshape(n, G, 8), pos, axis=-1)
+        window_start = np.array([0, 0, 2, 2, 4, 4])
+        local = pos - window_start
+        return vals.reshape(n, G * 6).astype(np.int8), local.reshape(n, G * 6).astype(np.uint8)
+    raise ValueError("unsupported N:M")
+
+
+_CODE_SHIFT = np.array([8 * (i % 4) + 2 * (i // 4) for i in range(16)], dtype=np.uint32)
+_META_SHIFT = np.array([2 * i for i in range(16)], dtype=np.uint32)
+
+
+def _tile(units: np.ndarray) -> np.ndarray:
+    """[n_pad][U] unit dwords -> flat tiled order (panel, fragment, lane)."""
+    n_pad, U = units.shape
+    t = units.reshape(n_pad // PANEL, PANEL, U // 2, 2)      # [P][r][F][h]
+    return np.ascontiguousarray(t.transpose(0, 2, 3, 1)).reshape(-1)
+
+
+def _untile(flat: np.ndarray, n_pad: int, U: int) -> np.ndarray:
+    t = flat.reshape(n_pad // PANEL, U // 2, 2, PANEL)       # [P][F][h][r]
+    return np.ascontiguousarray(t.transpose(0, 3, 1, 2)).reshape(n_pad, U)
+
+
+def pack(W: np.ndarray, N: int, M: int, layout: int = LAYOUT_SPARSE):
+    """Mask + ternarize + pack a fp32 master (the library's pack call, layout id 1).
+
+    Returns dict(codes=uint32[...], meta=uint32[...] or None, gamma=fp32, K_eff, n_pad,
+    W_eff, keep).
+    """
+    W = np.asarray(W, dtype=np.float32)
+    n, K = W.shape
+    W_eff, gamma, keep = effective_weights(W, N, M)
+    vals, idx = weight_slots(W_eff, keep, N, M, layout)
+    ncode, nmeta, n_pad = packed_dwords(n, K, N, M, layout)
+    S = vals.shape[1]
+    U = S // 16
+    v = np.zeros((n_pad, S), dtype=np.int8)
+    v[:n] = vals
+    code_units = ((v.reshape(n_pad, U, 16).astype(np.int64) & 3).astype(np.uint32) << _CODE_SHIFT).sum(
+        axis=-1, dtype=np.uint64).astype(np.uint32)
+    codes = _tile(code_units)
+    meta = None
+    if layout == LAYOUT_SPARSE:
+        ix = np.zeros((n_pad, S), dtype=np.uint8)
+        ix[:, 1::2] = 1                                      # padded rows: windows (0, 1)
+        ix[:n] = idx
+        meta_units = (ix.reshape(n_pad, U, 16).astype(np.uint32) << _META_SHIFT).sum(
+            axis=-1, dtype=np.uint64).astype(np.uint32)
+        meta = _tile(meta_units)
+        assert meta.size == nmeta
+    assert codes.size == ncode
+    return dict(codes=codes, meta=meta, gamma=gamma, K_eff=S * 2 if layout == LAYOUT_SPARSE else S,
+                n_pad=n_pad, W_eff=W_eff, keep=keep)
+
+
+def unpack_slots(codes: np.ndarray, meta, n: int, K: int, N: int, M: int, layout: int):
+    """Inverse of the tiling and bit packing: (slot codes int8 [n][S], indices uint8 or None)."""
+    ncode, nmeta, n_pad = packed_dwords(n, K, N, M, layout)
+    codes = np.asarray(codes).view(np.uint32).reshape(-1)
+    assert codes.size == ncode
+    ke = k_eff(K, N, M, layout)
+    S = ke // 2 if layout == LAYOUT_SPARSE else ke
+    U = S // 16
+    cu = _untile(codes, n_pad, U)[:n]                                    # [n][U]
+    raw = (cu[..., None] >> _CODE_SHIFT) & 3                              # [n][U][16]
+    assert not np.any(raw == 2), "code 10 is never written"
+    vals = np.where(raw == 3, -1, raw).astype(np.int8).reshape(n, S)
+    if layout == LAYOUT_DENSE2:
+        return vals, None
+    mu = _untile(np.asarray(meta).view(np.uint32).reshape(-1), n_pad, U)[:n]
+    idx = ((mu[..., None] >> _META_SHIFT) & 3).astype(np.uint8).reshape(n, S)
+    return vals, idx
+
+
+def slots_to_dense(vals: np.ndarray, idx, K: int, N: int, M: int, layout: int) -> np.ndarray:
+    """Scatter slots back to the dense [n][K] ternary matrix (6:8 windows summed back)."""
+    n = vals.shape[0]
+    if layout == LAYOUT_DENSE2:
+        return vals.astype(np.int8)
+    S = vals.shape[1]
+    window = np.arange(S) // 2
+    lifted_pos = 4 * window[None, :] + idx.astype(np.int64)               # position on K_eff axis
+    if (N, M) == (2, 4):
+        dense_pos = lifted_pos
+    else:
+        g, rem = lifted_pos // 12, lifted_pos % 12                        # 12 lifted per 8 dense
+        dense_pos = 8 * g + 2 * (rem // 4) + (rem % 4)
+    out = np.zeros((n, K), dtype=np.int64)
+    rows = np.repeat(np.arange(n)[:, None], S, axis=1)
+    np.add.at(out, (rows, dense_pos), vals.astype(np.int64))
+    return out.astype(np.int8)
+
+
+# ----------------------------------------------------------------------------------------------
+# activations ([B158] "The mechanism", Activations: per-token symmetric 8-bit, [-Qb, Qb];
+# [SS] Activation Lifting for 6:8)
+# ----------------------------------------------------------------------------------------------
+
+def lift_68(q: np.ndarray) -> np.ndarray:
+    """x'[t][12g + 4w + j] = x[t][8g + 2w + j], w = 0..2, j = 0..3."""
+    T, K = q.shape
+    G = K // 8
+    src = np.array([8 * 0 + 2 * w + j for w in range(3) for j in range(4)])   # 12 per group
+    cols = (8 * np.arange(G)[:, None] + src[None, :]).reshape(-1)
+    return q[:, cols]
+
+
+def act_quant(x: np.ndarray, lift_M: int = 0) -> Tuple[np.ndarray, np.ndarray]:
+    """Per-token absmax int8 quantization (Qb = 127).  Returns (xq int8 [T][K_eff], scale fp32 [T])."""
+    x = np.asarray(x, dtype=np.float32)
+    absmax = np.max(np.abs(x), axis=1) if x.shape[1] else np.zeros(x.shape[0], np.float32)
+    nz = absmax > 0
+    s = np.zeros_like(absmax)
+    s[nz] = np.float32(QB) / absmax[nz]                          # fp32 division
+    prod = x * s[:, None]                                        # fp32 multiply
+    q = np.clip(np.rint(prod), -QB, QB).astype(np.int8)
+    scale = (absmax / np.float32(QB)).astype(np.float32)
+    scale[~nz] = 0.0
+    if lift_M == 8:
+        q = lift_68(q)
+    else:
+        assert lift_M == 0
+    return q, scale
+
+
+# ----------------------------------------------------------------------------------------------
+# accumulation and rescale ([B158] "The mechanism": a ternary MAC is add, subtract or skip;
+# integer accumulation of int8 activations, then rescale by gamma and the token scale)
+# ----------------------------------------------------------------------------------------------
+
+def acc_dense(W_eff: np.ndarray, q: np.ndarray) -> np.ndarray:
+    """acc[t][o] = sum_k W_eff[o][k] * q[t][k] in int64 (form i: dense matmul)."""
+    return np.asarray(q, np.int64) @ np.asarray(W_eff, np.int64).T
+
+
+def acc_addsub(vals: np.ndarray, idx, xq: np.ndarray, layout: int) -> np.ndarray:
+    """Form ii: per slot, add the activation under a +1 code, subtract it under a -1 code.
+
+    ``xq`` is on the packed K axis (lifted for 6:8).
+    """
+    T = xq.shape[0]
+    n, S = vals.shape
+    if layout == LAYOUT_DENSE2:
+        pos = np.broadcast_to(np.arange(S), (n, S))
+    else:
+        pos = 4 * (np.arange(S) // 2)[None, :] + idx.astype(np.int64)
+    xq64 = xq.astype(np.int64)
+    acc = np.zeros((T, n), dtype=np.int64)
+    for o in range(n):
+        plus = pos[o][vals[o] == 1]
+        minus = pos[o][vals[o] == -1]
+        acc[:, o] = xq64[:, plus].sum(axis=1) - xq64[:, minus].sum(axis=1)
+    return acc
+
+
+def rescale(acc: np.ndarray, gamma: np.float32, scale: np.ndarray) -> np.ndarray:
+    """y = acc * gamma * scale_t, evaluated in fp64 and rounded to fp32."""
+    y = np.asarray(acc, np.float64) * np.float64(gamma) * np.asarray(scale, np.float64)[:, None]
+    return y.astype(np.float32)
+
+
+def forward(W: np.ndarray, x: np.ndarray, N: int, M: int, layout: int = LAYOUT_SPARSE) -> Dict:
+    """Whole path: pack the master, quantize (and lift) x, accumulate, rescale."""
+    p = pack(W, N, M, layout)
+    lift = 8 if (layout == LAYOUT_SPARSE and (N, M) == (6, 8)) else 0
+    xq, scale = act_quant(x, lift)
+    acc = acc_dense(p["W_eff"], act_quant(x, 0)[0])
+    y = rescale(acc, p["gamma"], scale)
+    p.update(xq=xq, scale=scale, acc=acc, y=y)
+    return p

@@ -1,0 +1,366 @@
+"""Pins of the CPU oracle against the pages' definitions, closed forms and brute force.
+
+None of these tests needs a GPU.  Each test checks the oracle against something other
+than itself: hand-derived golden values (tests/golden), exact rational arithmetic,
+exhaustive search, closed-form thresholds or statistics, or a library routine.
+"""
+import itertools
+import math
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle as O
+from golden_io import hexu32, read_kv, read_lines
+
+
+def f32_from_bits(vals):
+    return np.array(vals, dtype=np.uint32).view(np.float32)
+
+
+def bits(x):
+    return int(np.float32(x).view(np.uint32))
+
+
+# ------------------------------------------------------------------------------------------
+# gamma
+# ------------------------------------------------------------------------------------------
+
+def test_gamma_closed_forms():
+    kv = read_kv("gamma_closed_forms.txt")
+    for c in range(1, 7):
+        W = f32_from_bits(hexu32(kv[f"case{c}_W"])).reshape(1, -1)
+        want = hexu32(kv[f"case{c}_gamma"])[0]
+        assert bits(O.absmean_gamma(W)) == want, c
+
+
+def _fraction_to_f32_bruteforce(r: Fraction) -> np.float32:
+    """Nearest fp32 to r (ties to even) by checking the neighbours of a candidate exactly."""
+    c = np.float32(float(r))
+    cands = {c, np.nextafter(c, np.float32(np.inf)), np.nextafter(c, np.float32(0))}
+    best = None
+    for v in sorted(cands, key=float):
+        d = abs(Fraction(float(v)) - r)
+        even = bits(v) % 2 == 0
+        key = (d, not even)
+        if best is None or key < best[0]:
+            best = (key, v)
+    return np.float32(best[1])
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_gamma_rational_bruteforce(seed):
+    g = np.random.default_rng(seed)
+    kind = seed % 3
+    if kind == 0:
+        W = g.normal(0, 0.02, size=(7, 13)).astype(np.float32)
+    elif kind == 1:   # very wide exponent range, including subnormals
+        W = (g.standard_normal((5, 11)) * np.exp2(g.integers(-149, 100, size=(5, 11)))).astype(np.float32)
+    else:             # tiny values only: the mean may be subnormal
+        W = (g.integers(-9, 10, size=(3, 8)) * np.float32(2.0 ** -149)).astype(np.float32)
+    exact = sum(Fraction(float(abs(w))) for w in W.ravel()) / W.size
+    assert bits(O.absmean_gamma(W)) == bits(_fraction_to_f32_bruteforce(exact))
+
+
+def test_round_ratio_matches_numpy_cast():
+    g = np.random.default_rng(3)
+    xs = list(np.abs(g.standard_normal(200)) * np.exp2(g.integers(-160, 120, 200)))
+    # exact fp32 midpoints and values one fp64 ulp either side of them
+    for k in range(1, 40):
+        m = (2 * k + 1) * 2.0 ** -25
+        xs += [1.0 + m, np.nextafter(1.0 + m, 2.0), np.nextafter(1.0 + m, 0.0)]
+    xs += [2.0 ** -150, 3 * 2.0 ** -150, 2.0 ** -149 * 1.5, 5e-324, 1.0]
+    for x in xs:
+        fr = Fraction(float(x))
+        got = O.round_ratio_to_f32(fr.numerator, fr.denominator)
+        want = np.float32(np.float64(x))   # numpy's fp64 -> fp32 cast rounds to nearest even
+        assert bits(got) == bits(want), x
+
+
+def test_gamma_invariances():
+    g = np.random.default_rng(11)
+    W = g.normal(0, 0.02, size=(64, 96)).astype(np.float32)
+    gam = O.absmean_gamma(W)
+    perm = g.permutation(W.size)
+    assert bits(O.absmean_gamma(W.ravel()[perm].reshape(96, 64))) == bits(gam)
+    assert bits(O.absmean_gamma(-W)) == bits(gam)
+    for k in (-3, 5, 17):
+        assert bits(O.absmean_gamma(W * np.float32(2.0 ** k))) == bits(np.float32(gam * 2.0 ** k))
+    c = np.float32(0.0173)
+    Wc = np.where(g.random(W.shape) < 0.5, c, -c).astype(np.float32)
+    assert bits(O.absmean_gamma(Wc)) == bits(c)
+
+
+def test_gamma_gaussian_statistic():
+    g = np.random.default_rng(5)
+    sigma = 0.02
+    W = g.normal(0, sigma, size=(1024, 1024)).astype(np.float32)
+    want = sigma * math.sqrt(2 / math.pi)      # E|w| for N(0, sigma^2)
+    assert abs(float(O.absmean_gamma(W)) / want - 1) < 3e-3
+
+
+# ------------------------------------------------------------------------------------------
+# mask
+# ------------------------------------------------------------------------------------------
+
+def test_mask_golden():
+    for line in read_lines("mask_ties.txt"):
+        nm, w, kept = [s.strip() for s in line.split("|")]
+        N, M = map(int, nm.split())
+        W = np.array([float(v) for v in w.split()], dtype=np.float32).reshape(1, M)
+        got = np.nonzero(O.nm_mask(W, N, M)[0])[0].tolist()
+        assert got == [int(v) for v in kept.split()], line
+
+
+def _topn_bruteforce(a, N):
+    """The unique N-subset whose kept entries all precede every dropped entry in the order
+    (|w| descending, index ascending)."""
+    M = len(a)
+    found = []
+    for S in itertools.combinations(range(M), N):
+        ok = all((abs(a[i]) > abs(a[j])) or (abs(a[i]) == abs(a[j]) and i < j)
+                 for i in S for j in range(M) if j not in S)
+        if ok:
+            found.append(S)
+    assert len(found) == 1
+    return list(found[0])
+
+
+@pytest.mark.parametrize("N,M", [(2, 4), (6, 8), (1, 4), (4, 4)])
+def test_mask_bruteforce(N, M):
+    g = np.random.default_rng(N * 10 + M)
+    pool = np.array([0.0, -0.0, 0.25, -0.25, 0.5, -0.5, 1.0], dtype=np.float32)
+    W = g.choice(pool, size=(40, M * 6)).astype(np.float32)
+    W[:20] = g.normal(0, 0.02, size=(20, M * 6)).astype(np.float32)
+    keep = O.nm_mask(W, N, M)
+    for r in range(W.shape[0]):
+        for gi in range(W.shape[1] // M):
+            grp = [float(v) for v in W[r, gi * M:(gi + 1) * M]]
+            want = _topn_bruteforce(grp, N)
+            assert np.nonzero(keep[r, gi * M:(gi + 1) * M])[0].tolist() == want
+    assert np.all(keep.reshape(W.shape[0], -1, M).sum(-1) == N)
+
+
+# ------------------------------------------------------------------------------------------
+# ternarize
+# ------------------------------------------------------------------------------------------
+
+def test_ternarize_golden():
+    kv = read_kv("ternarize_worked.txt")
+    W = np.array([float(v) for v in kv["W"]], dtype=np.float32).reshape(1, -1)
+    gam = O.absmean_gamma(W)
+    assert float(gam) == float(kv["gamma"][0])
+    assert O.ternarize(W, gam).ravel().tolist() == [int(v) for v in kv["t"]]
+    Wn = np.array([float(v) for v in kv["Wneg"]], dtype=np.float32).reshape(1, -1)
+    assert O.ternarize(Wn, O.absmean_gamma(Wn)).ravel().tolist() == [int(v) for v in kv["tneg"]]
+
+
+def test_ternarize_threshold_closed_form():
+    """fl32(|w|/gamma) > 0.5  <=>  |w| * 2^25 > gamma * (2^24 + 1)  (RNE; spacing above 0.5 is 2^-24).
+
+    Both sides of the right-hand comparison are exact in fp64 (a power-of-two scaling, and a
+    24-bit by 25-bit product)."""
+    g = np.random.default_rng(7)
+    gammas = np.abs(g.normal(0, 0.02, 64)).astype(np.float32)
+    for gam in gammas:
+        base = float(gam) * 0.5
+        near = [np.float32(base * (1 + k * 2.0 ** -26)) for k in range(-6, 7)]
+        near += [np.nextafter(np.float32(base), np.float32(1)), np.nextafter(np.float32(base), np.float32(0))]
+        far = list((g.normal(0, 0.05, 200)).astype(np.float32))
+        w = np.array(near + [-v for v in near] + far, dtype=np.float32).reshape(1, -1)
+        t = O.ternarize(w, gam).ravel()
+        a = np.abs(w.ravel()).astype(np.float64)
+        want = np.where(a * 2.0 ** 25 > np.float64(gam) * (2.0 ** 24 + 1), np.sign(w.ravel()), 0)
+        assert np.array_equal(t, want.astype(np.int8))
+
+
+def test_ternarize_zero_gamma_and_symmetry():
+    W = np.zeros((4, 8), np.float32)
+    assert O.absmean_gamma(W) == 0 and not O.ternarize(W, O.absmean_gamma(W)).any()
+    g = np.random.default_rng(2)
+    W = g.normal(0, 0.02, (32, 64)).astype(np.float32)
+    gam = O.absmean_gamma(W)
+    assert np.array_equal(O.ternarize(-W, gam), -O.ternarize(W, gam))
+
+
+def test_ternary_gaussian_zero_fraction():
+    """P(|w| <= gamma/2) for Gaussian w with gamma = E|w| is 2*Phi(sqrt(2/pi)/2) - 1 ~= 0.3101."""
+    g = np.random.default_rng(9)
+    W = g.normal(0, 0.02, (1024, 1024)).astype(np.float32)
+    t = O.ternarize(W, O.absmean_gamma(W))
+    want = math.erf(math.sqrt(2 / math.pi) / 2 / math.sqrt(2))
+    assert abs((t == 0).mean() - want) < 2e-3
+
+
+# ------------------------------------------------------------------------------------------
+# 6:8 windows
+# ------------------------------------------------------------------------------------------
+
+def test_windows_golden():
+    kv = read_kv("windows_68.txt")
+    table = O.window_table_68()
+    for sfx in ("", "_b", "_c"):
+        kept = [int(v) for v in kv["kept" + sfx]]
+        wins = table[sum(1 << p for p in kept)]
+        for w in range(3):
+            assert wins[w] == [int(v) for v in kv[f"w{w}{sfx}"]]
+
+
+def test_windows_cover_every_mask():
+    table = O.window_table_68()
+    assert len(table) == 28
+    for mask, wins in table.items():
+        flat = sorted(p for w in wins for p in w)
+        assert flat == [p for p in range(8) if mask >> p & 1]
+        for w, ps in enumerate(wins):
+            assert len(ps) == 2 and all(2 * w <= p <= 2 * w + 3 for p in ps)
+
+
+# ------------------------------------------------------------------------------------------
+# pack layout
+# ------------------------------------------------------------------------------------------
+
+def test_pack_golden_unit():
+    kv = read_kv("pack_2of4_unit.txt")
+    half = np.array([float(v) for v in kv["W"]], dtype=np.float32)
+    W = np.concatenate([half, -half]).reshape(1, 64)
+    p = O.pack(W, 2, 4, O.LAYOUT_SPARSE)
+    assert float(p["gamma"]) == 1.0
+    vals, idx = O.weight_slots(p["W_eff"], p["keep"], 2, 4, O.LAYOUT_SPARSE)
+    assert vals[0, :16].tolist() == [int(v) for v in kv["slot_codes_unit0"]]
+    assert idx[0, :16].tolist() == [int(v) for v in kv["slot_idx_unit0"]]
+    codes, meta = p["codes"], p["meta"]
+    assert codes.size == 64 and meta.size == 64
+    assert codes[0] == hexu32(kv["code_dword_0"])[0]
+    assert codes[32] == hexu32(kv["code_dword_32"])[0]
+    assert meta[0] == hexu32(kv["meta_dword_0"])[0]
+    assert meta[32] == hexu32(kv["meta_dword_32"])[0]
+    pad = hexu32(kv["pad_meta"])[0]
+    others = [i for i in range(64) if i not in (0, 32)]
+    assert not codes[others].any()
+    assert np.all(meta[others] == pad)
+
+
+@pytest.mark.parametrize("N,M,layout", [(2, 4, O.LAYOUT_SPARSE), (6, 8, O.LAYOUT_SPARSE),
+                                        (2, 4, O.LAYOUT_DENSE2), (6, 8, O.LAYOUT_DENSE2)])
+def test_pack_roundtrip(N, M, layout):
+    g = np.random.default_rng(N + M + layout)
+    n, K = 45, 256
+    W = g.normal(0, 0.02, (n, K)).astype(np.float32)
+    p = O.pack(W, N, M, layout)
+    vals, idx = O.unpack_slots(p["codes"], p["meta"], n, K, N, M, layout)
+    dense = O.slots_to_dense(vals, idx, K, N, M, layout)
+    assert np.array_equal(dense, p["W_eff"])
+    nnz = (p["W_eff"] != 0).reshape(n, K // M, M).sum(-1)
+    assert nnz.max() <= N
+
+
+# ------------------------------------------------------------------------------------------
+# activation quantization
+# ------------------------------------------------------------------------------------------
+
+def test_act_quant_golden():
+    kv = read_kv("act_quant_worked.txt")
+    x = np.array([[float(v) for v in kv[f"x{i}"]] for i in range(3)], dtype=np.float32)
+    q, scale = O.act_quant(x)
+    for i in range(3):
+        assert q[i].tolist() == [int(v) for v in kv[f"q{i}"]]
+    assert scale[0] == np.float32(1.0)
+    assert scale[1] == np.float32(np.float32(0.5) / np.float32(127))
+    assert scale[2] == 0
+
+
+def test_act_quant_invariants():
+    g = np.random.default_rng(4)
+    x = g.standard_normal((33, 200)).astype(np.float32)
+    x[5] = 0
+    q, scale = O.act_quant(x)
+    nz = np.abs(x).max(1) > 0
+    assert np.all(np.abs(q[nz]).max(1) == 127) and not q[~nz].any()
+    for k in (-7, 3, 20):
+        q2, s2 = O.act_quant(x * np.float32(2.0 ** k))
+        assert np.array_equal(q2, q)
+        assert np.array_equal(s2, (scale * np.float32(2.0 ** k)).astype(np.float32))
+
+
+def test_act_quant_close_to_real_rounding():
+    """Against rint(x * 127 / absmax) in fp64: any difference sits at a near-half-integer."""
+    g = np.random.default_rng(8)
+    x = (0.5 * g.standard_t(4, (64, 512))).astype(np.float32)
+    q, _ = O.act_quant(x)
+    am = np.abs(x).max(1, keepdims=True).astype(np.float64)
+    real = x.astype(np.float64) * 127 / am
+    ref = np.rint(real)
+    diff = q != ref
+    assert np.all(np.abs(q - ref)[diff] == 1)
+    assert np.all(np.abs(np.abs(real[diff] - np.floor(real[diff])) - 0.5) < 1e-4)
+
+
+def test_lift_68():
+    q = np.arange(2 * 16, dtype=np.int64).reshape(2, 16).astype(np.int8)
+    L = O.lift_68(q)
+    assert L.shape == (2, 24)
+    assert L[0].tolist() == [0, 1, 2, 3, 2, 3, 4, 5, 4, 5, 6, 7, 8, 9, 10, 11, 10, 11, 12, 13, 12, 13, 14, 15]
+
+
+# ------------------------------------------------------------------------------------------
+# accumulation and rescale
+# ------------------------------------------------------------------------------------------
+
+def test_acc_bruteforce_tiny():
+    g = np.random.default_rng(12)
+    W = g.integers(-1, 2, (3, 8)).astype(np.int8)
+    q = g.integers(-127, 128, (2, 8)).astype(np.int8)
+    acc = O.acc_dense(W, q)
+    for t in range(2):
+        for o in range(3):
+            s = 0
+            for k in range(8):
+                s += int(W[o][k]) * int(q[t][k])
+            assert acc[t][o] == s
+
+
+@pytest.mark.parametrize("N,M,layout", [(2, 4, O.LAYOUT_SPARSE), (6, 8, O.LAYOUT_SPARSE),
+                                        (2, 4, O.LAYOUT_DENSE2)])
+def test_acc_forms_agree(N, M, layout):
+    """Form i (dense int64 matmul of W_eff) equals form ii (add/sub over packed slots); for 6:8
+    the lifted 2:4 windows against lifted activations equal the dense product (lossless)."""
+    g = np.random.default_rng(20 + N)
+    n, K, T = 40, 256, 9
+    W = g.normal(0, 0.02, (n, K)).astype(np.float32)
+    x = g.standard_normal((T, K)).astype(np.float32)
+    p = O.pack(W, N, M, layout)
+    lift = 8 if (layout == O.LAYOUT_SPARSE and M == 8) else 0
+    xq, _ = O.act_quant(x, lift)
+    q, _ = O.act_quant(x, 0)
+    vals, idx = O.unpack_slots(p["codes"], p["meta"], n, K, N, M, layout)
+    assert np.array_equal(O.acc_addsub(vals, idx, xq, layout), O.acc_dense(p["W_eff"], q))
+
+
+def test_tokens_independent():
+    g = np.random.default_rng(13)
+    W = g.normal(0, 0.02, (64, 128)).astype(np.float32)
+    x = g.standard_normal((16, 128)).astype(np.float32)
+    big = O.forward(W, x, 2, 4)
+    small = O.forward(W, x[:1], 2, 4)
+    assert np.array_equal(big["acc"][:1], small["acc"]) and np.array_equal(big["y"][:1], small["y"])
+
+
+def test_rescale_exact_cases():
+    acc = np.array([[0, 3, -5]], dtype=np.int64)
+    y = O.rescale(acc, np.float32(0.5), np.array([0.25], np.float32))
+    assert y.tolist() == [[0.0, 0.375, -0.625]]
+    y0 = O.rescale(acc, np.float32(0.5), np.array([0.0], np.float32))
+    assert not y0.any()
+
+
+def test_tiny_workload_invariants():
+    from synth import workload_inputs
+    d = workload_inputs("tiny", 0)
+    W, x = d["W:w"], d["X:256"]
+    out = O.forward(W, x, 2, 4)
+    assert out["y"].shape == (16, 256) and np.all(np.isfinite(out["y"]))
+    nnz = (out["W_eff"] != 0).reshape(256, 64, 4).sum(-1)
+    assert nnz.max() <= 2
+    assert np.all(np.abs(out["acc"]) < 2 ** 31)
