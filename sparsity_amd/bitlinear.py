@@ -1,0 +1,160 @@
+"""ctypes binding of libbitlinear (argument marshalling only; every step runs in HIP kernels).
+
+Names mirror the C ABI: ``bitlinear_packed_bytes``, ``bitlinear_pack``, ``act_quant_i8``,
+``bitlinear_fwd``.  ``pack`` / ``act_quant`` / ``fwd`` are convenience wrappers that allocate the
+output tensors with torch on the input's device and enqueue on torch's current stream.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+BL_OK = 0
+BL_LAYOUT_SPARSE = 0
+BL_LAYOUT_DENSE2 = 1
+BL_DTYPE_F32 = 0
+BL_DTYPE_BF16 = 1
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libbitlinear.so")
+_lib = None
+
+
+class BitLinearError(RuntimeError):
+    def __init__(self, status: int, call: str):
+        msg = lib().bitlinear_strerror(status).decode()
+        super().__init__(f"{call} failed with status {status}: {msg}")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """Load libbitlinear.so (built by ``sparsity_amd.build``); raises if it is missing."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m sparsity_amd.build` "
+                               "(there is no fallback implementation)")
+        L = ctypes.CDLL(LIB_PATH)
+        i64, i32, vp, sz = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t
+        L.bitlinear_packed_bytes.argtypes = [i64, i64, i32, i32, i32, ctypes.POINTER(sz),
+                                             ctypes.POINTER(sz), ctypes.POINTER(i64), ctypes.POINTER(sz)]
+        L.bitlinear_pack.argtypes = [vp, i64, i64, i32, i32, i32, vp, vp, vp, vp, sz, vp]
+        L.act_quant_i8.argtypes = [vp, i32, i64, i64, i32, vp, vp, vp]
+        L.bitlinear_fwd.argtypes = [vp, vp, i64, i64, vp, vp, vp, i32, i32, i32, i64, vp, vp, vp]
+        L.bitlinear_strerror.argtypes = [i32]
+        L.bitlinear_strerror.restype = ctypes.c_char_p
+        L.bitlinear_layout_version.argtypes = []
+        for f in (L.bitlinear_packed_bytes, L.bitlinear_pack, L.act_quant_i8, L.bitlinear_fwd,
+                  L.bitlinear_layout_version):
+            f.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _check(status: int, call: str) -> None:
+    if status != BL_OK:
+        raise BitLinearError(status, call)
+
+
+# ---------------------------------------------------------------------------------------------
+# raw C ABI (integers and pointers)
+# ---------------------------------------------------------------------------------------------
+
+def bitlinear_packed_bytes(n: int, K: int, N: int, M: int, layout: int):
+    """Returns (status, codes_bytes, meta_bytes, K_eff, ws_bytes)."""
+    cb, mb, ws = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
+    ke = ctypes.c_int64()
+    st = lib().bitlinear_packed_bytes(n, K, N, M, layout, ctypes.byref(cb), ctypes.byref(mb),
+                                      ctypes.byref(ke), ctypes.byref(ws))
+    return st, cb.value, mb.value, ke.value, ws.value
+
+
+def bitlinear_pack(W, n, K, N, M, layout, codes, meta, gamma, ws, ws_bytes, stream) -> int:
+    return lib().bitlinear_pack(W, n, K, N, M, layout, codes, meta, gamma, ws, ws_bytes, stream)
+
+
+def act_quant_i8(x, x_dtype, T, K, lift_M, xq, x_scale, stream) -> int:
+    return lib().act_quant_i8(x, x_dtype, T, K, lift_M, xq, x_scale, stream)
+
+
+def bitlinear_fwd(xq, x_scale, T, K, codes, meta, gamma, N, M, layout, n, y, acc, stream) -> int:
+    return lib().bitlinear_fwd(xq, x_scale, T, K, codes, meta, gamma, N, M, layout, n, y, acc, stream)
+
+
+# ---------------------------------------------------------------------------------------------
+# torch convenience wrappers
+# ---------------------------------------------------------------------------------------------
+
+def _stream():
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def packed_bytes(n: int, K: int, N: int = 2, M: int = 4, layout: int = BL_LAYOUT_SPARSE):
+    st, cb, mb, ke, ws = bitlinear_packed_bytes(n, K, N, M, layout)
+    _check(st, "bitlinear_packed_bytes")
+    return cb, mb, ke, ws
+
+
+def pack(W, N: int = 2, M: int = 4, layout: int = BL_LAYOUT_SPARSE, out=None, ws=None):
+    """Mask + ternarize + pack a contiguous fp32 CUDA tensor W[n][K].
+
+    Returns (codes uint8, meta uint8 or None, gamma fp32[1]) on W's device.  ``out`` may supply
+    preallocated (codes, meta, gamma); ``ws`` a uint8 workspace.
+    """
+    import torch
+    assert W.is_cuda and W.dtype == torch.float32 and W.is_contiguous() and W.dim() == 2
+    n, K = W.shape
+    cb, mb, _, wsb = packed_bytes(n, K, N, M, layout)
+    if out is None:
+        codes = torch.empty(cb, dtype=torch.uint8, device=W.device)
+        meta = torch.empty(mb, dtype=torch.uint8, device=W.device) if mb else None
+        gamma = torch.empty(4, dtype=torch.float32, device=W.device)[:1]
+    else:
+        codes, meta, gamma = out
+    if ws is None:
+        ws = torch.empty(wsb, dtype=torch.uint8, device=W.device)
+    _check(bitlinear_pack(W.data_ptr(), n, K, N, M, layout, codes.data_ptr(), _ptr(meta),
+                          gamma.data_ptr(), ws.data_ptr(), ws.numel(), _stream()), "bitlinear_pack")
+    return codes, meta, gamma
+
+
+def act_quant(x, lift_M: int = 0, out=None):
+    """Per-token int8 quantization of a contiguous fp32/bf16 CUDA tensor x[T][K].
+
+    Returns (xq int8 [T][K_eff], scale fp32 [T]).
+    """
+    import torch
+    assert x.is_cuda and x.is_contiguous() and x.dim() == 2
+    T, K = x.shape
+    dt = {torch.float32: BL_DTYPE_F32, torch.bfloat16: BL_DTYPE_BF16}[x.dtype]
+    ke = K // 2 * 3 if lift_M == 8 else K
+    if out is None:
+        xq = torch.empty((T, ke), dtype=torch.int8, device=x.device)
+        scale = torch.empty(max(T, 4), dtype=torch.float32, device=x.device)[:T]
+    else:
+        xq, scale = out
+    _check(act_quant_i8(x.data_ptr(), dt, T, K, lift_M, xq.data_ptr(), scale.data_ptr(), _stream()),
+           "act_quant_i8")
+    return xq, scale
+
+
+def fwd(xq, scale, K: int, codes, meta, gamma, n: int, N: int = 2, M: int = 4,
+        layout: int = BL_LAYOUT_SPARSE, want_acc: bool = False, out=None):
+    """y[T][n] fp32 from int8 activations and packed weights; optionally also int32 acc."""
+    import torch
+    T = xq.shape[0]
+    if out is None:
+        y = torch.empty((T, n), dtype=torch.float32, device=xq.device)
+        acc = torch.empty((T, n), dtype=torch.int32, device=xq.device) if want_acc else None
+    else:
+        y, acc = out
+    _check(bitlinear_fwd(xq.data_ptr(), scale.data_ptr(), T, K, codes.data_ptr(), _ptr(meta),
+                         gamma.data_ptr(), N, M, layout, n, y.data_ptr(), _ptr(acc), _stream()),
+           "bitlinear_fwd")
+    return (y, acc) if want_acc else y

@@ -1,0 +1,301 @@
+// Absmean scale, N:M mask, ternarization and 2-bit packing of fp32 master weights.
+//
+// gamma is the mean |W| over the whole dense master (BitNet b1.58 page, "The mechanism",
+// absmean quantization), taken before the mask (Sparse-BitNet technical summary, section 2,
+// Forward Pass: quantize, then mask).  The mask keeps the N largest |w| of the continuous master
+// in each M-group (same summary, Maskering) and 6:8 groups are rewritten as three overlapping
+// 2:4 windows (SlideSparse abstract, Sliding Window Decomposition).
+//
+// Three launches, all on the caller's stream:
+//   1. gamma_partial_kernel   fp64 partial sums of |w| (HBM-bound read of W)
+//   2. gamma_finalize_kernel  one block: sums the partials, certifies the fp32 rounding of the
+//                             exact mean with a rigorous error bound, and only when the bound
+//                             cannot decide falls back to an exact exponent-binned integer sum;
+//                             then derives the ternary threshold tau
+//   3. pack_kernel            W again (mostly from the 256 MB last-level cache), mask, codes by
+//                             |w| >= tau, slots assembled in LDS, coalesced dword stores
+#include "device_common.hpp"
+#include "launch.hpp"
+
+namespace bl {
+
+struct PackWs {
+  double partial[kGammaBlocks];
+  float tau;            // smallest fp32 x with fl32(x / gamma) > 0.5 (+inf when gamma == 0)
+  uint32_t exact_used;  // 1 when the exact fallback decided gamma (diagnostic)
+};
+static_assert(sizeof(PackWs) <= kPackWsBytes, "pack workspace");
+
+__global__ __launch_bounds__(kGammaThreads) void gamma_partial_kernel(const float4* __restrict__ W4,
+                                                                      int64_t n4,
+                                                                      double* __restrict__ partial) {
+  double acc = 0.0;
+  const int64_t stride = (int64_t)kGammaBlocks * kGammaThreads;
+  for (int64_t i = (int64_t)blockIdx.x * kGammaThreads + threadIdx.x; i < n4; i += stride) {
+    const float4 v = W4[i];
+    acc += fabs((double)v.x);
+    acc += fabs((double)v.y);
+    acc += fabs((double)v.z);
+    acc += fabs((double)v.w);
+  }
+  acc = wave_sum_f64(acc);
+  __shared__ double red[kGammaThreads / 64];
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    double s = 0.0;
+    for (int w = 0; w < kGammaThreads / 64; ++w) s += red[w];
+    partial[blockIdx.x] = s;
+  }
+}
+
+// Round (sum_e bins[e] * 2^(max(e,1)-150)) / count to the nearest fp32, ties to even, exactly.
+// bins[e] is the integer sum of the 24-bit significands of the magnitudes with biased exponent e.
+__device__ float exact_mean_from_bins(const unsigned long long* bins, uint64_t count) {
+  constexpr int L = 10;  // 320-bit integer in units of 2^-149 (sum < 2^310)
+  uint32_t lim[L];
+  for (int i = 0; i < L; ++i) lim[i] = 0;
+  for (int e = 0; e < 255; ++e) {
+    unsigned long long v = bins[e];
+    if (!v) continue;
+    const int sh = (e > 0 ? e : 1) - 1;
+    int w = sh >> 5;
+    const int b = sh & 31;
+    // v << b spans at most 88 bits: three 32-bit words starting at limb w
+    uint32_t part[3];
+    part[0] = (uint32_t)(v << b);
+    part[1] = (uint32_t)((b ? (v >> (32 - b)) : (v >> 32)) & 0xFFFFFFFFull);
+    part[2] = (uint32_t)(b ? (v >> (64 - b)) : 0ull);
+    uint64_t carry = 0;
+    for (int k = 0; w + k < L; ++k) {
+      uint64_t add = (k < 3 ? part[k] : 0u) + carry + (uint64_t)lim[w + k];
+      lim[w + k] = (uint32_t)add;
+      carry = add >> 32;
+      if (k >= 2 && carry == 0) break;
+    }
+  }
+  // long division by count (< 2^32)
+  uint32_t q[L];
+  uint64_t rem = 0;
+  for (int i = L - 1; i >= 0; --i) {
+    const uint64_t cur = (rem << 32) | lim[i];
+    q[i] = (uint32_t)(cur / count);
+    rem = cur % count;
+  }
+  // bit length of the quotient
+  int len = 0;
+  for (int i = L - 1; i >= 0; --i)
+    if (q[i]) { len = 32 * i + (32 - __clz(q[i])); break; }
+  const int shift = len > 24 ? len - 24 : 0;
+  auto bit = [&](int pos) -> uint32_t { return (q[pos >> 5] >> (pos & 31)) & 1u; };
+  uint32_t sig = 0;
+  for (int k = 23; k >= 0; --k) sig = (sig << 1) | (shift + k < 32 * L ? bit(shift + k) : 0u);
+  bool up;
+  if (shift == 0) {
+    up = (2 * rem > count) || (2 * rem == count && (sig & 1));
+  } else {
+    const uint32_t half = bit(shift - 1);
+    bool lower = rem != 0;
+    for (int pos = 0; pos < shift - 1 && !lower; ++pos) lower = bit(pos) != 0;
+    up = half && (lower || (sig & 1));
+  }
+  int sh = shift;
+  sig += up ? 1u : 0u;
+  if (sig == (1u << 24)) { sig = 1u << 23; sh += 1; }
+  const uint32_t out = sig >= (1u << 23) ? (((uint32_t)(sh + 1) << 23) | (sig & 0x7FFFFFu)) : sig;
+  return __uint_as_float(out);
+}
+
+// Smallest fp32 tau with fl32(tau / gamma) > 0.5.  Under round-to-nearest-even the fp32 quotient
+// exceeds 0.5 exactly when the real quotient exceeds 0.5 + 2^-25 (the spacing above 0.5 is
+// 2^-24), i.e. when x > gamma * (2^24 + 1) * 2^-25; that product is exact in fp64.
+__device__ float ternary_threshold(float gamma) {
+  if (!(gamma > 0.f)) return __int_as_float(0x7f800000);
+  const double t = (double)gamma * 16777217.0 * 0x1p-25;
+  float f = (float)t;
+  if ((double)f <= t) f = __int_as_float(__float_as_int(f) + 1);
+  while (true) {
+    const float prev = __int_as_float(__float_as_int(f) - 1);
+    if ((double)prev > t) f = prev; else break;
+  }
+  return f;
+}
+
+__global__ __launch_bounds__(1024) void gamma_finalize_kernel(const float* __restrict__ W,
+                                                              int64_t count, PackWs* ws,
+                                                              float* __restrict__ gamma_out) {
+  static_assert(kGammaBlocks == 1024, "one partial per thread");
+  __shared__ double red[16];
+  __shared__ unsigned long long bins[256];
+  __shared__ int certified;
+  __shared__ float g;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  double v = wave_sum_f64(ws->partial[threadIdx.x]);
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    double S = 0.0;
+    for (int w = 0; w < 16; ++w) S += red[w];
+    // longest chain of fp64 additions any |w| goes through: the per-thread loop (4 per float4),
+    // the wave butterfly (6), the block sum (4), the finalize butterfly (6) and sum (16)
+    const int64_t n4 = count / 4;
+    const int64_t per_thread = (n4 + (int64_t)kGammaBlocks * kGammaThreads - 1) / ((int64_t)kGammaBlocks * kGammaThreads);
+    const double depth = 4.0 * (double)per_thread + 64.0;
+    const double u = 0x1p-53;
+    const double err = 2.0 * depth * u * S;  // >= ((1+u)^depth - 1) * S for nonnegative terms
+    const double cnt = (double)count;
+    const double lo = (S - err) / cnt * (1.0 - 4.0 * u);
+    const double hi = (S + err) / cnt * (1.0 + 4.0 * u);
+    const float glo = (float)lo, ghi = (float)hi;
+    if (S == 0.0) { certified = 1; g = 0.f; }
+    else if (glo == ghi) { certified = 1; g = glo; }
+    else certified = 0;
+  }
+  __syncthreads();
+  if (!certified) {
+    for (int i = threadIdx.x; i < 256; i += 1024) bins[i] = 0ull;
+    __syncthreads();
+    for (int64_t i = threadIdx.x; i < count; i += 1024) {
+      const uint32_t b = __float_as_uint(W[i]) & 0x7FFFFFFFu;
+      const uint32_t e = b >> 23;
+      const uint32_t m = (b & 0x7FFFFFu) | (e ? 0x800000u : 0u);
+      atomicAdd(&bins[e], (unsigned long long)m);
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) g = exact_mean_from_bins(bins, (uint64_t)count);
+  }
+  if (threadIdx.x == 0) {
+    gamma_out[0] = g;
+    ws->tau = ternary_threshold(g);
+    ws->exact_used = certified ? 0u : 1u;
+  }
+}
+
+constexpr int kPackKB = 256;  // dense K columns per pack tile
+
+// One block packs one 32-row panel x 256 dense columns.  Phase 1 stages the fp32 tile in LDS with
+// coalesced 1 KB row reads; phase 2 turns each M-group into slot bytes (code | index << 2);
+// phase 3 assembles 16-slot units into code/meta dwords, which land contiguously in the tiled
+// layout (unit v = 32*u + r of the tile is dword base + v).
+template <int LAYOUT, int M>
+__global__ __launch_bounds__(256) void pack_kernel(const float* __restrict__ W, int n, int K, int N,
+                                                   int k_tiles, const float* __restrict__ tau_p,
+                                                   uint32_t* __restrict__ codes,
+                                                   uint32_t* __restrict__ meta) {
+  constexpr bool SP = LAYOUT == kLayoutSparse;
+  constexpr int WS = kPackKB + 4;                                      // padded fp32 row
+  constexpr int SLOTS = SP ? (M == 4 ? kPackKB / 2 : kPackKB * 3 / 4) : kPackKB;
+  constexpr int SS = SLOTS + 16;                                       // padded slot row
+  constexpr int GPR = kPackKB / M;                                     // groups per tile row
+  constexpr int UPR = SLOTS / 16;                                      // units per tile row
+  __shared__ __attribute__((aligned(16))) float tile[32 * WS];
+  __shared__ __attribute__((aligned(16))) uint8_t slots[32 * SS];
+
+  const int P = blockIdx.x / k_tiles;
+  const int kb = blockIdx.x % k_tiles;
+  const int k0 = kb * kPackKB;
+  const int r0 = P * kPanel;
+  const int kw = min(kPackKB, K - k0);
+  const float tau = *tau_p;
+
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int row = i * 4 + (threadIdx.x >> 6);
+    const int c4 = threadIdx.x & 63;
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (r0 + row < n && 4 * c4 < kw) v = *(const float4*)(W + (size_t)(r0 + row) * K + k0 + 4 * c4);
+    *(float4*)&tile[row * WS + 4 * c4] = v;
+  }
+  __syncthreads();
+
+  const int nkeep = SP ? (M == 4 ? 2 : 6) : N;
+  for (int gid = threadIdx.x; gid < 32 * GPR; gid += 256) {
+    const int row = gid / GPR, g = gid % GPR;
+    float w[M];
+    uint32_t a[M];
+#pragma unroll
+    for (int j = 0; j < M; ++j) {
+      w[j] = tile[row * WS + g * M + j];
+      a[j] = __float_as_uint(w[j]) & 0x7FFFFFFFu;
+    }
+    uint32_t keep = 0;
+#pragma unroll
+    for (int i = 0; i < M; ++i) {
+      int rank = 0;
+#pragma unroll
+      for (int j = 0; j < M; ++j)
+        if (j != i) rank += (a[j] > a[i]) || (a[j] == a[i] && j < i);
+      if (rank < nkeep) keep |= 1u << i;
+    }
+    auto code = [&](int j) -> uint32_t { return fabsf(w[j]) >= tau ? (w[j] < 0.f ? 3u : 1u) : 0u; };
+    uint8_t* out = &slots[row * SS];
+    if constexpr (SP && M == 4) {
+      int s = 0;
+#pragma unroll
+      for (int p = 0; p < 4; ++p)
+        if (keep >> p & 1u) { out[2 * g + s] = (uint8_t)(code(p) | (p << 2)); ++s; }
+    } else if constexpr (SP && M == 8) {
+      // windows 0-3, 2-5, 4-7; ascending positions, each window takes at most two
+      int c0 = 0, c1 = 0, c2 = 0;
+#pragma unroll
+      for (int p = 0; p < 8; ++p) {
+        if (!(keep >> p & 1u)) continue;
+        int wdw;
+        if (p <= 3 && c0 < 2) { wdw = 0; ++c0; }
+        else if (p <= 5 && c1 < 2) { wdw = 1; ++c1; }
+        else { wdw = 2; ++c2; }
+        const int slot = 2 * wdw + (wdw == 0 ? c0 : wdw == 1 ? c1 : c2) - 1;
+        out[6 * g + slot] = (uint8_t)(code(p) | ((p - 2 * wdw) << 2));
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < M; ++j) out[g * M + j] = (uint8_t)((keep >> j & 1u) ? code(j) : 0u);
+    }
+  }
+  __syncthreads();
+
+  const int valid_slots = SP ? (M == 4 ? kw / 2 : kw * 3 / 4) : kw;
+  const int units_valid = valid_slots / 16;
+  const int nfrag = SP ? (M == 4 ? K : K * 3 / 2) / 64 : K / 32;     // fragments per panel
+  const size_t base = ((size_t)P * nfrag + (size_t)kb * (UPR / 2)) * 64;
+  for (int v = threadIdx.x; v < 32 * UPR; v += 256) {
+    const int u = v >> 5, r = v & 31;
+    if (u >= units_valid) continue;
+    const uint4 sb = *(const uint4*)&slots[r * SS + 16 * u];
+    const uint32_t wd[4] = {sb.x, sb.y, sb.z, sb.w};
+    uint32_t cw = 0, mw = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const uint32_t b = (wd[i >> 2] >> (8 * (i & 3))) & 0xFFu;
+      cw |= (b & 3u) << (8 * (i & 3) + 2 * (i >> 2));
+      mw |= (b >> 2) << (2 * i);
+    }
+    codes[base + v] = cw;
+    if constexpr (SP) meta[base + v] = mw;
+  }
+}
+
+hipError_t launch_pack(const float* W, int64_t n, int64_t K, int N, int M, int layout,
+                       uint32_t* codes, uint32_t* meta, float* gamma, void* ws_raw, hipStream_t s) {
+  PackWs* ws = (PackWs*)ws_raw;
+  const int64_t count = n * K;
+  gamma_partial_kernel<<<kGammaBlocks, kGammaThreads, 0, s>>>((const float4*)W, count / 4, ws->partial);
+  gamma_finalize_kernel<<<1, 1024, 0, s>>>(W, count, ws, gamma);
+  const int panels = (int)((n + kPanel - 1) / kPanel);
+  const int k_tiles = (int)((K + kPackKB - 1) / kPackKB);
+  const dim3 grid((unsigned)(panels * k_tiles));
+  if (layout == kLayoutSparse) {
+    if (M == 4)
+      pack_kernel<kLayoutSparse, 4><<<grid, 256, 0, s>>>(W, (int)n, (int)K, N, k_tiles, &ws->tau, codes, meta);
+    else
+      pack_kernel<kLayoutSparse, 8><<<grid, 256, 0, s>>>(W, (int)n, (int)K, N, k_tiles, &ws->tau, codes, meta);
+  } else {
+    if (M == 4)
+      pack_kernel<kLayoutDense2, 4><<<grid, 256, 0, s>>>(W, (int)n, (int)K, N, k_tiles, &ws->tau, codes, nullptr);
+    else
+      pack_kernel<kLayoutDense2, 8><<<grid, 256, 0, s>>>(W, (int)n, (int)K, N, k_tiles, &ws->tau, codes, nullptr);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace bl

@@ -1,0 +1,135 @@
+"""C ABI checks that need no GPU: the library loads, exports every symbol the header declares,
+reports packed sizes that match the layout definition, and rejects bad arguments before it
+touches the HIP runtime (fake, never dereferenced device addresses are passed)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle as O
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bitlinear.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    from sparsity_amd import bitlinear as B
+    if not os.path.exists(B.LIB_PATH):
+        from sparsity_amd import build
+        build.build()
+    return B
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\**(\w+)\s*\(", src, flags=re.M)))
+
+
+def test_exports_every_declared_symbol(L):
+    names = _declared()
+    assert {"bitlinear_pack", "act_quant_i8", "bitlinear_fwd", "bitlinear_packed_bytes",
+            "bitlinear_strerror", "bitlinear_layout_version"} <= set(names)
+    lib = ctypes.CDLL(L.LIB_PATH)
+    for nm in names:
+        assert hasattr(lib, nm), nm
+
+
+def test_layout_version_and_strerror(L):
+    assert L.lib().bitlinear_layout_version() == 1
+    for st in (0, -22, -95, -28, -5, 7):
+        assert isinstance(L.lib().bitlinear_strerror(st), bytes)
+
+
+@pytest.mark.parametrize("n,K,N,M,layout", [
+    (1, 64, 2, 4, 0), (6912, 2560, 2, 4, 0), (2560, 6912, 2, 4, 0), (11008, 4096, 2, 4, 0),
+    (4096, 4096, 6, 8, 0), (45, 384, 6, 8, 0), (33, 288, 2, 4, 1), (33, 288, 6, 8, 1),
+    (8640, 3200, 2, 4, 0), (3200, 8640, 2, 4, 0), (100, 96, 4, 4, 1)])
+def test_packed_bytes_match_layout(L, n, K, N, M, layout):
+    st, cb, mb, ke, ws = L.bitlinear_packed_bytes(n, K, N, M, layout)
+    assert st == 0
+    ncode, nmeta, _ = O.packed_dwords(n, K, N, M, layout)
+    assert cb == 4 * ncode and mb == 4 * nmeta and ke == O.k_eff(K, N, M, layout) and ws > 0
+
+
+@pytest.mark.parametrize("n,K,N,M,layout,want", [
+    (64, 100, 2, 4, 0, -22),       # K % 64
+    (64, 192, 6, 8, 0, -22),       # 6:8 needs K % 128
+    (64, 48, 2, 4, 1, -22),        # DENSE2 needs K % 32
+    (0, 256, 2, 4, 0, -22),        # n >= 1
+    (64, 256, 3, 4, 0, -95),       # SPARSE supports 2:4 and 6:8 only
+    (64, 256, 2, 4, 7, -95),       # unknown layout
+    (64, 256, 5, 4, 1, -95),       # N > M
+    (64, 256, 2, 16, 1, -95),      # M in {4, 8}
+    (1 << 20, 1 << 12, 2, 4, 0, -22),  # n*K >= 2^32
+])
+def test_packed_bytes_rejects(L, n, K, N, M, layout, want):
+    assert L.bitlinear_packed_bytes(n, K, N, M, layout)[0] == want
+
+
+FAKE = 0x7F0000000000   # 16-byte aligned, never dereferenced (validation fails before use)
+
+
+def test_pack_rejects_before_launch(L):
+    P = FAKE
+    ok = dict(W=P, n=64, K=256, N=2, M=4, layout=0, codes=P, meta=P, gamma=P, ws=P, ws_bytes=1 << 20)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return L.bitlinear_pack(a["W"], a["n"], a["K"], a["N"], a["M"], a["layout"], a["codes"],
+                                a["meta"], a["gamma"], a["ws"], a["ws_bytes"], None)
+    assert call(K=100) == -22
+    assert call(N=3) == -95
+    assert call(W=None) == -22
+    assert call(W=P + 4) == -22
+    assert call(codes=P + 8) == -22
+    assert call(meta=None) == -22
+    assert call(layout=1, meta=P) == -22          # DENSE2 takes no meta buffer
+    assert call(gamma=None) == -22
+    assert call(ws=None) == -22
+    assert call(ws_bytes=16) == -28
+
+
+def test_act_quant_rejects_before_launch(L):
+    P = FAKE
+    assert L.act_quant_i8(P, 2, 4, 256, 0, P, P, None) == -95        # dtype
+    assert L.act_quant_i8(P, 0, 4, 256, 4, P, P, None) == -22        # lift_M
+    assert L.act_quant_i8(P, 0, -1, 256, 0, P, P, None) == -22       # T < 0
+    assert L.act_quant_i8(P, 0, 4, 100, 0, P, P, None) == -22        # K % 8
+    assert L.act_quant_i8(None, 0, 4, 256, 0, P, P, None) == -22
+    assert L.act_quant_i8(P, 1, 4, 256, 0, P + 2, P, None) == -22
+    assert L.act_quant_i8(P, 0, 0, 256, 0, P, P, None) == 0          # T == 0: nothing enqueued
+    assert L.act_quant_i8(None, 0, 0, 256, 0, None, None, None) == 0
+
+
+def test_fwd_rejects_before_launch(L):
+    P = FAKE
+    ok = dict(xq=P, xs=P, T=4, K=256, codes=P, meta=P, gamma=P, N=2, M=4, layout=0, n=64, y=P, acc=None)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return L.bitlinear_fwd(a["xq"], a["xs"], a["T"], a["K"], a["codes"], a["meta"], a["gamma"],
+                               a["N"], a["M"], a["layout"], a["n"], a["y"], a["acc"], None)
+    assert call(K=100) == -22
+    assert call(N=6, M=8, K=192) == -22
+    assert call(N=1, M=4) == -95
+    assert call(T=-1) == -22
+    assert call(xq=P + 1) == -22
+    assert call(y=None) == -22
+    assert call(meta=None) == -22
+    assert call(layout=1, meta=P) == -22
+    assert call(acc=P + 2) == -22
+    assert call(T=0) == 0
+    assert call(T=0, xq=None, xs=None, y=None) == 0
+
+
+def test_product_path_never_imports_oracle():
+    pkg = os.path.join(ROOT, "sparsity_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".hpp", ".cpp", ".h")):
+                txt = open(os.path.join(dirpath, f)).read()
+                assert not re.search(r"\boracle\b", txt), f
