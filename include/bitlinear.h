@@ -46,7 +46,7 @@
  *
  * Shapes: n >= 1 (out features), K (in features): SPARSE 2:4 needs K % 64 == 0; SPARSE 6:8
  * needs K % 128 == 0; DENSE2 needs K % 32 == 0 and K % M == 0 with M in {4, 8}, 1 <= N <= M.
- * n * K < 2^32.  K_eff * 127 < 2^31.  T >= 0 tokens (T == 0 enqueues nothing).
+ * n * K < 2^32.  K_eff * 127 < 2^31.  T >= 0 tokens (T == 0 enqueues nothing), T * K_eff < 2^31.
  *
  * Conventions for every call:
  *   - All buffers are device memory owned by the caller; the library allocates nothing and keeps

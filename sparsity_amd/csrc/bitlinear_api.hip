@@ -3,7 +3,7 @@
 #include <errno.h>
 #include <stdint.h>
 
-#include "../../include/bitlinear.h"
+#include "bitlinear.h"
 #include "launch.hpp"
 
 namespace {
@@ -92,6 +92,7 @@ int bitlinear_fwd(const int8_t* xq, const float* x_scale, int64_t T, int64_t K,
   const int st = check_shape(n, K, N, M, layout, &ke);
   if (st != BL_OK) return st;
   if (T < 0 || T > INT32_MAX || (uint64_t)T * (uint64_t)n >= (1ull << 40)) return BL_EINVAL;
+  if ((uint64_t)T * (uint64_t)ke >= (1ull << 31)) return BL_EINVAL;  // 32-bit activation offsets
   if (T == 0) return BL_OK;  // nothing is read or written; pointers may be NULL
   if (!aligned16(xq) || !aligned16(x_scale) || !aligned16(codes) || !aligned16(gamma) ||
       !aligned16(y))

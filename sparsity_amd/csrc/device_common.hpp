@@ -8,6 +8,7 @@ namespace bl {
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef int v16i __attribute__((ext_vector_type(16)));
+typedef float v4f __attribute__((ext_vector_type(4)));
 
 constexpr int kLayoutSparse = 0;
 constexpr int kLayoutDense2 = 1;

@@ -51,7 +51,11 @@ __device__ __forceinline__ void store_out(float* __restrict__ y, int32_t* __rest
 // ---------------------------------------------------------------------------------------------
 // decode GEMV
 // ---------------------------------------------------------------------------------------------
-template <int LAYOUT, int NW, int UNROLL>
+// One block per 32-row panel; wave w owns the K steps [w*per, (w+1)*per).  Every wave issues all of
+// its weight and activation loads before its first MFMA, so the whole panel is in flight at once
+// (a decode matrix is only a few MB: the kernel is bound by latency, not by bandwidth).  Partial
+// accumulators of the live tokens are summed across waves through LDS in wave order.
+template <int LAYOUT, int NW, int MAXU>
 __global__ __launch_bounds__(64 * NW) void gemv_kernel(const int8_t* __restrict__ xq,
                                                        const float* __restrict__ xs, int T,
                                                        int Keff, const uint32_t* __restrict__ codes,
@@ -64,34 +68,40 @@ __global__ __launch_bounds__(64 * NW) void gemv_kernel(const int8_t* __restrict_
   const int P = blockIdx.x;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int NF = Keff / KSTEP;
+  const int per = (NF + NW - 1) / NW;
+  const int s_begin = wave * per;
+  const int s_end = min(NF, s_begin + per);
   const uint32_t* cp = codes + (size_t)P * NF * 64 + lane;
   const uint32_t* mp = SP ? meta + (size_t)P * NF * 64 + lane : nullptr;
   const int tok = lane & 31, h = lane >> 5;
   const bool live = tok < T;
-  const int8_t* xp = xq + (size_t)(live ? tok : 0) * Keff + 16 * h;
+  // lanes of dead tokens read token T-1 (their D columns are never stored): no branches
+  const int8_t* xp = xq + (size_t)min(tok, T - 1) * Keff + 16 * h;
   v16i acc = {};
-  for (int s0 = wave * UNROLL; s0 < NF; s0 += NW * UNROLL) {
-    uint32_t c[UNROLL], m[UNROLL];
-    int4 blo[UNROLL], bhi[UNROLL];
+  for (int s0 = s_begin; s0 < s_end; s0 += MAXU) {
+    uint32_t c[MAXU], m[MAXU];
+    int4 blo[MAXU], bhi[MAXU];
 #pragma unroll
-    for (int u = 0; u < UNROLL; ++u) {
-      const int s = s0 + u;
-      const bool ok = s < NF;
-      c[u] = ok ? __builtin_nontemporal_load(cp + (size_t)s * 64) : 0u;
-      m[u] = (SP && ok) ? __builtin_nontemporal_load(mp + (size_t)s * 64) : kPadMeta;
-      blo[u] = make_int4(0, 0, 0, 0);
-      bhi[u] = make_int4(0, 0, 0, 0);
-      if (ok && live) {
-        blo[u] = *(const int4*)(xp + (size_t)s * KSTEP);
-        if constexpr (SP) bhi[u] = *(const int4*)(xp + (size_t)s * KSTEP + 32);
-      }
+    for (int u = 0; u < MAXU; ++u) {
+      const int s = min(s0 + u, s_end - 1);     // past the end: reload the last step, code zeroed
+      c[u] = __builtin_nontemporal_load(cp + (size_t)s * 64);
+      m[u] = SP ? __builtin_nontemporal_load(mp + (size_t)s * 64) : kPadMeta;
+      blo[u] = *(const int4*)(xp + (size_t)s * KSTEP);
+      bhi[u] = SP ? *(const int4*)(xp + (size_t)s * KSTEP + 32) : make_int4(0, 0, 0, 0);
     }
 #pragma unroll
-    for (int u = 0; u < UNROLL; ++u) acc = mfma_step<SP>(c[u], m[u], blo[u], bhi[u], acc);
+    for (int u = 0; u < MAXU; ++u) {
+      const uint32_t cu = (s0 + u < s_end) ? c[u] : 0u;
+      acc = mfma_step<SP>(cu, m[u], blo[u], bhi[u], acc);
+    }
   }
+
+  // live tokens only: D column = token = lane % 32
   __shared__ int red[NW][16][64];
+  if (live) {
 #pragma unroll
-  for (int r = 0; r < 16; ++r) red[wave][r][lane] = acc[r];
+    for (int r = 0; r < 16; ++r) red[wave][r][lane] = acc[r];
+  }
   __syncthreads();
   const float gamma = *gamma_p;
   for (int i = threadIdx.x; i < 16 * 64; i += 64 * NW) {
@@ -219,15 +229,282 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(
   }
 }
 
+// Large-tile prefill GEMM: block tile 256 rows x 256 tokens, 8 waves as 2 (rows) x 4 (tokens),
+// each wave 128 rows x 64 tokens = 4 panels x 2 token groups = 8 MFMA tiles (128 int32
+// accumulators per lane, so two waves share a SIMD and hide each other's LDS latency).
+//
+// Operands reach LDS with direct global->LDS loads (global_load_lds_dwordx4: lane l's 16 bytes
+// land at the wave-uniform LDS base + 16*l), so no VGPRs stage them, and a ring of three stage
+// buffers keeps two stages in flight while the third is multiplied.  A stage is KS MFMA K-steps:
+// B = 256 tokens x 128 bytes, A = 8 panels x KS fragments of codes (and of meta).  The three
+// buffers are distinct __shared__ variables and the stage loop is unrolled by three, so every
+// access names its buffer statically.  The loads are inline asm the compiler does not track, so
+// each wave waits on its own vmcnt (every stage issues exactly LPS loads per wave) and meets the
+// others at a bare s_barrier (no fence: a fence would also drain the loads meant to stay in
+// flight).  B rows are
+// XOR-swizzled in 16-byte chunks (chunk c of token t sits at position c ^ (t % 8)) so fragment
+// reads spread over the LDS banks.
+//
+// Rows past the last panel, tokens past T and K past the end (a partial last stage) read clamped,
+// valid addresses; their codes are zeroed or their results never stored.
+//
+// Blocks are mapped XCD-major: the hardware deals consecutive block ids round-robin to the 8
+// XCDs, so block b takes tile (b % 8) * (tiles / 8) + b / 8 and each XCD walks a contiguous run
+// of tiles that share a token tile, which then stays in that XCD's L2.
+constexpr int kBigStage = 256 * 128 + 8 * 1024;   // B + A bytes of one stage (both layouts)
+__shared__ __attribute__((aligned(16))) int8_t g_stage0[kBigStage];
+__shared__ __attribute__((aligned(16))) int8_t g_stage1[kBigStage];
+__shared__ __attribute__((aligned(16))) int8_t g_stage2[kBigStage];
+
+template <int B>
+__device__ __forceinline__ int8_t* stage_buf() {
+  return B == 0 ? g_stage0 : (B == 1 ? g_stage1 : g_stage2);
+}
+
+__device__ __forceinline__ void block_barrier_nofence() {
+  asm volatile("s_barrier" ::: "memory");
+}
+
+typedef __attribute__((address_space(3))) int8_t lds_i8;
+__device__ __forceinline__ uint32_t lds_offset(const void* p) { return (uint32_t)(uintptr_t)(lds_i8*)p; }
+
+// global_load_lds_dwordx4 issued as inline asm: 16 bytes per lane from `src` to LDS at
+// m0 + 16 * lane.  It writes no VGPR, so nothing can consume a register before the data lands;
+// completion is tracked by the caller's explicit vmcnt waits.  (Issued through the builtin, the
+// compiler cannot prove the in-flight loads miss the buffer being read and drains them all before
+// every LDS read, which serializes the pipeline.)  One wait state separates the m0 write from
+// its use.
+__device__ __forceinline__ void lds_dma16(const void* src, uint32_t m0) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+               :: "s"(m0), "v"(src) : "memory", "m0");
+}
+
+template <int LAYOUT>
+struct BigGemm {
+  static constexpr bool SP = LAYOUT == kLayoutSparse;
+  static constexpr int KSTEP = SP ? 64 : 32;
+  static constexpr int KS = SP ? 2 : 4;              // MFMA K-steps per stage: 128 K bytes
+  static constexpr int NWAVE = 8;
+  static constexpr int WM = 4, WN = 2;
+  static constexpr int BM = 256, BN = 256;
+  static constexpr int SK = KS * KSTEP;              // 128 bytes of K per token per stage
+  static constexpr int B_BYTES = BN * SK;            // 32 KB
+  static constexpr int A_PANEL = KS * 256 * (SP ? 2 : 1);
+  static constexpr int A_BYTES = 8 * A_PANEL;        // 8 KB
+  static constexpr int B_LOADS = B_BYTES / 1024 / NWAVE;
+  static constexpr int A_LOADS = A_BYTES / 1024 / NWAVE;
+  static constexpr int LPS = B_LOADS + A_LOADS;
+  static_assert(SK == 128 && B_BYTES + A_BYTES == kBigStage, "stage layout");
+  static_assert(A_LOADS >= 1 && A_BYTES % (1024 * NWAVE) == 0, "A stage splits evenly over waves");
+
+  const int8_t* __restrict__ xq;
+  const uint32_t* __restrict__ codes;
+  const uint32_t* __restrict__ meta;
+  int Keff, NF, NS, lane, wave, wm, wn, h, b_chunk;
+  uint32_t b_src[B_LOADS];
+  uint32_t a_src[A_LOADS];
+  bool a_meta[A_LOADS];
+  int a_frag0[A_LOADS];
+  v16i acc[WM][WN];
+
+  // Loads of stage st (clamped to the last real stage: the padded stages of the unrolled loop
+  // reload valid data that their zeroed codes never use).
+  template <int BUF>
+  __device__ __forceinline__ void issue(int st_in) {
+    int8_t* base = stage_buf<BUF>();
+    const int st = min(st_in, NS - 1);
+    const int kk = min(st * SK + b_chunk, Keff - 16);   // chunks past K_eff reread the last one
+    const uint32_t wbase = __builtin_amdgcn_readfirstlane(lds_offset(base) + (uint32_t)wave * (B_LOADS * 1024));
+#pragma unroll
+    for (int i = 0; i < B_LOADS; ++i) lds_dma16(xq + b_src[i] + kk, wbase + i * 1024);
+    const uint32_t abase = __builtin_amdgcn_readfirstlane(lds_offset(base) + B_BYTES + (uint32_t)wave * (A_LOADS * 1024));
+#pragma unroll
+    for (int q = 0; q < A_LOADS; ++q) {
+      const int s = min(st * KS + a_frag0[q], NF - 1);
+      const uint32_t* src = (a_meta[q] ? meta : codes) + a_src[q] + (uint32_t)s * 64;
+      lds_dma16(src, abase + q * 1024);
+    }
+  }
+
+  // One stage: wait for its loads (at most the next stage's LPS loads stay outstanding), barrier,
+  // refill the buffer freed by the previous stage, multiply.  Straight-line code on purpose: a
+  // branch between the refill and the reads makes the compiler drain every load before the reads.
+  template <int BUF>
+  __device__ __forceinline__ void stage(int st) {
+    __builtin_amdgcn_s_waitcnt(0x3F70 | LPS);
+    block_barrier_nofence();
+    issue<(BUF + 2) % 3>(st + 2);
+    const int8_t* bb = stage_buf<BUF>();
+    const int8_t* ab = bb + B_BYTES;
+#pragma unroll
+    for (int j = 0; j < KS; ++j) {
+      const bool live_step = st * KS + j < NF;
+      v4i a[WM];
+      uint32_t mm[WM];
+#pragma unroll
+      for (int p = 0; p < WM; ++p) {
+        const int8_t* pa = ab + (wm * WM + p) * A_PANEL + j * 256 + 4 * lane;
+        const uint32_t code = *(const uint32_t*)pa;
+        a[p] = expand_codes(live_step ? code : 0u);
+        mm[p] = SP ? *(const uint32_t*)(pa + KS * 256) : 0u;
+      }
+#pragma unroll
+      for (int g = 0; g < WN; ++g) {
+        const int tt = (wn * WN + g) * 32 + (lane & 31);
+        const int8_t* rowp = bb + tt * SK;
+        const int c1 = (j * KSTEP) / 16 + h;
+        const int4 blo = *(const int4*)(rowp + 16 * (c1 ^ (tt & 7)));
+        if constexpr (SP) {
+          const int4 bhi = *(const int4*)(rowp + 16 * ((c1 + 2) ^ (tt & 7)));
+          v8i bv;
+          bv[0] = blo.x; bv[1] = blo.y; bv[2] = blo.z; bv[3] = blo.w;
+          bv[4] = bhi.x; bv[5] = bhi.y; bv[6] = bhi.z; bv[7] = bhi.w;
+#pragma unroll
+          for (int p = 0; p < WM; ++p)
+            acc[p][g] = __builtin_amdgcn_smfmac_i32_32x32x64_i8(a[p], bv, acc[p][g], (int)mm[p], 0, 0);
+        } else {
+          v4i bv;
+          bv[0] = blo.x; bv[1] = blo.y; bv[2] = blo.z; bv[3] = blo.w;
+#pragma unroll
+          for (int p = 0; p < WM; ++p)
+            acc[p][g] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[p], bv, acc[p][g], 0, 0, 0);
+        }
+      }
+    }
+  }
+};
+
+template <int LAYOUT>
+__global__ __launch_bounds__(512, 1) void gemm_big_kernel(
+    const int8_t* __restrict__ xq, const float* __restrict__ xs, int T, int Keff,
+    const uint32_t* __restrict__ codes, const uint32_t* __restrict__ meta,
+    const float* __restrict__ gamma_p, int n, int npanels, float* __restrict__ y,
+    int32_t* __restrict__ acc_out, int tiles_m, int tiles) {
+  using G = BigGemm<LAYOUT>;
+  G k;
+  k.xq = xq; k.codes = codes; k.meta = meta; k.Keff = Keff;
+  k.lane = threadIdx.x & 63;
+  k.wave = threadIdx.x >> 6;
+  k.wm = k.wave & 1;
+  k.wn = k.wave >> 1;
+  k.h = k.lane >> 5;
+  const int full = (tiles / 8) * 8;
+  const int b = blockIdx.x;
+  const int t = b < full ? (b % 8) * (tiles / 8) + b / 8 : b;
+  const int tm = t % tiles_m, tn = t / tiles_m;
+  const int row0 = tm * G::BM, tok0 = tn * G::BN;
+  k.NF = Keff / G::KSTEP;
+  k.NS = (k.NF + G::KS - 1) / G::KS;
+
+  // B: load i of a wave fills LDS bytes [(wave*B_LOADS + i) * 1024, +1024) = 8 token rows; lane l
+  // covers row position l % 8 of token row l / 8 and fetches global chunk (l % 8) ^ (row % 8)
+  k.b_chunk = 16 * ((k.lane & 7) ^ ((k.lane >> 3) & 7));
+#pragma unroll
+  for (int i = 0; i < G::B_LOADS; ++i) {
+    const int tt = (k.wave * G::B_LOADS + i) * 8 + (k.lane >> 3);
+    k.b_src[i] = (uint32_t)(min(tok0 + tt, T - 1) * Keff);
+  }
+  // A: load q of a wave fills LDS bytes [(wave*A_LOADS + q) * 1024, +1024) of the A stage, laid
+  // out [panel][codes: KS fragments][meta: KS fragments], 256 bytes per fragment
+#pragma unroll
+  for (int q = 0; q < G::A_LOADS; ++q) {
+    const int byte0 = (k.wave * G::A_LOADS + q) * 1024 + k.lane * 16;
+    const int pw = byte0 / G::A_PANEL;
+    const int inpanel = byte0 % G::A_PANEL;
+    k.a_meta[q] = G::SP && inpanel >= G::KS * 256;
+    const int inrun = inpanel % (G::KS * 256);
+    k.a_frag0[q] = inrun / 256;
+    const int panel = min(row0 / kPanel + pw, npanels - 1);
+    k.a_src[q] = (uint32_t)(panel * k.NF * 64 + (inrun % 256) / 4);
+  }
+#pragma unroll
+  for (int p = 0; p < G::WM; ++p)
+#pragma unroll
+    for (int g = 0; g < G::WN; ++g) k.acc[p][g] = v16i{};
+
+  // stage count padded to a multiple of 3; padded stages have every code zeroed
+  k.template issue<0>(0);
+  k.template issue<1>(1);
+  for (int st = 0; st < k.NS; st += 3) {
+    k.template stage<0>(st);
+    k.template stage<1>(st + 1);
+    k.template stage<2>(st + 2);
+  }
+  __builtin_amdgcn_s_waitcnt(0x3F70);   // no load may still be writing LDS when the block ends
+
+  const float gamma = *gamma_p;
+  const int lane = k.lane, h = k.h;
+  // Lane (token lane % 32) holds rows 8j + 4h + i (i = 0..3) of each 32-row panel: four runs of
+  // four consecutive outputs.  Full panels with 16-byte aligned rows take one 16-byte store per
+  // run; ragged edges fall back to element stores.  The four stores of a token complete one
+  // 128-byte line, which L2 merges; nontemporal stores would send the 32-byte pieces to HBM one by
+  // one (measured 1.7x slower for the whole GEMM).
+  const bool vec_ok = (n & 3) == 0;
+#pragma unroll
+  for (int g = 0; g < G::WN; ++g) {
+    const int tk = tok0 + (k.wn * G::WN + g) * 32 + (lane & 31);
+    if (tk >= T) continue;
+    const float sc = xs[tk];
+    float* yrow = y + (size_t)tk * n;
+#pragma unroll
+    for (int p = 0; p < G::WM; ++p) {
+      const int o0 = row0 + (k.wm * G::WM + p) * 32;
+      if (vec_ok && o0 + 32 <= n) {
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const int o = o0 + 8 * jj + 4 * h;
+          v4f v;
+          v[0] = ((float)k.acc[p][g][4 * jj + 0] * gamma) * sc;
+          v[1] = ((float)k.acc[p][g][4 * jj + 1] * gamma) * sc;
+          v[2] = ((float)k.acc[p][g][4 * jj + 2] * gamma) * sc;
+          v[3] = ((float)k.acc[p][g][4 * jj + 3] * gamma) * sc;
+          *(v4f*)(yrow + o) = v;
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int o = o0 + 8 * (r >> 2) + 4 * h + (r & 3);
+          if (o < n) yrow[o] = ((float)k.acc[p][g][r] * gamma) * sc;
+        }
+      }
+    }
+  }
+  if (acc_out) {
+#pragma unroll
+    for (int g = 0; g < G::WN; ++g) {
+      const int tk = tok0 + (k.wn * G::WN + g) * 32 + (lane & 31);
+      if (tk >= T) continue;
+#pragma unroll
+      for (int p = 0; p < G::WM; ++p)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int o = row0 + (k.wm * G::WM + p) * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+          if (o < n) acc_out[(size_t)tk * n + o] = k.acc[p][g][r];
+        }
+    }
+  }
+}
+
 template <int LAYOUT>
 static hipError_t launch_fwd_layout(const int8_t* xq, const float* xs, int64_t T, int64_t Keff,
                                     const uint32_t* codes, const uint32_t* meta,
                                     const float* gamma, int64_t n, float* y, int32_t* acc,
                                     hipStream_t s) {
   const int npanels = (int)((n + kPanel - 1) / kPanel);
+  constexpr int KSTEP = LAYOUT == kLayoutSparse ? 64 : 32;
+  const int64_t nf = Keff / KSTEP;
   if (T <= 32) {
-    gemv_kernel<LAYOUT, 8, 4><<<npanels, 512, 0, s>>>(xq, xs, (int)T, (int)Keff, codes, meta, gamma,
-                                                      (int)n, y, acc);
+    if (nf <= 8 * 4)
+      gemv_kernel<LAYOUT, 8, 4><<<npanels, 512, 0, s>>>(xq, xs, (int)T, (int)Keff, codes, meta,
+                                                        gamma, (int)n, y, acc);
+    else
+      gemv_kernel<LAYOUT, 16, 8><<<npanels, 1024, 0, s>>>(xq, xs, (int)T, (int)Keff, codes, meta,
+                                                          gamma, (int)n, y, acc);
+  } else if (T > 128) {
+    const int tiles_m = (int)((n + 255) / 256);
+    const int tiles = tiles_m * (int)((T + 255) / 256);
+    gemm_big_kernel<LAYOUT><<<tiles, 512, 0, s>>>(xq, xs, (int)T, (int)Keff, codes, meta, gamma,
+                                                     (int)n, npanels, y, acc, tiles_m, tiles);
   } else {
     constexpr int WM = 2, WN = 2, WAM = 2, WAN = 2;
     constexpr int BM = 32 * WM * WAM, BN = 32 * WN * WAN;

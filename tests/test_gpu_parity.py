@@ -175,6 +175,13 @@ def test_fwd_gemm(N, M, layout, T):
     _fwd_case(300, K, T, N, M, layout, seed=T * 17 + M)
 
 
+@pytest.mark.parametrize("N,M,layout,K", [(2, 4, O.LAYOUT_SPARSE, 320), (2, 4, O.LAYOUT_SPARSE, 704),
+                                          (6, 8, O.LAYOUT_SPARSE, 640), (2, 4, O.LAYOUT_DENSE2, 352)])
+def test_fwd_gemm_partial_stage(N, M, layout, K):
+    # K steps that do not fill the last 128-byte stage of the large-tile GEMM
+    _fwd_case(520, K, 300, N, M, layout, seed=K)
+
+
 def test_fwd_edge_tokens():
     g = rng(9)
     T, K = 70, 256
