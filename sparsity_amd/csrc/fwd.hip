@@ -242,8 +242,10 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(
 // each wave waits on its own vmcnt (every stage issues exactly LPS loads per wave) and meets the
 // others at a bare s_barrier (no fence: a fence would also drain the loads meant to stay in
 // flight).  B rows are
-// XOR-swizzled in 16-byte chunks (chunk c of token t sits at position c ^ (t % 8)) so fragment
-// reads spread over the LDS banks.
+// XOR-swizzled in 16-byte chunks: chunk c of token t sits at position c ^ ((t / 2) % 8).  Two
+// 128-byte rows fill the 64 four-byte banks once, so the 16 lanes served together (16 consecutive
+// tokens, one chunk each) then hit 16 distinct 16-byte bank groups; swizzling by t % 8 instead
+// pairs rows t and t+8 on the same banks (measured 1.7x slower reads).
 //
 // Rows past the last panel, tokens past T and K past the end (a partial last stage) read clamped,
 // valid addresses; their codes are zeroed or their results never stored.
@@ -251,18 +253,19 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(
 // Blocks are mapped XCD-major: the hardware deals consecutive block ids round-robin to the 8
 // XCDs, so block b takes tile (b % 8) * (tiles / 8) + b / 8 and each XCD walks a contiguous run
 // of tiles that share a token tile, which then stays in that XCD's L2.
-constexpr int kBigStage = 256 * 128 + 8 * 1024;   // B + A bytes of one stage (both layouts)
-__shared__ __attribute__((aligned(16))) int8_t g_stage0[kBigStage];
-__shared__ __attribute__((aligned(16))) int8_t g_stage1[kBigStage];
-__shared__ __attribute__((aligned(16))) int8_t g_stage2[kBigStage];
-
-template <int B>
-__device__ __forceinline__ int8_t* stage_buf() {
-  return B == 0 ? g_stage0 : (B == 1 ? g_stage1 : g_stage2);
-}
+#ifndef BL_BIG_WAVES
+#define BL_BIG_WAVES 4
+#endif
+constexpr int kBigWaves = BL_BIG_WAVES;   // waves per block: 2 (rows) x kBigWaves/2 (tokens)
 
 __device__ __forceinline__ void block_barrier_nofence() {
   asm volatile("s_barrier" ::: "memory");
+}
+
+// s_waitcnt immediate for gfx9: vmcnt in bits 3:0 and 15:14, expcnt 6:4 (7 = no wait), lgkmcnt
+// 11:8 (15 = no wait).
+constexpr int waitcnt_imm(int vm, int lgkm = 15) {
+  return (vm & 0xF) | (((vm >> 4) & 3) << 14) | (7 << 4) | ((lgkm & 0xF) << 8);
 }
 
 typedef __attribute__((address_space(3))) int8_t lds_i8;
@@ -278,110 +281,155 @@ __device__ __forceinline__ void lds_dma16(const void* src, uint32_t m0) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
                :: "s"(m0), "v"(src) : "memory", "m0");
 }
+// Same, scalar base + per-lane 32-bit byte offset (no VALU address arithmetic per load).
+__device__ __forceinline__ void lds_dma16_s(const void* sbase, uint32_t voff, uint32_t m0) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :: "s"(m0), "v"(voff), "s"(sbase) : "memory", "m0");
+}
 
-template <int LAYOUT>
+template <int LAYOUT, int NWAVE_>
 struct BigGemm {
   static constexpr bool SP = LAYOUT == kLayoutSparse;
   static constexpr int KSTEP = SP ? 64 : 32;
   static constexpr int KS = SP ? 2 : 4;              // MFMA K-steps per stage: 128 K bytes
-  static constexpr int NWAVE = 8;
-  static constexpr int WM = 4, WN = 2;
-  static constexpr int BM = 256, BN = 256;
+  static constexpr int NWAVE = NWAVE_;               // waves as 2 (rows) x NWAVE/2 (tokens)
+  static constexpr int WM = 4, WN = 2;                // 128 rows x 64 tokens per wave
+  static constexpr int BM = 256, BN = 32 * WN * (NWAVE / 2);
   static constexpr int SK = KS * KSTEP;              // 128 bytes of K per token per stage
-  static constexpr int B_BYTES = BN * SK;            // 32 KB
+  static constexpr int B_BYTES = BN * SK;
   static constexpr int A_PANEL = KS * 256 * (SP ? 2 : 1);
   static constexpr int A_BYTES = 8 * A_PANEL;        // 8 KB
   static constexpr int B_LOADS = B_BYTES / 1024 / NWAVE;
   static constexpr int A_LOADS = A_BYTES / 1024 / NWAVE;
-  static constexpr int LPS = B_LOADS + A_LOADS;
-  static_assert(SK == 128 && B_BYTES + A_BYTES == kBigStage, "stage layout");
+  static constexpr int LPS = B_LOADS + (SP ? 2 : 1) * A_LOADS;   // loads per wave per stage
+  static constexpr int STAGE = B_BYTES + A_BYTES;
+  static_assert(SK == 128, "stage layout");
   static_assert(A_LOADS >= 1 && A_BYTES % (1024 * NWAVE) == 0, "A stage splits evenly over waves");
 
+  int8_t* ring;                                      // 3 stage buffers in LDS
   const int8_t* __restrict__ xq;
   const uint32_t* __restrict__ codes;
   const uint32_t* __restrict__ meta;
-  int Keff, NF, NS, lane, wave, wm, wn, h, b_chunk;
-  uint32_t b_src[B_LOADS];
-  uint32_t a_src[A_LOADS];
-  bool a_meta[A_LOADS];
-  int a_frag0[A_LOADS];
+  int Keff, NF, NS, lane, wave, wm, wn, h;
+  uint32_t m0_b, m0_a;                  // this wave's LDS destinations inside a stage buffer
+  uint32_t b_off[B_LOADS], b_off_tail[B_LOADS];   // per-lane byte offsets from xq + st * SK
+  uint32_t a_off[A_LOADS], a_off_tail[A_LOADS];   // per-lane byte offsets from codes/meta + st * KS * 256
   v16i acc[WM][WN];
 
   // Loads of stage st (clamped to the last real stage: the padded stages of the unrolled loop
-  // reload valid data that their zeroed codes never use).
+  // reload valid data that their zeroed codes never use).  The stage advance lives in the scalar
+  // base; the one partial stage (K_eff not a multiple of the stage) uses offsets clamped inside
+  // each row.  A loads come in a code half (lanes 0-31) and a meta half (lanes 32-63).
   template <int BUF>
   __device__ __forceinline__ void issue(int st_in) {
-    int8_t* base = stage_buf<BUF>();
     const int st = min(st_in, NS - 1);
-    const int kk = min(st * SK + b_chunk, Keff - 16);   // chunks past K_eff reread the last one
-    const uint32_t wbase = __builtin_amdgcn_readfirstlane(lds_offset(base) + (uint32_t)wave * (B_LOADS * 1024));
+    const bool partial = (st + 1) * KS > NF;
+    const uint32_t m0b = m0_b + BUF * STAGE, m0a = m0_a + BUF * STAGE;
+    const int8_t* sb = xq + (size_t)st * SK;
+    const uint8_t* sc = (const uint8_t*)codes + (size_t)st * (KS * 256);
+    const uint8_t* sm = (const uint8_t*)meta + (size_t)st * (KS * 256);
+    if (!partial) {   // uniform branch: the offsets stay in VGPRs, no per-lane selects
 #pragma unroll
-    for (int i = 0; i < B_LOADS; ++i) lds_dma16(xq + b_src[i] + kk, wbase + i * 1024);
-    const uint32_t abase = __builtin_amdgcn_readfirstlane(lds_offset(base) + B_BYTES + (uint32_t)wave * (A_LOADS * 1024));
+      for (int i = 0; i < B_LOADS; ++i) lds_dma16_s(sb, b_off[i], m0b + i * 1024);
 #pragma unroll
-    for (int q = 0; q < A_LOADS; ++q) {
-      const int s = min(st * KS + a_frag0[q], NF - 1);
-      const uint32_t* src = (a_meta[q] ? meta : codes) + a_src[q] + (uint32_t)s * 64;
-      lds_dma16(src, abase + q * 1024);
+      for (int q = 0; q < A_LOADS; ++q) {
+        if (!SP || lane < 32) lds_dma16_s(sc, a_off[q], m0a + q * 1024);
+        if (SP && lane >= 32) lds_dma16_s(sm, a_off[q], m0a + q * 1024);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < B_LOADS; ++i) lds_dma16_s(sb, b_off_tail[i], m0b + i * 1024);
+#pragma unroll
+      for (int q = 0; q < A_LOADS; ++q) {
+        if (!SP || lane < 32) lds_dma16_s(sc, a_off_tail[q], m0a + q * 1024);
+        if (SP && lane >= 32) lds_dma16_s(sm, a_off_tail[q], m0a + q * 1024);
+      }
     }
   }
 
-  // One stage: wait for its loads (at most the next stage's LPS loads stay outstanding), barrier,
-  // refill the buffer freed by the previous stage, multiply.  Straight-line code on purpose: a
-  // branch between the refill and the reads makes the compiler drain every load before the reads.
-  template <int BUF>
-  __device__ __forceinline__ void stage(int st) {
-    __builtin_amdgcn_s_waitcnt(0x3F70 | LPS);
-    block_barrier_nofence();
-    issue<(BUF + 2) % 3>(st + 2);
-    const int8_t* bb = stage_buf<BUF>();
+  // Operands of one MFMA K-step, read from LDS one step ahead of their use.
+  struct StepRegs {
+    uint32_t code[WM];
+    uint32_t meta[WM];
+    v8i b[WN];
+  };
+
+  __device__ __forceinline__ void read_step(const int8_t* bb, int j, StepRegs& r) const {
     const int8_t* ab = bb + B_BYTES;
 #pragma unroll
-    for (int j = 0; j < KS; ++j) {
-      const bool live_step = st * KS + j < NF;
-      v4i a[WM];
-      uint32_t mm[WM];
+    for (int p = 0; p < WM; ++p) {
+      const int8_t* pa = ab + (wm * WM + p) * A_PANEL + j * 256 + 4 * lane;
+      r.code[p] = *(const uint32_t*)pa;
+      r.meta[p] = SP ? *(const uint32_t*)(pa + KS * 256) : 0u;
+    }
+#pragma unroll
+    for (int g = 0; g < WN; ++g) {
+      const int tt = (wn * WN + g) * 32 + (lane & 31);
+      const int8_t* rowp = bb + tt * SK;
+      const int c1 = (j * KSTEP) / 16 + h;
+      const int sw = (tt >> 1) & 7;
+      const int4 blo = *(const int4*)(rowp + 16 * (c1 ^ sw));
+      r.b[g][0] = blo.x; r.b[g][1] = blo.y; r.b[g][2] = blo.z; r.b[g][3] = blo.w;
+      if constexpr (SP) {
+        const int4 bhi = *(const int4*)(rowp + 16 * ((c1 + 2) ^ sw));
+        r.b[g][4] = bhi.x; r.b[g][5] = bhi.y; r.b[g][6] = bhi.z; r.b[g][7] = bhi.w;
+      }
+    }
+  }
+
+  __device__ __forceinline__ void mma_step(const StepRegs& r, bool live) {
+    v4i a[WM];
+#pragma unroll
+    for (int p = 0; p < WM; ++p) a[p] = expand_codes(live ? r.code[p] : 0u);
+#pragma unroll
+    for (int g = 0; g < WN; ++g)
 #pragma unroll
       for (int p = 0; p < WM; ++p) {
-        const int8_t* pa = ab + (wm * WM + p) * A_PANEL + j * 256 + 4 * lane;
-        const uint32_t code = *(const uint32_t*)pa;
-        a[p] = expand_codes(live_step ? code : 0u);
-        mm[p] = SP ? *(const uint32_t*)(pa + KS * 256) : 0u;
-      }
-#pragma unroll
-      for (int g = 0; g < WN; ++g) {
-        const int tt = (wn * WN + g) * 32 + (lane & 31);
-        const int8_t* rowp = bb + tt * SK;
-        const int c1 = (j * KSTEP) / 16 + h;
-        const int4 blo = *(const int4*)(rowp + 16 * (c1 ^ (tt & 7)));
         if constexpr (SP) {
-          const int4 bhi = *(const int4*)(rowp + 16 * ((c1 + 2) ^ (tt & 7)));
-          v8i bv;
-          bv[0] = blo.x; bv[1] = blo.y; bv[2] = blo.z; bv[3] = blo.w;
-          bv[4] = bhi.x; bv[5] = bhi.y; bv[6] = bhi.z; bv[7] = bhi.w;
-#pragma unroll
-          for (int p = 0; p < WM; ++p)
-            acc[p][g] = __builtin_amdgcn_smfmac_i32_32x32x64_i8(a[p], bv, acc[p][g], (int)mm[p], 0, 0);
+          acc[p][g] = __builtin_amdgcn_smfmac_i32_32x32x64_i8(a[p], r.b[g], acc[p][g], (int)r.meta[p], 0, 0);
         } else {
-          v4i bv;
-          bv[0] = blo.x; bv[1] = blo.y; bv[2] = blo.z; bv[3] = blo.w;
-#pragma unroll
-          for (int p = 0; p < WM; ++p)
-            acc[p][g] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[p], bv, acc[p][g], 0, 0, 0);
+          v4i bd;
+          bd[0] = r.b[g][0]; bd[1] = r.b[g][1]; bd[2] = r.b[g][2]; bd[3] = r.b[g][3];
+          acc[p][g] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[p], bd, acc[p][g], 0, 0, 0);
         }
       }
+  }
+
+  // One stage (buffer BUF) as KS pipelined steps: while step j's MFMAs run, step j+1's operands
+  // are read from LDS into the other register set.  At the last step the next stage's buffer is
+  // needed, so the wave first waits for its own loads of that stage (at most the LPS loads of the
+  // stage after it stay outstanding) and for its outstanding LDS reads, meets the other waves at a
+  // bare s_barrier (after which no wave reads this stage's buffer again), refills this buffer with
+  // stage st+3 and reads the next stage's first step.  ALL_LIVE: every step of the stage is real.
+  template <int BUF, bool ALL_LIVE>
+  __device__ __forceinline__ void stage(int st, StepRegs& R0, StepRegs& R1) {
+#pragma unroll
+    for (int j = 0; j < KS; ++j) {
+      StepRegs& cur = (j % 2 == 0) ? R0 : R1;
+      StepRegs& nxt = (j % 2 == 0) ? R1 : R0;
+      if (j + 1 < KS) {
+        read_step(ring + BUF * STAGE, j + 1, nxt);
+      } else {
+        __builtin_amdgcn_s_waitcnt(waitcnt_imm(LPS, 0));
+        block_barrier_nofence();
+        issue<BUF>(st + 3);
+        read_step(ring + ((BUF + 1) % 3) * STAGE, 0, nxt);
+      }
+      mma_step(cur, ALL_LIVE || st * KS + j < NF);
     }
   }
 };
 
-template <int LAYOUT>
-__global__ __launch_bounds__(512, 1) void gemm_big_kernel(
+template <int LAYOUT, int NWAVE>
+__global__ __launch_bounds__(64 * NWAVE, NWAVE == 4 ? 2 : 1) void gemm_big_kernel(
     const int8_t* __restrict__ xq, const float* __restrict__ xs, int T, int Keff,
     const uint32_t* __restrict__ codes, const uint32_t* __restrict__ meta,
     const float* __restrict__ gamma_p, int n, int npanels, float* __restrict__ y,
     int32_t* __restrict__ acc_out, int tiles_m, int tiles) {
-  using G = BigGemm<LAYOUT>;
+  using G = BigGemm<LAYOUT, NWAVE>;
+  __shared__ __attribute__((aligned(16))) int8_t ring[3 * G::STAGE];
   G k;
+  k.ring = ring;
   k.xq = xq; k.codes = codes; k.meta = meta; k.Keff = Keff;
   k.lane = threadIdx.x & 63;
   k.wave = threadIdx.x >> 6;
@@ -396,41 +444,64 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(
   k.NF = Keff / G::KSTEP;
   k.NS = (k.NF + G::KS - 1) / G::KS;
 
-  // B: load i of a wave fills LDS bytes [(wave*B_LOADS + i) * 1024, +1024) = 8 token rows; lane l
-  // covers row position l % 8 of token row l / 8 and fetches global chunk (l % 8) ^ (row % 8)
-  k.b_chunk = 16 * ((k.lane & 7) ^ ((k.lane >> 3) & 7));
+  // B: load i of a wave fills LDS bytes [(wave*B_LOADS + i) * 1024, +1024) of a stage = 8 token
+  // rows of SK bytes; lane l covers position l % 8 of token row tt and fetches global chunk
+  // (l % 8) ^ ((tt / 2) % 8).  In the partial last stage chunks past K_eff reread the last chunk.
+  const int last = k.NS - 1;
 #pragma unroll
   for (int i = 0; i < G::B_LOADS; ++i) {
     const int tt = (k.wave * G::B_LOADS + i) * 8 + (k.lane >> 3);
-    k.b_src[i] = (uint32_t)(min(tok0 + tt, T - 1) * Keff);
+    const int chunk = 16 * ((k.lane & 7) ^ ((tt >> 1) & 7));
+    const uint32_t row = (uint32_t)(min(tok0 + tt, T - 1) * Keff);
+    k.b_off[i] = row + chunk;
+    k.b_off_tail[i] = row + (uint32_t)(min(last * G::SK + chunk, Keff - 16) - last * G::SK);
   }
   // A: load q of a wave fills LDS bytes [(wave*A_LOADS + q) * 1024, +1024) of the A stage, laid
-  // out [panel][codes: KS fragments][meta: KS fragments], 256 bytes per fragment
+  // out [panel][codes: KS fragments][meta: KS fragments], 256 bytes per fragment; lane l < 32
+  // fetches 16 code bytes, lane l >= 32 the matching 16 meta bytes (SPARSE).  In the partial
+  // last stage fragments past the last K step reread the last one.
 #pragma unroll
   for (int q = 0; q < G::A_LOADS; ++q) {
     const int byte0 = (k.wave * G::A_LOADS + q) * 1024 + k.lane * 16;
     const int pw = byte0 / G::A_PANEL;
-    const int inpanel = byte0 % G::A_PANEL;
-    k.a_meta[q] = G::SP && inpanel >= G::KS * 256;
-    const int inrun = inpanel % (G::KS * 256);
-    k.a_frag0[q] = inrun / 256;
+    const int inrun = (byte0 % G::A_PANEL) % (G::KS * 256);   // byte inside the codes/meta run
+    const int frag = inrun / 256;
     const int panel = min(row0 / kPanel + pw, npanels - 1);
-    k.a_src[q] = (uint32_t)(panel * k.NF * 64 + (inrun % 256) / 4);
+    const uint32_t pbase = (uint32_t)panel * k.NF * 256u + (uint32_t)(inrun % 256);
+    k.a_off[q] = pbase + frag * 256;
+    k.a_off_tail[q] = pbase + (uint32_t)(min(last * G::KS + frag, k.NF - 1) - last * G::KS) * 256u;
   }
+  k.m0_b = __builtin_amdgcn_readfirstlane(lds_offset(ring) + (uint32_t)k.wave * (G::B_LOADS * 1024));
+  k.m0_a = __builtin_amdgcn_readfirstlane(lds_offset(ring) + G::B_BYTES + (uint32_t)k.wave * (G::A_LOADS * 1024));
 #pragma unroll
   for (int p = 0; p < G::WM; ++p)
 #pragma unroll
     for (int g = 0; g < G::WN; ++g) k.acc[p][g] = v16i{};
 
-  // stage count padded to a multiple of 3; padded stages have every code zeroed
+  // Groups of three stages (one per ring buffer).  Groups made only of full stages skip the
+  // per-step liveness select; the last group, which may hold the partial stage and padding up to
+  // a multiple of 3, keeps it (padded steps have their codes zeroed).  Every stage issues its
+  // refill (clamped to real data), so each wave always has exactly LPS loads per stage in flight.
+  const int full_stages = k.NF / G::KS;
+  const int main_end = full_stages / 3 * 3;
+  typename G::StepRegs R0, R1;
   k.template issue<0>(0);
   k.template issue<1>(1);
-  for (int st = 0; st < k.NS; st += 3) {
-    k.template stage<0>(st);
-    k.template stage<1>(st + 1);
-    k.template stage<2>(st + 2);
+  k.template issue<2>(2);
+  __builtin_amdgcn_s_waitcnt(waitcnt_imm(2 * G::LPS));   // stage 0 landed (this wave's part)
+  block_barrier_nofence();
+  k.read_step(ring, 0, R0);
+  for (int st = 0; st < main_end; st += 3) {
+    k.template stage<0, true>(st, R0, R1);
+    k.template stage<1, true>(st + 1, R0, R1);
+    k.template stage<2, true>(st + 2, R0, R1);
   }
-  __builtin_amdgcn_s_waitcnt(0x3F70);   // no load may still be writing LDS when the block ends
+  if (main_end < k.NS) {
+    k.template stage<0, false>(main_end, R0, R1);
+    k.template stage<1, false>(main_end + 1, R0, R1);
+    k.template stage<2, false>(main_end + 2, R0, R1);
+  }
+  __builtin_amdgcn_s_waitcnt(waitcnt_imm(0));   // no load may still be writing LDS when the block ends
 
   const float gamma = *gamma_p;
   const int lane = k.lane, h = k.h;
@@ -501,9 +572,10 @@ static hipError_t launch_fwd_layout(const int8_t* xq, const float* xs, int64_t T
       gemv_kernel<LAYOUT, 16, 8><<<npanels, 1024, 0, s>>>(xq, xs, (int)T, (int)Keff, codes, meta,
                                                           gamma, (int)n, y, acc);
   } else if (T > 128) {
-    const int tiles_m = (int)((n + 255) / 256);
-    const int tiles = tiles_m * (int)((T + 255) / 256);
-    gemm_big_kernel<LAYOUT><<<tiles, 512, 0, s>>>(xq, xs, (int)T, (int)Keff, codes, meta, gamma,
+    using G = BigGemm<LAYOUT, kBigWaves>;
+    const int tiles_m = (int)((n + G::BM - 1) / G::BM);
+    const int tiles = tiles_m * (int)((T + G::BN - 1) / G::BN);
+    gemm_big_kernel<LAYOUT, kBigWaves><<<tiles, 64 * kBigWaves, 0, s>>>(xq, xs, (int)T, (int)Keff, codes, meta, gamma,
                                                      (int)n, npanels, y, acc, tiles_m, tiles);
   } else {
     constexpr int WM = 2, WN = 2, WAM = 2, WAN = 2;
