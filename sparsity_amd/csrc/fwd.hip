@@ -51,10 +51,13 @@ __device__ __forceinline__ void store_out(float* __restrict__ y, int32_t* __rest
 // ---------------------------------------------------------------------------------------------
 // decode GEMV
 // ---------------------------------------------------------------------------------------------
-// One block per 32-row panel; wave w owns the K steps [w*per, (w+1)*per).  Every wave issues all of
-// its weight and activation loads before its first MFMA, so the whole panel is in flight at once
-// (a decode matrix is only a few MB: the kernel is bound by latency, not by bandwidth).  Partial
-// accumulators of the live tokens are summed across waves through LDS in wave order.
+// One block per 32-row panel; wave w owns the K steps [w*per, (w+1)*per).  A decode matrix is only
+// a few MB, so the kernel is bound by latency: each wave first issues its weight loads (at most
+// MAXU code + MAXU meta dwords, well under the per-wave limit of outstanding vector loads), then
+// the block stages the int8 activations xq[T][K_eff] in LDS with wide coalesced loads (row stride
+// K_eff + 16 keeps the fragment reads of different tokens on different banks), and the MFMAs read
+// their B fragments from LDS.  Partial accumulators of the live tokens are summed across waves
+// through LDS in wave order.
 template <int LAYOUT, int NW, int MAXU>
 __global__ __launch_bounds__(64 * NW) void gemv_kernel(const int8_t* __restrict__ xq,
                                                        const float* __restrict__ xs, int T,
@@ -65,45 +68,72 @@ __global__ __launch_bounds__(64 * NW) void gemv_kernel(const int8_t* __restrict_
                                                        int32_t* __restrict__ acc_out) {
   constexpr bool SP = LAYOUT == kLayoutSparse;
   constexpr int KSTEP = SP ? 64 : 32;
+  extern __shared__ __attribute__((aligned(16))) int8_t gsm[];
   const int P = blockIdx.x;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int NF = Keff / KSTEP;
-  const int per = (NF + NW - 1) / NW;
-  const int s_begin = wave * per;
-  const int s_end = min(NF, s_begin + per);
+  const int per = (NF + NW - 1) / NW;            // host guarantees per <= MAXU
+  const int s_begin = min(wave * per, NF - 1);
+  const int cnt = min(per, NF - wave * per);    // may be <= 0 for trailing waves
   const uint32_t* cp = codes + (size_t)P * NF * 64 + lane;
   const uint32_t* mp = SP ? meta + (size_t)P * NF * 64 + lane : nullptr;
-  const int tok = lane & 31, h = lane >> 5;
-  const bool live = tok < T;
-  // lanes of dead tokens read token T-1 (their D columns are never stored): no branches
-  const int8_t* xp = xq + (size_t)min(tok, T - 1) * Keff + 16 * h;
-  v16i acc = {};
-  for (int s0 = s_begin; s0 < s_end; s0 += MAXU) {
-    uint32_t c[MAXU], m[MAXU];
-    int4 blo[MAXU], bhi[MAXU];
+  uint32_t c[MAXU], m[MAXU];
 #pragma unroll
-    for (int u = 0; u < MAXU; ++u) {
-      const int s = min(s0 + u, s_end - 1);     // past the end: reload the last step, code zeroed
-      c[u] = __builtin_nontemporal_load(cp + (size_t)s * 64);
-      m[u] = SP ? __builtin_nontemporal_load(mp + (size_t)s * 64) : kPadMeta;
-      blo[u] = *(const int4*)(xp + (size_t)s * KSTEP);
-      bhi[u] = SP ? *(const int4*)(xp + (size_t)s * KSTEP + 32) : make_int4(0, 0, 0, 0);
-    }
-#pragma unroll
-    for (int u = 0; u < MAXU; ++u) {
-      const uint32_t cu = (s0 + u < s_end) ? c[u] : 0u;
-      acc = mfma_step<SP>(cu, m[u], blo[u], bhi[u], acc);
-    }
+  for (int u = 0; u < MAXU; ++u) {
+    const int s = min(s_begin + u, NF - 1);     // past the end: reload the last step, code zeroed
+    c[u] = cp[(size_t)s * 64];
+    m[u] = SP ? mp[(size_t)s * 64] : kPadMeta;
   }
 
-  // live tokens only: D column = token = lane % 32
-  __shared__ int red[NW][16][64];
-  if (live) {
+  // epilogue operands early: their latency hides behind the weight loads
+  const int tok = lane & 31, h = lane >> 5;
+  const float gamma = *gamma_p;
+  const float sc_l = xs[min(tok, T - 1)];
+
+  // activations -> LDS, rows of K_eff bytes at stride K_eff + 16; all of a thread's loads are in
+  // flight before its first LDS store (a load-store loop would pay one L2 round trip per chunk)
+  const int stride = Keff + 16;
+  const int cpr = Keff / 16;
+  const int chunks = T * cpr;
+  for (int c0 = 0; c0 < chunks; c0 += 64 * NW * 8) {
+    int4 v[8];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) red[wave][r][lane] = acc[r];
+    for (int k = 0; k < 8; ++k) {
+      const int ci = min(c0 + k * 64 * NW + (int)threadIdx.x, chunks - 1);
+      v[k] = *(const int4*)(xq + (size_t)(ci / cpr) * Keff + 16 * (ci % cpr));
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int ci = c0 + k * 64 * NW + (int)threadIdx.x;
+      if (ci < chunks) *(int4*)&gsm[(ci / cpr) * stride + 16 * (ci % cpr)] = v[k];
+    }
   }
   __syncthreads();
-  const float gamma = *gamma_p;
+
+  // two accumulators halve the dependent MFMA chain
+  const int8_t* xr = gsm + min(tok, T - 1) * stride + 16 * h;   // dead token lanes read row T-1
+  v16i acc0 = {}, acc1 = {};
+#pragma unroll
+  for (int u = 0; u < MAXU; ++u) {
+    const int s = min(s_begin + u, NF - 1);
+    const int4 blo = *(const int4*)(xr + s * KSTEP);
+    const int4 bhi = SP ? *(const int4*)(xr + s * KSTEP + 32) : make_int4(0, 0, 0, 0);
+    if (u & 1) acc1 = mfma_step<SP>(u < cnt ? c[u] : 0u, m[u], blo, bhi, acc1);
+    else acc0 = mfma_step<SP>(u < cnt ? c[u] : 0u, m[u], blo, bhi, acc0);
+  }
+  v16i acc;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) acc[r] = acc0[r] + acc1[r];
+
+  // live tokens only: D column = token = lane % 32
+  int* red = (int*)(gsm + ((T * stride + 15) & ~15));
+  const bool live = tok < T;
+  if (live) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) red[(wave * 16 + r) * 64 + lane] = acc[r];
+  }
+  __syncthreads();
+  // thread i sums output (register r, lane l) with l = i % 64: its own token's scale is sc_l
   for (int i = threadIdx.x; i < 16 * 64; i += 64 * NW) {
     const int r = i >> 6, l = i & 63;
     const int tk = l & 31;
@@ -111,10 +141,17 @@ __global__ __launch_bounds__(64 * NW) void gemv_kernel(const int8_t* __restrict_
     if (tk < T && o < n) {
       int32_t sum = 0;
 #pragma unroll
-      for (int w = 0; w < NW; ++w) sum += red[w][r][l];
-      store_out(y, acc_out, (size_t)tk * n + o, sum, gamma, xs[tk]);
+      for (int w = 0; w < NW; ++w) sum += red[(w * 16 + r) * 64 + l];
+      store_out(y, acc_out, (size_t)tk * n + o, sum, gamma, sc_l);
     }
   }
+}
+
+template <int NW>
+constexpr size_t gemv_red_bytes() { return (size_t)NW * 16 * 64 * 4; }
+
+inline size_t gemv_smem_bytes(int64_t T, int64_t Keff, int nw) {
+  return ((size_t)T * (Keff + 16) + 15) / 16 * 16 + (size_t)nw * 16 * 64 * 4;
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -564,13 +601,19 @@ static hipError_t launch_fwd_layout(const int8_t* xq, const float* xs, int64_t T
   const int npanels = (int)((n + kPanel - 1) / kPanel);
   constexpr int KSTEP = LAYOUT == kLayoutSparse ? 64 : 32;
   const int64_t nf = Keff / KSTEP;
-  if (T <= 32) {
-    if (nf <= 8 * 4)
-      gemv_kernel<LAYOUT, 8, 4><<<npanels, 512, 0, s>>>(xq, xs, (int)T, (int)Keff, codes, meta,
-                                                        gamma, (int)n, y, acc);
-    else
-      gemv_kernel<LAYOUT, 16, 8><<<npanels, 1024, 0, s>>>(xq, xs, (int)T, (int)Keff, codes, meta,
-                                                          gamma, (int)n, y, acc);
+  if (T <= 32 && nf <= 8 * 16 && gemv_smem_bytes(T, Keff, 8) <= 160 * 1024) {
+    const size_t smem = gemv_smem_bytes(T, Keff, 8);
+    auto run = [&](auto kern) -> hipError_t {
+      hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                         (int)smem);
+      if (e != hipSuccess) return e;
+      kern<<<npanels, 512, smem, s>>>(xq, xs, (int)T, (int)Keff, codes, meta, gamma, (int)n, y, acc);
+      return hipGetLastError();
+    };
+    // steps per wave bounded by MAXU; the smallest MAXU that fits keeps the load count low
+    if (nf <= 8 * 4) return run(gemv_kernel<LAYOUT, 8, 4>);
+    if (nf <= 8 * 8) return run(gemv_kernel<LAYOUT, 8, 8>);
+    return run(gemv_kernel<LAYOUT, 8, 16>);
   } else if (T > 128) {
     using G = BigGemm<LAYOUT, kBigWaves>;
     const int tiles_m = (int)((n + G::BM - 1) / G::BM);
