@@ -50,8 +50,9 @@
  *
  * Conventions for every call:
  *   - All buffers are device memory owned by the caller; the library allocates nothing and keeps
- *     no pointer after a call returns.  Buffers must be 16-byte aligned and non-NULL unless a
- *     parameter says otherwise; with T == 0 the token-sized buffers of act_quant_i8 and
+ *     no pointer after a call returns (a group table keeps the pointers it was built with).
+ *     Buffers must be 16-byte aligned and non-NULL unless a parameter says otherwise (x_scale
+ *     and acc_opt need only 4-byte alignment, so a token slice of a larger buffer qualifies); with T == 0 the token-sized buffers of act_quant_i8 and
  *     bitlinear_fwd are never touched and may be NULL (the call then enqueues nothing).
  *   - `stream` is a hipStream_t (NULL = the null stream).  Calls are enqueued asynchronously on
  *     it and are stream-ordered; no call synchronizes the host.  The library has no global
@@ -111,6 +112,58 @@ int act_quant_i8(const void* x, int x_dtype, int64_t T, int64_t K, int lift_M, i
 int bitlinear_fwd(const int8_t* xq, const float* x_scale, int64_t T, int64_t K,
                   const uint8_t* codes, const uint8_t* meta, const float* gamma, int N, int M,
                   int layout, int64_t n, float* y, int32_t* acc_opt, void* stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * Grouped decode forward: many independent bitlinear_fwd projections in one launch.
+ *
+ * The operation of each projection is exactly bitlinear_fwd's (same definitions, same packed
+ * layout, same results bit for bit).  A decode projection is a few MB of packed weights, so one
+ * launch per projection is bound by launch and memory latency, not by HBM bandwidth; a group
+ * covers projections that do not depend on each other (the Q/K/V or gate/up projections of a
+ * decoder block, the experts of a layer, or a stream of layers whose activations are already
+ * quantized) with one grid that streams all of their weights.
+ *
+ * Each descriptor holds the arguments of one bitlinear_fwd call; all projections of a group share
+ * (N, M, layout).  Per projection: 0 <= T <= 32 (T == 0 projections are skipped and may hold NULL
+ * token buffers), the bitlinear_fwd shape and alignment rules, acc_opt may be NULL.
+ * Projections may share xq / x_scale; their y and acc_opt buffers must not overlap.
+ *
+ * Use: bitlinear_group_table_bytes sizes a device table, bitlinear_group_build validates every
+ * descriptor on the host and writes the table (it synchronizes `stream`: build once, outside any
+ * graph capture), and bitlinear_fwd_group launches the group (asynchronous, stream-ordered,
+ * capturable, no host work beyond argument checks).  The table holds the descriptors' pointers:
+ * their buffers must stay allocated while the table is used, and their contents are read at launch
+ * time, so new activations written into the same xq / x_scale buffers need no rebuild.
+ * N, M and layout passed to bitlinear_fwd_group must be the table's, and work_items the count
+ * bitlinear_group_table_bytes reported; a table of another layout is ignored (nothing is written).
+ */
+typedef struct bl_fwd_desc {
+  const int8_t* xq;      /* [T][K_eff] int8 activations */
+  const float* x_scale;  /* [T] fp32 token scales */
+  int64_t T;             /* tokens, 0..32 */
+  int64_t K;             /* master in-features */
+  const uint8_t* codes;  /* packed codes from bitlinear_pack */
+  const uint8_t* meta;   /* packed meta (SPARSE) or NULL (DENSE2) */
+  const float* gamma;    /* device scalar from bitlinear_pack */
+  int64_t n;             /* out-features */
+  float* y;              /* [T][n] fp32 output */
+  int32_t* acc_opt;      /* [T][n] int32 accumulators, or NULL */
+} bl_fwd_desc;
+
+/* Validates descs[0..count) (host memory) and reports the device table size in bytes and the
+ * number of work items of the group.  Output pointers may be NULL.  Enqueues nothing. */
+int bitlinear_group_table_bytes(const bl_fwd_desc* descs, int64_t count, int N, int M, int layout,
+                                size_t* table_bytes, int64_t* work_items);
+
+/* Validates the group and writes its device table (table: 16-byte aligned device memory of at
+ * least table_bytes, caller-owned).  Copies on `stream` and waits for it: returns when the table
+ * is in place.  BL_ENOSPC if table_bytes is too small. */
+int bitlinear_group_build(const bl_fwd_desc* descs, int64_t count, int N, int M, int layout,
+                          void* table, size_t table_bytes, void* stream);
+
+/* Enqueues the grouped forward of a built table on `stream`.  work_items == 0 enqueues nothing. */
+int bitlinear_fwd_group(const void* table, int64_t work_items, int N, int M, int layout,
+                        void* stream);
 
 /* Static description of a status code. */
 const char* bitlinear_strerror(int status);

@@ -5,7 +5,8 @@ The compute path lives in ``libbitlinear.so`` (hand-written HIP for gfx950, C AB
 names.  PyTorch is used only to own device memory and streams.
 """
 from .bitlinear import (  # noqa: F401
-    BL_DTYPE_BF16, BL_DTYPE_F32, BL_LAYOUT_DENSE2, BL_LAYOUT_SPARSE, BitLinearError, act_quant,
-    act_quant_i8, bitlinear_fwd, bitlinear_pack, bitlinear_packed_bytes, fwd, lib, pack,
+    BL_DTYPE_BF16, BL_DTYPE_F32, BL_LAYOUT_DENSE2, BL_LAYOUT_SPARSE, BitLinearError, BlFwdDesc,
+    FwdGroup, act_quant, act_quant_i8, bitlinear_fwd, bitlinear_fwd_group, bitlinear_group_build,
+    bitlinear_group_table_bytes, bitlinear_pack, bitlinear_packed_bytes, fwd, lib, pack,
     packed_bytes,
 )

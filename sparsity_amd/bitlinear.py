@@ -1,8 +1,10 @@
 """ctypes binding of libbitlinear (argument marshalling only; every step runs in HIP kernels).
 
 Names mirror the C ABI: ``bitlinear_packed_bytes``, ``bitlinear_pack``, ``act_quant_i8``,
-``bitlinear_fwd``.  ``pack`` / ``act_quant`` / ``fwd`` are convenience wrappers that allocate the
-output tensors with torch on the input's device and enqueue on torch's current stream.
+``bitlinear_fwd``, ``bitlinear_group_table_bytes``, ``bitlinear_group_build``,
+``bitlinear_fwd_group``.  ``pack`` / ``act_quant`` / ``fwd`` / ``FwdGroup`` are convenience
+wrappers that allocate the output tensors with torch on the input's device and enqueue on torch's
+current stream.
 """
 from __future__ import annotations
 
@@ -15,6 +17,16 @@ BL_LAYOUT_SPARSE = 0
 BL_LAYOUT_DENSE2 = 1
 BL_DTYPE_F32 = 0
 BL_DTYPE_BF16 = 1
+
+
+
+class BlFwdDesc(ctypes.Structure):
+    """bl_fwd_desc: the arguments of one bitlinear_fwd call inside a group."""
+    _fields_ = [("xq", ctypes.c_void_p), ("x_scale", ctypes.c_void_p), ("T", ctypes.c_int64),
+                ("K", ctypes.c_int64), ("codes", ctypes.c_void_p), ("meta", ctypes.c_void_p),
+                ("gamma", ctypes.c_void_p), ("n", ctypes.c_int64), ("y", ctypes.c_void_p),
+                ("acc_opt", ctypes.c_void_p)]
+
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libbitlinear.so")
@@ -42,11 +54,17 @@ def lib() -> ctypes.CDLL:
         L.bitlinear_pack.argtypes = [vp, i64, i64, i32, i32, i32, vp, vp, vp, vp, sz, vp]
         L.act_quant_i8.argtypes = [vp, i32, i64, i64, i32, vp, vp, vp]
         L.bitlinear_fwd.argtypes = [vp, vp, i64, i64, vp, vp, vp, i32, i32, i32, i64, vp, vp, vp]
+        dp = ctypes.POINTER(BlFwdDesc)
+        L.bitlinear_group_table_bytes.argtypes = [dp, i64, i32, i32, i32, ctypes.POINTER(sz),
+                                                  ctypes.POINTER(i64)]
+        L.bitlinear_group_build.argtypes = [dp, i64, i32, i32, i32, vp, sz, vp]
+        L.bitlinear_fwd_group.argtypes = [vp, i64, i32, i32, i32, vp]
         L.bitlinear_strerror.argtypes = [i32]
         L.bitlinear_strerror.restype = ctypes.c_char_p
         L.bitlinear_layout_version.argtypes = []
         for f in (L.bitlinear_packed_bytes, L.bitlinear_pack, L.act_quant_i8, L.bitlinear_fwd,
-                  L.bitlinear_layout_version):
+                  L.bitlinear_layout_version, L.bitlinear_group_table_bytes,
+                  L.bitlinear_group_build, L.bitlinear_fwd_group):
             f.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -80,6 +98,22 @@ def act_quant_i8(x, x_dtype, T, K, lift_M, xq, x_scale, stream) -> int:
 
 def bitlinear_fwd(xq, x_scale, T, K, codes, meta, gamma, N, M, layout, n, y, acc, stream) -> int:
     return lib().bitlinear_fwd(xq, x_scale, T, K, codes, meta, gamma, N, M, layout, n, y, acc, stream)
+
+
+def bitlinear_group_table_bytes(descs, N, M, layout):
+    """descs: a ctypes array of BlFwdDesc.  Returns (status, table_bytes, work_items)."""
+    tb, wi = ctypes.c_size_t(), ctypes.c_int64()
+    st = lib().bitlinear_group_table_bytes(descs, len(descs), N, M, layout, ctypes.byref(tb),
+                                           ctypes.byref(wi))
+    return st, tb.value, wi.value
+
+
+def bitlinear_group_build(descs, N, M, layout, table, table_bytes, stream) -> int:
+    return lib().bitlinear_group_build(descs, len(descs), N, M, layout, table, table_bytes, stream)
+
+
+def bitlinear_fwd_group(table, work_items, N, M, layout, stream) -> int:
+    return lib().bitlinear_fwd_group(table, work_items, N, M, layout, stream)
 
 
 # ---------------------------------------------------------------------------------------------
@@ -158,3 +192,34 @@ def fwd(xq, scale, K: int, codes, meta, gamma, n: int, N: int = 2, M: int = 4,
                          gamma.data_ptr(), N, M, layout, n, y.data_ptr(), _ptr(acc), _stream()),
            "bitlinear_fwd")
     return (y, acc) if want_acc else y
+
+
+class FwdGroup:
+    """A built group of independent projections: ``FwdGroup(projs)`` then ``group()`` launches.
+
+    ``projs`` is a list of dicts with keys xq, scale, K, codes, meta, gamma, n, y and optionally
+    acc (torch CUDA tensors / ints), all sharing (N, M, layout).  The tensors are referenced, not
+    copied: keep them alive while the group is used; their contents are read at each launch.
+    """
+
+    def __init__(self, projs, N: int = 2, M: int = 4, layout: int = BL_LAYOUT_SPARSE):
+        import torch
+        self.N, self.M, self.layout = N, M, layout
+        self._keep = list(projs)
+        arr = (BlFwdDesc * len(projs))()
+        for i, p in enumerate(projs):
+            arr[i] = BlFwdDesc(_ptr(p["xq"]), _ptr(p["scale"]), p["xq"].shape[0], p["K"],
+                               _ptr(p["codes"]), _ptr(p.get("meta")), _ptr(p["gamma"]), p["n"],
+                               _ptr(p["y"]), _ptr(p.get("acc")))
+        self.descs = arr
+        st, tb, wi = bitlinear_group_table_bytes(arr, N, M, layout)
+        _check(st, "bitlinear_group_table_bytes")
+        dev = projs[0]["codes"].device
+        self.table = torch.empty(max(tb, 16), dtype=torch.uint8, device=dev)
+        self.work_items = wi
+        _check(bitlinear_group_build(arr, N, M, layout, self.table.data_ptr(), self.table.numel(),
+                                     _stream()), "bitlinear_group_build")
+
+    def __call__(self):
+        _check(bitlinear_fwd_group(self.table.data_ptr(), self.work_items, self.N, self.M,
+                                   self.layout, _stream()), "bitlinear_fwd_group")

@@ -2,6 +2,9 @@
 // Every check runs before anything is enqueued, so every error path is testable without a GPU.
 #include <errno.h>
 #include <stdint.h>
+#include <string.h>
+
+#include <vector>
 
 #include "bitlinear.h"
 #include "launch.hpp"
@@ -9,6 +12,7 @@
 namespace {
 
 bool aligned16(const void* p) { return p && ((uintptr_t)p & 15u) == 0; }
+bool aligned4(const void* p) { return p && ((uintptr_t)p & 3u) == 0; }
 
 // Shape rules of the packed layout; returns BL_OK and the packed K axis, or a status.
 int check_shape(int64_t n, int64_t K, int N, int M, int layout, int64_t* keff) {
@@ -30,6 +34,46 @@ int check_shape(int64_t n, int64_t K, int N, int M, int layout, int64_t* keff) {
 }
 
 int status_of(hipError_t e) { return e == hipSuccess ? BL_OK : BL_EIO; }
+
+// Shared checks of one bitlinear_fwd-style projection; returns BL_OK and its packed K axis.
+int check_fwd(const int8_t* xq, const float* x_scale, int64_t T, int64_t K, const uint8_t* codes,
+              const uint8_t* meta, const float* gamma, int N, int M, int layout, int64_t n,
+              const float* y, const int32_t* acc_opt, int64_t* keff) {
+  const int st = check_shape(n, K, N, M, layout, keff);
+  if (st != BL_OK) return st;
+  if (T < 0 || T > INT32_MAX || (uint64_t)T * (uint64_t)n >= (1ull << 40)) return BL_EINVAL;
+  if ((uint64_t)T * (uint64_t)*keff >= (1ull << 31)) return BL_EINVAL;  // 32-bit activation offsets
+  if (T == 0) return BL_OK;  // nothing is read or written; pointers may be NULL
+  if (!aligned16(xq) || !aligned4(x_scale) || !aligned16(codes) || !aligned16(gamma) ||
+      !aligned16(y))
+    return BL_EINVAL;
+  if (layout == BL_LAYOUT_SPARSE ? !aligned16(meta) : meta != nullptr) return BL_EINVAL;
+  if (acc_opt && ((uintptr_t)acc_opt & 3u)) return BL_EINVAL;
+  return BL_OK;
+}
+
+// Validates a group and sizes its device table: header, one record per projection, one uint32
+// per work item.
+int group_size(const bl_fwd_desc* d, int64_t count, int N, int M, int layout, int64_t* items,
+               size_t* bytes) {
+  if (!d || count < 1 || count > (1 << 24)) return BL_EINVAL;
+  int64_t it = 0;
+  for (int64_t i = 0; i < count; ++i) {
+    int64_t ke = 0;
+    const int st = check_fwd(d[i].xq, d[i].x_scale, d[i].T, d[i].K, d[i].codes, d[i].meta,
+                             d[i].gamma, N, M, layout, d[i].n, d[i].y, d[i].acc_opt, &ke);
+    if (st != BL_OK) return st;
+    if (d[i].T > 32) return BL_EINVAL;
+    if (d[i].T == 0) continue;
+    const int64_t panels = (d[i].n + 31) / 32;
+    it += (panels + bl::kGroupWaves - 1) / bl::kGroupWaves;
+    if (it > INT32_MAX) return BL_EINVAL;
+  }
+  *items = it;
+  *bytes = sizeof(bl::GroupHeader) + (size_t)count * sizeof(bl::GroupLayer) + (size_t)it * 4;
+  *bytes = (*bytes + 15) / 16 * 16;
+  return BL_OK;
+}
 
 }  // namespace
 
@@ -80,7 +124,7 @@ int act_quant_i8(const void* x, int x_dtype, int64_t T, int64_t K, int lift_M, i
   if (lift_M != 0 && lift_M != 8) return BL_EINVAL;
   if (T < 0 || T > INT32_MAX || K < 8 || K % 8 != 0 || K > (int64_t)1 << 24) return BL_EINVAL;
   if (T == 0) return BL_OK;  // nothing is read or written; pointers may be NULL
-  if (!aligned16(x) || !aligned16(xq) || !aligned16(x_scale)) return BL_EINVAL;
+  if (!aligned16(x) || !aligned16(xq) || !aligned4(x_scale)) return BL_EINVAL;
   return status_of(bl::launch_act_quant(x, x_dtype == BL_DTYPE_BF16, T, K, lift_M, xq, x_scale,
                                         (hipStream_t)stream));
 }
@@ -89,18 +133,80 @@ int bitlinear_fwd(const int8_t* xq, const float* x_scale, int64_t T, int64_t K,
                   const uint8_t* codes, const uint8_t* meta, const float* gamma, int N, int M,
                   int layout, int64_t n, float* y, int32_t* acc_opt, void* stream) {
   int64_t ke = 0;
-  const int st = check_shape(n, K, N, M, layout, &ke);
-  if (st != BL_OK) return st;
-  if (T < 0 || T > INT32_MAX || (uint64_t)T * (uint64_t)n >= (1ull << 40)) return BL_EINVAL;
-  if ((uint64_t)T * (uint64_t)ke >= (1ull << 31)) return BL_EINVAL;  // 32-bit activation offsets
-  if (T == 0) return BL_OK;  // nothing is read or written; pointers may be NULL
-  if (!aligned16(xq) || !aligned16(x_scale) || !aligned16(codes) || !aligned16(gamma) ||
-      !aligned16(y))
-    return BL_EINVAL;
-  if (layout == BL_LAYOUT_SPARSE ? !aligned16(meta) : meta != nullptr) return BL_EINVAL;
-  if (acc_opt && ((uintptr_t)acc_opt & 3u)) return BL_EINVAL;
+  const int st = check_fwd(xq, x_scale, T, K, codes, meta, gamma, N, M, layout, n, y, acc_opt, &ke);
+  if (st != BL_OK || T == 0) return st;
   return status_of(bl::launch_fwd(xq, x_scale, T, ke, (const uint32_t*)codes, (const uint32_t*)meta,
                                   gamma, layout, n, y, acc_opt, (hipStream_t)stream));
+}
+
+int bitlinear_group_table_bytes(const bl_fwd_desc* descs, int64_t count, int N, int M, int layout,
+                                size_t* table_bytes, int64_t* work_items) {
+  int64_t items = 0;
+  size_t bytes = 0;
+  const int st = group_size(descs, count, N, M, layout, &items, &bytes);
+  if (st != BL_OK) return st;
+  if (table_bytes) *table_bytes = bytes;
+  if (work_items) *work_items = items;
+  return BL_OK;
+}
+
+int bitlinear_group_build(const bl_fwd_desc* descs, int64_t count, int N, int M, int layout,
+                          void* table, size_t table_bytes, void* stream) {
+  int64_t items = 0;
+  size_t bytes = 0;
+  const int st = group_size(descs, count, N, M, layout, &items, &bytes);
+  if (st != BL_OK) return st;
+  if (!aligned16(table)) return BL_EINVAL;
+  if (table_bytes < bytes) return BL_ENOSPC;
+  std::vector<uint8_t> img(bytes, 0);
+  bl::GroupHeader hdr;
+  memset(&hdr, 0, sizeof hdr);
+  hdr.magic = bl::kGroupMagic;
+  hdr.layout = layout;
+  hdr.N = N;
+  hdr.M = M;
+  hdr.count = count;
+  hdr.items = items;
+  memcpy(img.data(), &hdr, sizeof hdr);
+  bl::GroupLayer* rec = (bl::GroupLayer*)(img.data() + sizeof hdr);
+  uint32_t* item_layer = (uint32_t*)(img.data() + sizeof hdr + count * sizeof(bl::GroupLayer));
+  int64_t first = 0;
+  for (int64_t i = 0; i < count; ++i) {
+    const bl_fwd_desc& d = descs[i];
+    const int64_t ke = (layout == BL_LAYOUT_SPARSE && M == 8) ? d.K / 2 * 3 : d.K;
+    const int64_t nit = d.T == 0 ? 0 : ((d.n + 31) / 32 + bl::kGroupWaves - 1) / bl::kGroupWaves;
+    bl::GroupLayer r;
+    memset(&r, 0, sizeof r);
+    r.xq = d.xq;
+    r.xs = d.x_scale;
+    r.codes = (const uint32_t*)d.codes;
+    r.meta = (const uint32_t*)d.meta;
+    r.gamma = d.gamma;
+    r.y = d.y;
+    r.acc = d.acc_opt;
+    r.T = (int32_t)d.T;
+    r.Keff = (int32_t)ke;
+    r.n = (int32_t)d.n;
+    r.first_item = (int32_t)first;
+    memcpy(&rec[i], &r, sizeof r);
+    for (int64_t k = 0; k < nit; ++k) item_layer[first + k] = (uint32_t)i;
+    first += nit;
+  }
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = hipMemcpyAsync(table, img.data(), bytes, hipMemcpyHostToDevice, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);  // img is released on return
+  return status_of(e);
+}
+
+int bitlinear_fwd_group(const void* table, int64_t work_items, int N, int M, int layout,
+                        void* stream) {
+  int64_t ke = 0;
+  const int st = check_shape(1, 128, N, M, layout, &ke);  // N:M and layout only
+  if (st != BL_OK) return st;
+  if (work_items < 0 || work_items > INT32_MAX) return BL_EINVAL;
+  if (work_items == 0) return BL_OK;
+  if (!aligned16(table)) return BL_EINVAL;
+  return status_of(bl::launch_fwd_group(table, work_items, layout, (hipStream_t)stream));
 }
 
 }  // extern "C"

@@ -29,6 +29,25 @@ __device__ __forceinline__ v4i expand_codes(uint32_t c) {
   return r;
 }
 
+// One 32x32 int8 MFMA step of a panel: A = the expanded code dword (16 int8 per lane), B = the
+// token fragment (SPARSE: 32 bytes per lane covering 64 K positions, with `meta` as the sparse
+// instruction's index operand; DENSE2: 16 bytes per lane covering 32 K positions).
+template <bool SP>
+__device__ __forceinline__ v16i mfma_step(uint32_t code, uint32_t meta, const int4& blo,
+                                          const int4& bhi, v16i acc) {
+  const v4i a = expand_codes(code);
+  if constexpr (SP) {
+    v8i b;
+    b[0] = blo.x; b[1] = blo.y; b[2] = blo.z; b[3] = blo.w;
+    b[4] = bhi.x; b[5] = bhi.y; b[6] = bhi.z; b[7] = bhi.w;
+    return __builtin_amdgcn_smfmac_i32_32x32x64_i8(a, b, acc, (int)meta, 0, 0);
+  } else {
+    v4i b;
+    b[0] = blo.x; b[1] = blo.y; b[2] = blo.z; b[3] = blo.w;
+    return __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, acc, 0, 0, 0);
+  }
+}
+
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o, 64));
@@ -39,6 +58,27 @@ __device__ __forceinline__ double wave_sum_f64(double v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
   return v;
+}
+
+// Workgroup barrier without the memory fence __syncthreads adds: the fence makes the compiler drain
+// every outstanding global load (vmcnt(0)), which would empty a prefetch ring at each barrier.
+// The "memory" clobber still keeps the compiler from moving memory accesses across it; callers
+// wait for their own LDS writes (block_sync_lds) or LDS DMA (explicit vmcnt) first.
+__device__ __forceinline__ void block_barrier_nofence() {
+  asm volatile("s_barrier" ::: "memory");
+}
+
+// s_waitcnt immediate for gfx9: vmcnt in bits 3:0 and 15:14, expcnt 6:4 (7 = no wait), lgkmcnt
+// 11:8 (15 = no wait).
+constexpr int waitcnt_imm(int vm, int lgkm = 15) {
+  return (vm & 0xF) | (((vm >> 4) & 3) << 14) | (7 << 4) | ((lgkm & 0xF) << 8);
+}
+
+// Barrier after plain LDS writes: this wave's LDS operations complete, then all waves meet.
+// Outstanding global loads stay in flight.
+__device__ __forceinline__ void block_sync_lds() {
+  __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
+  block_barrier_nofence();
 }
 
 }  // namespace bl

@@ -25,22 +25,6 @@
 
 namespace bl {
 
-template <bool SP>
-__device__ __forceinline__ v16i mfma_step(uint32_t code, uint32_t meta, const int4& blo,
-                                          const int4& bhi, v16i acc) {
-  const v4i a = expand_codes(code);
-  if constexpr (SP) {
-    v8i b;
-    b[0] = blo.x; b[1] = blo.y; b[2] = blo.z; b[3] = blo.w;
-    b[4] = bhi.x; b[5] = bhi.y; b[6] = bhi.z; b[7] = bhi.w;
-    return __builtin_amdgcn_smfmac_i32_32x32x64_i8(a, b, acc, (int)meta, 0, 0);
-  } else {
-    v4i b;
-    b[0] = blo.x; b[1] = blo.y; b[2] = blo.z; b[3] = blo.w;
-    return __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, acc, 0, 0, 0);
-  }
-}
-
 __device__ __forceinline__ void store_out(float* __restrict__ y, int32_t* __restrict__ acc_out,
                                           size_t idx, int32_t a, float gamma, float sc) {
   const float v = ((float)a * gamma) * sc;
@@ -294,16 +278,6 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(
 #define BL_BIG_WAVES 4
 #endif
 constexpr int kBigWaves = BL_BIG_WAVES;   // waves per block: 2 (rows) x kBigWaves/2 (tokens)
-
-__device__ __forceinline__ void block_barrier_nofence() {
-  asm volatile("s_barrier" ::: "memory");
-}
-
-// s_waitcnt immediate for gfx9: vmcnt in bits 3:0 and 15:14, expcnt 6:4 (7 = no wait), lgkmcnt
-// 11:8 (15 = no wait).
-constexpr int waitcnt_imm(int vm, int lgkm = 15) {
-  return (vm & 0xF) | (((vm >> 4) & 3) << 14) | (7 << 4) | ((lgkm & 0xF) << 8);
-}
 
 typedef __attribute__((address_space(3))) int8_t lds_i8;
 __device__ __forceinline__ uint32_t lds_offset(const void* p) { return (uint32_t)(uintptr_t)(lds_i8*)p; }

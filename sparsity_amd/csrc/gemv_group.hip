@@ -1,0 +1,189 @@
+// Grouped decode GEMV: many independent sparse ternary projections (T <= 32 tokens each) in one
+// launch, y = gamma * scale[t] * (xq . W_eff^T) for every projection of the group.
+//
+// A single decode projection is a few MB of packed weights, too little to cover the launch and
+// memory latency of a kernel of its own; a group streams the weights of all its projections
+// through one grid, so the chip sees one long HBM stream.  This is the shape of the independent
+// projections of a decoder (Q/K/V, gate/up) and of a stream of layers whose activations are
+// already quantized.
+//
+// Work item = 8 consecutive 32-row panels of one projection; wave w of the block owns panel w over
+// the whole K axis, so no cross-wave reduction is needed.  K is walked in chunks of kGS MFMA steps:
+//   - the wave's packed weights (one code and one meta dword per lane per step) are loaded straight
+//     into a ring of kGD register chunks, kGD - 1 chunks ahead of the MFMAs;
+//   - the block's token rows for the chunk (T x kGS*KSTEP int8) ride in the same ring, one or two
+//     16-byte loads per thread, and are written to a double-buffered LDS tile one chunk ahead, so
+//     the 8 waves share every activation byte they read from L2;
+//   - the MFMAs read their B fragments from LDS (row stride + 16 bytes keeps 16 tokens' 16-byte
+//     reads on distinct banks).
+// Steps past the end of K re-read the last step with the code forced to 0 (zero weights add 0).
+#include "device_common.hpp"
+#include "launch.hpp"
+
+namespace bl {
+
+namespace {
+constexpr int kGS = 8;  // MFMA steps per chunk
+constexpr int kGD = 3;  // register ring depth in chunks
+
+typedef __attribute__((address_space(1))) const uint32_t g_u32;
+typedef __attribute__((address_space(1))) const v4i g_v4i;
+}  // namespace
+
+// One chunk of the register ring: a wave's code/meta dwords for kGS steps and this thread's share
+// of the block's token rows for the same K range.
+template <int BPT>
+struct GroupChunk {
+  uint32_t c[kGS], m[kGS];
+  v4i b[BPT];
+};
+
+template <int LAYOUT>
+struct GroupGemv {
+  static constexpr bool SP = LAYOUT == kLayoutSparse;
+  static constexpr int KSTEP = SP ? 64 : 32;           // K positions per MFMA step
+  static constexpr int NT = 64 * kGroupWaves;
+  static constexpr int CB = kGS * KSTEP;               // bytes of one token row per chunk
+  static constexpr int ROW = CB + 16;                  // LDS row stride
+  static constexpr int V16 = CB / 16;                  // 16-byte pieces per token row per chunk
+  static constexpr int BPT = (32 * V16 + NT - 1) / NT; // pieces per thread at T = 32
+  typedef GroupChunk<BPT> Chunk;
+
+  int8_t* bs;             // LDS: two buffers of 32 rows x ROW bytes
+  g_u32* cp;              // this lane's code dword of step 0 of the wave's panel
+  g_u32* mp;
+  __attribute__((address_space(1))) const int8_t* xq;
+  int tid, T, Keff, NF, nch, bpieces, brow, h;
+  v16i acc;
+
+  // Every call issues the same number of loads (addresses clamped into the projection), so the
+  // compiler waits for one chunk with a fixed vmcnt instead of draining the ring.  Clamped reads
+  // past the end of K only meet steps whose code is forced to 0.
+  __device__ __forceinline__ void issue(int j, Chunk& r) const {
+#pragma unroll
+    for (int u = 0; u < kGS; ++u) {
+      const int s = min(j * kGS + u, NF - 1);
+      r.c[u] = cp[(size_t)s * 64];
+      r.m[u] = SP ? mp[(size_t)s * 64] : kPadMeta;
+    }
+#pragma unroll
+    for (int k = 0; k < BPT; ++k) {
+      const int pc = tid + k * NT;
+      const int row = min(pc / V16, T - 1), col = min(16 * (pc % V16) + j * CB, Keff - 16);
+      r.b[k] = *(g_v4i*)(xq + (size_t)row * Keff + col);
+    }
+  }
+  __device__ __forceinline__ void put(int j, const Chunk& r) const {
+    int8_t* dst = bs + (j & 1) * (32 * ROW);
+#pragma unroll
+    for (int k = 0; k < BPT; ++k) {
+      const int pc = tid + k * NT;
+      if (pc < bpieces) *(v4i*)&dst[(pc / V16) * ROW + 16 * (pc % V16)] = r.b[k];
+    }
+  }
+  __device__ __forceinline__ void compute(int j, const Chunk& r) {
+    const int8_t* xr = bs + (j & 1) * (32 * ROW) + brow * ROW + 16 * h;
+#pragma unroll
+    for (int u = 0; u < kGS; ++u) {
+      const int4 blo = *(const int4*)(xr + u * KSTEP);
+      const int4 bhi = SP ? *(const int4*)(xr + u * KSTEP + 32) : make_int4(0, 0, 0, 0);
+      acc = mfma_step<SP>(j * kGS + u < NF ? r.c[u] : 0u, r.m[u], blo, bhi, acc);
+    }
+  }
+  // chunk j: MFMAs from LDS buffer j & 1 (skipped past the end), chunk j + 1's rows to the other
+  // buffer, chunk j + kGD's loads into the slot chunk j just freed, then one barrier.
+  __device__ __forceinline__ void step(int j, Chunk& cur, const Chunk& nxt) {
+    if (j < nch) compute(j, cur);
+    put(j + 1, nxt);
+    issue(j + kGD, cur);
+    block_sync_lds();
+  }
+};
+
+template <int LAYOUT>
+__global__ __launch_bounds__(64 * kGroupWaves, 2) void gemv_group_kernel(
+    const uint8_t* __restrict__ table) {
+  typedef GroupGemv<LAYOUT> G;
+  __shared__ __attribute__((aligned(16))) int8_t bs[2 * 32 * G::ROW];
+
+  const GroupHeader* hdr = (const GroupHeader*)table;
+  const int item = blockIdx.x;
+  // uniform across the block: a table of another layout, or a grid larger than the table, does nothing
+  if (hdr->magic != kGroupMagic || hdr->layout != LAYOUT || item >= hdr->items) return;
+  const uint32_t li = ((const uint32_t*)(table + sizeof(GroupHeader) +
+                                         hdr->count * sizeof(GroupLayer)))[item];
+  const GroupLayer L = ((const GroupLayer*)(table + sizeof(GroupHeader)))[li];
+
+  G k;
+  k.tid = threadIdx.x;
+  const int lane = k.tid & 63, wave = k.tid >> 6;
+  k.T = L.T;
+  k.Keff = L.Keff;
+  const int n = L.n;
+  const int npanels = (n + kPanel - 1) / kPanel;
+  const int P = (item - L.first_item) * kGroupWaves + wave;
+  const int Pl = min(P, npanels - 1);        // surplus waves load a real panel, store nothing
+  k.NF = k.Keff / G::KSTEP;
+  k.nch = (k.NF + kGS - 1) / kGS;
+  k.cp = (g_u32*)L.codes + (size_t)Pl * k.NF * 64 + lane;
+  k.mp = G::SP ? (g_u32*)L.meta + (size_t)Pl * k.NF * 64 + lane : nullptr;
+  k.xq = (__attribute__((address_space(1))) const int8_t*)L.xq;
+  k.bs = bs;
+  k.bpieces = k.T * G::V16;
+  const int tok = lane & 31;
+  k.h = lane >> 5;
+  k.brow = min(tok, k.T - 1);                // dead token lanes read a live row
+  const float gamma = *(__attribute__((address_space(1))) const float*)L.gamma;
+  const float sc = *((__attribute__((address_space(1))) const float*)L.xs + k.brow);
+
+  typename G::Chunk r0, r1, r2;
+  k.issue(0, r0);
+  k.issue(1, r1);
+  k.issue(2, r2);
+  k.put(0, r0);
+  block_sync_lds();
+  k.acc = v16i{};
+  // nch rounded up to the ring depth: the trailing chunks skip their MFMAs, not their loads
+  for (int j = 0; j < k.nch; j += kGD) {
+    k.step(j, r0, r1);
+    k.step(j + 1, r1, r2);
+    k.step(j + 2, r2, r0);
+  }
+  const v16i acc = k.acc;
+
+  if (tok >= k.T || P >= npanels) return;
+  const int h = k.h;
+  const bool vec = (n & 3) == 0;
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    const int o = P * kPanel + 8 * g + 4 * h;
+    const size_t idx = (size_t)tok * n + o;
+    float v[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = ((float)acc[4 * g + i] * gamma) * sc;
+    if (vec && o + 3 < n) {
+      *(float4*)(L.y + idx) = make_float4(v[0], v[1], v[2], v[3]);
+      if (L.acc)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) L.acc[idx + i] = acc[4 * g + i];
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (o + i < n) {
+          L.y[idx + i] = v[i];
+          if (L.acc) L.acc[idx + i] = acc[4 * g + i];
+        }
+    }
+  }
+}
+
+hipError_t launch_fwd_group(const void* table, int64_t items, int layout, hipStream_t s) {
+  const dim3 grid((unsigned)items), block(64 * kGroupWaves);
+  if (layout == kLayoutSparse)
+    gemv_group_kernel<kLayoutSparse><<<grid, block, 0, s>>>((const uint8_t*)table);
+  else
+    gemv_group_kernel<kLayoutDense2><<<grid, block, 0, s>>>((const uint8_t*)table);
+  return hipGetLastError();
+}
+
+}  // namespace bl

@@ -22,3 +22,36 @@ hipError_t launch_fwd(const int8_t* xq, const float* x_scale, int64_t T, int64_t
                       int64_t n, float* y, int32_t* acc_opt, hipStream_t s);
 
 }  // namespace bl
+
+namespace bl {
+
+// Device table of a group of independent decode projections (bitlinear_group_build writes it,
+// gemv_group_kernel reads it): a header, one GroupLayer per projection, then one uint32 per work
+// item naming its projection.  A work item is kGroupWaves consecutive 32-row panels of one
+// projection, one panel per wave.
+constexpr int kGroupWaves = 8;
+constexpr uint32_t kGroupMagic = 0x31474c42u;  // "BLG1"
+
+struct GroupHeader {
+  uint32_t magic;
+  int32_t layout, N, M;
+  int64_t count, items;
+  int64_t reserved[4];
+};
+static_assert(sizeof(GroupHeader) == 64, "group table header is 64 bytes");
+
+struct GroupLayer {
+  const int8_t* xq;
+  const float* xs;
+  const uint32_t* codes;
+  const uint32_t* meta;
+  const float* gamma;
+  float* y;
+  int32_t* acc;
+  int32_t T, Keff, n, first_item;
+};
+static_assert(sizeof(GroupLayer) == 72, "group layer record is 72 bytes");
+
+hipError_t launch_fwd_group(const void* table, int64_t items, int layout, hipStream_t s);
+
+}  // namespace bl

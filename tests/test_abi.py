@@ -133,3 +133,41 @@ def test_product_path_never_imports_oracle():
             if f.endswith((".py", ".hip", ".hpp", ".cpp", ".h")):
                 txt = open(os.path.join(dirpath, f)).read()
                 assert not re.search(r"\boracle\b", txt), f
+
+
+def _desc(L, **kw):
+    P = FAKE
+    a = dict(xq=P, x_scale=P, T=4, K=256, codes=P, meta=P, gamma=P, n=100, y=P, acc_opt=None)
+    a.update(kw)
+    return L.BlFwdDesc(**a)
+
+
+def test_group_sizes_and_rejects_before_launch(L):
+    arr = (L.BlFwdDesc * 3)(_desc(L), _desc(L, n=6912, K=2560, T=16), _desc(L, T=0, xq=None))
+    st, tb, wi = L.bitlinear_group_table_bytes(arr, 2, 4, 0)
+    assert st == 0
+    # 8 panels of 32 rows per work item; the T == 0 projection has none
+    assert wi == 1 + 6912 // 32 // 8 + 0
+    assert tb >= 64 + 3 * 72 + 4 * wi and tb % 16 == 0
+
+    def one(**kw):
+        return L.bitlinear_group_table_bytes((L.BlFwdDesc * 1)(_desc(L, **kw)), 2, 4, 0)[0]
+    assert one(T=33) == -22                       # a group is decode-sized: T <= 32
+    assert one(T=-1) == -22
+    assert one(K=100) == -22
+    assert one(xq=FAKE + 4) == -22
+    assert one(meta=None) == -22
+    assert one(acc_opt=FAKE + 2) == -22
+    assert L.bitlinear_group_table_bytes((L.BlFwdDesc * 1)(_desc(L)), 3, 4, 0)[0] == -95
+    assert L.bitlinear_group_table_bytes((L.BlFwdDesc * 1)(_desc(L, meta=None)), 2, 4, 1)[0] == 0
+    lib = L.lib()
+    assert lib.bitlinear_group_table_bytes(None, 1, 2, 4, 0, None, None) == -22
+    assert lib.bitlinear_group_table_bytes(arr, 0, 2, 4, 0, None, None) == -22
+    # build: table too small or misaligned is rejected before anything is copied
+    assert L.bitlinear_group_build(arr, 2, 4, 0, FAKE, tb - 16, None) == -28
+    assert L.bitlinear_group_build(arr, 2, 4, 0, FAKE + 8, tb, None) == -22
+    # launch: argument checks only
+    assert L.bitlinear_fwd_group(FAKE, -1, 2, 4, 0, None) == -22
+    assert L.bitlinear_fwd_group(FAKE + 4, 3, 2, 4, 0, None) == -22
+    assert L.bitlinear_fwd_group(FAKE, 3, 2, 4, 9, None) == -95
+    assert L.bitlinear_fwd_group(None, 0, 2, 4, 0, None) == 0   # nothing to launch
