@@ -4,6 +4,7 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <algorithm>
 #include <vector>
 
 #include "bitlinear.h"
@@ -52,12 +53,18 @@ int check_fwd(const int8_t* xq, const float* x_scale, int64_t T, int64_t K, cons
   return BL_OK;
 }
 
-// Validates a group and sizes its device table: header, one record per projection, one uint32
-// per work item.
-int group_size(const bl_fwd_desc* d, int64_t count, int N, int M, int layout, int64_t* items,
-               size_t* bytes) {
+// Work-item plan of a group.  Items are runs of kGroupWaves panels of one projection; the hardware
+// hands workgroup b to XCD b % kXcds, so the plan cuts the projections' items (in projection order)
+// into kXcds contiguous runs of about equal weight bytes -- each projection's activation rows then
+// land in one or two XCDs' L2 -- and orders each XCD's run largest item first, so the launch ends
+// on short items.  Launch position b = p * kXcds + x holds item p of XCD x (padded with empty
+// items).
+int plan_group(const bl_fwd_desc* d, int64_t count, int N, int M, int layout,
+               std::vector<bl::GroupItem>* plan) {
   if (!d || count < 1 || count > (1 << 24)) return BL_EINVAL;
-  int64_t it = 0;
+  struct It { uint32_t layer, panel0; uint64_t cost; };
+  std::vector<It> items;
+  uint64_t total = 0;
   for (int64_t i = 0; i < count; ++i) {
     int64_t ke = 0;
     const int st = check_fwd(d[i].xq, d[i].x_scale, d[i].T, d[i].K, d[i].codes, d[i].meta,
@@ -66,13 +73,38 @@ int group_size(const bl_fwd_desc* d, int64_t count, int N, int M, int layout, in
     if (d[i].T > 32) return BL_EINVAL;
     if (d[i].T == 0) continue;
     const int64_t panels = (d[i].n + 31) / 32;
-    it += (panels + bl::kGroupWaves - 1) / bl::kGroupWaves;
-    if (it > INT32_MAX) return BL_EINVAL;
+    for (int64_t p0 = 0; p0 < panels; p0 += bl::kGroupWaves) {
+      const uint64_t np = (uint64_t)std::min<int64_t>(bl::kGroupWaves, panels - p0);
+      items.push_back({(uint32_t)i, (uint32_t)p0, np * (uint64_t)ke});
+      total += np * (uint64_t)ke;
+      if (items.size() > (size_t)INT32_MAX / (2 * bl::kXcds)) return BL_EINVAL;
+    }
   }
-  *items = it;
-  *bytes = sizeof(bl::GroupHeader) + (size_t)count * sizeof(bl::GroupLayer) + (size_t)it * 4;
-  *bytes = (*bytes + 15) / 16 * 16;
+  std::vector<std::vector<It>> per(bl::kXcds);
+  uint64_t run = 0;
+  for (const It& it : items) {
+    // XCD of the item's midpoint in the cumulative weight stream
+    const uint64_t mid = run + it.cost / 2;
+    const int x = (int)std::min<uint64_t>(bl::kXcds - 1, mid * bl::kXcds / std::max<uint64_t>(total, 1));
+    per[x].push_back(it);
+    run += it.cost;
+  }
+  size_t depth = 0;
+  for (auto& v : per) {
+    std::stable_sort(v.begin(), v.end(), [](const It& a, const It& b) { return a.cost > b.cost; });
+    depth = std::max(depth, v.size());
+  }
+  plan->assign(depth * bl::kXcds, bl::GroupItem{bl::kGroupNoItem, 0});
+  for (int x = 0; x < bl::kXcds; ++x)
+    for (size_t p = 0; p < per[x].size(); ++p)
+      (*plan)[p * bl::kXcds + x] = bl::GroupItem{per[x][p].layer, per[x][p].panel0};
   return BL_OK;
+}
+
+size_t group_table_bytes(int64_t count, size_t items) {
+  const size_t b = sizeof(bl::GroupHeader) + (size_t)count * sizeof(bl::GroupLayer) +
+                   items * sizeof(bl::GroupItem);
+  return (b + 15) / 16 * 16;
 }
 
 }  // namespace
@@ -141,21 +173,20 @@ int bitlinear_fwd(const int8_t* xq, const float* x_scale, int64_t T, int64_t K,
 
 int bitlinear_group_table_bytes(const bl_fwd_desc* descs, int64_t count, int N, int M, int layout,
                                 size_t* table_bytes, int64_t* work_items) {
-  int64_t items = 0;
-  size_t bytes = 0;
-  const int st = group_size(descs, count, N, M, layout, &items, &bytes);
+  std::vector<bl::GroupItem> plan;
+  const int st = plan_group(descs, count, N, M, layout, &plan);
   if (st != BL_OK) return st;
-  if (table_bytes) *table_bytes = bytes;
-  if (work_items) *work_items = items;
+  if (table_bytes) *table_bytes = group_table_bytes(count, plan.size());
+  if (work_items) *work_items = (int64_t)plan.size();
   return BL_OK;
 }
 
 int bitlinear_group_build(const bl_fwd_desc* descs, int64_t count, int N, int M, int layout,
                           void* table, size_t table_bytes, void* stream) {
-  int64_t items = 0;
-  size_t bytes = 0;
-  const int st = group_size(descs, count, N, M, layout, &items, &bytes);
+  std::vector<bl::GroupItem> plan;
+  const int st = plan_group(descs, count, N, M, layout, &plan);
   if (st != BL_OK) return st;
+  const size_t bytes = group_table_bytes(count, plan.size());
   if (!aligned16(table)) return BL_EINVAL;
   if (table_bytes < bytes) return BL_ENOSPC;
   std::vector<uint8_t> img(bytes, 0);
@@ -166,15 +197,12 @@ int bitlinear_group_build(const bl_fwd_desc* descs, int64_t count, int N, int M,
   hdr.N = N;
   hdr.M = M;
   hdr.count = count;
-  hdr.items = items;
+  hdr.items = (int64_t)plan.size();
   memcpy(img.data(), &hdr, sizeof hdr);
   bl::GroupLayer* rec = (bl::GroupLayer*)(img.data() + sizeof hdr);
-  uint32_t* item_layer = (uint32_t*)(img.data() + sizeof hdr + count * sizeof(bl::GroupLayer));
-  int64_t first = 0;
   for (int64_t i = 0; i < count; ++i) {
     const bl_fwd_desc& d = descs[i];
     const int64_t ke = (layout == BL_LAYOUT_SPARSE && M == 8) ? d.K / 2 * 3 : d.K;
-    const int64_t nit = d.T == 0 ? 0 : ((d.n + 31) / 32 + bl::kGroupWaves - 1) / bl::kGroupWaves;
     bl::GroupLayer r;
     memset(&r, 0, sizeof r);
     r.xq = d.xq;
@@ -187,11 +215,11 @@ int bitlinear_group_build(const bl_fwd_desc* descs, int64_t count, int N, int M,
     r.T = (int32_t)d.T;
     r.Keff = (int32_t)ke;
     r.n = (int32_t)d.n;
-    r.first_item = (int32_t)first;
     memcpy(&rec[i], &r, sizeof r);
-    for (int64_t k = 0; k < nit; ++k) item_layer[first + k] = (uint32_t)i;
-    first += nit;
   }
+  if (!plan.empty())
+    memcpy(img.data() + sizeof hdr + count * sizeof(bl::GroupLayer), plan.data(),
+           plan.size() * sizeof(bl::GroupItem));
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = hipMemcpyAsync(table, img.data(), bytes, hipMemcpyHostToDevice, s);
   if (e == hipSuccess) e = hipStreamSynchronize(s);  // img is released on return

@@ -7,13 +7,15 @@
 // projections of a decoder (Q/K/V, gate/up) and of a stream of layers whose activations are
 // already quantized.
 //
-// Work item = 8 consecutive 32-row panels of one projection; wave w of the block owns panel w over
-// the whole K axis, so no cross-wave reduction is needed.  K is walked in chunks of kGS MFMA steps:
+// Work item = up to 8 consecutive 32-row panels of one projection; wave w of the block owns panel
+// w over the whole K axis, so no cross-wave reduction is needed.  The host lays the items out so
+// that each XCD gets a contiguous run of the projections (their activation rows stay in that XCD's
+// L2) and starts with its largest items.  K is walked in chunks of kGS MFMA steps:
 //   - the wave's packed weights (one code and one meta dword per lane per step) are loaded straight
 //     into a ring of kGD register chunks, kGD - 1 chunks ahead of the MFMAs;
-//   - the block's token rows for the chunk (T x kGS*KSTEP int8) ride in the same ring, one or two
-//     16-byte loads per thread, and are written to a double-buffered LDS tile one chunk ahead, so
-//     the 8 waves share every activation byte they read from L2;
+//   - the block's token rows for the chunk (T x kGS*KSTEP int8, at most one 16-byte load per
+//     thread) ride in the same ring and are written to a double-buffered LDS tile one chunk ahead,
+//     so the 8 waves share every activation byte they read from L2;
 //   - the MFMAs read their B fragments from LDS (row stride + 16 bytes keeps 16 tokens' 16-byte
 //     reads on distinct banks).
 // Steps past the end of K re-read the last step with the code forced to 0 (zero weights add 0).
@@ -23,8 +25,8 @@
 namespace bl {
 
 namespace {
-constexpr int kGS = 8;  // MFMA steps per chunk
-constexpr int kGD = 3;  // register ring depth in chunks
+constexpr int kGS = 4;  // MFMA steps per chunk
+constexpr int kGD = 4;  // register ring depth in chunks
 
 typedef __attribute__((address_space(1))) const uint32_t g_u32;
 typedef __attribute__((address_space(1))) const v4i g_v4i;
@@ -110,9 +112,10 @@ __global__ __launch_bounds__(64 * kGroupWaves, 2) void gemv_group_kernel(
   const int item = blockIdx.x;
   // uniform across the block: a table of another layout, or a grid larger than the table, does nothing
   if (hdr->magic != kGroupMagic || hdr->layout != LAYOUT || item >= hdr->items) return;
-  const uint32_t li = ((const uint32_t*)(table + sizeof(GroupHeader) +
-                                         hdr->count * sizeof(GroupLayer)))[item];
-  const GroupLayer L = ((const GroupLayer*)(table + sizeof(GroupHeader)))[li];
+  const GroupItem it = ((const GroupItem*)(table + sizeof(GroupHeader) +
+                                           hdr->count * sizeof(GroupLayer)))[item];
+  if (it.layer == kGroupNoItem) return;
+  const GroupLayer L = ((const GroupLayer*)(table + sizeof(GroupHeader)))[it.layer];
 
   G k;
   k.tid = threadIdx.x;
@@ -121,7 +124,7 @@ __global__ __launch_bounds__(64 * kGroupWaves, 2) void gemv_group_kernel(
   k.Keff = L.Keff;
   const int n = L.n;
   const int npanels = (n + kPanel - 1) / kPanel;
-  const int P = (item - L.first_item) * kGroupWaves + wave;
+  const int P = (int)it.panel0 + wave;
   const int Pl = min(P, npanels - 1);        // surplus waves load a real panel, store nothing
   k.NF = k.Keff / G::KSTEP;
   k.nch = (k.NF + kGS - 1) / kGS;
@@ -136,18 +139,21 @@ __global__ __launch_bounds__(64 * kGroupWaves, 2) void gemv_group_kernel(
   const float gamma = *(__attribute__((address_space(1))) const float*)L.gamma;
   const float sc = *((__attribute__((address_space(1))) const float*)L.xs + k.brow);
 
-  typename G::Chunk r0, r1, r2;
-  k.issue(0, r0);
-  k.issue(1, r1);
-  k.issue(2, r2);
-  k.put(0, r0);
+  typename G::Chunk r[kGD];
+  // chunk by chunk, in the loop's issue order: the wait for a chunk in the loop is then the same
+  // count on the first pass as on every later one (otherwise the compiler takes the smaller one)
+#pragma unroll
+  for (int q = 0; q < kGD; ++q) {
+    k.issue(q, r[q]);
+    asm volatile("" ::: "memory");
+  }
+  k.put(0, r[0]);
   block_sync_lds();
   k.acc = v16i{};
   // nch rounded up to the ring depth: the trailing chunks skip their MFMAs, not their loads
   for (int j = 0; j < k.nch; j += kGD) {
-    k.step(j, r0, r1);
-    k.step(j + 1, r1, r2);
-    k.step(j + 2, r2, r0);
+#pragma unroll
+    for (int q = 0; q < kGD; ++q) k.step(j + q, r[q], r[(q + 1) % kGD]);
   }
   const v16i acc = k.acc;
 

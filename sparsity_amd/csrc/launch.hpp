@@ -26,11 +26,13 @@ hipError_t launch_fwd(const int8_t* xq, const float* x_scale, int64_t T, int64_t
 namespace bl {
 
 // Device table of a group of independent decode projections (bitlinear_group_build writes it,
-// gemv_group_kernel reads it): a header, one GroupLayer per projection, then one uint32 per work
-// item naming its projection.  A work item is kGroupWaves consecutive 32-row panels of one
+// gemv_group_kernel reads it): a header, one GroupLayer per projection, then one GroupItem per
+// work item in launch order.  A work item is up to kGroupWaves consecutive 32-row panels of one
 // projection, one panel per wave.
 constexpr int kGroupWaves = 8;
-constexpr uint32_t kGroupMagic = 0x31474c42u;  // "BLG1"
+constexpr int kXcds = 8;                       // MI355X: 8 XCDs, workgroups dealt round-robin
+constexpr uint32_t kGroupMagic = 0x32474c42u;  // "BLG2"
+constexpr uint32_t kGroupNoItem = 0xFFFFFFFFu; // padding item: its block does nothing
 
 struct GroupHeader {
   uint32_t magic;
@@ -48,9 +50,14 @@ struct GroupLayer {
   const float* gamma;
   float* y;
   int32_t* acc;
-  int32_t T, Keff, n, first_item;
+  int32_t T, Keff, n, reserved;
 };
 static_assert(sizeof(GroupLayer) == 72, "group layer record is 72 bytes");
+
+struct GroupItem {
+  uint32_t layer;   // projection index, or kGroupNoItem
+  uint32_t panel0;  // first 32-row panel of the item
+};
 
 hipError_t launch_fwd_group(const void* table, int64_t items, int layout, hipStream_t s);
 
