@@ -1,0 +1,132 @@
+"""Parity at the benchmark workloads' full sizes, in the launch configurations bench.py times.
+
+Packed codes, metadata, gamma and int8 activations are compared in full, bit for bit.  Outputs are
+compared in full where the oracle's int64 product is cheap (decode), else on sampled tokens (all
+output rows) and sampled rows (all tokens).  Inputs come from the seeded generators in synth/.
+"""
+import numpy as np
+import pytest
+
+import oracle as O
+from parity_util import assert_y_close, dev, f32_bits, host
+from synth import workload_inputs
+
+pytestmark = pytest.mark.gpu
+
+S = pytest.importorskip("sparsity_amd")
+
+
+def _bf16_dev(bits):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda().view(torch.bfloat16)
+
+
+def _check_pack(W, N, M, layout, what):
+    ref = O.pack(W, N, M, layout)
+    codes, meta, gamma = S.pack(dev(W), N, M, layout)
+    assert f32_bits(host(gamma)[0]) == f32_bits(ref["gamma"]), f"{what}: gamma"
+    assert np.array_equal(host(codes).view(np.uint32), ref["codes"]), f"{what}: codes"
+    if meta is not None:
+        assert np.array_equal(host(meta).view(np.uint32), ref["meta"]), f"{what}: meta"
+    return ref, (codes, meta, gamma)
+
+
+def _check_quant(x, bits, lift, what):
+    xq, sc = S.act_quant(_bf16_dev(bits), lift)
+    q_ref, s_ref = O.act_quant(x, lift)
+    assert np.array_equal(host(xq), q_ref), f"{what}: int8 activations"
+    assert np.array_equal(f32_bits(host(sc)), f32_bits(s_ref)), f"{what}: token scales"
+    return xq, sc
+
+
+def _check_sampled(ref, x, y, acc, toks, rows, what):
+    """Accumulators and outputs of sampled tokens (all rows) and sampled rows (all tokens)."""
+    q, s = O.act_quant(x, 0)
+    acc_t = O.acc_dense(ref["W_eff"], q[toks])
+    assert np.array_equal(acc[toks], acc_t), f"{what}: accumulators of sampled tokens"
+    assert_y_close(y[toks], O.rescale(acc_t, ref["gamma"], s[toks]), what=f"{what} sampled tokens")
+    acc_r = O.acc_dense(ref["W_eff"][rows], q)
+    assert np.array_equal(acc[:, rows], acc_r), f"{what}: accumulators of sampled rows"
+    assert_y_close(y[:, rows], O.rescale(acc_r, ref["gamma"], s), what=f"{what} sampled rows")
+
+
+def test_decode_full_size_grouped():
+    """FFN up 6912x2560 and down 2560x6912 (2:4) at T = 1, 4, 16 in one grouped launch, as the
+    decode benchmark runs them; every output compared; single-projection calls agree bitwise."""
+    import torch
+    d = workload_inputs("decode", 0)
+    projs = []
+    for name, K in (("up", 2560), ("down", 6912)):
+        W = d[f"W:{name}"]
+        ref, (codes, meta, gamma) = _check_pack(W, 2, 4, O.LAYOUT_SPARSE, f"decode {name}")
+        print(f"decode {name}: pack bit-exact", flush=True)
+        for T in (1, 4, 16):
+            x, bits = d[f"X:{K}"][:T], d[f"Xbits:{K}"][:T]
+            xq, sc = _check_quant(x, bits, 0, f"decode {name} T={T}")
+            n = W.shape[0]
+            projs.append(dict(xq=xq, scale=sc, K=K, codes=codes, meta=meta, gamma=gamma, n=n,
+                              y=torch.empty((T, n), device="cuda"),
+                              acc=torch.empty((T, n), dtype=torch.int32, device="cuda"),
+                              ref=ref, x=x, name=f"{name} T={T}"))
+    S.FwdGroup(projs)()
+    for p in projs:
+        q, s = O.act_quant(p["x"], 0)
+        acc_ref = O.acc_dense(p["ref"]["W_eff"], q)
+        assert np.array_equal(host(p["acc"]), acc_ref), f"decode {p['name']}: accumulators"
+        assert_y_close(host(p["y"]), O.rescale(acc_ref, p["ref"]["gamma"], s), what=p["name"])
+        y1 = S.fwd(p["xq"], p["scale"], p["K"], p["codes"], p["meta"], p["gamma"], p["n"])
+        assert np.array_equal(f32_bits(host(y1)), f32_bits(host(p["y"]))), p["name"]
+        print(f"decode {p['name']}: ok", flush=True)
+
+
+def test_prefill_full_size():
+    """4096 Student-t tokens x 4096 -> 11008 (2:4), the large-tile GEMM."""
+    d = workload_inputs("prefill", 0)
+    W, x, bits = d["W:gate_up"], d["X:4096"], d["Xbits:4096"]
+    ref, (codes, meta, gamma) = _check_pack(W, 2, 4, O.LAYOUT_SPARSE, "prefill")
+    print("prefill: pack bit-exact", flush=True)
+    xq, sc = _check_quant(x, bits, 0, "prefill")
+    y, acc = S.fwd(xq, sc, 4096, codes, meta, gamma, 11008, want_acc=True)
+    g = np.random.default_rng(11)
+    toks = np.unique(np.concatenate([[0, 4095], g.choice(4096, 30, replace=False)]))
+    rows = np.unique(np.concatenate([[0, 11007], g.choice(11008, 30, replace=False)]))
+    _check_sampled(ref, x, host(y), host(acc), toks, rows, "prefill")
+    print("prefill: sampled outputs ok", flush=True)
+
+
+def test_six_eight_full_size():
+    """6:8 through three 2:4 windows, 2048 x 4096 -> 4096: pack and lifted activations bit-exact,
+    sampled outputs against the oracle, and the dense-stored path bitwise equal at full size."""
+    d = workload_inputs("six_eight", 0)
+    W, x, bits = d["W:w"], d["X:4096"], d["Xbits:4096"]
+    ref, (cs, ms, gs) = _check_pack(W, 6, 8, O.LAYOUT_SPARSE, "6:8 windows")
+    _, (cd, _, gd) = _check_pack(W, 6, 8, O.LAYOUT_DENSE2, "6:8 dense")
+    print("6:8: both packs bit-exact", flush=True)
+    xl, sl = _check_quant(x, bits, 8, "6:8 lifted")
+    xd, sd = _check_quant(x, bits, 0, "6:8 plain")
+    ys, accs = S.fwd(xl, sl, 4096, cs, ms, gs, 4096, 6, 8, O.LAYOUT_SPARSE, want_acc=True)
+    yd = S.fwd(xd, sd, 4096, cd, None, gd, 4096, 6, 8, O.LAYOUT_DENSE2)
+    assert np.array_equal(f32_bits(host(ys)), f32_bits(host(yd))), "windows path != dense path"
+    g = np.random.default_rng(68)
+    toks = np.unique(np.concatenate([[0, 2047], g.choice(2048, 30, replace=False)]))
+    rows = np.unique(np.concatenate([[0, 4095], g.choice(4096, 30, replace=False)]))
+    _check_sampled(ref, x, host(ys), host(accs), toks, rows, "6:8")
+    print("6:8: sampled outputs ok", flush=True)
+
+
+def test_train_step_full_size():
+    """3B-alike layer set at 8192 tokens: all seven masters packed bit-exactly, both activation
+    matrices quantized bit-exactly, each forward checked on sampled tokens and rows."""
+    d = workload_inputs("train_step", 0)
+    Q = {K: _check_quant(d[f"X:{K}"], d[f"Xbits:{K}"], 0, f"train X:{K}") for K in (3200, 8640)}
+    g = np.random.default_rng(35)
+    for L in ("q", "k", "v", "o", "gate", "up", "down"):
+        W = d[f"W:{L}"]
+        n, K = W.shape
+        ref, (codes, meta, gamma) = _check_pack(W, 2, 4, O.LAYOUT_SPARSE, f"train {L}")
+        xq, sc = Q[K]
+        y, acc = S.fwd(xq, sc, K, codes, meta, gamma, n, want_acc=True)
+        toks = np.unique(np.concatenate([[0, 8191], g.choice(8192, 6, replace=False)]))
+        rows = np.unique(np.concatenate([[0, n - 1], g.choice(n, 6, replace=False)]))
+        _check_sampled(ref, d[f"X:{K}"], host(y), host(acc), toks, rows, f"train {L}")
+        print(f"train {L} {n}x{K}: pack bit-exact, sampled outputs ok", flush=True)
