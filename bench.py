@@ -58,9 +58,10 @@ def parse():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the 6:8 and training-step legs")
     ap.add_argument("--cpu-budget-s", type=float, default=15.0)
-    ap.add_argument("--profile-pass", action="store_true",
-                    help="for hardware-counter runs: two eager decode steps, then a plain copy of "
-                         "COPY_BYTES (the counters' scale reference); no graph, no JSON line")
+    ap.add_argument("--profile-pass", choices=("decode", "prefill"), default=None,
+                    help="for hardware-counter runs, no graph and no JSON line.  decode: two eager "
+                         "decode steps, then a plain copy of COPY_BYTES (the counters' scale "
+                         "reference); prefill: the prefill GEMM launched three times")
     return ap.parse_args()
 
 
@@ -321,9 +322,14 @@ def main():
     import sparsity_amd as S
     S.lib()
     torch.cuda.set_device(0)
+    if args.profile_pass == "prefill":
+        prefill_leg(S, torch, iters=2)
+        torch.cuda.synchronize()
+        log("profile pass done: prefill GEMM x 5")
+        return
     log(f"device {torch.cuda.get_device_name(0)}; packing {2 * N_PAIRS} matrices")
     D = Decode(S, torch)
-    if args.profile_pass:
+    if args.profile_pass == "decode":
         for _ in range(2):
             D.step(S)
         torch.cuda.synchronize()
