@@ -58,10 +58,11 @@ def parse():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the 6:8 and training-step legs")
     ap.add_argument("--cpu-budget-s", type=float, default=15.0)
-    ap.add_argument("--profile-pass", choices=("decode", "prefill"), default=None,
+    ap.add_argument("--profile-pass", choices=("decode", "prefill", "train"), default=None,
                     help="for hardware-counter runs, no graph and no JSON line.  decode: two eager "
                          "decode steps, then a plain copy of COPY_BYTES (the counters' scale "
-                         "reference); prefill: the prefill GEMM launched three times")
+                         "reference); prefill: the prefill GEMM launched five times; train: the "
+                         "training-step leg with two timed steps")
     return ap.parse_args()
 
 
@@ -240,7 +241,8 @@ TRAIN_LAYERS = (("q", 3200, 3200), ("k", 3200, 3200), ("v", 3200, 3200), ("o", 3
 
 def train_step_leg(S, torch, iters=3):
     """3B-alike decoder layer set at 8192 tokens: re-mask + ternarize + pack all 7 fp32 masters,
-    quantize the two activation matrices once, then the 7 2:4 forwards."""
+    quantize the two activation matrices once, then the 7 2:4 forwards.  Each phase is one HIP
+    graph (checked against the eager run) timed with events around its replays."""
     T = 8192
     g = torch.Generator(device="cuda")
     g.manual_seed(35)
@@ -268,9 +270,35 @@ def train_step_leg(S, torch, iters=3):
             xq, sc = Q[K]
             S.fwd(xq, sc, K, c, m, ga, n, out=(y, None))
 
-    t_pack = _event_ms(torch, pack_all, iters)
-    t_quant = _event_ms(torch, quant_all, iters)
-    t_fwd = _event_ms(torch, fwd_all, iters)
+    # each phase captured once as a HIP graph (no host launch overhead between the 7 matrices);
+    # two replays are checked bitwise against the eager results first
+    def outputs():
+        return [t.clone() for (c, m, ga) in packed for t in (c, m, ga)] + [y.clone() for y in ys]
+
+    pack_all()
+    quant_all()
+    fwd_all()
+    torch.cuda.synchronize()
+    ref = outputs()
+    graphs = []
+    cap = torch.cuda.Stream()
+    for fn in (pack_all, quant_all, fwd_all):
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr, stream=cap):
+            fn()
+        graphs.append(gr)
+    for _ in range(2):
+        for t in [t for (c, m, ga) in packed for t in (c, m, ga)] + ys:
+            t.zero_()
+        for gr in graphs:
+            gr.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(outputs(), ref):
+            if not torch.equal(a, b):
+                raise RuntimeError("training-step graph replay differs from the eager run")
+    t_pack = _event_ms(torch, graphs[0].replay, iters)
+    t_quant = _event_ms(torch, graphs[1].replay, iters)
+    t_fwd = _event_ms(torch, graphs[2].replay, iters)
     pack_bytes = sum(4 * n * K + p[0].numel() + p[1].numel() for (_, n, K), p in zip(TRAIN_LAYERS, packed))
     ops = sum(2.0 * T * K * n for (_, n, K) in TRAIN_LAYERS)
     return {"workload": "3B-alike layer set (QKV 3x3200x3200, O, gate/up 8640x3200, down 3200x8640), "
@@ -322,6 +350,11 @@ def main():
     import sparsity_amd as S
     S.lib()
     torch.cuda.set_device(0)
+    if args.profile_pass == "train":
+        train_step_leg(S, torch, iters=2)
+        torch.cuda.synchronize()
+        log("profile pass done: training-step layer set")
+        return
     if args.profile_pass == "prefill":
         prefill_leg(S, torch, iters=2)
         torch.cuda.synchronize()

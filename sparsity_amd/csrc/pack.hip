@@ -6,14 +6,16 @@
 // in each M-group (same summary, Maskering) and 6:8 groups are rewritten as three overlapping
 // 2:4 windows (SlideSparse abstract, Sliding Window Decomposition).
 //
-// Three launches, all on the caller's stream:
+// Two launches, both on the caller's stream:
 //   1. gamma_partial_kernel   fp64 partial sums of |w| (HBM-bound read of W)
-//   2. gamma_finalize_kernel  one block: sums the partials, certifies the fp32 rounding of the
-//                             exact mean with a rigorous error bound, and only when the bound
-//                             cannot decide falls back to an exact exponent-binned integer sum;
-//                             then derives the ternary threshold tau
-//   3. pack_kernel            W again (mostly from the 256 MB last-level cache), mask, codes by
-//                             |w| >= tau, slots assembled in LDS, coalesced dword stores
+//   2. pack_kernel            every block first derives gamma from the partials (same data, same
+//                             order, so every block gets the same bits): it certifies the fp32
+//                             rounding of the exact mean with a rigorous error bound, and only
+//                             when the bound cannot decide falls back to an exact exponent-binned
+//                             integer sum over W; then the ternary threshold tau.  Its tile of W
+//                             (mostly from the 256 MB last-level cache) is already in flight
+//                             meanwhile.  Mask, codes by |w| >= tau, slots assembled in LDS,
+//                             coalesced dword stores.
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -21,23 +23,31 @@ namespace bl {
 
 struct PackWs {
   double partial[kGammaBlocks];
-  float tau;            // smallest fp32 x with fl32(x / gamma) > 0.5 (+inf when gamma == 0)
-  uint32_t exact_used;  // 1 when the exact fallback decided gamma (diagnostic)
+  uint32_t exact_used;  // 1 when the exact fallback decided gamma (diagnostic, written by block 0)
 };
 static_assert(sizeof(PackWs) <= kPackWsBytes, "pack workspace");
 
 __global__ __launch_bounds__(kGammaThreads) void gamma_partial_kernel(const float4* __restrict__ W4,
                                                                       int64_t n4,
                                                                       double* __restrict__ partial) {
-  double acc = 0.0;
+  // Four independent fp64 chains per thread keep four 16-byte loads in flight.  Every |w| still
+  // passes through at most 4 * ceil(n4 / threads) + 2 additions before the wave sum, inside the
+  // depth the finalize step assumes for its error bound.
   const int64_t stride = (int64_t)kGammaBlocks * kGammaThreads;
-  for (int64_t i = (int64_t)blockIdx.x * kGammaThreads + threadIdx.x; i < n4; i += stride) {
-    const float4 v = W4[i];
-    acc += fabs((double)v.x);
-    acc += fabs((double)v.y);
-    acc += fabs((double)v.z);
-    acc += fabs((double)v.w);
+  double a0 = 0.0, a1 = 0.0, a2 = 0.0, a3 = 0.0;
+  int64_t i = (int64_t)blockIdx.x * kGammaThreads + threadIdx.x;
+  for (; i + 3 * stride < n4; i += 4 * stride) {
+    const float4 v0 = W4[i], v1 = W4[i + stride], v2 = W4[i + 2 * stride], v3 = W4[i + 3 * stride];
+    a0 += fabs((double)v0.x); a0 += fabs((double)v0.y); a0 += fabs((double)v0.z); a0 += fabs((double)v0.w);
+    a1 += fabs((double)v1.x); a1 += fabs((double)v1.y); a1 += fabs((double)v1.z); a1 += fabs((double)v1.w);
+    a2 += fabs((double)v2.x); a2 += fabs((double)v2.y); a2 += fabs((double)v2.z); a2 += fabs((double)v2.w);
+    a3 += fabs((double)v3.x); a3 += fabs((double)v3.y); a3 += fabs((double)v3.z); a3 += fabs((double)v3.w);
   }
+  for (; i < n4; i += stride) {
+    const float4 v = W4[i];
+    a0 += fabs((double)v.x); a0 += fabs((double)v.y); a0 += fabs((double)v.z); a0 += fabs((double)v.w);
+  }
+  double acc = (a0 + a1) + (a2 + a3);
   acc = wave_sum_f64(acc);
   __shared__ double red[kGammaThreads / 64];
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = acc;
@@ -121,23 +131,44 @@ __device__ float ternary_threshold(float gamma) {
   return f;
 }
 
-__global__ __launch_bounds__(1024) void gamma_finalize_kernel(const float* __restrict__ W,
-                                                              int64_t count, PackWs* ws,
-                                                              float* __restrict__ gamma_out) {
-  static_assert(kGammaBlocks == 1024, "one partial per thread");
-  __shared__ double red[16];
-  __shared__ unsigned long long bins[256];
-  __shared__ int certified;
-  __shared__ float g;
+// gamma and tau from the partial sums, computed by one whole block (every pack block runs it and
+// gets the same bits).  Returns through LDS: *g_sh, *tau_sh, *exact_sh.
+// `v` is this thread's sum of partials threadIdx.x + i * NT (loaded by the caller, ahead of its
+// own tile loads, so waiting for them does not wait for the tile).
+// Rare path of block_gamma: the exact mean of |W| by the whole block (exponent-binned integer
+// sums in LDS), kept out of line so the common path stays small.  Every thread of the block calls
+// it; thread 0 writes *g_sh.
+template <int NT>
+__device__ __noinline__ void exact_gamma_block(const float* __restrict__ W, int64_t count,
+                                               float* g_sh, unsigned long long* bins_sh) {
+  for (int i = threadIdx.x; i < 256; i += NT) bins_sh[i] = 0ull;
+  __syncthreads();
+  for (int64_t i = threadIdx.x; i < count; i += NT) {
+    const uint32_t b = __float_as_uint(W[i]) & 0x7FFFFFFFu;
+    const uint32_t e = b >> 23;
+    const uint32_t m = (b & 0x7FFFFFu) | (e ? 0x800000u : 0u);
+    atomicAdd(&bins_sh[e], (unsigned long long)m);
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) *g_sh = exact_mean_from_bins(bins_sh, (uint64_t)count);
+}
+
+template <int NT>
+__device__ __forceinline__ void block_gamma(double v, const float* __restrict__ W, int64_t count, float* g_sh,
+                            float* tau_sh, int* exact_sh, double* red_sh,
+                            unsigned long long* bins_sh) {
+  static_assert(kGammaBlocks % NT == 0 && NT % 64 == 0, "partials split evenly");
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  double v = wave_sum_f64(ws->partial[threadIdx.x]);
-  if (lane == 0) red[wave] = v;
+  v = wave_sum_f64(v);
+  if (lane == 0) red_sh[wave] = v;
   __syncthreads();
   if (threadIdx.x == 0) {
     double S = 0.0;
-    for (int w = 0; w < 16; ++w) S += red[w];
-    // longest chain of fp64 additions any |w| goes through: the per-thread loop (4 per float4),
-    // the wave butterfly (6), the block sum (4), the finalize butterfly (6) and sum (16)
+    for (int w = 0; w < NT / 64; ++w) S += red_sh[w];
+    // longest chain of fp64 additions any |w| goes through: the partial kernel's per-thread
+    // chains (at most 4 per float4 it reads, plus 2 to join its four chains), its wave butterfly
+    // (6) and block sum (4), then here the per-thread sum (kGammaBlocks / NT), the butterfly (6)
+    // and the block sum (NT / 64); 64 covers every fixed term
     const int64_t n4 = count / 4;
     const int64_t per_thread = (n4 + (int64_t)kGammaBlocks * kGammaThreads - 1) / ((int64_t)kGammaBlocks * kGammaThreads);
     const double depth = 4.0 * (double)per_thread + 64.0;
@@ -147,28 +178,15 @@ __global__ __launch_bounds__(1024) void gamma_finalize_kernel(const float* __res
     const double lo = (S - err) / cnt * (1.0 - 4.0 * u);
     const double hi = (S + err) / cnt * (1.0 + 4.0 * u);
     const float glo = (float)lo, ghi = (float)hi;
-    if (S == 0.0) { certified = 1; g = 0.f; }
-    else if (glo == ghi) { certified = 1; g = glo; }
-    else certified = 0;
+    if (S == 0.0) { *exact_sh = 0; *g_sh = 0.f; }
+    else if (glo == ghi) { *exact_sh = 0; *g_sh = glo; }
+    else *exact_sh = 1;
   }
   __syncthreads();
-  if (!certified) {
-    for (int i = threadIdx.x; i < 256; i += 1024) bins[i] = 0ull;
-    __syncthreads();
-    for (int64_t i = threadIdx.x; i < count; i += 1024) {
-      const uint32_t b = __float_as_uint(W[i]) & 0x7FFFFFFFu;
-      const uint32_t e = b >> 23;
-      const uint32_t m = (b & 0x7FFFFFu) | (e ? 0x800000u : 0u);
-      atomicAdd(&bins[e], (unsigned long long)m);
-    }
-    __syncthreads();
-    if (threadIdx.x == 0) g = exact_mean_from_bins(bins, (uint64_t)count);
-  }
-  if (threadIdx.x == 0) {
-    gamma_out[0] = g;
-    ws->tau = ternary_threshold(g);
-    ws->exact_used = certified ? 0u : 1u;
-  }
+  if (*exact_sh)   // uniform; rare: the bound straddles an fp32 rounding boundary
+    exact_gamma_block<NT>(W, count, g_sh, bins_sh);
+  if (threadIdx.x == 0) *tau_sh = ternary_threshold(*g_sh);
+  __syncthreads();
 }
 
 constexpr int kPackKB = 256;  // dense K columns per pack tile
@@ -179,7 +197,8 @@ constexpr int kPackKB = 256;  // dense K columns per pack tile
 // layout (unit v = 32*u + r of the tile is dword base + v).
 template <int LAYOUT, int M>
 __global__ __launch_bounds__(256) void pack_kernel(const float* __restrict__ W, int n, int K, int N,
-                                                   int k_tiles, const float* __restrict__ tau_p,
+                                                   int k_tiles, PackWs* __restrict__ ws,
+                                                   float* __restrict__ gamma_out,
                                                    uint32_t* __restrict__ codes,
                                                    uint32_t* __restrict__ meta) {
   constexpr bool SP = LAYOUT == kLayoutSparse;
@@ -190,22 +209,48 @@ __global__ __launch_bounds__(256) void pack_kernel(const float* __restrict__ W, 
   constexpr int UPR = SLOTS / 16;                                      // units per tile row
   __shared__ __attribute__((aligned(16))) float tile[32 * WS];
   __shared__ __attribute__((aligned(16))) uint8_t slots[32 * SS];
+  __shared__ double red_sh[4];
+  __shared__ unsigned long long bins_sh[256];
+  __shared__ float g_sh, tau_sh;
+  __shared__ int exact_sh;
 
   const int P = blockIdx.x / k_tiles;
   const int kb = blockIdx.x % k_tiles;
   const int k0 = kb * kPackKB;
   const int r0 = P * kPanel;
   const int kw = min(kPackKB, K - k0);
-  const float tau = *tau_p;
 
+  // this thread's share of the gamma partial sums first (L2 hits), then all eight 16-byte tile
+  // loads before its first LDS store (addresses clamped into the matrix; out-of-range rows and
+  // columns are zeroed after the load)
+  double pv = 0.0;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int row = i * 4 + (threadIdx.x >> 6);
+  for (int i = 0; i < kGammaBlocks / 256; ++i) pv += ws->partial[threadIdx.x + i * 256];
+  asm volatile("" ::: "memory");
+  {
     const int c4 = threadIdx.x & 63;
-    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (r0 + row < n && 4 * c4 < kw) v = *(const float4*)(W + (size_t)(r0 + row) * K + k0 + 4 * c4);
-    *(float4*)&tile[row * WS + 4 * c4] = v;
+    const bool col_ok = 4 * c4 < kw;
+    const int col = k0 + min(4 * c4, kw - 4);
+    float4 v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int row = i * 4 + (threadIdx.x >> 6);
+      v[i] = *(const float4*)(W + (size_t)min(r0 + row, n - 1) * K + col);
+    }
+    // gamma while the tile is in flight
+    block_gamma<256>(pv, W, (int64_t)n * K, &g_sh, &tau_sh, &exact_sh, red_sh, bins_sh);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int row = i * 4 + (threadIdx.x >> 6);
+      if (!(col_ok && r0 + row < n)) v[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+      *(float4*)&tile[row * WS + 4 * c4] = v[i];
+    }
   }
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    gamma_out[0] = g_sh;
+    ws->exact_used = (uint32_t)exact_sh;
+  }
+  const float tau = tau_sh;
   __syncthreads();
 
   const int nkeep = SP ? (M == 4 ? 2 : 6) : N;
@@ -280,20 +325,19 @@ hipError_t launch_pack(const float* W, int64_t n, int64_t K, int N, int M, int l
   PackWs* ws = (PackWs*)ws_raw;
   const int64_t count = n * K;
   gamma_partial_kernel<<<kGammaBlocks, kGammaThreads, 0, s>>>((const float4*)W, count / 4, ws->partial);
-  gamma_finalize_kernel<<<1, 1024, 0, s>>>(W, count, ws, gamma);
   const int panels = (int)((n + kPanel - 1) / kPanel);
   const int k_tiles = (int)((K + kPackKB - 1) / kPackKB);
   const dim3 grid((unsigned)(panels * k_tiles));
   if (layout == kLayoutSparse) {
     if (M == 4)
-      pack_kernel<kLayoutSparse, 4><<<grid, 256, 0, s>>>(W, (int)n, (int)K, N, k_tiles, &ws->tau, codes, meta);
+      pack_kernel<kLayoutSparse, 4><<<grid, 256, 0, s>>>(W, (int)n, (int)K, N, k_tiles, ws, gamma, codes, meta);
     else
-      pack_kernel<kLayoutSparse, 8><<<grid, 256, 0, s>>>(W, (int)n, (int)K, N, k_tiles, &ws->tau, codes, meta);
+      pack_kernel<kLayoutSparse, 8><<<grid, 256, 0, s>>>(W, (int)n, (int)K, N, k_tiles, ws, gamma, codes, meta);
   } else {
     if (M == 4)
-      pack_kernel<kLayoutDense2, 4><<<grid, 256, 0, s>>>(W, (int)n, (int)K, N, k_tiles, &ws->tau, codes, nullptr);
+      pack_kernel<kLayoutDense2, 4><<<grid, 256, 0, s>>>(W, (int)n, (int)K, N, k_tiles, ws, gamma, codes, nullptr);
     else
-      pack_kernel<kLayoutDense2, 8><<<grid, 256, 0, s>>>(W, (int)n, (int)K, N, k_tiles, &ws->tau, codes, nullptr);
+      pack_kernel<kLayoutDense2, 8><<<grid, 256, 0, s>>>(W, (int)n, (int)K, N, k_tiles, ws, gamma, codes, nullptr);
   }
   return hipGetLastError();
 }
