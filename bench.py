@@ -39,6 +39,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 SMFMAC_I8_PEAK_TOPS = 10100.0  # MI355X int8 with 2:4 structured sparsity, dense-equivalent
+MFMA_I8_PEAK_TOPS = 5000.0     # MI355X dense int8 MFMA
 UP = (6912, 2560)
 DOWN = (2560, 6912)
 N_PAIRS = 64
@@ -230,6 +231,10 @@ def six_eight_leg(S, torch, iters=10):
             "dense_TOPS": round(ops / (t_d * 1e-3) / 1e12, 1),
             "gemm_ms": {"windows": round(t_s, 4), "dense": round(t_d, 4)},
             "act_quant_ms": {"lifted": round(t_ql, 4), "plain": round(t_qd, 4)},
+            "roofline": {"windows": {"bound": "mfma", "peak": SMFMAC_I8_PEAK_TOPS, "unit": "TOPS",
+                                     "frac": round(ops / (t_s * 1e-3) / 1e12 / SMFMAC_I8_PEAK_TOPS, 4)},
+                         "dense": {"bound": "mfma", "peak": MFMA_I8_PEAK_TOPS, "unit": "TOPS",
+                                   "frac": round(ops / (t_d * 1e-3) / 1e12 / MFMA_I8_PEAK_TOPS, 4)}},
             "speedup_vs_dense": round(t_d / t_s, 3),
             "speedup_with_quant": round((t_d + t_qd) / (t_s + t_ql), 3), "bound": round(4 / 3, 3),
             "outputs_identical": same}
@@ -300,13 +305,28 @@ def train_step_leg(S, torch, iters=3):
     t_quant = _event_ms(torch, graphs[1].replay, iters)
     t_fwd = _event_ms(torch, graphs[2].replay, iters)
     pack_bytes = sum(4 * n * K + p[0].numel() + p[1].numel() for (_, n, K), p in zip(TRAIN_LAYERS, packed))
+    # act_quant: bf16 read + int8 write per element + 4 B scale per token
+    quant_bytes = sum(T * K * 3 + 4 * T for K in X)
     ops = sum(2.0 * T * K * n for (_, n, K) in TRAIN_LAYERS)
+    pack_gbs = pack_bytes / (t_pack * 1e-3) / 1e9
+    quant_gbs = quant_bytes / (t_quant * 1e-3) / 1e9
+    fwd_tops = ops / (t_fwd * 1e-3) / 1e12
     return {"workload": "3B-alike layer set (QKV 3x3200x3200, O, gate/up 8640x3200, down 3200x8640), "
                         "8192 tokens, 2:4, bf16 N(0,1) activations",
             "step_ms": round(t_pack + t_quant + t_fwd, 4),
-            "pack_ms": round(t_pack, 4), "pack_GBps": round(pack_bytes / (t_pack * 1e-3) / 1e9, 1),
-            "act_quant_ms": round(t_quant, 4), "fwd_ms": round(t_fwd, 4),
-            "fwd_TOPS": round(ops / (t_fwd * 1e-3) / 1e12, 1)}
+            "pack_ms": round(t_pack, 4), "pack_GBps": round(pack_gbs, 1),
+            "act_quant_ms": round(t_quant, 4), "act_quant_GBps": round(quant_gbs, 1),
+            "fwd_ms": round(t_fwd, 4), "fwd_TOPS": round(fwd_tops, 1),
+            # algorithmic bytes (pack: 4 B read + packed bytes written per weight, one pass over
+            # the master; act_quant: 3 B per element + 4 B per token) or dense-equivalent ops
+            "roofline": {"pack": {"bound": "hbm", "achieved": round(pack_gbs, 1), "peak": HBM_PEAK_GBS,
+                                  "unit": "GB/s", "frac": round(pack_gbs / HBM_PEAK_GBS, 4)},
+                         "act_quant": {"bound": "hbm", "achieved": round(quant_gbs, 1),
+                                       "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                       "frac": round(quant_gbs / HBM_PEAK_GBS, 4)},
+                         "fwd": {"bound": "mfma", "achieved": round(fwd_tops, 1),
+                                 "peak": SMFMAC_I8_PEAK_TOPS, "unit": "TOPS",
+                                 "frac": round(fwd_tops / SMFMAC_I8_PEAK_TOPS, 4)}}}
 
 
 # ---------------------------------------------------------------------------------------------
