@@ -29,15 +29,17 @@ formulas of Eqs. 1-3 in extraction):
   * Activations: absmax_t = max_k |x_tk|; s_t = fl32(127 / absmax_t);
     q = clamp(rint(fl32(x * s_t)), -127, 127); scale_t = fl32(absmax_t / 127);
     absmax_t == 0 gives q = 0 and scale_t = 0.
-  * 6:8 windows: window w in {0,1,2} covers positions 2w..2w+3 of an 8-group;
-    greedy assignment in ascending position order (w0 takes kept positions in
-    0..3, at most 2; w1 takes the remaining kept positions in 2..5, at most 2;
-    w2 takes the rest).  Lifted activations: x'[12g + 4w + j] = x[8g + 2w + j].
+  * (2N-2):2N windows (6:8 and 14:16): with M = 2N, window w in 0..N-2 covers
+    positions 2w..2w+3 of an M-group; kept positions are assigned in ascending
+    order, each to the lowest window that covers it and holds fewer than 2
+    (for 6:8: w0 takes kept positions in 0..3, at most 2; w1 takes the
+    remaining ones in 2..5, at most 2; w2 takes the rest).  Lifted activations:
+    x'[(2M-4)g + 4w + j] = x[Mg + 2w + j] (6:8: 12 per 8, 14:16: 28 per 16).
   * Output: y = acc * gamma * scale_t evaluated in fp64, rounded to fp32.
 
 Packed layout (layout id 1), the format of the library's packed buffers:
-  A *slot* is one kept weight.  SPARSE layout (2:4, or 6:8 lifted into 2:4
-  windows): each 4-wide window j of a row's (lifted) K axis holds slots 2j and
+  A *slot* is one kept weight.  SPARSE layout (2:4, or 6:8 / 14:16 lifted into
+  2:4 windows): each 4-wide window j of a row's (lifted) K axis holds slots 2j and
   2j+1 -- the kept positions in ascending order -- with a 2-bit ternary code
   (00 = 0, 01 = +1, 11 = -1) and a 2-bit position index 0..3 within the window.
   DENSE2 layout: every position is a slot with a 2-bit code and no index.
@@ -56,11 +58,12 @@ Pinned functions (tests/test_oracle_*.py) and what pins them:
   nm_mask            exhaustive subset search on tie-heavy groups
   ternarize          worked example with an exact half, the closed-form
                      threshold |w| * 2^25 > gamma * (2^24 + 1), sign symmetry
-  window_table_68    the worked example; every valid 6:8 mask reconstructs
+  window_table       worked examples (6:8, 14:16); every valid 6:8 and 14:16
+                     mask is decomposed and reconstructs
   pack / unpack      hand-encoded dwords (tests/golden), round trip
   act_quant          worked example with exact halves, invariants
   acc_dense          brute-force Python loops on tiny inputs; agrees with the
-                     add/sub form acc_addsub; 6:8 lifted == dense
+                     add/sub form acc_addsub; 6:8 and 14:16 lifted == dense
   rescale            zero case and exact small products
 """
 from __future__ import annotations
@@ -80,8 +83,9 @@ PAD_META = 0x44444444     # meta dword of a padded row: every window (0, 1)
 __all__ = [
     "LAYOUT_SPARSE", "LAYOUT_DENSE2", "QB", "PAD_META",
     "round_ratio_to_f32", "absmean_gamma", "nm_mask", "ternarize", "effective_weights",
-    "window_table_68", "k_eff", "packed_dwords", "weight_slots", "pack", "unpack_slots",
-    "slots_to_dense", "act_quant", "lift_68", "acc_dense", "acc_addsub", "rescale", "forward",
+    "WINDOW_M", "window_table", "window_table_68", "k_eff", "packed_dwords", "weight_slots",
+    "pack", "unpack_slots", "slots_to_dense", "act_quant", "lift", "lift_68", "acc_dense",
+    "acc_addsub", "rescale", "forward",
 ]
 
 
@@ -186,31 +190,50 @@ def effective_weights(W: np.ndarray, N: int, M: int) -> Tuple[np.ndarray, np.flo
 
 
 # ----------------------------------------------------------------------------------------------
-# 6:8 sliding windows ([SS] Sliding Window Decomposition)
+# (2N-2):2N sliding windows ([SS] Sliding Window Decomposition): 6:8 and 14:16
 # ----------------------------------------------------------------------------------------------
 
+WINDOW_M = (8, 16)        # group sizes M = 2N decomposed into N - 1 overlapping 2:4 windows
+
+
+def _assign_windows(kept: List[int], M: int) -> List[List[int]]:
+    """Kept positions of an M-group (M - 2 of them) -> positions per window.
+
+    Window w (0 <= w < M/2 - 1) covers positions 2w..2w+3.  Positions are taken in ascending
+    order, each by the lowest window that covers it and still holds fewer than two.
+    """
+    nw = M // 2 - 1
+    assert len(kept) == M - 2
+    wins: List[List[int]] = [[] for _ in range(nw)]
+    for p in sorted(kept):
+        for w in range(nw):
+            if 2 * w <= p <= 2 * w + 3 and len(wins[w]) < 2:
+                wins[w].append(p)
+                break
+        else:
+            raise AssertionError(f"no window for position {p} of {sorted(kept)}")
+    assert all(len(w) == 2 for w in wins), kept
+    return wins
+
+
 def _assign_windows_68(kept: List[int]) -> List[List[int]]:
-    """Greedy assignment of the 6 kept positions of an 8-group to windows 0..3, 2..5, 4..7."""
-    assert len(kept) == 6
-    kept = sorted(kept)
-    w0 = [p for p in kept if p <= 3][:2]
-    rest = [p for p in kept if p not in w0]
-    w1 = [p for p in rest if 2 <= p <= 5][:2]
-    w2 = [p for p in rest if p not in w1]
-    assert len(w0) == 2 and len(w1) == 2 and len(w2) == 2, kept
-    assert all(4 <= p <= 7 for p in w2)
-    return [w0, w1, w2]
+    """6:8 case of _assign_windows (windows 0..3, 2..5, 4..7)."""
+    return _assign_windows(kept, 8)
+
+
+def window_table(M: int) -> Dict[int, List[List[int]]]:
+    """keep-bitmask of an M-group (bit p = position p kept) -> positions per window."""
+    table = {}
+    for drop in range(M):
+        for drop2 in range(drop + 1, M):
+            kept = [p for p in range(M) if p not in (drop, drop2)]
+            mask = sum(1 << p for p in kept)
+            table[mask] = _assign_windows(kept, M)
+    return table
 
 
 def window_table_68() -> Dict[int, List[List[int]]]:
-    """keep-bitmask of an 8-group (bit p = position p kept) -> positions per window."""
-    table = {}
-    for drop in range(8):
-        for drop2 in range(drop + 1, 8):
-            kept = [p for p in range(8) if p not in (drop, drop2)]
-            mask = sum(1 << p for p in kept)
-            table[mask] = _assign_windows_68(kept)
-    return table
+    return window_table(8)
 
 
 # ----------------------------------------------------------------------------------------------
@@ -218,14 +241,15 @@ def window_table_68() -> Dict[int, List[List[int]]]:
 # ----------------------------------------------------------------------------------------------
 
 def k_eff(K: int, N: int, M: int, layout: int) -> int:
-    """Length of the packed K axis: K for 2:4 and DENSE2, 3K/2 for 6:8 windows."""
+    """Length of the packed K axis: K for 2:4 and DENSE2, (2M - 4) K / M for (M-2):M windows
+    (3K/2 for 6:8, 7K/4 for 14:16)."""
     if layout == LAYOUT_DENSE2:
         return K
     if (N, M) == (2, 4):
         return K
-    if (N, M) == (6, 8):
-        return K * 3 // 2
-    raise ValueError("SPARSE layout supports 2:4 and 6:8")
+    if M in WINDOW_M and N == M - 2:
+        return K * (2 * M - 4) // M
+    raise ValueError("SPARSE layout supports 2:4, 6:8 and 14:16")
 
 
 def packed_dwords(n: int, K: int, N: int, M: int, layout: int) -> Tuple[int, int, int]:
@@ -249,21 +273,21 @@ def weight_slots(W_eff: np.ndarray, keep: np.ndarray, N: int, M: int, layout: in
         pos = np.argsort(~kg, axis=-1, kind="stable")[..., :2]          # kept positions, ascending
         vals = np.take_along_axis(W_eff.reshape(n, K // 4, 4), pos, axis=-1)
         return vals.reshape(n, K // 2).astype(np.int8), pos.reshape(n, K // 2).astype(np.uint8)
-    if (N, M) == (6, 8):
-        table = window_table_68()
-        G = K // 8
-        kg = keep.reshape(n, G, 8)
-        bitmask = (kg.astype(np.int64) << np.arange(8)).sum(axis=-1)
-        # dense position (0..7) of each of the 6 slots per group, for every valid bitmask
-        lut = np.zeros((256, 6), dtype=np.int64)
+    if M in WINDOW_M and N == M - 2:
+        table = window_table(M)
+        G = K // M
+        kg = keep.reshape(n, G, M)
+        bitmask = (kg.astype(np.int64) << np.arange(M)).sum(axis=-1)
+        # dense position (0..M-1) of each of the M-2 slots per group, for every valid bitmask
+        lut = np.zeros((1 << M, N), dtype=np.int64)
         for msk, wins in table.items():
             lut[msk] = [p for w in wins for p in w]
         assert np.all(np.isin(bitmask, list(table.keys())))
-        pos = lut[bitmask]                                                # [n][G][6]
-        vals = np.take_along_axis(W_eff.reshape(n, G, 8), pos, axis=-1)
-        window_start = np.array([0, 0, 2, 2, 4, 4])
+        pos = lut[bitmask]                                                # [n][G][M-2]
+        vals = np.take_along_axis(W_eff.reshape(n, G, M), pos, axis=-1)
+        window_start = 2 * (np.arange(N) // 2)                            # 0,0,2,2,4,4,...
         local = pos - window_start
-        return vals.reshape(n, G * 6).astype(np.int8), local.reshape(n, G * 6).astype(np.uint8)
+        return vals.reshape(n, G * N).astype(np.int8), local.reshape(n, G * N).astype(np.uint8)
     raise ValueError("unsupported N:M")
 
 
@@ -345,8 +369,9 @@ def slots_to_dense(vals: np.ndarray, idx, K: int, N: int, M: int, layout: int) -
     if (N, M) == (2, 4):
         dense_pos = lifted_pos
     else:
-        g, rem = lifted_pos // 12, lifted_pos % 12                        # 12 lifted per 8 dense
-        dense_pos = 8 * g + 2 * (rem // 4) + (rem % 4)
+        L = 2 * M - 4                                                     # lifted per M dense
+        g, rem = lifted_pos // L, lifted_pos % L
+        dense_pos = M * g + 2 * (rem // 4) + (rem % 4)
     out = np.zeros((n, K), dtype=np.int64)
     rows = np.repeat(np.arange(n)[:, None], S, axis=1)
     np.add.at(out, (rows, dense_pos), vals.astype(np.int64))
@@ -358,13 +383,18 @@ def slots_to_dense(vals: np.ndarray, idx, K: int, N: int, M: int, layout: int) -
 # [SS] Activation Lifting for 6:8)
 # ----------------------------------------------------------------------------------------------
 
+def lift(q: np.ndarray, M: int) -> np.ndarray:
+    """x'[t][(2M-4)g + 4w + j] = x[t][Mg + 2w + j], w = 0..M/2-2, j = 0..3."""
+    T, K = q.shape
+    G = K // M
+    src = np.array([2 * w + j for w in range(M // 2 - 1) for j in range(4)])   # 2M-4 per group
+    cols = (M * np.arange(G)[:, None] + src[None, :]).reshape(-1)
+    return q[:, cols]
+
+
 def lift_68(q: np.ndarray) -> np.ndarray:
     """x'[t][12g + 4w + j] = x[t][8g + 2w + j], w = 0..2, j = 0..3."""
-    T, K = q.shape
-    G = K // 8
-    src = np.array([8 * 0 + 2 * w + j for w in range(3) for j in range(4)])   # 12 per group
-    cols = (8 * np.arange(G)[:, None] + src[None, :]).reshape(-1)
-    return q[:, cols]
+    return lift(q, 8)
 
 
 def act_quant(x: np.ndarray, lift_M: int = 0) -> Tuple[np.ndarray, np.ndarray]:
@@ -378,8 +408,8 @@ def act_quant(x: np.ndarray, lift_M: int = 0) -> Tuple[np.ndarray, np.ndarray]:
     q = np.clip(np.rint(prod), -QB, QB).astype(np.int8)
     scale = (absmax / np.float32(QB)).astype(np.float32)
     scale[~nz] = 0.0
-    if lift_M == 8:
-        q = lift_68(q)
+    if lift_M in WINDOW_M:
+        q = lift(q, lift_M)
     else:
         assert lift_M == 0
     return q, scale
@@ -398,7 +428,7 @@ def acc_dense(W_eff: np.ndarray, q: np.ndarray) -> np.ndarray:
 def acc_addsub(vals: np.ndarray, idx, xq: np.ndarray, layout: int) -> np.ndarray:
     """Form ii: per slot, add the activation under a +1 code, subtract it under a -1 code.
 
-    ``xq`` is on the packed K axis (lifted for 6:8).
+    ``xq`` is on the packed K axis (lifted for 6:8 and 14:16).
     """
     T = xq.shape[0]
     n, S = vals.shape
@@ -424,7 +454,7 @@ def rescale(acc: np.ndarray, gamma: np.float32, scale: np.ndarray) -> np.ndarray
 def forward(W: np.ndarray, x: np.ndarray, N: int, M: int, layout: int = LAYOUT_SPARSE) -> Dict:
     """Whole path: pack the master, quantize (and lift) x, accumulate, rescale."""
     p = pack(W, N, M, layout)
-    lift = 8 if (layout == LAYOUT_SPARSE and (N, M) == (6, 8)) else 0
+    lift = M if (layout == LAYOUT_SPARSE and M in WINDOW_M) else 0
     xq, scale = act_quant(x, lift)
     acc = acc_dense(p["W_eff"], act_quant(x, 0)[0])
     y = rescale(acc, p["gamma"], scale)

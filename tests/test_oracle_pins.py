@@ -207,12 +207,26 @@ def test_windows_golden():
             assert wins[w] == [int(v) for v in kv[f"w{w}{sfx}"]]
 
 
-def test_windows_cover_every_mask():
-    table = O.window_table_68()
-    assert len(table) == 28
+def test_windows_1416_golden():
+    kv = read_kv("windows_1416.txt")
+    table = O.window_table(16)
+    for sfx in ("", "_b", "_c"):
+        kept = [int(v) for v in kv["kept" + sfx]]
+        wins = table[sum(1 << p for p in kept)]
+        for w in range(7):
+            assert wins[w] == [int(v) for v in kv[f"w{w}{sfx}"]]
+
+
+@pytest.mark.parametrize("M,count", [(8, 28), (16, 120)])
+def test_windows_cover_every_mask(M, count):
+    """Every (M-2):M mask splits into M/2 - 1 windows of two kept positions each, each position
+    inside its window's span (the decomposition is lossless for every mask)."""
+    table = O.window_table(M)
+    assert len(table) == count
     for mask, wins in table.items():
+        assert len(wins) == M // 2 - 1
         flat = sorted(p for w in wins for p in w)
-        assert flat == [p for p in range(8) if mask >> p & 1]
+        assert flat == [p for p in range(M) if mask >> p & 1]
         for w, ps in enumerate(wins):
             assert len(ps) == 2 and all(2 * w <= p <= 2 * w + 3 for p in ps)
 
@@ -243,7 +257,8 @@ def test_pack_golden_unit():
 
 
 @pytest.mark.parametrize("N,M,layout", [(2, 4, O.LAYOUT_SPARSE), (6, 8, O.LAYOUT_SPARSE),
-                                        (2, 4, O.LAYOUT_DENSE2), (6, 8, O.LAYOUT_DENSE2)])
+                                        (14, 16, O.LAYOUT_SPARSE), (2, 4, O.LAYOUT_DENSE2),
+                                        (6, 8, O.LAYOUT_DENSE2), (14, 16, O.LAYOUT_DENSE2)])
 def test_pack_roundtrip(N, M, layout):
     g = np.random.default_rng(N + M + layout)
     n, K = 45, 256
@@ -297,6 +312,17 @@ def test_act_quant_close_to_real_rounding():
     assert np.all(np.abs(np.abs(real[diff] - np.floor(real[diff])) - 0.5) < 1e-4)
 
 
+def test_lift_1416():
+    kv = read_kv("windows_1416.txt")
+    q = np.arange(2 * 32, dtype=np.int64).reshape(2, 32).astype(np.int8)
+    L = O.lift(q, 16)
+    assert L.shape == (2, 56)
+    want = [int(v) for v in kv["lift16"]]
+    assert L[0, :28].tolist() == want
+    assert L[0, 28:].tolist() == [16 + v for v in want]
+    assert O.k_eff(256, 14, 16, O.LAYOUT_SPARSE) == 448
+
+
 def test_lift_68():
     q = np.arange(2 * 16, dtype=np.int64).reshape(2, 16).astype(np.int8)
     L = O.lift_68(q)
@@ -322,16 +348,18 @@ def test_acc_bruteforce_tiny():
 
 
 @pytest.mark.parametrize("N,M,layout", [(2, 4, O.LAYOUT_SPARSE), (6, 8, O.LAYOUT_SPARSE),
-                                        (2, 4, O.LAYOUT_DENSE2)])
+                                        (14, 16, O.LAYOUT_SPARSE), (2, 4, O.LAYOUT_DENSE2),
+                                        (14, 16, O.LAYOUT_DENSE2)])
 def test_acc_forms_agree(N, M, layout):
     """Form i (dense int64 matmul of W_eff) equals form ii (add/sub over packed slots); for 6:8
-    the lifted 2:4 windows against lifted activations equal the dense product (lossless)."""
+    and 14:16 the lifted 2:4 windows against lifted activations equal the dense product
+    (lossless)."""
     g = np.random.default_rng(20 + N)
     n, K, T = 40, 256, 9
     W = g.normal(0, 0.02, (n, K)).astype(np.float32)
     x = g.standard_normal((T, K)).astype(np.float32)
     p = O.pack(W, N, M, layout)
-    lift = 8 if (layout == O.LAYOUT_SPARSE and M == 8) else 0
+    lift = M if (layout == O.LAYOUT_SPARSE and M in (8, 16)) else 0
     xq, _ = O.act_quant(x, lift)
     q, _ = O.act_quant(x, 0)
     vals, idx = O.unpack_slots(p["codes"], p["meta"], n, K, N, M, layout)
