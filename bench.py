@@ -19,6 +19,9 @@ Also in the same JSON line:
                 from the committed rocprofv3 counter summary when it was taken on the current
                 kernel source (else null)
   prefill       4096 x 4096 -> 11008 2:4 GEMM (Student-t activations): dense-equivalent int8 TOPS
+  six_eight, fourteen_sixteen
+                (2N-2):2N through overlapping 2:4 windows vs the dense path, 2048 x 4096 -> 4096
+  train_step    the 3B-alike layer set at 8192 tokens: pack, act_quant and forward
   cpu_baseline  the CPU oracle on a bounded sample of the same decode workload
 """
 from __future__ import annotations
@@ -57,7 +60,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
-    ap.add_argument("--no-extra", action="store_true", help="skip the 6:8 and training-step legs")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the 6:8, 14:16 and training-step legs")
     ap.add_argument("--cpu-budget-s", type=float, default=15.0)
     ap.add_argument("--profile-pass", choices=("decode", "prefill", "train"), default=None,
                     help="for hardware-counter runs, no graph and no JSON line.  decode: two eager "
@@ -200,33 +204,35 @@ def _event_ms(torch, fn, iters):
     return float(np.mean([a.elapsed_time(b) for a, b in ev]))
 
 
-def six_eight_leg(S, torch, iters=10):
-    """6:8 through three overlapping 2:4 windows (lifted activations, sparse MFMA) against the
-    dense-stored path of the same masked ternary weights (dense MFMA): 2048 x 4096 -> 4096."""
+def windows_leg(S, torch, N, M, iters=10):
+    """(M-2):M through M/2 - 1 overlapping 2:4 windows (lifted activations, sparse MFMA) against
+    the dense-stored path of the same masked ternary weights (dense MFMA): 2048 x 4096 -> 4096."""
     n, K, T = 4096, 4096, 2048
     g = torch.Generator(device="cuda")
-    g.manual_seed(68)
+    g.manual_seed(68 if M == 8 else 1416)
     W = (torch.randn((n, K), generator=g, device="cuda", dtype=torch.float32) * 0.02).contiguous()
-    cs, ms, gs = S.pack(W, 6, 8, S.BL_LAYOUT_SPARSE)
-    cd, _, gd = S.pack(W, 6, 8, S.BL_LAYOUT_DENSE2)
+    cs, ms, gs = S.pack(W, N, M, S.BL_LAYOUT_SPARSE)
+    cd, _, gd = S.pack(W, N, M, S.BL_LAYOUT_DENSE2)
     del W
     x = torch.randn((T, K), generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
-    xl, sl = S.act_quant(x, 8)
+    xl, sl = S.act_quant(x, M)
     xd, sd = S.act_quant(x, 0)
     ys = torch.empty((T, n), dtype=torch.float32, device="cuda")
     yd = torch.empty((T, n), dtype=torch.float32, device="cuda")
-    t_s = _event_ms(torch, lambda: S.fwd(xl, sl, K, cs, ms, gs, n, 6, 8, S.BL_LAYOUT_SPARSE,
+    t_s = _event_ms(torch, lambda: S.fwd(xl, sl, K, cs, ms, gs, n, N, M, S.BL_LAYOUT_SPARSE,
                                          out=(ys, None)), iters)
-    t_d = _event_ms(torch, lambda: S.fwd(xd, sd, K, cd, None, gd, n, 6, 8, S.BL_LAYOUT_DENSE2,
+    t_d = _event_ms(torch, lambda: S.fwd(xd, sd, K, cd, None, gd, n, N, M, S.BL_LAYOUT_DENSE2,
                                          out=(yd, None)), iters)
-    t_ql = _event_ms(torch, lambda: S.act_quant(x, 8, out=(xl, sl)), iters)
+    t_ql = _event_ms(torch, lambda: S.act_quant(x, M, out=(xl, sl)), iters)
     t_qd = _event_ms(torch, lambda: S.act_quant(x, 0, out=(xd, sd)), iters)
     torch.cuda.synchronize()
     same = bool(torch.equal(ys, yd))   # same masked ternary product, bit for bit, at full size
     if not same:
-        raise RuntimeError("6:8 window path and dense path disagree")
+        raise RuntimeError(f"{N}:{M} window path and dense path disagree")
     ops = 2.0 * T * K * n
-    return {"workload": "6:8 as 3 overlapping 2:4 windows, 2048 tokens x 4096 -> 4096, N(0,1) bf16",
+    windows = M // 2 - 1
+    return {"workload": f"{N}:{M} as {windows} overlapping 2:4 windows, 2048 tokens x 4096 -> 4096, "
+                        "N(0,1) bf16",
             "windows_TOPS": round(ops / (t_s * 1e-3) / 1e12, 1),
             "dense_TOPS": round(ops / (t_d * 1e-3) / 1e12, 1),
             "gemm_ms": {"windows": round(t_s, 4), "dense": round(t_d, 4)},
@@ -236,7 +242,8 @@ def six_eight_leg(S, torch, iters=10):
                          "dense": {"bound": "mfma", "peak": MFMA_I8_PEAK_TOPS, "unit": "TOPS",
                                    "frac": round(ops / (t_d * 1e-3) / 1e12 / MFMA_I8_PEAK_TOPS, 4)}},
             "speedup_vs_dense": round(t_d / t_s, 3),
-            "speedup_with_quant": round((t_d + t_qd) / (t_s + t_ql), 3), "bound": round(4 / 3, 3),
+            "speedup_with_quant": round((t_d + t_qd) / (t_s + t_ql), 3),
+            "bound": round((M // 2) / (M // 2 - 1), 3),
             "outputs_identical": same}
 
 
@@ -465,9 +472,10 @@ def main():
         out["prefill"] = prefill_leg(S, torch)
         log(f"prefill {out['prefill']['value']} TOPS")
     if not args.no_extra:
-        log("6:8 leg")
-        out["six_eight"] = six_eight_leg(S, torch)
-        log(f"6:8 windows {out['six_eight']['windows_TOPS']} TOPS, dense {out['six_eight']['dense_TOPS']} TOPS")
+        for key, N, M in (("six_eight", 6, 8), ("fourteen_sixteen", 14, 16)):
+            log(f"{N}:{M} leg")
+            out[key] = windows_leg(S, torch, N, M)
+            log(f"{N}:{M} windows {out[key]['windows_TOPS']} TOPS, dense {out[key]['dense_TOPS']} TOPS")
         log("training-step layer set leg")
         out["train_step"] = train_step_leg(S, torch)
         log(f"train step {out['train_step']['step_ms']} ms")

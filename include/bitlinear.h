@@ -10,9 +10,10 @@
  *     technical summary section 2 (Sparse-BitLinear): an N:M mask keeps the N largest |w| of
  *     the continuous master weights in every group of M, recomputed at every training step,
  *     and is applied to the ternary weights (quantize, then mask).
- *   - SlideSparse abstract on "Is 2:4 Sparsity Still Worth It? ...": a 6:8 block is rewritten
- *     losslessly as 3 overlapping 2:4 windows (Sliding Window Decomposition), and the
- *     activations are rearranged to match inside per-token quantization (Activation Lifting).
+ *   - SlideSparse abstract on "Is 2:4 Sparsity Still Worth It? ...": a (2N-2):2N block (6:8,
+ *     14:16) is rewritten losslessly as N-1 overlapping 2:4 windows (Sliding Window
+ *     Decomposition), and the activations are rearranged to match inside per-token
+ *     quantization (Activation Lifting).
  *
  * y[t][o] = gamma * scale[t] * sum_k W_eff[o][k] * xq[t][k]   (int32 accumulation, fp32 out)
  * with W_eff = mask(W) * RoundClip(W / gamma) and (xq, scale) the int8 activations.
@@ -30,10 +31,12 @@
  * Packed weight layout (layout id BL_LAYOUT_VERSION = 1)
  *   slot    one kept weight.  BL_LAYOUT_SPARSE: each 4-wide window j of a row's packed K axis
  *           holds slots 2j, 2j+1 = its two kept positions in ascending order; 2:4 windows are
- *           the M-groups, 6:8 groups become 3 windows covering positions 0-3, 2-5, 4-7 of the
- *           group (packed K axis K_eff = 3K/2; greedy assignment in ascending position order:
- *           window 0 takes up to 2 kept positions in 0-3, window 1 up to 2 of the rest in 2-5,
- *           window 2 the rest).  BL_LAYOUT_DENSE2: every position is a slot (K_eff = K).
+ *           the M-groups; an (M-2):M group (6:8, 14:16) becomes M/2 - 1 windows, window w
+ *           covering positions 2w..2w+3 of the group (packed K axis K_eff = (2M-4)K/M: 3K/2
+ *           for 6:8, 7K/4 for 14:16).  Assignment: kept positions in ascending order, each to
+ *           the lowest window that covers it and holds fewer than two (for 6:8: window 0 takes
+ *           up to 2 kept positions in 0-3, window 1 up to 2 of the rest in 2-5, window 2 the
+ *           rest).  BL_LAYOUT_DENSE2: every position is a slot (K_eff = K).
  *   code    2 bits per slot: 00 = 0, 01 = +1, 11 = -1 (10 is never written).
  *   index   2 bits per slot (SPARSE only): the slot's position 0..3 inside its window.
  *   unit    16 consecutive slots of one row = one little-endian code dword (slot i at bits
@@ -45,7 +48,8 @@
  *           or dense MFMA 32x32x32 (DENSE2) instruction: lane = (c%2)*32 + r%32.
  *
  * Shapes: n >= 1 (out features), K (in features): SPARSE 2:4 needs K % 64 == 0; SPARSE 6:8
- * needs K % 128 == 0; DENSE2 needs K % 32 == 0 and K % M == 0 with M in {4, 8}, 1 <= N <= M.
+ * needs K % 128 == 0; SPARSE 14:16 needs K % 256 == 0; DENSE2 needs K % 32 == 0 and K % M == 0
+ * with M in {4, 8, 16}, 1 <= N <= M.
  * n * K < 2^32.  K_eff * 127 < 2^31.  T >= 0 tokens (T == 0 enqueues nothing), T * K_eff < 2^31.
  *
  * Conventions for every call:
@@ -99,14 +103,15 @@ int bitlinear_pack(const float* W, int64_t n, int64_t K, int N, int M, int layou
 
 /* Per-token absmax int8 quantization of x[T][K] (row-major; x_dtype BL_DTYPE_F32 or
  * BL_DTYPE_BF16).  Writes xq[T][K_eff] int8 and x_scale[T] fp32 (absmax/127).
- * lift_M = 0: K_eff = K.  lift_M = 8: activation lifting for 6:8 windows, K_eff = 3K/2,
- * xq[t][12g + 4w + j] = q[t][8g + 2w + j] (w = 0..2, j = 0..3); needs K % 8 == 0. */
+ * lift_M = 0: K_eff = K.  lift_M = 8 or 16: activation lifting for (M-2):M windows,
+ * K_eff = (2M-4)K/M, xq[t][(2M-4)g + 4w + j] = q[t][Mg + 2w + j] (w = 0..M/2-2, j = 0..3);
+ * needs K % 8 == 0 (and K % 16 == 0 for lift_M = 16). */
 int act_quant_i8(const void* x, int x_dtype, int64_t T, int64_t K, int lift_M, int8_t* xq,
                  float* x_scale, void* stream);
 
 /* y[T][n] fp32 = gamma * x_scale[t] * (xq[T][K_eff] . W_eff^T), int32 accumulation.
  * K is the master's in-feature count; (N, M, layout) must be those the weights were packed
- * with, and xq must be on the packed K axis (lifted with lift_M = 8 for SPARSE 6:8).
+ * with, and xq must be on the packed K axis (lifted with lift_M = M for SPARSE 6:8 and 14:16).
  * gamma is the device scalar written by bitlinear_pack.  acc_opt, if not NULL, receives the
  * int32 accumulators [T][n] (4-byte alignment suffices for it). */
 int bitlinear_fwd(const int8_t* xq, const float* x_scale, int64_t T, int64_t K,

@@ -167,7 +167,7 @@ def act_quant(x, lift_M: int = 0, out=None):
     assert x.is_cuda and x.is_contiguous() and x.dim() == 2
     T, K = x.shape
     dt = {torch.float32: BL_DTYPE_F32, torch.bfloat16: BL_DTYPE_BF16}[x.dtype]
-    ke = K // 2 * 3 if lift_M == 8 else K
+    ke = K // lift_M * (2 * lift_M - 4) if lift_M else K
     if out is None:
         xq = torch.empty((T, ke), dtype=torch.int8, device=x.device)
         scale = torch.empty(max(T, 4), dtype=torch.float32, device=x.device)[:T]

@@ -15,20 +15,27 @@ namespace {
 bool aligned16(const void* p) { return p && ((uintptr_t)p & 15u) == 0; }
 bool aligned4(const void* p) { return p && ((uintptr_t)p & 3u) == 0; }
 
+// Packed K axis: K for 2:4 and DENSE2; (2M - 4) K / M for (M-2):M windows (6:8: 3K/2, 14:16:
+// 7K/4).
+int64_t keff_of(int64_t K, int M, int layout) {
+  return (layout == BL_LAYOUT_SPARSE && M > 4) ? K / M * (2 * M - 4) : K;
+}
+
 // Shape rules of the packed layout; returns BL_OK and the packed K axis, or a status.
 int check_shape(int64_t n, int64_t K, int N, int M, int layout, int64_t* keff) {
   if (layout != BL_LAYOUT_SPARSE && layout != BL_LAYOUT_DENSE2) return BL_ENOTSUP;
   if (layout == BL_LAYOUT_SPARSE) {
-    if (!((N == 2 && M == 4) || (N == 6 && M == 8))) return BL_ENOTSUP;
+    if (!((N == 2 && M == 4) || (N == 6 && M == 8) || (N == 14 && M == 16))) return BL_ENOTSUP;
   } else {
-    if (!(M == 4 || M == 8) || N < 1 || N > M) return BL_ENOTSUP;
+    if (!(M == 4 || M == 8 || M == 16) || N < 1 || N > M) return BL_ENOTSUP;
   }
   if (n < 1 || K < 1) return BL_EINVAL;
-  const int64_t kq = layout == BL_LAYOUT_DENSE2 ? 32 : (M == 4 ? 64 : 128);
-  if (K % kq != 0) return BL_EINVAL;
+  // whole 64-position sparse MFMA steps on the packed axis (and whole 32-position dense steps)
+  const int64_t kq = layout == BL_LAYOUT_DENSE2 ? 32 : (M == 4 ? 64 : M == 8 ? 128 : 256);
+  if (K % kq != 0 || K % M != 0) return BL_EINVAL;
   if (n > INT32_MAX || K > INT32_MAX) return BL_EINVAL;
   if ((uint64_t)n * (uint64_t)K >= (1ull << 32)) return BL_EINVAL;
-  const int64_t ke = (layout == BL_LAYOUT_SPARSE && M == 8) ? K / 2 * 3 : K;
+  const int64_t ke = keff_of(K, M, layout);
   if (ke * 127 >= (int64_t)INT32_MAX) return BL_EINVAL;
   *keff = ke;
   return BL_OK;
@@ -153,7 +160,8 @@ int bitlinear_pack(const float* W, int64_t n, int64_t K, int N, int M, int layou
 int act_quant_i8(const void* x, int x_dtype, int64_t T, int64_t K, int lift_M, int8_t* xq,
                  float* x_scale, void* stream) {
   if (x_dtype != BL_DTYPE_F32 && x_dtype != BL_DTYPE_BF16) return BL_ENOTSUP;
-  if (lift_M != 0 && lift_M != 8) return BL_EINVAL;
+  if (lift_M != 0 && lift_M != 8 && lift_M != 16) return BL_EINVAL;
+  if (lift_M == 16 && K % 16 != 0) return BL_EINVAL;
   if (T < 0 || T > INT32_MAX || K < 8 || K % 8 != 0 || K > (int64_t)1 << 24) return BL_EINVAL;
   if (T == 0) return BL_OK;  // nothing is read or written; pointers may be NULL
   if (!aligned16(x) || !aligned16(xq) || !aligned4(x_scale)) return BL_EINVAL;
@@ -202,7 +210,7 @@ int bitlinear_group_build(const bl_fwd_desc* descs, int64_t count, int N, int M,
   bl::GroupLayer* rec = (bl::GroupLayer*)(img.data() + sizeof hdr);
   for (int64_t i = 0; i < count; ++i) {
     const bl_fwd_desc& d = descs[i];
-    const int64_t ke = (layout == BL_LAYOUT_SPARSE && M == 8) ? d.K / 2 * 3 : d.K;
+    const int64_t ke = keff_of(d.K, M, layout);
     bl::GroupLayer r;
     memset(&r, 0, sizeof r);
     r.xq = d.xq;
@@ -229,7 +237,7 @@ int bitlinear_group_build(const bl_fwd_desc* descs, int64_t count, int N, int M,
 int bitlinear_fwd_group(const void* table, int64_t work_items, int N, int M, int layout,
                         void* stream) {
   int64_t ke = 0;
-  const int st = check_shape(1, 128, N, M, layout, &ke);  // N:M and layout only
+  const int st = check_shape(1, 256, N, M, layout, &ke);  // N:M and layout only
   if (st != BL_OK) return st;
   if (work_items < 0 || work_items > INT32_MAX) return BL_EINVAL;
   if (work_items == 0) return BL_OK;

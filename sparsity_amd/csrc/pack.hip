@@ -3,8 +3,8 @@
 // gamma is the mean |W| over the whole dense master (BitNet b1.58 page, "The mechanism",
 // absmean quantization), taken before the mask (Sparse-BitNet technical summary, section 2,
 // Forward Pass: quantize, then mask).  The mask keeps the N largest |w| of the continuous master
-// in each M-group (same summary, Maskering) and 6:8 groups are rewritten as three overlapping
-// 2:4 windows (SlideSparse abstract, Sliding Window Decomposition).
+// in each M-group (same summary, Maskering) and (2N-2):2N groups -- 6:8, 14:16 -- are rewritten
+// as N-1 overlapping 2:4 windows (SlideSparse abstract, Sliding Window Decomposition).
 //
 // Two launches, both on the caller's stream:
 //   1. gamma_partial_kernel   fp64 partial sums of |w| (HBM-bound read of W)
@@ -203,7 +203,8 @@ __global__ __launch_bounds__(256) void pack_kernel(const float* __restrict__ W, 
                                                    uint32_t* __restrict__ meta) {
   constexpr bool SP = LAYOUT == kLayoutSparse;
   constexpr int WS = kPackKB + 4;                                      // padded fp32 row
-  constexpr int SLOTS = SP ? (M == 4 ? kPackKB / 2 : kPackKB * 3 / 4) : kPackKB;
+  constexpr int NKEEP = M == 4 ? 2 : M - 2;                           // SPARSE: 2:4, 6:8, 14:16
+  constexpr int SLOTS = SP ? kPackKB * NKEEP / M : kPackKB;
   constexpr int SS = SLOTS + 16;                                       // padded slot row
   constexpr int GPR = kPackKB / M;                                     // groups per tile row
   constexpr int UPR = SLOTS / 16;                                      // units per tile row
@@ -253,7 +254,7 @@ __global__ __launch_bounds__(256) void pack_kernel(const float* __restrict__ W, 
   const float tau = tau_sh;
   __syncthreads();
 
-  const int nkeep = SP ? (M == 4 ? 2 : 6) : N;
+  const int nkeep = SP ? NKEEP : N;
   for (int gid = threadIdx.x; gid < 32 * GPR; gid += 256) {
     const int row = gid / GPR, g = gid % GPR;
     float w[M];
@@ -279,18 +280,23 @@ __global__ __launch_bounds__(256) void pack_kernel(const float* __restrict__ W, 
 #pragma unroll
       for (int p = 0; p < 4; ++p)
         if (keep >> p & 1u) { out[2 * g + s] = (uint8_t)(code(p) | (p << 2)); ++s; }
-    } else if constexpr (SP && M == 8) {
-      // windows 0-3, 2-5, 4-7; ascending positions, each window takes at most two
-      int c0 = 0, c1 = 0, c2 = 0;
+    } else if constexpr (SP) {
+      // (M-2):M into M/2 - 1 windows covering positions 2w..2w+3: kept positions in ascending
+      // order, each to the lowest window that covers it and holds fewer than two (position p
+      // is covered by windows (p - 2) / 2 and p / 2, clipped to the window range)
+      constexpr int NWIN = M / 2 - 1;
+      int cnt[NWIN];
 #pragma unroll
-      for (int p = 0; p < 8; ++p) {
+      for (int w = 0; w < NWIN; ++w) cnt[w] = 0;
+#pragma unroll
+      for (int p = 0; p < M; ++p) {
         if (!(keep >> p & 1u)) continue;
-        int wdw;
-        if (p <= 3 && c0 < 2) { wdw = 0; ++c0; }
-        else if (p <= 5 && c1 < 2) { wdw = 1; ++c1; }
-        else { wdw = 2; ++c2; }
-        const int slot = 2 * wdw + (wdw == 0 ? c0 : wdw == 1 ? c1 : c2) - 1;
-        out[6 * g + slot] = (uint8_t)(code(p) | ((p - 2 * wdw) << 2));
+        const int wlo = p >= 2 ? (p - 2) >> 1 : 0;                     // constants after unrolling
+        const int whi = (p >> 1) < NWIN - 1 ? (p >> 1) : NWIN - 1;
+        int wdw, slot;
+        if (cnt[wlo] < 2) { wdw = wlo; slot = 2 * wlo + cnt[wlo]; ++cnt[wlo]; }
+        else { wdw = whi; slot = 2 * whi + cnt[whi]; ++cnt[whi]; }
+        out[NKEEP * g + slot] = (uint8_t)(code(p) | ((p - 2 * wdw) << 2));
       }
     } else {
 #pragma unroll
@@ -299,9 +305,9 @@ __global__ __launch_bounds__(256) void pack_kernel(const float* __restrict__ W, 
   }
   __syncthreads();
 
-  const int valid_slots = SP ? (M == 4 ? kw / 2 : kw * 3 / 4) : kw;
+  const int valid_slots = SP ? kw * NKEEP / M : kw;
   const int units_valid = valid_slots / 16;
-  const int nfrag = SP ? (M == 4 ? K : K * 3 / 2) / 64 : K / 32;     // fragments per panel
+  const int nfrag = SP ? (M == 4 ? K : K / M * (2 * M - 4)) / 64 : K / 32;   // fragments per panel
   const size_t base = ((size_t)P * nfrag + (size_t)kb * (UPR / 2)) * 64;
   for (int v = threadIdx.x; v < 32 * UPR; v += 256) {
     const int u = v >> 5, r = v & 31;
@@ -328,16 +334,17 @@ hipError_t launch_pack(const float* W, int64_t n, int64_t K, int N, int M, int l
   const int panels = (int)((n + kPanel - 1) / kPanel);
   const int k_tiles = (int)((K + kPackKB - 1) / kPackKB);
   const dim3 grid((unsigned)(panels * k_tiles));
+  auto run = [&](auto kern, uint32_t* mt) {
+    kern<<<grid, 256, 0, s>>>(W, (int)n, (int)K, N, k_tiles, ws, gamma, codes, mt);
+  };
   if (layout == kLayoutSparse) {
-    if (M == 4)
-      pack_kernel<kLayoutSparse, 4><<<grid, 256, 0, s>>>(W, (int)n, (int)K, N, k_tiles, ws, gamma, codes, meta);
-    else
-      pack_kernel<kLayoutSparse, 8><<<grid, 256, 0, s>>>(W, (int)n, (int)K, N, k_tiles, ws, gamma, codes, meta);
+    if (M == 4) run(pack_kernel<kLayoutSparse, 4>, meta);
+    else if (M == 8) run(pack_kernel<kLayoutSparse, 8>, meta);
+    else run(pack_kernel<kLayoutSparse, 16>, meta);
   } else {
-    if (M == 4)
-      pack_kernel<kLayoutDense2, 4><<<grid, 256, 0, s>>>(W, (int)n, (int)K, N, k_tiles, ws, gamma, codes, nullptr);
-    else
-      pack_kernel<kLayoutDense2, 8><<<grid, 256, 0, s>>>(W, (int)n, (int)K, N, k_tiles, ws, gamma, codes, nullptr);
+    if (M == 4) run(pack_kernel<kLayoutDense2, 4>, nullptr);
+    else if (M == 8) run(pack_kernel<kLayoutDense2, 8>, nullptr);
+    else run(pack_kernel<kLayoutDense2, 16>, nullptr);
   }
   return hipGetLastError();
 }

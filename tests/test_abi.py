@@ -47,7 +47,8 @@ def test_layout_version_and_strerror(L):
 @pytest.mark.parametrize("n,K,N,M,layout", [
     (1, 64, 2, 4, 0), (6912, 2560, 2, 4, 0), (2560, 6912, 2, 4, 0), (11008, 4096, 2, 4, 0),
     (4096, 4096, 6, 8, 0), (45, 384, 6, 8, 0), (33, 288, 2, 4, 1), (33, 288, 6, 8, 1),
-    (8640, 3200, 2, 4, 0), (3200, 8640, 2, 4, 0), (100, 96, 4, 4, 1)])
+    (8640, 3200, 2, 4, 0), (3200, 8640, 2, 4, 0), (100, 96, 4, 4, 1),
+    (4096, 4096, 14, 16, 0), (45, 512, 14, 16, 0), (33, 288, 14, 16, 1)])
 def test_packed_bytes_match_layout(L, n, K, N, M, layout):
     st, cb, mb, ke, ws = L.bitlinear_packed_bytes(n, K, N, M, layout)
     assert st == 0
@@ -63,7 +64,10 @@ def test_packed_bytes_match_layout(L, n, K, N, M, layout):
     (64, 256, 3, 4, 0, -95),       # SPARSE supports 2:4 and 6:8 only
     (64, 256, 2, 4, 7, -95),       # unknown layout
     (64, 256, 5, 4, 1, -95),       # N > M
-    (64, 256, 2, 16, 1, -95),      # M in {4, 8}
+    (64, 256, 2, 32, 1, -95),      # M in {4, 8, 16}
+    (64, 128, 14, 16, 0, -22),     # 14:16 needs K % 256
+    (64, 256, 12, 16, 0, -95),     # SPARSE windows are (M-2):M
+    (64, 256, 6, 16, 0, -95),
     (1 << 20, 1 << 12, 2, 4, 0, -22),  # n*K >= 2^32
 ])
 def test_packed_bytes_rejects(L, n, K, N, M, layout, want):
@@ -97,6 +101,7 @@ def test_act_quant_rejects_before_launch(L):
     P = FAKE
     assert L.act_quant_i8(P, 2, 4, 256, 0, P, P, None) == -95        # dtype
     assert L.act_quant_i8(P, 0, 4, 256, 4, P, P, None) == -22        # lift_M
+    assert L.act_quant_i8(P, 0, 4, 264, 16, P, P, None) == -22       # lift 16 needs K % 16
     assert L.act_quant_i8(P, 0, -1, 256, 0, P, P, None) == -22       # T < 0
     assert L.act_quant_i8(P, 0, 4, 100, 0, P, P, None) == -22        # K % 8
     assert L.act_quant_i8(None, 0, 4, 256, 0, P, P, None) == -22

@@ -16,12 +16,12 @@ pytestmark = pytest.mark.gpu
 
 S = pytest.importorskip("sparsity_amd")
 
-CASES_NM = [(2, 4, O.LAYOUT_SPARSE), (6, 8, O.LAYOUT_SPARSE), (2, 4, O.LAYOUT_DENSE2),
-            (4, 4, O.LAYOUT_DENSE2)]
+CASES_NM = [(2, 4, O.LAYOUT_SPARSE), (6, 8, O.LAYOUT_SPARSE), (14, 16, O.LAYOUT_SPARSE),
+            (2, 4, O.LAYOUT_DENSE2), (4, 4, O.LAYOUT_DENSE2)]
 
 
 def _kq(N, M, layout):
-    return 32 if layout == O.LAYOUT_DENSE2 else (64 if M == 4 else 128)
+    return 32 if layout == O.LAYOUT_DENSE2 else {4: 64, 8: 128, 16: 256}[M]
 
 
 def _make(n, K, T, N, M, layout, seed, x=None):
@@ -32,7 +32,7 @@ def _make(n, K, T, N, M, layout, seed, x=None):
     if x is None:
         x = act_normal(g, max(T, 1), K)[:T]
     ref = O.pack(W, N, M, layout)
-    lift = 8 if (layout == O.LAYOUT_SPARSE and M == 8) else 0
+    lift = M if (layout == O.LAYOUT_SPARSE and M in (8, 16)) else 0
     codes, meta, gamma = S.pack(dev(W), N, M, layout)
     if T:
         xq, sc = S.act_quant(dev(x), lift)
@@ -40,7 +40,7 @@ def _make(n, K, T, N, M, layout, seed, x=None):
         acc_ref = O.acc_dense(ref["W_eff"], q)
         y_ref = O.rescale(acc_ref, ref["gamma"], s)
     else:
-        ke = K // 2 * 3 if lift else K
+        ke = K // lift * (2 * lift - 4) if lift else K
         xq = torch.zeros((0, ke), dtype=torch.int8, device="cuda")
         sc = torch.zeros(4, dtype=torch.float32, device="cuda")[:0]
         acc_ref = np.zeros((0, n), np.int64)

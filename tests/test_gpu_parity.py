@@ -17,7 +17,19 @@ pytestmark = pytest.mark.gpu
 S = pytest.importorskip("sparsity_amd")
 
 CASES_NM = [(2, 4, O.LAYOUT_SPARSE), (6, 8, O.LAYOUT_SPARSE), (2, 4, O.LAYOUT_DENSE2),
-            (6, 8, O.LAYOUT_DENSE2), (4, 4, O.LAYOUT_DENSE2)]
+            (6, 8, O.LAYOUT_DENSE2), (4, 4, O.LAYOUT_DENSE2), (14, 16, O.LAYOUT_SPARSE),
+            (14, 16, O.LAYOUT_DENSE2)]
+
+
+def _lift(N, M, layout):
+    return M if (layout == O.LAYOUT_SPARSE and M in (8, 16)) else 0
+
+
+def _kq(N, M, layout):
+    """K granularity of a layout: whole sparse-MFMA steps on the packed axis."""
+    if layout == O.LAYOUT_DENSE2:
+        return 32
+    return {4: 64, 8: 128, 16: 256}[M]
 
 
 def _pack_gpu(W, N, M, layout):
@@ -44,8 +56,8 @@ def _check_pack(W, N, M, layout):
 @pytest.mark.parametrize("N,M,layout", CASES_NM)
 @pytest.mark.parametrize("n,K", [(45, 256), (96, 384), (200, 1024), (33, 640)])
 def test_pack_random(N, M, layout, n, K):
-    if layout == O.LAYOUT_SPARSE and M == 8 and K % 128:
-        pytest.skip("6:8 windows need K % 128 == 0")
+    if K % _kq(N, M, layout):
+        pytest.skip(f"{N}:{M} windows need K % {_kq(N, M, layout)} == 0")
     W = master_weights(rng(n * 7 + K + M), n, K)
     _check_pack(W, N, M, layout)
 
@@ -108,7 +120,7 @@ def test_pack_gamma_at_fp32_midpoint(bump, want):
 # act_quant
 # ---------------------------------------------------------------------------------------------
 
-@pytest.mark.parametrize("lift", [0, 8])
+@pytest.mark.parametrize("lift", [0, 8, 16])
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
 @pytest.mark.parametrize("T,K", [(1, 256), (7, 4096), (64, 8640), (300, 512)])
 def test_act_quant(lift, dtype, T, K):
@@ -146,7 +158,7 @@ def _fwd_case(n, K, T, N, M, layout, seed, x=None):
     if x is None:
         x = act_normal(g, T, K)
     ref = O.pack(W, N, M, layout)
-    lift = 8 if (layout == O.LAYOUT_SPARSE and M == 8) else 0
+    lift = _lift(N, M, layout)
     xq_ref, sc_ref = O.act_quant(x, lift)
     acc_ref = O.acc_dense(ref["W_eff"], O.act_quant(x, 0)[0])
     y_ref = O.rescale(acc_ref, ref["gamma"], sc_ref)
@@ -164,7 +176,7 @@ def _fwd_case(n, K, T, N, M, layout, seed, x=None):
 @pytest.mark.parametrize("N,M,layout", CASES_NM)
 @pytest.mark.parametrize("T", [1, 3, 16, 32])
 def test_fwd_gemv(N, M, layout, T):
-    K = 384 if M == 8 and layout == O.LAYOUT_SPARSE else 320
+    K = {64: 320, 128: 384, 256: 512, 32: 320}[_kq(N, M, layout)]
     _fwd_case(200, K, T, N, M, layout, seed=T * 13 + M)
 
 
@@ -230,3 +242,21 @@ def test_six_eight_lifted_equals_dense_path():
     _, a1 = S.fwd(xl, sl, K, c1, m1, g1, n, 6, 8, O.LAYOUT_SPARSE, want_acc=True)
     _, a2 = S.fwd(xd, sd, K, c2, None, g2, n, 6, 8, O.LAYOUT_DENSE2, want_acc=True)
     assert np.array_equal(host(a1), host(a2))
+
+
+def test_fourteen_sixteen_lifted_equals_dense_path():
+    """14:16 through seven 2:4 windows equals the dense-stored product of the same weights."""
+    g = rng(1416)
+    n, K, T = 200, 768, 70
+    W = master_weights(g, n, K)
+    x = act_normal(g, T, K)
+    c1, m1, g1 = S.pack(dev(W), 14, 16, O.LAYOUT_SPARSE)
+    c2, _, g2 = S.pack(dev(W), 14, 16, O.LAYOUT_DENSE2)
+    xl, sl = S.act_quant(dev(x), 16)
+    xd, sd = S.act_quant(dev(x), 0)
+    for TT in (T, 16):   # the GEMM and the GEMV paths
+        _, a1 = S.fwd(xl[:TT], sl[:TT], K, c1, m1, g1, n, 14, 16, O.LAYOUT_SPARSE, want_acc=True)
+        _, a2 = S.fwd(xd[:TT], sd[:TT], K, c2, None, g2, n, 14, 16, O.LAYOUT_DENSE2, want_acc=True)
+        assert np.array_equal(host(a1), host(a2))
+        q, _ = O.act_quant(x[:TT], 0)
+        assert np.array_equal(host(a1), O.acc_dense(O.pack(W, 14, 16)["W_eff"], q))
