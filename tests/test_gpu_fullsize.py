@@ -130,3 +130,24 @@ def test_train_step_full_size():
         rows = np.unique(np.concatenate([[0, n - 1], g.choice(n, 6, replace=False)]))
         _check_sampled(ref, d[f"X:{K}"], host(y), host(acc), toks, rows, f"train {L}")
         print(f"train {L} {n}x{K}: pack bit-exact, sampled outputs ok", flush=True)
+
+
+def test_fourteen_sixteen_full_size():
+    """14:16 through seven 2:4 windows at the 6:8 workload's shapes (2048 x 4096 -> 4096, same
+    seeded master and activations): packs and lifted activations bit-exact, sampled outputs
+    against the oracle, the dense-stored path bitwise equal at full size."""
+    d = workload_inputs("six_eight", 0)
+    W, x, bits = d["W:w"], d["X:4096"], d["Xbits:4096"]
+    ref, (cs, ms, gs) = _check_pack(W, 14, 16, O.LAYOUT_SPARSE, "14:16 windows")
+    _, (cd, _, gd) = _check_pack(W, 14, 16, O.LAYOUT_DENSE2, "14:16 dense")
+    print("14:16: both packs bit-exact", flush=True)
+    xl, sl = _check_quant(x, bits, 16, "14:16 lifted")
+    xd, sd = _check_quant(x, bits, 0, "14:16 plain")
+    ys, accs = S.fwd(xl, sl, 4096, cs, ms, gs, 4096, 14, 16, O.LAYOUT_SPARSE, want_acc=True)
+    yd = S.fwd(xd, sd, 4096, cd, None, gd, 4096, 14, 16, O.LAYOUT_DENSE2)
+    assert np.array_equal(f32_bits(host(ys)), f32_bits(host(yd))), "windows path != dense path"
+    g = np.random.default_rng(1416)
+    toks = np.unique(np.concatenate([[0, 2047], g.choice(2048, 30, replace=False)]))
+    rows = np.unique(np.concatenate([[0, 4095], g.choice(4096, 30, replace=False)]))
+    _check_sampled(ref, x, host(ys), host(accs), toks, rows, "14:16")
+    print("14:16: sampled outputs ok", flush=True)
