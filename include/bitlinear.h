@@ -28,7 +28,7 @@
  *             fl32(absmax_t / 127); absmax_t = 0 gives xq = 0 and scale = 0.
  *
  * ---------------------------------------------------------------------------------------------
- * Packed weight layout (layout id BL_LAYOUT_VERSION = 1)
+ * Packed weight layout (layout id BL_LAYOUT_VERSION = 2)
  *   slot    one kept weight.  BL_LAYOUT_SPARSE: each 4-wide window j of a row's packed K axis
  *           holds slots 2j, 2j+1 = its two kept positions in ascending order; 2:4 windows are
  *           the M-groups; an (M-2):M group (6:8, 14:16) becomes M/2 - 1 windows, window w
@@ -37,7 +37,7 @@
  *           the lowest window that covers it and holds fewer than two (for 6:8: window 0 takes
  *           up to 2 kept positions in 0-3, window 1 up to 2 of the rest in 2-5, window 2 the
  *           rest).  BL_LAYOUT_DENSE2: every position is a slot (K_eff = K).
- *   code    2 bits per slot: 00 = 0, 01 = +1, 11 = -1 (10 is never written).
+ *   code    2 bits per slot: 00 = 0, 01 = +1, 10 = -1 (11 is never written).
  *   index   2 bits per slot (SPARSE only): the slot's position 0..3 inside its window.
  *   unit    16 consecutive slots of one row = one little-endian code dword (slot i at bits
  *           8*(i%4) + 2*(i/4)) and, for SPARSE, one meta dword (slot i's index at bits 2*i).
@@ -83,7 +83,7 @@ extern "C" {
 
 #define BL_LAYOUT_SPARSE 0
 #define BL_LAYOUT_DENSE2 1
-#define BL_LAYOUT_VERSION 1
+#define BL_LAYOUT_VERSION 2
 
 #define BL_DTYPE_F32 0
 #define BL_DTYPE_BF16 1

@@ -37,11 +37,12 @@ formulas of Eqs. 1-3 in extraction):
     x'[(2M-4)g + 4w + j] = x[Mg + 2w + j] (6:8: 12 per 8, 14:16: 28 per 16).
   * Output: y = acc * gamma * scale_t evaluated in fp64, rounded to fp32.
 
-Packed layout (layout id 1), the format of the library's packed buffers:
+Packed layout (layout id 2), the format of the library's packed buffers:
   A *slot* is one kept weight.  SPARSE layout (2:4, or 6:8 / 14:16 lifted into
   2:4 windows): each 4-wide window j of a row's (lifted) K axis holds slots 2j and
   2j+1 -- the kept positions in ascending order -- with a 2-bit ternary code
-  (00 = 0, 01 = +1, 11 = -1) and a 2-bit position index 0..3 within the window.
+  (00 = 0, 01 = +1, 10 = -1; 11 is never written) and a 2-bit position index 0..3
+  within the window.
   DENSE2 layout: every position is a slot with a 2-bit code and no index.
   A *unit* is 16 consecutive slots of one row (row r, unit c) and is stored as
   one little-endian code dword -- slot i at bits 8*(i%4) + 2*(i//4) -- and,
@@ -308,7 +309,7 @@ def _untile(flat: np.ndarray, n_pad: int, U: int) -> np.ndarray:
 
 
 def pack(W: np.ndarray, N: int, M: int, layout: int = LAYOUT_SPARSE):
-    """Mask + ternarize + pack a fp32 master (the library's pack call, layout id 1).
+    """Mask + ternarize + pack a fp32 master (the library's pack call, layout id 2).
 
     Returns dict(codes=uint32[...], meta=uint32[...] or None, gamma=fp32, K_eff, n_pad,
     W_eff, keep).
@@ -322,7 +323,8 @@ def pack(W: np.ndarray, N: int, M: int, layout: int = LAYOUT_SPARSE):
     U = S // 16
     v = np.zeros((n_pad, S), dtype=np.int8)
     v[:n] = vals
-    code_units = ((v.reshape(n_pad, U, 16).astype(np.int64) & 3).astype(np.uint32) << _CODE_SHIFT).sum(
+    code2 = np.where(v < 0, 2, v).astype(np.uint32)                  # 0 -> 00, +1 -> 01, -1 -> 10
+    code_units = (code2.reshape(n_pad, U, 16) << _CODE_SHIFT).sum(
         axis=-1, dtype=np.uint64).astype(np.uint32)
     codes = _tile(code_units)
     meta = None
@@ -349,8 +351,8 @@ def unpack_slots(codes: np.ndarray, meta, n: int, K: int, N: int, M: int, layout
     U = S // 16
     cu = _untile(codes, n_pad, U)[:n]                                    # [n][U]
     raw = (cu[..., None] >> _CODE_SHIFT) & 3                              # [n][U][16]
-    assert not np.any(raw == 2), "code 10 is never written"
-    vals = np.where(raw == 3, -1, raw).astype(np.int8).reshape(n, S)
+    assert not np.any(raw == 3), "code 11 is never written"
+    vals = np.where(raw == 2, -1, raw).astype(np.int8).reshape(n, S)
     if layout == LAYOUT_DENSE2:
         return vals, None
     mu = _untile(np.asarray(meta).view(np.uint32).reshape(-1), n_pad, U)[:n]

@@ -15,17 +15,24 @@ constexpr int kLayoutDense2 = 1;
 constexpr int kPanel = 32;       // rows per packed panel (the M side of a 32x32 MFMA tile)
 constexpr uint32_t kPadMeta = 0x44444444u;
 
-// Expand one packed code dword (16 two-bit codes, slot i at bits 8*(i%4) + 2*(i/4)) into the
-// 16 int8 values of an MFMA A operand: register q, byte p holds slot 4q + p.  Each register is
-// one v_perm_b32 lookup: selector byte = code (0, 1 or 3) picks byte 0 (0x00), 1 (0x01) or
-// 3 (0xFF) of the table operand.
+// Expand one packed code dword (16 two-bit codes, slot i at bits 8*(i%4) + 2*(i/4); 00 = 0,
+// 01 = +1, 10 = -1) into the 16 int8 values of an MFMA A operand: register q, byte p holds slot
+// 4q + p.  Each register is one v_perm_b32 byte lookup on a masked selector; a selector byte 0..7
+// picks a byte of {src0, src1} (0-3 from src1, 4-7 from src0) and 8 replicates bit 15 of src1.
+//   q = 0, 2: selector = code (0, 1, 2)      -> src1 bytes 0, 1, 2 = 0x00, 0x01, 0xFF
+//   q = 1, 3: selector = code << 2 (0, 4, 8) -> src1 byte 0 (0x00), src0 byte 0 (0x01), or
+//             bit 15 of src1 (set: 0xFF)
+// Nine VALU instructions per dword: one shift, four masks, four permutes.
 __device__ __forceinline__ v4i expand_codes(uint32_t c) {
-  const uint32_t table = 0xFF000100u;
+  const uint32_t t_even = 0x00FF0100u;   // src1 of the q = 0, 2 lookups
+  const uint32_t t_odd1 = 0x00008000u;   // src1 of the q = 1, 3 lookups (byte 0 = 0, bit 15 set)
+  const uint32_t t_odd0 = 0x00000001u;   // src0 of the q = 1, 3 lookups (byte 0 = +1)
+  const uint32_t c4 = c >> 4;
   v4i r;
-  r[0] = (int)__builtin_amdgcn_perm(0u, table, c & 0x03030303u);
-  r[1] = (int)__builtin_amdgcn_perm(0u, table, (c >> 2) & 0x03030303u);
-  r[2] = (int)__builtin_amdgcn_perm(0u, table, (c >> 4) & 0x03030303u);
-  r[3] = (int)__builtin_amdgcn_perm(0u, table, (c >> 6) & 0x03030303u);
+  r[0] = (int)__builtin_amdgcn_perm(0u, t_even, c & 0x03030303u);
+  r[1] = (int)__builtin_amdgcn_perm(t_odd0, t_odd1, c & 0x0C0C0C0Cu);
+  r[2] = (int)__builtin_amdgcn_perm(0u, t_even, c4 & 0x03030303u);
+  r[3] = (int)__builtin_amdgcn_perm(t_odd0, t_odd1, c4 & 0x0C0C0C0Cu);
   return r;
 }
 

@@ -409,7 +409,7 @@ struct BigGemm {
     }
 #pragma unroll
     for (int p = 0; p < WM; ++p) {
-      __builtin_amdgcn_sched_group_barrier(0x002, 11, 0);   // one code expansion (VALU)
+      __builtin_amdgcn_sched_group_barrier(0x002, 9, 0);    // one code expansion (VALU)
       __builtin_amdgcn_sched_group_barrier(0x008, WN, 0);   // its MFMAs
     }
   }

@@ -273,7 +273,8 @@ __global__ __launch_bounds__(256) void pack_kernel(const float* __restrict__ W, 
         if (j != i) rank += (a[j] > a[i]) || (a[j] == a[i] && j < i);
       if (rank < nkeep) keep |= 1u << i;
     }
-    auto code = [&](int j) -> uint32_t { return fabsf(w[j]) >= tau ? (w[j] < 0.f ? 3u : 1u) : 0u; };
+    // 00 = 0, 01 = +1, 10 = -1
+    auto code = [&](int j) -> uint32_t { return fabsf(w[j]) >= tau ? (w[j] < 0.f ? 2u : 1u) : 0u; };
     uint8_t* out = &slots[row * SS];
     if constexpr (SP && M == 4) {
       int s = 0;

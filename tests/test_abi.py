@@ -39,7 +39,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_layout_version_and_strerror(L):
-    assert L.lib().bitlinear_layout_version() == 1
+    assert L.lib().bitlinear_layout_version() == 2
     for st in (0, -22, -95, -28, -5, 7):
         assert isinstance(L.lib().bitlinear_strerror(st), bytes)
 
