@@ -36,6 +36,14 @@ formulas of Eqs. 1-3 in extraction):
     remaining ones in 2..5, at most 2; w2 takes the rest).  Lifted activations:
     x'[(2M-4)g + 4w + j] = x[Mg + 2w + j] (6:8: 12 per 8, 14:16: 28 per 16).
   * Output: y = acc * gamma * scale_t evaluated in fp64, rounded to fp32.
+  * Backward ([SB] Training Strategie, Dual STE): the rounding, the clip and the Top-N
+    selection are passed straight through, so with W_q = gamma * W_eff the layer is
+    y = X^ W_q^T and its gradients are dX = dY W_q = gamma * (dY W_eff) and
+    dW = dY^T X^.  dW reaches every master weight, masked ones included: it does not
+    depend on the mask.  dY is bfloat16 (the Sparse-BitNet summary trains in BF16);
+    X^ is the dequantized activation held in bfloat16:
+    X^ = bf16(fp32(q * scale_t)), both roundings to nearest even.  The gradient
+    w.r.t. gamma and the token scales is not propagated (straight through).
 
 Packed layout (layout id 2), the format of the library's packed buffers:
   A *slot* is one kept weight.  SPARSE layout (2:4, or 6:8 / 14:16 lifted into
@@ -66,6 +74,12 @@ Pinned functions (tests/test_oracle_*.py) and what pins them:
   acc_dense          brute-force Python loops on tiny inputs; agrees with the
                      add/sub form acc_addsub; 6:8 and 14:16 lifted == dense
   rescale            zero case and exact small products
+  bf16_round         hand-derived ties and neighbours, exact rational nearest search,
+                     torch's CPU float32 -> bfloat16 cast
+  dequant_act        hand-derived values (tests/golden/bwd_tiny.txt), exact products
+  backward           hand-derived tiny case (tests/golden/bwd_tiny.txt), brute-force Python
+                     loops, the adjoint identities <dX, X^> = <dY, Y> = <dW, W_q> against
+                     the pinned forward, mask independence of dW
 """
 from __future__ import annotations
 
@@ -86,7 +100,7 @@ __all__ = [
     "round_ratio_to_f32", "absmean_gamma", "nm_mask", "ternarize", "effective_weights",
     "WINDOW_M", "window_table", "window_table_68", "k_eff", "packed_dwords", "weight_slots",
     "pack", "unpack_slots", "slots_to_dense", "act_quant", "lift", "lift_68", "acc_dense",
-    "acc_addsub", "rescale", "forward",
+    "acc_addsub", "rescale", "forward", "bf16_round", "dequant_act", "backward",
 ]
 
 
@@ -462,3 +476,41 @@ def forward(W: np.ndarray, x: np.ndarray, N: int, M: int, layout: int = LAYOUT_S
     y = rescale(acc, p["gamma"], scale)
     p.update(xq=xq, scale=scale, acc=acc, y=y)
     return p
+
+
+# ----------------------------------------------------------------------------------------------
+# backward ([SB] technical summary, Training Strategie: Dual STE -- the quantizer and the Top-N
+# selection are bypassed by straight-through estimators and the gradient reaches every master
+# weight, the masked ones too; the plain-language section says the same of removed weights)
+# ----------------------------------------------------------------------------------------------
+
+def bf16_round(v: np.ndarray) -> np.ndarray:
+    """Round finite fp32 values to the nearest bfloat16 (8 significant bits), ties to even.
+
+    Returned as fp32 values.  v = m * 2^e with 0.5 <= |m| < 1 (frexp); the bfloat16 grid near v
+    has spacing 2^(e - 8), or 2^-133 below the normal range (e < -125).
+    """
+    v = np.asarray(v, dtype=np.float32).astype(np.float64)
+    _, e = np.frexp(v)
+    step = np.exp2(np.maximum(e, -125) - 8).astype(np.float64)
+    return (np.rint(v / step) * step).astype(np.float32)
+
+
+def dequant_act(q: np.ndarray, scale: np.ndarray) -> np.ndarray:
+    """X^[t][k] = bf16(fp32(q[t][k] * scale_t)): the dequantized activation in bfloat16."""
+    prod = np.asarray(q, np.float32) * np.asarray(scale, np.float32)[:, None]   # fp32 multiply
+    return bf16_round(prod)
+
+
+def backward(dy: np.ndarray, W_eff: np.ndarray, gamma: np.float32, q: np.ndarray,
+             scale: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """Straight-through gradients of y = X^ (gamma W_eff)^T, in fp64.
+
+    dy: [T][n] bfloat16 values (as floats); W_eff: [n][K] ternary (mask applied); q: [T][K] int8
+    (not lifted) with scale [T].  Returns dX [T][K] = gamma * (dY @ W_eff) and
+    dW [n][K] = dY^T @ X^ (the gradient of every master weight, masked or kept).
+    """
+    dy64 = np.asarray(dy, np.float64)
+    dx = np.float64(gamma) * (dy64 @ np.asarray(W_eff, np.float64))
+    dw = dy64.T @ dequant_act(q, scale).astype(np.float64)
+    return dx, dw

@@ -115,3 +115,31 @@ def workload_inputs(key: str, seed: int = 0, layers: List[str] | None = None,
             out[f"Xbits:{K}"] = bits
         out[f"X:{K}"] = x
     return out
+
+
+GRAD_SIGMA = 2.0 ** -10
+
+
+def grad_bf16(g: np.random.Generator, T: int, n: int, sigma: float = GRAD_SIGMA):
+    """Output gradients dY ~ N(0, sigma^2) on the bfloat16 grid: (values as float32, uint16 bits)."""
+    return to_bf16((g.standard_normal(size=(T, n)) * sigma).astype(np.float32))
+
+
+def grad_int_bf16(g: np.random.Generator, T: int, n: int, lim: int = 8):
+    """Integer output gradients in [-lim, lim] (exact in bfloat16): (float32 values, uint16 bits)."""
+    return to_bf16(g.integers(-lim, lim + 1, size=(T, n)).astype(np.float32))
+
+
+def workload_grads(key: str, seed: int = 0, tokens: int | None = None) -> Dict[str, np.ndarray]:
+    """Output gradients of a workload's layers, ``dY:<layer>`` (values) and ``dYbits:<layer>``.
+
+    Drawn from a stream of their own (seed sequence [seed, 1]) so the masters and activations of
+    ``workload_inputs`` stay as they are.
+    """
+    wl = WORKLOADS[key]
+    g = np.random.default_rng([seed, 1])
+    T = tokens if tokens is not None else max(wl.tokens)
+    out: Dict[str, np.ndarray] = {}
+    for L in wl.layers:
+        out[f"dY:{L.name}"], out[f"dYbits:{L.name}"] = grad_bf16(g, T, L.n)
+    return out
