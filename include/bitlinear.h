@@ -170,6 +170,48 @@ int bitlinear_group_build(const bl_fwd_desc* descs, int64_t count, int N, int M,
 int bitlinear_fwd_group(const void* table, int64_t work_items, int N, int M, int layout,
                         void* stream);
 
+/* ---------------------------------------------------------------------------------------------
+ * Backward for training (Sparse-BitNet technical summary, Training Strategie: Dual STE).
+ *
+ * The rounding, the clip and the Top-N selection are passed straight through, and the gradient
+ * reaches every master weight, the masked ones included.  With the forward y = X^ (gamma W_eff)^T
+ * of bitlinear_fwd (X^ = q * scale_t):
+ *   dx[T][K] = gamma * (dY . W_eff)         fp32; W_eff is the masked ternary matrix of the packed
+ *                                           weights (any layout and N:M bitlinear_fwd accepts)
+ *   dw[n][K] = dY^T . X^                    fp32, the gradient of the dense fp32 master;
+ *                                           X^[t][k] = bf16(fp32(q[t][k] * x_scale[t])), both
+ *                                           roundings to nearest even
+ * dy is the output gradient in bfloat16 (bit patterns, row-major [T][n]).  xq is the plain
+ * (never lifted) int8 activation [T][K] of act_quant_i8 with lift_M = 0 and x_scale its token
+ * scales.  Products are exact (bf16 x bf16 in fp32) and sums are fp32 in an unspecified order;
+ * dx is rounded once more by the gamma product.  No gradient flows to gamma or to the token
+ * scales (straight through).
+ *
+ * flags: BL_BWD_ACCUM_DX adds the result to dx (dx += ...), BL_BWD_ACCUM_DW to dw; otherwise the
+ * outputs are overwritten.  dx or dw may be NULL to skip that gradient (not both).  T == 0 leaves
+ * dx alone and writes dw = 0 (or leaves it unchanged under BL_BWD_ACCUM_DW); dy, xq and x_scale
+ * may then be NULL.
+ *
+ * Shapes follow bitlinear_fwd (K, N:M and layout as packed; n >= 1); in addition every operand of
+ * the two products must stay below 2^31 bytes: T * n32, K * n32, n * T32 and K * T32 bf16
+ * elements, where n32 and T32 are n and T rounded up to multiples of 32.  Alignment: dy, xq,
+ * codes, meta, dx and dw 16 bytes, x_scale and gamma 4 bytes, ws 256 bytes.
+ *
+ * ws: caller-owned device workspace of at least bitlinear_bwd_workspace_bytes bytes, used for the
+ * transposed bf16 operands; its contents on entry do not matter and are scratch afterwards.
+ * Asynchronous and stream-ordered; calls that share a workspace must be ordered on one stream.
+ */
+#define BL_BWD_ACCUM_DX 1
+#define BL_BWD_ACCUM_DW 2
+
+/* Workspace bytes of bitlinear_bwd for T tokens, n out-features and K in-features. */
+int bitlinear_bwd_workspace_bytes(int64_t T, int64_t n, int64_t K, size_t* ws_bytes);
+
+int bitlinear_bwd(const uint16_t* dy, int64_t T, int64_t n, const int8_t* xq,
+                  const float* x_scale, int64_t K, const uint8_t* codes, const uint8_t* meta,
+                  const float* gamma, int N, int M, int layout, float* dx, float* dw, int flags,
+                  void* ws, size_t ws_bytes, void* stream);
+
 /* Static description of a status code. */
 const char* bitlinear_strerror(int status);
 

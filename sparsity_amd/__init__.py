@@ -1,12 +1,13 @@
-"""MI355X-native sparse ternary BitLinear (Sparse-BitNet / BitNet b1.58 forward).
+"""MI355X-native sparse ternary BitLinear (Sparse-BitNet / BitNet b1.58 forward and backward).
 
 The compute path lives in ``libbitlinear.so`` (hand-written HIP for gfx950, C ABI declared in
 ``include/bitlinear.h``); ``sparsity_amd.bitlinear`` is a thin ctypes binding with the same
 names.  PyTorch is used only to own device memory and streams.
 """
 from .bitlinear import (  # noqa: F401
-    BL_DTYPE_BF16, BL_DTYPE_F32, BL_LAYOUT_DENSE2, BL_LAYOUT_SPARSE, BitLinearError, BlFwdDesc,
-    FwdGroup, act_quant, act_quant_i8, bitlinear_fwd, bitlinear_fwd_group, bitlinear_group_build,
-    bitlinear_group_table_bytes, bitlinear_pack, bitlinear_packed_bytes, fwd, lib, pack,
-    packed_bytes,
+    BL_BWD_ACCUM_DW, BL_BWD_ACCUM_DX, BL_DTYPE_BF16, BL_DTYPE_F32, BL_LAYOUT_DENSE2,
+    BL_LAYOUT_SPARSE, BitLinearError, BlFwdDesc, FwdGroup, act_quant, act_quant_i8, bitlinear_bwd,
+    bitlinear_bwd_workspace_bytes, bitlinear_fwd, bitlinear_fwd_group, bitlinear_group_build,
+    bitlinear_group_table_bytes, bitlinear_pack, bitlinear_packed_bytes, bwd, bwd_workspace_bytes,
+    fwd, lib, pack, packed_bytes,
 )

@@ -2,7 +2,8 @@
 
 Names mirror the C ABI: ``bitlinear_packed_bytes``, ``bitlinear_pack``, ``act_quant_i8``,
 ``bitlinear_fwd``, ``bitlinear_group_table_bytes``, ``bitlinear_group_build``,
-``bitlinear_fwd_group``.  ``pack`` / ``act_quant`` / ``fwd`` / ``FwdGroup`` are convenience
+``bitlinear_fwd_group``, ``bitlinear_bwd_workspace_bytes``, ``bitlinear_bwd``.
+``pack`` / ``act_quant`` / ``fwd`` / ``FwdGroup`` / ``bwd`` are convenience
 wrappers that allocate the output tensors with torch on the input's device and enqueue on torch's
 current stream.
 """
@@ -17,6 +18,8 @@ BL_LAYOUT_SPARSE = 0
 BL_LAYOUT_DENSE2 = 1
 BL_DTYPE_F32 = 0
 BL_DTYPE_BF16 = 1
+BL_BWD_ACCUM_DX = 1
+BL_BWD_ACCUM_DW = 2
 
 
 
@@ -59,12 +62,16 @@ def lib() -> ctypes.CDLL:
                                                   ctypes.POINTER(i64)]
         L.bitlinear_group_build.argtypes = [dp, i64, i32, i32, i32, vp, sz, vp]
         L.bitlinear_fwd_group.argtypes = [vp, i64, i32, i32, i32, vp]
+        L.bitlinear_bwd_workspace_bytes.argtypes = [i64, i64, i64, ctypes.POINTER(sz)]
+        L.bitlinear_bwd.argtypes = [vp, i64, i64, vp, vp, i64, vp, vp, vp, i32, i32, i32, vp, vp,
+                                    i32, vp, sz, vp]
         L.bitlinear_strerror.argtypes = [i32]
         L.bitlinear_strerror.restype = ctypes.c_char_p
         L.bitlinear_layout_version.argtypes = []
         for f in (L.bitlinear_packed_bytes, L.bitlinear_pack, L.act_quant_i8, L.bitlinear_fwd,
                   L.bitlinear_layout_version, L.bitlinear_group_table_bytes,
-                  L.bitlinear_group_build, L.bitlinear_fwd_group):
+                  L.bitlinear_group_build, L.bitlinear_fwd_group,
+                  L.bitlinear_bwd_workspace_bytes, L.bitlinear_bwd):
             f.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -114,6 +121,19 @@ def bitlinear_group_build(descs, N, M, layout, table, table_bytes, stream) -> in
 
 def bitlinear_fwd_group(table, work_items, N, M, layout, stream) -> int:
     return lib().bitlinear_fwd_group(table, work_items, N, M, layout, stream)
+
+
+def bitlinear_bwd_workspace_bytes(T, n, K):
+    """Returns (status, ws_bytes)."""
+    ws = ctypes.c_size_t()
+    st = lib().bitlinear_bwd_workspace_bytes(T, n, K, ctypes.byref(ws))
+    return st, ws.value
+
+
+def bitlinear_bwd(dy, T, n, xq, x_scale, K, codes, meta, gamma, N, M, layout, dx, dw, flags, ws,
+                  ws_bytes, stream) -> int:
+    return lib().bitlinear_bwd(dy, T, n, xq, x_scale, K, codes, meta, gamma, N, M, layout, dx, dw,
+                               flags, ws, ws_bytes, stream)
 
 
 # ---------------------------------------------------------------------------------------------
@@ -223,3 +243,35 @@ class FwdGroup:
     def __call__(self):
         _check(bitlinear_fwd_group(self.table.data_ptr(), self.work_items, self.N, self.M,
                                    self.layout, _stream()), "bitlinear_fwd_group")
+
+
+def bwd_workspace_bytes(T: int, n: int, K: int) -> int:
+    st, ws = bitlinear_bwd_workspace_bytes(T, n, K)
+    _check(st, "bitlinear_bwd_workspace_bytes")
+    return ws
+
+
+def bwd(dy, xq, scale, K: int, codes, meta, gamma, n: int, N: int = 2, M: int = 4,
+        layout: int = BL_LAYOUT_SPARSE, want_dx: bool = True, want_dw: bool = True,
+        out=None, accumulate: Tuple[bool, bool] = (False, False), ws=None):
+    """Straight-through gradients (dx fp32 [T][K], dw fp32 [n][K]) of one BitLinear.
+
+    dy: bf16 [T][n]; xq / scale: the plain (unlifted) int8 activations and token scales; codes /
+    meta / gamma: the packed weights.  ``out`` may supply (dx, dw) (either may be None when not
+    wanted); ``accumulate`` adds into them.  ``ws`` may supply a uint8 workspace.
+    """
+    import torch
+    T = dy.shape[0]
+    dev = dy.device
+    if out is None:
+        dx = torch.empty((T, K), dtype=torch.float32, device=dev) if want_dx else None
+        dw = torch.empty((n, K), dtype=torch.float32, device=dev) if want_dw else None
+    else:
+        dx, dw = out
+    if ws is None:
+        ws = torch.empty(max(bwd_workspace_bytes(T, n, K), 256), dtype=torch.uint8, device=dev)
+    flags = (BL_BWD_ACCUM_DX if accumulate[0] else 0) | (BL_BWD_ACCUM_DW if accumulate[1] else 0)
+    _check(bitlinear_bwd(_ptr(dy), T, n, _ptr(xq), _ptr(scale), K, _ptr(codes), _ptr(meta),
+                         _ptr(gamma), N, M, layout, _ptr(dx), _ptr(dw), flags, _ptr(ws), ws.numel(),
+                         _stream()), "bitlinear_bwd")
+    return dx, dw

@@ -245,4 +245,43 @@ int bitlinear_fwd_group(const void* table, int64_t work_items, int N, int M, int
   return status_of(bl::launch_fwd_group(table, work_items, layout, (hipStream_t)stream));
 }
 
+int bitlinear_bwd_workspace_bytes(int64_t T, int64_t n, int64_t K, size_t* ws_bytes) {
+  if (T < 0 || T > INT32_MAX || n < 1 || n > INT32_MAX || K < 1 || K > INT32_MAX || !ws_bytes)
+    return BL_EINVAL;
+  *ws_bytes = bl::bwd_workspace(T, n, K).total;
+  return BL_OK;
+}
+
+int bitlinear_bwd(const uint16_t* dy, int64_t T, int64_t n, const int8_t* xq,
+                  const float* x_scale, int64_t K, const uint8_t* codes, const uint8_t* meta,
+                  const float* gamma, int N, int M, int layout, float* dx, float* dw, int flags,
+                  void* ws, size_t ws_bytes, void* stream) {
+  int64_t ke = 0;
+  const int st = check_shape(n, K, N, M, layout, &ke);
+  if (st != BL_OK) return st;
+  if (T < 0 || T > INT32_MAX) return BL_EINVAL;
+  if ((flags & ~(BL_BWD_ACCUM_DX | BL_BWD_ACCUM_DW)) != 0) return BL_EINVAL;
+  if (!dx && !dw) return BL_EINVAL;
+  const bl::BwdWorkspace w = bl::bwd_workspace(T, n, K);
+  const uint64_t lim = 1ull << 30;   // bf16 elements: operands stay below 2^31 bytes
+  if ((uint64_t)T * w.n32 >= lim || (uint64_t)K * w.n32 >= lim || (uint64_t)n * w.t32 >= lim ||
+      (uint64_t)K * w.t32 >= lim)
+    return BL_EINVAL;
+  if (dx && T > 0) {
+    if (!aligned16(codes) || !aligned4(gamma) || !aligned16(dx)) return BL_EINVAL;
+    if (layout == BL_LAYOUT_SPARSE ? !aligned16(meta) : meta != nullptr) return BL_EINVAL;
+  }
+  if (dw && !aligned16(dw)) return BL_EINVAL;
+  if (T > 0) {
+    if (!aligned16(dy)) return BL_EINVAL;
+    if (dw && (!aligned16(xq) || !aligned4(x_scale))) return BL_EINVAL;
+  }
+  if (!ws || ((uintptr_t)ws & 255u)) return BL_EINVAL;
+  if (ws_bytes < w.total) return BL_ENOSPC;
+  if (T == 0 && !dw) return BL_OK;   // no rows of dx: nothing to enqueue
+  return status_of(bl::launch_bwd(dy, T, n, xq, x_scale, K, (const uint32_t*)codes,
+                                  (const uint32_t*)meta, gamma, N, M, layout, dx, dw, flags, ws,
+                                  (hipStream_t)stream));
+}
+
 }  // extern "C"

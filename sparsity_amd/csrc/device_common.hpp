@@ -88,4 +88,23 @@ __device__ __forceinline__ void block_sync_lds() {
   block_barrier_nofence();
 }
 
+typedef __attribute__((address_space(3))) int8_t lds_i8;
+__device__ __forceinline__ uint32_t lds_offset(const void* p) { return (uint32_t)(uintptr_t)(lds_i8*)p; }
+
+// global_load_lds_dwordx4 issued as inline asm: 16 bytes per lane from `src` to LDS at
+// m0 + 16 * lane.  It writes no VGPR, so nothing can consume a register before the data lands;
+// completion is tracked by the caller's explicit vmcnt waits.  (Issued through the builtin, the
+// compiler cannot prove the in-flight loads miss the buffer being read and drains them all before
+// every LDS read, which serializes the pipeline.)  One wait state separates the m0 write from
+// its use.
+__device__ __forceinline__ void lds_dma16(const void* src, uint32_t m0) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+               :: "s"(m0), "v"(src) : "memory", "m0");
+}
+// Same, scalar base + per-lane 32-bit byte offset (no VALU address arithmetic per load).
+__device__ __forceinline__ void lds_dma16_s(const void* sbase, uint32_t voff, uint32_t m0) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :: "s"(m0), "v"(voff), "s"(sbase) : "memory", "m0");
+}
+
 }  // namespace bl

@@ -62,3 +62,37 @@ struct GroupItem {
 hipError_t launch_fwd_group(const void* table, int64_t items, int layout, hipStream_t s);
 
 }  // namespace bl
+
+namespace bl {
+
+// Workspace of bitlinear_bwd, in bytes from its start (segments 256-byte aligned):
+//   wt  [K][n32] bf16   W_eff^T (dX only)
+//   dyp [T][n32] bf16   dY with rows zero-padded to n32 (dX only, when n % 32 != 0)
+//   dyt [n][t32] bf16   dY^T, tokens zero-padded to t32 (dW only)
+//   xt  [K][t32] bf16   X^^T (dW only)
+// n32 and t32 are n and T rounded up to multiples of 32.
+struct BwdWorkspace {
+  int64_t n32, t32;
+  size_t wt_off, dyp_off, dyt_off, xt_off, total;
+};
+
+inline BwdWorkspace bwd_workspace(int64_t T, int64_t n, int64_t K) {
+  auto up = [](size_t v, size_t a) { return (v + a - 1) / a * a; };
+  BwdWorkspace w;
+  w.n32 = (n + 31) / 32 * 32;
+  w.t32 = (T + 31) / 32 * 32;
+  size_t off = 0;
+  w.wt_off = off;  off = up(off + (size_t)K * w.n32 * 2, 256);
+  w.dyp_off = off; off = up(off + (w.n32 != n ? (size_t)T * w.n32 * 2 : 0), 256);
+  w.dyt_off = off; off = up(off + (size_t)n * w.t32 * 2, 256);
+  w.xt_off = off;  off = up(off + (size_t)K * w.t32 * 2, 256);
+  w.total = off;
+  return w;
+}
+
+hipError_t launch_bwd(const uint16_t* dy, int64_t T, int64_t n, const int8_t* xq,
+                      const float* x_scale, int64_t K, const uint32_t* codes, const uint32_t* meta,
+                      const float* gamma, int N, int M, int layout, float* dx, float* dw, int flags,
+                      void* ws, hipStream_t s);
+
+}  // namespace bl

@@ -177,3 +177,55 @@ def test_group_sizes_and_rejects_before_launch(L):
     assert L.bitlinear_fwd_group(FAKE + 4, 3, 2, 4, 0, None) == -22
     assert L.bitlinear_fwd_group(FAKE, 3, 2, 4, 9, None) == -95
     assert L.bitlinear_fwd_group(None, 0, 2, 4, 0, None) == 0   # nothing to launch
+
+
+def _up32(v):
+    return (v + 31) // 32 * 32
+
+
+@pytest.mark.parametrize("T,n,K", [(8192, 3200, 3200), (8192, 8640, 3200), (8192, 3200, 8640),
+                                   (1, 45, 64), (0, 100, 256), (33, 96, 128)])
+def test_bwd_workspace_bytes(L, T, n, K):
+    """Four bf16 operands (W_eff^T, padded dY when n % 32, dY^T, X^^T), 256-byte aligned."""
+    st, ws = L.bitlinear_bwd_workspace_bytes(T, n, K)
+    assert st == 0
+    up = lambda v: (v + 255) // 256 * 256
+    n32, t32 = _up32(n), _up32(T)
+    want = up(2 * K * n32) + up(2 * T * n32 if n32 != n else 0) + up(2 * n * t32) + up(2 * K * t32)
+    assert ws == want
+    assert L.bitlinear_bwd_workspace_bytes(-1, n, K)[0] == -22
+    assert L.bitlinear_bwd_workspace_bytes(T, 0, K)[0] == -22
+
+
+def test_bwd_rejects_before_launch(L):
+    P = FAKE
+    ws_ok = 1 << 30
+    ok = dict(dy=P, T=64, n=128, xq=P, xs=P, K=256, codes=P, meta=P, gamma=P, N=2, M=4, layout=0,
+              dx=P, dw=P, flags=0, ws=P, wsb=ws_ok)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return L.bitlinear_bwd(a["dy"], a["T"], a["n"], a["xq"], a["xs"], a["K"], a["codes"],
+                               a["meta"], a["gamma"], a["N"], a["M"], a["layout"], a["dx"], a["dw"],
+                               a["flags"], a["ws"], a["wsb"], None)
+    assert call(K=100) == -22                     # packed-layout shape rules
+    assert call(N=1, M=4) == -95
+    assert call(N=6, M=8, K=192) == -22
+    assert call(T=-1) == -22
+    assert call(flags=4) == -22
+    assert call(dx=None, dw=None) == -22          # nothing asked for
+    assert call(dy=P + 2) == -22
+    assert call(dy=None) == -22
+    assert call(xq=P + 1) == -22
+    assert call(xs=P + 2) == -22
+    assert call(codes=P + 8) == -22
+    assert call(meta=None) == -22
+    assert call(layout=1, meta=P) == -22
+    assert call(dx=P + 4) == -22
+    assert call(dw=P + 4) == -22
+    assert call(ws=P + 128) == -22
+    assert call(wsb=L.bitlinear_bwd_workspace_bytes(64, 128, 256)[1] - 1) == -28
+    # operands of 2^31 bytes or more (32-bit offsets inside the kernels)
+    assert call(T=1 << 20, n=1024, K=256) == -22
+    # dX only with no tokens: nothing to do, nothing enqueued, token buffers may be NULL
+    assert call(T=0, dw=None, dy=None, xq=None, xs=None) == 0
