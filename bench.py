@@ -41,6 +41,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 SMFMAC_I8_PEAK_TOPS = 10100.0  # MI355X int8 with 2:4 structured sparsity, dense-equivalent
 MFMA_I8_PEAK_TOPS = 5000.0     # MI355X dense int8 MFMA
 UP = (6912, 2560)
@@ -63,7 +64,7 @@ def parse():
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the 6:8, 14:16 and training-step legs")
     ap.add_argument("--cpu-budget-s", type=float, default=15.0)
-    ap.add_argument("--profile-pass", choices=("decode", "prefill", "train"), default=None,
+    ap.add_argument("--profile-pass", choices=("decode", "prefill", "train", "bwd"), default=None,
                     help="for hardware-counter runs, no graph and no JSON line.  decode: two eager "
                          "decode steps, then a plain copy of COPY_BYTES (the counters' scale "
                          "reference); prefill: the prefill GEMM launched five times; train: the "
@@ -268,6 +269,14 @@ def train_step_leg(S, torch, iters=3):
     X = {K: torch.randn((T, K), generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
          for K in (3200, 8640)}
     Q = {K: S.act_quant(X[K]) for K in X}
+    # backward operands: output gradients dY (bf16 N(0, 2^-20)), the weight gradients of every
+    # master, and one input gradient per activation matrix, summed over the projections reading it
+    dYs = [(torch.randn((T, n), generator=g, device="cuda", dtype=torch.float32) * 2.0 ** -10)
+           .to(torch.bfloat16) for (_, n, K) in TRAIN_LAYERS]
+    dWs = [torch.empty((n, K), dtype=torch.float32, device="cuda") for (_, n, K) in TRAIN_LAYERS]
+    dXs = {K: torch.empty((T, K), dtype=torch.float32, device="cuda") for K in X}
+    bws = torch.empty(max(S.bwd_workspace_bytes(T, n, K) for (_, n, K) in TRAIN_LAYERS),
+                      dtype=torch.uint8, device="cuda")
 
     def pack_all():
         for W, out in zip(masters, packed):
@@ -282,25 +291,37 @@ def train_step_leg(S, torch, iters=3):
             xq, sc = Q[K]
             S.fwd(xq, sc, K, c, m, ga, n, out=(y, None))
 
+    def bwd_all():
+        seen = set()
+        for (_, n, K), (c, m, ga), dy, dw in zip(TRAIN_LAYERS, packed, dYs, dWs):
+            xq, sc = Q[K]
+            S.bwd(dy, xq, sc, K, c, m, ga, n, out=(dXs[K], dw), accumulate=(K in seen, False),
+                  ws=bws)
+            seen.add(K)
+
     # each phase captured once as a HIP graph (no host launch overhead between the 7 matrices);
     # two replays are checked bitwise against the eager results first
+    def results():
+        return [t for (c, m, ga) in packed for t in (c, m, ga)] + ys + dWs + list(dXs.values())
+
     def outputs():
-        return [t.clone() for (c, m, ga) in packed for t in (c, m, ga)] + [y.clone() for y in ys]
+        return [t.clone() for t in results()]
 
     pack_all()
     quant_all()
     fwd_all()
+    bwd_all()
     torch.cuda.synchronize()
     ref = outputs()
     graphs = []
     cap = torch.cuda.Stream()
-    for fn in (pack_all, quant_all, fwd_all):
+    for fn in (pack_all, quant_all, fwd_all, bwd_all):
         gr = torch.cuda.CUDAGraph()
         with torch.cuda.graph(gr, stream=cap):
             fn()
         graphs.append(gr)
     for _ in range(2):
-        for t in [t for (c, m, ga) in packed for t in (c, m, ga)] + ys:
+        for t in results():
             t.zero_()
         for gr in graphs:
             gr.replay()
@@ -311,6 +332,7 @@ def train_step_leg(S, torch, iters=3):
     t_pack = _event_ms(torch, graphs[0].replay, iters)
     t_quant = _event_ms(torch, graphs[1].replay, iters)
     t_fwd = _event_ms(torch, graphs[2].replay, iters)
+    t_bwd = _event_ms(torch, graphs[3].replay, iters)
     pack_bytes = sum(4 * n * K + p[0].numel() + p[1].numel() for (_, n, K), p in zip(TRAIN_LAYERS, packed))
     # act_quant: bf16 read + int8 write per element + 4 B scale per token
     quant_bytes = sum(T * K * 3 + 4 * T for K in X)
@@ -318,9 +340,12 @@ def train_step_leg(S, torch, iters=3):
     pack_gbs = pack_bytes / (t_pack * 1e-3) / 1e9
     quant_gbs = quant_bytes / (t_quant * 1e-3) / 1e9
     fwd_tops = ops / (t_fwd * 1e-3) / 1e12
+    # backward: two dense bf16 products (dX and dW) of 2 T K n flops each per projection
+    bwd_tflops = 2 * ops / (t_bwd * 1e-3) / 1e12
     return {"workload": "3B-alike layer set (QKV 3x3200x3200, O, gate/up 8640x3200, down 3200x8640), "
-                        "8192 tokens, 2:4, bf16 N(0,1) activations",
-            "step_ms": round(t_pack + t_quant + t_fwd, 4),
+                        "8192 tokens, 2:4, bf16 N(0,1) activations, bf16 output gradients",
+            "step_ms": round(t_pack + t_quant + t_fwd + t_bwd, 4),
+            "bwd_ms": round(t_bwd, 4), "bwd_TFLOPS": round(bwd_tflops, 1),
             "pack_ms": round(t_pack, 4), "pack_GBps": round(pack_gbs, 1),
             "act_quant_ms": round(t_quant, 4), "act_quant_GBps": round(quant_gbs, 1),
             "fwd_ms": round(t_fwd, 4), "fwd_TOPS": round(fwd_tops, 1),
@@ -333,7 +358,27 @@ def train_step_leg(S, torch, iters=3):
                                        "frac": round(quant_gbs / HBM_PEAK_GBS, 4)},
                          "fwd": {"bound": "mfma", "achieved": round(fwd_tops, 1),
                                  "peak": SMFMAC_I8_PEAK_TOPS, "unit": "TOPS",
-                                 "frac": round(fwd_tops / SMFMAC_I8_PEAK_TOPS, 4)}}}
+                                 "frac": round(fwd_tops / SMFMAC_I8_PEAK_TOPS, 4)},
+                         "bwd": {"bound": "mfma", "achieved": round(bwd_tflops, 1),
+                                 "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                 "frac": round(bwd_tflops / BF16_PEAK_TFLOPS, 4)}}}
+
+
+def bwd_profile_pass(S, torch):
+    """Backward of one training-step projection (gate, 8640 x 3200, 8192 tokens), three times."""
+    T, n, K = 8192, 8640, 3200
+    g = torch.Generator(device="cuda")
+    g.manual_seed(36)
+    W = (torch.randn((n, K), generator=g, device="cuda") * 0.02).contiguous()
+    codes, meta, gamma = S.pack(W, 2, 4)
+    x = torch.randn((T, K), generator=g, device="cuda").to(torch.bfloat16)
+    xq, sc = S.act_quant(x)
+    dy = (torch.randn((T, n), generator=g, device="cuda") * 2.0 ** -10).to(torch.bfloat16)
+    dx = torch.empty((T, K), device="cuda")
+    dw = torch.empty((n, K), device="cuda")
+    ws = torch.empty(S.bwd_workspace_bytes(T, n, K), dtype=torch.uint8, device="cuda")
+    for _ in range(3):
+        S.bwd(dy, xq, sc, K, codes, meta, gamma, n, out=(dx, dw), ws=ws)
 
 
 # ---------------------------------------------------------------------------------------------
@@ -377,6 +422,11 @@ def main():
     import sparsity_amd as S
     S.lib()
     torch.cuda.set_device(0)
+    if args.profile_pass == "bwd":
+        bwd_profile_pass(S, torch)
+        torch.cuda.synchronize()
+        log("profile pass done: backward of the gate projection x 3")
+        return
     if args.profile_pass == "train":
         train_step_leg(S, torch, iters=2)
         torch.cuda.synchronize()

@@ -193,9 +193,10 @@ __global__ __launch_bounds__(256) void pad_rows_kernel(const uint16_t* __restric
 // lane then holds one i and four runs of four consecutive j, stored as 16-byte vectors.
 //
 // Operands reach LDS with direct global->LDS loads (16 bytes per lane, no VGPR staging).  A stage
-// is 32 reduction elements (64 bytes) of all 256 A rows and 256 B rows, 32 KB; a ring of four
-// stage buffers keeps three stages in flight while one is multiplied, and each wave waits on its
-// own vmcnt (every stage issues exactly kNtLoads loads per wave) before a bare s_barrier.  Rows
+// is 32 reduction elements (64 bytes) of all 256 A rows and 256 B rows, 32 KB; a ring of five
+// stage buffers keeps three stages in flight while one is multiplied and the previous one is
+// still being read, and each wave waits on its own vmcnt (every stage issues exactly kNtLoads
+// loads per wave) before a bare s_barrier.  Rows
 // are stored 64 bytes apart with their 16-byte chunks XOR-swizzled by (row / 4) % 4, so the 16
 // lanes served together (16 consecutive rows, one chunk each) hit 16 distinct 16-byte bank groups.
 // Rows past rows_a / rows_b load clamped, valid rows whose results are never stored.
@@ -205,8 +206,9 @@ constexpr int kNtBI = 256, kNtBJ = 256;      // block tile (2 x 2 waves)
 constexpr int kNtRowBytes = 64;              // bytes of the reduction axis per row per stage
 constexpr int kNtHalf = kNtBI * kNtRowBytes; // A part of a stage (B follows)
 constexpr int kNtStage = (kNtBI + kNtBJ) * kNtRowBytes;
-constexpr int kNtRing = 4;
+constexpr int kNtRing = 5;                   // 5 x 32 KB: all of the CU's 160 KB of LDS
 constexpr int kNtLoads = kNtStage / 1024 / 4;   // global->LDS loads per wave per stage
+constexpr int kNtGroupI = 8;                     // row tiles per group of the tile order
 static_assert(kNtLoads == 8, "stage split");
 
 struct NtArgs {
@@ -243,43 +245,79 @@ struct NtGemm {
     for (int q = 0; q < kNtLoads / 2; ++q) lds_dma16_s(sb, b_off[q], base + kNtHalf + q * 1024);
   }
 
+  // Fragment f of reduction step j: f = 0..3 the A fragments (rows wi*128 + 32f ..), f = 4..7 the B
+  // fragments.  Lane l reads row l % 32 of the fragment, 8 bf16 at reduction offset 16j + 8(l/32).
+  __device__ __forceinline__ void read_frag(const uint8_t* buf, int j, int f, Regs& r) const {
+    const bool is_a = f < kNtWI;
+    const int row = (is_a ? wi : wj) * 128 + (is_a ? f : f - kNtWI) * 32 + (lane & 31);
+    const int chunk = (2 * j + h) ^ ((row >> 2) & 3);
+    const bf16x8 v = *(const bf16x8*)(buf + (is_a ? 0 : kNtHalf) + row * kNtRowBytes + chunk * 16);
+    if (is_a) r.a[f] = v; else r.b[f - kNtWI] = v;
+  }
+
   __device__ __forceinline__ void read_step(const uint8_t* buf, int j, Regs& r) const {
 #pragma unroll
-    for (int f = 0; f < kNtWI; ++f) {
-      const int row = wi * 128 + f * 32 + (lane & 31);
-      const int chunk = (2 * j + h) ^ ((row >> 2) & 3);
-      r.a[f] = *(const bf16x8*)(buf + row * kNtRowBytes + chunk * 16);
-    }
-#pragma unroll
-    for (int f = 0; f < kNtWJ; ++f) {
-      const int row = wj * 128 + f * 32 + (lane & 31);
-      const int chunk = (2 * j + h) ^ ((row >> 2) & 3);
-      r.b[f] = *(const bf16x8*)(buf + kNtHalf + row * kNtRowBytes + chunk * 16);
-    }
+    for (int f = 0; f < kNtWI + kNtWJ; ++f) read_frag(buf, j, f, r);
+  }
+
+  __device__ __forceinline__ void mma_one(const Regs& r, int fi, int fj) {
+    acc[fi][fj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(r.b[fj], r.a[fi], acc[fi][fj], 0, 0, 0);
   }
 
   __device__ __forceinline__ void mma(const Regs& r) {
 #pragma unroll
     for (int fi = 0; fi < kNtWI; ++fi)
 #pragma unroll
-      for (int fj = 0; fj < kNtWJ; ++fj)
-        acc[fi][fj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(r.b[fj], r.a[fi], acc[fi][fj], 0, 0, 0);
+      for (int fj = 0; fj < kNtWJ; ++fj) mma_one(r, fi, fj);
+  }
+
+  // The next step's eight LDS reads go out one before each of the first eight MFMAs, so their
+  // latency hides under the current step's matrix work (left alone, the scheduler sinks them
+  // below all sixteen MFMAs and the next step waits on them).
+  __device__ __forceinline__ static void interleave_reads() {
+#pragma unroll
+    for (int q = 0; q < kNtWI + kNtWJ; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one DS read
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, kNtWI * kNtWJ - (kNtWI + kNtWJ), 0);
   }
 
   // One stage (two reduction steps) from buffer BUF.  On entry R0 holds its first step; on exit
-  // R0 holds the next stage's first step.  Before the last step's MFMAs the wave waits for its own
-  // loads of the next stage (the two stages after it stay in flight), meets the other waves (after
-  // which nobody reads BUF again), refills BUF with stage st + 4 and reads the next stage's first
-  // step.
+  // R0 holds the next stage's first step.
+  //   First half: step 0's sixteen MFMAs, with step 1's reads interleaved.
+  //   Then the wave waits for its own loads of the next stage (the two stages after it stay in
+  //   flight) and meets the other waves: every wave has consumed its reads of the previous
+  //   stage's buffer by now, so the barrier waits on no LDS read.
+  //   Second half: step 1's sixteen MFMAs in pairs; before each pair go one global->LDS load of
+  //   stage st + 4 into the previous stage's buffer and one read of the next stage's first step.
+  //   A burst of eight loads would stall the wave's issue behind the memory pipeline (one wave per
+  //   SIMD: the matrix core would idle); spread out, each load is accepted while MFMAs run.  The
+  //   scheduling fences keep exactly this order.
   template <int BUF>
   __device__ __forceinline__ void stage(int st, Regs& R0, Regs& R1) {
     read_step(ring + BUF * kNtStage, 1, R1);
     mma(R0);
-    __builtin_amdgcn_s_waitcnt(waitcnt_imm(2 * kNtLoads, 0));
+    interleave_reads();
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(2 * kNtLoads));
     block_barrier_nofence();
-    issue<BUF>(st + kNtRing);
-    read_step(ring + ((BUF + 1) % kNtRing) * kNtStage, 0, R0);
-    mma(R1);
+    constexpr int REFILL = (BUF + kNtRing - 1) % kNtRing;
+    const int stn = min(st + kNtRing - 1, NS - 1);
+    const uint8_t* sa = a + (size_t)stn * kNtRowBytes;
+    const uint8_t* sb = b + (size_t)stn * kNtRowBytes;
+    const uint32_t base = m0 + REFILL * kNtStage;
+    const uint8_t* nbuf = ring + ((BUF + 1) % kNtRing) * kNtStage;
+    static_assert(kNtLoads == kNtWI + kNtWJ && kNtWI * kNtWJ == 2 * kNtLoads, "pairing");
+#pragma unroll
+    for (int q = 0; q < kNtLoads; ++q) {
+      __builtin_amdgcn_sched_barrier(0);
+      if (q < kNtLoads / 2) lds_dma16_s(sa, a_off[q], base + q * 1024);
+      else lds_dma16_s(sb, b_off[q - kNtLoads / 2], base + kNtHalf + (q - kNtLoads / 2) * 1024);
+      read_frag(nbuf, 0, q, R0);
+      mma_one(R1, q / 2, 2 * (q % 2));
+      mma_one(R1, q / 2, 2 * (q % 2) + 1);
+    }
+    __builtin_amdgcn_sched_barrier(0);
   }
 };
 
@@ -295,12 +333,19 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_kernel(NtArgs p) {
   k.wj = wave >> 1;
   k.h = k.lane >> 5;
   k.NS = p.R / 32;
-  // XCD-major tile order: block b runs on XCD b % 8; each XCD walks a contiguous run of tiles with
-  // i fastest, so a run shares its B tile (and neighbouring runs their A tiles) in L2.
+  // XCD-major tile order: block b runs on XCD b % 8 and each XCD takes a contiguous run of tile
+  // numbers t.  Tile numbers run through groups of kNtGroupI row tiles (i) by all column tiles
+  // (j), i fastest inside a group, so the 32 tiles an XCD's 32 CUs hold at once form an 8 x 4
+  // patch: 12 operand tiles per 32 output tiles stay in that XCD's L2, where a run along i alone
+  // (32 x 1) streams 33.
   const int full = (p.tiles / 8) * 8;
   const int b = blockIdx.x;
   const int t = b < full ? (b % 8) * (p.tiles / 8) + b / 8 : b;
-  const int ti = t % p.tiles_i, tj = t / p.tiles_i;
+  const int tiles_j = p.tiles / p.tiles_i;
+  const int per_group = kNtGroupI * tiles_j;
+  const int first_i = (t / per_group) * kNtGroupI;
+  const int gsize = min(p.tiles_i - first_i, kNtGroupI);
+  const int ti = first_i + (t % per_group) % gsize, tj = (t % per_group) / gsize;
   const int i0 = ti * kNtBI, j0 = tj * kNtBJ;
 
   // Load q of a wave covers rows (wave * 4 + q) * 16 .. +15 of the A (or B) part of a stage: lane
@@ -327,11 +372,13 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_kernel(NtArgs p) {
     __builtin_amdgcn_s_waitcnt(waitcnt_imm(3 * kNtLoads));   // stage 0 landed (this wave's part)
     block_barrier_nofence();
     k.read_step(ring, 0, R0);
+    static_assert(kNtRing == 5, "the stage loop is unrolled over the ring");
     for (int st = 0; st < k.NS; st += kNtRing) {
       k.stage<0>(st, R0, R1);
       if (st + 1 < k.NS) k.stage<1>(st + 1, R0, R1);
       if (st + 2 < k.NS) k.stage<2>(st + 2, R0, R1);
       if (st + 3 < k.NS) k.stage<3>(st + 3, R0, R1);
+      if (st + 4 < k.NS) k.stage<4>(st + 4, R0, R1);
     }
     __builtin_amdgcn_s_waitcnt(waitcnt_imm(0));   // no load may still be writing LDS at exit
   }
