@@ -312,32 +312,29 @@ struct BigGemm {
   // Loads of stage st (clamped to the last real stage: the padded stages of the unrolled loop
   // reload valid data that their zeroed codes never use).  The stage advance lives in the scalar
   // base; the one partial stage (K_eff not a multiple of the stage) uses offsets clamped inside
-  // each row.  A loads come in a code half (lanes 0-31) and a meta half (lanes 32-63).
+  // each row.  A loads come in a code half (lanes 0-31) and a meta half (lanes 32-63).  Load q of
+  // a stage: q < B_LOADS the token rows, then per A load a code and (SPARSE) a meta instruction.
   template <int BUF>
-  __device__ __forceinline__ void issue(int st_in) {
+  __device__ __forceinline__ void issue_one(int st_in, int q) {
     const int st = min(st_in, NS - 1);
     const bool partial = (st + 1) * KS > NF;
     const uint32_t m0b = m0_b + BUF * STAGE, m0a = m0_a + BUF * STAGE;
-    const int8_t* sb = xq + (size_t)st * SK;
-    const uint8_t* sc = (const uint8_t*)codes + (size_t)st * (KS * 256);
-    const uint8_t* sm = (const uint8_t*)meta + (size_t)st * (KS * 256);
-    if (!partial) {   // uniform branch: the offsets stay in VGPRs, no per-lane selects
-#pragma unroll
-      for (int i = 0; i < B_LOADS; ++i) lds_dma16_s(sb, b_off[i], m0b + i * 1024);
-#pragma unroll
-      for (int q = 0; q < A_LOADS; ++q) {
-        if (!SP || lane < 32) lds_dma16_s(sc, a_off[q], m0a + q * 1024);
-        if (SP && lane >= 32) lds_dma16_s(sm, a_off[q], m0a + q * 1024);
-      }
+    if (q < B_LOADS) {
+      const int8_t* sb = xq + (size_t)st * SK;
+      lds_dma16_s(sb, partial ? b_off_tail[q] : b_off[q], m0b + q * 1024);
     } else {
-#pragma unroll
-      for (int i = 0; i < B_LOADS; ++i) lds_dma16_s(sb, b_off_tail[i], m0b + i * 1024);
-#pragma unroll
-      for (int q = 0; q < A_LOADS; ++q) {
-        if (!SP || lane < 32) lds_dma16_s(sc, a_off_tail[q], m0a + q * 1024);
-        if (SP && lane >= 32) lds_dma16_s(sm, a_off_tail[q], m0a + q * 1024);
-      }
+      const int qa = (q - B_LOADS) / (SP ? 2 : 1);
+      const bool is_meta = SP && ((q - B_LOADS) & 1);
+      const uint8_t* src = (const uint8_t*)(is_meta ? meta : codes) + (size_t)st * (KS * 256);
+      const uint32_t off = partial ? a_off_tail[qa] : a_off[qa];
+      if (!SP || (lane < 32) != is_meta) lds_dma16_s(src, off, m0a + qa * 1024);
     }
+  }
+
+  template <int BUF>
+  __device__ __forceinline__ void issue(int st_in) {
+#pragma unroll
+    for (int q = 0; q < LPS; ++q) issue_one<BUF>(st_in, q);
   }
 
   // Operands of one MFMA K-step, read from LDS one step ahead of their use.
@@ -395,12 +392,47 @@ struct BigGemm {
     }
   }
 
+  // The last step of a stage, with the refill of this stage's buffer spread over it: before each
+  // MFMA goes one global->LDS load (LPS <= WM * WN; any rest follows), the next stage's first-step
+  // reads go out with the first one.  Issued as a burst, the loads stall the wave behind the memory pipeline while
+  // the matrix core idles; spread out, each is accepted while MFMAs run.  The scheduling fences
+  // keep exactly this order.
+  template <int BUF>
+  __device__ __forceinline__ void mma_step_refill(const StepRegs& r, bool live, int st_refill,
+                                                  StepRegs& nxt) {
+#pragma unroll
+    for (int p = 0; p < WM; ++p) {
+      __builtin_amdgcn_sched_barrier(0);
+      if (p * WN < LPS) issue_one<BUF>(st_refill, p * WN);
+      if (p == 0) read_step(ring + ((BUF + 1) % 3) * STAGE, 0, nxt);
+      const v4i ap = expand_codes(live ? r.code[p] : 0u);
+#pragma unroll
+      for (int g = 0; g < WN; ++g) {
+        if (g > 0) {
+          __builtin_amdgcn_sched_barrier(0);
+          if (p * WN + g < LPS) issue_one<BUF>(st_refill, p * WN + g);
+        }
+        if constexpr (SP) {
+          acc[p][g] = __builtin_amdgcn_smfmac_i32_32x32x64_i8(ap, r.b[g], acc[p][g], (int)r.meta[p], 0, 0);
+        } else {
+          v4i bd;
+          bd[0] = r.b[g][0]; bd[1] = r.b[g][1]; bd[2] = r.b[g][2]; bd[3] = r.b[g][3];
+          acc[p][g] = __builtin_amdgcn_mfma_i32_32x32x32_i8(ap, bd, acc[p][g], 0, 0, 0);
+        }
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int q = WM * WN; q < LPS; ++q) issue_one<BUF>(st_refill, q);
+  }
+
   // One stage (buffer BUF) as KS pipelined steps: while step j's MFMAs run, step j+1's operands
   // are read from LDS into the other register set.  At the last step the next stage's buffer is
   // needed, so the wave first waits for its own loads of that stage (at most the LPS loads of the
   // stage after it stay outstanding) and for its outstanding LDS reads, meets the other waves at a
-  // bare s_barrier (after which no wave reads this stage's buffer again), refills this buffer with
-  // stage st+3 and reads the next stage's first step.  ALL_LIVE: every step of the stage is real.
+  // bare s_barrier (after which no wave reads this stage's buffer again), then refills this buffer
+  // with stage st+3 and reads the next stage's first step while the step's MFMAs run.
+  // ALL_LIVE: every step of the stage is real.
   template <int BUF, bool ALL_LIVE>
   __device__ __forceinline__ void stage(int st, StepRegs& R0, StepRegs& R1) {
 #pragma unroll
@@ -409,13 +441,12 @@ struct BigGemm {
       StepRegs& nxt = (j % 2 == 0) ? R1 : R0;
       if (j + 1 < KS) {
         read_step(ring + BUF * STAGE, j + 1, nxt);
+        mma_step(cur, ALL_LIVE || st * KS + j < NF);
       } else {
         __builtin_amdgcn_s_waitcnt(waitcnt_imm(LPS, 0));
         block_barrier_nofence();
-        issue<BUF>(st + 3);
-        read_step(ring + ((BUF + 1) % 3) * STAGE, 0, nxt);
+        mma_step_refill<BUF>(cur, ALL_LIVE || st * KS + j < NF, st + 3, nxt);
       }
-      mma_step(cur, ALL_LIVE || st * KS + j < NF);
     }
   }
 };
