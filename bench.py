@@ -111,6 +111,17 @@ class Decode:
                                   codes=codes, meta=meta, gamma=gamma, n=n, y=y))
             self.ys[T] = [p["y"] for p in projs]
             self.groups[T] = S.FwdGroup(projs)
+        # fused variant: the same projections read the bf16 rows and quantize them in-kernel
+        self.fused, self.ys_fused = {}, {}
+        for T in DECODE_T:
+            projs = []
+            for i, (n, K, codes, meta, gamma) in enumerate(self.mats):
+                j = i // 2
+                projs.append(dict(x=self.x[(T, K)][j * T:(j + 1) * T], K=K, codes=codes, meta=meta,
+                                  gamma=gamma, n=n,
+                                  y=torch.empty((T, n), dtype=torch.float32, device="cuda")))
+            self.ys_fused[T] = [p["y"] for p in projs]
+            self.fused[T] = S.FusedGroup(projs)
         torch.cuda.synchronize()
 
     def algorithmic_bytes(self, T):
@@ -118,6 +129,20 @@ class Decode:
         fp32 outputs and gamma of every projection."""
         return sum(c.numel() + m.numel() + T * K + 4 * T + 4 * T * n + 4
                    for (n, K, c, m, _) in self.mats)
+
+    def algorithmic_bytes_fused(self, T):
+        """Bytes one fused launch must move: packed weights, bf16 activations, fp32 outputs, gamma."""
+        return sum(c.numel() + m.numel() + 2 * T * K + 4 * T * n + 4
+                   for (n, K, c, m, _) in self.mats)
+
+    def step_fused(self, S, events=None):
+        """One decode step with quantization fused into the grouped GEMV: one launch per T."""
+        for T in DECODE_T:
+            if events is not None:
+                events[T][0].record()
+            self.fused[T]()
+            if events is not None:
+                events[T][1].record()
 
     def step(self, S, events=None):
         """One decode step over the layer stream at every T: quantize the stacked activations
@@ -130,6 +155,62 @@ class Decode:
             self.groups[T]()
             if events is not None:
                 events[T][1].record()
+
+
+def decode_fused_leg(S, torch, D, ref, steps, warmup):
+    """The decode step with act_quant fused into the grouped GEMV (bitlinear_fwd_group_fused):
+    graph-captured, checked bitwise against the plain step's outputs, timed like the main metric."""
+    D.step_fused(S)
+    torch.cuda.synchronize()
+    for T in DECODE_T:
+        for y, r in zip(D.ys_fused[T], ref[T]):
+            if not torch.equal(y, r):
+                raise RuntimeError("fused decode differs from act_quant + grouped GEMV")
+    graph = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    with torch.cuda.graph(graph, stream=cap):
+        D.step_fused(S)
+    for _ in range(2):
+        for T in DECODE_T:
+            for y in D.ys_fused[T]:
+                y.fill_(float("nan"))
+        graph.replay()
+        torch.cuda.synchronize()
+        for T in DECODE_T:
+            for y, r in zip(D.ys_fused[T], ref[T]):
+                if not torch.equal(y, r):
+                    raise RuntimeError("fused graph replay differs from the plain eager run")
+    for _ in range(warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        graph.replay()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    value = D.packed_bytes * len(DECODE_T) / (ms * 1e-3) / 1e9
+    per_T = {T: [] for T in DECODE_T}
+    for _ in range(max(1, min(steps, 10))):
+        events = {T: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  for T in DECODE_T}
+        D.step_fused(S, events)
+        torch.cuda.synchronize()
+        for T in DECODE_T:
+            per_T[T].append(events[T][0].elapsed_time(events[T][1]) * 1e-3)
+    mean_t = {T: float(np.mean(per_T[T])) for T in DECODE_T}
+    algo = {T: D.algorithmic_bytes_fused(T) for T in DECODE_T}
+    achieved = sum(algo.values()) / sum(mean_t.values()) / 1e9
+    return {"workload": "the decode stream with per-token quantization fused into the grouped "
+                        "GEMV: one launch per T, bf16 activations in",
+            "metric": "decode weight GB/s", "value": round(value, 1), "unit": "GB/s",
+            "ms_per_step": round(ms, 4), "outputs_identical_to_unfused": True,
+            "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                         "kernel": "gemv_group_kernel<SPARSE, fused>",
+                         "per_T": {str(T): {"launch_us": round(mean_t[T] * 1e6, 2),
+                                            "algorithmic_bytes": algo[T],
+                                            "GBps": round(algo[T] / mean_t[T] / 1e9, 1)}
+                                   for T in DECODE_T}}}
 
 
 def kernel_source_sha():
@@ -517,6 +598,9 @@ def main():
                      "traffic": traffic, "kernel": "gemv_group_kernel<SPARSE>",
                      "per_T": per_T_out},
     }
+    log("fused decode leg")
+    out["decode_fused"] = decode_fused_leg(S, torch, D, ref, args.steps, args.warmup)
+    log(f"fused decode {out['decode_fused']['value']} GB/s")
     if not args.no_prefill:
         log("prefill leg")
         out["prefill"] = prefill_leg(S, torch)

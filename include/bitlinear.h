@@ -171,6 +171,41 @@ int bitlinear_fwd_group(const void* table, int64_t work_items, int N, int M, int
                         void* stream);
 
 /* ---------------------------------------------------------------------------------------------
+ * Fused decode: activation quantization inside the grouped forward.
+ *
+ * The same grouped forward as above, but each projection hands over its activations x[T][K] as
+ * bfloat16 (bit patterns, row-major) instead of act_quant_i8's int8 rows and token scales: the
+ * kernel takes the per-token absmax and quantizes the rows itself (BitNet b1.58 page, "The
+ * mechanism"), with exactly act_quant_i8's expressions, so y (and acc_opt) are bit-identical to
+ * act_quant_i8 followed by bitlinear_fwd_group.  A decode step then needs one launch instead of a
+ * quantization launch per activation matrix plus the group launch.
+ *
+ * Layouts without activation lifting only: BL_LAYOUT_SPARSE with N:M = 2:4, or BL_LAYOUT_DENSE2
+ * (BL_ENOTSUP otherwise).  Per projection: 0 <= T <= 32, T * K * 2 < 2^31, x 16-byte aligned,
+ * the other rules and the build / launch protocol as for the plain group; projections may share
+ * x.  A fused table launched through bitlinear_fwd_group (or a plain one through
+ * bitlinear_fwd_group_fused) writes nothing.
+ */
+typedef struct bl_fwd_x_desc {
+  const uint16_t* x;     /* [T][K] bf16 activations */
+  int64_t T;             /* tokens, 0..32 */
+  int64_t K;             /* master in-features */
+  const uint8_t* codes;  /* packed codes from bitlinear_pack */
+  const uint8_t* meta;   /* packed meta (SPARSE) or NULL (DENSE2) */
+  const float* gamma;    /* device scalar from bitlinear_pack */
+  int64_t n;             /* out-features */
+  float* y;              /* [T][n] fp32 output */
+  int32_t* acc_opt;      /* [T][n] int32 accumulators, or NULL */
+} bl_fwd_x_desc;
+
+int bitlinear_group_fused_table_bytes(const bl_fwd_x_desc* descs, int64_t count, int N, int M,
+                                      int layout, size_t* table_bytes, int64_t* work_items);
+int bitlinear_group_fused_build(const bl_fwd_x_desc* descs, int64_t count, int N, int M,
+                                int layout, void* table, size_t table_bytes, void* stream);
+int bitlinear_fwd_group_fused(const void* table, int64_t work_items, int N, int M, int layout,
+                              void* stream);
+
+/* ---------------------------------------------------------------------------------------------
  * Backward for training (Sparse-BitNet technical summary, Training Strategie: Dual STE).
  *
  * The rounding, the clip and the Top-N selection are passed straight through, and the gradient

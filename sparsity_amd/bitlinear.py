@@ -2,8 +2,9 @@
 
 Names mirror the C ABI: ``bitlinear_packed_bytes``, ``bitlinear_pack``, ``act_quant_i8``,
 ``bitlinear_fwd``, ``bitlinear_group_table_bytes``, ``bitlinear_group_build``,
-``bitlinear_fwd_group``, ``bitlinear_bwd_workspace_bytes``, ``bitlinear_bwd``.
-``pack`` / ``act_quant`` / ``fwd`` / ``FwdGroup`` / ``bwd`` are convenience
+``bitlinear_fwd_group``, ``bitlinear_group_fused_table_bytes``, ``bitlinear_group_fused_build``,
+``bitlinear_fwd_group_fused``, ``bitlinear_bwd_workspace_bytes``, ``bitlinear_bwd``.
+``pack`` / ``act_quant`` / ``fwd`` / ``FwdGroup`` / ``FusedGroup`` / ``bwd`` are convenience
 wrappers that allocate the output tensors with torch on the input's device and enqueue on torch's
 current stream.
 """
@@ -29,6 +30,13 @@ class BlFwdDesc(ctypes.Structure):
                 ("K", ctypes.c_int64), ("codes", ctypes.c_void_p), ("meta", ctypes.c_void_p),
                 ("gamma", ctypes.c_void_p), ("n", ctypes.c_int64), ("y", ctypes.c_void_p),
                 ("acc_opt", ctypes.c_void_p)]
+
+
+class BlFwdXDesc(ctypes.Structure):
+    """bl_fwd_x_desc: one projection of a fused group (bf16 activations, quantized in-kernel)."""
+    _fields_ = [("x", ctypes.c_void_p), ("T", ctypes.c_int64), ("K", ctypes.c_int64),
+                ("codes", ctypes.c_void_p), ("meta", ctypes.c_void_p), ("gamma", ctypes.c_void_p),
+                ("n", ctypes.c_int64), ("y", ctypes.c_void_p), ("acc_opt", ctypes.c_void_p)]
 
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -62,6 +70,11 @@ def lib() -> ctypes.CDLL:
                                                   ctypes.POINTER(i64)]
         L.bitlinear_group_build.argtypes = [dp, i64, i32, i32, i32, vp, sz, vp]
         L.bitlinear_fwd_group.argtypes = [vp, i64, i32, i32, i32, vp]
+        xp = ctypes.POINTER(BlFwdXDesc)
+        L.bitlinear_group_fused_table_bytes.argtypes = [xp, i64, i32, i32, i32,
+                                                        ctypes.POINTER(sz), ctypes.POINTER(i64)]
+        L.bitlinear_group_fused_build.argtypes = [xp, i64, i32, i32, i32, vp, sz, vp]
+        L.bitlinear_fwd_group_fused.argtypes = [vp, i64, i32, i32, i32, vp]
         L.bitlinear_bwd_workspace_bytes.argtypes = [i64, i64, i64, ctypes.POINTER(sz)]
         L.bitlinear_bwd.argtypes = [vp, i64, i64, vp, vp, i64, vp, vp, vp, i32, i32, i32, vp, vp,
                                     i32, vp, sz, vp]
@@ -71,7 +84,9 @@ def lib() -> ctypes.CDLL:
         for f in (L.bitlinear_packed_bytes, L.bitlinear_pack, L.act_quant_i8, L.bitlinear_fwd,
                   L.bitlinear_layout_version, L.bitlinear_group_table_bytes,
                   L.bitlinear_group_build, L.bitlinear_fwd_group,
-                  L.bitlinear_bwd_workspace_bytes, L.bitlinear_bwd):
+                  L.bitlinear_bwd_workspace_bytes, L.bitlinear_bwd,
+                  L.bitlinear_group_fused_table_bytes, L.bitlinear_group_fused_build,
+                  L.bitlinear_fwd_group_fused):
             f.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -121,6 +136,23 @@ def bitlinear_group_build(descs, N, M, layout, table, table_bytes, stream) -> in
 
 def bitlinear_fwd_group(table, work_items, N, M, layout, stream) -> int:
     return lib().bitlinear_fwd_group(table, work_items, N, M, layout, stream)
+
+
+def bitlinear_group_fused_table_bytes(descs, N, M, layout):
+    """descs: a ctypes array of BlFwdXDesc.  Returns (status, table_bytes, work_items)."""
+    tb, wi = ctypes.c_size_t(), ctypes.c_int64()
+    st = lib().bitlinear_group_fused_table_bytes(descs, len(descs), N, M, layout,
+                                                 ctypes.byref(tb), ctypes.byref(wi))
+    return st, tb.value, wi.value
+
+
+def bitlinear_group_fused_build(descs, N, M, layout, table, table_bytes, stream) -> int:
+    return lib().bitlinear_group_fused_build(descs, len(descs), N, M, layout, table, table_bytes,
+                                             stream)
+
+
+def bitlinear_fwd_group_fused(table, work_items, N, M, layout, stream) -> int:
+    return lib().bitlinear_fwd_group_fused(table, work_items, N, M, layout, stream)
 
 
 def bitlinear_bwd_workspace_bytes(T, n, K):
@@ -243,6 +275,38 @@ class FwdGroup:
     def __call__(self):
         _check(bitlinear_fwd_group(self.table.data_ptr(), self.work_items, self.N, self.M,
                                    self.layout, _stream()), "bitlinear_fwd_group")
+
+
+class FusedGroup:
+    """A built fused group: ``FusedGroup(projs)`` then ``group()`` quantizes and multiplies.
+
+    ``projs`` is a list of dicts with keys x (bf16 CUDA tensor [T][K]), K, codes, meta, gamma, n,
+    y and optionally acc, all sharing (N, M, layout) with no activation lifting (2:4 SPARSE or
+    DENSE2).  Tensors are referenced, not copied; their contents are read at each launch.
+    """
+
+    def __init__(self, projs, N: int = 2, M: int = 4, layout: int = BL_LAYOUT_SPARSE):
+        import torch
+        self.N, self.M, self.layout = N, M, layout
+        self._keep = list(projs)
+        arr = (BlFwdXDesc * len(projs))()
+        for i, p in enumerate(projs):
+            arr[i] = BlFwdXDesc(_ptr(p["x"]), p["x"].shape[0], p["K"], _ptr(p["codes"]),
+                                _ptr(p.get("meta")), _ptr(p["gamma"]), p["n"], _ptr(p["y"]),
+                                _ptr(p.get("acc")))
+        self.descs = arr
+        st, tb, wi = bitlinear_group_fused_table_bytes(arr, N, M, layout)
+        _check(st, "bitlinear_group_fused_table_bytes")
+        dev = projs[0]["codes"].device
+        self.table = torch.empty(max(tb, 16), dtype=torch.uint8, device=dev)
+        self.work_items = wi
+        _check(bitlinear_group_fused_build(arr, N, M, layout, self.table.data_ptr(),
+                                           self.table.numel(), _stream()),
+               "bitlinear_group_fused_build")
+
+    def __call__(self):
+        _check(bitlinear_fwd_group_fused(self.table.data_ptr(), self.work_items, self.N, self.M,
+                                         self.layout, _stream()), "bitlinear_fwd_group_fused")
 
 
 def bwd_workspace_bytes(T: int, n: int, K: int) -> int:

@@ -31,12 +31,6 @@ __device__ __forceinline__ void load8(const void* __restrict__ x, size_t off, fl
   }
 }
 
-__device__ __forceinline__ uint32_t q8(float v, float s) {
-  float r = rintf(v * s);
-  r = fminf(fmaxf(r, -127.f), 127.f);
-  return (uint32_t)(int32_t)r & 0xFFu;
-}
-
 // LM = 0: plain.  LM = 8 or 16: (LM-2):LM activation lifting, each LM-group becomes LM/2 - 1
 // windows of four values, window w = x[2w .. 2w+3] (2LM - 4 bytes per group).
 template <bool BF16, int LM>

@@ -114,6 +114,80 @@ size_t group_table_bytes(int64_t count, size_t items) {
   return (b + 15) / 16 * 16;
 }
 
+// Validates the group and writes its device table; fused: the descriptors' xq are bf16 rows.
+int group_build(const bl_fwd_desc* descs, int64_t count, int N, int M, int layout, int fused,
+                void* table, size_t table_bytes, void* stream) {
+  std::vector<bl::GroupItem> plan;
+  const int st = plan_group(descs, count, N, M, layout, &plan);
+  if (st != BL_OK) return st;
+  const size_t bytes = group_table_bytes(count, plan.size());
+  if (!aligned16(table)) return BL_EINVAL;
+  if (table_bytes < bytes) return BL_ENOSPC;
+  std::vector<uint8_t> img(bytes, 0);
+  bl::GroupHeader hdr;
+  memset(&hdr, 0, sizeof hdr);
+  hdr.magic = bl::kGroupMagic;
+  hdr.layout = layout;
+  hdr.N = N;
+  hdr.M = M;
+  hdr.count = count;
+  hdr.items = (int64_t)plan.size();
+  hdr.fused = fused;
+  memcpy(img.data(), &hdr, sizeof hdr);
+  bl::GroupLayer* rec = (bl::GroupLayer*)(img.data() + sizeof hdr);
+  for (int64_t i = 0; i < count; ++i) {
+    const bl_fwd_desc& d = descs[i];
+    const int64_t ke = keff_of(d.K, M, layout);
+    bl::GroupLayer r;
+    memset(&r, 0, sizeof r);
+    r.xq = d.xq;
+    r.xs = fused ? nullptr : d.x_scale;
+    r.codes = (const uint32_t*)d.codes;
+    r.meta = (const uint32_t*)d.meta;
+    r.gamma = d.gamma;
+    r.y = d.y;
+    r.acc = d.acc_opt;
+    r.T = (int32_t)d.T;
+    r.Keff = (int32_t)ke;
+    r.n = (int32_t)d.n;
+    memcpy(&rec[i], &r, sizeof r);
+  }
+  if (!plan.empty())
+    memcpy(img.data() + sizeof hdr + count * sizeof(bl::GroupLayer), plan.data(),
+           plan.size() * sizeof(bl::GroupItem));
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = hipMemcpyAsync(table, img.data(), bytes, hipMemcpyHostToDevice, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);  // img is released on return
+  return status_of(e);
+}
+
+
+// A fused group's descriptors as plain ones (xq = the bf16 rows; x_scale is not read, the row
+// pointer stands in for the NULL check), after the checks that are the fused path's own: no
+// lifting (2:4 SPARSE or DENSE2) and bf16 rows addressable with 32-bit offsets.
+int fused_as_plain(const bl_fwd_x_desc* d, int64_t count, int M, int layout,
+                   std::vector<bl_fwd_desc>* out) {
+  if (!d || count < 1 || count > (1 << 24)) return BL_EINVAL;
+  if (layout == BL_LAYOUT_SPARSE && M != 4) return BL_ENOTSUP;
+  out->resize((size_t)count);
+  for (int64_t i = 0; i < count; ++i) {
+    if (d[i].T < 0 || d[i].K < 1) return BL_EINVAL;
+    if ((uint64_t)d[i].T * (uint64_t)d[i].K * 2u >= (1ull << 31)) return BL_EINVAL;
+    bl_fwd_desc& p = (*out)[(size_t)i];
+    p.xq = (const int8_t*)d[i].x;
+    p.x_scale = (const float*)d[i].x;
+    p.T = d[i].T;
+    p.K = d[i].K;
+    p.codes = d[i].codes;
+    p.meta = d[i].meta;
+    p.gamma = d[i].gamma;
+    p.n = d[i].n;
+    p.y = d[i].y;
+    p.acc_opt = d[i].acc_opt;
+  }
+  return BL_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -191,47 +265,7 @@ int bitlinear_group_table_bytes(const bl_fwd_desc* descs, int64_t count, int N, 
 
 int bitlinear_group_build(const bl_fwd_desc* descs, int64_t count, int N, int M, int layout,
                           void* table, size_t table_bytes, void* stream) {
-  std::vector<bl::GroupItem> plan;
-  const int st = plan_group(descs, count, N, M, layout, &plan);
-  if (st != BL_OK) return st;
-  const size_t bytes = group_table_bytes(count, plan.size());
-  if (!aligned16(table)) return BL_EINVAL;
-  if (table_bytes < bytes) return BL_ENOSPC;
-  std::vector<uint8_t> img(bytes, 0);
-  bl::GroupHeader hdr;
-  memset(&hdr, 0, sizeof hdr);
-  hdr.magic = bl::kGroupMagic;
-  hdr.layout = layout;
-  hdr.N = N;
-  hdr.M = M;
-  hdr.count = count;
-  hdr.items = (int64_t)plan.size();
-  memcpy(img.data(), &hdr, sizeof hdr);
-  bl::GroupLayer* rec = (bl::GroupLayer*)(img.data() + sizeof hdr);
-  for (int64_t i = 0; i < count; ++i) {
-    const bl_fwd_desc& d = descs[i];
-    const int64_t ke = keff_of(d.K, M, layout);
-    bl::GroupLayer r;
-    memset(&r, 0, sizeof r);
-    r.xq = d.xq;
-    r.xs = d.x_scale;
-    r.codes = (const uint32_t*)d.codes;
-    r.meta = (const uint32_t*)d.meta;
-    r.gamma = d.gamma;
-    r.y = d.y;
-    r.acc = d.acc_opt;
-    r.T = (int32_t)d.T;
-    r.Keff = (int32_t)ke;
-    r.n = (int32_t)d.n;
-    memcpy(&rec[i], &r, sizeof r);
-  }
-  if (!plan.empty())
-    memcpy(img.data() + sizeof hdr + count * sizeof(bl::GroupLayer), plan.data(),
-           plan.size() * sizeof(bl::GroupItem));
-  hipStream_t s = (hipStream_t)stream;
-  hipError_t e = hipMemcpyAsync(table, img.data(), bytes, hipMemcpyHostToDevice, s);
-  if (e == hipSuccess) e = hipStreamSynchronize(s);  // img is released on return
-  return status_of(e);
+  return group_build(descs, count, N, M, layout, 0, table, table_bytes, stream);
 }
 
 int bitlinear_fwd_group(const void* table, int64_t work_items, int N, int M, int layout,
@@ -242,7 +276,35 @@ int bitlinear_fwd_group(const void* table, int64_t work_items, int N, int M, int
   if (work_items < 0 || work_items > INT32_MAX) return BL_EINVAL;
   if (work_items == 0) return BL_OK;
   if (!aligned16(table)) return BL_EINVAL;
-  return status_of(bl::launch_fwd_group(table, work_items, layout, (hipStream_t)stream));
+  return status_of(bl::launch_fwd_group(table, work_items, layout, 0, (hipStream_t)stream));
+}
+
+int bitlinear_group_fused_table_bytes(const bl_fwd_x_desc* descs, int64_t count, int N, int M,
+                                      int layout, size_t* table_bytes, int64_t* work_items) {
+  std::vector<bl_fwd_desc> plain;
+  const int st = fused_as_plain(descs, count, M, layout, &plain);
+  if (st != BL_OK) return st;
+  return bitlinear_group_table_bytes(plain.data(), count, N, M, layout, table_bytes, work_items);
+}
+
+int bitlinear_group_fused_build(const bl_fwd_x_desc* descs, int64_t count, int N, int M,
+                                int layout, void* table, size_t table_bytes, void* stream) {
+  std::vector<bl_fwd_desc> plain;
+  const int st = fused_as_plain(descs, count, M, layout, &plain);
+  if (st != BL_OK) return st;
+  return group_build(plain.data(), count, N, M, layout, 1, table, table_bytes, stream);
+}
+
+int bitlinear_fwd_group_fused(const void* table, int64_t work_items, int N, int M, int layout,
+                              void* stream) {
+  int64_t ke = 0;
+  const int st = check_shape(1, 256, N, M, layout, &ke);  // N:M and layout only
+  if (st != BL_OK) return st;
+  if (layout == BL_LAYOUT_SPARSE && M != 4) return BL_ENOTSUP;
+  if (work_items < 0 || work_items > INT32_MAX) return BL_EINVAL;
+  if (work_items == 0) return BL_OK;
+  if (!aligned16(table)) return BL_EINVAL;
+  return status_of(bl::launch_fwd_group(table, work_items, layout, 1, (hipStream_t)stream));
 }
 
 int bitlinear_bwd_workspace_bytes(int64_t T, int64_t n, int64_t K, size_t* ws_bytes) {

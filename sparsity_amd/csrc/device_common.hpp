@@ -55,6 +55,15 @@ __device__ __forceinline__ v16i mfma_step(uint32_t code, uint32_t meta, const in
   }
 }
 
+// One activation onto the int8 grid: clamp(rint(fl32(v * s)), -127, 127) with round-half-even,
+// as an unsigned byte.  s = fl32(127 / absmax) of the token (BitNet b1.58 page, "The mechanism",
+// per-token absmax quantization to [-Qb, Qb]).
+__device__ __forceinline__ uint32_t q8(float v, float s) {
+  float r = rintf(v * s);
+  r = fminf(fmaxf(r, -127.f), 127.f);
+  return (uint32_t)(int32_t)r & 0xFFu;
+}
+
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o, 64));

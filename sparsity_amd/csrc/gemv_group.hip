@@ -19,6 +19,14 @@
 //   - the MFMAs read their B fragments from LDS (row stride + 16 bytes keeps 16 tokens' 16-byte
 //     reads on distinct banks).
 // Steps past the end of K re-read the last step with the code forced to 0 (zero weights add 0).
+//
+// Fused variant (tables built by bitlinear_group_fused_build): the projections hold bf16
+// activations instead of int8 ones, and the kernel quantizes them itself (per-token absmax, BitNet
+// b1.58 page, "The mechanism"), so a decode step needs no separate quantization launch.  Each work
+// item first takes the absmax of its projection's T token rows (the rows are shared by all items
+// of the projection and come from L2), then its token pieces ride the ring as bf16 and are
+// quantized on their way into LDS with the very expression of act_quant_i8, so results are
+// bit-identical to act_quant_i8 + the plain group.  Only unlifted layouts (2:4 SPARSE, DENSE2).
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -33,29 +41,32 @@ typedef __attribute__((address_space(1))) const v4i g_v4i;
 }  // namespace
 
 // One chunk of the register ring: a wave's code/meta dwords for kGS steps and this thread's share
-// of the block's token rows for the same K range.
-template <int BPT>
+// of the block's token rows for the same K range (a 16-position piece: 16 int8 bytes, or 32 bytes
+// of bf16 in the fused variant).
+template <int BPT, int VPP>
 struct GroupChunk {
   uint32_t c[kGS], m[kGS];
-  v4i b[BPT];
+  v4i b[BPT * VPP];
 };
 
-template <int LAYOUT>
+template <int LAYOUT, bool FUSED>
 struct GroupGemv {
   static constexpr bool SP = LAYOUT == kLayoutSparse;
   static constexpr int KSTEP = SP ? 64 : 32;           // K positions per MFMA step
   static constexpr int NT = 64 * kGroupWaves;
   static constexpr int CB = kGS * KSTEP;               // bytes of one token row per chunk
   static constexpr int ROW = CB + 16;                  // LDS row stride
-  static constexpr int V16 = CB / 16;                  // 16-byte pieces per token row per chunk
+  static constexpr int V16 = CB / 16;                  // 16-position pieces per token row per chunk
   static constexpr int BPT = (32 * V16 + NT - 1) / NT; // pieces per thread at T = 32
-  typedef GroupChunk<BPT> Chunk;
+  static constexpr int VPP = FUSED ? 2 : 1;            // 16-byte loads per piece
+  typedef GroupChunk<BPT, VPP> Chunk;
 
   int8_t* bs;             // LDS: two buffers of 32 rows x ROW bytes
   g_u32* cp;              // this lane's code dword of step 0 of the wave's panel
   g_u32* mp;
-  __attribute__((address_space(1))) const int8_t* xq;
+  __attribute__((address_space(1))) const int8_t* xq;   // int8 rows, or bf16 rows (fused)
   int tid, T, Keff, NF, nch, bpieces, brow, h;
+  float qs[BPT];          // fused: 127 / absmax of the token row of each of this thread's pieces
   v16i acc;
 
   // Every call issues the same number of loads (addresses clamped into the projection), so the
@@ -72,7 +83,27 @@ struct GroupGemv {
     for (int k = 0; k < BPT; ++k) {
       const int pc = tid + k * NT;
       const int row = min(pc / V16, T - 1), col = min(16 * (pc % V16) + j * CB, Keff - 16);
-      r.b[k] = *(g_v4i*)(xq + (size_t)row * Keff + col);
+      const size_t e = (size_t)row * Keff + col;   // element offset of the piece
+#pragma unroll
+      for (int v = 0; v < VPP; ++v) r.b[k * VPP + v] = *(g_v4i*)(xq + e * VPP + 16 * v);
+    }
+  }
+  // int8 bytes of one piece: as loaded, or (fused) 16 bf16 values quantized with the token's s
+  __device__ __forceinline__ v4i piece(const Chunk& r, int k) const {
+    if constexpr (!FUSED) {
+      return r.b[k];
+    } else {
+      v4i out;
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        const uint32_t w0 = (uint32_t)r.b[2 * k + d / 2][2 * (d % 2)];
+        const uint32_t w1 = (uint32_t)r.b[2 * k + d / 2][2 * (d % 2) + 1];
+        out[d] = (int)(q8(__uint_as_float(w0 << 16), qs[k]) |
+                       (q8(__uint_as_float(w0 & 0xFFFF0000u), qs[k]) << 8) |
+                       (q8(__uint_as_float(w1 << 16), qs[k]) << 16) |
+                       (q8(__uint_as_float(w1 & 0xFFFF0000u), qs[k]) << 24));
+      }
+      return out;
     }
   }
   __device__ __forceinline__ void put(int j, const Chunk& r) const {
@@ -80,7 +111,7 @@ struct GroupGemv {
 #pragma unroll
     for (int k = 0; k < BPT; ++k) {
       const int pc = tid + k * NT;
-      if (pc < bpieces) *(v4i*)&dst[(pc / V16) * ROW + 16 * (pc % V16)] = r.b[k];
+      if (pc < bpieces) *(v4i*)&dst[(pc / V16) * ROW + 16 * (pc % V16)] = piece(r, k);
     }
   }
   __device__ __forceinline__ void compute(int j, const Chunk& r) {
@@ -102,16 +133,20 @@ struct GroupGemv {
   }
 };
 
-template <int LAYOUT>
+template <int LAYOUT, bool FUSED>
 __global__ __launch_bounds__(64 * kGroupWaves, 2) void gemv_group_kernel(
     const uint8_t* __restrict__ table) {
-  typedef GroupGemv<LAYOUT> G;
+  typedef GroupGemv<LAYOUT, FUSED> G;
   __shared__ __attribute__((aligned(16))) int8_t bs[2 * 32 * G::ROW];
+  __shared__ float tok_s[32], tok_scale[32];   // fused: 127 / absmax and absmax / 127 per token
 
   const GroupHeader* hdr = (const GroupHeader*)table;
   const int item = blockIdx.x;
-  // uniform across the block: a table of another layout, or a grid larger than the table, does nothing
-  if (hdr->magic != kGroupMagic || hdr->layout != LAYOUT || item >= hdr->items) return;
+  // uniform across the block: a table of another layout or kind, or a grid larger than the
+  // table, does nothing
+  if (hdr->magic != kGroupMagic || hdr->layout != LAYOUT || hdr->fused != (int)FUSED ||
+      item >= hdr->items)
+    return;
   const GroupItem it = ((const GroupItem*)(table + sizeof(GroupHeader) +
                                            hdr->count * sizeof(GroupLayer)))[item];
   if (it.layer == kGroupNoItem) return;
@@ -137,7 +172,35 @@ __global__ __launch_bounds__(64 * kGroupWaves, 2) void gemv_group_kernel(
   k.h = lane >> 5;
   k.brow = min(tok, k.T - 1);                // dead token lanes read a live row
   const float gamma = *(__attribute__((address_space(1))) const float*)L.gamma;
-  const float sc = *((__attribute__((address_space(1))) const float*)L.xs + k.brow);
+  if constexpr (FUSED) {
+    // absmax of each token row over all K (max of the |x| bit patterns: exact, order free), one
+    // wave per row, 8 bf16 per lane per load; then the two scales exactly as act_quant_i8 forms
+    // them
+    for (int t = wave; t < k.T; t += kGroupWaves) {
+      g_v4i* rowp = (g_v4i*)(k.xq + (size_t)t * k.Keff * 2);
+      uint32_t mx = 0;
+#pragma unroll 4
+      for (int c = lane; c < k.Keff / 8; c += 64) {
+        const v4i u = rowp[c];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint32_t w = (uint32_t)u[q];
+          mx = max(mx, max(w & 0x7FFFu, (w >> 16) & 0x7FFFu));
+        }
+      }
+      mx = wave_max_u32(mx);
+      if (lane == 0) {
+        const float amax = __uint_as_float(mx << 16);
+        tok_s[t] = amax > 0.f ? 127.f / amax : 0.f;
+        tok_scale[t] = amax / 127.f;
+      }
+    }
+    block_sync_lds();
+#pragma unroll
+    for (int q = 0; q < G::BPT; ++q) k.qs[q] = tok_s[min((k.tid + q * G::NT) / G::V16, k.T - 1)];
+  }
+  const float sc = FUSED ? tok_scale[k.brow]
+                         : *((__attribute__((address_space(1))) const float*)L.xs + k.brow);
 
   typename G::Chunk r[kGD];
   // chunk by chunk, in the loop's issue order: the wait for a chunk in the loop is then the same
@@ -147,6 +210,7 @@ __global__ __launch_bounds__(64 * kGroupWaves, 2) void gemv_group_kernel(
     k.issue(q, r[q]);
     asm volatile("" ::: "memory");
   }
+
   k.put(0, r[0]);
   block_sync_lds();
   k.acc = v16i{};
@@ -183,12 +247,17 @@ __global__ __launch_bounds__(64 * kGroupWaves, 2) void gemv_group_kernel(
   }
 }
 
-hipError_t launch_fwd_group(const void* table, int64_t items, int layout, hipStream_t s) {
+hipError_t launch_fwd_group(const void* table, int64_t items, int layout, int fused,
+                            hipStream_t s) {
   const dim3 grid((unsigned)items), block(64 * kGroupWaves);
-  if (layout == kLayoutSparse)
-    gemv_group_kernel<kLayoutSparse><<<grid, block, 0, s>>>((const uint8_t*)table);
-  else
-    gemv_group_kernel<kLayoutDense2><<<grid, block, 0, s>>>((const uint8_t*)table);
+  const uint8_t* t = (const uint8_t*)table;
+  if (layout == kLayoutSparse) {
+    if (fused) gemv_group_kernel<kLayoutSparse, true><<<grid, block, 0, s>>>(t);
+    else gemv_group_kernel<kLayoutSparse, false><<<grid, block, 0, s>>>(t);
+  } else {
+    if (fused) gemv_group_kernel<kLayoutDense2, true><<<grid, block, 0, s>>>(t);
+    else gemv_group_kernel<kLayoutDense2, false><<<grid, block, 0, s>>>(t);
+  }
   return hipGetLastError();
 }
 

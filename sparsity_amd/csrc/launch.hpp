@@ -38,13 +38,15 @@ struct GroupHeader {
   uint32_t magic;
   int32_t layout, N, M;
   int64_t count, items;
-  int64_t reserved[4];
+  int32_t fused;          // 1: layers hold bf16 activations, quantized inside the kernel
+  int32_t pad;
+  int64_t reserved[3];
 };
 static_assert(sizeof(GroupHeader) == 64, "group table header is 64 bytes");
 
 struct GroupLayer {
-  const int8_t* xq;
-  const float* xs;
+  const int8_t* xq;       // int8 activations, or (fused) bf16 activations [T][K]
+  const float* xs;        // token scales (not used by fused tables)
   const uint32_t* codes;
   const uint32_t* meta;
   const float* gamma;
@@ -59,7 +61,8 @@ struct GroupItem {
   uint32_t panel0;  // first 32-row panel of the item
 };
 
-hipError_t launch_fwd_group(const void* table, int64_t items, int layout, hipStream_t s);
+hipError_t launch_fwd_group(const void* table, int64_t items, int layout, int fused,
+                            hipStream_t s);
 
 }  // namespace bl
 

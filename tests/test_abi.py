@@ -229,3 +229,31 @@ def test_bwd_rejects_before_launch(L):
     assert call(T=1 << 20, n=1024, K=256) == -22
     # dX only with no tokens: nothing to do, nothing enqueued, token buffers may be NULL
     assert call(T=0, dw=None, dy=None, xq=None, xs=None) == 0
+
+
+def _xdesc(L, **kw):
+    P = FAKE
+    a = dict(x=P, T=4, K=256, codes=P, meta=P, gamma=P, n=100, y=P, acc_opt=None)
+    a.update(kw)
+    return L.BlFwdXDesc(**a)
+
+
+def test_fused_group_sizes_and_rejects_before_launch(L):
+    """The fused group plans exactly like the plain one; it refuses lifted layouts."""
+    xs = (L.BlFwdXDesc * 3)(_xdesc(L), _xdesc(L, n=6912, K=2560, T=16), _xdesc(L, T=0, x=None))
+    ps = (L.BlFwdDesc * 3)(_desc(L), _desc(L, n=6912, K=2560, T=16), _desc(L, T=0, xq=None))
+    assert L.bitlinear_group_fused_table_bytes(xs, 2, 4, 0) == L.bitlinear_group_table_bytes(ps, 2, 4, 0)
+
+    def one(N=2, M=4, layout=0, **kw):
+        return L.bitlinear_group_fused_table_bytes((L.BlFwdXDesc * 1)(_xdesc(L, **kw)), N, M, layout)[0]
+    assert one() == 0
+    assert one(N=6, M=8, K=512) == -95             # lifted layouts are not fused
+    assert one(N=14, M=16, K=512) == -95
+    assert one(N=6, M=8, layout=1, meta=None) == 0  # dense 2-bit 6:8 has no lifting
+    assert one(T=33) == -22
+    assert one(x=FAKE + 8) == -22
+    assert one(x=None) == -22
+    assert L.bitlinear_group_fused_build(xs, 2, 4, 0, FAKE, 16, None) == -28
+    assert L.bitlinear_fwd_group_fused(FAKE, 3, 6, 8, 0, None) == -95
+    assert L.bitlinear_fwd_group_fused(FAKE + 4, 3, 2, 4, 0, None) == -22
+    assert L.bitlinear_fwd_group_fused(None, 0, 2, 4, 0, None) == 0

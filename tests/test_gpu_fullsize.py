@@ -52,7 +52,8 @@ def _check_sampled(ref, x, y, acc, toks, rows, what):
 
 def test_decode_full_size_grouped():
     """FFN up 6912x2560 and down 2560x6912 (2:4) at T = 1, 4, 16 in one grouped launch, as the
-    decode benchmark runs them; every output compared; single-projection calls agree bitwise."""
+    decode benchmark runs them; every output compared; single-projection calls and the fused
+    (in-kernel quantization) group agree bitwise."""
     import torch
     d = workload_inputs("decode", 0)
     projs = []
@@ -69,6 +70,19 @@ def test_decode_full_size_grouped():
                               acc=torch.empty((T, n), dtype=torch.int32, device="cuda"),
                               ref=ref, x=x, name=f"{name} T={T}"))
     S.FwdGroup(projs)()
+    # the same projections with quantization fused into the grouped GEMV: bitwise the same
+    fused = []
+    for name, K in (("up", 2560), ("down", 6912)):
+        for T in (1, 4, 16):
+            p = next(q for q in projs if q["name"] == f"{name} T={T}")
+            fused.append(dict(x=_bf16_dev(d[f"Xbits:{K}"][:T]), K=K, codes=p["codes"],
+                              meta=p["meta"], gamma=p["gamma"], n=p["n"],
+                              y=torch.empty_like(p["y"]), acc=torch.empty_like(p["acc"]), ref=p))
+    S.FusedGroup(fused)()
+    for f in fused:
+        assert np.array_equal(f32_bits(host(f["y"])), f32_bits(host(f["ref"]["y"]))), f["ref"]["name"]
+        assert np.array_equal(host(f["acc"]), host(f["ref"]["acc"])), f["ref"]["name"]
+    print("decode fused group: bitwise equal to act_quant + group", flush=True)
     for p in projs:
         q, s = O.act_quant(p["x"], 0)
         acc_ref = O.acc_dense(p["ref"]["W_eff"], q)
