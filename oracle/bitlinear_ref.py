@@ -52,9 +52,6 @@ Packed layout (layout id 2), the format of the library's packed buffers:
   (00 = 0, 01 = +1, 10 = -1; 11 is never written) and a 2-bit position index 0..3
   within the window.
   DENSE2 layout: every position is a slot with a 2-bit code and no index.
-  SPARSE_X8 layout (id 2, for the prefill GEMM): the SPARSE slots and meta, but each unit's 16
-  slot values are stored as 16 signed bytes (slot i at byte i) in a 16-byte record that sits
-  where SPARSE puts the unit's code dword (record index = dword index below).
   A *unit* is 16 consecutive slots of one row (row r, unit c) and is stored as
   one little-endian code dword -- slot i at bits 8*(i%4) + 2*(i//4) -- and,
   for SPARSE, one meta dword -- slot i's index at bits 2*i.  Units are tiled
@@ -72,8 +69,7 @@ Pinned functions (tests/test_oracle_*.py) and what pins them:
                      threshold |w| * 2^25 > gamma * (2^24 + 1), sign symmetry
   window_table       worked examples (6:8, 14:16); every valid 6:8 and 14:16
                      mask is decomposed and reconstructs
-  pack / unpack      hand-encoded dwords and x8 records (tests/golden), round trip, x8 records
-                     equal to the decoded SPARSE code dwords
+  pack / unpack      hand-encoded dwords (tests/golden), round trip
   act_quant          worked example with exact halves, invariants
   acc_dense          brute-force Python loops on tiny inputs; agrees with the
                      add/sub form acc_addsub; 6:8 and 14:16 lifted == dense
@@ -95,13 +91,12 @@ import numpy as np
 
 LAYOUT_SPARSE = 0
 LAYOUT_DENSE2 = 1
-LAYOUT_SPARSE_X8 = 2      # SPARSE slots and meta, slot values stored as int8 (prefill layout)
 QB = 127                  # activation range [-Qb, Qb]
 PANEL = 32                # rows per tile panel
 PAD_META = 0x44444444     # meta dword of a padded row: every window (0, 1)
 
 __all__ = [
-    "LAYOUT_SPARSE", "LAYOUT_DENSE2", "LAYOUT_SPARSE_X8", "QB", "PAD_META", "is_sparse",
+    "LAYOUT_SPARSE", "LAYOUT_DENSE2", "QB", "PAD_META",
     "round_ratio_to_f32", "absmean_gamma", "nm_mask", "ternarize", "effective_weights",
     "WINDOW_M", "window_table", "window_table_68", "k_eff", "packed_dwords", "weight_slots",
     "pack", "unpack_slots", "slots_to_dense", "act_quant", "lift", "lift_68", "acc_dense",
@@ -260,12 +255,6 @@ def window_table_68() -> Dict[int, List[List[int]]]:
 # slots and the packed layout
 # ----------------------------------------------------------------------------------------------
 
-def is_sparse(layout: int) -> bool:
-    """SPARSE and SPARSE_X8 hold the same slots and meta; they differ only in how slot values are
-    stored (2-bit codes, or int8)."""
-    return layout in (LAYOUT_SPARSE, LAYOUT_SPARSE_X8)
-
-
 def k_eff(K: int, N: int, M: int, layout: int) -> int:
     """Length of the packed K axis: K for 2:4 and DENSE2, (2M - 4) K / M for (M-2):M windows
     (3K/2 for 6:8, 7K/4 for 14:16)."""
@@ -286,8 +275,6 @@ def packed_dwords(n: int, K: int, N: int, M: int, layout: int) -> Tuple[int, int
         assert K % 32 == 0
         return n_pad * K // 16, 0, n_pad
     assert ke % 64 == 0
-    if layout == LAYOUT_SPARSE_X8:                           # one byte per slot
-        return n_pad * ke // 8, n_pad * ke // 32, n_pad
     return n_pad * ke // 32, n_pad * ke // 32, n_pad
 
 
@@ -335,19 +322,6 @@ def _untile(flat: np.ndarray, n_pad: int, U: int) -> np.ndarray:
     return np.ascontiguousarray(t.transpose(0, 3, 1, 2)).reshape(n_pad, U)
 
 
-def _tile_x8(units: np.ndarray) -> np.ndarray:
-    """[n_pad][U][16] int8 unit records -> flat tiled bytes, each record where _tile puts its
-    unit's code dword (record index = dword index, 16 bytes per record)."""
-    n_pad, U, _ = units.shape
-    t = units.reshape(n_pad // PANEL, PANEL, U // 2, 2, 16)  # [P][r][F][h][16]
-    return np.ascontiguousarray(t.transpose(0, 2, 3, 1, 4)).reshape(-1)
-
-
-def _untile_x8(flat: np.ndarray, n_pad: int, U: int) -> np.ndarray:
-    t = flat.reshape(n_pad // PANEL, U // 2, 2, PANEL, 16)   # [P][F][h][r][16]
-    return np.ascontiguousarray(t.transpose(0, 3, 1, 2, 4)).reshape(n_pad, U, 16)
-
-
 def pack(W: np.ndarray, N: int, M: int, layout: int = LAYOUT_SPARSE):
     """Mask + ternarize + pack a fp32 master (the library's pack call, layout id 2).
 
@@ -363,15 +337,12 @@ def pack(W: np.ndarray, N: int, M: int, layout: int = LAYOUT_SPARSE):
     U = S // 16
     v = np.zeros((n_pad, S), dtype=np.int8)
     v[:n] = vals
-    if layout == LAYOUT_SPARSE_X8:
-        codes = _tile_x8(v.reshape(n_pad, U, 16)).view(np.uint32)    # slot i of a unit = byte i
-    else:
-        code2 = np.where(v < 0, 2, v).astype(np.uint32)              # 0 -> 00, +1 -> 01, -1 -> 10
-        code_units = (code2.reshape(n_pad, U, 16) << _CODE_SHIFT).sum(
-            axis=-1, dtype=np.uint64).astype(np.uint32)
-        codes = _tile(code_units)
+    code2 = np.where(v < 0, 2, v).astype(np.uint32)                  # 0 -> 00, +1 -> 01, -1 -> 10
+    code_units = (code2.reshape(n_pad, U, 16) << _CODE_SHIFT).sum(
+        axis=-1, dtype=np.uint64).astype(np.uint32)
+    codes = _tile(code_units)
     meta = None
-    if is_sparse(layout):
+    if layout == LAYOUT_SPARSE:
         ix = np.zeros((n_pad, S), dtype=np.uint8)
         ix[:, 1::2] = 1                                      # padded rows: windows (0, 1)
         ix[:n] = idx
@@ -380,7 +351,7 @@ def pack(W: np.ndarray, N: int, M: int, layout: int = LAYOUT_SPARSE):
         meta = _tile(meta_units)
         assert meta.size == nmeta
     assert codes.size == ncode
-    return dict(codes=codes, meta=meta, gamma=gamma, K_eff=S * 2 if is_sparse(layout) else S,
+    return dict(codes=codes, meta=meta, gamma=gamma, K_eff=S * 2 if layout == LAYOUT_SPARSE else S,
                 n_pad=n_pad, W_eff=W_eff, keep=keep)
 
 
@@ -390,16 +361,12 @@ def unpack_slots(codes: np.ndarray, meta, n: int, K: int, N: int, M: int, layout
     codes = np.asarray(codes).view(np.uint32).reshape(-1)
     assert codes.size == ncode
     ke = k_eff(K, N, M, layout)
-    S = ke // 2 if is_sparse(layout) else ke
+    S = ke // 2 if layout == LAYOUT_SPARSE else ke
     U = S // 16
-    if layout == LAYOUT_SPARSE_X8:
-        vals = _untile_x8(codes.view(np.int8), n_pad, U)[:n].reshape(n, S)
-        assert np.all(np.abs(vals.astype(np.int64)) <= 1), "slot values are ternary"
-    else:
-        cu = _untile(codes, n_pad, U)[:n]                                # [n][U]
-        raw = (cu[..., None] >> _CODE_SHIFT) & 3                          # [n][U][16]
-        assert not np.any(raw == 3), "code 11 is never written"
-        vals = np.where(raw == 2, -1, raw).astype(np.int8).reshape(n, S)
+    cu = _untile(codes, n_pad, U)[:n]                                    # [n][U]
+    raw = (cu[..., None] >> _CODE_SHIFT) & 3                              # [n][U][16]
+    assert not np.any(raw == 3), "code 11 is never written"
+    vals = np.where(raw == 2, -1, raw).astype(np.int8).reshape(n, S)
     if layout == LAYOUT_DENSE2:
         return vals, None
     mu = _untile(np.asarray(meta).view(np.uint32).reshape(-1), n_pad, U)[:n]
@@ -503,7 +470,7 @@ def rescale(acc: np.ndarray, gamma: np.float32, scale: np.ndarray) -> np.ndarray
 def forward(W: np.ndarray, x: np.ndarray, N: int, M: int, layout: int = LAYOUT_SPARSE) -> Dict:
     """Whole path: pack the master, quantize (and lift) x, accumulate, rescale."""
     p = pack(W, N, M, layout)
-    lift = M if (is_sparse(layout) and M in WINDOW_M) else 0
+    lift = M if (layout == LAYOUT_SPARSE and M in WINDOW_M) else 0
     xq, scale = act_quant(x, lift)
     acc = acc_dense(p["W_eff"], act_quant(x, 0)[0])
     y = rescale(acc, p["gamma"], scale)

@@ -256,42 +256,9 @@ def test_pack_golden_unit():
     assert np.all(meta[others] == pad)
 
 
-def test_pack_golden_unit_x8():
-    """Hand-encoded records of the int8 prefill layout (tests/golden/pack_2of4_unit.txt)."""
-    kv = read_kv("pack_2of4_unit.txt")
-    half = np.array([float(v) for v in kv["W"]], dtype=np.float32)
-    W = np.concatenate([half, -half]).reshape(1, 64)
-    p = O.pack(W, 2, 4, O.LAYOUT_SPARSE_X8)
-    b = p["codes"].view(np.uint8).reshape(64, 16)
-    assert b[0].tolist() == [int(v, 16) for v in kv["x8_record_0"]]
-    assert b[32].tolist() == [int(v, 16) for v in kv["x8_record_32"]]
-    others = [i for i in range(64) if i not in (0, 32)]
-    assert not b[others].any()
-    assert np.array_equal(p["meta"], O.pack(W, 2, 4, O.LAYOUT_SPARSE)["meta"])
-
-
-@pytest.mark.parametrize("N,M", [(2, 4), (6, 8), (14, 16)])
-def test_pack_x8_is_the_sparse_slots(N, M):
-    """SPARSE_X8 holds exactly the SPARSE layout's slots (decoded from the 2-bit codes) and the
-    very same meta, record by record."""
-    g = np.random.default_rng(80 + M)
-    n, K = 70, 512
-    W = g.normal(0, 0.02, (n, K)).astype(np.float32)
-    ps, px = O.pack(W, N, M, O.LAYOUT_SPARSE), O.pack(W, N, M, O.LAYOUT_SPARSE_X8)
-    assert np.array_equal(ps["meta"], px["meta"])
-    assert px["codes"].size == 4 * ps["codes"].size
-    # decode every SPARSE code dword by its bit layout and compare with the x8 record
-    raw = (ps["codes"][:, None] >> np.array([8 * (i % 4) + 2 * (i // 4) for i in range(16)],
-                                             np.uint32)) & 3
-    want = np.where(raw == 2, -1, raw).astype(np.int8)
-    assert np.array_equal(px["codes"].view(np.int8).reshape(-1, 16), want)
-
-
 @pytest.mark.parametrize("N,M,layout", [(2, 4, O.LAYOUT_SPARSE), (6, 8, O.LAYOUT_SPARSE),
                                         (14, 16, O.LAYOUT_SPARSE), (2, 4, O.LAYOUT_DENSE2),
-                                        (6, 8, O.LAYOUT_DENSE2), (14, 16, O.LAYOUT_DENSE2),
-                                        (2, 4, O.LAYOUT_SPARSE_X8), (6, 8, O.LAYOUT_SPARSE_X8),
-                                        (14, 16, O.LAYOUT_SPARSE_X8)])
+                                        (6, 8, O.LAYOUT_DENSE2), (14, 16, O.LAYOUT_DENSE2)])
 def test_pack_roundtrip(N, M, layout):
     g = np.random.default_rng(N + M + layout)
     n, K = 45, 256
