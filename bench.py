@@ -112,6 +112,7 @@ class Decode:
             self.ys[T] = [p["y"] for p in projs]
             self.groups[T] = S.FwdGroup(projs)
         # fused variant: the same projections read the bf16 rows and quantize them in-kernel
+        self.last_ms_per_step = None
         self.fused, self.ys_fused = {}, {}
         for T in DECODE_T:
             projs = []
@@ -213,6 +214,61 @@ def decode_fused_leg(S, torch, D, ref, steps, warmup):
                                    for T in DECODE_T}}}
 
 
+def decode_dense_leg(S, torch, D, steps, warmup):
+    """Comparator: the same decode stream on dense ternary weights (every position a 2-bit code,
+    no mask: the BitNet b1.58 layer without Sparse-BitNet's N:M, BL_LAYOUT_DENSE2 with N = M = 4),
+    same activations and launch structure.  Both formats move 0.25 B per dense weight."""
+    g = torch.Generator(device="cuda")
+    g.manual_seed(1000)                              # the decode masters, drawn in the same order
+    mats = []
+    for i in range(N_PAIRS):
+        for (n, K) in (UP, DOWN):
+            W = (torch.randn((n, K), generator=g, device="cuda", dtype=torch.float32) * 0.02)
+            codes, _, gamma = S.pack(W.contiguous(), 4, 4, S.BL_LAYOUT_DENSE2)
+            del W
+            mats.append((n, K, codes, gamma))
+    packed = sum(c.numel() for (_, _, c, _) in mats)
+    groups = {}
+    for T in DECODE_T:
+        projs = []
+        for i, (n, K, codes, gamma) in enumerate(mats):
+            xq, sc = D.q[(T, K)]
+            j = i // 2
+            projs.append(dict(xq=xq[j * T:(j + 1) * T], scale=sc[j * T:(j + 1) * T], K=K,
+                              codes=codes, meta=None, gamma=gamma, n=n,
+                              y=torch.empty((T, n), dtype=torch.float32, device="cuda")))
+        groups[T] = S.FwdGroup(projs, 4, 4, S.BL_LAYOUT_DENSE2)
+
+    def step():
+        for T in DECODE_T:
+            for K in (UP[1], DOWN[1]):
+                S.act_quant(D.x[(T, K)], out=D.q[(T, K)])
+            groups[T]()
+
+    step()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    with torch.cuda.graph(graph, stream=cap):
+        step()
+    for _ in range(warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        graph.replay()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    dense_weights = sum(n * K for (n, K, _, _) in mats)
+    return {"workload": "the decode stream (64 up/down pairs, T = 1, 4, 16) on dense ternary "
+                        "weights: 2-bit codes at every position, no N:M mask (4:4, dense 2-bit "
+                        "layout), same activations and grouped launches",
+            "ms_per_step": round(ms, 4), "packed_bytes_per_pass": packed,
+            "weight_GBps": round(packed * len(DECODE_T) / (ms * 1e-3) / 1e9, 1),
+            "dense_weights_per_s": float(f"{dense_weights * len(DECODE_T) / (ms * 1e-3):.4g}"),
+            "vs_sparse_2of4_step": round(ms / D.last_ms_per_step, 3) if D.last_ms_per_step else None}
+
+
 def kernel_source_sha():
     h = hashlib.sha256()
     for f in GROUP_SRC:
@@ -274,8 +330,10 @@ def prefill_leg(S, torch, iters=10):
 
 
 def _event_ms(torch, fn, iters):
-    """Mean duration of fn() over iters launches, HIP events on the launch stream."""
-    fn()
+    """Mean duration of fn() over iters launches (after three warm-up calls), HIP events on the
+    launch stream."""
+    for _ in range(3):
+        fn()
     torch.cuda.synchronize()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
     for a, b in ev:
@@ -563,6 +621,7 @@ def main():
     ms_per_step = wall * 1e3 / args.steps
     value = D.packed_bytes * len(DECODE_T) / (ms_per_step * 1e-3) / 1e9
     log(f"decode step {ms_per_step:.3f} ms -> {value:.1f} GB/s of packed weights")
+    D.last_ms_per_step = ms_per_step
 
     # grouped-GEMV launch durations: HIP events on the launch stream, eager steps
     per_T = {T: [] for T in DECODE_T}
@@ -601,6 +660,10 @@ def main():
     log("fused decode leg")
     out["decode_fused"] = decode_fused_leg(S, torch, D, ref, args.steps, args.warmup)
     log(f"fused decode {out['decode_fused']['value']} GB/s")
+    if not args.no_extra:
+        log("dense ternary decode comparator")
+        out["decode_dense_ternary"] = decode_dense_leg(S, torch, D, args.steps, args.warmup)
+        log(f"dense ternary decode {out['decode_dense_ternary']['ms_per_step']} ms/step")
     if not args.no_prefill:
         log("prefill leg")
         out["prefill"] = prefill_leg(S, torch)
