@@ -64,11 +64,14 @@ def parse():
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the 6:8, 14:16 and training-step legs")
     ap.add_argument("--cpu-budget-s", type=float, default=15.0)
-    ap.add_argument("--profile-pass", choices=("decode", "prefill", "train", "bwd"), default=None,
+    ap.add_argument("--profile-pass", choices=("decode", "prefill", "train", "bwd", "bwdgroup"),
+                    default=None,
                     help="for hardware-counter runs, no graph and no JSON line.  decode: two eager "
                          "decode steps, then a plain copy of COPY_BYTES (the counters' scale "
                          "reference); prefill: the prefill GEMM launched five times; train: the "
-                         "training-step leg with two timed steps")
+                         "training-step leg with two timed steps; bwd: the gate projection's "
+                         "backward three times; bwdgroup: the layer set's grouped backward three "
+                         "times, then the plain copies")
     return ap.parse_args()
 
 
@@ -430,13 +433,25 @@ def train_step_leg(S, torch, iters=3):
             xq, sc = Q[K]
             S.fwd(xq, sc, K, c, m, ga, n, out=(y, None))
 
-    def bwd_all():
+    def bwd_seq():
         seen = set()
         for (_, n, K), (c, m, ga), dy, dw in zip(TRAIN_LAYERS, packed, dYs, dWs):
             xq, sc = Q[K]
             S.bwd(dy, xq, sc, K, c, m, ga, n, out=(dXs[K], dw), accumulate=(K in seen, False),
                   ws=bws)
             seen.add(K)
+
+    # the same seven calls as one grouped backward (one operand launch, one product launch)
+    projs, seen = [], set()
+    for (_, n, K), (c, m, ga), dy, dw in zip(TRAIN_LAYERS, packed, dYs, dWs):
+        xq, sc = Q[K]
+        projs.append(dict(dy=dy, xq=xq, scale=sc, K=K, codes=c, meta=m, gamma=ga, n=n,
+                          dx=dXs[K], dw=dw, accumulate=(K in seen, False)))
+        seen.add(K)
+    bgroup = S.BwdGroup(projs, T)
+
+    def bwd_all():
+        bgroup()
 
     # each phase captured once as a HIP graph (no host launch overhead between the 7 matrices);
     # two replays are checked bitwise against the eager results first
@@ -449,12 +464,19 @@ def train_step_leg(S, torch, iters=3):
     pack_all()
     quant_all()
     fwd_all()
-    bwd_all()
+    bwd_seq()
     torch.cuda.synchronize()
     ref = outputs()
+    for t in dWs + list(dXs.values()):
+        t.zero_()
+    bwd_all()
+    torch.cuda.synchronize()
+    for a, b in zip(outputs(), ref):
+        if not torch.equal(a, b):
+            raise RuntimeError("grouped backward differs from the sequential calls")
     graphs = []
     cap = torch.cuda.Stream()
-    for fn in (pack_all, quant_all, fwd_all, bwd_all):
+    for fn in (pack_all, quant_all, fwd_all, bwd_seq, bwd_all):
         gr = torch.cuda.CUDAGraph()
         with torch.cuda.graph(gr, stream=cap):
             fn()
@@ -471,7 +493,8 @@ def train_step_leg(S, torch, iters=3):
     t_pack = _event_ms(torch, graphs[0].replay, iters)
     t_quant = _event_ms(torch, graphs[1].replay, iters)
     t_fwd = _event_ms(torch, graphs[2].replay, iters)
-    t_bwd = _event_ms(torch, graphs[3].replay, iters)
+    t_bwd_seq = _event_ms(torch, graphs[3].replay, iters)
+    t_bwd = _event_ms(torch, graphs[4].replay, iters)
     pack_bytes = sum(4 * n * K + p[0].numel() + p[1].numel() for (_, n, K), p in zip(TRAIN_LAYERS, packed))
     # act_quant: bf16 read + int8 write per element + 4 B scale per token
     quant_bytes = sum(T * K * 3 + 4 * T for K in X)
@@ -485,6 +508,8 @@ def train_step_leg(S, torch, iters=3):
                         "8192 tokens, 2:4, bf16 N(0,1) activations, bf16 output gradients",
             "step_ms": round(t_pack + t_quant + t_fwd + t_bwd, 4),
             "bwd_ms": round(t_bwd, 4), "bwd_TFLOPS": round(bwd_tflops, 1),
+            # the seven bitlinear_bwd calls one after another (same results, bit for bit)
+            "bwd_sequential_ms": round(t_bwd_seq, 4),
             "pack_ms": round(t_pack, 4), "pack_GBps": round(pack_gbs, 1),
             "act_quant_ms": round(t_quant, 4), "act_quant_GBps": round(quant_gbs, 1),
             "fwd_ms": round(t_fwd, 4), "fwd_TOPS": round(fwd_tops, 1),
@@ -518,6 +543,34 @@ def bwd_profile_pass(S, torch):
     ws = torch.empty(S.bwd_workspace_bytes(T, n, K), dtype=torch.uint8, device="cuda")
     for _ in range(3):
         S.bwd(dy, xq, sc, K, codes, meta, gamma, n, out=(dx, dw), ws=ws)
+
+
+def bwd_group_profile_pass(S, torch):
+    """Grouped backward of the training-step layer set (8192 tokens) three times, then two plain
+    device copies of COPY_BYTES (the counters' scale reference)."""
+    T = 8192
+    g = torch.Generator(device="cuda")
+    g.manual_seed(37)
+    X = {K: S.act_quant(torch.randn((T, K), generator=g, device="cuda").to(torch.bfloat16))
+         for K in (3200, 8640)}
+    dXs = {K: torch.empty((T, K), device="cuda") for K in X}
+    projs, seen = [], set()
+    for (_, n, K) in TRAIN_LAYERS:
+        W = (torch.randn((n, K), generator=g, device="cuda") * 0.02).contiguous()
+        c, m, ga = S.pack(W, 2, 4)
+        dy = (torch.randn((T, n), generator=g, device="cuda") * 2.0 ** -10).to(torch.bfloat16)
+        projs.append(dict(dy=dy, xq=X[K][0], scale=X[K][1], K=K, codes=c, meta=m, gamma=ga, n=n,
+                          dx=dXs[K], dw=torch.empty((n, K), device="cuda"),
+                          accumulate=(K in seen, False)))
+        seen.add(K)
+    grp = S.BwdGroup(projs, T)
+    for _ in range(3):
+        grp()
+    torch.cuda.synchronize()
+    src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
 
 
 # ---------------------------------------------------------------------------------------------
@@ -565,6 +618,11 @@ def main():
         bwd_profile_pass(S, torch)
         torch.cuda.synchronize()
         log("profile pass done: backward of the gate projection x 3")
+        return
+    if args.profile_pass == "bwdgroup":
+        bwd_group_profile_pass(S, torch)
+        torch.cuda.synchronize()
+        log("profile pass done: grouped backward of the layer set x 3, copies x 2")
         return
     if args.profile_pass == "train":
         train_step_leg(S, torch, iters=2)

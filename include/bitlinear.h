@@ -247,6 +247,71 @@ int bitlinear_bwd(const uint16_t* dy, int64_t T, int64_t n, const int8_t* xq,
                   const float* gamma, int N, int M, int layout, float* dx, float* dw, int flags,
                   void* ws, size_t ws_bytes, void* stream);
 
+/* ---------------------------------------------------------------------------------------------
+ * Grouped backward: the bitlinear_bwd calls of a whole layer set in two launches.
+ *
+ * The operation is exactly that of calling bitlinear_bwd for descs[0], descs[1], ... in order on
+ * one stream, bit for bit (same definitions as above).  One launch prepares every operand (the
+ * W_eff^T expansions, the dY copies and transposes, and one X^^T per distinct activation: the
+ * projections that share xq / x_scale transpose it once); the other runs every 256 x 256 output
+ * tile of every dX and dW product as one grid, longest tiles first, so the grid tails of the
+ * separate calls become one.  Projections that name the same dx (same pointer and K, e.g. Q/K/V
+ * reading one activation) sum into it in descriptor order, each term with its own flags: a
+ * descriptor with BL_BWD_ACCUM_DX adds to what the earlier ones left, one without overwrites it.
+ *
+ * All projections share T and (N, M, layout).  Per projection the rules of bitlinear_bwd apply;
+ * in addition outputs must not overlap each other (apart from a shared dx) or any input of the
+ * group (dy, xq, x_scale, codes, meta, gamma): BL_EINVAL.
+ *
+ * Use: bitlinear_bwd_group_plan validates the descriptors and sizes the device table and the
+ * workspace; bitlinear_bwd_group_build writes the table (16-byte aligned device memory, caller-
+ * owned) for one workspace (256-byte aligned device memory, caller-owned) -- it synchronizes
+ * `stream`, so build once, outside any graph capture; bitlinear_bwd_group enqueues the two
+ * launches (asynchronous, stream-ordered, capturable).  The table holds the descriptors' pointers
+ * and the workspace's: they must stay allocated while it is used, and their contents are read at
+ * launch time, so new gradients and activations in the same buffers need no rebuild.  Launches
+ * that share a workspace must be ordered on one stream.  The plan passed to bitlinear_bwd_group
+ * must be the one reported for the table's descriptors; a table of another N:M or layout is
+ * ignored (nothing is written).
+ */
+typedef struct bl_bwd_desc {
+  const uint16_t* dy;     /* [T][n] bf16 output gradient */
+  const int8_t* xq;       /* [T][K] int8 activations (act_quant_i8, lift_M = 0) */
+  const float* x_scale;   /* [T] token scales */
+  int64_t K;              /* master in-features */
+  const uint8_t* codes;   /* packed codes from bitlinear_pack */
+  const uint8_t* meta;    /* packed meta (SPARSE) or NULL (DENSE2) */
+  const float* gamma;     /* device scalar from bitlinear_pack */
+  int64_t n;              /* out-features */
+  float* dx;              /* [T][K] fp32 input gradient, or NULL */
+  float* dw;              /* [n][K] fp32 master-weight gradient, or NULL */
+  int32_t flags;          /* BL_BWD_ACCUM_DX | BL_BWD_ACCUM_DW, as for bitlinear_bwd */
+  int32_t reserved;
+} bl_bwd_desc;
+
+typedef struct bl_bwd_group_plan {
+  size_t table_bytes;     /* device table */
+  size_t ws_bytes;        /* device workspace */
+  int64_t prep_blocks;    /* workgroups of the operand launch */
+  int64_t jobs;           /* workgroups of the product launch */
+  int32_t N, M, layout;   /* the group's packing */
+  int32_t reserved;
+} bl_bwd_group_plan;
+
+/* Validates descs[0..count) (host memory, 1 <= count <= 65536) and fills *plan.  Enqueues
+ * nothing. */
+int bitlinear_bwd_group_plan(const bl_bwd_desc* descs, int64_t count, int64_t T, int N, int M,
+                             int layout, bl_bwd_group_plan* plan);
+
+/* Validates the group and writes its device table for workspace ws.  Copies on `stream` and waits
+ * for it.  BL_ENOSPC if ws_bytes or table_bytes is below the plan's. */
+int bitlinear_bwd_group_build(const bl_bwd_desc* descs, int64_t count, int64_t T, int N, int M,
+                              int layout, void* ws, size_t ws_bytes, void* table,
+                              size_t table_bytes, void* stream);
+
+/* Enqueues the grouped backward of a built table on `stream`. */
+int bitlinear_bwd_group(const void* table, const bl_bwd_group_plan* plan, void* stream);
+
 /* Static description of a status code. */
 const char* bitlinear_strerror(int status);
 

@@ -3,8 +3,10 @@
 Names mirror the C ABI: ``bitlinear_packed_bytes``, ``bitlinear_pack``, ``act_quant_i8``,
 ``bitlinear_fwd``, ``bitlinear_group_table_bytes``, ``bitlinear_group_build``,
 ``bitlinear_fwd_group``, ``bitlinear_group_fused_table_bytes``, ``bitlinear_group_fused_build``,
-``bitlinear_fwd_group_fused``, ``bitlinear_bwd_workspace_bytes``, ``bitlinear_bwd``.
-``pack`` / ``act_quant`` / ``fwd`` / ``FwdGroup`` / ``FusedGroup`` / ``bwd`` are convenience
+``bitlinear_fwd_group_fused``, ``bitlinear_bwd_workspace_bytes``, ``bitlinear_bwd``,
+``bitlinear_bwd_group_plan``, ``bitlinear_bwd_group_build``, ``bitlinear_bwd_group``.
+``pack`` / ``act_quant`` / ``fwd`` / ``FwdGroup`` / ``FusedGroup`` / ``bwd`` / ``BwdGroup`` are
+convenience
 wrappers that allocate the output tensors with torch on the input's device and enqueue on torch's
 current stream.
 """
@@ -37,6 +39,22 @@ class BlFwdXDesc(ctypes.Structure):
     _fields_ = [("x", ctypes.c_void_p), ("T", ctypes.c_int64), ("K", ctypes.c_int64),
                 ("codes", ctypes.c_void_p), ("meta", ctypes.c_void_p), ("gamma", ctypes.c_void_p),
                 ("n", ctypes.c_int64), ("y", ctypes.c_void_p), ("acc_opt", ctypes.c_void_p)]
+
+
+class BlBwdDesc(ctypes.Structure):
+    """bl_bwd_desc: the arguments of one bitlinear_bwd call inside a grouped backward."""
+    _fields_ = [("dy", ctypes.c_void_p), ("xq", ctypes.c_void_p), ("x_scale", ctypes.c_void_p),
+                ("K", ctypes.c_int64), ("codes", ctypes.c_void_p), ("meta", ctypes.c_void_p),
+                ("gamma", ctypes.c_void_p), ("n", ctypes.c_int64), ("dx", ctypes.c_void_p),
+                ("dw", ctypes.c_void_p), ("flags", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
+class BlBwdGroupPlan(ctypes.Structure):
+    """bl_bwd_group_plan: table and workspace sizes and the two launch grids of a group."""
+    _fields_ = [("table_bytes", ctypes.c_size_t), ("ws_bytes", ctypes.c_size_t),
+                ("prep_blocks", ctypes.c_int64), ("jobs", ctypes.c_int64),
+                ("N", ctypes.c_int32), ("M", ctypes.c_int32), ("layout", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
 
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -78,6 +96,11 @@ def lib() -> ctypes.CDLL:
         L.bitlinear_bwd_workspace_bytes.argtypes = [i64, i64, i64, ctypes.POINTER(sz)]
         L.bitlinear_bwd.argtypes = [vp, i64, i64, vp, vp, i64, vp, vp, vp, i32, i32, i32, vp, vp,
                                     i32, vp, sz, vp]
+        bp = ctypes.POINTER(BlBwdDesc)
+        pp = ctypes.POINTER(BlBwdGroupPlan)
+        L.bitlinear_bwd_group_plan.argtypes = [bp, i64, i64, i32, i32, i32, pp]
+        L.bitlinear_bwd_group_build.argtypes = [bp, i64, i64, i32, i32, i32, vp, sz, vp, sz, vp]
+        L.bitlinear_bwd_group.argtypes = [vp, pp, vp]
         L.bitlinear_strerror.argtypes = [i32]
         L.bitlinear_strerror.restype = ctypes.c_char_p
         L.bitlinear_layout_version.argtypes = []
@@ -86,7 +109,8 @@ def lib() -> ctypes.CDLL:
                   L.bitlinear_group_build, L.bitlinear_fwd_group,
                   L.bitlinear_bwd_workspace_bytes, L.bitlinear_bwd,
                   L.bitlinear_group_fused_table_bytes, L.bitlinear_group_fused_build,
-                  L.bitlinear_fwd_group_fused):
+                  L.bitlinear_fwd_group_fused, L.bitlinear_bwd_group_plan,
+                  L.bitlinear_bwd_group_build, L.bitlinear_bwd_group):
             f.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -166,6 +190,24 @@ def bitlinear_bwd(dy, T, n, xq, x_scale, K, codes, meta, gamma, N, M, layout, dx
                   ws_bytes, stream) -> int:
     return lib().bitlinear_bwd(dy, T, n, xq, x_scale, K, codes, meta, gamma, N, M, layout, dx, dw,
                                flags, ws, ws_bytes, stream)
+
+
+def bitlinear_bwd_group_plan(descs, T, N, M, layout):
+    """Returns (status, BlBwdGroupPlan)."""
+    plan = BlBwdGroupPlan()
+    st = lib().bitlinear_bwd_group_plan(descs, len(descs), T, N, M, layout, ctypes.byref(plan))
+    return st, plan
+
+
+def bitlinear_bwd_group_build(descs, T, N, M, layout, ws, ws_bytes, table, table_bytes,
+                              stream) -> int:
+    return lib().bitlinear_bwd_group_build(descs, len(descs), T, N, M, layout, ws, ws_bytes, table,
+                                           table_bytes, stream)
+
+
+def bitlinear_bwd_group(table, plan, stream) -> int:
+    return lib().bitlinear_bwd_group(table, ctypes.byref(plan) if plan is not None else None,
+                                     stream)
 
 
 # ---------------------------------------------------------------------------------------------
@@ -339,3 +381,43 @@ def bwd(dy, xq, scale, K: int, codes, meta, gamma, n: int, N: int = 2, M: int = 
                          _ptr(gamma), N, M, layout, _ptr(dx), _ptr(dw), flags, _ptr(ws), ws.numel(),
                          _stream()), "bitlinear_bwd")
     return dx, dw
+
+
+class BwdGroup:
+    """A built grouped backward: ``BwdGroup(projs, T)`` then ``group()`` computes every gradient.
+
+    ``projs`` is a list of dicts with keys dy (bf16 [T][n]), xq, scale, K, codes, meta, gamma, n,
+    dx, dw (fp32 tensors or None) and optionally accumulate = (dx?, dw?), all sharing T and
+    (N, M, layout).  The result is that of ``bwd`` called for each projection in list order;
+    projections that name the same dx tensor sum into it (with accumulate[0] set on the later
+    ones).  Tensors are referenced, not copied; their contents are read at each launch.  ``ws``
+    may supply the uint8 workspace.
+    """
+
+    def __init__(self, projs, T: int, N: int = 2, M: int = 4, layout: int = BL_LAYOUT_SPARSE,
+                 ws=None):
+        import torch
+        self._keep = list(projs)
+        arr = (BlBwdDesc * len(projs))()
+        for i, p in enumerate(projs):
+            acc = p.get("accumulate", (False, False))
+            flags = (BL_BWD_ACCUM_DX if acc[0] else 0) | (BL_BWD_ACCUM_DW if acc[1] else 0)
+            arr[i] = BlBwdDesc(_ptr(p["dy"]), _ptr(p["xq"]), _ptr(p["scale"]), p["K"],
+                               _ptr(p["codes"]), _ptr(p.get("meta")), _ptr(p["gamma"]), p["n"],
+                               _ptr(p.get("dx")), _ptr(p.get("dw")), flags, 0)
+        self.descs = arr
+        st, plan = bitlinear_bwd_group_plan(arr, T, N, M, layout)
+        _check(st, "bitlinear_bwd_group_plan")
+        self.plan = plan
+        dev = projs[0]["codes"].device
+        self.table = torch.empty(max(plan.table_bytes, 16), dtype=torch.uint8, device=dev)
+        if ws is None:
+            ws = torch.empty(max(plan.ws_bytes, 256), dtype=torch.uint8, device=dev)
+        self.ws = ws
+        _check(bitlinear_bwd_group_build(arr, T, N, M, layout, ws.data_ptr(), ws.numel(),
+                                         self.table.data_ptr(), self.table.numel(), _stream()),
+               "bitlinear_bwd_group_build")
+
+    def __call__(self):
+        _check(bitlinear_bwd_group(self.table.data_ptr(), self.plan, _stream()),
+               "bitlinear_bwd_group")

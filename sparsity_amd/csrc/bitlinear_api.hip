@@ -8,6 +8,7 @@
 #include <vector>
 
 #include "bitlinear.h"
+#include "bwd_group.hpp"
 #include "launch.hpp"
 
 namespace {
@@ -161,6 +162,271 @@ int group_build(const bl_fwd_desc* descs, int64_t count, int N, int M, int layou
   return status_of(e);
 }
 
+
+// Checks of one bitlinear_bwd call apart from its workspace.
+int check_bwd(const uint16_t* dy, int64_t T, int64_t n, const int8_t* xq, const float* x_scale,
+              int64_t K, const uint8_t* codes, const uint8_t* meta, const float* gamma, int N,
+              int M, int layout, const float* dx, const float* dw, int flags) {
+  int64_t ke = 0;
+  const int st = check_shape(n, K, N, M, layout, &ke);
+  if (st != BL_OK) return st;
+  if (T < 0 || T > INT32_MAX) return BL_EINVAL;
+  if ((flags & ~(BL_BWD_ACCUM_DX | BL_BWD_ACCUM_DW)) != 0) return BL_EINVAL;
+  if (!dx && !dw) return BL_EINVAL;
+  const bl::BwdWorkspace w = bl::bwd_workspace(T, n, K);
+  const uint64_t lim = 1ull << 30;   // bf16 elements: operands stay below 2^31 bytes
+  if ((uint64_t)T * w.n32 >= lim || (uint64_t)K * w.n32 >= lim || (uint64_t)n * w.t32 >= lim ||
+      (uint64_t)K * w.t32 >= lim)
+    return BL_EINVAL;
+  if (dx && T > 0) {
+    if (!aligned16(codes) || !aligned4(gamma) || !aligned16(dx)) return BL_EINVAL;
+    if (layout == BL_LAYOUT_SPARSE ? !aligned16(meta) : meta != nullptr) return BL_EINVAL;
+  }
+  if (dw && !aligned16(dw)) return BL_EINVAL;
+  if (T > 0) {
+    if (!aligned16(dy)) return BL_EINVAL;
+    if (dw && (!aligned16(xq) || !aligned4(x_scale))) return BL_EINVAL;
+  }
+  return BL_OK;
+}
+
+// Host plan of a grouped backward: the workspace layout, the prep items, the product jobs and
+// their segments.  With ws == NULL the pointers into the workspace are offsets (sizing only).
+struct BwdGroupPlan {
+  size_t ws_bytes = 0;
+  int64_t prep_blocks = 0;
+  std::vector<bl::BwdPrep> prep;
+  std::vector<bl::BwdJob> jobs;
+  std::vector<bl::BwdSeg> segs;
+  size_t prep_off = 0, jobs_off = 0, segs_off = 0, table_bytes = 0;
+  int64_t t32 = 0;
+};
+
+// Per-tile cost of a segment beyond its reduction stages (prologue and epilogue), in stages.
+constexpr int64_t kSegCost = 8;
+
+struct Range {
+  uintptr_t lo, hi;
+};
+
+// Output buffers may not overlap each other or any input, except that projections may name the
+// same dx (same pointer, same K): those are summed in descriptor order.
+int check_bwd_overlaps(const bl_bwd_desc* d, int64_t count, int64_t T, int N, int M, int layout) {
+  std::vector<Range> in;
+  struct Out { uintptr_t lo, hi; bool dx; };
+  std::vector<Out> out;
+  for (int64_t i = 0; i < count; ++i) {
+    const bl_bwd_desc& q = d[i];
+    size_t cb = 0, mb = 0;
+    bitlinear_packed_bytes(q.n, q.K, N, M, layout, &cb, &mb, nullptr, nullptr);
+    auto add_in = [&](const void* p, uint64_t bytes) {
+      if (p && bytes) in.push_back({(uintptr_t)p, (uintptr_t)p + bytes});
+    };
+    if (T > 0) {
+      add_in(q.dy, (uint64_t)T * q.n * 2);
+      if (q.dw) {
+        add_in(q.xq, (uint64_t)T * q.K);
+        add_in(q.x_scale, (uint64_t)T * 4);
+      }
+      if (q.dx) {
+        add_in(q.codes, cb);
+        add_in(q.meta, mb);
+        add_in(q.gamma, 4);
+      }
+    }
+    if (q.dx && T > 0)
+      out.push_back({(uintptr_t)q.dx, (uintptr_t)q.dx + (uint64_t)T * q.K * 4, true});
+    if (q.dw) out.push_back({(uintptr_t)q.dw, (uintptr_t)q.dw + (uint64_t)q.n * q.K * 4, false});
+  }
+  std::sort(out.begin(), out.end(), [](const Out& a, const Out& b) {
+    return a.lo != b.lo ? a.lo < b.lo : a.hi < b.hi;
+  });
+  // sorted by (start, end), identical ranges are neighbours: a range may start below the running
+  // maximum end only as a copy of the dx range just before it
+  uintptr_t maxhi = 0;
+  for (size_t i = 0; i < out.size(); ++i) {
+    const bool same = i > 0 && out[i].dx && out[i - 1].dx && out[i].lo == out[i - 1].lo &&
+                      out[i].hi == out[i - 1].hi;
+    if (!same && out[i].lo < maxhi) return BL_EINVAL;
+    maxhi = std::max(maxhi, out[i].hi);
+  }
+  std::sort(in.begin(), in.end(), [](const Range& a, const Range& b) { return a.lo < b.lo; });
+  std::vector<uintptr_t> pmax(in.size());
+  for (size_t i = 0; i < in.size(); ++i) pmax[i] = std::max(in[i].hi, i ? pmax[i - 1] : 0);
+  for (const Out& o : out) {
+    // inputs starting before o.hi; the largest end among them must stay at or below o.lo
+    const size_t k = (size_t)(std::lower_bound(in.begin(), in.end(), o.hi,
+                                               [](const Range& r, uintptr_t v) { return r.lo < v; }) -
+                              in.begin());
+    if (k > 0 && pmax[k - 1] > o.lo) return BL_EINVAL;
+  }
+  return BL_OK;
+}
+
+int plan_bwd_group(const bl_bwd_desc* d, int64_t count, int64_t T, int N, int M, int layout,
+                   uint8_t* ws, BwdGroupPlan* P) {
+  if (!d || count < 1 || count > (1 << 16)) return BL_EINVAL;
+  if (T < 0 || T > INT32_MAX) return BL_EINVAL;
+  for (int64_t i = 0; i < count; ++i) {
+    const bl_bwd_desc& q = d[i];
+    const int st = check_bwd(q.dy, T, q.n, q.xq, q.x_scale, q.K, q.codes, q.meta, q.gamma, N, M,
+                             layout, q.dx, q.dw, q.flags);
+    if (st != BL_OK) return st;
+  }
+  {
+    const int st = check_bwd_overlaps(d, count, T, N, M, layout);
+    if (st != BL_OK) return st;
+  }
+  auto up = [](size_t v, size_t a) { return (v + a - 1) / a * a; };
+  const int64_t t32 = (T + 31) / 32 * 32;
+  P->t32 = t32;
+  const int tt = (int)((T + 63) / 64);
+  size_t off = 0;
+  auto carve = [&](size_t bytes) {
+    uint8_t* p = ws + off;   // an offset when ws is NULL
+    off = up(off + bytes, 256);
+    return p;
+  };
+  // workspace and prep items, in descriptor order
+  std::vector<const uint16_t*> dx_a(count), wt(count), dyt(count), xt(count);
+  struct XKey { const int8_t* xq; const float* xs; int64_t K; const uint16_t* xt; };
+  std::vector<XKey> xs_seen;
+  int64_t blocks = 0;
+  auto add_prep = [&](int32_t kind, int64_t nblocks, int a0, int a1, int a2, const void* s0,
+                      const void* s1, void* dst) {
+    if (nblocks <= 0) return;
+    bl::BwdPrep it;
+    memset(&it, 0, sizeof it);
+    it.kind = kind;
+    it.block0 = (int32_t)blocks;
+    it.a0 = a0; it.a1 = a1; it.a2 = a2;
+    it.src0 = s0; it.src1 = s1; it.dst = dst;
+    P->prep.push_back(it);
+    blocks += nblocks;
+  };
+  for (int64_t i = 0; i < count && T > 0; ++i) {
+    const bl_bwd_desc& q = d[i];
+    const int64_t n32 = (q.n + 31) / 32 * 32;
+    if (q.dx) {
+      uint16_t* w = (uint16_t*)carve((size_t)q.K * n32 * 2);
+      wt[i] = w;
+      const int64_t ke = keff_of(q.K, M, layout);
+      const int U = (int)(layout == BL_LAYOUT_SPARSE ? ke / 32 : q.K / 16);
+      const int64_t groups = q.K / M, pairs = n32 / 2;
+      add_prep(bl::kPrepWt, (groups * pairs + 255) / 256, U, (int)groups, (int)pairs, q.codes,
+               q.meta, w);
+      if (n32 != q.n) {
+        uint16_t* p = (uint16_t*)carve((size_t)T * n32 * 2);
+        add_prep(bl::kPrepPad, (T * n32 + 255) / 256, (int)q.n, (int)n32, 0, q.dy, nullptr, p);
+        dx_a[i] = p;
+      } else {
+        dx_a[i] = q.dy;
+      }
+    }
+    if (q.dw) {
+      uint16_t* p = (uint16_t*)carve((size_t)q.n * t32 * 2);
+      const int tn = (int)((q.n + 63) / 64);
+      add_prep(bl::kPrepTrDy, (int64_t)tt * tn, (int)q.n, tn, 0, q.dy, nullptr, p);
+      dyt[i] = p;
+      const XKey* hit = nullptr;
+      for (const XKey& k : xs_seen)
+        if (k.xq == q.xq && k.xs == q.x_scale && k.K == q.K) hit = &k;
+      if (hit) {
+        xt[i] = hit->xt;
+      } else {
+        uint16_t* x = (uint16_t*)carve((size_t)q.K * t32 * 2);
+        const int tk = (int)((q.K + 63) / 64);
+        add_prep(bl::kPrepTrX, (int64_t)tt * tk, (int)q.K, tk, 0, q.xq, q.x_scale, x);
+        xs_seen.push_back({q.xq, q.x_scale, q.K, x});
+        xt[i] = x;
+      }
+    }
+    if (blocks > INT32_MAX) return BL_EINVAL;
+  }
+  P->ws_bytes = off;
+  P->prep_blocks = blocks;
+
+  // products: one per distinct dx (segments = its projections in order), one per dw
+  struct Gemm { float* c; int64_t rows_a, rows_b, ldc; int32_t seg0, nseg; int64_t work; };
+  std::vector<Gemm> gemms;
+  std::vector<float*> dx_seen;
+  for (int64_t i = 0; i < count && T > 0; ++i) {
+    if (!d[i].dx || std::find(dx_seen.begin(), dx_seen.end(), d[i].dx) != dx_seen.end()) continue;
+    dx_seen.push_back(d[i].dx);
+    Gemm g{d[i].dx, T, d[i].K, d[i].K, (int32_t)P->segs.size(), 0, 0};
+    for (int64_t j = i; j < count; ++j) {
+      if (d[j].dx != d[i].dx) continue;
+      const int64_t n32 = (d[j].n + 31) / 32 * 32;
+      bl::BwdSeg sg;
+      memset(&sg, 0, sizeof sg);
+      sg.a = dx_a[j]; sg.b = wt[j]; sg.alpha = d[j].gamma;
+      sg.lda = (int32_t)n32; sg.ldb = (int32_t)n32; sg.R = (int32_t)n32;
+      sg.accumulate = (d[j].flags & BL_BWD_ACCUM_DX) != 0;
+      P->segs.push_back(sg);
+      ++g.nseg;
+      g.work += n32 / 32 + kSegCost;
+    }
+    gemms.push_back(g);
+  }
+  for (int64_t i = 0; i < count; ++i) {
+    if (!d[i].dw) continue;
+    Gemm g{d[i].dw, d[i].n, d[i].K, d[i].K, (int32_t)P->segs.size(), 1, t32 / 32 + kSegCost};
+    bl::BwdSeg sg;
+    memset(&sg, 0, sizeof sg);
+    sg.a = dyt[i]; sg.b = xt[i]; sg.alpha = nullptr;
+    sg.lda = (int32_t)t32; sg.ldb = (int32_t)t32; sg.R = (int32_t)t32;
+    sg.accumulate = (d[i].flags & BL_BWD_ACCUM_DW) != 0;
+    P->segs.push_back(sg);
+    gemms.push_back(g);
+  }
+  // 8 x 4 tile patches (an XCD's 32 CUs hold one patch at a time, so its operand tiles stay in
+  // that XCD's L2), dealt longest first to the least-loaded XCD; each XCD's list runs longest
+  // first and block b of the launch takes entry b / 8 of XCD b % 8's list.
+  struct Patch { int32_t g, pi, pj; int64_t work, tiles; };
+  std::vector<Patch> patches;
+  for (size_t g = 0; g < gemms.size(); ++g) {
+    const int64_t ti = (gemms[g].rows_a + 255) / 256, tj = (gemms[g].rows_b + 255) / 256;
+    for (int64_t pi = 0; pi < ti; pi += 8)
+      for (int64_t pj = 0; pj < tj; pj += 4)
+        patches.push_back({(int32_t)g, (int32_t)pi, (int32_t)pj, gemms[g].work,
+                           std::min<int64_t>(8, ti - pi) * std::min<int64_t>(4, tj - pj)});
+  }
+  std::stable_sort(patches.begin(), patches.end(),
+                   [](const Patch& a, const Patch& b) { return a.work > b.work; });
+  std::vector<std::vector<bl::BwdJob>> per(bl::kXcds);
+  int64_t load[bl::kXcds] = {};
+  for (const Patch& pt : patches) {
+    const int x = (int)(std::min_element(load, load + bl::kXcds) - load);
+    load[x] += pt.work * pt.tiles;
+    const Gemm& g = gemms[pt.g];
+    const int64_t ti = (g.rows_a + 255) / 256, tj = (g.rows_b + 255) / 256;
+    for (int64_t j = pt.pj; j < std::min<int64_t>(pt.pj + 4, tj); ++j)
+      for (int64_t i = pt.pi; i < std::min<int64_t>(pt.pi + 8, ti); ++i) {
+        bl::BwdJob jb;
+        memset(&jb, 0, sizeof jb);
+        jb.c = g.c;
+        jb.seg0 = g.seg0; jb.nseg = g.nseg;
+        jb.i0 = (int32_t)(i * 256); jb.j0 = (int32_t)(j * 256);
+        jb.rows_a = (int32_t)g.rows_a; jb.rows_b = (int32_t)g.rows_b; jb.ldc = (int32_t)g.ldc;
+        per[x].push_back(jb);
+      }
+  }
+  size_t depth = 0;
+  for (const auto& v : per) depth = std::max(depth, v.size());
+  if (depth * bl::kXcds > (size_t)INT32_MAX || P->segs.size() > (size_t)INT32_MAX)
+    return BL_EINVAL;
+  bl::BwdJob pad;
+  memset(&pad, 0, sizeof pad);
+  P->jobs.assign(depth * bl::kXcds, pad);
+  for (int x = 0; x < bl::kXcds; ++x)
+    for (size_t k = 0; k < per[x].size(); ++k) P->jobs[k * bl::kXcds + x] = per[x][k];
+
+  P->prep_off = sizeof(bl::BwdHeader);
+  P->jobs_off = up(P->prep_off + P->prep.size() * sizeof(bl::BwdPrep), 16);
+  P->segs_off = up(P->jobs_off + P->jobs.size() * sizeof(bl::BwdJob), 16);
+  P->table_bytes = up(P->segs_off + P->segs.size() * sizeof(bl::BwdSeg), 16);
+  return BL_OK;
+}
 
 // A fused group's descriptors as plain ones (xq = the bf16 rows; x_scale is not read, the row
 // pointer stands in for the NULL check), after the checks that are the fused path's own: no
@@ -318,32 +584,81 @@ int bitlinear_bwd(const uint16_t* dy, int64_t T, int64_t n, const int8_t* xq,
                   const float* x_scale, int64_t K, const uint8_t* codes, const uint8_t* meta,
                   const float* gamma, int N, int M, int layout, float* dx, float* dw, int flags,
                   void* ws, size_t ws_bytes, void* stream) {
-  int64_t ke = 0;
-  const int st = check_shape(n, K, N, M, layout, &ke);
+  const int st = check_bwd(dy, T, n, xq, x_scale, K, codes, meta, gamma, N, M, layout, dx, dw,
+                           flags);
   if (st != BL_OK) return st;
-  if (T < 0 || T > INT32_MAX) return BL_EINVAL;
-  if ((flags & ~(BL_BWD_ACCUM_DX | BL_BWD_ACCUM_DW)) != 0) return BL_EINVAL;
-  if (!dx && !dw) return BL_EINVAL;
-  const bl::BwdWorkspace w = bl::bwd_workspace(T, n, K);
-  const uint64_t lim = 1ull << 30;   // bf16 elements: operands stay below 2^31 bytes
-  if ((uint64_t)T * w.n32 >= lim || (uint64_t)K * w.n32 >= lim || (uint64_t)n * w.t32 >= lim ||
-      (uint64_t)K * w.t32 >= lim)
-    return BL_EINVAL;
-  if (dx && T > 0) {
-    if (!aligned16(codes) || !aligned4(gamma) || !aligned16(dx)) return BL_EINVAL;
-    if (layout == BL_LAYOUT_SPARSE ? !aligned16(meta) : meta != nullptr) return BL_EINVAL;
-  }
-  if (dw && !aligned16(dw)) return BL_EINVAL;
-  if (T > 0) {
-    if (!aligned16(dy)) return BL_EINVAL;
-    if (dw && (!aligned16(xq) || !aligned4(x_scale))) return BL_EINVAL;
-  }
   if (!ws || ((uintptr_t)ws & 255u)) return BL_EINVAL;
-  if (ws_bytes < w.total) return BL_ENOSPC;
+  if (ws_bytes < bl::bwd_workspace(T, n, K).total) return BL_ENOSPC;
   if (T == 0 && !dw) return BL_OK;   // no rows of dx: nothing to enqueue
   return status_of(bl::launch_bwd(dy, T, n, xq, x_scale, K, (const uint32_t*)codes,
                                   (const uint32_t*)meta, gamma, N, M, layout, dx, dw, flags, ws,
                                   (hipStream_t)stream));
+}
+
+int bitlinear_bwd_group_plan(const bl_bwd_desc* descs, int64_t count, int64_t T, int N, int M,
+                             int layout, bl_bwd_group_plan* plan) {
+  if (!plan) return BL_EINVAL;
+  BwdGroupPlan P;
+  const int st = plan_bwd_group(descs, count, T, N, M, layout, nullptr, &P);
+  if (st != BL_OK) return st;
+  memset(plan, 0, sizeof *plan);
+  plan->table_bytes = P.table_bytes;
+  plan->ws_bytes = P.ws_bytes;
+  plan->prep_blocks = P.prep_blocks;
+  plan->jobs = (int64_t)P.jobs.size();
+  plan->N = N;
+  plan->M = M;
+  plan->layout = layout;
+  return BL_OK;
+}
+
+int bitlinear_bwd_group_build(const bl_bwd_desc* descs, int64_t count, int64_t T, int N, int M,
+                              int layout, void* ws, size_t ws_bytes, void* table,
+                              size_t table_bytes, void* stream) {
+  if (!ws || ((uintptr_t)ws & 255u) || !aligned16(table)) return BL_EINVAL;
+  BwdGroupPlan P;
+  const int st = plan_bwd_group(descs, count, T, N, M, layout, (uint8_t*)ws, &P);
+  if (st != BL_OK) return st;
+  if (ws_bytes < P.ws_bytes || table_bytes < P.table_bytes) return BL_ENOSPC;
+  std::vector<uint8_t> img(P.table_bytes, 0);
+  bl::BwdHeader hdr;
+  memset(&hdr, 0, sizeof hdr);
+  hdr.magic = bl::kBwdMagic;
+  hdr.layout = layout;
+  hdr.N = N;
+  hdr.M = M;
+  hdr.T = T;
+  hdr.prep_items = (int32_t)P.prep.size();
+  hdr.prep_blocks = (int32_t)P.prep_blocks;
+  hdr.jobs = (int32_t)P.jobs.size();
+  hdr.segs = (int32_t)P.segs.size();
+  hdr.prep_off = (int64_t)P.prep_off;
+  hdr.jobs_off = (int64_t)P.jobs_off;
+  hdr.segs_off = (int64_t)P.segs_off;
+  hdr.t32 = P.t32;
+  memcpy(img.data(), &hdr, sizeof hdr);
+  if (!P.prep.empty())
+    memcpy(img.data() + P.prep_off, P.prep.data(), P.prep.size() * sizeof(bl::BwdPrep));
+  if (!P.jobs.empty())
+    memcpy(img.data() + P.jobs_off, P.jobs.data(), P.jobs.size() * sizeof(bl::BwdJob));
+  if (!P.segs.empty())
+    memcpy(img.data() + P.segs_off, P.segs.data(), P.segs.size() * sizeof(bl::BwdSeg));
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = hipMemcpyAsync(table, img.data(), P.table_bytes, hipMemcpyHostToDevice, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);  // img is released on return
+  return status_of(e);
+}
+
+int bitlinear_bwd_group(const void* table, const bl_bwd_group_plan* plan, void* stream) {
+  if (!plan || !aligned16(table)) return BL_EINVAL;
+  int64_t ke = 0;
+  const int st = check_shape(1, 256, plan->N, plan->M, plan->layout, &ke);
+  if (st != BL_OK) return st;
+  if (plan->prep_blocks < 0 || plan->prep_blocks > INT32_MAX || plan->jobs < 0 ||
+      plan->jobs > INT32_MAX)
+    return BL_EINVAL;
+  return status_of(bl::launch_bwd_group(table, plan->prep_blocks, plan->jobs, plan->layout,
+                                        plan->M, (hipStream_t)stream));
 }
 
 }  // extern "C"

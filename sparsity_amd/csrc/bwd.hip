@@ -17,6 +17,7 @@
 //   Xt[k][t]  = X^[t][k]                                                       (dW's B)
 // and dX's A is dY itself (or a zero-padded copy when n is not a multiple of 32).  The reduction
 // axis of every operand is zero-padded to a multiple of 32, so the kernel has no reduction tail.
+#include "bwd_group.hpp"
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -48,11 +49,9 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
 //   DENSE2: slot s is position s.
 // ---------------------------------------------------------------------------------------------
 template <int LAYOUT, int M>
-__global__ __launch_bounds__(256) void wt_expand_kernel(const uint32_t* __restrict__ codes,
-                                                        const uint32_t* __restrict__ meta, int U,
-                                                        int groups, int pairs,
-                                                        uint32_t* __restrict__ wt) {
-  const int64_t id = (int64_t)blockIdx.x * 256 + threadIdx.x;
+__device__ __forceinline__ void wt_expand_one(const uint32_t* __restrict__ codes,
+                                              const uint32_t* __restrict__ meta, int U, int groups,
+                                              int pairs, uint32_t* __restrict__ wt, int64_t id) {
   if (id >= (int64_t)groups * pairs) return;
   const int p = (int)(id % pairs), g = (int)(id / pairs);
   const int r = 2 * p, panel = r / kPanel, rr = r % kPanel;
@@ -99,6 +98,15 @@ __global__ __launch_bounds__(256) void wt_expand_kernel(const uint32_t* __restri
   for (int j = 0; j < M; ++j) wt[(int64_t)(g * M + j) * row_dwords + p] = out[j];
 }
 
+template <int LAYOUT, int M>
+__global__ __launch_bounds__(256) void wt_expand_kernel(const uint32_t* __restrict__ codes,
+                                                        const uint32_t* __restrict__ meta, int U,
+                                                        int groups, int pairs,
+                                                        uint32_t* __restrict__ wt) {
+  wt_expand_one<LAYOUT, M>(codes, meta, U, groups, pairs, wt,
+                           (int64_t)blockIdx.x * 256 + threadIdx.x);
+}
+
 // ---------------------------------------------------------------------------------------------
 // Transposes to the reduction-contiguous layouts of dW, 64 x 64 element tiles through LDS.
 //   Q8:  src = xq int8 [T][C] with scale[T]; dst[c][t] = bf16(fp32(q * scale_t))
@@ -111,13 +119,11 @@ __global__ __launch_bounds__(256) void wt_expand_kernel(const uint32_t* __restri
 constexpr int kTrPitch = 66;
 
 template <bool Q8>
-__global__ __launch_bounds__(256) void transpose_kernel(const void* __restrict__ src,
-                                                        const float* __restrict__ scale, int T,
-                                                        int C, int ld_src, uint16_t* __restrict__ dst,
-                                                        int ld_dst, int tiles_c) {
-  __shared__ uint16_t tile[64 * kTrPitch];
+__device__ __forceinline__ void transpose_tile(const void* __restrict__ src,
+                                               const float* __restrict__ scale, int T, int C,
+                                               int ld_src, uint16_t* __restrict__ dst, int ld_dst,
+                                               int tc, int tt, uint16_t* tile) {
   const int tid = threadIdx.x;
-  const int tc = blockIdx.x % tiles_c, tt = blockIdx.x / tiles_c;
   const int t0 = tt * 64, c0 = tc * 64;
   {
     const int t = tid >> 2, cc = (tid & 3) * 16;
@@ -172,14 +178,28 @@ __global__ __launch_bounds__(256) void transpose_kernel(const void* __restrict__
   }
 }
 
+template <bool Q8>
+__global__ __launch_bounds__(256) void transpose_kernel(const void* __restrict__ src,
+                                                        const float* __restrict__ scale, int T,
+                                                        int C, int ld_src, uint16_t* __restrict__ dst,
+                                                        int ld_dst, int tiles_c) {
+  __shared__ uint16_t tile[64 * kTrPitch];
+  transpose_tile<Q8>(src, scale, T, C, ld_src, dst, ld_dst, (int)(blockIdx.x % tiles_c),
+                     (int)(blockIdx.x / tiles_c), tile);
+}
+
 // dYp[t][o] = dY[t][o] for o < n, 0 for n <= o < ld (rows padded to a multiple of 32).
-__global__ __launch_bounds__(256) void pad_rows_kernel(const uint16_t* __restrict__ src, int64_t T,
-                                                       int n, int ld, uint16_t* __restrict__ dst) {
-  const int64_t id = (int64_t)blockIdx.x * 256 + threadIdx.x;
+__device__ __forceinline__ void pad_rows_one(const uint16_t* __restrict__ src, int64_t T, int n,
+                                             int ld, uint16_t* __restrict__ dst, int64_t id) {
   if (id >= T * ld) return;
   const int64_t t = id / ld;
   const int o = (int)(id % ld);
   dst[id] = o < n ? src[t * n + o] : (uint16_t)0;
+}
+
+__global__ __launch_bounds__(256) void pad_rows_kernel(const uint16_t* __restrict__ src, int64_t T,
+                                                       int n, int ld, uint16_t* __restrict__ dst) {
+  pad_rows_one(src, T, n, ld, dst, (int64_t)blockIdx.x * 256 + threadIdx.x);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -321,32 +341,33 @@ struct NtGemm {
   }
 };
 
-__global__ __launch_bounds__(256, 1) void gemm_nt_kernel(NtArgs p) {
-  __shared__ __attribute__((aligned(16))) uint8_t ring[kNtRing * kNtStage];
+// One 256 x 256 output tile at (i0, j0): the pipeline over the whole reduction, then the epilogue.
+// On entry the ring may still be in use by an earlier tile of the same block only if the caller
+// has drained and synchronized it (gemm_nt_group_kernel does before every segment after the
+// first).
+struct NtTile {
+  const uint16_t* a;
+  const uint16_t* b;
+  const float* alpha;   // device scalar, or NULL for 1
+  float* c;
+  int rows_a, rows_b, lda, ldb, ldc, R, accumulate, i0, j0;
+};
+
+typedef __attribute__((address_space(1))) float g_f32;
+typedef __attribute__((address_space(1))) v4f g_v4f;
+
+__device__ __forceinline__ void nt_tile(uint8_t* ring, const NtTile& p, int tid) {
   NtGemm k;
   k.ring = ring;
   k.a = (const uint8_t*)p.a;
   k.b = (const uint8_t*)p.b;
-  k.lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  k.lane = tid & 63;
+  const int wave = tid >> 6;
   k.wi = wave & 1;
   k.wj = wave >> 1;
   k.h = k.lane >> 5;
   k.NS = p.R / 32;
-  // XCD-major tile order: block b runs on XCD b % 8 and each XCD takes a contiguous run of tile
-  // numbers t.  Tile numbers run through groups of kNtGroupI row tiles (i) by all column tiles
-  // (j), i fastest inside a group, so the 32 tiles an XCD's 32 CUs hold at once form an 8 x 4
-  // patch: 12 operand tiles per 32 output tiles stay in that XCD's L2, where a run along i alone
-  // (32 x 1) streams 33.
-  const int full = (p.tiles / 8) * 8;
-  const int b = blockIdx.x;
-  const int t = b < full ? (b % 8) * (p.tiles / 8) + b / 8 : b;
-  const int tiles_j = p.tiles / p.tiles_i;
-  const int per_group = kNtGroupI * tiles_j;
-  const int first_i = (t / per_group) * kNtGroupI;
-  const int gsize = min(p.tiles_i - first_i, kNtGroupI);
-  const int ti = first_i + (t % per_group) % gsize, tj = (t % per_group) / gsize;
-  const int i0 = ti * kNtBI, j0 = tj * kNtBJ;
+  const int i0 = p.i0, j0 = p.j0;
 
   // Load q of a wave covers rows (wave * 4 + q) * 16 .. +15 of the A (or B) part of a stage: lane
   // l fills position l % 4 of row l / 4 with the global chunk (l % 4) ^ ((row / 4) % 4).
@@ -383,14 +404,14 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_kernel(NtArgs p) {
     __builtin_amdgcn_s_waitcnt(waitcnt_imm(0));   // no load may still be writing LDS at exit
   }
 
-  const float alpha = p.alpha ? *p.alpha : 1.0f;
+  const float alpha = p.alpha ? *(const g_f32*)p.alpha : 1.0f;
   const int lane = k.lane, h = k.h;
   const bool vec_ok = (p.rows_b & 3) == 0 && (p.ldc & 3) == 0;
 #pragma unroll
   for (int fi = 0; fi < kNtWI; ++fi) {
     const int i = i0 + k.wi * 128 + fi * 32 + (lane & 31);
     if (i >= p.rows_a) continue;
-    float* crow = p.c + (size_t)i * p.ldc;
+    g_f32* crow = (g_f32*)p.c + (size_t)i * p.ldc;
 #pragma unroll
     for (int fj = 0; fj < kNtWJ; ++fj) {
       const int jb = j0 + k.wj * 128 + fj * 32;
@@ -403,8 +424,8 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_kernel(NtArgs p) {
           v[1] = k.acc[fi][fj][4 * jj + 1] * alpha;
           v[2] = k.acc[fi][fj][4 * jj + 2] * alpha;
           v[3] = k.acc[fi][fj][4 * jj + 3] * alpha;
-          if (p.accumulate) v += *(const v4f*)(crow + j);
-          *(v4f*)(crow + j) = v;
+          if (p.accumulate) v += *(const g_v4f*)(crow + j);
+          *(g_v4f*)(crow + j) = v;
         }
       } else {
 #pragma unroll
@@ -418,6 +439,106 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_kernel(NtArgs p) {
         }
       }
     }
+  }
+}
+
+__global__ __launch_bounds__(256, 1) void gemm_nt_kernel(NtArgs p) {
+  __shared__ __attribute__((aligned(16))) uint8_t ring[kNtRing * kNtStage];
+  // XCD-major tile order: block b runs on XCD b % 8 and each XCD takes a contiguous run of tile
+  // numbers t.  Tile numbers run through groups of kNtGroupI row tiles (i) by all column tiles
+  // (j), i fastest inside a group, so the 32 tiles an XCD's 32 CUs hold at once form an 8 x 4
+  // patch: 12 operand tiles per 32 output tiles stay in that XCD's L2, where a run along i alone
+  // (32 x 1) streams 33.
+  const int full = (p.tiles / 8) * 8;
+  const int b = blockIdx.x;
+  const int t = b < full ? (b % 8) * (p.tiles / 8) + b / 8 : b;
+  const int tiles_j = p.tiles / p.tiles_i;
+  const int per_group = kNtGroupI * tiles_j;
+  const int first_i = (t / per_group) * kNtGroupI;
+  const int gsize = min(p.tiles_i - first_i, kNtGroupI);
+  const int ti = first_i + (t % per_group) % gsize, tj = (t % per_group) / gsize;
+  NtTile tile;
+  tile.a = p.a; tile.b = p.b; tile.alpha = p.alpha; tile.c = p.c;
+  tile.rows_a = p.rows_a; tile.rows_b = p.rows_b; tile.lda = p.lda; tile.ldb = p.ldb;
+  tile.ldc = p.ldc; tile.R = p.R; tile.accumulate = p.accumulate;
+  tile.i0 = ti * kNtBI; tile.j0 = tj * kNtBJ;
+  nt_tile(ring, tile, threadIdx.x);
+}
+
+// ---------------------------------------------------------------------------------------------
+// Grouped backward: every projection of a layer set in two launches.  bwd_prep_kernel runs all
+// operand preparations (W_eff^T expansions, dY pads and transposes, one X^^T per distinct
+// activation); gemm_nt_group_kernel runs every output tile of every dX and dW product, one job
+// per block.  A dX buffer named by several projections is one set of tiles whose segments (one
+// per projection, in descriptor order) each finish with the store or accumulate of that
+// projection's call, so the result is bit for bit that of the calls one after another.  The host
+// orders the jobs longest first and deals 8 x 4 tile patches to the XCDs by load, so the tails of
+// the separate launches become one tail.
+// ---------------------------------------------------------------------------------------------
+template <int LAYOUT, int M>
+__global__ __launch_bounds__(256) void bwd_prep_kernel(const uint8_t* __restrict__ table) {
+  __shared__ uint16_t tile[64 * kTrPitch];
+  const BwdHeader* hd = (const BwdHeader*)table;
+  if (hd->magic != kBwdMagic || hd->layout != LAYOUT || hd->M != M) return;
+  const int b = blockIdx.x;
+  if (b >= hd->prep_blocks) return;
+  const BwdPrep* items = (const BwdPrep*)(table + hd->prep_off);
+  int lo = 0, hi = hd->prep_items - 1;   // last item with block0 <= b
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (items[mid].block0 <= b) lo = mid; else hi = mid - 1;
+  }
+  const BwdPrep it = items[lo];
+  const int local = b - it.block0;
+  const int T = (int)hd->T;
+  switch (it.kind) {
+    case kPrepWt:
+      wt_expand_one<LAYOUT, M>((const uint32_t*)it.src0, (const uint32_t*)it.src1, it.a0, it.a1,
+                               it.a2, (uint32_t*)it.dst, (int64_t)local * 256 + threadIdx.x);
+      break;
+    case kPrepPad:
+      pad_rows_one((const uint16_t*)it.src0, T, it.a0, it.a1, (uint16_t*)it.dst,
+                   (int64_t)local * 256 + threadIdx.x);
+      break;
+    case kPrepTrDy:
+      transpose_tile<false>(it.src0, nullptr, T, it.a0, it.a0, (uint16_t*)it.dst, (int)hd->t32,
+                            local % it.a1, local / it.a1, tile);
+      break;
+    default:
+      transpose_tile<true>(it.src0, (const float*)it.src1, T, it.a0, it.a0, (uint16_t*)it.dst,
+                           (int)hd->t32, local % it.a1, local / it.a1, tile);
+      break;
+  }
+}
+
+__global__ __launch_bounds__(256, 1) void gemm_nt_group_kernel(const uint8_t* __restrict__ table,
+                                                                 int layout, int M) {
+  __shared__ __attribute__((aligned(16))) uint8_t ring[kNtRing * kNtStage];
+  const BwdHeader* hd = (const BwdHeader*)table;
+  if (hd->magic != kBwdMagic || hd->layout != layout || hd->M != M || (int)blockIdx.x >= hd->jobs)
+    return;
+  const BwdJob job = ((const BwdJob*)(table + hd->jobs_off))[blockIdx.x];
+  const BwdSeg* segs = (const BwdSeg*)(table + hd->segs_off) + job.seg0;
+  for (int s = 0; s < job.nseg; ++s) {
+    if (s > 0) {
+      // the previous segment's LDS reads and loads are done in every wave before the ring refills
+      __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
+      block_barrier_nofence();
+    }
+    const BwdSeg sg = segs[s];
+    NtTile t;
+    t.a = sg.a; t.b = sg.b; t.alpha = sg.alpha; t.c = job.c;
+    t.rows_a = job.rows_a; t.rows_b = job.rows_b; t.lda = sg.lda; t.ldb = sg.ldb;
+    t.ldc = job.ldc; t.R = sg.R; t.accumulate = sg.accumulate;
+    t.i0 = job.i0; t.j0 = job.j0;
+    // Opaque per-segment copies: without them the compiler hoists the tile's address arithmetic
+    // out of the segment loop, and the values it keeps live across the main loop spill (the
+    // main loop already holds 256 accumulators and all 256 vector registers).
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    asm volatile("" : "+s"(t.c), "+s"(t.rows_a), "+s"(t.rows_b), "+s"(t.ldc), "+s"(t.i0),
+                 "+s"(t.j0));
+    nt_tile(ring, t, tid);
   }
 }
 
@@ -488,6 +609,27 @@ hipError_t launch_bwd(const uint16_t* dy, int64_t T, int64_t n, const int8_t* xq
                                   nullptr, dw, (int)K, (flags & 2) != 0, s);
     if (e != hipSuccess) return e;
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_group(const void* table, int64_t prep_blocks, int64_t jobs, int layout,
+                            int M, hipStream_t s) {
+  const uint8_t* t = (const uint8_t*)table;
+  if (prep_blocks > 0) {
+    const unsigned g = (unsigned)prep_blocks;
+    if (layout == kLayoutSparse) {
+      if (M == 4) bwd_prep_kernel<kLayoutSparse, 4><<<g, 256, 0, s>>>(t);
+      else if (M == 8) bwd_prep_kernel<kLayoutSparse, 8><<<g, 256, 0, s>>>(t);
+      else bwd_prep_kernel<kLayoutSparse, 16><<<g, 256, 0, s>>>(t);
+    } else {
+      if (M == 4) bwd_prep_kernel<kLayoutDense2, 4><<<g, 256, 0, s>>>(t);
+      else if (M == 8) bwd_prep_kernel<kLayoutDense2, 8><<<g, 256, 0, s>>>(t);
+      else bwd_prep_kernel<kLayoutDense2, 16><<<g, 256, 0, s>>>(t);
+    }
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (jobs > 0) gemm_nt_group_kernel<<<(unsigned)jobs, 256, 0, s>>>(t, layout, M);
   return hipGetLastError();
 }
 

@@ -231,6 +231,110 @@ def test_bwd_rejects_before_launch(L):
     assert call(T=0, dw=None, dy=None, xq=None, xs=None) == 0
 
 
+GB = 1 << 30
+
+
+def _bdesc(L, slot, **kw):
+    """A grouped-backward descriptor whose buffers sit in their own 1 GiB slot of fake space."""
+    base = FAKE + slot * 16 * GB
+    a = dict(dy=base, xq=base + GB, x_scale=base + 2 * GB, K=256, codes=base + 3 * GB,
+             meta=base + 4 * GB, gamma=base + 5 * GB, n=128, dx=base + 6 * GB, dw=base + 7 * GB,
+             flags=0, reserved=0)
+    a.update(kw)
+    return L.BlBwdDesc(**a)
+
+
+def _bplan(L, descs, T=64, N=2, M=4, layout=0):
+    return L.bitlinear_bwd_group_plan((L.BlBwdDesc * len(descs))(*descs), T, N, M, layout)
+
+
+def test_bwd_group_plan_sizes(L):
+    """One projection needs the workspace of bitlinear_bwd; projections sharing an activation
+    share its transposed copy; jobs fill whole rounds of the 8 XCDs."""
+    T, n, K = 300, 300, 640
+    st, plan = _bplan(L, [_bdesc(L, 0, n=n, K=K)], T=T)
+    assert st == 0
+    assert plan.ws_bytes == L.bitlinear_bwd_workspace_bytes(T, n, K)[1]
+    assert (plan.N, plan.M, plan.layout) == (2, 4, 0)
+    tiles_dx = 2 * 3                         # ceil(300 / 256) x ceil(640 / 256)
+    tiles_dw = 2 * 3
+    assert plan.jobs % 8 == 0 and tiles_dx + tiles_dw <= plan.jobs < tiles_dx + tiles_dw + 8 * 8
+    # prep blocks: W_eff^T (K/M groups x n32/2 row pairs, 256 per block), dY pad (T x n32),
+    # dY^T and X^^T (64 x 64 tiles)
+    n32, tt = _up32(n), (T + 63) // 64
+    want = (-(-(K // 4 * n32 // 2) // 256) + -(-(T * n32) // 256) + tt * ((n + 63) // 64)
+            + tt * ((K + 63) // 64))
+    assert plan.prep_blocks == want
+    up = lambda v: (v + 255) // 256 * 256
+    t32 = _up32(T)
+    # two projections reading one activation (same xq, x_scale, K) and summing into one dx
+    a = _bdesc(L, 0, n=n, K=K)
+    b = _bdesc(L, 1, n=n, K=K, xq=a.xq, x_scale=a.x_scale, dx=a.dx, flags=1)
+    st, p2 = _bplan(L, [a, b], T=T)
+    assert st == 0
+    assert p2.ws_bytes == 2 * plan.ws_bytes - up(2 * K * t32)
+    assert p2.prep_blocks == 2 * plan.prep_blocks - tt * ((K + 63) // 64)
+    # T == 0: dx untouched, dw zeroed by the product launch; nothing to prepare
+    st, p0 = _bplan(L, [_bdesc(L, 0, dy=None, xq=None, x_scale=None)], T=0)
+    assert st == 0 and p0.prep_blocks == 0 and p0.ws_bytes == 0 and p0.jobs == 8
+    st, p0 = _bplan(L, [_bdesc(L, 0, dw=None)], T=0)
+    assert st == 0 and p0.jobs == 0
+
+
+def test_bwd_group_rejects_before_launch(L):
+    ok = _bdesc(L, 0)
+    assert _bplan(L, [ok])[0] == 0
+    assert _bplan(L, [_bdesc(L, 0, K=100)])[0] == -22
+    assert _bplan(L, [ok], N=1)[0] == -95
+    assert _bplan(L, [ok], T=-1)[0] == -22
+    assert _bplan(L, [_bdesc(L, 0, flags=4)])[0] == -22
+    assert _bplan(L, [_bdesc(L, 0, dx=None, dw=None)])[0] == -22
+    assert _bplan(L, [_bdesc(L, 0, dy=FAKE + 2)])[0] == -22
+    assert _bplan(L, [_bdesc(L, 0, meta=None)])[0] == -22
+    lib = L.lib()
+    assert lib.bitlinear_bwd_group_plan(None, 1, 64, 2, 4, 0, ctypes.byref(L.BlBwdGroupPlan())) == -22
+    assert lib.bitlinear_bwd_group_plan((L.BlBwdDesc * 1)(ok), 0, 64, 2, 4, 0,
+                                        ctypes.byref(L.BlBwdGroupPlan())) == -22
+    assert lib.bitlinear_bwd_group_plan((L.BlBwdDesc * 1)(ok), 1, 64, 2, 4, 0, None) == -22
+    # outputs: a shared dx must be the same buffer with the same K; nothing else may overlap
+    b = _bdesc(L, 1)
+    assert _bplan(L, [ok, _bdesc(L, 1, dx=ok.dx)])[0] == 0
+    assert _bplan(L, [ok, _bdesc(L, 1, dx=ok.dx + 64)])[0] == -22       # partial overlap
+    assert _bplan(L, [ok, _bdesc(L, 1, dx=ok.dx, K=512)])[0] == -22      # same start, other K
+    assert _bplan(L, [ok, _bdesc(L, 1, dw=ok.dw)])[0] == -22             # dw shared
+    assert _bplan(L, [ok, _bdesc(L, 1, dw=ok.dx + 1024)])[0] == -22      # dw inside a dx
+    assert _bplan(L, [ok, _bdesc(L, 1, dx=ok.dw)])[0] == -22             # dx on a dw
+    assert _bplan(L, [_bdesc(L, 0, dw=ok.dx + 64 * 256 * 4)])[0] == 0    # adjacent: fine
+    # an output over any input of the group
+    assert _bplan(L, [ok, _bdesc(L, 1, dx=ok.dy)])[0] == -22
+    assert _bplan(L, [ok, _bdesc(L, 1, dw=ok.xq)])[0] == -22
+    assert _bplan(L, [ok, _bdesc(L, 1, dw=ok.gamma - 8)])[0] == -22
+    assert _bplan(L, [ok, _bdesc(L, 1, dx=ok.codes + 2048)])[0] == -22   # codes: 4096 bytes
+    assert _bplan(L, [ok, _bdesc(L, 1, dx=ok.codes + 4096)])[0] == 0
+    assert _bplan(L, [ok, b])[0] == 0
+    # build: workspace / table checks come before anything is copied
+    st, plan = _bplan(L, [ok, b])
+    arr = (L.BlBwdDesc * 2)(ok, b)
+    W, TB = FAKE + 64 * 16 * GB, FAKE + 80 * 16 * GB
+    assert L.bitlinear_bwd_group_build(arr, 64, 2, 4, 0, W, plan.ws_bytes - 1, TB,
+                                       plan.table_bytes, None) == -28
+    assert L.bitlinear_bwd_group_build(arr, 64, 2, 4, 0, W, plan.ws_bytes, TB,
+                                       plan.table_bytes - 16, None) == -28
+    assert L.bitlinear_bwd_group_build(arr, 64, 2, 4, 0, W + 128, plan.ws_bytes, TB,
+                                       plan.table_bytes, None) == -22
+    assert L.bitlinear_bwd_group_build(arr, 64, 2, 4, 0, W, plan.ws_bytes, TB + 8,
+                                       plan.table_bytes, None) == -22
+    # launch: argument checks only
+    assert L.bitlinear_bwd_group(TB, None, None) == -22
+    assert L.bitlinear_bwd_group(TB + 4, plan, None) == -22
+    bad = L.BlBwdGroupPlan.from_buffer_copy(plan)
+    bad.layout = 7
+    assert L.bitlinear_bwd_group(TB, bad, None) == -95
+    bad = L.BlBwdGroupPlan.from_buffer_copy(plan)
+    bad.jobs = -1
+    assert L.bitlinear_bwd_group(TB, bad, None) == -22
+
+
 def _xdesc(L, **kw):
     P = FAKE
     a = dict(x=P, T=4, K=256, codes=P, meta=P, gamma=P, n=100, y=P, acc_opt=None)
