@@ -65,8 +65,8 @@ __global__ __launch_bounds__(64 * NW) void gemv_kernel(const int8_t* __restrict_
 #pragma unroll
   for (int u = 0; u < MAXU; ++u) {
     const int s = min(s_begin + u, NF - 1);     // past the end: reload the last step, code zeroed
-    c[u] = cp[(size_t)s * 64];
-    m[u] = SP ? mp[(size_t)s * 64] : kPadMeta;
+    c[u] = __builtin_nontemporal_load(cp + (size_t)s * 64);   // read once: streamed past the caches
+    m[u] = SP ? __builtin_nontemporal_load(mp + (size_t)s * 64) : kPadMeta;
   }
 
   // epilogue operands early: their latency hides behind the weight loads
