@@ -49,6 +49,7 @@ DOWN = (2560, 6912)
 N_PAIRS = 64
 DECODE_T = (1, 4, 16)
 COPY_BYTES = 512 << 20         # plain device copy used to scale HBM byte counters
+LAYER_STREAM_LAUNCHES = 100    # back-to-back grouped launches per T in the layer-stream reading
 PROFILE_PMC = os.path.join(ROOT, "profiles", "gemv_group_decode_pmc.md")
 GROUP_SRC = [os.path.join(ROOT, "sparsity_amd", "csrc", f)
              for f in ("gemv_group.hip", "device_common.hpp", "launch.hpp")]
@@ -700,6 +701,26 @@ def main():
     log(f"grouped GEMV: " + ", ".join(f"T={T} {mean_t[T] * 1e6:.1f} us" for T in DECODE_T) +
         f" -> {achieved:.1f} GB/s algorithmic")
 
+    # layer stream: the grouped launch repeated back to back on already quantized activations
+    # (the steady state of a long decode), weight bytes / (last end - first start)
+    layer_stream = {}
+    for T in DECODE_T:
+        for _ in range(3):
+            D.groups[T]()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(LAYER_STREAM_LAUNCHES):
+            D.groups[T]()
+        e1.record()
+        torch.cuda.synchronize()
+        t = e0.elapsed_time(e1) * 1e-3 / LAYER_STREAM_LAUNCHES
+        layer_stream[str(T)] = {"launch_us": round(t * 1e6, 2),
+                                "weight_GBps": round(D.packed_bytes / t / 1e9, 1),
+                                "algorithmic_GBps": round(algo[T] / t / 1e9, 1),
+                                "frac": round(algo[T] / t / 1e9 / HBM_PEAK_GBS, 4)}
+    log("layer stream: " + ", ".join(f"T={T} {layer_stream[str(T)]['algorithmic_GBps']} GB/s"
+                                     for T in DECODE_T))
+
     out = {
         "metric": "decode weight GB/s", "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
@@ -713,7 +734,8 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "kernel": "gemv_group_kernel<SPARSE>",
-                     "per_T": per_T_out},
+                     "per_T": per_T_out,
+                     "layer_stream": {"launches": LAYER_STREAM_LAUNCHES, "per_T": layer_stream}},
     }
     log("fused decode leg")
     out["decode_fused"] = decode_fused_leg(S, torch, D, ref, args.steps, args.warmup)

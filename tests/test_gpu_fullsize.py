@@ -9,7 +9,7 @@ import pytest
 
 import oracle as O
 from parity_util import assert_y_close, dev, f32_bits, host
-from synth import workload_inputs
+from synth import workload_grads, workload_inputs
 
 pytestmark = pytest.mark.gpu
 
@@ -165,3 +165,78 @@ def test_fourteen_sixteen_full_size():
     rows = np.unique(np.concatenate([[0, 4095], g.choice(4096, 30, replace=False)]))
     _check_sampled(ref, x, host(ys), host(accs), toks, rows, "14:16")
     print("14:16: sampled outputs ok", flush=True)
+
+
+U = 2.0 ** -24
+
+
+def _within(got, ref, bound, what):
+    got = np.asarray(got, np.float64)
+    bad = np.abs(got - ref) > bound + 1e-45
+    if bad.any():
+        i = tuple(np.argwhere(bad)[0])
+        raise AssertionError(f"{what}: {int(bad.sum())} outside the fp32 summation bound; first at "
+                             f"{i}: gpu {got[i]!r} ref {ref[i]!r} bound {bound[i]!r}")
+
+
+def test_train_step_backward_full_size_grouped():
+    """The layer set's grouped backward at 8192 tokens, launched as the training-step benchmark
+    launches it (the six K = 3200 projections summing into one dX in layer order, down into its
+    own): sampled dW rows and columns of every projection, sampled dX tokens and columns, against
+    the oracle's backward on the same slices, within the bound of fp32 summation in any order
+    (2 R u sum|terms| + u |ref| per product, plus u |partial sum| per dX accumulation)."""
+    import torch
+    T = 8192
+    d = workload_inputs("train_step", 0)
+    gr = workload_grads("train_step", 0)
+    Q = {K: _check_quant(d[f"X:{K}"], d[f"Xbits:{K}"], 0, f"bwd X:{K}") for K in (3200, 8640)}
+    q_ref = {K: O.act_quant(d[f"X:{K}"], 0) for K in Q}
+    dX = {K: torch.empty((T, K), dtype=torch.float32, device="cuda") for K in Q}
+    projs, refs, seen = [], [], set()
+    for L in ("q", "k", "v", "o", "gate", "up", "down"):
+        W = d[f"W:{L}"]
+        n, K = W.shape
+        ref, (codes, meta, gamma) = _check_pack(W, 2, 4, O.LAYOUT_SPARSE, f"bwd {L}")
+        projs.append(dict(dy=_bf16_dev(gr[f"dYbits:{L}"]), xq=Q[K][0], scale=Q[K][1], K=K,
+                          codes=codes, meta=meta, gamma=gamma, n=n, dx=dX[K],
+                          dw=torch.empty((n, K), dtype=torch.float32, device="cuda"),
+                          accumulate=(K in seen, False)))
+        refs.append((L, ref, n, K))
+        seen.add(K)
+    S.BwdGroup(projs, T)()
+    torch.cuda.synchronize()
+    print("grouped backward done", flush=True)
+    g = np.random.default_rng(808)
+    toks = np.unique(np.concatenate([[0, T - 1], g.choice(T, 2, replace=False)]))
+    sums = {K: (np.zeros((len(toks), K)), np.zeros((len(toks), K)))
+            for K in Q}   # running reference sum and its bound, sampled dX rows
+    for (L, ref, n, K), p in zip(refs, projs):
+        dy = gr[f"dY:{L}"].astype(np.float64)
+        q, sc = q_ref[K]
+        W_eff, gamma = ref["W_eff"], ref["gamma"]
+        dw = host(p["dw"])
+        rows = np.unique(np.concatenate([[0, n - 1], g.choice(n, 2, replace=False)]))
+        cols = np.unique(np.concatenate([[0, K - 1], g.choice(K, 2, replace=False)]))
+        # dW rows: dW[o] = dY[:, o]^T X^, over all K
+        _, dw_r = O.backward(dy[:, rows], W_eff[rows], gamma, q, sc)
+        xh = np.abs(O.dequant_act(q, sc).astype(np.float64))
+        mag = np.abs(dy[:, rows]).T @ xh
+        _within(dw[rows], dw_r, 2 * T * U * mag + U * np.abs(dw_r), f"{L} dW rows")
+        # dW columns: dW[:, k] = dY^T X^[:, k], over all out-features
+        _, dw_c = O.backward(dy, W_eff[:, cols], gamma, q[:, cols], sc)
+        mag = np.abs(dy).T @ xh[:, cols]
+        _within(dw[:, cols], dw_c, 2 * T * U * mag + U * np.abs(dw_c), f"{L} dW columns")
+        del xh
+        # dX tokens: this projection's term of the running sum in layer order
+        dx_t, _ = O.backward(dy[toks], W_eff, gamma, q[toks], sc[toks])
+        mag = np.float64(gamma) * (np.abs(dy[toks]) @ np.abs(W_eff.astype(np.float64)))
+        r, b = sums[K]
+        r += dx_t
+        b += 2 * n * U * mag + U * np.abs(dx_t)
+        if p["accumulate"][0]:
+            b += U * np.abs(r)
+        print(f"{L} {n}x{K}: sampled dW rows and columns ok", flush=True)
+    for K in Q:
+        r, b = sums[K]
+        _within(host(dX[K])[toks], r, b, f"dX:{K} sampled tokens")
+        print(f"dX:{K}: sampled tokens ok", flush=True)
