@@ -5,6 +5,8 @@
 #include <string.h>
 
 #include <algorithm>
+#include <map>
+#include <tuple>
 #include <vector>
 
 #include "bitlinear.h"
@@ -289,8 +291,7 @@ int plan_bwd_group(const bl_bwd_desc* d, int64_t count, int64_t T, int N, int M,
   };
   // workspace and prep items, in descriptor order
   std::vector<const uint16_t*> dx_a(count), wt(count), dyt(count), xt(count);
-  struct XKey { const int8_t* xq; const float* xs; int64_t K; const uint16_t* xt; };
-  std::vector<XKey> xs_seen;
+  std::map<std::tuple<const int8_t*, const float*, int64_t>, const uint16_t*> xs_seen;
   int64_t blocks = 0;
   auto add_prep = [&](int32_t kind, int64_t nblocks, int a0, int a1, int a2, const void* s0,
                       const void* s1, void* dst) {
@@ -328,16 +329,15 @@ int plan_bwd_group(const bl_bwd_desc* d, int64_t count, int64_t T, int N, int M,
       const int tn = (int)((q.n + 63) / 64);
       add_prep(bl::kPrepTrDy, (int64_t)tt * tn, (int)q.n, tn, 0, q.dy, nullptr, p);
       dyt[i] = p;
-      const XKey* hit = nullptr;
-      for (const XKey& k : xs_seen)
-        if (k.xq == q.xq && k.xs == q.x_scale && k.K == q.K) hit = &k;
-      if (hit) {
-        xt[i] = hit->xt;
+      const auto key = std::make_tuple(q.xq, q.x_scale, q.K);
+      const auto hit = xs_seen.find(key);
+      if (hit != xs_seen.end()) {
+        xt[i] = hit->second;
       } else {
         uint16_t* x = (uint16_t*)carve((size_t)q.K * t32 * 2);
         const int tk = (int)((q.K + 63) / 64);
         add_prep(bl::kPrepTrX, (int64_t)tt * tk, (int)q.K, tk, 0, q.xq, q.x_scale, x);
-        xs_seen.push_back({q.xq, q.x_scale, q.K, x});
+        xs_seen.emplace(key, x);
         xt[i] = x;
       }
     }
@@ -349,13 +349,20 @@ int plan_bwd_group(const bl_bwd_desc* d, int64_t count, int64_t T, int N, int M,
   // products: one per distinct dx (segments = its projections in order), one per dw
   struct Gemm { float* c; int64_t rows_a, rows_b, ldc; int32_t seg0, nseg; int64_t work; };
   std::vector<Gemm> gemms;
-  std::vector<float*> dx_seen;
+  // projections of each distinct dx, in descriptor order; dx buffers in order of first use
+  std::map<float*, std::vector<int64_t>> dx_users;
+  std::vector<float*> dx_order;
   for (int64_t i = 0; i < count && T > 0; ++i) {
-    if (!d[i].dx || std::find(dx_seen.begin(), dx_seen.end(), d[i].dx) != dx_seen.end()) continue;
-    dx_seen.push_back(d[i].dx);
-    Gemm g{d[i].dx, T, d[i].K, d[i].K, (int32_t)P->segs.size(), 0, 0};
-    for (int64_t j = i; j < count; ++j) {
-      if (d[j].dx != d[i].dx) continue;
+    if (!d[i].dx) continue;
+    auto& users = dx_users[d[i].dx];
+    if (users.empty()) dx_order.push_back(d[i].dx);
+    users.push_back(i);
+  }
+  for (float* dxp : dx_order) {
+    const std::vector<int64_t>& users = dx_users[dxp];
+    const int64_t i = users.front();
+    Gemm g{dxp, T, d[i].K, d[i].K, (int32_t)P->segs.size(), 0, 0};
+    for (const int64_t j : users) {
       const int64_t n32 = (d[j].n + 31) / 32 * 32;
       bl::BwdSeg sg;
       memset(&sg, 0, sizeof sg);
