@@ -6,8 +6,11 @@
 // pass (SlideSparse abstract, Activation Lifting): group g of 8 becomes 12 values
 // [x0 x1 x2 x3 | x2 x3 x4 x5 | x4 x5 x6 x7], a group of 16 becomes 28 (seven windows).
 //
-// One block per token: pass 1 takes absmax as the maximum of |x| bit patterns (exact, order
-// free); pass 2 re-reads the row (L2 resident) and writes int8 with round-half-even.
+// absmax is the maximum of the |x| bit patterns (exact, order free); the int8 values are written
+// with round-half-even.  Rows of up to 16384 elements (bf16; 8192 fp32) go to act_quant_row_kernel:
+// one wave per token, holding its share of the row in registers, so the row is read from memory
+// once and the token needs no block barrier.  Longer rows fall back to act_quant_kernel: one block
+// per token, the row read twice (the second pass from L2).
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -83,8 +86,128 @@ __global__ __launch_bounds__(256) void act_quant_kernel(const void* __restrict__
   if (threadIdx.x == 0) xs[t] = amax / 127.f;
 }
 
+// Raw bits of one 8-element piece: 4 dwords of bf16 pairs, or 8 fp32.
+template <bool BF16>
+struct Piece {
+  uint32_t w[BF16 ? 4 : 8];
+};
+
+template <bool BF16>
+__device__ __forceinline__ void load_piece(const void* __restrict__ x, size_t off, Piece<BF16>& p) {
+  if constexpr (BF16) {
+    const uint4 u = *(const uint4*)((const uint16_t*)x + off);
+    p.w[0] = u.x; p.w[1] = u.y; p.w[2] = u.z; p.w[3] = u.w;
+  } else {
+    const uint4 a = *(const uint4*)((const float*)x + off);
+    const uint4 b = *(const uint4*)((const float*)x + off + 4);
+    p.w[0] = a.x; p.w[1] = a.y; p.w[2] = a.z; p.w[3] = a.w;
+    p.w[4] = b.x; p.w[5] = b.y; p.w[6] = b.z; p.w[7] = b.w;
+  }
+}
+
+template <bool BF16>
+__device__ __forceinline__ float piece_value(const Piece<BF16>& p, int j) {
+  if constexpr (BF16) return __uint_as_float(j & 1 ? p.w[j / 2] & 0xFFFF0000u : p.w[j / 2] << 16);
+  else return __uint_as_float(p.w[j]);
+}
+
+// One wave per token, four tokens per block.  Lane l holds chunks l, l + 64, ... (CPL at most) of
+// its token's row, CH elements each (8, or the LM elements of a lifting group), loaded before the
+// absmax so all of a lane's loads are in flight at once; the quantized chunks are written from the
+// registers.
+template <bool BF16, int LM, int CPL>
+__global__ __launch_bounds__(256) void act_quant_row_kernel(const void* __restrict__ x, int T,
+                                                            int K, int8_t* __restrict__ xq,
+                                                            float* __restrict__ xs) {
+  constexpr int CH = LM ? LM : 8;
+  constexpr int PPC = CH / 8;             // pieces per chunk
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;                     // the whole wave
+  const int nchunk = K / CH;
+  const size_t row = (size_t)t * K;
+  Piece<BF16> p[CPL][PPC];
+#pragma unroll
+  for (int i = 0; i < CPL; ++i) {
+    const int c = min(lane + 64 * i, nchunk - 1);   // past the end: reload the last chunk
+#pragma unroll
+    for (int h = 0; h < PPC; ++h) load_piece<BF16>(x, row + (size_t)CH * c + 8 * h, p[i][h]);
+  }
+  uint32_t mx = 0;
+#pragma unroll
+  for (int i = 0; i < CPL; ++i)
+#pragma unroll
+    for (int h = 0; h < PPC; ++h)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) mx = max(mx, __float_as_uint(piece_value<BF16>(p[i][h], j)) & 0x7FFFFFFFu);
+  // the raw words pass through opaque copies: without them the compiler keeps every element's
+  // unpacked value from the absmax loop alive for the quantization (twice the registers)
+#pragma unroll
+  for (int i = 0; i < CPL; ++i)
+#pragma unroll
+    for (int h = 0; h < PPC; ++h)
+#pragma unroll
+      for (int k = 0; k < (BF16 ? 4 : 8); ++k) asm volatile("" : "+v"(p[i][h].w[k]));
+  mx = wave_max_u32(mx);
+  const float amax = __uint_as_float(mx);
+  const float s = amax > 0.f ? 127.f / amax : 0.f;
+#pragma unroll
+  for (int i = 0; i < CPL; ++i) {
+    const int c = lane + 64 * i;
+    if (c >= nchunk) break;
+    uint32_t q[CH];
+#pragma unroll
+    for (int h = 0; h < PPC; ++h)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) q[8 * h + j] = q8(piece_value<BF16>(p[i][h], j), s);
+    if constexpr (LM != 0) {
+      constexpr int NW = LM / 2 - 1;
+      const size_t keff = (size_t)K / LM * (2 * LM - 4);
+      uint32_t* o = (uint32_t*)(xq + (size_t)t * keff + (size_t)(2 * LM - 4) * c);
+#pragma unroll
+      for (int w = 0; w < NW; ++w)
+        o[w] = q[2 * w] | (q[2 * w + 1] << 8) | (q[2 * w + 2] << 16) | (q[2 * w + 3] << 24);
+    } else {
+      const uint32_t lo = q[0] | (q[1] << 8) | (q[2] << 16) | (q[3] << 24);
+      const uint32_t hi = q[4] | (q[5] << 8) | (q[6] << 16) | (q[7] << 24);
+      *(uint2*)(xq + row + 8 * (size_t)c) = make_uint2(lo, hi);
+    }
+  }
+  if (lane == 0) xs[t] = amax / 127.f;
+}
+
+template <bool BF16, int LM>
+static bool launch_rows(const void* x, int64_t T, int64_t K, int8_t* xq, float* xs,
+                        hipStream_t s) {
+  constexpr int CH = LM ? LM : 8;
+  const int64_t cpl = (K / CH + 63) / 64;      // chunks per lane
+  const dim3 grid((unsigned)((T + 3) / 4));
+  auto run = [&](auto kern) { kern<<<grid, 256, 0, s>>>(x, (int)T, (int)K, xq, xs); };
+  // raw registers per lane: CPL * CH / 2 (bf16) or CPL * CH (fp32); at most 128
+  constexpr int MAXR = 128 / (BF16 ? CH / 2 : CH);
+  if (cpl <= 4) run(act_quant_row_kernel<BF16, LM, 4>);
+  else if (cpl <= 8) run(act_quant_row_kernel<BF16, LM, 8>);
+  else if (cpl <= 12 && MAXR >= 12) run(act_quant_row_kernel<BF16, LM, (MAXR >= 12 ? 12 : 4)>);
+  else if (cpl <= 16 && MAXR >= 16) run(act_quant_row_kernel<BF16, LM, (MAXR >= 16 ? 16 : 4)>);
+  else if (cpl <= 24 && MAXR >= 24) run(act_quant_row_kernel<BF16, LM, (MAXR >= 24 ? 24 : 4)>);
+  else if (cpl <= 32 && MAXR >= 32) run(act_quant_row_kernel<BF16, LM, (MAXR >= 32 ? 32 : 4)>);
+  else return false;
+  return true;
+}
+
 hipError_t launch_act_quant(const void* x, int x_is_bf16, int64_t T, int64_t K, int lift_M,
                             int8_t* xq, float* x_scale, hipStream_t s) {
+  bool done;
+  if (x_is_bf16) {
+    if (lift_M == 8) done = launch_rows<true, 8>(x, T, K, xq, x_scale, s);
+    else if (lift_M == 16) done = launch_rows<true, 16>(x, T, K, xq, x_scale, s);
+    else done = launch_rows<true, 0>(x, T, K, xq, x_scale, s);
+  } else {
+    if (lift_M == 8) done = launch_rows<false, 8>(x, T, K, xq, x_scale, s);
+    else if (lift_M == 16) done = launch_rows<false, 16>(x, T, K, xq, x_scale, s);
+    else done = launch_rows<false, 0>(x, T, K, xq, x_scale, s);
+  }
+  if (done) return hipGetLastError();
   const dim3 grid((unsigned)T);
   auto run = [&](auto kern) { kern<<<grid, 256, 0, s>>>(x, (int)K, xq, x_scale); };
   if (x_is_bf16) {

@@ -141,6 +141,29 @@ def test_act_quant(lift, dtype, T, K):
     assert np.array_equal(f32_bits(host(sc)), f32_bits(sc_ref))
 
 
+@pytest.mark.parametrize("lift", [0, 8, 16])
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("K", [2560, 6144, 8192, 12288, 16384, 16400])
+def test_act_quant_row_widths(lift, dtype, K):
+    """Every register budget of the one-wave-per-token kernel (4 to 32 chunks per lane) and the
+    fallback to the two-pass kernel for longer rows (fp32 past 8192, bf16 past 16384), with a
+    token count that leaves the last block of four tokens partly empty."""
+    g = rng(K + lift + (dtype == "bf16"))
+    T = 5
+    x = act_normal(g, T, K)
+    x[1, K - 1] = -300.0                # absmax in the last element of a row
+    x[4, :] = 0.0
+    if dtype == "bf16":
+        x, bits = to_bf16(x)
+        xd = bf16_dev(bits)
+    else:
+        xd = dev(x)
+    xq_ref, sc_ref = O.act_quant(x, lift)
+    xq, sc = S.act_quant(xd, lift)
+    assert np.array_equal(host(xq), xq_ref)
+    assert np.array_equal(f32_bits(host(sc)), f32_bits(sc_ref))
+
+
 def test_act_quant_empty():
     import torch
     x = torch.zeros((0, 256), dtype=torch.float32, device="cuda")
