@@ -63,7 +63,7 @@ int check_fwd(const int8_t* xq, const float* x_scale, int64_t T, int64_t K, cons
   return BL_OK;
 }
 
-// Work-item plan of a group.  Items are runs of kGroupWaves panels of one projection; the hardware
+// Work-item plan of a group.  Items are runs of kGroupPanels panels of one projection; the hardware
 // hands workgroup b to XCD b % kXcds, so the plan cuts the projections' items (in projection order)
 // into kXcds contiguous runs of about equal weight bytes -- each projection's activation rows then
 // land in one or two XCDs' L2 -- and orders each XCD's run largest item first, so the launch ends
@@ -83,8 +83,8 @@ int plan_group(const bl_fwd_desc* d, int64_t count, int N, int M, int layout,
     if (d[i].T > 32) return BL_EINVAL;
     if (d[i].T == 0) continue;
     const int64_t panels = (d[i].n + 31) / 32;
-    for (int64_t p0 = 0; p0 < panels; p0 += bl::kGroupWaves) {
-      const uint64_t np = (uint64_t)std::min<int64_t>(bl::kGroupWaves, panels - p0);
+    for (int64_t p0 = 0; p0 < panels; p0 += bl::kGroupPanels) {
+      const uint64_t np = (uint64_t)std::min<int64_t>(bl::kGroupPanels, panels - p0);
       items.push_back({(uint32_t)i, (uint32_t)p0, np * (uint64_t)ke});
       total += np * (uint64_t)ke;
       if (items.size() > (size_t)INT32_MAX / (2 * bl::kXcds)) return BL_EINVAL;

@@ -7,8 +7,10 @@
 // projections of a decoder (Q/K/V, gate/up) and of a stream of layers whose activations are
 // already quantized.
 //
-// Work item = up to 8 consecutive 32-row panels of one projection; wave w of the block owns panel
-// w over the whole K axis, so no cross-wave reduction is needed.  The host lays the items out so
+// Work item = up to 16 consecutive 32-row panels of one projection; wave w of the block owns panels
+// w and w + 8 over the whole K axis, so no cross-wave reduction is needed, and every activation
+// byte staged in LDS feeds two MFMAs per wave (at T = 16 the item's activation rows are a quarter
+// of its weight bytes, read from L2 once per item).  The host lays the items out so
 // that each XCD gets a contiguous run of the projections (their activation rows stay in that XCD's
 // L2) and starts with its largest items.  K is walked in chunks of kGS MFMA steps:
 //   - the wave's packed weights (one code and one meta dword per lane per step) are loaded straight
@@ -36,7 +38,8 @@ namespace bl {
 
 namespace {
 constexpr int kGS = 4;  // MFMA steps per chunk
-constexpr int kGD = 4;  // register ring depth in chunks
+constexpr int kGD = 3;  // register ring depth in chunks (two panels per wave: 121 VGPRs, two
+                        // blocks per CU)
 
 typedef __attribute__((address_space(1))) const uint32_t g_u32;
 typedef __attribute__((address_space(1))) const v4i g_v4i;
@@ -47,7 +50,7 @@ typedef __attribute__((address_space(1))) const v4i g_v4i;
 // of bf16 in the fused variant).
 template <int BPT, int VPP>
 struct GroupChunk {
-  uint32_t c[kGS], m[kGS];
+  uint32_t c[kGS * kGroupPanelsPerWave], m[kGS * kGroupPanelsPerWave];   // [panel][step]
   v4i b[BPT * VPP];
 };
 
@@ -64,23 +67,26 @@ struct GroupGemv {
   typedef GroupChunk<BPT, VPP> Chunk;
 
   int8_t* bs;             // LDS: two buffers of 32 rows x ROW bytes
-  g_u32* cp;              // this lane's code dword of step 0 of the wave's panel
-  g_u32* mp;
+  g_u32* cp[kGroupPanelsPerWave];   // this lane's code dword of step 0 of each of the wave's panels
+  g_u32* mp[kGroupPanelsPerWave];
+  int cs[kGroupPanelsPerWave];      // dwords between steps: 64, or 0 for a panel past the end
   __attribute__((address_space(1))) const int8_t* xq;   // int8 rows, or bf16 rows (fused)
   int tid, T, Keff, NF, nch, bpieces, brow, h;
   float qs[BPT];          // fused: 127 / absmax of the token row of each of this thread's pieces
-  v16i acc;
+  v16i acc[kGroupPanelsPerWave];
 
   // Every call issues the same number of loads (addresses clamped into the projection), so the
   // compiler waits for one chunk with a fixed vmcnt instead of draining the ring.  Clamped reads
   // past the end of K only meet steps whose code is forced to 0.
   __device__ __forceinline__ void issue(int j, Chunk& r) const {
 #pragma unroll
-    for (int u = 0; u < kGS; ++u) {
-      const int s = min(j * kGS + u, NF - 1);
-      r.c[u] = __builtin_nontemporal_load(cp + (size_t)s * 64);
-      r.m[u] = SP ? __builtin_nontemporal_load(mp + (size_t)s * 64) : kPadMeta;
-    }
+    for (int p = 0; p < kGroupPanelsPerWave; ++p)
+#pragma unroll
+      for (int u = 0; u < kGS; ++u) {
+        const int s = min(j * kGS + u, NF - 1);
+        r.c[p * kGS + u] = __builtin_nontemporal_load(cp[p] + (size_t)s * cs[p]);
+        r.m[p * kGS + u] = SP ? __builtin_nontemporal_load(mp[p] + (size_t)s * cs[p]) : kPadMeta;
+      }
 #pragma unroll
     for (int k = 0; k < BPT; ++k) {
       const int pc = tid + k * NT;
@@ -122,7 +128,10 @@ struct GroupGemv {
     for (int u = 0; u < kGS; ++u) {
       const int4 blo = *(const int4*)(xr + u * KSTEP);
       const int4 bhi = SP ? *(const int4*)(xr + u * KSTEP + 32) : make_int4(0, 0, 0, 0);
-      acc = mfma_step<SP>(j * kGS + u < NF ? r.c[u] : 0u, r.m[u], blo, bhi, acc);
+      const bool live = j * kGS + u < NF;
+#pragma unroll
+      for (int p = 0; p < kGroupPanelsPerWave; ++p)
+        acc[p] = mfma_step<SP>(live ? r.c[p * kGS + u] : 0u, r.m[p * kGS + u], blo, bhi, acc[p]);
     }
   }
   // chunk j: MFMAs from LDS buffer j & 1 (skipped past the end), chunk j + 1's rows to the other
@@ -161,12 +170,19 @@ __global__ __launch_bounds__(64 * kGroupWaves, 2) void gemv_group_kernel(
   k.Keff = L.Keff;
   const int n = L.n;
   const int npanels = (n + kPanel - 1) / kPanel;
-  const int P = (int)it.panel0 + wave;
-  const int Pl = min(P, npanels - 1);        // surplus waves load a real panel, store nothing
   k.NF = k.Keff / G::KSTEP;
   k.nch = (k.NF + kGS - 1) / kGS;
-  k.cp = (g_u32*)L.codes + (size_t)Pl * k.NF * 64 + lane;
-  k.mp = G::SP ? (g_u32*)L.meta + (size_t)Pl * k.NF * 64 + lane : nullptr;
+  int P[kGroupPanelsPerWave];
+#pragma unroll
+  for (int p = 0; p < kGroupPanelsPerWave; ++p) {
+    P[p] = (int)it.panel0 + p * kGroupWaves + wave;
+    // a panel past the projection re-reads one step of the last real panel at every step (a
+    // cache hit: the loads of every chunk stay the same in number) and stores nothing
+    const int Pl = min(P[p], npanels - 1);
+    k.cp[p] = (g_u32*)L.codes + (size_t)Pl * k.NF * 64 + lane;
+    k.mp[p] = G::SP ? (g_u32*)L.meta + (size_t)Pl * k.NF * 64 + lane : nullptr;
+    k.cs[p] = P[p] < npanels ? 64 : 0;
+  }
   k.xq = (__attribute__((address_space(1))) const int8_t*)L.xq;
   k.bs = bs;
   k.bpieces = k.T * G::V16;
@@ -215,36 +231,40 @@ __global__ __launch_bounds__(64 * kGroupWaves, 2) void gemv_group_kernel(
 
   k.put(0, r[0]);
   block_sync_lds();
-  k.acc = v16i{};
+#pragma unroll
+  for (int p = 0; p < kGroupPanelsPerWave; ++p) k.acc[p] = v16i{};
   // nch rounded up to the ring depth: the trailing chunks skip their MFMAs, not their loads
   for (int j = 0; j < k.nch; j += kGD) {
 #pragma unroll
     for (int q = 0; q < kGD; ++q) k.step(j + q, r[q], r[(q + 1) % kGD]);
   }
-  const v16i acc = k.acc;
-
-  if (tok >= k.T || P >= npanels) return;
+  if (tok >= k.T) return;
   const int h = k.h;
   const bool vec = (n & 3) == 0;
 #pragma unroll
-  for (int g = 0; g < 4; ++g) {
-    const int o = P * kPanel + 8 * g + 4 * h;
-    const size_t idx = (size_t)tok * n + o;
-    float v[4];
+  for (int p = 0; p < kGroupPanelsPerWave; ++p) {
+    if (P[p] >= npanels) break;
+    const v16i acc = k.acc[p];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) v[i] = ((float)acc[4 * g + i] * gamma) * sc;
-    if (vec && o + 3 < n) {
-      *(float4*)(L.y + idx) = make_float4(v[0], v[1], v[2], v[3]);
-      if (L.acc)
+    for (int g = 0; g < 4; ++g) {
+      const int o = P[p] * kPanel + 8 * g + 4 * h;
+      const size_t idx = (size_t)tok * n + o;
+      float v[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) L.acc[idx + i] = acc[4 * g + i];
-    } else {
+      for (int i = 0; i < 4; ++i) v[i] = ((float)acc[4 * g + i] * gamma) * sc;
+      if (vec && o + 3 < n) {
+        *(float4*)(L.y + idx) = make_float4(v[0], v[1], v[2], v[3]);
+        if (L.acc)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (o + i < n) {
-          L.y[idx + i] = v[i];
-          if (L.acc) L.acc[idx + i] = acc[4 * g + i];
-        }
+          for (int i = 0; i < 4; ++i) L.acc[idx + i] = acc[4 * g + i];
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (o + i < n) {
+            L.y[idx + i] = v[i];
+            if (L.acc) L.acc[idx + i] = acc[4 * g + i];
+          }
+      }
     }
   }
 }

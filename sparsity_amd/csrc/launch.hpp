@@ -27,9 +27,11 @@ namespace bl {
 
 // Device table of a group of independent decode projections (bitlinear_group_build writes it,
 // gemv_group_kernel reads it): a header, one GroupLayer per projection, then one GroupItem per
-// work item in launch order.  A work item is up to kGroupWaves consecutive 32-row panels of one
-// projection, one panel per wave.
+// work item in launch order.  A work item is up to kGroupPanels consecutive 32-row panels of one
+// projection: wave w of the block takes panels w and w + kGroupWaves.
 constexpr int kGroupWaves = 8;
+constexpr int kGroupPanelsPerWave = 2;
+constexpr int kGroupPanels = kGroupWaves * kGroupPanelsPerWave;
 constexpr int kXcds = 8;                       // MI355X: 8 XCDs, workgroups dealt round-robin
 constexpr uint32_t kGroupMagic = 0x32474c42u;  // "BLG2"
 constexpr uint32_t kGroupNoItem = 0xFFFFFFFFu; // padding item: its block does nothing

@@ -151,9 +151,9 @@ def test_group_sizes_and_rejects_before_launch(L):
     arr = (L.BlFwdDesc * 3)(_desc(L), _desc(L, n=6912, K=2560, T=16), _desc(L, T=0, xq=None))
     st, tb, wi = L.bitlinear_group_table_bytes(arr, 2, 4, 0)
     assert st == 0
-    # 8 panels of 32 rows per work item (1 + 27 items; the T == 0 projection has none), laid out
+    # 16 panels of 32 rows per work item (1 + 14 items; the T == 0 projection has none), laid out
     # over the 8 XCDs' launch positions, padded to a whole number of rounds
-    assert wi % 8 == 0 and 28 <= wi <= 28 + 8 * 8
+    assert wi % 8 == 0 and 15 <= wi <= 15 + 8 * 8
     assert tb >= 64 + 3 * 72 + 8 * wi and tb % 16 == 0
 
     def one(**kw):
