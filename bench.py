@@ -221,8 +221,8 @@ def decode_fused_leg(S, torch, D, ref, steps, warmup):
 def decode_mall_leg(S, torch, D, pairs=24, launches=100):
     """The decode layer stream shrunk to fit the 256 MB last-level cache: the first `pairs` up/down
     pairs (212 MB of packed weights for 24: enough work items to fill the chip) in one grouped
-    launch at T = 1, repeated back to back,
-    so every launch after the first reads its weights from the cache rather than HBM."""
+    launch at T = 1, repeated back to back, so every launch after the first can read its weights
+    from the cache rather than HBM."""
     xq, sc = D.q[(1, UP[1])]
     xd, sd = D.q[(1, DOWN[1])]
     projs = []
