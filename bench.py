@@ -427,9 +427,11 @@ TRAIN_LAYERS = (("q", 3200, 3200), ("k", 3200, 3200), ("v", 3200, 3200), ("o", 3
 
 
 def train_step_leg(S, torch, iters=3):
-    """3B-alike decoder layer set at 8192 tokens: re-mask + ternarize + pack all 7 fp32 masters,
-    quantize the two activation matrices once, then the 7 2:4 forwards.  Each phase is one HIP
-    graph (checked against the eager run) timed with events around its replays."""
+    """3B-alike decoder layer set at 8192 tokens: re-mask + ternarize + pack all 7 fp32 masters
+    (one grouped pack), quantize the two activation matrices once, the 7 2:4 forwards, then the
+    grouped backward of all 7.  Each phase is one HIP graph (checked against the eager run of the
+    separate calls) timed with events around its replays; the separate pack and backward calls
+    are timed beside the grouped ones."""
     T = 8192
     g = torch.Generator(device="cuda")
     g.manual_seed(35)
@@ -452,9 +454,15 @@ def train_step_leg(S, torch, iters=3):
     bws = torch.empty(max(S.bwd_workspace_bytes(T, n, K) for (_, n, K) in TRAIN_LAYERS),
                       dtype=torch.uint8, device="cuda")
 
-    def pack_all():
+    def pack_seq():
         for W, out in zip(masters, packed):
             S.pack(W, 2, 4, out=out, ws=ws)
+
+    # the same seven packs as one grouped pack (one partial-sum launch, one pack launch)
+    pgroup = S.PackGroup([dict(W=W, out=p) for W, p in zip(masters, packed)])
+
+    def pack_all():
+        pgroup()
 
     def quant_all():
         for K in X:
@@ -493,22 +501,25 @@ def train_step_leg(S, torch, iters=3):
     def outputs():
         return [t.clone() for t in results()]
 
-    pack_all()
+    pack_seq()
     quant_all()
     fwd_all()
     bwd_seq()
     torch.cuda.synchronize()
     ref = outputs()
-    for t in dWs + list(dXs.values()):
+    for t in results():
         t.zero_()
+    pack_all()
+    quant_all()
+    fwd_all()
     bwd_all()
     torch.cuda.synchronize()
     for a, b in zip(outputs(), ref):
         if not torch.equal(a, b):
-            raise RuntimeError("grouped backward differs from the sequential calls")
+            raise RuntimeError("grouped pack or backward differs from the sequential calls")
     graphs = []
     cap = torch.cuda.Stream()
-    for fn in (pack_all, quant_all, fwd_all, bwd_seq, bwd_all):
+    for fn in (pack_seq, pack_all, quant_all, fwd_all, bwd_seq, bwd_all):
         gr = torch.cuda.CUDAGraph()
         with torch.cuda.graph(gr, stream=cap):
             fn()
@@ -522,11 +533,12 @@ def train_step_leg(S, torch, iters=3):
         for a, b in zip(outputs(), ref):
             if not torch.equal(a, b):
                 raise RuntimeError("training-step graph replay differs from the eager run")
-    t_pack = _event_ms(torch, graphs[0].replay, iters)
-    t_quant = _event_ms(torch, graphs[1].replay, iters)
-    t_fwd = _event_ms(torch, graphs[2].replay, iters)
-    t_bwd_seq = _event_ms(torch, graphs[3].replay, iters)
-    t_bwd = _event_ms(torch, graphs[4].replay, iters)
+    t_pack_seq = _event_ms(torch, graphs[0].replay, iters)
+    t_pack = _event_ms(torch, graphs[1].replay, iters)
+    t_quant = _event_ms(torch, graphs[2].replay, iters)
+    t_fwd = _event_ms(torch, graphs[3].replay, iters)
+    t_bwd_seq = _event_ms(torch, graphs[4].replay, iters)
+    t_bwd = _event_ms(torch, graphs[5].replay, iters)
     pack_bytes = sum(4 * n * K + p[0].numel() + p[1].numel() for (_, n, K), p in zip(TRAIN_LAYERS, packed))
     # act_quant: bf16 read + int8 write per element + 4 B scale per token
     quant_bytes = sum(T * K * 3 + 4 * T for K in X)
@@ -543,6 +555,8 @@ def train_step_leg(S, torch, iters=3):
             # the seven bitlinear_bwd calls one after another (same results, bit for bit)
             "bwd_sequential_ms": round(t_bwd_seq, 4),
             "pack_ms": round(t_pack, 4), "pack_GBps": round(pack_gbs, 1),
+            # the seven bitlinear_pack calls one after another (same results, bit for bit)
+            "pack_sequential_ms": round(t_pack_seq, 4),
             "act_quant_ms": round(t_quant, 4), "act_quant_GBps": round(quant_gbs, 1),
             "fwd_ms": round(t_fwd, 4), "fwd_TOPS": round(fwd_tops, 1),
             # algorithmic bytes (pack: 4 B read + packed bytes written per weight, one pass over

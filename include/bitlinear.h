@@ -119,6 +119,50 @@ int bitlinear_fwd(const int8_t* xq, const float* x_scale, int64_t T, int64_t K,
                   int layout, int64_t n, float* y, int32_t* acc_opt, void* stream);
 
 /* ---------------------------------------------------------------------------------------------
+ * Grouped pack: the bitlinear_pack calls of several masters (a training step re-packs every
+ * master of a layer set; Sparse-BitNet technical summary, the mask is recomputed at each step) in
+ * two launches instead of two per master.
+ *
+ * Each master's gamma, codes and meta are exactly bitlinear_pack's, bit for bit.  One launch
+ * takes the partial sums of |W| of every master; the other masks, ternarizes and packs every
+ * tile of every master, the masters read last by the first launch first (they are still in the
+ * last-level cache).  All masters share (N, M, layout); each follows bitlinear_pack's shape and
+ * alignment rules.  Masters may be shared or overlap; outputs (codes, meta, gamma) must not
+ * overlap each other or any master (BL_EINVAL).  1 <= count <= 4096.
+ *
+ * Use: bitlinear_pack_group_plan sizes the table and workspace; bitlinear_pack_group_build writes
+ * the table (16-byte aligned device memory, caller-owned) for one workspace (256-byte aligned,
+ * caller-owned, contents on entry irrelevant) and synchronizes `stream`: build once, outside any
+ * graph capture; bitlinear_pack_group enqueues the two launches (asynchronous, stream-ordered,
+ * capturable).  The table keeps the descriptors' pointers; masters are read at launch time, so
+ * updated masters in the same buffers need no rebuild.  Launches sharing a workspace must be
+ * ordered on one stream.  A table of another N:M or layout is ignored (nothing is written).
+ */
+typedef struct bl_pack_desc {
+  const float* W;         /* [n][K] fp32 master */
+  int64_t n, K;
+  uint8_t* codes;         /* bitlinear_packed_bytes' codes_bytes */
+  uint8_t* meta;          /* meta_bytes (SPARSE) or NULL (DENSE2) */
+  float* gamma;           /* device scalar */
+} bl_pack_desc;
+
+typedef struct bl_pack_group_plan {
+  size_t table_bytes;     /* device table */
+  size_t ws_bytes;        /* device workspace */
+  int64_t count;          /* masters */
+  int64_t pack_blocks;    /* workgroups of the pack launch */
+  int32_t N, M, layout;
+  int32_t reserved;
+} bl_pack_group_plan;
+
+int bitlinear_pack_group_plan(const bl_pack_desc* descs, int64_t count, int N, int M, int layout,
+                              bl_pack_group_plan* plan);
+int bitlinear_pack_group_build(const bl_pack_desc* descs, int64_t count, int N, int M,
+                               int layout, void* ws, size_t ws_bytes, void* table,
+                               size_t table_bytes, void* stream);
+int bitlinear_pack_group(const void* table, const bl_pack_group_plan* plan, void* stream);
+
+/* ---------------------------------------------------------------------------------------------
  * Grouped decode forward: many independent bitlinear_fwd projections in one launch.
  *
  * The operation of each projection is exactly bitlinear_fwd's (same definitions, same packed

@@ -4,9 +4,10 @@ Names mirror the C ABI: ``bitlinear_packed_bytes``, ``bitlinear_pack``, ``act_qu
 ``bitlinear_fwd``, ``bitlinear_group_table_bytes``, ``bitlinear_group_build``,
 ``bitlinear_fwd_group``, ``bitlinear_group_fused_table_bytes``, ``bitlinear_group_fused_build``,
 ``bitlinear_fwd_group_fused``, ``bitlinear_bwd_workspace_bytes``, ``bitlinear_bwd``,
-``bitlinear_bwd_group_plan``, ``bitlinear_bwd_group_build``, ``bitlinear_bwd_group``.
-``pack`` / ``act_quant`` / ``fwd`` / ``FwdGroup`` / ``FusedGroup`` / ``bwd`` / ``BwdGroup`` are
-convenience
+``bitlinear_bwd_group_plan``, ``bitlinear_bwd_group_build``, ``bitlinear_bwd_group``,
+``bitlinear_pack_group_plan``, ``bitlinear_pack_group_build``, ``bitlinear_pack_group``.
+``pack`` / ``PackGroup`` / ``act_quant`` / ``fwd`` / ``FwdGroup`` / ``FusedGroup`` / ``bwd`` /
+``BwdGroup`` are convenience
 wrappers that allocate the output tensors with torch on the input's device and enqueue on torch's
 current stream.
 """
@@ -57,6 +58,20 @@ class BlBwdGroupPlan(ctypes.Structure):
                 ("reserved", ctypes.c_int32)]
 
 
+class BlPackDesc(ctypes.Structure):
+    """bl_pack_desc: the arguments of one bitlinear_pack call inside a grouped pack."""
+    _fields_ = [("W", ctypes.c_void_p), ("n", ctypes.c_int64), ("K", ctypes.c_int64),
+                ("codes", ctypes.c_void_p), ("meta", ctypes.c_void_p), ("gamma", ctypes.c_void_p)]
+
+
+class BlPackGroupPlan(ctypes.Structure):
+    """bl_pack_group_plan: table and workspace sizes and the pack launch's grid."""
+    _fields_ = [("table_bytes", ctypes.c_size_t), ("ws_bytes", ctypes.c_size_t),
+                ("count", ctypes.c_int64), ("pack_blocks", ctypes.c_int64),
+                ("N", ctypes.c_int32), ("M", ctypes.c_int32), ("layout", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
+
+
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libbitlinear.so")
 _lib = None
@@ -101,6 +116,11 @@ def lib() -> ctypes.CDLL:
         L.bitlinear_bwd_group_plan.argtypes = [bp, i64, i64, i32, i32, i32, pp]
         L.bitlinear_bwd_group_build.argtypes = [bp, i64, i64, i32, i32, i32, vp, sz, vp, sz, vp]
         L.bitlinear_bwd_group.argtypes = [vp, pp, vp]
+        kp = ctypes.POINTER(BlPackDesc)
+        kpp = ctypes.POINTER(BlPackGroupPlan)
+        L.bitlinear_pack_group_plan.argtypes = [kp, i64, i32, i32, i32, kpp]
+        L.bitlinear_pack_group_build.argtypes = [kp, i64, i32, i32, i32, vp, sz, vp, sz, vp]
+        L.bitlinear_pack_group.argtypes = [vp, kpp, vp]
         L.bitlinear_strerror.argtypes = [i32]
         L.bitlinear_strerror.restype = ctypes.c_char_p
         L.bitlinear_layout_version.argtypes = []
@@ -110,7 +130,9 @@ def lib() -> ctypes.CDLL:
                   L.bitlinear_bwd_workspace_bytes, L.bitlinear_bwd,
                   L.bitlinear_group_fused_table_bytes, L.bitlinear_group_fused_build,
                   L.bitlinear_fwd_group_fused, L.bitlinear_bwd_group_plan,
-                  L.bitlinear_bwd_group_build, L.bitlinear_bwd_group):
+                  L.bitlinear_bwd_group_build, L.bitlinear_bwd_group,
+                  L.bitlinear_pack_group_plan, L.bitlinear_pack_group_build,
+                  L.bitlinear_pack_group):
             f.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -190,6 +212,23 @@ def bitlinear_bwd(dy, T, n, xq, x_scale, K, codes, meta, gamma, N, M, layout, dx
                   ws_bytes, stream) -> int:
     return lib().bitlinear_bwd(dy, T, n, xq, x_scale, K, codes, meta, gamma, N, M, layout, dx, dw,
                                flags, ws, ws_bytes, stream)
+
+
+def bitlinear_pack_group_plan(descs, N, M, layout):
+    """Returns (status, BlPackGroupPlan)."""
+    plan = BlPackGroupPlan()
+    st = lib().bitlinear_pack_group_plan(descs, len(descs), N, M, layout, ctypes.byref(plan))
+    return st, plan
+
+
+def bitlinear_pack_group_build(descs, N, M, layout, ws, ws_bytes, table, table_bytes, stream) -> int:
+    return lib().bitlinear_pack_group_build(descs, len(descs), N, M, layout, ws, ws_bytes, table,
+                                            table_bytes, stream)
+
+
+def bitlinear_pack_group(table, plan, stream) -> int:
+    return lib().bitlinear_pack_group(table, ctypes.byref(plan) if plan is not None else None,
+                                      stream)
 
 
 def bitlinear_bwd_group_plan(descs, T, N, M, layout):
@@ -286,6 +325,52 @@ def fwd(xq, scale, K: int, codes, meta, gamma, n: int, N: int = 2, M: int = 4,
                          gamma.data_ptr(), N, M, layout, n, y.data_ptr(), _ptr(acc), _stream()),
            "bitlinear_fwd")
     return (y, acc) if want_acc else y
+
+
+class PackGroup:
+    """A built grouped pack: ``PackGroup(masters)`` then ``group()`` re-packs every master.
+
+    ``masters`` is a list of dicts with keys W (contiguous fp32 CUDA tensor [n][K]) and optionally
+    out = (codes, meta, gamma); outputs are allocated when not given and exposed as
+    ``group.outputs`` (a list of (codes, meta, gamma)).  Results equal ``pack`` per master, bit
+    for bit.  Tensors are referenced, not copied; the masters are read at each launch.
+    """
+
+    def __init__(self, masters, N: int = 2, M: int = 4, layout: int = BL_LAYOUT_SPARSE, ws=None):
+        import torch
+        self._keep = list(masters)
+        arr = (BlPackDesc * len(masters))()
+        self.outputs = []
+        for i, m in enumerate(masters):
+            W = m["W"]
+            assert W.is_cuda and W.dtype == torch.float32 and W.is_contiguous() and W.dim() == 2
+            n, K = W.shape
+            if m.get("out") is None:
+                cb, mb, _, _ = packed_bytes(n, K, N, M, layout)
+                out = (torch.empty(cb, dtype=torch.uint8, device=W.device),
+                       torch.empty(mb, dtype=torch.uint8, device=W.device) if mb else None,
+                       torch.empty(4, dtype=torch.float32, device=W.device)[:1])
+            else:
+                out = m["out"]
+            self.outputs.append(out)
+            arr[i] = BlPackDesc(W.data_ptr(), n, K, out[0].data_ptr(), _ptr(out[1]),
+                                out[2].data_ptr())
+        self.descs = arr
+        st, plan = bitlinear_pack_group_plan(arr, N, M, layout)
+        _check(st, "bitlinear_pack_group_plan")
+        self.plan = plan
+        dev = masters[0]["W"].device
+        self.table = torch.empty(max(plan.table_bytes, 16), dtype=torch.uint8, device=dev)
+        if ws is None:
+            ws = torch.empty(max(plan.ws_bytes, 256), dtype=torch.uint8, device=dev)
+        self.ws = ws
+        _check(bitlinear_pack_group_build(arr, N, M, layout, ws.data_ptr(), ws.numel(),
+                                          self.table.data_ptr(), self.table.numel(), _stream()),
+               "bitlinear_pack_group_build")
+
+    def __call__(self):
+        _check(bitlinear_pack_group(self.table.data_ptr(), self.plan, _stream()),
+               "bitlinear_pack_group")
 
 
 class FwdGroup:

@@ -12,6 +12,7 @@
 #include "bitlinear.h"
 #include "bwd_group.hpp"
 #include "launch.hpp"
+#include "pack_group.hpp"
 
 namespace {
 
@@ -435,6 +436,61 @@ int plan_bwd_group(const bl_bwd_desc* d, int64_t count, int64_t T, int N, int M,
   return BL_OK;
 }
 
+// Grouped pack: per-master workspace slices of kPackWsBytes rounded to 256 bytes.
+constexpr size_t kPackWsSlice = (bl::kPackWsBytes + 255) / 256 * 256;
+
+// Validates a grouped pack: every descriptor as bitlinear_pack; no output (codes, meta, gamma)
+// may overlap another output or any master.  Fills the items (ws offsets from `ws`) and returns
+// the pack launch's block count.
+int plan_pack_group(const bl_pack_desc* d, int64_t count, int N, int M, int layout, uint8_t* ws,
+                    std::vector<bl::PackGroupItem>* items, int64_t* pack_blocks) {
+  if (!d || count < 1 || count > 4096) return BL_EINVAL;
+  struct R { uintptr_t lo, hi; bool out; };
+  std::vector<R> rs;
+  items->assign((size_t)count, bl::PackGroupItem{});
+  for (int64_t i = 0; i < count; ++i) {
+    const bl_pack_desc& q = d[i];
+    int64_t ke = 0;
+    const int st = check_shape(q.n, q.K, N, M, layout, &ke);
+    if (st != BL_OK) return st;
+    if (!aligned16(q.W) || !aligned16(q.codes) || !aligned16(q.gamma)) return BL_EINVAL;
+    if (layout == BL_LAYOUT_SPARSE ? !aligned16(q.meta) : q.meta != nullptr) return BL_EINVAL;
+    size_t cb = 0, mb = 0;
+    bitlinear_packed_bytes(q.n, q.K, N, M, layout, &cb, &mb, nullptr, nullptr);
+    rs.push_back({(uintptr_t)q.W, (uintptr_t)q.W + (uint64_t)q.n * q.K * 4, false});
+    rs.push_back({(uintptr_t)q.codes, (uintptr_t)q.codes + cb, true});
+    if (mb) rs.push_back({(uintptr_t)q.meta, (uintptr_t)q.meta + mb, true});
+    rs.push_back({(uintptr_t)q.gamma, (uintptr_t)q.gamma + 4, true});
+    bl::PackGroupItem& it = (*items)[(size_t)i];
+    it.W = q.W;
+    it.codes = (uint32_t*)q.codes;
+    it.meta = (uint32_t*)q.meta;
+    it.gamma = q.gamma;
+    it.ws = ws + (size_t)i * kPackWsSlice;
+    it.n = (int32_t)q.n;
+    it.K = (int32_t)q.K;
+    it.k_tiles = (int32_t)((q.K + 255) / 256);
+  }
+  // any overlap involving an output is an error (masters may be shared or overlap each other)
+  std::sort(rs.begin(), rs.end(), [](const R& a, const R& b) { return a.lo < b.lo; });
+  uintptr_t out_hi = 0, any_hi = 0;
+  for (const R& r : rs) {
+    if (r.lo < out_hi || (r.out && r.lo < any_hi)) return BL_EINVAL;
+    any_hi = std::max(any_hi, r.hi);
+    if (r.out) out_hi = std::max(out_hi, r.hi);
+  }
+  // pack blocks in reverse descriptor order
+  int64_t blocks = 0;
+  for (int64_t i = count - 1; i >= 0; --i) {
+    bl::PackGroupItem& it = (*items)[(size_t)i];
+    it.block0 = (int32_t)blocks;
+    blocks += (int64_t)((it.n + 31) / 32) * it.k_tiles;
+    if (blocks > INT32_MAX) return BL_EINVAL;
+  }
+  *pack_blocks = blocks;
+  return BL_OK;
+}
+
 // A fused group's descriptors as plain ones (xq = the bf16 rows; x_scale is not read, the row
 // pointer stands in for the NULL check), after the checks that are the fused path's own: no
 // lifting (2:4 SPARSE or DENSE2) and bf16 rows addressable with 32-bit offsets.
@@ -502,6 +558,63 @@ int bitlinear_pack(const float* W, int64_t n, int64_t K, int N, int M, int layou
   if (ws_bytes < bl::kPackWsBytes) return BL_ENOSPC;
   return status_of(bl::launch_pack(W, n, K, N, M, layout, (uint32_t*)codes, (uint32_t*)meta, gamma,
                                    ws, (hipStream_t)stream));
+}
+
+int bitlinear_pack_group_plan(const bl_pack_desc* descs, int64_t count, int N, int M, int layout,
+                              bl_pack_group_plan* plan) {
+  if (!plan) return BL_EINVAL;
+  std::vector<bl::PackGroupItem> items;
+  int64_t blocks = 0;
+  const int st = plan_pack_group(descs, count, N, M, layout, nullptr, &items, &blocks);
+  if (st != BL_OK) return st;
+  memset(plan, 0, sizeof *plan);
+  plan->table_bytes = sizeof(bl::PackGroupHeader) + (size_t)count * sizeof(bl::PackGroupItem);
+  plan->ws_bytes = (size_t)count * kPackWsSlice;
+  plan->count = count;
+  plan->pack_blocks = blocks;
+  plan->N = N;
+  plan->M = M;
+  plan->layout = layout;
+  return BL_OK;
+}
+
+int bitlinear_pack_group_build(const bl_pack_desc* descs, int64_t count, int N, int M,
+                               int layout, void* ws, size_t ws_bytes, void* table,
+                               size_t table_bytes, void* stream) {
+  if (!ws || ((uintptr_t)ws & 255u) || !aligned16(table)) return BL_EINVAL;
+  std::vector<bl::PackGroupItem> items;
+  int64_t blocks = 0;
+  const int st = plan_pack_group(descs, count, N, M, layout, (uint8_t*)ws, &items, &blocks);
+  if (st != BL_OK) return st;
+  const size_t bytes = sizeof(bl::PackGroupHeader) + (size_t)count * sizeof(bl::PackGroupItem);
+  if (ws_bytes < (size_t)count * kPackWsSlice || table_bytes < bytes) return BL_ENOSPC;
+  std::vector<uint8_t> img(bytes, 0);
+  bl::PackGroupHeader hdr;
+  memset(&hdr, 0, sizeof hdr);
+  hdr.magic = bl::kPackGroupMagic;
+  hdr.layout = layout;
+  hdr.N = N;
+  hdr.M = M;
+  hdr.count = (int32_t)count;
+  hdr.pack_blocks = (int32_t)blocks;
+  memcpy(img.data(), &hdr, sizeof hdr);
+  memcpy(img.data() + sizeof hdr, items.data(), items.size() * sizeof(bl::PackGroupItem));
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = hipMemcpyAsync(table, img.data(), bytes, hipMemcpyHostToDevice, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);  // img is released on return
+  return status_of(e);
+}
+
+int bitlinear_pack_group(const void* table, const bl_pack_group_plan* plan, void* stream) {
+  if (!plan || !aligned16(table)) return BL_EINVAL;
+  int64_t ke = 0;
+  const int st = check_shape(1, 256, plan->N, plan->M, plan->layout, &ke);
+  if (st != BL_OK) return st;
+  if (plan->count < 1 || plan->count > 4096 || plan->pack_blocks < 1 ||
+      plan->pack_blocks > INT32_MAX)
+    return BL_EINVAL;
+  return status_of(bl::launch_pack_group(table, plan->count, plan->pack_blocks, plan->layout,
+                                         plan->M, (hipStream_t)stream));
 }
 
 int act_quant_i8(const void* x, int x_dtype, int64_t T, int64_t K, int lift_M, int8_t* xq,

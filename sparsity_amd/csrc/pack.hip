@@ -18,6 +18,7 @@
 //                             coalesced dword stores.
 #include "device_common.hpp"
 #include "launch.hpp"
+#include "pack_group.hpp"
 
 namespace bl {
 
@@ -27,15 +28,14 @@ struct PackWs {
 };
 static_assert(sizeof(PackWs) <= kPackWsBytes, "pack workspace");
 
-__global__ __launch_bounds__(kGammaThreads) void gamma_partial_kernel(const float4* __restrict__ W4,
-                                                                      int64_t n4,
-                                                                      double* __restrict__ partial) {
+__device__ __forceinline__ void gamma_partial_block(const float4* __restrict__ W4, int64_t n4,
+                                                    double* __restrict__ partial, int blk) {
   // Four independent fp64 chains per thread keep four 16-byte loads in flight.  Every |w| still
   // passes through at most 4 * ceil(n4 / threads) + 2 additions before the wave sum, inside the
   // depth the finalize step assumes for its error bound.
   const int64_t stride = (int64_t)kGammaBlocks * kGammaThreads;
   double a0 = 0.0, a1 = 0.0, a2 = 0.0, a3 = 0.0;
-  int64_t i = (int64_t)blockIdx.x * kGammaThreads + threadIdx.x;
+  int64_t i = (int64_t)blk * kGammaThreads + threadIdx.x;
   for (; i + 3 * stride < n4; i += 4 * stride) {
     const float4 v0 = W4[i], v1 = W4[i + stride], v2 = W4[i + 2 * stride], v3 = W4[i + 3 * stride];
     a0 += fabs((double)v0.x); a0 += fabs((double)v0.y); a0 += fabs((double)v0.z); a0 += fabs((double)v0.w);
@@ -55,8 +55,14 @@ __global__ __launch_bounds__(kGammaThreads) void gamma_partial_kernel(const floa
   if (threadIdx.x == 0) {
     double s = 0.0;
     for (int w = 0; w < kGammaThreads / 64; ++w) s += red[w];
-    partial[blockIdx.x] = s;
+    partial[blk] = s;
   }
+}
+
+__global__ __launch_bounds__(kGammaThreads) void gamma_partial_kernel(const float4* __restrict__ W4,
+                                                                      int64_t n4,
+                                                                      double* __restrict__ partial) {
+  gamma_partial_block(W4, n4, partial, blockIdx.x);
 }
 
 // Round (sum_e bins[e] * 2^(max(e,1)-150)) / count to the nearest fp32, ties to even, exactly.
@@ -196,11 +202,11 @@ constexpr int kPackKB = 256;  // dense K columns per pack tile
 // phase 3 assembles 16-slot units into code/meta dwords, which land contiguously in the tiled
 // layout (unit v = 32*u + r of the tile is dword base + v).
 template <int LAYOUT, int M>
-__global__ __launch_bounds__(256) void pack_kernel(const float* __restrict__ W, int n, int K, int N,
-                                                   int k_tiles, PackWs* __restrict__ ws,
-                                                   float* __restrict__ gamma_out,
-                                                   uint32_t* __restrict__ codes,
-                                                   uint32_t* __restrict__ meta) {
+__device__ __forceinline__ void pack_tile(const float* __restrict__ W, int n, int K, int N,
+                                          int k_tiles, PackWs* __restrict__ ws,
+                                          float* __restrict__ gamma_out,
+                                          uint32_t* __restrict__ codes,
+                                          uint32_t* __restrict__ meta, int blk) {
   constexpr bool SP = LAYOUT == kLayoutSparse;
   constexpr int WS = kPackKB + 4;                                      // padded fp32 row
   constexpr int NKEEP = M == 4 ? 2 : M - 2;                           // SPARSE: 2:4, 6:8, 14:16
@@ -215,8 +221,8 @@ __global__ __launch_bounds__(256) void pack_kernel(const float* __restrict__ W, 
   __shared__ float g_sh, tau_sh;
   __shared__ int exact_sh;
 
-  const int P = blockIdx.x / k_tiles;
-  const int kb = blockIdx.x % k_tiles;
+  const int P = blk / k_tiles;
+  const int kb = blk % k_tiles;
   const int k0 = kb * kPackKB;
   const int r0 = P * kPanel;
   const int kw = min(kPackKB, K - k0);
@@ -247,7 +253,7 @@ __global__ __launch_bounds__(256) void pack_kernel(const float* __restrict__ W, 
       *(float4*)&tile[row * WS + 4 * c4] = v[i];
     }
   }
-  if (blockIdx.x == 0 && threadIdx.x == 0) {
+  if (blk == 0 && threadIdx.x == 0) {
     gamma_out[0] = g_sh;
     ws->exact_used = (uint32_t)exact_sh;
   }
@@ -327,6 +333,50 @@ __global__ __launch_bounds__(256) void pack_kernel(const float* __restrict__ W, 
   }
 }
 
+template <int LAYOUT, int M>
+__global__ __launch_bounds__(256) void pack_kernel(const float* __restrict__ W, int n, int K, int N,
+                                                   int k_tiles, PackWs* __restrict__ ws,
+                                                   float* __restrict__ gamma_out,
+                                                   uint32_t* __restrict__ codes,
+                                                   uint32_t* __restrict__ meta) {
+  pack_tile<LAYOUT, M>(W, n, K, N, k_tiles, ws, gamma_out, codes, meta, blockIdx.x);
+}
+
+// ---------------------------------------------------------------------------------------------
+// Grouped pack: the bitlinear_pack calls of several masters in two launches, each tensor's blocks
+// running exactly the single call's arithmetic (so gamma, codes and meta are the same bits).
+// The partial-sum launch walks the tensors in table order and the pack launch in reverse, so
+// the tensors read last by the first launch -- still in the last-level cache -- are packed first.
+// ---------------------------------------------------------------------------------------------
+__global__ __launch_bounds__(kGammaThreads) void gamma_partial_group_kernel(
+    const uint8_t* __restrict__ table) {
+  const PackGroupHeader* hd = (const PackGroupHeader*)table;
+  if (hd->magic != kPackGroupMagic) return;
+  const int b = blockIdx.x;
+  if (b >= hd->count * kGammaBlocks) return;
+  const PackGroupItem it = ((const PackGroupItem*)(table + sizeof(PackGroupHeader)))[b / kGammaBlocks];
+  gamma_partial_block((const float4*)it.W, (int64_t)it.n * it.K / 4, ((PackWs*)it.ws)->partial,
+                      b % kGammaBlocks);
+}
+
+template <int LAYOUT, int M>
+__global__ __launch_bounds__(256) void pack_group_kernel(const uint8_t* __restrict__ table) {
+  const PackGroupHeader* hd = (const PackGroupHeader*)table;
+  if (hd->magic != kPackGroupMagic || hd->layout != LAYOUT || hd->M != M) return;
+  const int b = blockIdx.x;
+  if (b >= hd->pack_blocks) return;
+  const PackGroupItem* items = (const PackGroupItem*)(table + sizeof(PackGroupHeader));
+  // items[count - 1] owns the first blocks: find the last r with items[count - 1 - r].block0 <= b
+  int lo = 0, hi = hd->count - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (items[hd->count - 1 - mid].block0 <= b) lo = mid; else hi = mid - 1;
+  }
+  const PackGroupItem it = items[hd->count - 1 - lo];
+  pack_tile<LAYOUT, M>(it.W, it.n, it.K, hd->N, it.k_tiles, (PackWs*)it.ws, it.gamma, it.codes,
+                       it.meta, b - it.block0);
+}
+
 hipError_t launch_pack(const float* W, int64_t n, int64_t K, int N, int M, int layout,
                        uint32_t* codes, uint32_t* meta, float* gamma, void* ws_raw, hipStream_t s) {
   PackWs* ws = (PackWs*)ws_raw;
@@ -346,6 +396,25 @@ hipError_t launch_pack(const float* W, int64_t n, int64_t K, int N, int M, int l
     if (M == 4) run(pack_kernel<kLayoutDense2, 4>, nullptr);
     else if (M == 8) run(pack_kernel<kLayoutDense2, 8>, nullptr);
     else run(pack_kernel<kLayoutDense2, 16>, nullptr);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_pack_group(const void* table, int64_t count, int64_t pack_blocks, int layout,
+                             int M, hipStream_t s) {
+  const uint8_t* t = (const uint8_t*)table;
+  gamma_partial_group_kernel<<<(unsigned)(count * kGammaBlocks), kGammaThreads, 0, s>>>(t);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const unsigned g = (unsigned)pack_blocks;
+  if (layout == kLayoutSparse) {
+    if (M == 4) pack_group_kernel<kLayoutSparse, 4><<<g, 256, 0, s>>>(t);
+    else if (M == 8) pack_group_kernel<kLayoutSparse, 8><<<g, 256, 0, s>>>(t);
+    else pack_group_kernel<kLayoutSparse, 16><<<g, 256, 0, s>>>(t);
+  } else {
+    if (M == 4) pack_group_kernel<kLayoutDense2, 4><<<g, 256, 0, s>>>(t);
+    else if (M == 8) pack_group_kernel<kLayoutDense2, 8><<<g, 256, 0, s>>>(t);
+    else pack_group_kernel<kLayoutDense2, 16><<<g, 256, 0, s>>>(t);
   }
   return hipGetLastError();
 }

@@ -335,6 +335,62 @@ def test_bwd_group_rejects_before_launch(L):
     assert L.bitlinear_bwd_group(TB, bad, None) == -22
 
 
+def _pdesc(L, slot, **kw):
+    base = FAKE + slot * 16 * GB
+    a = dict(W=base, n=128, K=256, codes=base + GB, meta=base + 2 * GB, gamma=base + 3 * GB)
+    a.update(kw)
+    return L.BlPackDesc(**a)
+
+
+def _pplan(L, descs, N=2, M=4, layout=0):
+    return L.bitlinear_pack_group_plan((L.BlPackDesc * len(descs))(*descs), N, M, layout)
+
+
+def test_pack_group_plan_and_rejects_before_launch(L):
+    """Tiles of 32 rows x 256 columns per master, dealt in reverse master order; one workspace
+    slice per master; the single call's shape and alignment rules; no output overlaps."""
+    a, b = _pdesc(L, 0, n=300, K=640), _pdesc(L, 1, n=64, K=256)
+    st, plan = _pplan(L, [a, b])
+    assert st == 0
+    assert plan.count == 2 and plan.pack_blocks == 10 * 3 + 2 * 1
+    assert plan.table_bytes == 64 + 2 * 64
+    ws1 = L.bitlinear_packed_bytes(300, 640, 2, 4, 0)[4]
+    assert plan.ws_bytes == 2 * ((ws1 + 255) // 256 * 256)
+    assert _pplan(L, [_pdesc(L, 0, K=100)])[0] == -22
+    assert _pplan(L, [a], N=3)[0] == -95
+    assert _pplan(L, [_pdesc(L, 0, W=FAKE + 4)])[0] == -22
+    assert _pplan(L, [_pdesc(L, 0, gamma=FAKE + 3 * GB + 4)])[0] == -22
+    assert _pplan(L, [_pdesc(L, 0, meta=None)])[0] == -22
+    assert _pplan(L, [_pdesc(L, 0, meta=FAKE + 2 * GB)], layout=1)[0] == -22
+    assert _pplan(L, [_pdesc(L, 0, meta=None)], layout=1)[0] == 0
+    lib = L.lib()
+    assert lib.bitlinear_pack_group_plan(None, 1, 2, 4, 0, ctypes.byref(L.BlPackGroupPlan())) == -22
+    assert lib.bitlinear_pack_group_plan((L.BlPackDesc * 1)(a), 0, 2, 4, 0,
+                                         ctypes.byref(L.BlPackGroupPlan())) == -22
+    # masters may be shared; outputs may not overlap each other or a master
+    assert _pplan(L, [a, _pdesc(L, 1, W=a.W)])[0] == 0
+    assert _pplan(L, [a, _pdesc(L, 1, codes=a.codes)])[0] == -22
+    assert _pplan(L, [a, _pdesc(L, 1, gamma=a.codes + 16)])[0] == -22
+    assert _pplan(L, [a, _pdesc(L, 1, meta=a.W + 4096)])[0] == -22
+    assert _pplan(L, [_pdesc(L, 0, codes=FAKE + 1024)])[0] == -22   # own output inside own W
+    # build and launch argument checks (nothing is copied or launched)
+    arr = (L.BlPackDesc * 2)(a, b)
+    W, TB = FAKE + 64 * 16 * GB, FAKE + 80 * 16 * GB
+    assert L.bitlinear_pack_group_build(arr, 2, 4, 0, W, plan.ws_bytes - 1, TB, plan.table_bytes,
+                                        None) == -28
+    assert L.bitlinear_pack_group_build(arr, 2, 4, 0, W, plan.ws_bytes, TB, plan.table_bytes - 16,
+                                        None) == -28
+    assert L.bitlinear_pack_group_build(arr, 2, 4, 0, W + 16, plan.ws_bytes, TB, plan.table_bytes,
+                                        None) == -22
+    assert L.bitlinear_pack_group(TB, None, None) == -22
+    bad = L.BlPackGroupPlan.from_buffer_copy(plan)
+    bad.N = 3
+    assert L.bitlinear_pack_group(TB, bad, None) == -95
+    bad = L.BlPackGroupPlan.from_buffer_copy(plan)
+    bad.pack_blocks = 0
+    assert L.bitlinear_pack_group(TB, bad, None) == -22
+
+
 def _xdesc(L, **kw):
     P = FAKE
     a = dict(x=P, T=4, K=256, codes=P, meta=P, gamma=P, n=100, y=P, acc_opt=None)
