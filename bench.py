@@ -220,9 +220,10 @@ def decode_fused_leg(S, torch, D, ref, steps, warmup):
 
 def decode_mall_leg(S, torch, D, pairs=24, launches=100):
     """The decode layer stream shrunk to fit the 256 MB last-level cache: the first `pairs` up/down
-    pairs (212 MB of packed weights for 24: enough work items to fill the chip) in one grouped
-    launch at T = 1, repeated back to back, so every launch after the first can read its weights
-    from the cache rather than HBM."""
+    pairs (212 MB of packed weights for 24) in one grouped launch at T = 1, repeated back to back.
+    The kernel's weight loads are non-temporal (each byte is read once per launch), so the cache
+    is not kept warm between launches: this reading shows what a cache-sized stream gets with
+    them (456 work items for 512 block slots)."""
     xq, sc = D.q[(1, UP[1])]
     xd, sd = D.q[(1, DOWN[1])]
     projs = []
@@ -243,9 +244,10 @@ def decode_mall_leg(S, torch, D, pairs=24, launches=100):
     t = e0.elapsed_time(e1) * 1e-3 / launches
     wbytes = sum(c.numel() + m.numel() for (_, _, c, m, _) in D.mats[:2 * pairs])
     return {"workload": f"first {pairs} up/down pairs of the decode stream, T = 1, one grouped launch "
-                        f"repeated {launches} times back to back (weights resident in the last-level "
-                        "cache)",
-            "label": "MALL-resident", "packed_weight_bytes": wbytes,
+                        f"repeated {launches} times back to back (weights sized to fit the "
+                        "last-level cache)",
+            "label": "MALL-sized (non-temporal weight loads: not kept resident)",
+            "packed_weight_bytes": wbytes,
             "launch_us": round(t * 1e6, 2), "weight_GBps": round(wbytes / t / 1e9, 1)}
 
 
@@ -301,6 +303,68 @@ def decode_dense_leg(S, torch, D, steps, warmup):
             "ms_per_step": round(ms, 4), "packed_bytes_per_pass": packed,
             "weight_GBps": round(packed * len(DECODE_T) / (ms * 1e-3) / 1e9, 1),
             "dense_weights_per_s": float(f"{dense_weights * len(DECODE_T) / (ms * 1e-3):.4g}"),
+            "vs_sparse_2of4_step": round(ms / D.last_ms_per_step, 3) if D.last_ms_per_step else None}
+
+
+def decode_hybrid_leg(S, torch, D, steps, warmup, dense_frac=0.25):
+    """Comparator in the manner of Spense's hybrid format: each projection keeps a quarter of its
+    output rows dense (4:4 dense 2-bit codes) and the rest 2:4, as two grouped launches per T (one
+    per layout) over the same activations.  Both regions move 0.25 B per dense weight."""
+    g = torch.Generator(device="cuda")
+    g.manual_seed(1000)                              # the decode masters, drawn in the same order
+    sp, dn = [], []
+    for i in range(N_PAIRS):
+        for (n, K) in (UP, DOWN):
+            W = (torch.randn((n, K), generator=g, device="cuda", dtype=torch.float32) * 0.02)
+            r = int(round(n * dense_frac / 32)) * 32
+            c, _, ga = S.pack(W[:r].contiguous(), 4, 4, S.BL_LAYOUT_DENSE2)
+            dn.append((i, r, K, c, None, ga))
+            c, m, ga = S.pack(W[r:].contiguous(), 2, 4)
+            sp.append((i, n - r, K, c, m, ga))
+            del W
+    packed = sum(c.numel() + (m.numel() if m is not None else 0)
+                 for part in (sp, dn) for (_, _, _, c, m, _) in part)
+    groups = {}
+    for T in DECODE_T:
+        per_layout = []
+        for part, (N, M, layout) in ((sp, (2, 4, S.BL_LAYOUT_SPARSE)),
+                                     (dn, (4, 4, S.BL_LAYOUT_DENSE2))):
+            projs = []
+            for (i, n, K, c, m, ga) in part:
+                xq, sc = D.q[(T, K)]
+                j = i // 2
+                projs.append(dict(xq=xq[j * T:(j + 1) * T], scale=sc[j * T:(j + 1) * T], K=K,
+                                  codes=c, meta=m, gamma=ga, n=n,
+                                  y=torch.empty((T, n), dtype=torch.float32, device="cuda")))
+            per_layout.append(S.FwdGroup(projs, N, M, layout))
+        groups[T] = per_layout
+
+    def step():
+        for T in DECODE_T:
+            for K in (UP[1], DOWN[1]):
+                S.act_quant(D.x[(T, K)], out=D.q[(T, K)])
+            for grp in groups[T]:
+                grp()
+
+    step()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    with torch.cuda.graph(graph, stream=cap):
+        step()
+    for _ in range(warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        graph.replay()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    return {"workload": "the decode stream (64 up/down pairs, T = 1, 4, 16) with the first quarter "
+                        "of every projection's output rows dense ternary (4:4 dense 2-bit codes) "
+                        "and the rest 2:4: two grouped launches per T",
+            "ms_per_step": round(ms, 4), "packed_bytes_per_pass": packed,
+            "weight_GBps": round(packed * len(DECODE_T) / (ms * 1e-3) / 1e9, 1),
             "vs_sparse_2of4_step": round(ms / D.last_ms_per_step, 3) if D.last_ms_per_step else None}
 
 
@@ -786,12 +850,15 @@ def main():
     out["decode_fused"] = decode_fused_leg(S, torch, D, ref, args.steps, args.warmup)
     log(f"fused decode {out['decode_fused']['value']} GB/s")
     if not args.no_extra:
-        log("MALL-resident decode reading")
-        out["decode_mall_resident"] = decode_mall_leg(S, torch, D)
-        log(f"MALL-resident decode {out['decode_mall_resident']['weight_GBps']} GB/s")
+        log("MALL-sized decode reading")
+        out["decode_mall_sized"] = decode_mall_leg(S, torch, D)
+        log(f"MALL-sized decode {out['decode_mall_sized']['weight_GBps']} GB/s")
         log("dense ternary decode comparator")
         out["decode_dense_ternary"] = decode_dense_leg(S, torch, D, args.steps, args.warmup)
         log(f"dense ternary decode {out['decode_dense_ternary']['ms_per_step']} ms/step")
+        log("hybrid dense + 2:4 decode comparator")
+        out["decode_hybrid"] = decode_hybrid_leg(S, torch, D, args.steps, args.warmup)
+        log(f"hybrid decode {out['decode_hybrid']['ms_per_step']} ms/step")
     if not args.no_prefill:
         log("prefill leg")
         out["prefill"] = prefill_leg(S, torch)
