@@ -144,8 +144,11 @@ struct GroupGemv {
   }
 };
 
+// At most 128 VGPRs (four waves per SIMD: two blocks per CU).  The fused variant needs a few more
+// for its bf16 pieces and spills them outside the main loop only.
 template <int LAYOUT, bool FUSED>
-__global__ __launch_bounds__(64 * kGroupWaves, 2) void gemv_group_kernel(
+__global__ __launch_bounds__(64 * kGroupWaves) __attribute__((amdgpu_waves_per_eu(4)))
+void gemv_group_kernel(
     const uint8_t* __restrict__ table) {
   typedef GroupGemv<LAYOUT, FUSED> G;
   __shared__ __attribute__((aligned(16))) int8_t bs[2 * 32 * G::ROW];
