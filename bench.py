@@ -492,10 +492,10 @@ TRAIN_LAYERS = (("q", 3200, 3200), ("k", 3200, 3200), ("v", 3200, 3200), ("o", 3
 
 def train_step_leg(S, torch, iters=3):
     """3B-alike decoder layer set at 8192 tokens: re-mask + ternarize + pack all 7 fp32 masters
-    (one grouped pack), quantize the two activation matrices once, the 7 2:4 forwards, then the
-    grouped backward of all 7.  Each phase is one HIP graph (checked against the eager run of the
-    separate calls) timed with events around its replays; the separate pack and backward calls
-    are timed beside the grouped ones."""
+    (one grouped pack), quantize the two activation matrices once, the 7 2:4 forwards (one grouped
+    prefill launch), then the grouped backward of all 7.  Each phase is one HIP graph (checked
+    against the eager run of the separate calls) timed with events around its replays; the
+    separate pack, forward and backward calls are timed beside the grouped ones."""
     T = 8192
     g = torch.Generator(device="cuda")
     g.manual_seed(35)
@@ -532,10 +532,17 @@ def train_step_leg(S, torch, iters=3):
         for K in X:
             S.act_quant(X[K], out=Q[K])
 
-    def fwd_all():
+    def fwd_seq():
         for (_, n, K), (c, m, ga), y in zip(TRAIN_LAYERS, packed, ys):
             xq, sc = Q[K]
             S.fwd(xq, sc, K, c, m, ga, n, out=(y, None))
+
+    # the same seven forwards as one grouped prefill launch
+    fgroup = S.GemmGroup([dict(xq=Q[K][0], scale=Q[K][1], K=K, codes=c, meta=m, gamma=ga, n=n, y=y)
+                          for (_, n, K), (c, m, ga), y in zip(TRAIN_LAYERS, packed, ys)])
+
+    def fwd_all():
+        fgroup()
 
     def bwd_seq():
         seen = set()
@@ -567,7 +574,7 @@ def train_step_leg(S, torch, iters=3):
 
     pack_seq()
     quant_all()
-    fwd_all()
+    fwd_seq()
     bwd_seq()
     torch.cuda.synchronize()
     ref = outputs()
@@ -580,10 +587,10 @@ def train_step_leg(S, torch, iters=3):
     torch.cuda.synchronize()
     for a, b in zip(outputs(), ref):
         if not torch.equal(a, b):
-            raise RuntimeError("grouped pack or backward differs from the sequential calls")
+            raise RuntimeError("grouped pack, forward or backward differs from the sequential calls")
     graphs = []
     cap = torch.cuda.Stream()
-    for fn in (pack_seq, pack_all, quant_all, fwd_all, bwd_seq, bwd_all):
+    for fn in (pack_seq, pack_all, quant_all, fwd_seq, fwd_all, bwd_seq, bwd_all):
         gr = torch.cuda.CUDAGraph()
         with torch.cuda.graph(gr, stream=cap):
             fn()
@@ -600,9 +607,10 @@ def train_step_leg(S, torch, iters=3):
     t_pack_seq = _event_ms(torch, graphs[0].replay, iters)
     t_pack = _event_ms(torch, graphs[1].replay, iters)
     t_quant = _event_ms(torch, graphs[2].replay, iters)
-    t_fwd = _event_ms(torch, graphs[3].replay, iters)
-    t_bwd_seq = _event_ms(torch, graphs[4].replay, iters)
-    t_bwd = _event_ms(torch, graphs[5].replay, iters)
+    t_fwd_seq = _event_ms(torch, graphs[3].replay, iters)
+    t_fwd = _event_ms(torch, graphs[4].replay, iters)
+    t_bwd_seq = _event_ms(torch, graphs[5].replay, iters)
+    t_bwd = _event_ms(torch, graphs[6].replay, iters)
     pack_bytes = sum(4 * n * K + p[0].numel() + p[1].numel() for (_, n, K), p in zip(TRAIN_LAYERS, packed))
     # act_quant: bf16 read + int8 write per element + 4 B scale per token
     quant_bytes = sum(T * K * 3 + 4 * T for K in X)
@@ -623,6 +631,8 @@ def train_step_leg(S, torch, iters=3):
             "pack_sequential_ms": round(t_pack_seq, 4),
             "act_quant_ms": round(t_quant, 4), "act_quant_GBps": round(quant_gbs, 1),
             "fwd_ms": round(t_fwd, 4), "fwd_TOPS": round(fwd_tops, 1),
+            # the seven bitlinear_fwd calls one after another (same results, bit for bit)
+            "fwd_sequential_ms": round(t_fwd_seq, 4),
             # algorithmic bytes (pack: 4 B read + packed bytes written per weight, one pass over
             # the master; act_quant: 3 B per element + 4 B per token) or dense-equivalent ops
             "roofline": {"pack": {"bound": "hbm", "achieved": round(pack_gbs, 1), "peak": HBM_PEAK_GBS,

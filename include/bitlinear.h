@@ -189,7 +189,7 @@ int bitlinear_pack_group(const void* table, const bl_pack_group_plan* plan, void
 typedef struct bl_fwd_desc {
   const int8_t* xq;      /* [T][K_eff] int8 activations */
   const float* x_scale;  /* [T] fp32 token scales */
-  int64_t T;             /* tokens, 0..32 */
+  int64_t T;             /* tokens: 0..32 (decode group), > 128 (prefill group) */
   int64_t K;             /* master in-features */
   const uint8_t* codes;  /* packed codes from bitlinear_pack */
   const uint8_t* meta;   /* packed meta (SPARSE) or NULL (DENSE2) */
@@ -248,6 +248,40 @@ int bitlinear_group_fused_build(const bl_fwd_x_desc* descs, int64_t count, int N
                                 int layout, void* table, size_t table_bytes, void* stream);
 int bitlinear_fwd_group_fused(const void* table, int64_t work_items, int N, int M, int layout,
                               void* stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * Grouped prefill forward: the bitlinear_fwd calls of a layer set with prefill-sized T in one
+ * launch.
+ *
+ * Same operation and descriptors as the grouped decode forward (bl_fwd_desc; BitNet b1.58 page,
+ * "The mechanism"), but for 128 < T per projection: y (and acc_opt) are those of bitlinear_fwd
+ * for each descriptor, bit for bit.  Every 256-row x 128-token output tile of every projection
+ * is one workgroup of the launch, dealt to the XCDs longest first, so the separate launches'
+ * partial last waves become one.  All projections share (N, M, layout); each follows
+ * bitlinear_fwd's shape and alignment rules with T > 128 (BL_EINVAL otherwise).  Inputs (xq,
+ * x_scale, codes, meta, gamma) may be shared or overlap; outputs (y, acc_opt) may overlap
+ * nothing (BL_EINVAL).  1 <= count <= 4096.
+ *
+ * Use: bitlinear_gemm_group_plan validates the group and sizes the table (enqueues nothing);
+ * bitlinear_gemm_group_build writes it (table: 16-byte aligned device memory of at least
+ * table_bytes, caller-owned; copies on `stream` and waits for it, BL_ENOSPC if too small): build
+ * once, outside any graph capture; bitlinear_gemm_group enqueues the launch (asynchronous,
+ * stream-ordered, capturable).  The table keeps the descriptors' pointers, and their contents are
+ * read at launch time: new activations in the same buffers need no rebuild.  A table of another
+ * layout is ignored (nothing is written).
+ */
+typedef struct bl_gemm_group_plan {
+  size_t table_bytes;     /* device table */
+  int64_t jobs;           /* workgroups of the launch */
+  int32_t N, M, layout;   /* the group's packing */
+  int32_t reserved;
+} bl_gemm_group_plan;
+
+int bitlinear_gemm_group_plan(const bl_fwd_desc* descs, int64_t count, int N, int M, int layout,
+                              bl_gemm_group_plan* plan);
+int bitlinear_gemm_group_build(const bl_fwd_desc* descs, int64_t count, int N, int M, int layout,
+                               void* table, size_t table_bytes, void* stream);
+int bitlinear_gemm_group(const void* table, const bl_gemm_group_plan* plan, void* stream);
 
 /* ---------------------------------------------------------------------------------------------
  * Backward for training (Sparse-BitNet technical summary, Training Strategie: Dual STE).

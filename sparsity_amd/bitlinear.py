@@ -72,6 +72,13 @@ class BlPackGroupPlan(ctypes.Structure):
                 ("reserved", ctypes.c_int32)]
 
 
+class BlGemmGroupPlan(ctypes.Structure):
+    """bl_gemm_group_plan: table size and the grid of a grouped prefill forward."""
+    _fields_ = [("table_bytes", ctypes.c_size_t), ("jobs", ctypes.c_int64),
+                ("N", ctypes.c_int32), ("M", ctypes.c_int32), ("layout", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
+
+
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libbitlinear.so")
 _lib = None
@@ -121,6 +128,10 @@ def lib() -> ctypes.CDLL:
         L.bitlinear_pack_group_plan.argtypes = [kp, i64, i32, i32, i32, kpp]
         L.bitlinear_pack_group_build.argtypes = [kp, i64, i32, i32, i32, vp, sz, vp, sz, vp]
         L.bitlinear_pack_group.argtypes = [vp, kpp, vp]
+        gp = ctypes.POINTER(BlGemmGroupPlan)
+        L.bitlinear_gemm_group_plan.argtypes = [dp, i64, i32, i32, i32, gp]
+        L.bitlinear_gemm_group_build.argtypes = [dp, i64, i32, i32, i32, vp, sz, vp]
+        L.bitlinear_gemm_group.argtypes = [vp, gp, vp]
         L.bitlinear_strerror.argtypes = [i32]
         L.bitlinear_strerror.restype = ctypes.c_char_p
         L.bitlinear_layout_version.argtypes = []
@@ -132,7 +143,8 @@ def lib() -> ctypes.CDLL:
                   L.bitlinear_fwd_group_fused, L.bitlinear_bwd_group_plan,
                   L.bitlinear_bwd_group_build, L.bitlinear_bwd_group,
                   L.bitlinear_pack_group_plan, L.bitlinear_pack_group_build,
-                  L.bitlinear_pack_group):
+                  L.bitlinear_pack_group, L.bitlinear_gemm_group_plan,
+                  L.bitlinear_gemm_group_build, L.bitlinear_gemm_group):
             f.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -247,6 +259,23 @@ def bitlinear_bwd_group_build(descs, T, N, M, layout, ws, ws_bytes, table, table
 def bitlinear_bwd_group(table, plan, stream) -> int:
     return lib().bitlinear_bwd_group(table, ctypes.byref(plan) if plan is not None else None,
                                      stream)
+
+
+def bitlinear_gemm_group_plan(descs, N, M, layout):
+    """Returns (status, BlGemmGroupPlan)."""
+    plan = BlGemmGroupPlan()
+    st = lib().bitlinear_gemm_group_plan(descs, len(descs), N, M, layout, ctypes.byref(plan))
+    return st, plan
+
+
+def bitlinear_gemm_group_build(descs, N, M, layout, table, table_bytes, stream) -> int:
+    return lib().bitlinear_gemm_group_build(descs, len(descs), N, M, layout, table, table_bytes,
+                                            stream)
+
+
+def bitlinear_gemm_group(table, plan, stream) -> int:
+    return lib().bitlinear_gemm_group(table, ctypes.byref(plan) if plan is not None else None,
+                                      stream)
 
 
 # ---------------------------------------------------------------------------------------------
@@ -402,6 +431,36 @@ class FwdGroup:
     def __call__(self):
         _check(bitlinear_fwd_group(self.table.data_ptr(), self.work_items, self.N, self.M,
                                    self.layout, _stream()), "bitlinear_fwd_group")
+
+
+class GemmGroup:
+    """A built grouped prefill forward: ``GemmGroup(projs)`` then ``group()`` launches.
+
+    ``projs`` as for FwdGroup (T > 128 tokens each).  y (and acc) equal ``fwd`` per projection,
+    bit for bit.  The tensors are referenced, not copied; their contents are read at each launch.
+    """
+
+    def __init__(self, projs, N: int = 2, M: int = 4, layout: int = BL_LAYOUT_SPARSE):
+        import torch
+        self._keep = list(projs)
+        arr = (BlFwdDesc * len(projs))()
+        for i, p in enumerate(projs):
+            arr[i] = BlFwdDesc(_ptr(p["xq"]), _ptr(p["scale"]), p["xq"].shape[0], p["K"],
+                               _ptr(p["codes"]), _ptr(p.get("meta")), _ptr(p["gamma"]), p["n"],
+                               _ptr(p["y"]), _ptr(p.get("acc")))
+        self.descs = arr
+        st, plan = bitlinear_gemm_group_plan(arr, N, M, layout)
+        _check(st, "bitlinear_gemm_group_plan")
+        self.plan = plan
+        dev = projs[0]["codes"].device
+        self.table = torch.empty(max(plan.table_bytes, 16), dtype=torch.uint8, device=dev)
+        _check(bitlinear_gemm_group_build(arr, N, M, layout, self.table.data_ptr(),
+                                          self.table.numel(), _stream()),
+               "bitlinear_gemm_group_build")
+
+    def __call__(self):
+        _check(bitlinear_gemm_group(self.table.data_ptr(), self.plan, _stream()),
+               "bitlinear_gemm_group")
 
 
 class FusedGroup:

@@ -11,6 +11,7 @@
 
 #include "bitlinear.h"
 #include "bwd_group.hpp"
+#include "gemm_group.hpp"
 #include "launch.hpp"
 #include "pack_group.hpp"
 
@@ -491,6 +492,87 @@ int plan_pack_group(const bl_pack_desc* d, int64_t count, int N, int M, int layo
   return BL_OK;
 }
 
+// Byte offset of the jobs in a grouped prefill table of `count` projections (16-byte aligned).
+size_t gemm_jobs_offset(size_t count) {
+  return (sizeof(bl::GemmGroupHeader) + count * sizeof(bl::GemmGroupProj) + 15) / 16 * 16;
+}
+
+// Grouped prefill plan: validates the projections (bitlinear_fwd's rules, T > 128 each), checks
+// that no output overlaps another output or an input, and lays out the jobs.  Each projection's
+// tiles are cut into runs of up to kGemmRun consecutive tile numbers in gemm_big_kernel's own
+// order (row tiles fastest, so neighbouring blocks of a run read the same token tile and the
+// run's weight rows stay in the XCD's L2); runs are dealt longest first to the least-loaded XCD,
+// and block b takes entry b / 8 of XCD b % 8's list.
+constexpr int64_t kGemmRun = 64;   // two block slots on each of an XCD's 32 CUs
+
+int plan_gemm_group(const bl_fwd_desc* d, int64_t count, int N, int M, int layout,
+                    std::vector<bl::GemmGroupProj>* projs, std::vector<bl::GemmGroupJob>* jobs) {
+  if (!d || count < 1 || count > 4096) return BL_EINVAL;
+  struct Rg { uintptr_t lo, hi; bool out; };
+  std::vector<Rg> rs;
+  projs->assign((size_t)count, bl::GemmGroupProj{});
+  for (int64_t i = 0; i < count; ++i) {
+    int64_t ke = 0;
+    const int st = check_fwd(d[i].xq, d[i].x_scale, d[i].T, d[i].K, d[i].codes, d[i].meta,
+                             d[i].gamma, N, M, layout, d[i].n, d[i].y, d[i].acc_opt, &ke);
+    if (st != BL_OK) return st;
+    if (d[i].T <= 128) return BL_EINVAL;
+    const bl_fwd_desc& q = d[i];
+    size_t cb = 0, mb = 0;
+    bitlinear_packed_bytes(q.n, q.K, N, M, layout, &cb, &mb, nullptr, nullptr);
+    rs.push_back({(uintptr_t)q.xq, (uintptr_t)q.xq + (uint64_t)q.T * ke, false});
+    rs.push_back({(uintptr_t)q.x_scale, (uintptr_t)q.x_scale + (uint64_t)q.T * 4, false});
+    rs.push_back({(uintptr_t)q.codes, (uintptr_t)q.codes + cb, false});
+    if (mb) rs.push_back({(uintptr_t)q.meta, (uintptr_t)q.meta + mb, false});
+    rs.push_back({(uintptr_t)q.gamma, (uintptr_t)q.gamma + 4, false});
+    rs.push_back({(uintptr_t)q.y, (uintptr_t)q.y + (uint64_t)q.T * q.n * 4, true});
+    if (q.acc_opt) rs.push_back({(uintptr_t)q.acc_opt, (uintptr_t)q.acc_opt + (uint64_t)q.T * q.n * 4, true});
+    bl::GemmGroupProj& r = (*projs)[(size_t)i];
+    r.xq = q.xq; r.xs = q.x_scale;
+    r.codes = (const uint32_t*)q.codes; r.meta = (const uint32_t*)q.meta;
+    r.gamma = q.gamma; r.y = q.y; r.acc = q.acc_opt;
+    r.T = (int32_t)q.T; r.Keff = (int32_t)ke; r.n = (int32_t)q.n;
+    r.npanels = (int32_t)((q.n + 31) / 32);   // 32-row packed panels
+  }
+  // inputs may be shared or overlap; an output may overlap nothing
+  std::sort(rs.begin(), rs.end(), [](const Rg& a, const Rg& b) { return a.lo < b.lo; });
+  uintptr_t out_hi = 0, any_hi = 0;
+  for (const Rg& r : rs) {
+    if (r.lo < out_hi || (r.out && r.lo < any_hi)) return BL_EINVAL;
+    any_hi = std::max(any_hi, r.hi);
+    if (r.out) out_hi = std::max(out_hi, r.hi);
+  }
+  const int64_t BM = bl::gemm_group_tile_rows(), BN = bl::gemm_group_tile_tokens();
+  struct Run { int32_t proj; int64_t t0, t1, tiles_m, work; };
+  std::vector<Run> runs;
+  for (int64_t i = 0; i < count; ++i) {
+    const bl::GemmGroupProj& r = (*projs)[(size_t)i];
+    const int64_t tm = (r.n + BM - 1) / BM, tiles = tm * ((r.T + BN - 1) / BN);
+    for (int64_t t0 = 0; t0 < tiles; t0 += kGemmRun) {
+      const int64_t t1 = std::min(tiles, t0 + kGemmRun);
+      runs.push_back({(int32_t)i, t0, t1, tm, (t1 - t0) * (int64_t)r.Keff});
+    }
+    if ((int64_t)runs.size() > (int64_t)1 << 24) return BL_EINVAL;
+  }
+  std::stable_sort(runs.begin(), runs.end(),
+                   [](const Run& a, const Run& b) { return a.work > b.work; });
+  std::vector<std::vector<bl::GemmGroupJob>> per(bl::kXcds);
+  int64_t load[bl::kXcds] = {};
+  for (const Run& rn : runs) {
+    const int x = (int)(std::min_element(load, load + bl::kXcds) - load);
+    load[x] += rn.work;
+    for (int64_t t = rn.t0; t < rn.t1; ++t)
+      per[x].push_back({rn.proj, (int32_t)(t % rn.tiles_m), (int32_t)(t / rn.tiles_m), 0});
+  }
+  size_t depth = 0;
+  for (const auto& v : per) depth = std::max(depth, v.size());
+  if (depth * bl::kXcds > (size_t)INT32_MAX) return BL_EINVAL;
+  jobs->assign(depth * bl::kXcds, bl::GemmGroupJob{-1, 0, 0, 0});
+  for (int x = 0; x < bl::kXcds; ++x)
+    for (size_t k = 0; k < per[x].size(); ++k) (*jobs)[k * bl::kXcds + x] = per[x][k];
+  return BL_OK;
+}
+
 // A fused group's descriptors as plain ones (xq = the bf16 rows; x_scale is not read, the row
 // pointer stands in for the NULL check), after the checks that are the fused path's own: no
 // lifting (2:4 SPARSE or DENSE2) and bf16 rows addressable with 32-bit offsets.
@@ -615,6 +697,61 @@ int bitlinear_pack_group(const void* table, const bl_pack_group_plan* plan, void
     return BL_EINVAL;
   return status_of(bl::launch_pack_group(table, plan->count, plan->pack_blocks, plan->layout,
                                          plan->M, (hipStream_t)stream));
+}
+
+int bitlinear_gemm_group_plan(const bl_fwd_desc* descs, int64_t count, int N, int M, int layout,
+                              bl_gemm_group_plan* plan) {
+  if (!plan) return BL_EINVAL;
+  std::vector<bl::GemmGroupProj> projs;
+  std::vector<bl::GemmGroupJob> jobs;
+  const int st = plan_gemm_group(descs, count, N, M, layout, &projs, &jobs);
+  if (st != BL_OK) return st;
+  memset(plan, 0, sizeof *plan);
+  plan->table_bytes = gemm_jobs_offset(projs.size()) + jobs.size() * sizeof(bl::GemmGroupJob);
+  plan->jobs = (int64_t)jobs.size();
+  plan->N = N;
+  plan->M = M;
+  plan->layout = layout;
+  return BL_OK;
+}
+
+int bitlinear_gemm_group_build(const bl_fwd_desc* descs, int64_t count, int N, int M, int layout,
+                               void* table, size_t table_bytes, void* stream) {
+  if (!aligned16(table)) return BL_EINVAL;
+  std::vector<bl::GemmGroupProj> projs;
+  std::vector<bl::GemmGroupJob> jobs;
+  const int st = plan_gemm_group(descs, count, N, M, layout, &projs, &jobs);
+  if (st != BL_OK) return st;
+  const size_t pbytes = projs.size() * sizeof(bl::GemmGroupProj);
+  const size_t jobs_off = gemm_jobs_offset(projs.size());
+  const size_t bytes = jobs_off + jobs.size() * sizeof(bl::GemmGroupJob);
+  if (table_bytes < bytes) return BL_ENOSPC;
+  std::vector<uint8_t> img(bytes, 0);
+  bl::GemmGroupHeader hdr;
+  memset(&hdr, 0, sizeof hdr);
+  hdr.magic = bl::kGemmGroupMagic;
+  hdr.layout = layout;
+  hdr.N = N;
+  hdr.M = M;
+  hdr.count = (int32_t)count;
+  hdr.jobs = (int32_t)jobs.size();
+  hdr.jobs_off = (int64_t)jobs_off;
+  memcpy(img.data(), &hdr, sizeof hdr);
+  memcpy(img.data() + sizeof hdr, projs.data(), pbytes);
+  memcpy(img.data() + jobs_off, jobs.data(), jobs.size() * sizeof(bl::GemmGroupJob));
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = hipMemcpyAsync(table, img.data(), bytes, hipMemcpyHostToDevice, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);  // img is released on return
+  return status_of(e);
+}
+
+int bitlinear_gemm_group(const void* table, const bl_gemm_group_plan* plan, void* stream) {
+  if (!plan || !aligned16(table)) return BL_EINVAL;
+  int64_t ke = 0;
+  const int st = check_shape(1, 256, plan->N, plan->M, plan->layout, &ke);
+  if (st != BL_OK) return st;
+  if (plan->jobs < 1 || plan->jobs > INT32_MAX) return BL_EINVAL;
+  return status_of(bl::launch_gemm_group(table, plan->jobs, plan->layout, (hipStream_t)stream));
 }
 
 int act_quant_i8(const void* x, int x_dtype, int64_t T, int64_t K, int lift_M, int8_t* xq,

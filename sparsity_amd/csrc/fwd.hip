@@ -21,6 +21,7 @@
 //   gemm_kernel  prefill: block tile BM rows x BN tokens; B staged in LDS (double buffered),
 //                A loaded per wave straight into registers one step ahead.
 #include "device_common.hpp"
+#include "gemm_group.hpp"
 #include "launch.hpp"
 
 namespace bl {
@@ -451,14 +452,14 @@ struct BigGemm {
   }
 };
 
+// One 256-row x 128-token output tile at (row0, tok0): the pipelined main loop, then the epilogue.
 template <int LAYOUT, int NWAVE>
-__global__ __launch_bounds__(64 * NWAVE, 2) void gemm_big_kernel(
-    const int8_t* __restrict__ xq, const float* __restrict__ xs, int T, int Keff,
+__device__ __forceinline__ void big_tile(
+    int8_t* ring, const int8_t* __restrict__ xq, const float* __restrict__ xs, int T, int Keff,
     const uint32_t* __restrict__ codes, const uint32_t* __restrict__ meta,
     const float* __restrict__ gamma_p, int n, int npanels, float* __restrict__ y,
-    int32_t* __restrict__ acc_out, int tiles_m, int tiles) {
+    int32_t* __restrict__ acc_out, int row0, int tok0) {
   using G = BigGemm<LAYOUT, NWAVE, kBigWaveRows, kBigWaveM, kBigWaveN>;
-  __shared__ __attribute__((aligned(16))) int8_t ring[3 * G::STAGE];
   G k;
   k.ring = ring;
   k.xq = xq; k.codes = codes; k.meta = meta; k.Keff = Keff;
@@ -467,11 +468,6 @@ __global__ __launch_bounds__(64 * NWAVE, 2) void gemm_big_kernel(
   k.wm = k.wave % G::WR;
   k.wn = k.wave / G::WR;
   k.h = k.lane >> 5;
-  const int full = (tiles / 8) * 8;
-  const int b = blockIdx.x;
-  const int t = b < full ? (b % 8) * (tiles / 8) + b / 8 : b;
-  const int tm = t % tiles_m, tn = t / tiles_m;
-  const int row0 = tm * G::BM, tok0 = tn * G::BN;
   k.NF = Keff / G::KSTEP;
   k.NS = (k.NF + G::KS - 1) / G::KS;
 
@@ -586,6 +582,55 @@ __global__ __launch_bounds__(64 * NWAVE, 2) void gemm_big_kernel(
     }
   }
 }
+
+template <int LAYOUT, int NWAVE>
+__global__ __launch_bounds__(64 * NWAVE, 2) void gemm_big_kernel(
+    const int8_t* __restrict__ xq, const float* __restrict__ xs, int T, int Keff,
+    const uint32_t* __restrict__ codes, const uint32_t* __restrict__ meta,
+    const float* __restrict__ gamma_p, int n, int npanels, float* __restrict__ y,
+    int32_t* __restrict__ acc_out, int tiles_m, int tiles) {
+  using G = BigGemm<LAYOUT, NWAVE, kBigWaveRows, kBigWaveM, kBigWaveN>;
+  __shared__ __attribute__((aligned(16))) int8_t ring[3 * G::STAGE];
+  const int full = (tiles / 8) * 8;
+  const int b = blockIdx.x;
+  const int t = b < full ? (b % 8) * (tiles / 8) + b / 8 : b;
+  const int tm = t % tiles_m, tn = t / tiles_m;
+  big_tile<LAYOUT, NWAVE>(ring, xq, xs, T, Keff, codes, meta, gamma_p, n, npanels, y, acc_out,
+                          tm * G::BM, tn * G::BN);
+}
+
+// ---------------------------------------------------------------------------------------------
+// Grouped prefill: every tile of several projections (the bitlinear_fwd calls of a layer set with
+// prefill-sized T) in one launch.  Each job is one gemm_big_kernel tile with its projection's
+// arguments, so the results are those of the separate calls bit for bit; the host deals runs of
+// tiles that share a token tile to the XCDs longest first, so the grid tails of the separate
+// launches become one.
+// ---------------------------------------------------------------------------------------------
+template <int LAYOUT>
+__global__ __launch_bounds__(64 * kBigWaves, 2) void gemm_big_group_kernel(
+    const uint8_t* __restrict__ table) {
+  using G = BigGemm<LAYOUT, kBigWaves, kBigWaveRows, kBigWaveM, kBigWaveN>;
+  __shared__ __attribute__((aligned(16))) int8_t ring[3 * G::STAGE];
+  const GemmGroupHeader* hd = (const GemmGroupHeader*)table;
+  if (hd->magic != kGemmGroupMagic || hd->layout != LAYOUT || (int)blockIdx.x >= hd->jobs) return;
+  const GemmGroupJob jb = ((const GemmGroupJob*)(table + hd->jobs_off))[blockIdx.x];
+  if (jb.proj < 0) return;
+  const GemmGroupProj P = ((const GemmGroupProj*)(table + sizeof(GemmGroupHeader)))[jb.proj];
+  big_tile<LAYOUT, kBigWaves>(ring, P.xq, P.xs, P.T, P.Keff, P.codes, P.meta, P.gamma, P.n,
+                              P.npanels, P.y, P.acc, jb.tm * G::BM, jb.tn * G::BN);
+}
+
+hipError_t launch_gemm_group(const void* table, int64_t jobs, int layout, hipStream_t s) {
+  const uint8_t* t = (const uint8_t*)table;
+  if (layout == kLayoutSparse)
+    gemm_big_group_kernel<kLayoutSparse><<<(unsigned)jobs, 64 * kBigWaves, 0, s>>>(t);
+  else
+    gemm_big_group_kernel<kLayoutDense2><<<(unsigned)jobs, 64 * kBigWaves, 0, s>>>(t);
+  return hipGetLastError();
+}
+
+int gemm_group_tile_rows() { return BigGemm<kLayoutSparse, kBigWaves, kBigWaveRows, kBigWaveM, kBigWaveN>::BM; }
+int gemm_group_tile_tokens() { return BigGemm<kLayoutSparse, kBigWaves, kBigWaveRows, kBigWaveM, kBigWaveN>::BN; }
 
 template <int LAYOUT>
 static hipError_t launch_fwd_layout(const int8_t* xq, const float* xs, int64_t T, int64_t Keff,

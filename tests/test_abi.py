@@ -391,6 +391,75 @@ def test_pack_group_plan_and_rejects_before_launch(L):
     assert L.bitlinear_pack_group(TB, bad, None) == -22
 
 
+def _gdesc(L, slot, **kw):
+    """A grouped-prefill descriptor whose buffers sit in their own 1 GiB slots of fake space."""
+    base = FAKE + slot * 16 * GB
+    a = dict(xq=base, x_scale=base + GB, T=300, K=640, codes=base + 2 * GB, meta=base + 3 * GB,
+             gamma=base + 4 * GB, n=300, y=base + 5 * GB, acc_opt=None)
+    a.update(kw)
+    return L.BlFwdDesc(**a)
+
+
+def _gplan(L, descs, N=2, M=4, layout=0):
+    return L.bitlinear_gemm_group_plan((L.BlFwdDesc * len(descs))(*descs), N, M, layout)
+
+
+def test_gemm_group_plan_and_rejects_before_launch(L):
+    """256 x 128 output tiles per projection, runs of up to 64 tiles dealt to the least-loaded XCD
+    (heaviest tiles first), launch position p * 8 + x; bitlinear_fwd's rules with T > 128; no
+    output overlaps an input or another output."""
+    a = _gdesc(L, 0)                                     # 2 x 3 tiles, K_eff 320
+    b = _gdesc(L, 1, T=1000, n=1000, K=256)              # 4 x 8 tiles, K_eff 128
+    st, plan = _gplan(L, [a, b])
+    assert st == 0
+    assert plan.jobs == 8 * 32                            # b's 32 tiles on one XCD set the depth
+    assert plan.table_bytes == 64 + 144 + 16 * plan.jobs  # header, 2 x 72 (16-aligned), jobs
+    assert (plan.N, plan.M, plan.layout) == (2, 4, 0)
+    # 2048 tiles in 32 runs of 64: four runs per XCD, no padding
+    st, plan2 = _gplan(L, [_gdesc(L, 0, T=8192, n=8192, K=256)])
+    assert st == 0 and plan2.jobs == 2048
+    # the big projection's runs first, four per XCD; the small one's two tiles go to one XCD
+    st, plan3 = _gplan(L, [_gdesc(L, 0, T=129, n=64), _gdesc(L, 1, T=8192, n=8192, K=256)])
+    assert st == 0 and plan3.jobs == 8 * 258
+    assert _gplan(L, [_gdesc(L, 0, T=128)])[0] == -22   # prefill-sized only
+    assert _gplan(L, [_gdesc(L, 0, T=0)])[0] == -22
+    assert _gplan(L, [_gdesc(L, 0, K=100)])[0] == -22
+    assert _gplan(L, [_gdesc(L, 0, xq=FAKE + 4)])[0] == -22
+    assert _gplan(L, [_gdesc(L, 0, y=FAKE + 5 * GB + 8)])[0] == -22
+    assert _gplan(L, [_gdesc(L, 0, meta=None)])[0] == -22
+    assert _gplan(L, [_gdesc(L, 0, T=1 << 22, K=1024)])[0] == -22   # 32-bit activation offsets
+    assert _gplan(L, [a], N=3)[0] == -95
+    assert _gplan(L, [_gdesc(L, 0, meta=None)], layout=1)[0] == 0
+    lib = L.lib()
+    assert lib.bitlinear_gemm_group_plan(None, 1, 2, 4, 0, ctypes.byref(L.BlGemmGroupPlan())) == -22
+    assert lib.bitlinear_gemm_group_plan((L.BlFwdDesc * 1)(a), 0, 2, 4, 0,
+                                         ctypes.byref(L.BlGemmGroupPlan())) == -22
+    assert lib.bitlinear_gemm_group_plan((L.BlFwdDesc * 1)(a), 1, 2, 4, 0, None) == -22
+    # inputs may be shared; an output may overlap nothing
+    assert _gplan(L, [a, _gdesc(L, 1, xq=a.xq, x_scale=a.x_scale, codes=a.codes,
+                                meta=a.meta, gamma=a.gamma)])[0] == 0
+    assert _gplan(L, [a, _gdesc(L, 1, y=a.y)])[0] == -22
+    assert _gplan(L, [a, _gdesc(L, 1, y=a.y + 300 * 300 * 4 - 16)])[0] == -22
+    assert _gplan(L, [a, _gdesc(L, 1, y=a.y + 300 * 300 * 4)])[0] == 0      # adjacent
+    assert _gplan(L, [a, _gdesc(L, 1, y=a.codes + 1024)])[0] == -22
+    assert _gplan(L, [a, _gdesc(L, 1, xq=a.y + 64)])[0] == -22
+    assert _gplan(L, [_gdesc(L, 0, acc_opt=FAKE + 5 * GB + 4096)])[0] == -22   # acc inside y
+    assert _gplan(L, [_gdesc(L, 0, acc_opt=FAKE + 6 * GB)])[0] == 0
+    # build and launch argument checks (nothing is copied or launched)
+    arr = (L.BlFwdDesc * 2)(a, b)
+    TB = FAKE + 80 * 16 * GB
+    assert L.bitlinear_gemm_group_build(arr, 2, 4, 0, TB, plan.table_bytes - 16, None) == -28
+    assert L.bitlinear_gemm_group_build(arr, 2, 4, 0, TB + 8, plan.table_bytes, None) == -22
+    assert L.bitlinear_gemm_group(TB, None, None) == -22
+    assert L.bitlinear_gemm_group(TB + 4, plan, None) == -22
+    bad = L.BlGemmGroupPlan.from_buffer_copy(plan)
+    bad.N = 3
+    assert L.bitlinear_gemm_group(TB, bad, None) == -95
+    bad = L.BlGemmGroupPlan.from_buffer_copy(plan)
+    bad.jobs = 0
+    assert L.bitlinear_gemm_group(TB, bad, None) == -22
+
+
 def _xdesc(L, **kw):
     P = FAKE
     a = dict(x=P, T=4, K=256, codes=P, meta=P, gamma=P, n=100, y=P, acc_opt=None)
