@@ -65,14 +65,17 @@ def parse():
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the 6:8, 14:16 and training-step legs")
     ap.add_argument("--cpu-budget-s", type=float, default=15.0)
-    ap.add_argument("--profile-pass", choices=("decode", "prefill", "train", "bwd", "bwdgroup"),
+    ap.add_argument("--profile-pass",
+                    choices=("decode", "prefill", "train", "bwd", "bwdgroup", "fwdgroup"),
                     default=None,
                     help="for hardware-counter runs, no graph and no JSON line.  decode: two eager "
                          "decode steps, then a plain copy of COPY_BYTES (the counters' scale "
                          "reference); prefill: the prefill GEMM launched five times; train: the "
                          "training-step leg with two timed steps; bwd: the gate projection's "
                          "backward three times; bwdgroup: the layer set's grouped backward three "
-                         "times, then the plain copies")
+                         "times, then the plain copies; fwdgroup: the layer set's grouped forward "
+                         "three times, its seven separate forwards three times, then the plain "
+                         "copies")
     return ap.parse_args()
 
 
@@ -693,6 +696,35 @@ def bwd_group_profile_pass(S, torch):
         dst.copy_(src)
 
 
+def fwd_group_profile_pass(S, torch):
+    """Forward of the training-step layer set (8192 tokens, 2:4): the grouped prefill launch three
+    times, then the seven separate bitlinear_fwd calls three times, then two plain device copies
+    of COPY_BYTES (the counters' scale reference)."""
+    T = 8192
+    g = torch.Generator(device="cuda")
+    g.manual_seed(38)
+    X = {K: S.act_quant(torch.randn((T, K), generator=g, device="cuda").to(torch.bfloat16))
+         for K in (3200, 8640)}
+    projs = []
+    for (_, n, K) in TRAIN_LAYERS:
+        W = (torch.randn((n, K), generator=g, device="cuda") * 0.02).contiguous()
+        c, m, ga = S.pack(W, 2, 4)
+        projs.append(dict(xq=X[K][0], scale=X[K][1], K=K, codes=c, meta=m, gamma=ga, n=n,
+                          y=torch.empty((T, n), device="cuda")))
+    grp = S.GemmGroup(projs)
+    for _ in range(3):
+        grp()
+    for _ in range(3):
+        for p in projs:
+            S.fwd(p["xq"], p["scale"], p["K"], p["codes"], p["meta"], p["gamma"], p["n"],
+                  out=(p["y"], None))
+    torch.cuda.synchronize()
+    src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+
+
 # ---------------------------------------------------------------------------------------------
 # CPU oracle baseline (bounded sample of the decode workload)
 # ---------------------------------------------------------------------------------------------
@@ -743,6 +775,11 @@ def main():
         bwd_group_profile_pass(S, torch)
         torch.cuda.synchronize()
         log("profile pass done: grouped backward of the layer set x 3, copies x 2")
+        return
+    if args.profile_pass == "fwdgroup":
+        fwd_group_profile_pass(S, torch)
+        torch.cuda.synchronize()
+        log("profile pass done: grouped forward of the layer set x 3, separate calls x 3, copies x 2")
         return
     if args.profile_pass == "train":
         train_step_leg(S, torch, iters=2)
