@@ -5,8 +5,8 @@ Default workload (decode, 2:4): FFN up 6912x2560 and down 2560x6912 BitNet-2B-li
 64 distinct up/down pairs (566 MB of packed weights, more than twice the 256 MB last-level cache,
 so every step streams them from HBM), bf16 activations ~ N(0,1).  One step is the decode hot path
 for the whole layer stream at batch 1, 4 and 16 tokens: per T, per-token int8 quantization of
-the stacked activations of all layers (one act_quant launch per K) and one grouped sparse ternary
-GEMV launch with fused rescale over all 128 projections (the layers' activations are independent
+the stacked activations of all layers (one grouped act_quant launch for the two K) and one
+grouped sparse ternary GEMV launch with fused rescale over all 128 projections (the layers' activations are independent
 inputs).  Weights are packed once before timing (inference stores packed weights).  The step is
 captured once as a HIP graph and replayed; replays are checked bitwise against an eager run first.
 
@@ -152,12 +152,16 @@ class Decode:
             if events is not None:
                 events[T][1].record()
 
+    def quantize(self, S, T):
+        """The stacked activations of both K at T tokens, one grouped act_quant launch."""
+        S.act_quant_group([self.x[(T, K)] for K in (UP[1], DOWN[1])],
+                          outs=[self.q[(T, K)] for K in (UP[1], DOWN[1])])
+
     def step(self, S, events=None):
         """One decode step over the layer stream at every T: quantize the stacked activations
-        (one act_quant per K), then one grouped GEMV launch over all 128 projections."""
+        (one grouped act_quant launch), then one grouped GEMV launch over all 128 projections."""
         for T in DECODE_T:
-            for K in (UP[1], DOWN[1]):
-                S.act_quant(self.x[(T, K)], out=self.q[(T, K)])
+            self.quantize(S, T)
             if events is not None:
                 events[T][0].record()
             self.groups[T]()
@@ -281,8 +285,7 @@ def decode_dense_leg(S, torch, D, steps, warmup):
 
     def step():
         for T in DECODE_T:
-            for K in (UP[1], DOWN[1]):
-                S.act_quant(D.x[(T, K)], out=D.q[(T, K)])
+            D.quantize(S, T)
             groups[T]()
 
     step()
@@ -344,8 +347,7 @@ def decode_hybrid_leg(S, torch, D, steps, warmup, dense_frac=0.25):
 
     def step():
         for T in DECODE_T:
-            for K in (UP[1], DOWN[1]):
-                S.act_quant(D.x[(T, K)], out=D.q[(T, K)])
+            D.quantize(S, T)
             for grp in groups[T]:
                 grp()
 
@@ -495,10 +497,11 @@ TRAIN_LAYERS = (("q", 3200, 3200), ("k", 3200, 3200), ("v", 3200, 3200), ("o", 3
 
 def train_step_leg(S, torch, iters=3):
     """3B-alike decoder layer set at 8192 tokens: re-mask + ternarize + pack all 7 fp32 masters
-    (one grouped pack), quantize the two activation matrices once, the 7 2:4 forwards (one grouped
-    prefill launch), then the grouped backward of all 7.  Each phase is one HIP graph (checked
-    against the eager run of the separate calls) timed with events around its replays; the
-    separate pack, forward and backward calls are timed beside the grouped ones."""
+    (one grouped pack), quantize the two activation matrices once (one grouped act_quant), the 7
+    2:4 forwards (one grouped prefill launch), then the grouped backward of all 7.  Each phase is
+    one HIP graph (checked against the eager run of the separate calls) timed with events around
+    its replays; the separate pack, act_quant, forward and backward calls are timed beside the
+    grouped ones."""
     T = 8192
     g = torch.Generator(device="cuda")
     g.manual_seed(35)
@@ -531,9 +534,12 @@ def train_step_leg(S, torch, iters=3):
     def pack_all():
         pgroup()
 
-    def quant_all():
+    def quant_seq():
         for K in X:
             S.act_quant(X[K], out=Q[K])
+
+    def quant_all():
+        S.act_quant_group([X[K] for K in X], outs=[Q[K] for K in X])
 
     def fwd_seq():
         for (_, n, K), (c, m, ga), y in zip(TRAIN_LAYERS, packed, ys):
@@ -570,13 +576,14 @@ def train_step_leg(S, torch, iters=3):
     # each phase captured once as a HIP graph (no host launch overhead between the 7 matrices);
     # two replays are checked bitwise against the eager results first
     def results():
-        return [t for (c, m, ga) in packed for t in (c, m, ga)] + ys + dWs + list(dXs.values())
+        return ([t for (c, m, ga) in packed for t in (c, m, ga)] + [t for K in Q for t in Q[K]] +
+                ys + dWs + list(dXs.values()))
 
     def outputs():
         return [t.clone() for t in results()]
 
     pack_seq()
-    quant_all()
+    quant_seq()
     fwd_seq()
     bwd_seq()
     torch.cuda.synchronize()
@@ -590,10 +597,10 @@ def train_step_leg(S, torch, iters=3):
     torch.cuda.synchronize()
     for a, b in zip(outputs(), ref):
         if not torch.equal(a, b):
-            raise RuntimeError("grouped pack, forward or backward differs from the sequential calls")
+            raise RuntimeError("grouped pack, act_quant, forward or backward differs from the sequential calls")
     graphs = []
     cap = torch.cuda.Stream()
-    for fn in (pack_seq, pack_all, quant_all, fwd_seq, fwd_all, bwd_seq, bwd_all):
+    for fn in (pack_seq, pack_all, quant_seq, quant_all, fwd_seq, fwd_all, bwd_seq, bwd_all):
         gr = torch.cuda.CUDAGraph()
         with torch.cuda.graph(gr, stream=cap):
             fn()
@@ -609,11 +616,12 @@ def train_step_leg(S, torch, iters=3):
                 raise RuntimeError("training-step graph replay differs from the eager run")
     t_pack_seq = _event_ms(torch, graphs[0].replay, iters)
     t_pack = _event_ms(torch, graphs[1].replay, iters)
-    t_quant = _event_ms(torch, graphs[2].replay, iters)
-    t_fwd_seq = _event_ms(torch, graphs[3].replay, iters)
-    t_fwd = _event_ms(torch, graphs[4].replay, iters)
-    t_bwd_seq = _event_ms(torch, graphs[5].replay, iters)
-    t_bwd = _event_ms(torch, graphs[6].replay, iters)
+    t_quant_seq = _event_ms(torch, graphs[2].replay, iters)
+    t_quant = _event_ms(torch, graphs[3].replay, iters)
+    t_fwd_seq = _event_ms(torch, graphs[4].replay, iters)
+    t_fwd = _event_ms(torch, graphs[5].replay, iters)
+    t_bwd_seq = _event_ms(torch, graphs[6].replay, iters)
+    t_bwd = _event_ms(torch, graphs[7].replay, iters)
     pack_bytes = sum(4 * n * K + p[0].numel() + p[1].numel() for (_, n, K), p in zip(TRAIN_LAYERS, packed))
     # act_quant: bf16 read + int8 write per element + 4 B scale per token
     quant_bytes = sum(T * K * 3 + 4 * T for K in X)
@@ -633,6 +641,8 @@ def train_step_leg(S, torch, iters=3):
             # the seven bitlinear_pack calls one after another (same results, bit for bit)
             "pack_sequential_ms": round(t_pack_seq, 4),
             "act_quant_ms": round(t_quant, 4), "act_quant_GBps": round(quant_gbs, 1),
+            # the two act_quant_i8 calls one after another (same results, bit for bit)
+            "act_quant_sequential_ms": round(t_quant_seq, 4),
             "fwd_ms": round(t_fwd, 4), "fwd_TOPS": round(fwd_tops, 1),
             # the seven bitlinear_fwd calls one after another (same results, bit for bit)
             "fwd_sequential_ms": round(t_fwd_seq, 4),
@@ -884,7 +894,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": "decode GEMV 2:4 ternary, FFN up 6912x2560 + down 2560x6912, "
                                "64 distinct pairs (cold cache), T=1,4,16 bf16 N(0,1); per step and "
-                               "T: act_quant of the stacked activations + one grouped GEMV launch",
+                               "T: one grouped act_quant launch of the stacked activations + one "
+                               "grouped GEMV launch",
                    "tokens": list(DECODE_T), "layer_pairs": N_PAIRS,
                    "packed_weight_bytes_per_pass": D.packed_bytes, "parallelism": "none"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",

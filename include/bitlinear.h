@@ -109,6 +109,26 @@ int bitlinear_pack(const float* W, int64_t n, int64_t K, int N, int M, int layou
 int act_quant_i8(const void* x, int x_dtype, int64_t T, int64_t K, int lift_M, int8_t* xq,
                  float* x_scale, void* stream);
 
+/* act_quant_i8 of several activation matrices in one launch (a decode step quantizes the inputs
+ * of its independent projections together; BitNet b1.58 page, "The mechanism", per-token absmax
+ * quantization).  descs[i] holds the x, T, K, xq and x_scale of one act_quant_i8 call; all share
+ * x_dtype and lift_M.  Each matrix's xq and x_scale are bit-identical to that call's, and each
+ * follows its rules (T == 0 entries are skipped and may hold NULL pointers).  Inputs may be
+ * shared or overlap; an output (xq, x_scale) may overlap no other output and no input
+ * (BL_EINVAL).  1 <= count <= 16.  No table and no build step: the descriptors are copied into
+ * the launch's arguments, so the call is asynchronous and capturable like act_quant_i8.  Rows
+ * longer than 16384 bf16 (8192 fp32) elements make the group fall back to one launch per
+ * matrix. */
+typedef struct bl_quant_desc {
+  const void* x;         /* [T][K] activations, x_dtype */
+  int64_t T, K;
+  int8_t* xq;            /* [T][K_eff] int8 */
+  float* x_scale;        /* [T] fp32 token scales */
+} bl_quant_desc;
+
+int act_quant_i8_group(const bl_quant_desc* descs, int64_t count, int x_dtype, int lift_M,
+                       void* stream);
+
 /* y[T][n] fp32 = gamma * x_scale[t] * (xq[T][K_eff] . W_eff^T), int32 accumulation.
  * K is the master's in-feature count; (N, M, layout) must be those the weights were packed
  * with, and xq must be on the packed K axis (lifted with lift_M = M for SPARSE 6:8 and 14:16).

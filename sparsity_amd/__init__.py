@@ -7,7 +7,7 @@ names.  PyTorch is used only to own device memory and streams.
 from .bitlinear import (  # noqa: F401
     BL_BWD_ACCUM_DW, BL_BWD_ACCUM_DX, BL_DTYPE_BF16, BL_DTYPE_F32, BL_LAYOUT_DENSE2,
     BL_LAYOUT_SPARSE, BitLinearError, BlBwdDesc, BlBwdGroupPlan, BlFwdDesc, BlFwdXDesc, BlPackDesc,
-    BlGemmGroupPlan, BlPackGroupPlan, BwdGroup, FusedGroup, FwdGroup, GemmGroup, PackGroup,
+    BlGemmGroupPlan, BlPackGroupPlan, BlQuantDesc, act_quant_group, act_quant_i8_group, BwdGroup, FusedGroup, FwdGroup, GemmGroup, PackGroup,
     act_quant, act_quant_i8, bitlinear_gemm_group, bitlinear_gemm_group_build,
     bitlinear_gemm_group_plan,
     bitlinear_bwd, bitlinear_bwd_group, bitlinear_pack_group, bitlinear_pack_group_build,

@@ -72,6 +72,12 @@ class BlPackGroupPlan(ctypes.Structure):
                 ("reserved", ctypes.c_int32)]
 
 
+class BlQuantDesc(ctypes.Structure):
+    """bl_quant_desc: the arguments of one act_quant_i8 call inside a grouped quantization."""
+    _fields_ = [("x", ctypes.c_void_p), ("T", ctypes.c_int64), ("K", ctypes.c_int64),
+                ("xq", ctypes.c_void_p), ("x_scale", ctypes.c_void_p)]
+
+
 class BlGemmGroupPlan(ctypes.Structure):
     """bl_gemm_group_plan: table size and the grid of a grouped prefill forward."""
     _fields_ = [("table_bytes", ctypes.c_size_t), ("jobs", ctypes.c_int64),
@@ -104,6 +110,7 @@ def lib() -> ctypes.CDLL:
                                              ctypes.POINTER(sz), ctypes.POINTER(i64), ctypes.POINTER(sz)]
         L.bitlinear_pack.argtypes = [vp, i64, i64, i32, i32, i32, vp, vp, vp, vp, sz, vp]
         L.act_quant_i8.argtypes = [vp, i32, i64, i64, i32, vp, vp, vp]
+        L.act_quant_i8_group.argtypes = [ctypes.POINTER(BlQuantDesc), i64, i32, i32, vp]
         L.bitlinear_fwd.argtypes = [vp, vp, i64, i64, vp, vp, vp, i32, i32, i32, i64, vp, vp, vp]
         dp = ctypes.POINTER(BlFwdDesc)
         L.bitlinear_group_table_bytes.argtypes = [dp, i64, i32, i32, i32, ctypes.POINTER(sz),
@@ -144,7 +151,8 @@ def lib() -> ctypes.CDLL:
                   L.bitlinear_bwd_group_build, L.bitlinear_bwd_group,
                   L.bitlinear_pack_group_plan, L.bitlinear_pack_group_build,
                   L.bitlinear_pack_group, L.bitlinear_gemm_group_plan,
-                  L.bitlinear_gemm_group_build, L.bitlinear_gemm_group):
+                  L.bitlinear_gemm_group_build, L.bitlinear_gemm_group,
+                  L.act_quant_i8_group):
             f.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -174,6 +182,11 @@ def bitlinear_pack(W, n, K, N, M, layout, codes, meta, gamma, ws, ws_bytes, stre
 
 def act_quant_i8(x, x_dtype, T, K, lift_M, xq, x_scale, stream) -> int:
     return lib().act_quant_i8(x, x_dtype, T, K, lift_M, xq, x_scale, stream)
+
+
+def act_quant_i8_group(descs, x_dtype, lift_M, stream) -> int:
+    """descs: a ctypes array of BlQuantDesc."""
+    return lib().act_quant_i8_group(descs, len(descs), x_dtype, lift_M, stream)
 
 
 def bitlinear_fwd(xq, x_scale, T, K, codes, meta, gamma, N, M, layout, n, y, acc, stream) -> int:
@@ -338,6 +351,32 @@ def act_quant(x, lift_M: int = 0, out=None):
     _check(act_quant_i8(x.data_ptr(), dt, T, K, lift_M, xq.data_ptr(), scale.data_ptr(), _stream()),
            "act_quant_i8")
     return xq, scale
+
+
+def act_quant_group(xs, lift_M: int = 0, outs=None):
+    """act_quant of several contiguous CUDA tensors x[T][K] (one dtype) in one launch.
+
+    Returns a list of (xq, scale), equal to ``act_quant`` per tensor bit for bit; ``outs``, if
+    given, is a list of (xq, scale) buffers to write.
+    """
+    import torch
+    dts = {torch.float32: BL_DTYPE_F32, torch.bfloat16: BL_DTYPE_BF16}
+    dt = dts[xs[0].dtype]
+    arr = (BlQuantDesc * len(xs))()
+    res = []
+    for i, x in enumerate(xs):
+        assert x.is_cuda and x.is_contiguous() and x.dim() == 2 and dts[x.dtype] == dt
+        T, K = x.shape
+        ke = K // lift_M * (2 * lift_M - 4) if lift_M else K
+        if outs is None:
+            xq = torch.empty((T, ke), dtype=torch.int8, device=x.device)
+            scale = torch.empty(max(T, 4), dtype=torch.float32, device=x.device)[:T]
+        else:
+            xq, scale = outs[i]
+        res.append((xq, scale))
+        arr[i] = BlQuantDesc(_ptr(x), T, K, _ptr(xq), _ptr(scale))
+    _check(act_quant_i8_group(arr, dt, lift_M, _stream()), "act_quant_i8_group")
+    return res
 
 
 def fwd(xq, scale, K: int, codes, meta, gamma, n: int, N: int = 2, M: int = 4,

@@ -11,8 +11,12 @@
 // one wave per token, holding its share of the row in registers, so the row is read from memory
 // once and the token needs no block barrier.  Longer rows fall back to act_quant_kernel: one block
 // per token, the row read twice (the second pass from L2).
+#include <algorithm>
+#include <type_traits>
+
 #include "device_common.hpp"
 #include "launch.hpp"
+#include "quant_group.hpp"
 
 namespace bl {
 
@@ -111,43 +115,48 @@ __device__ __forceinline__ float piece_value(const Piece<BF16>& p, int j) {
   else return __uint_as_float(p.w[j]);
 }
 
-// One wave per token, four tokens per block.  Lane l holds chunks l, l + 64, ... (CPL at most) of
-// its token's row, CH elements each (8, or the LM elements of a lifting group), loaded before the
-// absmax so all of a lane's loads are in flight at once; the quantized chunks are written from the
-// registers.
+// One wave per token.  Lane l holds chunks l, l + 64, ... of its token's row (the first `cpl` of
+// the CPL register slots; cpl is uniform), CH elements each (8, or the LM elements of a lifting
+// group), loaded before the absmax so all of a lane's loads are in flight at once; the quantized
+// chunks are written from the registers.
 template <bool BF16, int LM, int CPL>
-__global__ __launch_bounds__(256) void act_quant_row_kernel(const void* __restrict__ x, int T,
-                                                            int K, int8_t* __restrict__ xq,
-                                                            float* __restrict__ xs) {
+__device__ __forceinline__ void quant_row(const void* __restrict__ x, int K, int8_t* __restrict__ xq,
+                                          float* __restrict__ xs, int t, int lane, int cpl) {
   constexpr int CH = LM ? LM : 8;
   constexpr int PPC = CH / 8;             // pieces per chunk
-  const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= T) return;                     // the whole wave
   const int nchunk = K / CH;
   const size_t row = (size_t)t * K;
   Piece<BF16> p[CPL][PPC];
 #pragma unroll
   for (int i = 0; i < CPL; ++i) {
-    const int c = min(lane + 64 * i, nchunk - 1);   // past the end: reload the last chunk
+    if (i < cpl) {
+      const int c = min(lane + 64 * i, nchunk - 1);   // past the end: reload the last chunk
 #pragma unroll
-    for (int h = 0; h < PPC; ++h) load_piece<BF16>(x, row + (size_t)CH * c + 8 * h, p[i][h]);
+      for (int h = 0; h < PPC; ++h) load_piece<BF16>(x, row + (size_t)CH * c + 8 * h, p[i][h]);
+    }
   }
   uint32_t mx = 0;
 #pragma unroll
-  for (int i = 0; i < CPL; ++i)
+  for (int i = 0; i < CPL; ++i) {
+    if (i < cpl) {
 #pragma unroll
-    for (int h = 0; h < PPC; ++h)
+      for (int h = 0; h < PPC; ++h)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) mx = max(mx, __float_as_uint(piece_value<BF16>(p[i][h], j)) & 0x7FFFFFFFu);
+        for (int j = 0; j < 8; ++j)
+          mx = max(mx, __float_as_uint(piece_value<BF16>(p[i][h], j)) & 0x7FFFFFFFu);
+    }
+  }
   // the raw words pass through opaque copies: without them the compiler keeps every element's
   // unpacked value from the absmax loop alive for the quantization (twice the registers)
 #pragma unroll
-  for (int i = 0; i < CPL; ++i)
+  for (int i = 0; i < CPL; ++i) {
+    if (i < cpl) {
 #pragma unroll
-    for (int h = 0; h < PPC; ++h)
+      for (int h = 0; h < PPC; ++h)
 #pragma unroll
-      for (int k = 0; k < (BF16 ? 4 : 8); ++k) asm volatile("" : "+v"(p[i][h].w[k]));
+        for (int k = 0; k < (BF16 ? 4 : 8); ++k) asm volatile("" : "+v"(p[i][h].w[k]));
+    }
+  }
   mx = wave_max_u32(mx);
   const float amax = __uint_as_float(mx);
   const float s = amax > 0.f ? 127.f / amax : 0.f;
@@ -176,23 +185,68 @@ __global__ __launch_bounds__(256) void act_quant_row_kernel(const void* __restri
   if (lane == 0) xs[t] = amax / 127.f;
 }
 
+// Four tokens per block, CPL register slots per lane for every row.
+template <bool BF16, int LM, int CPL>
+__global__ __launch_bounds__(256) void act_quant_row_kernel(const void* __restrict__ x, int T,
+                                                            int K, int8_t* __restrict__ xq,
+                                                            float* __restrict__ xs) {
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;                     // the whole wave
+  quant_row<BF16, LM, CPL>(x, K, xq, xs, t, threadIdx.x & 63, CPL);
+}
+
+// Grouped: the rows of several matrices in one launch.  Block b belongs to the last matrix whose
+// first block is at most b (matrices without tokens own no blocks); every wave loads only the
+// chunks of its own row, so a short-row matrix in a group with long rows reads nothing extra.
+template <bool BF16, int LM, int CPL>
+__global__ __launch_bounds__(256) void act_quant_group_kernel(QuantGroupArgs a) {
+  constexpr int CH = LM ? LM : 8;
+  const int b = blockIdx.x;
+  int m = 0;
+  for (int i = 1; i < a.count; ++i)
+    if (b >= a.block0[i]) m = i;
+  const int t = (b - a.block0[m]) * 4 + (threadIdx.x >> 6);
+  if (t >= a.T[m]) return;                // the whole wave
+  const int K = a.K[m];
+  quant_row<BF16, LM, CPL>(a.x[m], K, a.xq[m], a.xs[m], t, threadIdx.x & 63, (K / CH + 63) / 64);
+}
+
+// Calls f(std::integral_constant<int, CPL>) with the smallest CPL instantiation that holds cpl
+// chunks per lane within the register budget (raw registers per lane: CPL * CH / 2 for bf16,
+// CPL * CH for fp32; at most 128); false if the rows are too long for it.
+template <bool BF16, int LM, class F>
+static bool with_cpl(int64_t cpl, F&& f) {
+  constexpr int CH = LM ? LM : 8;
+  constexpr int MAXR = 128 / (BF16 ? CH / 2 : CH);
+  if (cpl <= 4) f(std::integral_constant<int, 4>{});
+  else if (cpl <= 8) f(std::integral_constant<int, 8>{});
+  else if (cpl <= 12 && MAXR >= 12) f(std::integral_constant<int, (MAXR >= 12 ? 12 : 4)>{});
+  else if (cpl <= 16 && MAXR >= 16) f(std::integral_constant<int, (MAXR >= 16 ? 16 : 4)>{});
+  else if (cpl <= 24 && MAXR >= 24) f(std::integral_constant<int, (MAXR >= 24 ? 24 : 4)>{});
+  else if (cpl <= 32 && MAXR >= 32) f(std::integral_constant<int, (MAXR >= 32 ? 32 : 4)>{});
+  else return false;
+  return true;
+}
+
 template <bool BF16, int LM>
 static bool launch_rows(const void* x, int64_t T, int64_t K, int8_t* xq, float* xs,
                         hipStream_t s) {
   constexpr int CH = LM ? LM : 8;
-  const int64_t cpl = (K / CH + 63) / 64;      // chunks per lane
   const dim3 grid((unsigned)((T + 3) / 4));
-  auto run = [&](auto kern) { kern<<<grid, 256, 0, s>>>(x, (int)T, (int)K, xq, xs); };
-  // raw registers per lane: CPL * CH / 2 (bf16) or CPL * CH (fp32); at most 128
-  constexpr int MAXR = 128 / (BF16 ? CH / 2 : CH);
-  if (cpl <= 4) run(act_quant_row_kernel<BF16, LM, 4>);
-  else if (cpl <= 8) run(act_quant_row_kernel<BF16, LM, 8>);
-  else if (cpl <= 12 && MAXR >= 12) run(act_quant_row_kernel<BF16, LM, (MAXR >= 12 ? 12 : 4)>);
-  else if (cpl <= 16 && MAXR >= 16) run(act_quant_row_kernel<BF16, LM, (MAXR >= 16 ? 16 : 4)>);
-  else if (cpl <= 24 && MAXR >= 24) run(act_quant_row_kernel<BF16, LM, (MAXR >= 24 ? 24 : 4)>);
-  else if (cpl <= 32 && MAXR >= 32) run(act_quant_row_kernel<BF16, LM, (MAXR >= 32 ? 32 : 4)>);
-  else return false;
-  return true;
+  return with_cpl<BF16, LM>((K / CH + 63) / 64, [&](auto c) {
+    act_quant_row_kernel<BF16, LM, decltype(c)::value><<<grid, 256, 0, s>>>(x, (int)T, (int)K, xq, xs);
+  });
+}
+
+template <bool BF16, int LM>
+static bool launch_group_rows(const QuantGroupArgs& a, hipStream_t s) {
+  constexpr int CH = LM ? LM : 8;
+  int64_t cpl = 0;
+  for (int i = 0; i < a.count; ++i) cpl = std::max<int64_t>(cpl, (a.K[i] / CH + 63) / 64);
+  const dim3 grid((unsigned)a.block0[a.count]);
+  return with_cpl<BF16, LM>(cpl, [&](auto c) {
+    act_quant_group_kernel<BF16, LM, decltype(c)::value><<<grid, 256, 0, s>>>(a);
+  });
 }
 
 hipError_t launch_act_quant(const void* x, int x_is_bf16, int64_t T, int64_t K, int lift_M,
@@ -220,6 +274,29 @@ hipError_t launch_act_quant(const void* x, int x_is_bf16, int64_t T, int64_t K, 
     else run(act_quant_kernel<false, 0>);
   }
   return hipGetLastError();
+}
+
+hipError_t launch_act_quant_group(const QuantGroupArgs& a, int x_is_bf16, int lift_M,
+                                  hipStream_t s) {
+  if (a.count < 1 || a.block0[a.count] < 1) return hipSuccess;
+  bool done;
+  if (x_is_bf16) {
+    if (lift_M == 8) done = launch_group_rows<true, 8>(a, s);
+    else if (lift_M == 16) done = launch_group_rows<true, 16>(a, s);
+    else done = launch_group_rows<true, 0>(a, s);
+  } else {
+    if (lift_M == 8) done = launch_group_rows<false, 8>(a, s);
+    else if (lift_M == 16) done = launch_group_rows<false, 16>(a, s);
+    else done = launch_group_rows<false, 0>(a, s);
+  }
+  if (done) return hipGetLastError();
+  // a row too long for the register budget: the matrices one launch each
+  for (int i = 0; i < a.count; ++i) {
+    const hipError_t e = launch_act_quant(a.x[i], x_is_bf16, a.T[i], a.K[i], lift_M, a.xq[i],
+                                          a.xs[i], s);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace bl

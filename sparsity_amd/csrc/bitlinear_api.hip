@@ -12,6 +12,7 @@
 #include "bitlinear.h"
 #include "bwd_group.hpp"
 #include "gemm_group.hpp"
+#include "quant_group.hpp"
 #include "launch.hpp"
 #include "pack_group.hpp"
 
@@ -47,6 +48,18 @@ int check_shape(int64_t n, int64_t K, int N, int M, int layout, int64_t* keff) {
 }
 
 int status_of(hipError_t e) { return e == hipSuccess ? BL_OK : BL_EIO; }
+
+// Checks of one act_quant_i8 call (pointers are not looked at when T == 0).
+int check_quant(const void* x, int x_dtype, int64_t T, int64_t K, int lift_M, const int8_t* xq,
+                const float* x_scale) {
+  if (x_dtype != BL_DTYPE_F32 && x_dtype != BL_DTYPE_BF16) return BL_ENOTSUP;
+  if (lift_M != 0 && lift_M != 8 && lift_M != 16) return BL_EINVAL;
+  if (lift_M == 16 && K % 16 != 0) return BL_EINVAL;
+  if (T < 0 || T > INT32_MAX || K < 8 || K % 8 != 0 || K > (int64_t)1 << 24) return BL_EINVAL;
+  if (T == 0) return BL_OK;
+  if (!aligned16(x) || !aligned16(xq) || !aligned4(x_scale)) return BL_EINVAL;
+  return BL_OK;
+}
 
 // Shared checks of one bitlinear_fwd-style projection; returns BL_OK and its packed K axis.
 int check_fwd(const int8_t* xq, const float* x_scale, int64_t T, int64_t K, const uint8_t* codes,
@@ -756,14 +769,52 @@ int bitlinear_gemm_group(const void* table, const bl_gemm_group_plan* plan, void
 
 int act_quant_i8(const void* x, int x_dtype, int64_t T, int64_t K, int lift_M, int8_t* xq,
                  float* x_scale, void* stream) {
-  if (x_dtype != BL_DTYPE_F32 && x_dtype != BL_DTYPE_BF16) return BL_ENOTSUP;
-  if (lift_M != 0 && lift_M != 8 && lift_M != 16) return BL_EINVAL;
-  if (lift_M == 16 && K % 16 != 0) return BL_EINVAL;
-  if (T < 0 || T > INT32_MAX || K < 8 || K % 8 != 0 || K > (int64_t)1 << 24) return BL_EINVAL;
-  if (T == 0) return BL_OK;  // nothing is read or written; pointers may be NULL
-  if (!aligned16(x) || !aligned16(xq) || !aligned4(x_scale)) return BL_EINVAL;
+  const int st = check_quant(x, x_dtype, T, K, lift_M, xq, x_scale);
+  if (st != BL_OK || T == 0) return st;   // T == 0: nothing is read or written
   return status_of(bl::launch_act_quant(x, x_dtype == BL_DTYPE_BF16, T, K, lift_M, xq, x_scale,
                                         (hipStream_t)stream));
+}
+
+int act_quant_i8_group(const bl_quant_desc* descs, int64_t count, int x_dtype, int lift_M,
+                       void* stream) {
+  if (!descs || count < 1 || count > bl::kQuantGroupMax) return BL_EINVAL;
+  struct Rg { uintptr_t lo, hi; bool out; };
+  std::vector<Rg> rs;
+  bl::QuantGroupArgs a;
+  memset(&a, 0, sizeof a);
+  int64_t blocks = 0;
+  for (int64_t i = 0; i < count; ++i) {
+    const bl_quant_desc& d = descs[i];
+    const int st = check_quant(d.x, x_dtype, d.T, d.K, lift_M, d.xq, d.x_scale);
+    if (st != BL_OK) return st;
+    if (d.T == 0) continue;
+    const uint64_t ke = lift_M ? (uint64_t)d.K / lift_M * (2 * lift_M - 4) : (uint64_t)d.K;
+    const uint64_t xb = x_dtype == BL_DTYPE_BF16 ? 2 : 4;
+    rs.push_back({(uintptr_t)d.x, (uintptr_t)d.x + (uint64_t)d.T * d.K * xb, false});
+    rs.push_back({(uintptr_t)d.xq, (uintptr_t)d.xq + (uint64_t)d.T * ke, true});
+    rs.push_back({(uintptr_t)d.x_scale, (uintptr_t)d.x_scale + (uint64_t)d.T * 4, true});
+    const int c = a.count++;
+    a.x[c] = d.x;
+    a.xq[c] = d.xq;
+    a.xs[c] = d.x_scale;
+    a.T[c] = (int32_t)d.T;
+    a.K[c] = (int32_t)d.K;
+    a.block0[c] = (int32_t)blocks;
+    blocks += (d.T + 3) / 4;
+    if (blocks > INT32_MAX) return BL_EINVAL;
+  }
+  a.block0[a.count] = (int32_t)blocks;
+  // inputs may be shared or overlap; an output may overlap nothing
+  std::sort(rs.begin(), rs.end(), [](const Rg& p, const Rg& q) { return p.lo < q.lo; });
+  uintptr_t out_hi = 0, any_hi = 0;
+  for (const Rg& r : rs) {
+    if (r.lo < out_hi || (r.out && r.lo < any_hi)) return BL_EINVAL;
+    any_hi = std::max(any_hi, r.hi);
+    if (r.out) out_hi = std::max(out_hi, r.hi);
+  }
+  if (a.count == 0) return BL_OK;
+  return status_of(bl::launch_act_quant_group(a, x_dtype == BL_DTYPE_BF16, lift_M,
+                                              (hipStream_t)stream));
 }
 
 int bitlinear_fwd(const int8_t* xq, const float* x_scale, int64_t T, int64_t K,

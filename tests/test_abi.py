@@ -460,6 +460,44 @@ def test_gemm_group_plan_and_rejects_before_launch(L):
     assert L.bitlinear_gemm_group(TB, bad, None) == -22
 
 
+def _qdesc(L, slot, **kw):
+    """A grouped-quantization descriptor whose buffers sit in their own 1 GiB slots."""
+    base = FAKE + slot * 16 * GB
+    a = dict(x=base, T=5, K=512, xq=base + GB, x_scale=base + 2 * GB)
+    a.update(kw)
+    return L.BlQuantDesc(**a)
+
+
+def _qgroup(L, descs, dtype=1, lift=0):
+    return L.act_quant_i8_group((L.BlQuantDesc * len(descs))(*descs), dtype, lift, None)
+
+
+def test_act_quant_group_rejects_before_launch(L):
+    """act_quant_i8's rules per matrix, 1..16 matrices, outputs overlapping nothing; groups with
+    nothing to do return OK without touching the runtime."""
+    assert _qgroup(L, [_qdesc(L, 0, T=0, x=None, xq=None, x_scale=None)]) == 0
+    assert _qgroup(L, [_qdesc(L, i, T=0) for i in range(16)]) == 0
+    assert _qgroup(L, [_qdesc(L, i, T=0) for i in range(17)]) == -22
+    lib = L.lib()
+    assert lib.act_quant_i8_group(None, 1, 1, 0, None) == -22
+    assert lib.act_quant_i8_group((L.BlQuantDesc * 1)(_qdesc(L, 0)), 0, 1, 0, None) == -22
+    assert _qgroup(L, [_qdesc(L, 0)], dtype=7) == -95
+    assert _qgroup(L, [_qdesc(L, 0)], lift=4) == -22
+    assert _qgroup(L, [_qdesc(L, 0, K=520)], lift=16) == -22
+    assert _qgroup(L, [_qdesc(L, 0, K=12)]) == -22
+    assert _qgroup(L, [_qdesc(L, 0, T=-1)]) == -22
+    assert _qgroup(L, [_qdesc(L, 0), _qdesc(L, 1, x=FAKE + 16 * GB + 8)]) == -22
+    assert _qgroup(L, [_qdesc(L, 0, xq=FAKE + GB + 4)]) == -22
+    assert _qgroup(L, [_qdesc(L, 0, x_scale=FAKE + 2 * GB + 2)]) == -22
+    # outputs may not overlap an input or another output (checked before anything is launched)
+    a = _qdesc(L, 0)
+    assert _qgroup(L, [a, _qdesc(L, 1, xq=a.xq)]) == -22
+    assert _qgroup(L, [a, _qdesc(L, 1, xq=a.xq + 5 * 512 - 16)]) == -22
+    assert _qgroup(L, [a, _qdesc(L, 1, x_scale=a.x + 64)]) == -22
+    assert _qgroup(L, [_qdesc(L, 0, xq=FAKE + 1024)]) == -22         # own xq inside own x
+    assert _qgroup(L, [a, _qdesc(L, 1, x_scale=a.x_scale + 16)]) == -22
+
+
 def _xdesc(L, **kw):
     P = FAKE
     a = dict(x=P, T=4, K=256, codes=P, meta=P, gamma=P, n=100, y=P, acc_opt=None)
