@@ -14,10 +14,11 @@ metric: decode weight GB/s = packed weight bytes streamed per step / step time.
 
 Also in the same JSON line:
   roofline      for the grouped GEMV kernel: algorithmic bytes per launch / mean launch duration,
-                the durations taken with HIP events on the launch stream around every grouped
-                launch of eager steps run right after the timed region; HBM traffic per launch
-                from the committed rocprofv3 counter summary when it was taken on the current
-                kernel source (else null)
+                the durations taken with HIP events on the launch stream around back-to-back
+                launches of each T's group right after the timed region (single launches with
+                events around each are reported beside them); HBM traffic per launch from the
+                committed rocprofv3 counter summary when it was taken on the current kernel
+                source (else null)
   prefill       4096 x 4096 -> 11008 2:4 GEMM (Student-t activations): dense-equivalent int8 TOPS
   six_eight, fourteen_sixteen
                 (2N-2):2N through overlapping 2:4 windows vs the dense path, 2048 x 4096 -> 4096
@@ -848,7 +849,9 @@ def main():
     log(f"decode step {ms_per_step:.3f} ms -> {value:.1f} GB/s of packed weights")
     D.last_ms_per_step = ms_per_step
 
-    # grouped-GEMV launch durations: HIP events on the launch stream, eager steps
+    # grouped-GEMV launch durations in isolation: HIP events on the launch stream around every
+    # grouped launch of eager steps (each measurement also holds the events' own dispatch
+    # overhead, several microseconds)
     per_T = {T: [] for T in DECODE_T}
     for _ in range(max(1, min(args.steps, 10))):
         events = {T: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -857,19 +860,13 @@ def main():
         torch.cuda.synchronize()
         for T in DECODE_T:
             per_T[T].append(events[T][0].elapsed_time(events[T][1]) * 1e-3)
-    mean_t = {T: float(np.mean(per_T[T])) for T in DECODE_T}
+    iso_t = {T: float(np.mean(per_T[T])) for T in DECODE_T}
     algo = {T: D.algorithmic_bytes(T) for T in DECODE_T}
-    achieved = sum(algo.values()) / sum(mean_t.values()) / 1e9
-    traffic = measured_traffic()
-    per_T_out = {str(T): {"launch_us": round(mean_t[T] * 1e6, 2),
-                          "algorithmic_bytes": algo[T],
-                          "GBps": round(algo[T] / mean_t[T] / 1e9, 1)} for T in DECODE_T}
-    log(f"grouped GEMV: " + ", ".join(f"T={T} {mean_t[T] * 1e6:.1f} us" for T in DECODE_T) +
-        f" -> {achieved:.1f} GB/s algorithmic")
 
     # layer stream: the grouped launch repeated back to back on already quantized activations
-    # (the steady state of a long decode), weight bytes / (last end - first start)
-    layer_stream = {}
+    # (the steady state of a long decode, and how the launches run inside the timed graph), HIP
+    # events on the launch stream around LAYER_STREAM_LAUNCHES launches: the mean launch duration
+    layer_stream, mean_t = {}, {}
     for T in DECODE_T:
         for _ in range(3):
             D.groups[T]()
@@ -880,12 +877,22 @@ def main():
         e1.record()
         torch.cuda.synchronize()
         t = e0.elapsed_time(e1) * 1e-3 / LAYER_STREAM_LAUNCHES
+        mean_t[T] = t
         layer_stream[str(T)] = {"launch_us": round(t * 1e6, 2),
                                 "weight_GBps": round(D.packed_bytes / t / 1e9, 1),
                                 "algorithmic_GBps": round(algo[T] / t / 1e9, 1),
                                 "frac": round(algo[T] / t / 1e9 / HBM_PEAK_GBS, 4)}
     log("layer stream: " + ", ".join(f"T={T} {layer_stream[str(T)]['algorithmic_GBps']} GB/s"
                                      for T in DECODE_T))
+    achieved = sum(algo.values()) / sum(mean_t.values()) / 1e9
+    traffic = measured_traffic()
+    per_T_out = {str(T): {"launch_us": round(mean_t[T] * 1e6, 2),
+                          "isolated_launch_us": round(iso_t[T] * 1e6, 2),
+                          "algorithmic_bytes": algo[T],
+                          "GBps": round(algo[T] / mean_t[T] / 1e9, 1)} for T in DECODE_T}
+    log(f"grouped GEMV: " + ", ".join(f"T={T} {mean_t[T] * 1e6:.1f} us (isolated "
+                                      f"{iso_t[T] * 1e6:.1f})" for T in DECODE_T) +
+        f" -> {achieved:.1f} GB/s algorithmic")
 
     out = {
         "metric": "decode weight GB/s", "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
