@@ -93,3 +93,18 @@ def test_quant_group_shared_input_and_graph_replay():
         for xq, sc in res:
             assert np.array_equal(host(xq), want[0][0]), "graph replay differs"
             assert np.array_equal(f32_bits(host(sc)), f32_bits(want[0][1]))
+
+
+def test_quant_group_training_step_sizes_sampled():
+    """The training step's two activation matrices (8192 x 3200 and 8192 x 8640, bf16) in one
+    group; 48 sampled rows of each against the oracle (every row is quantized on its own, so a
+    sampled row is an exact check), plus the first and last rows."""
+    T = 8192
+    hs, ds = _matrices([(T, 3200), (T, 8640)], "bf16", seed=17)
+    outs = S.act_quant_group(ds)
+    g = rng(18)
+    for x, (xq, sc) in zip(hs, outs):
+        rows = np.unique(np.concatenate([[0, T - 1], g.integers(0, T, 48)]))
+        q_ref, s_ref = O.act_quant(x[rows], 0)
+        assert np.array_equal(host(xq)[rows], q_ref)
+        assert np.array_equal(f32_bits(host(sc))[rows], f32_bits(s_ref))
