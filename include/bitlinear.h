@@ -97,7 +97,10 @@ int bitlinear_packed_bytes(int64_t n, int64_t K, int N, int M, int layout, size_
 /* Mask + ternarize + pack one fp32 master W[n][K] (row-major, nn.Linear out x in).
  * Writes codes[codes_bytes], meta[meta_bytes] (SPARSE; pass NULL for DENSE2) and gamma[1]
  * (device fp32), all in the packed layout above.  ws is scratch of at least ws_bytes (from
- * bitlinear_packed_bytes); its contents on entry do not matter.  W is only read. */
+ * bitlinear_packed_bytes, the same for every shape); its contents on entry do not matter.  W is
+ * only read.  Three launches: fp64 partial sums of |W|; gamma, certified by a rigorous bound of
+ * the fp64 sum, with an exact integer pass over W only when the exact mean lies too close to an
+ * fp32 rounding boundary for the bound to decide; the packing itself. */
 int bitlinear_pack(const float* W, int64_t n, int64_t K, int N, int M, int layout, uint8_t* codes,
                    uint8_t* meta, float* gamma, void* ws, size_t ws_bytes, void* stream);
 
@@ -141,19 +144,20 @@ int bitlinear_fwd(const int8_t* xq, const float* x_scale, int64_t T, int64_t K,
 /* ---------------------------------------------------------------------------------------------
  * Grouped pack: the bitlinear_pack calls of several masters (a training step re-packs every
  * master of a layer set; Sparse-BitNet technical summary, the mask is recomputed at each step) in
- * two launches instead of two per master.
+ * three launches instead of three per master.
  *
  * Each master's gamma, codes and meta are exactly bitlinear_pack's, bit for bit.  One launch
- * takes the partial sums of |W| of every master; the other masks, ternarizes and packs every
- * tile of every master, the masters read last by the first launch first (they are still in the
- * last-level cache).  All masters share (N, M, layout); each follows bitlinear_pack's shape and
+ * takes the partial sums of |W| of every master, one decides every master's gamma (the exact pass
+ * over a master runs only where the fp64 bound cannot decide its rounding), and the last masks,
+ * ternarizes and packs every tile of every master, the masters read last by the first launch
+ * first (they are still in the last-level cache).  All masters share (N, M, layout); each follows bitlinear_pack's shape and
  * alignment rules.  Masters may be shared or overlap; outputs (codes, meta, gamma) must not
  * overlap each other or any master (BL_EINVAL).  1 <= count <= 4096.
  *
  * Use: bitlinear_pack_group_plan sizes the table and workspace; bitlinear_pack_group_build writes
  * the table (16-byte aligned device memory, caller-owned) for one workspace (256-byte aligned,
  * caller-owned, contents on entry irrelevant) and synchronizes `stream`: build once, outside any
- * graph capture; bitlinear_pack_group enqueues the two launches (asynchronous, stream-ordered,
+ * graph capture; bitlinear_pack_group enqueues the three launches (asynchronous, stream-ordered,
  * capturable).  The table keeps the descriptors' pointers; masters are read at launch time, so
  * updated masters in the same buffers need no rebuild.  Launches sharing a workspace must be
  * ordered on one stream.  A table of another N:M or layout is ignored (nothing is written).

@@ -304,6 +304,22 @@ def _ptr(t) -> Optional[int]:
     return None if t is None else t.data_ptr()
 
 
+def _need(t, dtype, numel: int, device, name: str) -> None:
+    """Raise unless t is a contiguous CUDA tensor of `dtype` on `device` with at least `numel`
+    elements: the C ABI receives bare pointers and cannot check sizes, so a short or foreign
+    buffer would be read or written out of bounds by the kernels."""
+    if t is None:
+        raise ValueError(f"{name}: buffer missing")
+    if not t.is_cuda or t.device != device:
+        raise ValueError(f"{name}: must be a CUDA tensor on {device}, got {t.device}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name}: dtype must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    if t.numel() < numel:
+        raise ValueError(f"{name}: needs at least {numel} elements, got {t.numel()}")
+
+
 def packed_bytes(n: int, K: int, N: int = 2, M: int = 4, layout: int = BL_LAYOUT_SPARSE):
     st, cb, mb, ke, ws = bitlinear_packed_bytes(n, K, N, M, layout)
     _check(st, "bitlinear_packed_bytes")
@@ -328,6 +344,13 @@ def pack(W, N: int = 2, M: int = 4, layout: int = BL_LAYOUT_SPARSE, out=None, ws
         codes, meta, gamma = out
     if ws is None:
         ws = torch.empty(wsb, dtype=torch.uint8, device=W.device)
+    _need(codes, torch.uint8, cb, W.device, "codes")
+    if mb:
+        _need(meta, torch.uint8, mb, W.device, "meta")
+    elif meta is not None:
+        raise ValueError("meta: must be None for the dense 2-bit layout")
+    _need(gamma, torch.float32, 1, W.device, "gamma")
+    _need(ws, torch.uint8, wsb, W.device, "ws")
     _check(bitlinear_pack(W.data_ptr(), n, K, N, M, layout, codes.data_ptr(), _ptr(meta),
                           gamma.data_ptr(), ws.data_ptr(), ws.numel(), _stream()), "bitlinear_pack")
     return codes, meta, gamma
@@ -348,6 +371,8 @@ def act_quant(x, lift_M: int = 0, out=None):
         scale = torch.empty(max(T, 4), dtype=torch.float32, device=x.device)[:T]
     else:
         xq, scale = out
+    _need(xq, torch.int8, T * ke, x.device, "xq")
+    _need(scale, torch.float32, T, x.device, "scale")
     _check(act_quant_i8(x.data_ptr(), dt, T, K, lift_M, xq.data_ptr(), scale.data_ptr(), _stream()),
            "act_quant_i8")
     return xq, scale
@@ -373,6 +398,8 @@ def act_quant_group(xs, lift_M: int = 0, outs=None):
             scale = torch.empty(max(T, 4), dtype=torch.float32, device=x.device)[:T]
         else:
             xq, scale = outs[i]
+            _need(xq, torch.int8, T * ke, x.device, f"outs[{i}] xq")
+            _need(scale, torch.float32, T, x.device, f"outs[{i}] scale")
         res.append((xq, scale))
         arr[i] = BlQuantDesc(_ptr(x), T, K, _ptr(xq), _ptr(scale))
     _check(act_quant_i8_group(arr, dt, lift_M, _stream()), "act_quant_i8_group")
@@ -384,11 +411,26 @@ def fwd(xq, scale, K: int, codes, meta, gamma, n: int, N: int = 2, M: int = 4,
     """y[T][n] fp32 from int8 activations and packed weights; optionally also int32 acc."""
     import torch
     T = xq.shape[0]
+    cb, mb, ke, _ = packed_bytes(n, K, N, M, layout)
+    dev = xq.device
+    if xq.dim() != 2 or xq.shape[1] != ke:
+        raise ValueError(f"xq: must be [T][{ke}] (the packed K axis of K = {K}), got {tuple(xq.shape)}")
+    _need(xq, torch.int8, T * ke, dev, "xq")
+    _need(scale, torch.float32, T, dev, "scale")
+    _need(codes, torch.uint8, cb, dev, "codes")
+    if mb:
+        _need(meta, torch.uint8, mb, dev, "meta")
+    elif meta is not None:
+        raise ValueError("meta: must be None for the dense 2-bit layout")
+    _need(gamma, torch.float32, 1, dev, "gamma")
     if out is None:
-        y = torch.empty((T, n), dtype=torch.float32, device=xq.device)
-        acc = torch.empty((T, n), dtype=torch.int32, device=xq.device) if want_acc else None
+        y = torch.empty((T, n), dtype=torch.float32, device=dev)
+        acc = torch.empty((T, n), dtype=torch.int32, device=dev) if want_acc else None
     else:
         y, acc = out
+    _need(y, torch.float32, T * n, dev, "y")
+    if acc is not None:
+        _need(acc, torch.int32, T * n, dev, "acc")
     _check(bitlinear_fwd(xq.data_ptr(), scale.data_ptr(), T, K, codes.data_ptr(), _ptr(meta),
                          gamma.data_ptr(), N, M, layout, n, y.data_ptr(), _ptr(acc), _stream()),
            "bitlinear_fwd")

@@ -78,6 +78,40 @@ int check_fwd(const int8_t* xq, const float* x_scale, int64_t T, int64_t K, cons
   return BL_OK;
 }
 
+// Output buffers (y, acc_opt) of a set of projections may not overlap each other or any input
+// (xq, x_scale, codes, meta, gamma); inputs may be shared or overlap.  `in_bytes_per_token`: bytes
+// of one token row of xq per K_eff position (1 for int8 rows, 2 for the fused group's bf16 rows,
+// whose x_scale is not read).  T == 0 projections touch nothing.
+int check_fwd_overlaps(const bl_fwd_desc* d, int64_t count, int N, int M, int layout,
+                       int in_bytes_per_token) {
+  struct Rg { uintptr_t lo, hi; bool out; };
+  std::vector<Rg> rs;
+  for (int64_t i = 0; i < count; ++i) {
+    const bl_fwd_desc& q = d[i];
+    if (q.T == 0) continue;
+    size_t cb = 0, mb = 0;
+    int64_t ke = 0;
+    bitlinear_packed_bytes(q.n, q.K, N, M, layout, &cb, &mb, &ke, nullptr);
+    rs.push_back({(uintptr_t)q.xq, (uintptr_t)q.xq + (uint64_t)q.T * ke * in_bytes_per_token, false});
+    if (in_bytes_per_token == 1)
+      rs.push_back({(uintptr_t)q.x_scale, (uintptr_t)q.x_scale + (uint64_t)q.T * 4, false});
+    rs.push_back({(uintptr_t)q.codes, (uintptr_t)q.codes + cb, false});
+    if (mb) rs.push_back({(uintptr_t)q.meta, (uintptr_t)q.meta + mb, false});
+    rs.push_back({(uintptr_t)q.gamma, (uintptr_t)q.gamma + 4, false});
+    rs.push_back({(uintptr_t)q.y, (uintptr_t)q.y + (uint64_t)q.T * q.n * 4, true});
+    if (q.acc_opt)
+      rs.push_back({(uintptr_t)q.acc_opt, (uintptr_t)q.acc_opt + (uint64_t)q.T * q.n * 4, true});
+  }
+  std::sort(rs.begin(), rs.end(), [](const Rg& a, const Rg& b) { return a.lo < b.lo; });
+  uintptr_t out_hi = 0, any_hi = 0;
+  for (const Rg& r : rs) {
+    if (r.lo < out_hi || (r.out && r.lo < any_hi)) return BL_EINVAL;
+    any_hi = std::max(any_hi, r.hi);
+    if (r.out) out_hi = std::max(out_hi, r.hi);
+  }
+  return BL_OK;
+}
+
 // Work-item plan of a group.  Items are runs of kGroupPanels panels of one projection; the hardware
 // hands workgroup b to XCD b % kXcds, so the plan cuts the projections' items (in projection order)
 // into kXcds contiguous runs of about equal weight bytes -- each projection's activation rows then
@@ -85,7 +119,7 @@ int check_fwd(const int8_t* xq, const float* x_scale, int64_t T, int64_t K, cons
 // on short items.  Launch position b = p * kXcds + x holds item p of XCD x (padded with empty
 // items).
 int plan_group(const bl_fwd_desc* d, int64_t count, int N, int M, int layout,
-               std::vector<bl::GroupItem>* plan) {
+               std::vector<bl::GroupItem>* plan, int in_bytes_per_token) {
   if (!d || count < 1 || count > (1 << 24)) return BL_EINVAL;
   struct It { uint32_t layer, panel0; uint64_t cost; };
   std::vector<It> items;
@@ -96,6 +130,13 @@ int plan_group(const bl_fwd_desc* d, int64_t count, int N, int M, int layout,
                              d[i].gamma, N, M, layout, d[i].n, d[i].y, d[i].acc_opt, &ke);
     if (st != BL_OK) return st;
     if (d[i].T > 32) return BL_EINVAL;
+  }
+  {
+    const int st = check_fwd_overlaps(d, count, N, M, layout, in_bytes_per_token);
+    if (st != BL_OK) return st;
+  }
+  for (int64_t i = 0; i < count; ++i) {
+    const int64_t ke = keff_of(d[i].K, M, layout);
     if (d[i].T == 0) continue;
     const int64_t panels = (d[i].n + 31) / 32;
     for (int64_t p0 = 0; p0 < panels; p0 += bl::kGroupPanels) {
@@ -132,11 +173,22 @@ size_t group_table_bytes(int64_t count, size_t items) {
   return (b + 15) / 16 * 16;
 }
 
+// Table size and work items of a group; fused: the descriptors' xq are bf16 rows.
+int group_sizes(const bl_fwd_desc* descs, int64_t count, int N, int M, int layout, int fused,
+                size_t* table_bytes, int64_t* work_items) {
+  std::vector<bl::GroupItem> plan;
+  const int st = plan_group(descs, count, N, M, layout, &plan, fused ? 2 : 1);
+  if (st != BL_OK) return st;
+  if (table_bytes) *table_bytes = group_table_bytes(count, plan.size());
+  if (work_items) *work_items = (int64_t)plan.size();
+  return BL_OK;
+}
+
 // Validates the group and writes its device table; fused: the descriptors' xq are bf16 rows.
 int group_build(const bl_fwd_desc* descs, int64_t count, int N, int M, int layout, int fused,
                 void* table, size_t table_bytes, void* stream) {
   std::vector<bl::GroupItem> plan;
-  const int st = plan_group(descs, count, N, M, layout, &plan);
+  const int st = plan_group(descs, count, N, M, layout, &plan, fused ? 2 : 1);
   if (st != BL_OK) return st;
   const size_t bytes = group_table_bytes(count, plan.size());
   if (!aligned16(table)) return BL_EINVAL;
@@ -829,12 +881,7 @@ int bitlinear_fwd(const int8_t* xq, const float* x_scale, int64_t T, int64_t K,
 
 int bitlinear_group_table_bytes(const bl_fwd_desc* descs, int64_t count, int N, int M, int layout,
                                 size_t* table_bytes, int64_t* work_items) {
-  std::vector<bl::GroupItem> plan;
-  const int st = plan_group(descs, count, N, M, layout, &plan);
-  if (st != BL_OK) return st;
-  if (table_bytes) *table_bytes = group_table_bytes(count, plan.size());
-  if (work_items) *work_items = (int64_t)plan.size();
-  return BL_OK;
+  return group_sizes(descs, count, N, M, layout, 0, table_bytes, work_items);
 }
 
 int bitlinear_group_build(const bl_fwd_desc* descs, int64_t count, int N, int M, int layout,
@@ -858,7 +905,7 @@ int bitlinear_group_fused_table_bytes(const bl_fwd_x_desc* descs, int64_t count,
   std::vector<bl_fwd_desc> plain;
   const int st = fused_as_plain(descs, count, M, layout, &plain);
   if (st != BL_OK) return st;
-  return bitlinear_group_table_bytes(plain.data(), count, N, M, layout, table_bytes, work_items);
+  return group_sizes(plain.data(), count, N, M, layout, 1, table_bytes, work_items);
 }
 
 int bitlinear_group_fused_build(const bl_fwd_x_desc* descs, int64_t count, int N, int M,

@@ -6,10 +6,13 @@
 
 namespace bl {
 
-// Workspace of bitlinear_pack: per-block fp64 partial sums of |W|, then the ternary threshold.
+// Workspace of bitlinear_pack: per-block fp64 partial sums of |W|, the exact fallback's nine
+// accumulator words (one 128-byte line each), then gamma, the ternary threshold, a flag and a
+// counter (256-byte multiple).
 constexpr int kGammaBlocks = 1024;
 constexpr int kGammaThreads = 256;
-constexpr size_t kPackWsBytes = kGammaBlocks * sizeof(double) + 64;
+constexpr int kExactWords = 9;
+constexpr size_t kPackWsBytes = (kGammaBlocks * sizeof(double) + kExactWords * 128 + 16 + 255) / 256 * 256;
 
 hipError_t launch_pack(const float* W, int64_t n, int64_t K, int N, int M, int layout,
                        uint32_t* codes, uint32_t* meta, float* gamma, void* ws, hipStream_t s);

@@ -6,15 +6,19 @@
 // in each M-group (same summary, Maskering) and (2N-2):2N groups -- 6:8, 14:16 -- are rewritten
 // as N-1 overlapping 2:4 windows (SlideSparse abstract, Sliding Window Decomposition).
 //
-// Two launches, both on the caller's stream:
-//   1. gamma_partial_kernel   fp64 partial sums of |w| (HBM-bound read of W)
-//   2. pack_kernel            every block first derives gamma from the partials (same data, same
-//                             order, so every block gets the same bits): it certifies the fp32
-//                             rounding of the exact mean with a rigorous error bound, and only
-//                             when the bound cannot decide falls back to an exact exponent-binned
-//                             integer sum over W; then the ternary threshold tau.  Its tile of W
-//                             (mostly from the 256 MB last-level cache) is already in flight
-//                             meanwhile.  Mask, codes by |w| >= tau, slots assembled in LDS,
+// Three launches, all on the caller's stream:
+//   1. gamma_partial_kernel   fp64 partial sums of |w| (HBM-bound read of W); it also clears the
+//                             exact accumulator and the block counter of launch 2
+//   2. gamma_exact_kernel     every block sums the partials in one fixed order (all get the same
+//                             bits) and certifies the fp32 rounding of the exact mean with a
+//                             rigorous error bound.  Certified (the common case): block 0 stores
+//                             gamma and the ternary threshold tau, and every block exits.
+//                             Otherwise the blocks sum |W| exactly as integers (24-bit
+//                             significands shifted to a 2^-149 fixed point, kept as carry-free
+//                             32-bit words in 64-bit accumulators) and the last block to finish
+//                             rounds the exact mean to fp32 and stores gamma and tau: one extra
+//                             pass over W, once per master
+//   3. pack_kernel            reads tau; mask, codes by |w| >= tau, slots assembled in LDS,
 //                             coalesced dword stores.
 #include "device_common.hpp"
 #include "launch.hpp"
@@ -22,9 +26,18 @@
 
 namespace bl {
 
+
+// The exact fixed-point sum: |w| = m * 2^(max(e,1) - 150) with a 24-bit significand m is
+// m << (max(e,1) - 1) units of 2^-149, at most 24 + 253 bits, so word kExactWords - 1 = 8 is the
+// highest a piece reaches.
 struct PackWs {
-  double partial[kGammaBlocks];
-  uint32_t exact_used;  // 1 when the exact fallback decided gamma (diagnostic, written by block 0)
+  double partial[kGammaBlocks];      // fp64 partial sums of |w|, one per partial-sum block
+  // exact fallback: sum_i words[i][0] * 2^(32 i) units of 2^-149; one 128-byte line per word, so
+  // the blocks' atomics on different words do not queue on one cache line
+  unsigned long long words[kExactWords][16];
+  float gamma, tau;                  // gamma and the ternary threshold, read by every pack block
+  uint32_t exact_used;               // 1 when the exact fallback decided gamma (diagnostic)
+  uint32_t done;                     // exact fallback: blocks that have added their words
 };
 static_assert(sizeof(PackWs) <= kPackWsBytes, "pack workspace");
 
@@ -59,36 +72,32 @@ __device__ __forceinline__ void gamma_partial_block(const float4* __restrict__ W
   }
 }
 
-__global__ __launch_bounds__(kGammaThreads) void gamma_partial_kernel(const float4* __restrict__ W4,
-                                                                      int64_t n4,
-                                                                      double* __restrict__ partial) {
-  gamma_partial_block(W4, n4, partial, blockIdx.x);
+// Block 0 also clears the exact accumulator and the block counter: the exact launch may add to
+// them, and this launch has completed before it starts.
+__device__ __forceinline__ void clear_exact_state(PackWs* __restrict__ ws, int blk) {
+  if (blk == 0 && threadIdx.x < kExactWords) ws->words[threadIdx.x][0] = 0ull;
+  if (blk == 0 && threadIdx.x == kExactWords) ws->done = 0u;
 }
 
-// Round (sum_e bins[e] * 2^(max(e,1)-150)) / count to the nearest fp32, ties to even, exactly.
-// bins[e] is the integer sum of the 24-bit significands of the magnitudes with biased exponent e.
-__device__ float exact_mean_from_bins(const unsigned long long* bins, uint64_t count) {
-  constexpr int L = 10;  // 320-bit integer in units of 2^-149 (sum < 2^310)
+__global__ __launch_bounds__(kGammaThreads) void gamma_partial_kernel(const float4* __restrict__ W4,
+                                                                      int64_t n4,
+                                                                      PackWs* __restrict__ ws) {
+  clear_exact_state(ws, blockIdx.x);
+  gamma_partial_block(W4, n4, ws->partial, blockIdx.x);
+}
+
+// Round (sum_i words[i] * 2^(32 i - 149)) / count to the nearest fp32, ties to even, exactly.
+// Each word is a 64-bit sum of 32-bit pieces (carry-free form); the carries are taken here.
+__device__ float exact_mean_from_words(const unsigned long long* words, uint64_t count) {
+  constexpr int L = 11;  // 352-bit integer in units of 2^-149
   uint32_t lim[L];
-  for (int i = 0; i < L; ++i) lim[i] = 0;
-  for (int e = 0; e < 255; ++e) {
-    unsigned long long v = bins[e];
-    if (!v) continue;
-    const int sh = (e > 0 ? e : 1) - 1;
-    int w = sh >> 5;
-    const int b = sh & 31;
-    // v << b spans at most 88 bits: three 32-bit words starting at limb w
-    uint32_t part[3];
-    part[0] = (uint32_t)(v << b);
-    part[1] = (uint32_t)((b ? (v >> (32 - b)) : (v >> 32)) & 0xFFFFFFFFull);
-    part[2] = (uint32_t)(b ? (v >> (64 - b)) : 0ull);
-    uint64_t carry = 0;
-    for (int k = 0; w + k < L; ++k) {
-      uint64_t add = (k < 3 ? part[k] : 0u) + carry + (uint64_t)lim[w + k];
-      lim[w + k] = (uint32_t)add;
-      carry = add >> 32;
-      if (k >= 2 && carry == 0) break;
-    }
+  uint64_t carry = 0;
+  for (int i = 0; i < L; ++i) {
+    const unsigned long long w = i < kExactWords ? words[i] : 0ull;
+    // lim[i] = low word of (w + high word of the previous column + carry)
+    const uint64_t lo = (uint64_t)(uint32_t)w + carry;
+    lim[i] = (uint32_t)lo;
+    carry = (lo >> 32) + (w >> 32);
   }
   // long division by count (< 2^32)
   uint32_t q[L];
@@ -137,44 +146,34 @@ __device__ float ternary_threshold(float gamma) {
   return f;
 }
 
-// gamma and tau from the partial sums, computed by one whole block (every pack block runs it and
-// gets the same bits).  Returns through LDS: *g_sh, *tau_sh, *exact_sh.
-// `v` is this thread's sum of partials threadIdx.x + i * NT (loaded by the caller, ahead of its
-// own tile loads, so waiting for them does not wait for the tile).
-// Rare path of block_gamma: the exact mean of |W| by the whole block (exponent-binned integer
-// sums in LDS), kept out of line so the common path stays small.  Every thread of the block calls
-// it; thread 0 writes *g_sh.
-template <int NT>
-__device__ __noinline__ void exact_gamma_block(const float* __restrict__ W, int64_t count,
-                                               float* g_sh, unsigned long long* bins_sh) {
-  for (int i = threadIdx.x; i < 256; i += NT) bins_sh[i] = 0ull;
-  __syncthreads();
-  for (int64_t i = threadIdx.x; i < count; i += NT) {
-    const uint32_t b = __float_as_uint(W[i]) & 0x7FFFFFFFu;
-    const uint32_t e = b >> 23;
-    const uint32_t m = (b & 0x7FFFFFu) | (e ? 0x800000u : 0u);
-    atomicAdd(&bins_sh[e], (unsigned long long)m);
-  }
-  __syncthreads();
-  if (threadIdx.x == 0) *g_sh = exact_mean_from_bins(bins_sh, (uint64_t)count);
-}
+constexpr int kExactThreads = 1024;  // 16 waves: four per SIMD for the rare exact pass
+constexpr int kExactBlocks = 256;    // gamma_exact_kernel: blocks per master (one per CU; each
+                                     // adds its word sums with one atomic per word)
+constexpr int kExactLoads = 2;       // float4 loads in flight per thread in the exact pass
 
-template <int NT>
-__device__ __forceinline__ void block_gamma(double v, const float* __restrict__ W, int64_t count, float* g_sh,
-                            float* tau_sh, int* exact_sh, double* red_sh,
-                            unsigned long long* bins_sh) {
-  static_assert(kGammaBlocks % NT == 0 && NT % 64 == 0, "partials split evenly");
+// Certified fp32 rounding of mean |W| from the fp64 partial sums, computed by a whole block in one
+// fixed order (every block gets the same bits).  Returns 1 and *g when the rigorous error bound of
+// the fp64 sum decides the rounding (or the sum is 0), else 0.
+__device__ __forceinline__ int block_certify(const PackWs* __restrict__ ws, int64_t count,
+                                             float* __restrict__ g) {
+  static_assert(kGammaBlocks % kExactThreads == 0, "partials split evenly");
+  __shared__ double red_sh[kExactThreads / 64];
+  __shared__ float g_sh;
+  __shared__ int ok_sh;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  double v = 0.0;
+#pragma unroll
+  for (int i = 0; i < kGammaBlocks / kExactThreads; ++i) v += ws->partial[threadIdx.x + i * kExactThreads];
   v = wave_sum_f64(v);
   if (lane == 0) red_sh[wave] = v;
   __syncthreads();
   if (threadIdx.x == 0) {
     double S = 0.0;
-    for (int w = 0; w < NT / 64; ++w) S += red_sh[w];
+    for (int w = 0; w < kExactThreads / 64; ++w) S += red_sh[w];
     // longest chain of fp64 additions any |w| goes through: the partial kernel's per-thread
     // chains (at most 4 per float4 it reads, plus 2 to join its four chains), its wave butterfly
-    // (6) and block sum (4), then here the per-thread sum (kGammaBlocks / NT), the butterfly (6)
-    // and the block sum (NT / 64); 64 covers every fixed term
+    // (6) and block sum (4), then here the per-thread sum (kGammaBlocks / kExactThreads = 1),
+    // the butterfly (6) and the block sum (kExactThreads / 64 = 16); 64 covers every fixed term
     const int64_t n4 = count / 4;
     const int64_t per_thread = (n4 + (int64_t)kGammaBlocks * kGammaThreads - 1) / ((int64_t)kGammaBlocks * kGammaThreads);
     const double depth = 4.0 * (double)per_thread + 64.0;
@@ -184,15 +183,115 @@ __device__ __forceinline__ void block_gamma(double v, const float* __restrict__ 
     const double lo = (S - err) / cnt * (1.0 - 4.0 * u);
     const double hi = (S + err) / cnt * (1.0 + 4.0 * u);
     const float glo = (float)lo, ghi = (float)hi;
-    if (S == 0.0) { *exact_sh = 0; *g_sh = 0.f; }
-    else if (glo == ghi) { *exact_sh = 0; *g_sh = glo; }
-    else *exact_sh = 1;
+    if (S == 0.0) { ok_sh = 1; g_sh = 0.f; }
+    else if (glo == ghi) { ok_sh = 1; g_sh = glo; }
+    else ok_sh = 0;
   }
   __syncthreads();
-  if (*exact_sh)   // uniform; rare: the bound straddles an fp32 rounding boundary
-    exact_gamma_block<NT>(W, count, g_sh, bins_sh);
-  if (threadIdx.x == 0) *tau_sh = ternary_threshold(*g_sh);
+  *g = g_sh;
+  return ok_sh;
+}
+
+// The exact sum of |W| over this block's share (float4 i4 = blk * NT + tid, strided by the
+// master's blocks), added to ws->words; the last block to finish rounds the exact mean.
+// Each element's m << (max(e,1) - 1) is split into 32-bit pieces p0 (word w) and p1 (word w + 1);
+// a lane keeps one 64-bit sum per word, so no carry is taken until the end (every word sum stays
+// below count * 2^32 < 2^64).  Words no lane of the wave touches in an iteration are skipped.
+__device__ __forceinline__ void gamma_exact_block(const float* __restrict__ W, int64_t count, PackWs* __restrict__ ws,
+                                  float* __restrict__ gamma_out, int blk, int nblk) {
+  float g = 0.f;
+  if (block_certify(ws, count, &g)) {   // uniform across the block and the launch
+    if (blk == 0 && threadIdx.x == 0) {
+      ws->gamma = g;
+      ws->tau = ternary_threshold(g);
+      ws->exact_used = 0u;
+      gamma_out[0] = g;
+    }
+    return;
+  }
+  unsigned long long acc[kExactWords];
+#pragma unroll
+  for (int i = 0; i < kExactWords; ++i) acc[i] = 0ull;
+  typedef __attribute__((address_space(1))) const v4f g_v4f;
+  g_v4f* W4 = (g_v4f*)W;
+  const int64_t n4 = count / 4;
+  const int64_t stride = (int64_t)nblk * kExactThreads;
+  // kExactLoads float4 loads in flight per thread before any is used; then, per word that some
+  // lane of the wave touches, every element's piece for that word in one select chain
+  constexpr int U = kExactLoads;
+  constexpr int E = 4 * U;
+  for (int64_t base = (int64_t)blk * kExactThreads; base < n4; base += U * stride) {
+    v4f v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t i4 = base + u * stride + threadIdx.x;
+      v[u] = W4[min(i4, n4 - 1)];
+      if (i4 >= n4) v[u] = v4f{0.f, 0.f, 0.f, 0.f};
+    }
+    uint32_t wd[E], p0[E], p1[E];
+    uint32_t wlo = 0xFFu, whi = 0u;
+#pragma unroll
+    for (int j = 0; j < E; ++j) {
+      const float x = v[j / 4][j % 4];
+      const uint32_t b = __float_as_uint(x) & 0x7FFFFFFFu;
+      const uint32_t e = b >> 23;
+      const uint32_t m = (b & 0x7FFFFFu) | (e ? 0x800000u : 0u);
+      const uint32_t sh = (e ? e : 1u) - 1u;
+      const uint32_t bs = sh & 31u;
+      wd[j] = sh >> 5;
+      p0[j] = m << bs;
+      p1[j] = bs ? (m >> (32u - bs)) : 0u;
+      if (m) { wlo = min(wlo, wd[j]); whi = max(whi, wd[j] + 1u); }
+    }
+#pragma unroll
+    for (int i = 0; i < kExactWords; ++i) {
+      if (__ballot(wlo <= (uint32_t)i && (uint32_t)i <= whi) == 0ull) continue;   // uniform
+      uint64_t add = 0;
+#pragma unroll
+      for (int j = 0; j < E; ++j)
+        add += wd[j] == (uint32_t)i ? p0[j] : (wd[j] + 1u == (uint32_t)i ? p1[j] : 0u);
+      acc[i] += add;
+    }
+  }
+  // block sums per word, then one 64-bit atomic per word and block
+  __shared__ unsigned long long red[kExactThreads / 64][kExactWords];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int i = 0; i < kExactWords; ++i) {
+    unsigned long long x = acc[i];
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
+    if (lane == 0) red[wave][i] = x;
+  }
   __syncthreads();
+  if (threadIdx.x < kExactWords) {
+    unsigned long long x = 0ull;
+    for (int w = 0; w < kExactThreads / 64; ++w) x += red[w][threadIdx.x];
+    if (x) atomicAdd(&ws->words[threadIdx.x][0], x);
+  }
+  __shared__ int last_sh;
+  __threadfence();
+  __syncthreads();
+  if (threadIdx.x == 0) last_sh = atomicAdd(&ws->done, 1u) == (uint32_t)(nblk - 1);
+  __syncthreads();
+  if (last_sh && threadIdx.x == 0) {
+    __threadfence();
+    unsigned long long words[kExactWords];
+    for (int i = 0; i < kExactWords; ++i)
+      words[i] = __hip_atomic_load(&ws->words[i][0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const float ge = exact_mean_from_words(words, (uint64_t)count);
+    ws->gamma = ge;
+    ws->tau = ternary_threshold(ge);
+    ws->exact_used = 1u;
+    gamma_out[0] = ge;
+  }
+}
+
+__global__ __launch_bounds__(kExactThreads) void gamma_exact_kernel(const float* __restrict__ W,
+                                                                    int64_t count,
+                                                                    PackWs* __restrict__ ws,
+                                                                    float* __restrict__ gamma_out) {
+  gamma_exact_block(W, count, ws, gamma_out, blockIdx.x, gridDim.x);
 }
 
 constexpr int kPackKB = 256;  // dense K columns per pack tile
@@ -203,8 +302,7 @@ constexpr int kPackKB = 256;  // dense K columns per pack tile
 // layout (unit v = 32*u + r of the tile is dword base + v).
 template <int LAYOUT, int M>
 __device__ __forceinline__ void pack_tile(const float* __restrict__ W, int n, int K, int N,
-                                          int k_tiles, PackWs* __restrict__ ws,
-                                          float* __restrict__ gamma_out,
+                                          int k_tiles, const PackWs* __restrict__ ws,
                                           uint32_t* __restrict__ codes,
                                           uint32_t* __restrict__ meta, int blk) {
   constexpr bool SP = LAYOUT == kLayoutSparse;
@@ -216,10 +314,6 @@ __device__ __forceinline__ void pack_tile(const float* __restrict__ W, int n, in
   constexpr int UPR = SLOTS / 16;                                      // units per tile row
   __shared__ __attribute__((aligned(16))) float tile[32 * WS];
   __shared__ __attribute__((aligned(16))) uint8_t slots[32 * SS];
-  __shared__ double red_sh[4];
-  __shared__ unsigned long long bins_sh[256];
-  __shared__ float g_sh, tau_sh;
-  __shared__ int exact_sh;
 
   const int P = blk / k_tiles;
   const int kb = blk % k_tiles;
@@ -227,13 +321,9 @@ __device__ __forceinline__ void pack_tile(const float* __restrict__ W, int n, in
   const int r0 = P * kPanel;
   const int kw = min(kPackKB, K - k0);
 
-  // this thread's share of the gamma partial sums first (L2 hits), then all eight 16-byte tile
-  // loads before its first LDS store (addresses clamped into the matrix; out-of-range rows and
-  // columns are zeroed after the load)
-  double pv = 0.0;
-#pragma unroll
-  for (int i = 0; i < kGammaBlocks / 256; ++i) pv += ws->partial[threadIdx.x + i * 256];
-  asm volatile("" ::: "memory");
+  // all eight 16-byte tile loads before the first LDS store (addresses clamped into the matrix;
+  // out-of-range rows and columns are zeroed after the load)
+  const float tau = ws->tau;
   {
     const int c4 = threadIdx.x & 63;
     const bool col_ok = 4 * c4 < kw;
@@ -244,8 +334,6 @@ __device__ __forceinline__ void pack_tile(const float* __restrict__ W, int n, in
       const int row = i * 4 + (threadIdx.x >> 6);
       v[i] = *(const float4*)(W + (size_t)min(r0 + row, n - 1) * K + col);
     }
-    // gamma while the tile is in flight
-    block_gamma<256>(pv, W, (int64_t)n * K, &g_sh, &tau_sh, &exact_sh, red_sh, bins_sh);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int row = i * 4 + (threadIdx.x >> 6);
@@ -253,11 +341,6 @@ __device__ __forceinline__ void pack_tile(const float* __restrict__ W, int n, in
       *(float4*)&tile[row * WS + 4 * c4] = v[i];
     }
   }
-  if (blk == 0 && threadIdx.x == 0) {
-    gamma_out[0] = g_sh;
-    ws->exact_used = (uint32_t)exact_sh;
-  }
-  const float tau = tau_sh;
   __syncthreads();
 
   const int nkeep = SP ? NKEEP : N;
@@ -335,18 +418,18 @@ __device__ __forceinline__ void pack_tile(const float* __restrict__ W, int n, in
 
 template <int LAYOUT, int M>
 __global__ __launch_bounds__(256) void pack_kernel(const float* __restrict__ W, int n, int K, int N,
-                                                   int k_tiles, PackWs* __restrict__ ws,
-                                                   float* __restrict__ gamma_out,
+                                                   int k_tiles, const PackWs* __restrict__ ws,
                                                    uint32_t* __restrict__ codes,
                                                    uint32_t* __restrict__ meta) {
-  pack_tile<LAYOUT, M>(W, n, K, N, k_tiles, ws, gamma_out, codes, meta, blockIdx.x);
+  pack_tile<LAYOUT, M>(W, n, K, N, k_tiles, ws, codes, meta, blockIdx.x);
 }
 
 // ---------------------------------------------------------------------------------------------
-// Grouped pack: the bitlinear_pack calls of several masters in two launches, each tensor's blocks
-// running exactly the single call's arithmetic (so gamma, codes and meta are the same bits).
-// The partial-sum launch walks the tensors in table order and the pack launch in reverse, so
-// the tensors read last by the first launch -- still in the last-level cache -- are packed first.
+// Grouped pack: the bitlinear_pack calls of several masters in three launches, each tensor's
+// blocks running exactly the single call's arithmetic (so gamma, codes and meta are the same
+// bits).  The partial-sum launch walks the tensors in table order and the pack launch in reverse,
+// so the tensors read last by the first launch -- still in the last-level cache -- are packed
+// first.
 // ---------------------------------------------------------------------------------------------
 __global__ __launch_bounds__(kGammaThreads) void gamma_partial_group_kernel(
     const uint8_t* __restrict__ table) {
@@ -355,8 +438,21 @@ __global__ __launch_bounds__(kGammaThreads) void gamma_partial_group_kernel(
   const int b = blockIdx.x;
   if (b >= hd->count * kGammaBlocks) return;
   const PackGroupItem it = ((const PackGroupItem*)(table + sizeof(PackGroupHeader)))[b / kGammaBlocks];
+  clear_exact_state((PackWs*)it.ws, b % kGammaBlocks);
   gamma_partial_block((const float4*)it.W, (int64_t)it.n * it.K / 4, ((PackWs*)it.ws)->partial,
                       b % kGammaBlocks);
+}
+
+// kExactBlocks blocks per master, in table order (each exits at once unless its master is flagged).
+__global__ __launch_bounds__(kExactThreads) void gamma_exact_group_kernel(
+    const uint8_t* __restrict__ table) {
+  const PackGroupHeader* hd = (const PackGroupHeader*)table;
+  if (hd->magic != kPackGroupMagic) return;
+  const int b = blockIdx.x;
+  if (b >= hd->count * kExactBlocks) return;
+  const PackGroupItem it = ((const PackGroupItem*)(table + sizeof(PackGroupHeader)))[b / kExactBlocks];
+  gamma_exact_block(it.W, (int64_t)it.n * it.K, (PackWs*)it.ws, it.gamma, b % kExactBlocks,
+                    kExactBlocks);
 }
 
 template <int LAYOUT, int M>
@@ -373,7 +469,7 @@ __global__ __launch_bounds__(256) void pack_group_kernel(const uint8_t* __restri
     if (items[hd->count - 1 - mid].block0 <= b) lo = mid; else hi = mid - 1;
   }
   const PackGroupItem it = items[hd->count - 1 - lo];
-  pack_tile<LAYOUT, M>(it.W, it.n, it.K, hd->N, it.k_tiles, (PackWs*)it.ws, it.gamma, it.codes,
+  pack_tile<LAYOUT, M>(it.W, it.n, it.K, hd->N, it.k_tiles, (const PackWs*)it.ws, it.codes,
                        it.meta, b - it.block0);
 }
 
@@ -381,12 +477,13 @@ hipError_t launch_pack(const float* W, int64_t n, int64_t K, int N, int M, int l
                        uint32_t* codes, uint32_t* meta, float* gamma, void* ws_raw, hipStream_t s) {
   PackWs* ws = (PackWs*)ws_raw;
   const int64_t count = n * K;
-  gamma_partial_kernel<<<kGammaBlocks, kGammaThreads, 0, s>>>((const float4*)W, count / 4, ws->partial);
+  gamma_partial_kernel<<<kGammaBlocks, kGammaThreads, 0, s>>>((const float4*)W, count / 4, ws);
+  gamma_exact_kernel<<<kExactBlocks, kExactThreads, 0, s>>>(W, count, ws, gamma);
   const int panels = (int)((n + kPanel - 1) / kPanel);
   const int k_tiles = (int)((K + kPackKB - 1) / kPackKB);
   const dim3 grid((unsigned)(panels * k_tiles));
   auto run = [&](auto kern, uint32_t* mt) {
-    kern<<<grid, 256, 0, s>>>(W, (int)n, (int)K, N, k_tiles, ws, gamma, codes, mt);
+    kern<<<grid, 256, 0, s>>>(W, (int)n, (int)K, N, k_tiles, ws, codes, mt);
   };
   if (layout == kLayoutSparse) {
     if (M == 4) run(pack_kernel<kLayoutSparse, 4>, meta);
@@ -404,6 +501,7 @@ hipError_t launch_pack_group(const void* table, int64_t count, int64_t pack_bloc
                              int M, hipStream_t s) {
   const uint8_t* t = (const uint8_t*)table;
   gamma_partial_group_kernel<<<(unsigned)(count * kGammaBlocks), kGammaThreads, 0, s>>>(t);
+  gamma_exact_group_kernel<<<(unsigned)(count * kExactBlocks), kExactThreads, 0, s>>>(t);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const unsigned g = (unsigned)pack_blocks;

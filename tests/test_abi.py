@@ -140,15 +140,17 @@ def test_product_path_never_imports_oracle():
                 assert not re.search(r"\boracle\b", txt), f
 
 
-def _desc(L, **kw):
+def _desc(L, slot=0, **kw):
+    """A group descriptor: inputs share FAKE (allowed), the output sits in its own 16 GiB slot."""
     P = FAKE
-    a = dict(xq=P, x_scale=P, T=4, K=256, codes=P, meta=P, gamma=P, n=100, y=P, acc_opt=None)
+    a = dict(xq=P, x_scale=P, T=4, K=256, codes=P, meta=P, gamma=P, n=100,
+             y=FAKE + (slot + 1) * (16 << 30), acc_opt=None)
     a.update(kw)
     return L.BlFwdDesc(**a)
 
 
 def test_group_sizes_and_rejects_before_launch(L):
-    arr = (L.BlFwdDesc * 3)(_desc(L), _desc(L, n=6912, K=2560, T=16), _desc(L, T=0, xq=None))
+    arr = (L.BlFwdDesc * 3)(_desc(L), _desc(L, 1, n=6912, K=2560, T=16), _desc(L, 2, T=0, xq=None))
     st, tb, wi = L.bitlinear_group_table_bytes(arr, 2, 4, 0)
     assert st == 0
     # 16 panels of 32 rows per work item (1 + 14 items; the T == 0 projection has none), laid out
@@ -177,6 +179,27 @@ def test_group_sizes_and_rejects_before_launch(L):
     assert L.bitlinear_fwd_group(FAKE + 4, 3, 2, 4, 0, None) == -22
     assert L.bitlinear_fwd_group(FAKE, 3, 2, 4, 9, None) == -95
     assert L.bitlinear_fwd_group(None, 0, 2, 4, 0, None) == 0   # nothing to launch
+
+
+def test_group_rejects_overlapping_outputs(L):
+    """A decode group's outputs (y, acc_opt) may overlap no other output and no input; inputs may
+    be shared.  A T == 0 projection touches nothing."""
+    def sizes(*descs, fused=False):
+        if fused:
+            return L.bitlinear_group_fused_table_bytes((L.BlFwdXDesc * len(descs))(*descs), 2, 4, 0)[0]
+        return L.bitlinear_group_table_bytes((L.BlFwdDesc * len(descs))(*descs), 2, 4, 0)[0]
+    S = 16 << 30
+    assert sizes(_desc(L, 0), _desc(L, 1)) == 0
+    assert sizes(_desc(L, 0), _desc(L, 0)) == -22                       # the same y twice
+    assert sizes(_desc(L, 0), _desc(L, 1, y=FAKE + S + 4 * 4 * 100 - 16)) == -22   # y ranges overlap
+    assert sizes(_desc(L, 0, y=FAKE)) == -22                            # y over the inputs
+    assert sizes(_desc(L, 0, acc_opt=FAKE + S + 16)) == -22             # acc over y
+    assert sizes(_desc(L, 0, acc_opt=FAKE + 3 * S)) == 0
+    assert sizes(_desc(L, 0), _desc(L, 1, acc_opt=FAKE + S)) == -22     # acc over another y
+    assert sizes(_desc(L, 0), _desc(L, 1, T=0, y=FAKE + S)) == 0        # T == 0 writes nothing
+    assert sizes(_xdesc(L, 0), _xdesc(L, 0), fused=True) == -22
+    assert sizes(_xdesc(L, 0, y=FAKE + 2 * 4 * 256 - 16), fused=True) == -22   # y over the bf16 rows
+    assert sizes(_xdesc(L, 0, y=FAKE + 2 * 4 * 256 + 16), fused=True) == -22   # y over codes
 
 
 def _up32(v):
@@ -498,17 +521,18 @@ def test_act_quant_group_rejects_before_launch(L):
     assert _qgroup(L, [a, _qdesc(L, 1, x_scale=a.x_scale + 16)]) == -22
 
 
-def _xdesc(L, **kw):
+def _xdesc(L, slot=0, **kw):
     P = FAKE
-    a = dict(x=P, T=4, K=256, codes=P, meta=P, gamma=P, n=100, y=P, acc_opt=None)
+    a = dict(x=P, T=4, K=256, codes=P, meta=P, gamma=P, n=100,
+             y=FAKE + (slot + 1) * (16 << 30), acc_opt=None)
     a.update(kw)
     return L.BlFwdXDesc(**a)
 
 
 def test_fused_group_sizes_and_rejects_before_launch(L):
     """The fused group plans exactly like the plain one; it refuses lifted layouts."""
-    xs = (L.BlFwdXDesc * 3)(_xdesc(L), _xdesc(L, n=6912, K=2560, T=16), _xdesc(L, T=0, x=None))
-    ps = (L.BlFwdDesc * 3)(_desc(L), _desc(L, n=6912, K=2560, T=16), _desc(L, T=0, xq=None))
+    xs = (L.BlFwdXDesc * 3)(_xdesc(L), _xdesc(L, 1, n=6912, K=2560, T=16), _xdesc(L, 2, T=0, x=None))
+    ps = (L.BlFwdDesc * 3)(_desc(L), _desc(L, 1, n=6912, K=2560, T=16), _desc(L, 2, T=0, xq=None))
     assert L.bitlinear_group_fused_table_bytes(xs, 2, 4, 0) == L.bitlinear_group_table_bytes(ps, 2, 4, 0)
 
     def one(N=2, M=4, layout=0, **kw):
