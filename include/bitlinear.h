@@ -104,6 +104,19 @@ int bitlinear_packed_bytes(int64_t n, int64_t K, int N, int M, int layout, size_
 int bitlinear_pack(const float* W, int64_t n, int64_t K, int N, int M, int layout, uint8_t* codes,
                    uint8_t* meta, float* gamma, void* ws, size_t ws_bytes, void* stream);
 
+/* For callers that cannot allocate device memory (code under graph capture, tight serving loops,
+ * harnesses that forbid allocation): bitlinear_pack without a caller workspace.  Same arguments
+ * minus ws / ws_bytes, same shape, alignment and error rules, same results bit for bit.  The
+ * workspace is a static device array inside the library, BL_PACK_NOALLOC_WS_BYTES bytes (the
+ * workspace of one bitlinear_pack call, which does not depend on n or K, so every shape
+ * bitlinear_pack accepts fits; BL_ENOSPC would report a shape that did not).  Each GPU the
+ * library runs on holds its own copy from the first call there until the process ends; the call
+ * allocates nothing.  Every call on one GPU shares that copy: calls that may overlap on one GPU
+ * (different streams, or different host threads) race and must be serialized by the caller. */
+#define BL_PACK_NOALLOC_WS_BYTES 9472
+int bitlinear_pack_noalloc(const float* W, int64_t n, int64_t K, int N, int M, int layout,
+                           uint8_t* codes, uint8_t* meta, float* gamma, void* stream);
+
 /* Per-token absmax int8 quantization of x[T][K] (row-major; x_dtype BL_DTYPE_F32 or
  * BL_DTYPE_BF16).  Writes xq[T][K_eff] int8 and x_scale[T] fp32 (absmax/127).
  * lift_M = 0: K_eff = K.  lift_M = 8 or 16: activation lifting for (M-2):M windows,

@@ -1,6 +1,7 @@
 """ctypes binding of libbitlinear (argument marshalling only; every step runs in HIP kernels).
 
-Names mirror the C ABI: ``bitlinear_packed_bytes``, ``bitlinear_pack``, ``act_quant_i8``,
+Names mirror the C ABI: ``bitlinear_packed_bytes``, ``bitlinear_pack``, ``bitlinear_pack_noalloc``,
+``act_quant_i8``,
 ``bitlinear_fwd``, ``bitlinear_group_table_bytes``, ``bitlinear_group_build``,
 ``bitlinear_fwd_group``, ``bitlinear_group_fused_table_bytes``, ``bitlinear_group_fused_build``,
 ``bitlinear_fwd_group_fused``, ``bitlinear_bwd_workspace_bytes``, ``bitlinear_bwd``,
@@ -109,6 +110,7 @@ def lib() -> ctypes.CDLL:
         L.bitlinear_packed_bytes.argtypes = [i64, i64, i32, i32, i32, ctypes.POINTER(sz),
                                              ctypes.POINTER(sz), ctypes.POINTER(i64), ctypes.POINTER(sz)]
         L.bitlinear_pack.argtypes = [vp, i64, i64, i32, i32, i32, vp, vp, vp, vp, sz, vp]
+        L.bitlinear_pack_noalloc.argtypes = [vp, i64, i64, i32, i32, i32, vp, vp, vp, vp]
         L.act_quant_i8.argtypes = [vp, i32, i64, i64, i32, vp, vp, vp]
         L.act_quant_i8_group.argtypes = [ctypes.POINTER(BlQuantDesc), i64, i32, i32, vp]
         L.bitlinear_fwd.argtypes = [vp, vp, i64, i64, vp, vp, vp, i32, i32, i32, i64, vp, vp, vp]
@@ -142,7 +144,8 @@ def lib() -> ctypes.CDLL:
         L.bitlinear_strerror.argtypes = [i32]
         L.bitlinear_strerror.restype = ctypes.c_char_p
         L.bitlinear_layout_version.argtypes = []
-        for f in (L.bitlinear_packed_bytes, L.bitlinear_pack, L.act_quant_i8, L.bitlinear_fwd,
+        for f in (L.bitlinear_packed_bytes, L.bitlinear_pack, L.bitlinear_pack_noalloc,
+                  L.act_quant_i8, L.bitlinear_fwd,
                   L.bitlinear_layout_version, L.bitlinear_group_table_bytes,
                   L.bitlinear_group_build, L.bitlinear_fwd_group,
                   L.bitlinear_bwd_workspace_bytes, L.bitlinear_bwd,
@@ -178,6 +181,10 @@ def bitlinear_packed_bytes(n: int, K: int, N: int, M: int, layout: int):
 
 def bitlinear_pack(W, n, K, N, M, layout, codes, meta, gamma, ws, ws_bytes, stream) -> int:
     return lib().bitlinear_pack(W, n, K, N, M, layout, codes, meta, gamma, ws, ws_bytes, stream)
+
+
+def bitlinear_pack_noalloc(W, n, K, N, M, layout, codes, meta, gamma, stream) -> int:
+    return lib().bitlinear_pack_noalloc(W, n, K, N, M, layout, codes, meta, gamma, stream)
 
 
 def act_quant_i8(x, x_dtype, T, K, lift_M, xq, x_scale, stream) -> int:

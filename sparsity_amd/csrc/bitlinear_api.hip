@@ -16,6 +16,8 @@
 #include "launch.hpp"
 #include "pack_group.hpp"
 
+static_assert(BL_PACK_NOALLOC_WS_BYTES == bl::kPackWsBytes, "header states the static workspace size");
+
 namespace {
 
 bool aligned16(const void* p) { return p && ((uintptr_t)p & 15u) == 0; }
@@ -705,6 +707,19 @@ int bitlinear_pack(const float* W, int64_t n, int64_t K, int N, int M, int layou
   if (ws_bytes < bl::kPackWsBytes) return BL_ENOSPC;
   return status_of(bl::launch_pack(W, n, K, N, M, layout, (uint32_t*)codes, (uint32_t*)meta, gamma,
                                    ws, (hipStream_t)stream));
+}
+
+int bitlinear_pack_noalloc(const float* W, int64_t n, int64_t K, int N, int M, int layout,
+                           uint8_t* codes, uint8_t* meta, float* gamma, void* stream) {
+  int64_t ke = 0;
+  const int st = check_shape(n, K, N, M, layout, &ke);
+  if (st != BL_OK) return st;
+  if (!aligned16(W) || !aligned16(codes) || !aligned16(gamma)) return BL_EINVAL;
+  if (layout == BL_LAYOUT_SPARSE ? !aligned16(meta) : meta != nullptr) return BL_EINVAL;
+  // the static workspace holds one pack workspace, whose size does not depend on the shape
+  if (bl::kPackWsBytes > bl::pack_noalloc_capacity()) return BL_ENOSPC;
+  return status_of(bl::launch_pack_noalloc(W, n, K, N, M, layout, (uint32_t*)codes,
+                                           (uint32_t*)meta, gamma, (hipStream_t)stream));
 }
 
 int bitlinear_pack_group_plan(const bl_pack_desc* descs, int64_t count, int N, int M, int layout,

@@ -17,6 +17,11 @@ constexpr size_t kPackWsBytes = (kGammaBlocks * sizeof(double) + kExactWords * 1
 hipError_t launch_pack(const float* W, int64_t n, int64_t K, int N, int M, int layout,
                        uint32_t* codes, uint32_t* meta, float* gamma, void* ws, hipStream_t s);
 
+// bitlinear_pack with the library's static per-device workspace (no caller workspace).
+hipError_t launch_pack_noalloc(const float* W, int64_t n, int64_t K, int N, int M, int layout,
+                               uint32_t* codes, uint32_t* meta, float* gamma, hipStream_t s);
+size_t pack_noalloc_capacity();   // bytes of that workspace
+
 hipError_t launch_act_quant(const void* x, int x_is_bf16, int64_t T, int64_t K, int lift_M,
                             int8_t* xq, float* x_scale, hipStream_t s);
 

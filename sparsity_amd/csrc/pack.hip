@@ -20,6 +20,8 @@
 //                             pass over W, once per master
 //   3. pack_kernel            reads tau; mask, codes by |w| >= tau, slots assembled in LDS,
 //                             coalesced dword stores.
+#include <mutex>
+
 #include "device_common.hpp"
 #include "launch.hpp"
 #include "pack_group.hpp"
@@ -495,6 +497,52 @@ hipError_t launch_pack(const float* W, int64_t n, int64_t K, int N, int M, int l
     else run(pack_kernel<kLayoutDense2, 16>, nullptr);
   }
   return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------------------------
+// Allocation-free pack, for callers that cannot allocate (code under graph capture, serving loops,
+// harnesses that forbid allocation): bitlinear_pack with its workspace in this file's static
+// device array instead of a caller buffer.  The array holds one pack workspace (kPackWsBytes,
+// the same for every shape); each GPU the library runs on holds its own copy until the process
+// ends, and every call on that GPU shares it, so calls that overlap on one GPU race.  The
+// partial-sum launch clears the state the later launches accumulate into (exact words, block
+// counter), so a call never depends on what the previous one left there.
+// ---------------------------------------------------------------------------------------------
+static __device__ __align__(256) uint8_t scratch[kPackWsBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];   // device address of `scratch` on each device, once looked up
+}  // namespace
+
+size_t pack_noalloc_capacity() { return sizeof(scratch); }
+
+// The array's device address on the current device (looked up on the first call there).  In
+// host code `scratch` names a host-side stand-in, never the device memory itself.
+static hipError_t scratch_on_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
+hipError_t launch_pack_noalloc(const float* W, int64_t n, int64_t K, int N, int M, int layout,
+                               uint32_t* codes, uint32_t* meta, float* gamma, hipStream_t s) {
+  void* ws = nullptr;
+  const hipError_t e = scratch_on_current_device(&ws);
+  if (e != hipSuccess) return e;
+  return launch_pack(W, n, K, N, M, layout, codes, meta, gamma, ws, s);
 }
 
 hipError_t launch_pack_group(const void* table, int64_t count, int64_t pack_blocks, int layout,
