@@ -228,6 +228,103 @@ def decode_fused_leg(S, torch, D, ref, steps, warmup):
                                    for T in DECODE_T}}}
 
 
+def _graph_ms(torch, fn, steps, warmup):
+    """Capture fn once as a HIP graph; mean ms per replay over `steps` replays."""
+    fn()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    with torch.cuda.graph(graph, stream=cap):
+        fn()
+    for _ in range(warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        graph.replay()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * 1e3 / steps
+
+
+def decode_single_leg(S, torch, D, steps, warmup):
+    """The decode stream with one bitlinear_fwd launch per projection (no grouping): the same 128
+    projections and pre-quantized activations as the grouped GEMV, 128 launches per T, captured
+    as one HIP graph per T.  Its roofline uses the grouped GEMV's algorithmic bytes."""
+    out = {}
+    for T in DECODE_T:
+        projs = []
+        for i, (n, K, codes, meta, gamma) in enumerate(D.mats):
+            xq, sc = D.q[(T, K)]
+            j = i // 2
+            projs.append((xq[j * T:(j + 1) * T], sc[j * T:(j + 1) * T], K, codes, meta, gamma, n,
+                          torch.empty((T, n), dtype=torch.float32, device="cuda")))
+
+        def run():
+            for (xq, sc, K, c, m, ga, n, y) in projs:
+                S.fwd(xq, sc, K, c, m, ga, n, out=(y, None))
+        ms = _graph_ms(torch, run, steps, warmup)
+        algo = D.algorithmic_bytes(T)
+        out[str(T)] = {"ms": round(ms, 4), "per_launch_us": round(ms * 1e3 / len(projs), 2),
+                       "weight_GBps": round(D.packed_bytes / (ms * 1e-3) / 1e9, 1),
+                       "frac": round(algo / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    return {"workload": "the decode stream with one bitlinear_fwd launch per projection: 128 "
+                        "launches per T (graph-captured), pre-quantized independent activations",
+            "kernel": "gemv_kernel", "per_T": out}
+
+
+def decode_chain_leg(S, torch, D, steps, warmup):
+    """The decode stream as one dependent chain: up_0, down_0, up_1, ... (128 layers), each
+    layer's input the previous layer's fp32 output, starting from a bf16 token row block.
+    (a) bitlinear_fwd_chain: one persistent launch quantizing and multiplying every layer;
+    (b) the same chain as act_quant_i8 + bitlinear_fwd per layer (256 launches, graph-captured).
+    Outputs of (a) and (b) are checked bitwise equal first."""
+    out = {}
+    layers = [dict(codes=c, meta=m, gamma=ga, n=n, K=K) for (n, K, c, m, ga) in D.mats]
+    for T in DECODE_T:
+        x0 = D.x[(T, UP[1])][:T]
+        ch = S.Chain(layers, T)
+        ch(x0)
+        if ch.error():
+            raise RuntimeError("chain launch reported a barrier timeout")
+        ys = [torch.empty((T, ly["n"]), dtype=torch.float32, device="cuda") for ly in layers]
+        qs = [(torch.empty((T, ly["K"]), dtype=torch.int8, device="cuda"),
+               torch.empty(max(T, 4), dtype=torch.float32, device="cuda")[:T]) for ly in layers]
+
+        def calls():
+            inp = x0
+            for ly, y, (xq, sc) in zip(layers, ys, qs):
+                S.act_quant(inp, out=(xq, sc))
+                S.fwd(xq, sc, ly["K"], ly["codes"], ly["meta"], ly["gamma"], ly["n"], out=(y, None))
+                inp = y
+        calls()
+        torch.cuda.synchronize()
+        for a, b in zip(ys, ch.ys):
+            if not torch.equal(a, b):
+                raise RuntimeError("chain output differs from act_quant_i8 + bitlinear_fwd")
+        ms_calls = _graph_ms(torch, calls, steps, warmup)
+        for _ in range(3):
+            ch(x0)
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(steps)]
+        for a, b in ev:
+            a.record()
+            ch(x0)
+            b.record()
+        torch.cuda.synchronize()
+        if ch.error():
+            raise RuntimeError("chain launch reported a barrier timeout")
+        ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+        out[str(T)] = {"chain_ms": round(ms, 4), "per_layer_us": round(ms * 1e3 / len(layers), 2),
+                       "weight_GBps": round(D.packed_bytes / (ms * 1e-3) / 1e9, 1),
+                       "per_layer_calls_ms": round(ms_calls, 4),
+                       "speedup_vs_calls": round(ms_calls / ms, 3)}
+    return {"workload": "the decode stream as one dependent chain of 128 layers (up_0, down_0, "
+                        "up_1, ...; each input the previous fp32 output): one bitlinear_fwd_chain "
+                        "launch against act_quant_i8 + bitlinear_fwd per layer (graph-captured)",
+            "outputs_identical_to_calls": True, "per_T": out}
+
+
 def decode_mall_leg(S, torch, D, pairs=24, launches=100):
     """The decode layer stream shrunk to fit the 256 MB last-level cache: the first `pairs` up/down
     pairs (212 MB of packed weights for 24) in one grouped launch at T = 1, repeated back to back.
@@ -997,6 +1094,13 @@ def main():
     log("fused decode leg")
     out["decode_fused"] = decode_fused_leg(S, torch, D, ref, args.steps, args.warmup)
     log(f"fused decode {out['decode_fused']['value']} GB/s")
+    log("single-projection decode leg")
+    out["decode_single"] = decode_single_leg(S, torch, D, args.steps, args.warmup)
+    log("single: " + ", ".join(f"T={T} {v['weight_GBps']} GB/s" for T, v in out["decode_single"]["per_T"].items()))
+    log("dependent chain decode leg")
+    out["decode_chain"] = decode_chain_leg(S, torch, D, args.steps, args.warmup)
+    log("chain: " + ", ".join(f"T={T} {v['chain_ms']} ms (calls {v['per_layer_calls_ms']} ms)"
+                              for T, v in out["decode_chain"]["per_T"].items()))
     if not args.no_extra:
         log("MALL-sized decode reading")
         out["decode_mall_sized"] = decode_mall_leg(S, torch, D)

@@ -287,6 +287,61 @@ int bitlinear_fwd_group_fused(const void* table, int64_t work_items, int N, int 
                               void* stream);
 
 /* ---------------------------------------------------------------------------------------------
+ * Fused decode over a chain of dependent layers: layer l + 1's input is layer l's output y.
+ *
+ * In a decoder every layer reads the previous layer's output, so its per-token int8 quantization
+ * (BitNet b1.58 page, "The mechanism") cannot be batched with the others; separate calls pay an
+ * act_quant_i8 launch and a bitlinear_fwd launch per layer.  bitlinear_fwd_chain runs the whole
+ * chain in one persistent launch: per layer, the per-token absmax of its input, the int8
+ * quantization (act_quant_i8's expressions), the sparse ternary GEMV and the rescale
+ * (bitlinear_fwd's), with the next layer's absmax folded in as each layer writes its y.  Every
+ * layer's y and acc_opt are bit-identical to act_quant_i8(previous y, fp32) followed by
+ * bitlinear_fwd (layer 0: act_quant_i8(x0)).  Each layer's packed weights are loaded before its
+ * wait for the previous layer.
+ *
+ * Layers: 2:4 BL_LAYOUT_SPARSE only (BL_ENOTSUP otherwise); K of layer l + 1 == n of layer l;
+ * each n x K follows bitlinear_pack's shape rules with K <= 8192; 1 <= T <= 32 with
+ * T * (K + 16) <= 129024 (the layer's int8 input rows stay in LDS); 1 <= L <= 4096.
+ * codes, meta, y and x0 16-byte aligned, gamma 4 bytes, acc_opt 4 bytes or NULL.  Outputs (every
+ * y and acc_opt) may not overlap each other, x0 or any weight buffer (BL_EINVAL).
+ *
+ * Use: bitlinear_chain_plan sizes the device table and the workspace; bitlinear_chain_build
+ * writes the table (16-byte aligned device memory, caller-owned; synchronizes `stream`: build
+ * once, outside graph capture); bitlinear_fwd_chain enqueues a clear of the workspace (a small
+ * kernel) and the cooperative chain launch (64 workgroups, all resident).  The workspace
+ * (caller-owned device memory, 16-byte aligned, contents on entry irrelevant) holds the grid
+ * barrier's counter, an error word and per-workgroup partial absmax of every layer's input; calls
+ * sharing it
+ * must be ordered on one stream.  Every wait at the grid barrier is bounded by spin_limit polls
+ * (<= 0: a default of about a second); a wait that gives up sets the uint32 error word at byte
+ * offset 4 of the workspace to nonzero and its block returns, so the launch always ends -- then
+ * the outputs are invalid.  Read that word after the launch completes.
+ */
+typedef struct bl_chain_layer {
+  const uint8_t* codes;   /* packed 2:4 codes of the n x K master */
+  const uint8_t* meta;    /* packed meta */
+  const float* gamma;     /* device scalar */
+  int64_t n, K;           /* out- and in-features; K == previous layer's n */
+  float* y;               /* [T][n] fp32 output (the next layer's input) */
+  int32_t* acc_opt;       /* [T][n] int32 accumulators, or NULL */
+} bl_chain_layer;
+
+typedef struct bl_chain_plan {
+  size_t table_bytes;     /* device table */
+  size_t ws_bytes;        /* device workspace */
+  int64_t L, T;
+  int32_t smem;           /* dynamic LDS bytes of the chain launch */
+  int32_t reserved;
+} bl_chain_plan;
+
+int bitlinear_chain_plan(const bl_chain_layer* layers, int64_t L, int64_t T, int N, int M,
+                         int layout, bl_chain_plan* plan);
+int bitlinear_chain_build(const bl_chain_layer* layers, int64_t L, int64_t T, int N, int M,
+                          int layout, void* table, size_t table_bytes, void* stream);
+int bitlinear_fwd_chain(const void* table, const bl_chain_plan* plan, const void* x0, int x_dtype,
+                        void* ws, size_t ws_bytes, int64_t spin_limit, void* stream);
+
+/* ---------------------------------------------------------------------------------------------
  * Grouped prefill forward: the bitlinear_fwd calls of a layer set with prefill-sized T in one
  * launch.
  *

@@ -16,5 +16,6 @@ from .bitlinear import (  # noqa: F401
     bitlinear_fwd, bitlinear_fwd_group, bitlinear_fwd_group_fused, bitlinear_group_build,
     bitlinear_group_fused_build, bitlinear_group_fused_table_bytes, bitlinear_group_table_bytes,
     bitlinear_pack, bitlinear_packed_bytes, bwd, bwd_workspace_bytes, fwd, lib, pack,
-    packed_bytes,
+    packed_bytes, bitlinear_pack_noalloc, BlChainLayer, BlChainPlan, Chain, bitlinear_chain_plan,
+    bitlinear_chain_build, bitlinear_fwd_chain,
 )

@@ -86,6 +86,20 @@ class BlGemmGroupPlan(ctypes.Structure):
                 ("reserved", ctypes.c_int32)]
 
 
+class BlChainLayer(ctypes.Structure):
+    """bl_chain_layer: one layer of a fused decode chain (its input is the previous layer's y)."""
+    _fields_ = [("codes", ctypes.c_void_p), ("meta", ctypes.c_void_p), ("gamma", ctypes.c_void_p),
+                ("n", ctypes.c_int64), ("K", ctypes.c_int64), ("y", ctypes.c_void_p),
+                ("acc_opt", ctypes.c_void_p)]
+
+
+class BlChainPlan(ctypes.Structure):
+    """bl_chain_plan: table and workspace sizes and the launch's LDS bytes of a chain."""
+    _fields_ = [("table_bytes", ctypes.c_size_t), ("ws_bytes", ctypes.c_size_t),
+                ("L", ctypes.c_int64), ("T", ctypes.c_int64), ("smem", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
+
+
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libbitlinear.so")
 _lib = None
@@ -141,6 +155,11 @@ def lib() -> ctypes.CDLL:
         L.bitlinear_gemm_group_plan.argtypes = [dp, i64, i32, i32, i32, gp]
         L.bitlinear_gemm_group_build.argtypes = [dp, i64, i32, i32, i32, vp, sz, vp]
         L.bitlinear_gemm_group.argtypes = [vp, gp, vp]
+        cl = ctypes.POINTER(BlChainLayer)
+        cpp = ctypes.POINTER(BlChainPlan)
+        L.bitlinear_chain_plan.argtypes = [cl, i64, i64, i32, i32, i32, cpp]
+        L.bitlinear_chain_build.argtypes = [cl, i64, i64, i32, i32, i32, vp, sz, vp]
+        L.bitlinear_fwd_chain.argtypes = [vp, cpp, vp, i32, vp, sz, i64, vp]
         L.bitlinear_strerror.argtypes = [i32]
         L.bitlinear_strerror.restype = ctypes.c_char_p
         L.bitlinear_layout_version.argtypes = []
@@ -155,7 +174,8 @@ def lib() -> ctypes.CDLL:
                   L.bitlinear_pack_group_plan, L.bitlinear_pack_group_build,
                   L.bitlinear_pack_group, L.bitlinear_gemm_group_plan,
                   L.bitlinear_gemm_group_build, L.bitlinear_gemm_group,
-                  L.act_quant_i8_group):
+                  L.act_quant_i8_group, L.bitlinear_chain_plan, L.bitlinear_chain_build,
+                  L.bitlinear_fwd_chain):
             f.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -296,6 +316,23 @@ def bitlinear_gemm_group_build(descs, N, M, layout, table, table_bytes, stream) 
 def bitlinear_gemm_group(table, plan, stream) -> int:
     return lib().bitlinear_gemm_group(table, ctypes.byref(plan) if plan is not None else None,
                                       stream)
+
+
+def bitlinear_chain_plan(layers, T, N, M, layout):
+    """layers: a ctypes array of BlChainLayer.  Returns (status, BlChainPlan)."""
+    plan = BlChainPlan()
+    st = lib().bitlinear_chain_plan(layers, len(layers), T, N, M, layout, ctypes.byref(plan))
+    return st, plan
+
+
+def bitlinear_chain_build(layers, T, N, M, layout, table, table_bytes, stream) -> int:
+    return lib().bitlinear_chain_build(layers, len(layers), T, N, M, layout, table, table_bytes,
+                                       stream)
+
+
+def bitlinear_fwd_chain(table, plan, x0, x_dtype, ws, ws_bytes, spin_limit, stream) -> int:
+    return lib().bitlinear_fwd_chain(table, ctypes.byref(plan) if plan is not None else None, x0,
+                                     x_dtype, ws, ws_bytes, spin_limit, stream)
 
 
 # ---------------------------------------------------------------------------------------------
@@ -653,3 +690,64 @@ class BwdGroup:
     def __call__(self):
         _check(bitlinear_bwd_group(self.table.data_ptr(), self.plan, _stream()),
                "bitlinear_bwd_group")
+
+
+class Chain:
+    """A built fused decode chain: ``Chain(layers, T)`` then ``chain(x0)`` runs every layer.
+
+    ``layers`` is a list of dicts with keys codes, meta, gamma, n, K and optionally y and acc
+    (2:4 packed weights; K of each layer == n of the previous one).  y (fp32 [T][n]) is
+    allocated when not given; ``chain.ys`` / ``chain.accs`` list the outputs.  ``chain(x0)``
+    (bf16 or fp32 CUDA tensor [T][K0]) enqueues the whole chain; ``chain.error()`` (a host sync)
+    is nonzero if a bounded wait gave up, in which case the outputs are invalid.
+    """
+
+    def __init__(self, layers, T: int, ws=None):
+        import torch
+        self._keep = list(layers)
+        self.T = T
+        arr = (BlChainLayer * len(layers))()
+        self.ys, self.accs = [], []
+        dev = layers[0]["codes"].device
+        for i, ly in enumerate(layers):
+            y = ly.get("y")
+            if y is None:
+                y = torch.empty((T, ly["n"]), dtype=torch.float32, device=dev)
+            _need(y, torch.float32, T * ly["n"], dev, f"layers[{i}] y")
+            acc = ly.get("acc")
+            if acc is not None:
+                _need(acc, torch.int32, T * ly["n"], dev, f"layers[{i}] acc")
+            cb, mb, _, _ = packed_bytes(ly["n"], ly["K"])
+            _need(ly["codes"], torch.uint8, cb, dev, f"layers[{i}] codes")
+            _need(ly["meta"], torch.uint8, mb, dev, f"layers[{i}] meta")
+            _need(ly["gamma"], torch.float32, 1, dev, f"layers[{i}] gamma")
+            self.ys.append(y)
+            self.accs.append(acc)
+            arr[i] = BlChainLayer(_ptr(ly["codes"]), _ptr(ly["meta"]), _ptr(ly["gamma"]), ly["n"],
+                                  ly["K"], _ptr(y), _ptr(acc))
+        self.layers = arr
+        st, plan = bitlinear_chain_plan(arr, T, 2, 4, BL_LAYOUT_SPARSE)
+        _check(st, "bitlinear_chain_plan")
+        self.plan = plan
+        self.table = torch.empty(max(plan.table_bytes, 16), dtype=torch.uint8, device=dev)
+        if ws is None:
+            ws = torch.empty(max(plan.ws_bytes, 256), dtype=torch.uint8, device=dev)
+        _need(ws, torch.uint8, plan.ws_bytes, dev, "ws")
+        self.ws = ws
+        self.K0 = layers[0]["K"]
+        _check(bitlinear_chain_build(arr, T, 2, 4, BL_LAYOUT_SPARSE, self.table.data_ptr(),
+                                     self.table.numel(), _stream()), "bitlinear_chain_build")
+
+    def __call__(self, x0, spin_limit: int = 0):
+        import torch
+        dts = {torch.float32: BL_DTYPE_F32, torch.bfloat16: BL_DTYPE_BF16}
+        assert x0.is_cuda and x0.is_contiguous() and tuple(x0.shape) == (self.T, self.K0)
+        _check(bitlinear_fwd_chain(self.table.data_ptr(), self.plan, x0.data_ptr(), dts[x0.dtype],
+                                   self.ws.data_ptr(), self.ws.numel(), spin_limit, _stream()),
+               "bitlinear_fwd_chain")
+
+    def error(self) -> int:
+        """The workspace's error word (after the launch completes; synchronizes the device)."""
+        import torch
+        torch.cuda.synchronize()
+        return int(self.ws[4:8].cpu().view(torch.int32)[0])

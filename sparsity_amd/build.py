@@ -9,7 +9,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libbitlinear.so")
-SOURCES = ["bitlinear_api.hip", "pack.hip", "act_quant.hip", "fwd.hip", "gemv_group.hip", "bwd.hip"]
+SOURCES = ["bitlinear_api.hip", "pack.hip", "act_quant.hip", "fwd.hip", "gemv_group.hip", "bwd.hip",
+           "chain.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

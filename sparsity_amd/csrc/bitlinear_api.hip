@@ -11,6 +11,7 @@
 
 #include "bitlinear.h"
 #include "bwd_group.hpp"
+#include "chain.hpp"
 #include "gemm_group.hpp"
 #include "quant_group.hpp"
 #include "launch.hpp"
@@ -666,6 +667,54 @@ int fused_as_plain(const bl_fwd_x_desc* d, int64_t count, int M, int layout,
   return BL_OK;
 }
 
+// Validation of a chain (see bl_chain_layer in the header); returns BL_OK and the launch's
+// dynamic LDS bytes.
+constexpr int64_t kChainLdsMax = 163840 - 1024;
+
+int plan_chain(const bl_chain_layer* d, int64_t L, int64_t T, int N, int M, int layout,
+               int* smem) {
+  if (!d || L < 1 || L > 4096) return BL_EINVAL;
+  if (layout != BL_LAYOUT_SPARSE || N != 2 || M != 4) return BL_ENOTSUP;
+  if (T < 1 || T > bl::kChainMaxT) return BL_EINVAL;
+  int64_t need = 0;
+  struct Rg { uintptr_t lo, hi; bool out; };
+  std::vector<Rg> rs;
+  for (int64_t l = 0; l < L; ++l) {
+    const bl_chain_layer& q = d[l];
+    int64_t ke = 0;
+    const int st = check_shape(q.n, q.K, N, M, layout, &ke);
+    if (st != BL_OK) return st;
+    if (q.K > 8192) return BL_EINVAL;
+    if (l > 0 && q.K != d[l - 1].n) return BL_EINVAL;
+    if ((uint64_t)T * q.K * 4 >= (1ull << 31) || (uint64_t)T * q.n * 4 >= (1ull << 31)) return BL_EINVAL;
+    if (!aligned16(q.codes) || !aligned16(q.meta) || !aligned4(q.gamma) || !aligned16(q.y))
+      return BL_EINVAL;
+    if (q.acc_opt && ((uintptr_t)q.acc_opt & 3u)) return BL_EINVAL;
+    need = std::max<int64_t>(need, (T * (q.K + 16) + 15) / 16 * 16 + bl::kChainRedBytes);
+    size_t cb = 0, mb = 0;
+    bitlinear_packed_bytes(q.n, q.K, N, M, layout, &cb, &mb, nullptr, nullptr);
+    rs.push_back({(uintptr_t)q.codes, (uintptr_t)q.codes + cb, false});
+    rs.push_back({(uintptr_t)q.meta, (uintptr_t)q.meta + mb, false});
+    rs.push_back({(uintptr_t)q.gamma, (uintptr_t)q.gamma + 4, false});
+    rs.push_back({(uintptr_t)q.y, (uintptr_t)q.y + (uint64_t)T * q.n * 4, true});
+    if (q.acc_opt) rs.push_back({(uintptr_t)q.acc_opt, (uintptr_t)q.acc_opt + (uint64_t)T * q.n * 4, true});
+  }
+  if (need > kChainLdsMax) return BL_EINVAL;
+  std::sort(rs.begin(), rs.end(), [](const Rg& a, const Rg& b) { return a.lo < b.lo; });
+  uintptr_t out_hi = 0, any_hi = 0;
+  for (const Rg& r : rs) {
+    if (r.lo < out_hi || (r.out && r.lo < any_hi)) return BL_EINVAL;
+    any_hi = std::max(any_hi, r.hi);
+    if (r.out) out_hi = std::max(out_hi, r.hi);
+  }
+  *smem = (int)need;
+  return BL_OK;
+}
+
+size_t chain_table_bytes(int64_t L) {
+  return (sizeof(bl::ChainHeader) + (size_t)L * sizeof(bl::ChainLayer) + 15) / 16 * 16;
+}
+
 }  // namespace
 
 extern "C" {
@@ -941,6 +990,69 @@ int bitlinear_fwd_group_fused(const void* table, int64_t work_items, int N, int 
   if (work_items == 0) return BL_OK;
   if (!aligned16(table)) return BL_EINVAL;
   return status_of(bl::launch_fwd_group(table, work_items, layout, 1, (hipStream_t)stream));
+}
+
+int bitlinear_chain_plan(const bl_chain_layer* layers, int64_t L, int64_t T, int N, int M,
+                         int layout, bl_chain_plan* plan) {
+  if (!plan) return BL_EINVAL;
+  int smem = 0;
+  const int st = plan_chain(layers, L, T, N, M, layout, &smem);
+  if (st != BL_OK) return st;
+  memset(plan, 0, sizeof *plan);
+  plan->table_bytes = chain_table_bytes(L);
+  plan->ws_bytes = bl::chain_ws_bytes(L, T);
+  plan->L = L;
+  plan->T = T;
+  plan->smem = smem;
+  return BL_OK;
+}
+
+int bitlinear_chain_build(const bl_chain_layer* layers, int64_t L, int64_t T, int N, int M,
+                          int layout, void* table, size_t table_bytes, void* stream) {
+  int smem = 0;
+  const int st = plan_chain(layers, L, T, N, M, layout, &smem);
+  if (st != BL_OK) return st;
+  if (!aligned16(table)) return BL_EINVAL;
+  const size_t bytes = chain_table_bytes(L);
+  if (table_bytes < bytes) return BL_ENOSPC;
+  std::vector<uint8_t> img(bytes, 0);
+  bl::ChainHeader hdr;
+  memset(&hdr, 0, sizeof hdr);
+  hdr.magic = bl::kChainMagic;
+  hdr.L = (int32_t)L;
+  hdr.T = (int32_t)T;
+  hdr.smem = smem;
+  memcpy(img.data(), &hdr, sizeof hdr);
+  for (int64_t l = 0; l < L; ++l) {
+    bl::ChainLayer r;
+    memset(&r, 0, sizeof r);
+    r.codes = (const uint32_t*)layers[l].codes;
+    r.meta = (const uint32_t*)layers[l].meta;
+    r.gamma = layers[l].gamma;
+    r.y = layers[l].y;
+    r.acc = layers[l].acc_opt;
+    r.n = (int32_t)layers[l].n;
+    r.K = (int32_t)layers[l].K;
+    memcpy(img.data() + sizeof hdr + l * sizeof(bl::ChainLayer), &r, sizeof r);
+  }
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = hipMemcpyAsync(table, img.data(), bytes, hipMemcpyHostToDevice, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);  // img is released on return
+  return status_of(e);
+}
+
+int bitlinear_fwd_chain(const void* table, const bl_chain_plan* plan, const void* x0, int x_dtype,
+                        void* ws, size_t ws_bytes, int64_t spin_limit, void* stream) {
+  if (!plan || !aligned16(table) || !aligned16(x0) || !aligned16(ws)) return BL_EINVAL;
+  if (x_dtype != BL_DTYPE_F32 && x_dtype != BL_DTYPE_BF16) return BL_ENOTSUP;
+  if (plan->L < 1 || plan->L > 4096 || plan->T < 1 || plan->T > bl::kChainMaxT ||
+      plan->smem < 1 || plan->smem > kChainLdsMax)
+    return BL_EINVAL;
+  if (ws_bytes < bl::chain_ws_bytes(plan->L, plan->T)) return BL_ENOSPC;
+  // about a second of polls (each s_sleep 2 is ~128 clocks) unless the caller bounds it
+  const int64_t limit = spin_limit > 0 ? spin_limit : (int64_t)1 << 24;
+  return status_of(bl::launch_chain(table, plan->L, plan->T, plan->smem, x0,
+                                    x_dtype == BL_DTYPE_BF16, ws, limit, (hipStream_t)stream));
 }
 
 int bitlinear_bwd_workspace_bytes(int64_t T, int64_t n, int64_t K, size_t* ws_bytes) {

@@ -274,9 +274,8 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(
 // Rows past the last panel, tokens past T and K past the end (a partial last stage) read clamped,
 // valid addresses; their codes are zeroed or their results never stored.
 //
-// Blocks are mapped XCD-major: the hardware deals consecutive block ids round-robin to the 8
-// XCDs, so block b takes tile (b % 8) * (tiles / 8) + b / 8 and each XCD walks a contiguous run
-// of tiles that share a token tile, which then stays in that XCD's L2.
+// Blocks are mapped XCD-major (big_tile_of_block): each XCD owns a slab of token tiles and walks
+// them fastest, so its activations stay in its L2 and every weight panel is fetched once per XCD.
 constexpr int kBigWaves = 4;
 constexpr int kBigWaveRows = 4, kBigWaveM = 2, kBigWaveN = 4;
 
@@ -583,6 +582,26 @@ __device__ __forceinline__ void big_tile(
   }
 }
 
+// Tile of block b.  The hardware deals consecutive block ids round-robin to the 8 XCDs, each with
+// its own L2.  When the token tiles split evenly over the XCDs, XCD x = b % 8 owns token tiles
+// [x * ntn, (x + 1) * ntn) and walks them fastest, row tile by row tile (i = b / 8): its token
+// slab (ntn token tiles of activations) stays in its L2 and each packed weight panel is fetched
+// once per XCD, instead of once per token tile.  Otherwise each XCD takes a contiguous run of
+// tiles in row-tile-fastest order.
+__device__ __forceinline__ void big_tile_of_block(int b, int tiles_m, int tiles_n, int* tm, int* tn) {
+  const int tiles = tiles_m * tiles_n;
+  if ((tiles_n & 7) == 0) {
+    const int ntn = tiles_n >> 3, x = b & 7, i = b >> 3;
+    *tn = x * ntn + i % ntn;
+    *tm = i / ntn;
+    return;
+  }
+  const int full = (tiles / 8) * 8;
+  const int t = b < full ? (b % 8) * (tiles / 8) + b / 8 : b;
+  *tm = t % tiles_m;
+  *tn = t / tiles_m;
+}
+
 template <int LAYOUT, int NWAVE>
 __global__ __launch_bounds__(64 * NWAVE, 2) void gemm_big_kernel(
     const int8_t* __restrict__ xq, const float* __restrict__ xs, int T, int Keff,
@@ -591,10 +610,8 @@ __global__ __launch_bounds__(64 * NWAVE, 2) void gemm_big_kernel(
     int32_t* __restrict__ acc_out, int tiles_m, int tiles) {
   using G = BigGemm<LAYOUT, NWAVE, kBigWaveRows, kBigWaveM, kBigWaveN>;
   __shared__ __attribute__((aligned(16))) int8_t ring[3 * G::STAGE];
-  const int full = (tiles / 8) * 8;
-  const int b = blockIdx.x;
-  const int t = b < full ? (b % 8) * (tiles / 8) + b / 8 : b;
-  const int tm = t % tiles_m, tn = t / tiles_m;
+  int tm, tn;
+  big_tile_of_block(blockIdx.x, tiles_m, tiles / tiles_m, &tm, &tn);
   big_tile<LAYOUT, NWAVE>(ring, xq, xs, T, Keff, codes, meta, gamma_p, n, npanels, y, acc_out,
                           tm * G::BM, tn * G::BN);
 }

@@ -548,3 +548,57 @@ def test_fused_group_sizes_and_rejects_before_launch(L):
     assert L.bitlinear_fwd_group_fused(FAKE, 3, 6, 8, 0, None) == -95
     assert L.bitlinear_fwd_group_fused(FAKE + 4, 3, 2, 4, 0, None) == -22
     assert L.bitlinear_fwd_group_fused(None, 0, 2, 4, 0, None) == 0
+
+
+def _cdesc(L, slot, n, K, **kw):
+    """A chain layer whose buffers sit in their own 16 GiB slot of fake space."""
+    base = FAKE + slot * 16 * GB
+    a = dict(codes=base, meta=base + GB, gamma=base + 2 * GB, n=n, K=K, y=base + 3 * GB,
+             acc_opt=None)
+    a.update(kw)
+    return L.BlChainLayer(**a)
+
+
+def _cplan(L, layers, T=4, N=2, M=4, layout=0):
+    return L.bitlinear_chain_plan((L.BlChainLayer * len(layers))(*layers), T, N, M, layout)
+
+
+def test_chain_plan_sizes_and_rejects(L):
+    """A chain's table, workspace and LDS size; its layers must chain (K == previous n), be 2:4
+    and fit the per-wave step budget; outputs may not overlap anything."""
+    dims = [(6912, 2560), (2560, 6912), (6912, 2560)]
+    st, plan = _cplan(L, [_cdesc(L, i, n, K) for i, (n, K) in enumerate(dims)], T=16)
+    assert st == 0
+    assert plan.L == 3 and plan.T == 16
+    assert plan.table_bytes == (64 + 3 * 56 + 15) // 16 * 16
+    assert plan.ws_bytes == 4 * (64 + 4 * 64 * 16)   # per-workgroup absmax slots, 64 workgroups
+    # the widest layer's int8 input rows, then the eight waves' int32 partials
+    assert plan.smem == 16 * (6912 + 16) + 8 * 16 * 64 * 4
+    ok = [_cdesc(L, 0, 128, 256), _cdesc(L, 1, 64, 128)]
+    assert _cplan(L, ok)[0] == 0
+    assert _cplan(L, [_cdesc(L, 0, 128, 256), _cdesc(L, 1, 64, 192)])[0] == -22   # K != prev n
+    assert _cplan(L, ok, N=6, M=8)[0] == -95                                         # 2:4 only
+    assert _cplan(L, ok, layout=1)[0] == -95
+    assert _cplan(L, ok, T=0)[0] == -22
+    assert _cplan(L, ok, T=33)[0] == -22
+    assert _cplan(L, [_cdesc(L, 0, 64, 8256)])[0] == -22                            # K > 8192
+    assert _cplan(L, [_cdesc(L, 0, 64, 8192)], T=32)[0] == -22                      # LDS
+    assert _cplan(L, [_cdesc(L, 0, 64, 4096)], T=32)[0] == -22
+    assert _cplan(L, [_cdesc(L, 0, 64, 4032)], T=32)[0] == 0
+    assert _cplan(L, [_cdesc(L, 0, 64, 100)])[0] == -22
+    assert _cplan(L, [_cdesc(L, 0, 64, 128, codes=FAKE + 8)])[0] == -22
+    assert _cplan(L, [_cdesc(L, 0, 64, 128, y=FAKE + 4)])[0] == -22
+    # outputs: a y over another layer's y, over weights, or an acc over a y
+    assert _cplan(L, [_cdesc(L, 0, 128, 256), _cdesc(L, 1, 64, 128, y=FAKE + 3 * GB + 64)])[0] == -22
+    assert _cplan(L, [_cdesc(L, 0, 128, 256, y=FAKE + 16)])[0] == -22
+    assert _cplan(L, [_cdesc(L, 0, 128, 256, acc_opt=FAKE + 3 * GB + 16)])[0] == -22
+    assert _cplan(L, [_cdesc(L, 0, 128, 256, acc_opt=FAKE + 5 * GB)])[0] == 0
+    lib = L.lib()
+    assert lib.bitlinear_chain_plan(None, 1, 4, 2, 4, 0, None) == -22
+    # launch: argument checks only
+    assert L.bitlinear_fwd_chain(FAKE, plan, FAKE + 4, 1, FAKE, plan.ws_bytes, 0, None) == -22
+    assert L.bitlinear_fwd_chain(FAKE, plan, FAKE, 7, FAKE, plan.ws_bytes, 0, None) == -95
+    assert L.bitlinear_fwd_chain(FAKE, plan, FAKE, 1, FAKE, plan.ws_bytes - 4, 0, None) == -28
+    assert L.bitlinear_fwd_chain(FAKE, None, FAKE, 1, FAKE, plan.ws_bytes, 0, None) == -22
+    assert L.bitlinear_chain_build((L.BlChainLayer * 1)(_cdesc(L, 0, 64, 128)), 4, 2, 4, 0,
+                                   FAKE, 16, None) == -28
