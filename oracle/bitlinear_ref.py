@@ -205,10 +205,10 @@ def effective_weights(W: np.ndarray, N: int, M: int) -> Tuple[np.ndarray, np.flo
 
 
 # ----------------------------------------------------------------------------------------------
-# (2N-2):2N sliding windows ([SS] Sliding Window Decomposition): 6:8 and 14:16
+# (2N-2):2N sliding windows ([SS] Sliding Window Decomposition): 4:6, 6:8, ..., 14:16
 # ----------------------------------------------------------------------------------------------
 
-WINDOW_M = (8, 16)        # group sizes M = 2N decomposed into N - 1 overlapping 2:4 windows
+WINDOW_M = (6, 8, 10, 12, 14, 16)   # group sizes M = 2N decomposed into N - 1 overlapping 2:4 windows
 
 
 def _assign_windows(kept: List[int], M: int) -> List[List[int]]:
@@ -264,7 +264,7 @@ def k_eff(K: int, N: int, M: int, layout: int) -> int:
         return K
     if M in WINDOW_M and N == M - 2:
         return K * (2 * M - 4) // M
-    raise ValueError("SPARSE layout supports 2:4, 6:8 and 14:16")
+    raise ValueError("SPARSE layout supports 2:4 and (M-2):M for even M = 6..16")
 
 
 def packed_dwords(n: int, K: int, N: int, M: int, layout: int) -> Tuple[int, int, int]:

@@ -1,10 +1,10 @@
-// Per-token absmax int8 activation quantization, optionally with 6:8 or 14:16 activation lifting.
+// Per-token absmax int8 activation quantization, optionally with (M-2):M activation lifting.
 //
 // Each token's activations are scaled symmetrically onto [-127, 127] with no zero point
-// (BitNet b1.58 page, "The mechanism", Activations).  For 6:8 weights decomposed into three
+// (BitNet b1.58 page, "The mechanism", Activations).  For (M-2):M weights decomposed into M/2 - 1
 // overlapping 2:4 windows, the activations are rearranged to match the windows inside the same
-// pass (SlideSparse abstract, Activation Lifting): group g of 8 becomes 12 values
-// [x0 x1 x2 x3 | x2 x3 x4 x5 | x4 x5 x6 x7], a group of 16 becomes 28 (seven windows).
+// pass (SlideSparse abstract, Activation Lifting): a group of 8 becomes 12 values
+// [x0 x1 x2 x3 | x2 x3 x4 x5 | x4 x5 x6 x7], a group of M becomes 2M - 4 (M = 6, 8, ..., 16).
 //
 // absmax is the maximum of the |x| bit patterns (exact, order free); the int8 values are written
 // with round-half-even.  Rows of up to 16384 elements (bf16; 8192 fp32) go to act_quant_row_kernel:
@@ -38,13 +38,29 @@ __device__ __forceinline__ void load8(const void* __restrict__ x, size_t off, fl
   }
 }
 
-// LM = 0: plain.  LM = 8 or 16: (LM-2):LM activation lifting, each LM-group becomes LM/2 - 1
-// windows of four values, window w = x[2w .. 2w+3] (2LM - 4 bytes per group).
+// LM = 0: plain.  LM = 6, 8, ..., 16: (LM-2):LM activation lifting, each LM-group becomes
+// LM/2 - 1 windows of four values, window w = x[2w .. 2w+3] (2LM - 4 bytes per group).  A chunk
+// is lcm(LM, 8) elements (whole 8-element loads and whole groups).
+template <int LM>
+constexpr int chunk_elems() { return LM ? lcm_i(LM, 8) : 8; }
+
+// Lifted output of one chunk (CH quantized bytes q, CH / LM groups) at o (4-byte aligned).
+template <int LM, int CH>
+__device__ __forceinline__ void store_lifted(uint32_t* __restrict__ o, const uint32_t (&q)[CH]) {
+  constexpr int NW = LM / 2 - 1;
+#pragma unroll
+  for (int g = 0; g < CH / LM; ++g)
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const int b = g * LM + 2 * w;
+      o[g * NW + w] = q[b] | (q[b + 1] << 8) | (q[b + 2] << 16) | (q[b + 3] << 24);
+    }
+}
 template <bool BF16, int LM>
 __global__ __launch_bounds__(256) void act_quant_kernel(const void* __restrict__ x, int K,
                                                         int8_t* __restrict__ xq,
                                                         float* __restrict__ xs) {
-  constexpr int CH = LM ? LM : 8;         // elements per chunk
+  constexpr int CH = chunk_elems<LM>();   // elements per chunk
   const int t = blockIdx.x;
   const int nchunk = K / CH;
   const size_t row = (size_t)t * K;
@@ -75,12 +91,8 @@ __global__ __launch_bounds__(256) void act_quant_kernel(const void* __restrict__
       for (int j = 0; j < 8; ++j) q[8 * h + j] = q8(v[j], s);
     }
     if constexpr (LM != 0) {
-      constexpr int NW = LM / 2 - 1;
       const size_t keff = (size_t)K / LM * (2 * LM - 4);
-      uint32_t* o = (uint32_t*)(xq + (size_t)t * keff + (size_t)(2 * LM - 4) * c);
-#pragma unroll
-      for (int w = 0; w < NW; ++w)
-        o[w] = q[2 * w] | (q[2 * w + 1] << 8) | (q[2 * w + 2] << 16) | (q[2 * w + 3] << 24);
+      store_lifted<LM, CH>((uint32_t*)(xq + (size_t)t * keff + (size_t)(CH / LM) * (2 * LM - 4) * c), q);
     } else {
       const uint32_t lo = q[0] | (q[1] << 8) | (q[2] << 16) | (q[3] << 24);
       const uint32_t hi = q[4] | (q[5] << 8) | (q[6] << 16) | (q[7] << 24);
@@ -116,13 +128,13 @@ __device__ __forceinline__ float piece_value(const Piece<BF16>& p, int j) {
 }
 
 // One wave per token.  Lane l holds chunks l, l + 64, ... of its token's row (the first `cpl` of
-// the CPL register slots; cpl is uniform), CH elements each (8, or the LM elements of a lifting
-// group), loaded before the absmax so all of a lane's loads are in flight at once; the quantized
-// chunks are written from the registers.
+// the CPL register slots; cpl is uniform), CH elements each (8, or lcm(LM, 8) for lifting),
+// loaded before the absmax so all of a lane's loads are in flight at once; the quantized chunks
+// are written from the registers.
 template <bool BF16, int LM, int CPL>
 __device__ __forceinline__ void quant_row(const void* __restrict__ x, int K, int8_t* __restrict__ xq,
                                           float* __restrict__ xs, int t, int lane, int cpl) {
-  constexpr int CH = LM ? LM : 8;
+  constexpr int CH = chunk_elems<LM>();
   constexpr int PPC = CH / 8;             // pieces per chunk
   const int nchunk = K / CH;
   const size_t row = (size_t)t * K;
@@ -170,12 +182,8 @@ __device__ __forceinline__ void quant_row(const void* __restrict__ x, int K, int
 #pragma unroll
       for (int j = 0; j < 8; ++j) q[8 * h + j] = q8(piece_value<BF16>(p[i][h], j), s);
     if constexpr (LM != 0) {
-      constexpr int NW = LM / 2 - 1;
       const size_t keff = (size_t)K / LM * (2 * LM - 4);
-      uint32_t* o = (uint32_t*)(xq + (size_t)t * keff + (size_t)(2 * LM - 4) * c);
-#pragma unroll
-      for (int w = 0; w < NW; ++w)
-        o[w] = q[2 * w] | (q[2 * w + 1] << 8) | (q[2 * w + 2] << 16) | (q[2 * w + 3] << 24);
+      store_lifted<LM, CH>((uint32_t*)(xq + (size_t)t * keff + (size_t)(CH / LM) * (2 * LM - 4) * c), q);
     } else {
       const uint32_t lo = q[0] | (q[1] << 8) | (q[2] << 16) | (q[3] << 24);
       const uint32_t hi = q[4] | (q[5] << 8) | (q[6] << 16) | (q[7] << 24);
@@ -200,7 +208,7 @@ __global__ __launch_bounds__(256) void act_quant_row_kernel(const void* __restri
 // chunks of its own row, so a short-row matrix in a group with long rows reads nothing extra.
 template <bool BF16, int LM, int CPL>
 __global__ __launch_bounds__(256) void act_quant_group_kernel(QuantGroupArgs a) {
-  constexpr int CH = LM ? LM : 8;
+  constexpr int CH = chunk_elems<LM>();
   const int b = blockIdx.x;
   int m = 0;
   for (int i = 1; i < a.count; ++i)
@@ -216,22 +224,30 @@ __global__ __launch_bounds__(256) void act_quant_group_kernel(QuantGroupArgs a) 
 // CPL * CH for fp32; at most 128); false if the rows are too long for it.
 template <bool BF16, int LM, class F>
 static bool with_cpl(int64_t cpl, F&& f) {
-  constexpr int CH = LM ? LM : 8;
+  constexpr int CH = chunk_elems<LM>();
   constexpr int MAXR = 128 / (BF16 ? CH / 2 : CH);
-  if (cpl <= 4) f(std::integral_constant<int, 4>{});
-  else if (cpl <= 8) f(std::integral_constant<int, 8>{});
-  else if (cpl <= 12 && MAXR >= 12) f(std::integral_constant<int, (MAXR >= 12 ? 12 : 4)>{});
-  else if (cpl <= 16 && MAXR >= 16) f(std::integral_constant<int, (MAXR >= 16 ? 16 : 4)>{});
-  else if (cpl <= 24 && MAXR >= 24) f(std::integral_constant<int, (MAXR >= 24 ? 24 : 4)>{});
-  else if (cpl <= 32 && MAXR >= 32) f(std::integral_constant<int, (MAXR >= 32 ? 32 : 4)>{});
-  else return false;
-  return true;
+  bool done = false;
+  auto pick = [&](auto c) {
+    constexpr int C = decltype(c)::value;
+    if constexpr (C <= MAXR) {
+      if (!done && cpl <= C) { f(c); done = true; }
+    }
+  };
+  pick(std::integral_constant<int, 1>{});
+  pick(std::integral_constant<int, 2>{});
+  pick(std::integral_constant<int, 4>{});
+  pick(std::integral_constant<int, 8>{});
+  pick(std::integral_constant<int, 12>{});
+  pick(std::integral_constant<int, 16>{});
+  pick(std::integral_constant<int, 24>{});
+  pick(std::integral_constant<int, 32>{});
+  return done;
 }
 
 template <bool BF16, int LM>
 static bool launch_rows(const void* x, int64_t T, int64_t K, int8_t* xq, float* xs,
                         hipStream_t s) {
-  constexpr int CH = LM ? LM : 8;
+  constexpr int CH = chunk_elems<LM>();
   const dim3 grid((unsigned)((T + 3) / 4));
   return with_cpl<BF16, LM>((K / CH + 63) / 64, [&](auto c) {
     act_quant_row_kernel<BF16, LM, decltype(c)::value><<<grid, 256, 0, s>>>(x, (int)T, (int)K, xq, xs);
@@ -240,7 +256,7 @@ static bool launch_rows(const void* x, int64_t T, int64_t K, int8_t* xq, float* 
 
 template <bool BF16, int LM>
 static bool launch_group_rows(const QuantGroupArgs& a, hipStream_t s) {
-  constexpr int CH = LM ? LM : 8;
+  constexpr int CH = chunk_elems<LM>();
   int64_t cpl = 0;
   for (int i = 0; i < a.count; ++i) cpl = std::max<int64_t>(cpl, (a.K[i] / CH + 63) / 64);
   const dim3 grid((unsigned)a.block0[a.count]);
@@ -249,46 +265,39 @@ static bool launch_group_rows(const QuantGroupArgs& a, hipStream_t s) {
   });
 }
 
+// Calls f(std::integral_constant<int, LM>{}) for lift_M (0: no lifting).
+template <class F>
+static void with_lift(int lift_M, F&& f) {
+  if (lift_M == 0) f(std::integral_constant<int, 0>{});
+  else dispatch_m(lift_M, f);
+}
+
 hipError_t launch_act_quant(const void* x, int x_is_bf16, int64_t T, int64_t K, int lift_M,
                             int8_t* xq, float* x_scale, hipStream_t s) {
-  bool done;
-  if (x_is_bf16) {
-    if (lift_M == 8) done = launch_rows<true, 8>(x, T, K, xq, x_scale, s);
-    else if (lift_M == 16) done = launch_rows<true, 16>(x, T, K, xq, x_scale, s);
-    else done = launch_rows<true, 0>(x, T, K, xq, x_scale, s);
-  } else {
-    if (lift_M == 8) done = launch_rows<false, 8>(x, T, K, xq, x_scale, s);
-    else if (lift_M == 16) done = launch_rows<false, 16>(x, T, K, xq, x_scale, s);
-    else done = launch_rows<false, 0>(x, T, K, xq, x_scale, s);
-  }
+  bool done = false;
+  with_lift(lift_M, [&](auto lm) {
+    constexpr int LM = decltype(lm)::value;
+    done = x_is_bf16 ? launch_rows<true, LM>(x, T, K, xq, x_scale, s)
+                     : launch_rows<false, LM>(x, T, K, xq, x_scale, s);
+  });
   if (done) return hipGetLastError();
   const dim3 grid((unsigned)T);
-  auto run = [&](auto kern) { kern<<<grid, 256, 0, s>>>(x, (int)K, xq, x_scale); };
-  if (x_is_bf16) {
-    if (lift_M == 8) run(act_quant_kernel<true, 8>);
-    else if (lift_M == 16) run(act_quant_kernel<true, 16>);
-    else run(act_quant_kernel<true, 0>);
-  } else {
-    if (lift_M == 8) run(act_quant_kernel<false, 8>);
-    else if (lift_M == 16) run(act_quant_kernel<false, 16>);
-    else run(act_quant_kernel<false, 0>);
-  }
+  with_lift(lift_M, [&](auto lm) {
+    constexpr int LM = decltype(lm)::value;
+    if (x_is_bf16) act_quant_kernel<true, LM><<<grid, 256, 0, s>>>(x, (int)K, xq, x_scale);
+    else act_quant_kernel<false, LM><<<grid, 256, 0, s>>>(x, (int)K, xq, x_scale);
+  });
   return hipGetLastError();
 }
 
 hipError_t launch_act_quant_group(const QuantGroupArgs& a, int x_is_bf16, int lift_M,
                                   hipStream_t s) {
   if (a.count < 1 || a.block0[a.count] < 1) return hipSuccess;
-  bool done;
-  if (x_is_bf16) {
-    if (lift_M == 8) done = launch_group_rows<true, 8>(a, s);
-    else if (lift_M == 16) done = launch_group_rows<true, 16>(a, s);
-    else done = launch_group_rows<true, 0>(a, s);
-  } else {
-    if (lift_M == 8) done = launch_group_rows<false, 8>(a, s);
-    else if (lift_M == 16) done = launch_group_rows<false, 16>(a, s);
-    else done = launch_group_rows<false, 0>(a, s);
-  }
+  bool done = false;
+  with_lift(lift_M, [&](auto lm) {
+    constexpr int LM = decltype(lm)::value;
+    done = x_is_bf16 ? launch_group_rows<true, LM>(a, s) : launch_group_rows<false, LM>(a, s);
+  });
   if (done) return hipGetLastError();
   // a row too long for the register budget: the matrices one launch each
   for (int i = 0; i < a.count; ++i) {

@@ -14,6 +14,7 @@
 #include "chain.hpp"
 #include "gemm_group.hpp"
 #include "quant_group.hpp"
+#include "device_common.hpp"
 #include "launch.hpp"
 #include "pack_group.hpp"
 
@@ -30,18 +31,37 @@ int64_t keff_of(int64_t K, int M, int layout) {
   return (layout == BL_LAYOUT_SPARSE && M > 4) ? K / M * (2 * M - 4) : K;
 }
 
+bool even_m(int M) { return M >= 4 && M <= 16 && M % 2 == 0; }
+
+// K granularity of a layout: whole M-groups and whole MFMA steps on the packed axis (64
+// positions for the sparse instruction, 32 for the dense one); lifted layouts also need whole
+// lifting chunks of lcm(M, 8) positions.
+int64_t k_quantum(int M, int layout) {
+  if (layout == BL_LAYOUT_DENSE2) return bl::lcm_i(32, M);
+  if (M == 4) return 64;
+  for (int64_t k = M;; k += M)
+    if (k / M * (2 * M - 4) % 64 == 0 && k % bl::lcm_i(M, 8) == 0) return k;
+}
+
+// The N:M mask and layout alone: BL_OK or BL_ENOTSUP.
+int check_nm(int N, int M, int layout) {
+  if (layout != BL_LAYOUT_SPARSE && layout != BL_LAYOUT_DENSE2) return BL_ENOTSUP;
+  if (!even_m(M)) return BL_ENOTSUP;
+  if (layout == BL_LAYOUT_SPARSE) {
+    // 2:4, or (M-2):M as M/2 - 1 overlapping 2:4 windows
+    if (!((N == 2 && M == 4) || (M > 4 && N == M - 2))) return BL_ENOTSUP;
+  } else {
+    if (N < 1 || N > M) return BL_ENOTSUP;
+  }
+  return BL_OK;
+}
+
 // Shape rules of the packed layout; returns BL_OK and the packed K axis, or a status.
 int check_shape(int64_t n, int64_t K, int N, int M, int layout, int64_t* keff) {
-  if (layout != BL_LAYOUT_SPARSE && layout != BL_LAYOUT_DENSE2) return BL_ENOTSUP;
-  if (layout == BL_LAYOUT_SPARSE) {
-    if (!((N == 2 && M == 4) || (N == 6 && M == 8) || (N == 14 && M == 16))) return BL_ENOTSUP;
-  } else {
-    if (!(M == 4 || M == 8 || M == 16) || N < 1 || N > M) return BL_ENOTSUP;
-  }
+  const int nm = check_nm(N, M, layout);
+  if (nm != BL_OK) return nm;
   if (n < 1 || K < 1) return BL_EINVAL;
-  // whole 64-position sparse MFMA steps on the packed axis (and whole 32-position dense steps)
-  const int64_t kq = layout == BL_LAYOUT_DENSE2 ? 32 : (M == 4 ? 64 : M == 8 ? 128 : 256);
-  if (K % kq != 0 || K % M != 0) return BL_EINVAL;
+  if (K % k_quantum(M, layout) != 0) return BL_EINVAL;
   if (n > INT32_MAX || K > INT32_MAX) return BL_EINVAL;
   if ((uint64_t)n * (uint64_t)K >= (1ull << 32)) return BL_EINVAL;
   const int64_t ke = keff_of(K, M, layout);
@@ -56,8 +76,8 @@ int status_of(hipError_t e) { return e == hipSuccess ? BL_OK : BL_EIO; }
 int check_quant(const void* x, int x_dtype, int64_t T, int64_t K, int lift_M, const int8_t* xq,
                 const float* x_scale) {
   if (x_dtype != BL_DTYPE_F32 && x_dtype != BL_DTYPE_BF16) return BL_ENOTSUP;
-  if (lift_M != 0 && lift_M != 8 && lift_M != 16) return BL_EINVAL;
-  if (lift_M == 16 && K % 16 != 0) return BL_EINVAL;
+  if (lift_M != 0 && !(even_m(lift_M) && lift_M >= 6)) return BL_EINVAL;
+  if (lift_M != 0 && K % bl::lcm_i(lift_M, 8) != 0) return BL_EINVAL;
   if (T < 0 || T > INT32_MAX || K < 8 || K % 8 != 0 || K > (int64_t)1 << 24) return BL_EINVAL;
   if (T == 0) return BL_OK;
   if (!aligned16(x) || !aligned16(xq) || !aligned4(x_scale)) return BL_EINVAL;
@@ -538,7 +558,7 @@ int plan_pack_group(const bl_pack_desc* d, int64_t count, int N, int M, int layo
     it.ws = ws + (size_t)i * kPackWsSlice;
     it.n = (int32_t)q.n;
     it.K = (int32_t)q.K;
-    it.k_tiles = (int32_t)((q.K + 255) / 256);
+    it.k_tiles = (int32_t)((q.K + bl::pack_cols(layout, M) - 1) / bl::pack_cols(layout, M));
   }
   // any overlap involving an output is an error (masters may be shared or overlap each other)
   std::sort(rs.begin(), rs.end(), [](const R& a, const R& b) { return a.lo < b.lo; });
@@ -818,8 +838,7 @@ int bitlinear_pack_group_build(const bl_pack_desc* descs, int64_t count, int N, 
 
 int bitlinear_pack_group(const void* table, const bl_pack_group_plan* plan, void* stream) {
   if (!plan || !aligned16(table)) return BL_EINVAL;
-  int64_t ke = 0;
-  const int st = check_shape(1, 256, plan->N, plan->M, plan->layout, &ke);
+  const int st = check_nm(plan->N, plan->M, plan->layout);
   if (st != BL_OK) return st;
   if (plan->count < 1 || plan->count > 4096 || plan->pack_blocks < 1 ||
       plan->pack_blocks > INT32_MAX)
@@ -876,8 +895,7 @@ int bitlinear_gemm_group_build(const bl_fwd_desc* descs, int64_t count, int N, i
 
 int bitlinear_gemm_group(const void* table, const bl_gemm_group_plan* plan, void* stream) {
   if (!plan || !aligned16(table)) return BL_EINVAL;
-  int64_t ke = 0;
-  const int st = check_shape(1, 256, plan->N, plan->M, plan->layout, &ke);
+  const int st = check_nm(plan->N, plan->M, plan->layout);
   if (st != BL_OK) return st;
   if (plan->jobs < 1 || plan->jobs > INT32_MAX) return BL_EINVAL;
   return status_of(bl::launch_gemm_group(table, plan->jobs, plan->layout, (hipStream_t)stream));
@@ -955,8 +973,7 @@ int bitlinear_group_build(const bl_fwd_desc* descs, int64_t count, int N, int M,
 
 int bitlinear_fwd_group(const void* table, int64_t work_items, int N, int M, int layout,
                         void* stream) {
-  int64_t ke = 0;
-  const int st = check_shape(1, 256, N, M, layout, &ke);  // N:M and layout only
+  const int st = check_nm(N, M, layout);
   if (st != BL_OK) return st;
   if (work_items < 0 || work_items > INT32_MAX) return BL_EINVAL;
   if (work_items == 0) return BL_OK;
@@ -982,8 +999,7 @@ int bitlinear_group_fused_build(const bl_fwd_x_desc* descs, int64_t count, int N
 
 int bitlinear_fwd_group_fused(const void* table, int64_t work_items, int N, int M, int layout,
                               void* stream) {
-  int64_t ke = 0;
-  const int st = check_shape(1, 256, N, M, layout, &ke);  // N:M and layout only
+  const int st = check_nm(N, M, layout);
   if (st != BL_OK) return st;
   if (layout == BL_LAYOUT_SPARSE && M != 4) return BL_ENOTSUP;
   if (work_items < 0 || work_items > INT32_MAX) return BL_EINVAL;
@@ -1133,8 +1149,7 @@ int bitlinear_bwd_group_build(const bl_bwd_desc* descs, int64_t count, int64_t T
 
 int bitlinear_bwd_group(const void* table, const bl_bwd_group_plan* plan, void* stream) {
   if (!plan || !aligned16(table)) return BL_EINVAL;
-  int64_t ke = 0;
-  const int st = check_shape(1, 256, plan->N, plan->M, plan->layout, &ke);
+  const int st = check_nm(plan->N, plan->M, plan->layout);
   if (st != BL_OK) return st;
   if (plan->prep_blocks < 0 || plan->prep_blocks > INT32_MAX || plan->jobs < 0 ||
       plan->jobs > INT32_MAX)

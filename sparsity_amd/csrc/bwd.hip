@@ -574,15 +574,12 @@ hipError_t launch_bwd(const uint16_t* dy, int64_t T, int64_t n, const int8_t* xq
     const int64_t keff = (layout == kLayoutSparse && M > 4) ? K / M * (2 * M - 4) : K;
     const int U = (int)(layout == kLayoutSparse ? keff / 32 : K / 16);
     const int groups = (int)(K / M), pairs = (int)(w.n32 / 2);
-    if (layout == kLayoutSparse) {
-      if (M == 4) launch_wt<kLayoutSparse, 4>(codes, meta, U, groups, pairs, (uint32_t*)wt, s);
-      else if (M == 8) launch_wt<kLayoutSparse, 8>(codes, meta, U, groups, pairs, (uint32_t*)wt, s);
-      else launch_wt<kLayoutSparse, 16>(codes, meta, U, groups, pairs, (uint32_t*)wt, s);
-    } else {
-      if (M == 4) launch_wt<kLayoutDense2, 4>(codes, nullptr, U, groups, pairs, (uint32_t*)wt, s);
-      else if (M == 8) launch_wt<kLayoutDense2, 8>(codes, nullptr, U, groups, pairs, (uint32_t*)wt, s);
-      else launch_wt<kLayoutDense2, 16>(codes, nullptr, U, groups, pairs, (uint32_t*)wt, s);
-    }
+    const bool ok = dispatch_m(M, [&](auto m) {
+      constexpr int MM = decltype(m)::value;
+      if (layout == kLayoutSparse) launch_wt<kLayoutSparse, MM>(codes, meta, U, groups, pairs, (uint32_t*)wt, s);
+      else launch_wt<kLayoutDense2, MM>(codes, nullptr, U, groups, pairs, (uint32_t*)wt, s);
+    });
+    if (!ok) return hipErrorInvalidValue;
     const uint16_t* a = dy;
     if (w.n32 != n) {
       uint16_t* dyp = (uint16_t*)(base + w.dyp_off);
@@ -617,15 +614,12 @@ hipError_t launch_bwd_group(const void* table, int64_t prep_blocks, int64_t jobs
   const uint8_t* t = (const uint8_t*)table;
   if (prep_blocks > 0) {
     const unsigned g = (unsigned)prep_blocks;
-    if (layout == kLayoutSparse) {
-      if (M == 4) bwd_prep_kernel<kLayoutSparse, 4><<<g, 256, 0, s>>>(t);
-      else if (M == 8) bwd_prep_kernel<kLayoutSparse, 8><<<g, 256, 0, s>>>(t);
-      else bwd_prep_kernel<kLayoutSparse, 16><<<g, 256, 0, s>>>(t);
-    } else {
-      if (M == 4) bwd_prep_kernel<kLayoutDense2, 4><<<g, 256, 0, s>>>(t);
-      else if (M == 8) bwd_prep_kernel<kLayoutDense2, 8><<<g, 256, 0, s>>>(t);
-      else bwd_prep_kernel<kLayoutDense2, 16><<<g, 256, 0, s>>>(t);
-    }
+    const bool ok = dispatch_m(M, [&](auto m) {
+      constexpr int MM = decltype(m)::value;
+      if (layout == kLayoutSparse) bwd_prep_kernel<kLayoutSparse, MM><<<g, 256, 0, s>>>(t);
+      else bwd_prep_kernel<kLayoutDense2, MM><<<g, 256, 0, s>>>(t);
+    });
+    if (!ok) return hipErrorInvalidValue;
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

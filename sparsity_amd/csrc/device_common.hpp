@@ -3,12 +3,45 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace bl {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+
+// Group sizes M of the N:M masks: 2:4, and (M-2):M for even M = 6..16 as M/2 - 1 overlapping 2:4
+// windows (SlideSparse abstract, Sliding Window Decomposition: (2N-2):2N into N-1 windows).
+// Calls f(std::integral_constant<int, M>{}) for a supported M; false otherwise.
+template <class F>
+inline bool dispatch_m(int M, F&& f) {
+  switch (M) {
+    case 4: f(std::integral_constant<int, 4>{}); return true;
+    case 6: f(std::integral_constant<int, 6>{}); return true;
+    case 8: f(std::integral_constant<int, 8>{}); return true;
+    case 10: f(std::integral_constant<int, 10>{}); return true;
+    case 12: f(std::integral_constant<int, 12>{}); return true;
+    case 14: f(std::integral_constant<int, 14>{}); return true;
+    case 16: f(std::integral_constant<int, 16>{}); return true;
+    default: return false;
+  }
+}
+
+constexpr int gcd_i(int a, int b) { return b ? gcd_i(b, a % b) : a; }
+constexpr int lcm_i(int a, int b) { return a / gcd_i(a, b) * b; }
+
+// Dense K columns of one pack tile (at most 256): whole M-groups, and whole 32-slot fragments of
+// the packed row (SPARSE: (M-2)/M slots per column, 2:4 one per two; DENSE2: one per column).
+constexpr int pack_cols(int layout, int M) {
+  int best = 0;
+  for (int kb = M; kb <= 256; kb += M) {
+    const int slots = layout == 0 ? (M == 4 ? kb / 2 : kb / M * (M - 2)) : kb;
+    if (slots % 32 == 0) best = kb;
+  }
+  return best;
+}
 
 constexpr int kLayoutSparse = 0;
 constexpr int kLayoutDense2 = 1;

@@ -296,9 +296,10 @@ __global__ __launch_bounds__(kExactThreads) void gamma_exact_kernel(const float*
   gamma_exact_block(W, count, ws, gamma_out, blockIdx.x, gridDim.x);
 }
 
-constexpr int kPackKB = 256;  // dense K columns per pack tile
+constexpr int kPackWidth = 256;  // LDS width of a pack tile (fp32 columns)
 
-// One block packs one 32-row panel x 256 dense columns.  Phase 1 stages the fp32 tile in LDS with
+// One block packs one 32-row panel x KB dense columns (KB = pack_cols: whole M-groups and whole
+// 32-slot fragments, at most 256).  Phase 1 stages the fp32 tile in LDS with
 // coalesced 1 KB row reads; phase 2 turns each M-group into slot bytes (code | index << 2);
 // phase 3 assembles 16-slot units into code/meta dwords, which land contiguously in the tiled
 // layout (unit v = 32*u + r of the tile is dword base + v).
@@ -308,20 +309,21 @@ __device__ __forceinline__ void pack_tile(const float* __restrict__ W, int n, in
                                           uint32_t* __restrict__ codes,
                                           uint32_t* __restrict__ meta, int blk) {
   constexpr bool SP = LAYOUT == kLayoutSparse;
-  constexpr int WS = kPackKB + 4;                                      // padded fp32 row
-  constexpr int NKEEP = M == 4 ? 2 : M - 2;                           // SPARSE: 2:4, 6:8, 14:16
-  constexpr int SLOTS = SP ? kPackKB * NKEEP / M : kPackKB;
+  constexpr int KB = pack_cols(LAYOUT, M);
+  constexpr int WS = kPackWidth + 4;                                   // padded fp32 row
+  constexpr int NKEEP = M == 4 ? 2 : M - 2;                           // SPARSE: 2:4, (M-2):M
+  constexpr int SLOTS = SP ? KB * NKEEP / M : KB;
   constexpr int SS = SLOTS + 16;                                       // padded slot row
-  constexpr int GPR = kPackKB / M;                                     // groups per tile row
+  constexpr int GPR = KB / M;                                          // groups per tile row
   constexpr int UPR = SLOTS / 16;                                      // units per tile row
   __shared__ __attribute__((aligned(16))) float tile[32 * WS];
   __shared__ __attribute__((aligned(16))) uint8_t slots[32 * SS];
 
   const int P = blk / k_tiles;
   const int kb = blk % k_tiles;
-  const int k0 = kb * kPackKB;
+  const int k0 = kb * KB;
   const int r0 = P * kPanel;
-  const int kw = min(kPackKB, K - k0);
+  const int kw = min(KB, K - k0);
 
   // all eight 16-byte tile loads before the first LDS store (addresses clamped into the matrix;
   // out-of-range rows and columns are zeroed after the load)
@@ -482,20 +484,16 @@ hipError_t launch_pack(const float* W, int64_t n, int64_t K, int N, int M, int l
   gamma_partial_kernel<<<kGammaBlocks, kGammaThreads, 0, s>>>((const float4*)W, count / 4, ws);
   gamma_exact_kernel<<<kExactBlocks, kExactThreads, 0, s>>>(W, count, ws, gamma);
   const int panels = (int)((n + kPanel - 1) / kPanel);
-  const int k_tiles = (int)((K + kPackKB - 1) / kPackKB);
+  const int k_tiles = (int)((K + pack_cols(layout, M) - 1) / pack_cols(layout, M));
   const dim3 grid((unsigned)(panels * k_tiles));
-  auto run = [&](auto kern, uint32_t* mt) {
-    kern<<<grid, 256, 0, s>>>(W, (int)n, (int)K, N, k_tiles, ws, codes, mt);
-  };
-  if (layout == kLayoutSparse) {
-    if (M == 4) run(pack_kernel<kLayoutSparse, 4>, meta);
-    else if (M == 8) run(pack_kernel<kLayoutSparse, 8>, meta);
-    else run(pack_kernel<kLayoutSparse, 16>, meta);
-  } else {
-    if (M == 4) run(pack_kernel<kLayoutDense2, 4>, nullptr);
-    else if (M == 8) run(pack_kernel<kLayoutDense2, 8>, nullptr);
-    else run(pack_kernel<kLayoutDense2, 16>, nullptr);
-  }
+  const bool ok = dispatch_m(M, [&](auto m) {
+    constexpr int MM = decltype(m)::value;
+    if (layout == kLayoutSparse)
+      pack_kernel<kLayoutSparse, MM><<<grid, 256, 0, s>>>(W, (int)n, (int)K, N, k_tiles, ws, codes, meta);
+    else
+      pack_kernel<kLayoutDense2, MM><<<grid, 256, 0, s>>>(W, (int)n, (int)K, N, k_tiles, ws, codes, nullptr);
+  });
+  if (!ok) return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
@@ -553,15 +551,12 @@ hipError_t launch_pack_group(const void* table, int64_t count, int64_t pack_bloc
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const unsigned g = (unsigned)pack_blocks;
-  if (layout == kLayoutSparse) {
-    if (M == 4) pack_group_kernel<kLayoutSparse, 4><<<g, 256, 0, s>>>(t);
-    else if (M == 8) pack_group_kernel<kLayoutSparse, 8><<<g, 256, 0, s>>>(t);
-    else pack_group_kernel<kLayoutSparse, 16><<<g, 256, 0, s>>>(t);
-  } else {
-    if (M == 4) pack_group_kernel<kLayoutDense2, 4><<<g, 256, 0, s>>>(t);
-    else if (M == 8) pack_group_kernel<kLayoutDense2, 8><<<g, 256, 0, s>>>(t);
-    else pack_group_kernel<kLayoutDense2, 16><<<g, 256, 0, s>>>(t);
-  }
+  const bool ok = dispatch_m(M, [&](auto m) {
+    constexpr int MM = decltype(m)::value;
+    if (layout == kLayoutSparse) pack_group_kernel<kLayoutSparse, MM><<<g, 256, 0, s>>>(t);
+    else pack_group_kernel<kLayoutDense2, MM><<<g, 256, 0, s>>>(t);
+  });
+  if (!ok) return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

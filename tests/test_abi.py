@@ -48,7 +48,9 @@ def test_layout_version_and_strerror(L):
     (1, 64, 2, 4, 0), (6912, 2560, 2, 4, 0), (2560, 6912, 2, 4, 0), (11008, 4096, 2, 4, 0),
     (4096, 4096, 6, 8, 0), (45, 384, 6, 8, 0), (33, 288, 2, 4, 1), (33, 288, 6, 8, 1),
     (8640, 3200, 2, 4, 0), (3200, 8640, 2, 4, 0), (100, 96, 4, 4, 1),
-    (4096, 4096, 14, 16, 0), (45, 512, 14, 16, 0), (33, 288, 14, 16, 1)])
+    (4096, 4096, 14, 16, 0), (45, 512, 14, 16, 0), (33, 288, 14, 16, 1),
+    (45, 240, 4, 6, 0), (33, 480, 8, 10, 0), (33, 384, 10, 12, 0), (33, 224, 12, 14, 0),
+    (33, 96, 4, 6, 1), (33, 160, 8, 10, 1), (33, 96, 10, 12, 1), (33, 224, 12, 14, 1)])
 def test_packed_bytes_match_layout(L, n, K, N, M, layout):
     st, cb, mb, ke, ws = L.bitlinear_packed_bytes(n, K, N, M, layout)
     assert st == 0
@@ -69,6 +71,13 @@ def test_packed_bytes_match_layout(L, n, K, N, M, layout):
     (64, 256, 12, 16, 0, -95),     # SPARSE windows are (M-2):M
     (64, 256, 6, 16, 0, -95),
     (1 << 20, 1 << 12, 2, 4, 0, -22),  # n*K >= 2^32
+    (64, 120, 4, 6, 0, -22),       # 4:6 needs K % 48 (whole lifted MFMA steps)
+    (64, 220, 8, 10, 0, -22),      # 8:10 needs K % 40
+    (64, 240, 10, 12, 0, -22),     # 10:12 needs K % 192
+    (64, 168, 12, 14, 0, -22),     # 12:14 needs K % 112
+    (64, 240, 3, 6, 0, -95),       # (M-2):M only
+    (64, 224, 2, 7, 1, -95),       # even M only
+    (64, 48, 4, 6, 1, -22),        # DENSE2 4:6 needs K % 96
 ])
 def test_packed_bytes_rejects(L, n, K, N, M, layout, want):
     assert L.bitlinear_packed_bytes(n, K, N, M, layout)[0] == want
@@ -102,6 +111,13 @@ def test_act_quant_rejects_before_launch(L):
     assert L.act_quant_i8(P, 2, 4, 256, 0, P, P, None) == -95        # dtype
     assert L.act_quant_i8(P, 0, 4, 256, 4, P, P, None) == -22        # lift_M
     assert L.act_quant_i8(P, 0, 4, 264, 16, P, P, None) == -22       # lift 16 needs K % 16
+    assert L.act_quant_i8(P, 0, 4, 256, 7, P, P, None) == -22        # odd lift
+    assert L.act_quant_i8(P, 0, 4, 256, 18, P, P, None) == -22       # M > 16
+    assert L.act_quant_i8(P, 0, 4, 252, 6, P, P, None) == -22        # lift 6 needs K % 24
+    assert L.act_quant_i8(P, 0, 4, 308, 14, P, P, None) == -22       # lift 14 needs K % 56
+    assert L.act_quant_i8(P, 0, 0, 240, 6, P, P, None) == 0          # valid, nothing enqueued
+    assert L.act_quant_i8(P, 0, 0, 280, 10, P, P, None) == 0
+    assert L.act_quant_i8(P, 0, 0, 216, 12, P, P, None) == 0
     assert L.act_quant_i8(P, 0, -1, 256, 0, P, P, None) == -22       # T < 0
     assert L.act_quant_i8(P, 0, 4, 100, 0, P, P, None) == -22        # K % 8
     assert L.act_quant_i8(None, 0, 4, 256, 0, P, P, None) == -22

@@ -27,7 +27,7 @@ def _kq(N, M, layout):
 
 
 def _lift(M, layout):
-    return M if (layout == O.LAYOUT_SPARSE and M in (8, 16)) else 0
+    return M if (layout == O.LAYOUT_SPARSE and M in O.WINDOW_M) else 0
 
 
 def _make(n, K, T, N, M, layout, seed, with_acc=True):

@@ -32,7 +32,7 @@ def _make(n, K, T, N, M, layout, seed, x=None):
     if x is None:
         x = act_normal(g, max(T, 1), K)[:T]
     ref = O.pack(W, N, M, layout)
-    lift = M if (layout == O.LAYOUT_SPARSE and M in (8, 16)) else 0
+    lift = M if (layout == O.LAYOUT_SPARSE and M in O.WINDOW_M) else 0
     codes, meta, gamma = S.pack(dev(W), N, M, layout)
     if T:
         xq, sc = S.act_quant(dev(x), lift)

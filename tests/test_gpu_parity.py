@@ -22,7 +22,7 @@ CASES_NM = [(2, 4, O.LAYOUT_SPARSE), (6, 8, O.LAYOUT_SPARSE), (2, 4, O.LAYOUT_DE
 
 
 def _lift(N, M, layout):
-    return M if (layout == O.LAYOUT_SPARSE and M in (8, 16)) else 0
+    return M if (layout == O.LAYOUT_SPARSE and M in O.WINDOW_M) else 0
 
 
 def _kq(N, M, layout):

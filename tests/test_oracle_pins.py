@@ -217,7 +217,19 @@ def test_windows_1416_golden():
             assert wins[w] == [int(v) for v in kv[f"w{w}{sfx}"]]
 
 
-@pytest.mark.parametrize("M,count", [(8, 28), (16, 120)])
+@pytest.mark.parametrize("prefix,M", [("m6", 6), ("m6b", 6), ("m10", 10), ("m10b", 10),
+                                      ("m12", 12), ("m14", 14)])
+def test_windows_general_golden(prefix, M):
+    """Hand-derived decompositions of 4:6, 8:10, 10:12 and 12:14 groups (windows_general.txt)."""
+    kv = read_kv("windows_general.txt")
+    kept = [int(v) for v in kv[prefix + "_kept"]]
+    wins = O.window_table(M)[sum(1 << p for p in kept)]
+    assert len(wins) == M // 2 - 1
+    for w in range(M // 2 - 1):
+        assert wins[w] == [int(v) for v in kv[f"{prefix}_w{w}"]]
+
+
+@pytest.mark.parametrize("M,count", [(6, 15), (8, 28), (10, 45), (12, 66), (14, 91), (16, 120)])
 def test_windows_cover_every_mask(M, count):
     """Every (M-2):M mask splits into M/2 - 1 windows of two kept positions each, each position
     inside its window's span (the decomposition is lossless for every mask)."""
@@ -234,6 +246,10 @@ def test_windows_cover_every_mask(M, count):
 # ------------------------------------------------------------------------------------------
 # pack layout
 # ------------------------------------------------------------------------------------------
+
+# K per group size M: whole groups and whole 64-position sparse MFMA steps on the lifted axis
+GENERAL_K = {4: 256, 6: 240, 8: 256, 10: 240, 12: 384, 14: 224, 16: 256}
+
 
 def test_pack_golden_unit():
     kv = read_kv("pack_2of4_unit.txt")
@@ -258,10 +274,12 @@ def test_pack_golden_unit():
 
 @pytest.mark.parametrize("N,M,layout", [(2, 4, O.LAYOUT_SPARSE), (6, 8, O.LAYOUT_SPARSE),
                                         (14, 16, O.LAYOUT_SPARSE), (2, 4, O.LAYOUT_DENSE2),
-                                        (6, 8, O.LAYOUT_DENSE2), (14, 16, O.LAYOUT_DENSE2)])
+                                        (6, 8, O.LAYOUT_DENSE2), (14, 16, O.LAYOUT_DENSE2),
+                                        (4, 6, O.LAYOUT_SPARSE), (8, 10, O.LAYOUT_SPARSE),
+                                        (10, 12, O.LAYOUT_SPARSE), (12, 14, O.LAYOUT_SPARSE)])
 def test_pack_roundtrip(N, M, layout):
     g = np.random.default_rng(N + M + layout)
-    n, K = 45, 256
+    n, K = 45, GENERAL_K[M]
     W = g.normal(0, 0.02, (n, K)).astype(np.float32)
     p = O.pack(W, N, M, layout)
     vals, idx = O.unpack_slots(p["codes"], p["meta"], n, K, N, M, layout)
@@ -330,6 +348,23 @@ def test_lift_68():
     assert L[0].tolist() == [0, 1, 2, 3, 2, 3, 4, 5, 4, 5, 6, 7, 8, 9, 10, 11, 10, 11, 12, 13, 12, 13, 14, 15]
 
 
+def test_lift_general():
+    """Written out by hand from the lifting rule (window w of a group = its positions 2w..2w+3):
+    4:6 makes 8 of every 6 values, 8:10 16 of every 10, 10:12 20 of 12, 12:14 24 of 14."""
+    q = np.arange(12, dtype=np.int64).reshape(1, 12).astype(np.int8)
+    assert O.lift(q, 6)[0].tolist() == [0, 1, 2, 3, 2, 3, 4, 5, 6, 7, 8, 9, 8, 9, 10, 11]
+    q = np.arange(10, dtype=np.int64).reshape(1, 10).astype(np.int8)
+    assert O.lift(q, 10)[0].tolist() == [0, 1, 2, 3, 2, 3, 4, 5, 4, 5, 6, 7, 6, 7, 8, 9]
+    q = np.arange(12, dtype=np.int64).reshape(1, 12).astype(np.int8)
+    assert O.lift(q, 12)[0].tolist() == [0, 1, 2, 3, 2, 3, 4, 5, 4, 5, 6, 7, 6, 7, 8, 9,
+                                         8, 9, 10, 11]
+    q = np.arange(14, dtype=np.int64).reshape(1, 14).astype(np.int8)
+    assert O.lift(q, 14)[0].tolist() == [0, 1, 2, 3, 2, 3, 4, 5, 4, 5, 6, 7, 6, 7, 8, 9,
+                                         8, 9, 10, 11, 10, 11, 12, 13]
+    assert [O.k_eff(k, m - 2, m, O.LAYOUT_SPARSE) for k, m in ((240, 6), (240, 10), (384, 12),
+                                                              (224, 14))] == [320, 384, 640, 384]
+
+
 # ------------------------------------------------------------------------------------------
 # accumulation and rescale
 # ------------------------------------------------------------------------------------------
@@ -349,17 +384,19 @@ def test_acc_bruteforce_tiny():
 
 @pytest.mark.parametrize("N,M,layout", [(2, 4, O.LAYOUT_SPARSE), (6, 8, O.LAYOUT_SPARSE),
                                         (14, 16, O.LAYOUT_SPARSE), (2, 4, O.LAYOUT_DENSE2),
-                                        (14, 16, O.LAYOUT_DENSE2)])
+                                        (14, 16, O.LAYOUT_DENSE2), (4, 6, O.LAYOUT_SPARSE),
+                                        (8, 10, O.LAYOUT_SPARSE), (10, 12, O.LAYOUT_SPARSE),
+                                        (12, 14, O.LAYOUT_SPARSE)])
 def test_acc_forms_agree(N, M, layout):
-    """Form i (dense int64 matmul of W_eff) equals form ii (add/sub over packed slots); for 6:8
-    and 14:16 the lifted 2:4 windows against lifted activations equal the dense product
+    """Form i (dense int64 matmul of W_eff) equals form ii (add/sub over packed slots); for the
+    (M-2):M windows the lifted 2:4 windows against lifted activations equal the dense product
     (lossless)."""
     g = np.random.default_rng(20 + N)
-    n, K, T = 40, 256, 9
+    n, K, T = 40, GENERAL_K[M], 9
     W = g.normal(0, 0.02, (n, K)).astype(np.float32)
     x = g.standard_normal((T, K)).astype(np.float32)
     p = O.pack(W, N, M, layout)
-    lift = M if (layout == O.LAYOUT_SPARSE and M in (8, 16)) else 0
+    lift = M if (layout == O.LAYOUT_SPARSE and M in O.WINDOW_M) else 0
     xq, _ = O.act_quant(x, lift)
     q, _ = O.act_quant(x, 0)
     vals, idx = O.unpack_slots(p["codes"], p["meta"], n, K, N, M, layout)
