@@ -548,12 +548,12 @@ def _event_ms(torch, fn, iters):
     return float(np.mean([a.elapsed_time(b) for a, b in ev]))
 
 
-def windows_leg(S, torch, N, M, iters=10):
+def windows_leg(S, torch, N, M, iters=10, K=4096):
     """(M-2):M through M/2 - 1 overlapping 2:4 windows (lifted activations, sparse MFMA) against
-    the dense-stored path of the same masked ternary weights (dense MFMA): 2048 x 4096 -> 4096."""
-    n, K, T = 4096, 4096, 2048
+    the dense-stored path of the same masked ternary weights (dense MFMA): 2048 x K -> 4096."""
+    n, T = 4096, 2048
     g = torch.Generator(device="cuda")
-    g.manual_seed(68 if M == 8 else 1416)
+    g.manual_seed(68 if M == 8 else 1416 if M == 16 else 1000 + M)
     W = (torch.randn((n, K), generator=g, device="cuda", dtype=torch.float32) * 0.02).contiguous()
     cs, ms, gs = S.pack(W, N, M, S.BL_LAYOUT_SPARSE)
     cd, _, gd = S.pack(W, N, M, S.BL_LAYOUT_DENSE2)
@@ -575,7 +575,7 @@ def windows_leg(S, torch, N, M, iters=10):
         raise RuntimeError(f"{N}:{M} window path and dense path disagree")
     ops = 2.0 * T * K * n
     windows = M // 2 - 1
-    return {"workload": f"{N}:{M} as {windows} overlapping 2:4 windows, 2048 tokens x 4096 -> 4096, "
+    return {"workload": f"{N}:{M} as {windows} overlapping 2:4 windows, 2048 tokens x {K} -> 4096, "
                         "N(0,1) bf16",
             "windows_TOPS": round(ops / (t_s * 1e-3) / 1e12, 1),
             "dense_TOPS": round(ops / (t_d * 1e-3) / 1e12, 1),
@@ -1120,6 +1120,14 @@ def main():
             log(f"{N}:{M} leg")
             out[key] = windows_leg(S, torch, N, M)
             log(f"{N}:{M} windows {out[key]['windows_TOPS']} TOPS, dense {out[key]['dense_TOPS']} TOPS")
+        # the other (2N-2):2N group sizes, K near 4096 where windows and dense storage both fit
+        gen = {}
+        for N, M, K in ((4, 6, 3840), (8, 10, 3840), (10, 12, 3840), (12, 14, 3584)):
+            r = windows_leg(S, torch, N, M, K=K)
+            gen[f"{N}:{M}"] = {k: r[k] for k in ("workload", "windows_TOPS", "dense_TOPS",
+                                                 "speedup_vs_dense", "bound", "outputs_identical")}
+            log(f"{N}:{M} windows {r['windows_TOPS']} TOPS, dense {r['dense_TOPS']} TOPS")
+        out["windows_general"] = gen
         log("training-step layer set leg")
         out["train_step"] = train_step_leg(S, torch)
         log(f"train step {out['train_step']['step_ms']} ms")
