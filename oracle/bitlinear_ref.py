@@ -59,6 +59,10 @@ Packed layout (layout id 2), the format of the library's packed buffers:
   codes 0, every window's indices (0, 1)), and unit (r, c) lives at dword
   ((r // 32) * (U // 2) + c // 2) * 64 + (c % 2) * 32 + r % 32, where U is the
   number of units per row (K_eff / 32 for SPARSE, K / 16 for DENSE2).
+  SPARSE6 (a 2:4 matrix re-encoded for decode, 6 bits per 4-wide group): the pages
+  fix no sub-2-bit format, so this one is the plainest: the 54 states of a group
+  (6 kept-position pairs x 3 x 3 ternary values) numbered 9 * pair + 3 * digit(lower)
+  + digit(upper), and laid out for 16-row MFMA tiles (pack6 states the tiling).
 
 Pinned functions (tests/test_oracle_*.py) and what pins them:
   absmean_gamma      rational brute force, closed forms, permutation and 2^k
@@ -77,6 +81,10 @@ Pinned functions (tests/test_oracle_*.py) and what pins them:
   bf16_round         hand-derived ties and neighbours, exact rational nearest search,
                      torch's CPU float32 -> bfloat16 cast
   dequant_act        hand-derived values (tests/golden/bwd_tiny.txt), exact products
+  state6 / pack6     the 54 states written out by hand (tests/golden/state6.txt),
+                     bijection over every 2:4 mask and ternary pair, hand-encoded
+                     stream dwords over two panels and two step pairs
+                     (tests/golden/pack6_unit.txt), round trip through unpack6
   backward           hand-derived tiny case (tests/golden/bwd_tiny.txt), brute-force Python
                      loops, the adjoint identities <dX, X^> = <dY, Y> = <dW, W_q> against
                      the pinned forward, mask independence of dW
@@ -101,6 +109,8 @@ __all__ = [
     "WINDOW_M", "window_table", "window_table_68", "k_eff", "packed_dwords", "weight_slots",
     "pack", "unpack_slots", "slots_to_dense", "act_quant", "lift", "lift_68", "acc_dense",
     "acc_addsub", "rescale", "forward", "bf16_round", "dequant_act", "backward",
+    "LAYOUT_SPARSE6", "STATE6_PAIRS", "STATE6_COUNT", "state6", "state6_decode", "state6_dense",
+    "packed6_dwords", "pack6", "unpack6",
 ]
 
 
@@ -392,6 +402,116 @@ def slots_to_dense(vals: np.ndarray, idx, K: int, N: int, M: int, layout: int) -
     rows = np.repeat(np.arange(n)[:, None], S, axis=1)
     np.add.at(out, (rows, dense_pos), vals.astype(np.int64))
     return out.astype(np.int8)
+
+
+# ----------------------------------------------------------------------------------------------
+# 6-bit 2:4 decode encoding (layout id 2 SPARSE6).  The Bitnet.cpp abstract (aitopics "bitnet"
+# tag page) motivates ternary formats below 2 bits per weight; the pages fix no format.  A 2:4
+# group has C(4,2) = 6 kept-position pairs and 3 x 3 ternary values on them: 54 states, which
+# fit in 6 bits (0.1875 bytes per weight against the 0.25 of 2-bit codes plus 2-bit indices).
+# ----------------------------------------------------------------------------------------------
+
+LAYOUT_SPARSE6 = 2
+STATE6_PAIRS = ((0, 1), (0, 2), (0, 3), (1, 2), (1, 3), (2, 3))   # kept positions, state // 9
+STATE6_COUNT = 54
+_TERN_DIGIT = {0: 0, 1: 1, -1: 2}           # ternary value -> digit
+_DIGIT_TERN = (0, 1, -1)
+
+
+def state6(i: int, j: int, a: int, b: int) -> int:
+    """State of a 2:4 group keeping positions i < j, with ternary value a at i and b at j:
+    9 * (index of (i, j) in STATE6_PAIRS) + 3 * digit(a) + digit(b), digit(0, +1, -1) = 0, 1, 2."""
+    return 9 * STATE6_PAIRS.index((i, j)) + 3 * _TERN_DIGIT[int(a)] + _TERN_DIGIT[int(b)]
+
+
+def state6_decode(s: int) -> Tuple[int, int, int, int]:
+    """(i, j, a, b) of a state 0..53; states 54..63 are never written."""
+    if not 0 <= s < STATE6_COUNT:
+        raise ValueError(f"6-bit state {s} is not one of the 54 states")
+    p, r = divmod(s, 9)
+    i, j = STATE6_PAIRS[p]
+    return i, j, _DIGIT_TERN[r // 3], _DIGIT_TERN[r % 3]
+
+
+def state6_dense(s: int) -> Tuple[int, int, int, int]:
+    """The group's four effective ternary weights (zero where not kept)."""
+    i, j, a, b = state6_decode(s)
+    w = [0, 0, 0, 0]
+    w[i], w[j] = a, b
+    return tuple(w)
+
+
+def packed6_dwords(n: int, K: int) -> Tuple[int, int, int]:
+    """(stream dwords, n_pad, step pairs) of a SPARSE6 matrix: rows padded to 32, the K axis
+    to whole 128-column step pairs; three dwords per lane per (panel, step pair)."""
+    if K % 64 != 0:
+        raise ValueError("SPARSE6 needs K % 64 == 0 (the 2:4 packed K axis)")
+    n_pad = -(-n // PANEL) * PANEL
+    NC = -(-K // 128)
+    return (n_pad // PANEL) * NC * 64 * 3, n_pad, NC
+
+
+def _state6_matrix(vals: np.ndarray, idx: np.ndarray) -> np.ndarray:
+    """[n][S] 2:4 slot values / indices (two slots per 4-wide group) -> [n][K/4] states."""
+    n, S = vals.shape
+    st = np.zeros((n, S // 2), dtype=np.int64)
+    for r in range(n):
+        for g in range(S // 2):
+            i, j = int(idx[r, 2 * g]), int(idx[r, 2 * g + 1])
+            st[r, g] = state6(i, j, int(vals[r, 2 * g]), int(vals[r, 2 * g + 1]))
+    return st
+
+
+def pack6(vals: np.ndarray, idx: np.ndarray, n: int, K: int) -> np.ndarray:
+    """2:4 slots (weight_slots / unpack_slots of a 2:4 SPARSE matrix) -> SPARSE6 stream dwords.
+
+    Unit: one 32-row panel P and one step pair c (128 columns: 32 groups).  Lane l (0..63) holds
+    96 bits, little-endian over its three dwords, field f at bits 6f..6f+5; field
+    f = 8 * s2 + 4 * rt + g' (s2, rt in {0, 1}, g' in 0..3) is the state of row 32P + 16rt + l % 16,
+    group 32c + 16s2 + 4(l // 16) + g'.  Lane l's dwords sit at dword ((P * NC + c) * 64 + l) * 3.
+    Padded rows and groups past K hold state 0 (positions (0, 1), both values 0: zero weights).
+    """
+    nd, n_pad, NC = packed6_dwords(n, K)
+    st = np.zeros((n_pad, NC * 32), dtype=np.int64)
+    st[:n, :K // 4] = _state6_matrix(vals, idx)
+    out = np.zeros(nd, dtype=np.uint32)
+    for P in range(n_pad // PANEL):
+        for c in range(NC):
+            for l in range(64):
+                bits = 0
+                for s2 in range(2):
+                    for rt in range(2):
+                        for gq in range(4):
+                            f = 8 * s2 + 4 * rt + gq
+                            row = PANEL * P + 16 * rt + l % 16
+                            grp = 32 * c + 16 * s2 + 4 * (l // 16) + gq
+                            bits |= int(st[row, grp]) << (6 * f)
+                base = ((P * NC + c) * 64 + l) * 3
+                for d in range(3):
+                    out[base + d] = (bits >> (32 * d)) & 0xFFFFFFFF
+    return out
+
+
+def unpack6(stream: np.ndarray, n: int, K: int) -> Tuple[np.ndarray, np.ndarray]:
+    """Inverse of pack6: (effective ternary weights int8 [n][K], kept mask bool [n][K])."""
+    nd, n_pad, NC = packed6_dwords(n, K)
+    stream = np.asarray(stream).view(np.uint32).reshape(-1)
+    assert stream.size == nd
+    W = np.zeros((n_pad, NC * 128), dtype=np.int8)
+    keep = np.zeros((n_pad, NC * 128), dtype=bool)
+    for P in range(n_pad // PANEL):
+        for c in range(NC):
+            for l in range(64):
+                base = ((P * NC + c) * 64 + l) * 3
+                bits = sum(int(stream[base + d]) << (32 * d) for d in range(3))
+                for f in range(16):
+                    s2, rt, gq = f // 8, (f // 4) % 2, f % 4
+                    row = PANEL * P + 16 * rt + l % 16
+                    grp = 32 * c + 16 * s2 + 4 * (l // 16) + gq
+                    i, j, a, b = state6_decode((bits >> (6 * f)) & 63)
+                    W[row, 4 * grp + i], W[row, 4 * grp + j] = a, b
+                    keep[row, 4 * grp + i] = keep[row, 4 * grp + j] = True
+    return W[:n, :K], keep[:n, :K]
 
 
 # ----------------------------------------------------------------------------------------------

@@ -290,6 +290,91 @@ def test_pack_roundtrip(N, M, layout):
 
 
 # ------------------------------------------------------------------------------------------
+# 6-bit 2:4 decode encoding (SPARSE6)
+# ------------------------------------------------------------------------------------------
+
+def test_state6_golden_table():
+    table = read_kv("state6.txt")
+    assert sorted(int(k) for k in table) == list(range(54))
+    for k, v in table.items():
+        s = int(k)
+        i, j, *w = (int(t) for t in v)
+        assert O.state6_decode(s)[:2] == (i, j)
+        assert O.state6_dense(s) == tuple(w)
+        assert O.state6(i, j, w[i], w[j]) == s
+    for s in range(54, 64):
+        with pytest.raises(ValueError):
+            O.state6_decode(s)
+
+
+def test_state6_bijection():
+    # every 2:4 mask (a pair of kept positions) with every pair of ternary values: 54 distinct
+    # states below 54, each decoding back to its mask and values
+    seen = set()
+    for i in range(4):
+        for j in range(i + 1, 4):
+            for a in (-1, 0, 1):
+                for b in (-1, 0, 1):
+                    s = O.state6(i, j, a, b)
+                    assert 0 <= s < 54 and s not in seen
+                    seen.add(s)
+                    assert O.state6_decode(s) == (i, j, a, b)
+                    w = [0] * 4
+                    w[i], w[j] = a, b
+                    assert O.state6_dense(s) == tuple(w)
+    assert len(seen) == O.STATE6_COUNT == 54 <= 64
+
+
+def _golden_pack6():
+    kv = read_kv("pack6_unit.txt")
+    n, K = int(kv["n"][0]), int(kv["K"][0])
+    W = np.zeros((n, K), dtype=np.int8)
+    keep = np.zeros((n, K), dtype=bool)
+    keep[:, 0::4] = keep[:, 1::4] = True          # all-zero groups keep (0, 1)
+    for key, v in kv.items():
+        if key.startswith("g "):
+            r, g = (int(t) for t in key.split()[1:])
+            w0, w1, w2, w3, i, j = (int(t) for t in v)
+            W[r, 4 * g:4 * g + 4] = (w0, w1, w2, w3)
+            keep[r, 4 * g:4 * g + 4] = False
+            keep[r, 4 * g + i] = keep[r, 4 * g + j] = True
+    exp = {int(key.split()[1]): hexu32(v)[0] for key, v in kv.items() if key.startswith("d ")}
+    return n, K, W, keep, int(kv["dwords"][0]), exp
+
+
+def test_pack6_golden_unit():
+    n, K, W, keep, nd, exp = _golden_pack6()
+    assert O.packed6_dwords(n, K) == (nd, 64, 2)
+    vals, idx = O.weight_slots(W, keep, 2, 4, O.LAYOUT_SPARSE)
+    out = O.pack6(vals, idx, n, K)
+    assert out.size == nd
+    for d, v in exp.items():
+        assert int(out[d]) == v, (d, hex(int(out[d])), hex(v))
+    others = np.array([d for d in range(nd) if d not in exp])
+    assert not out[others].any()
+    Wd, kd = O.unpack6(out, n, K)
+    assert np.array_equal(Wd, W) and np.array_equal(kd, keep)
+
+
+@pytest.mark.parametrize("n,K", [(1, 64), (45, 384), (70, 320), (64, 256)])
+def test_pack6_roundtrip_from_pack(n, K):
+    # the 2:4 packed buffers of a master, through their slots, re-encode to a stream whose
+    # decoded weights and mask are the master's effective weights and mask
+    g = np.random.default_rng(n + K)
+    Wm = g.normal(0, 0.02, (n, K)).astype(np.float32)
+    Wm[:, :8] = 0.0                                # all-zero groups
+    p = O.pack(Wm, 2, 4, O.LAYOUT_SPARSE)
+    vals, idx = O.unpack_slots(p["codes"], p["meta"], n, K, 2, 4, O.LAYOUT_SPARSE)
+    s = O.pack6(vals, idx, n, K)
+    assert s.size == O.packed6_dwords(n, K)[0]
+    Wd, kd = O.unpack6(s, n, K)
+    assert np.array_equal(Wd, p["W_eff"]) and np.array_equal(kd, p["keep"])
+    # 0.1875 bytes per weight once rows and step pairs are whole
+    if n % 32 == 0 and K % 128 == 0:
+        assert s.size * 4 == n * K * 6 // 32
+
+
+# ------------------------------------------------------------------------------------------
 # activation quantization
 # ------------------------------------------------------------------------------------------
 
