@@ -412,6 +412,81 @@ def decode_dense_leg(S, torch, D, steps, warmup):
             "vs_sparse_2of4_step": round(ms / D.last_ms_per_step, 3) if D.last_ms_per_step else None}
 
 
+def decode_sparse6_leg(S, torch, D, ref, steps, warmup):
+    """The decode stream on SPARSE6 weights: the 128 packed 2:4 masters re-encoded at 6 bits per
+    4-wide group (0.1875 B per weight against 0.25), same activations and grouped launches.
+    Checked bitwise against the 2:4 step's outputs, graph-captured and timed like the main metric;
+    the group launch of each T is also timed with events beside the 2:4 group's."""
+    mats6 = [(n, K, S.transcode6(codes, meta, n, K), gamma)
+             for (n, K, codes, meta, gamma) in D.mats]
+    stream_bytes = sum(st.numel() for (_, _, st, _) in mats6)
+    groups, ys = {}, {}
+    for T in DECODE_T:
+        projs = []
+        for i, (n, K, st, gamma) in enumerate(mats6):
+            xq, sc = D.q[(T, K)]
+            j = i // 2
+            projs.append(dict(xq=xq[j * T:(j + 1) * T], scale=sc[j * T:(j + 1) * T], K=K,
+                              codes=st, meta=None, gamma=gamma, n=n,
+                              y=torch.empty((T, n), dtype=torch.float32, device="cuda")))
+        ys[T] = [p["y"] for p in projs]
+        groups[T] = S.FwdGroup(projs, 2, 4, S.BL_LAYOUT_SPARSE6)
+
+    def step(events=None):
+        for T in DECODE_T:
+            D.quantize(S, T)
+            if events is not None:
+                events[T][0].record()
+            groups[T]()
+            if events is not None:
+                events[T][1].record()
+
+    step()
+    torch.cuda.synchronize()
+    for T in DECODE_T:
+        for y, r in zip(ys[T], ref[T]):
+            if not torch.equal(y, r):
+                raise RuntimeError("SPARSE6 decode differs from the 2:4 decode")
+    ms = _graph_ms(torch, step, steps, warmup)
+    per_T = {T: [] for T in DECODE_T}
+    per_T4 = {T: [] for T in DECODE_T}
+    for _ in range(max(1, min(steps, 10))):
+        ev = {T: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for T in DECODE_T}
+        ev4 = {T: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for T in DECODE_T}
+        step(ev)
+        D.step(S, ev4)
+        torch.cuda.synchronize()
+        for T in DECODE_T:
+            per_T[T].append(ev[T][0].elapsed_time(ev[T][1]) * 1e-3)
+            per_T4[T].append(ev4[T][0].elapsed_time(ev4[T][1]) * 1e-3)
+    algo = {T: sum(st.numel() + T * K + 4 * T + 4 * T * n + 4 for (n, K, st, _) in mats6)
+            for T in DECODE_T}
+    t6 = {T: float(np.mean(per_T[T])) for T in DECODE_T}
+    t4 = {T: float(np.mean(per_T4[T])) for T in DECODE_T}
+    achieved = sum(algo.values()) / sum(t6.values()) / 1e9
+    dense_weights = sum(n * K for (n, K, _, _) in mats6)
+    return {"workload": "the decode stream (64 up/down pairs, T = 1, 4, 16) on SPARSE6 weights: the "
+                        "2:4 masters re-encoded at 6 bits per group, same activations and grouped "
+                        "launches",
+            "ms_per_step": round(ms, 4), "stream_bytes_per_pass": stream_bytes,
+            "packed_2of4_bytes_per_pass": D.packed_bytes,
+            "weight_GBps": round(stream_bytes * len(DECODE_T) / (ms * 1e-3) / 1e9, 1),
+            "dense_weights_per_s": float(f"{dense_weights * len(DECODE_T) / (ms * 1e-3):.4g}"),
+            "vs_sparse_2of4_step": round(ms / D.last_ms_per_step, 3) if D.last_ms_per_step else None,
+            "outputs_identical_to_2of4": True,
+            "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                         "kernel": "gemv6_group_kernel",
+                         "per_T": {str(T): {"launch_us": round(t6[T] * 1e6, 2),
+                                            "launch_us_2of4": round(t4[T] * 1e6, 2),
+                                            "speedup_vs_2of4": round(t4[T] / t6[T], 3),
+                                            "algorithmic_bytes": algo[T],
+                                            "GBps": round(algo[T] / t6[T] / 1e9, 1)}
+                                   for T in DECODE_T}}}
+
+
 def decode_hybrid_leg(S, torch, D, steps, warmup, dense_frac=0.25):
     """Comparator in the manner of Spense's hybrid format: each projection keeps a quarter of its
     output rows dense (4:4 dense 2-bit codes) and the rest 2:4, as two grouped launches per T (one
@@ -1094,6 +1169,10 @@ def main():
     log("fused decode leg")
     out["decode_fused"] = decode_fused_leg(S, torch, D, ref, args.steps, args.warmup)
     log(f"fused decode {out['decode_fused']['value']} GB/s")
+    log("SPARSE6 decode leg")
+    out["decode_sparse6"] = decode_sparse6_leg(S, torch, D, ref, args.steps, args.warmup)
+    log("sparse6: " + ", ".join(f"T={T} {v['launch_us']} us ({v['speedup_vs_2of4']}x 2:4)"
+                                for T, v in out["decode_sparse6"]["roofline"]["per_T"].items()))
     log("single-projection decode leg")
     out["decode_single"] = decode_single_leg(S, torch, D, args.steps, args.warmup)
     log("single: " + ", ".join(f"T={T} {v['weight_GBps']} GB/s" for T, v in out["decode_single"]["per_T"].items()))

@@ -47,9 +47,24 @@
  *           One 64-dword fragment is the A operand of one int8 sparse-MFMA 32x32x64 (SPARSE)
  *           or dense MFMA 32x32x32 (DENSE2) instruction: lane = (c%2)*32 + r%32.
  *
- * Shapes: n >= 1 (out features), K (in features): SPARSE 2:4 needs K % 64 == 0; SPARSE 6:8
- * needs K % 128 == 0; SPARSE 14:16 needs K % 256 == 0; DENSE2 needs K % 32 == 0 and K % M == 0
- * with M in {4, 8, 16}, 1 <= N <= M.
+ * SPARSE6 (BL_LAYOUT_SPARSE6, decode only): a 2:4 SPARSE matrix re-encoded at 6 bits per 4-wide
+ * group, 0.1875 bytes per weight against 0.25 (the Bitnet.cpp abstract on the aitopics "bitnet"
+ * tag page argues for ternary formats below 2 bits per weight; the pages fix no format).  A
+ * group's 54 states (kept pair (i, j) of 6, one ternary value on each) are numbered
+ * state = 9 * pair + 3 * code(lower) + code(upper), pairs in the order (0,1) (0,2) (0,3) (1,2)
+ * (1,3) (2,3), code = the 2-bit code above (0, +1, -1 -> 0, 1, 2); 54..63 are never written.
+ * Tiling for 16-row MFMA tiles: rows padded to 32, K to whole step pairs of 128 columns
+ * (NC = ceil(K/128)); lane l (0..63) of (panel P, pair c) holds 96 bits in three little-endian
+ * dwords at dword ((P*NC + c)*64 + l)*3, field f = 8*s2 + 4*rt + g (s2, rt in {0,1}, g in 0..3)
+ * at bits 6f..6f+5 = the state of row 32P + 16rt + l%16, group 32c + 16s2 + 4(l/16) + g.
+ * Padded rows and groups past K hold state 0 (zero weights).  Written by bitlinear_transcode6
+ * from the 2:4 packed buffers; read by bitlinear_fwd (T <= 32) and the decode group.
+ *
+ * Shapes: n >= 1 (out features), K (in features).  SPARSE 2:4 (and SPARSE6) needs K % 64 == 0.
+ * SPARSE (M-2):M for even M = 6..16 needs K to be a multiple of the smallest multiple k of M for
+ * which both the packed axis k(2M-4)/M is a multiple of 64 and k is a multiple of lcm(M, 8):
+ * 4:6 48, 6:8 128, 8:10 40, 10:12 192, 12:14 112, 14:16 256.  DENSE2 needs even M in 4..16,
+ * 1 <= N <= M and K % lcm(32, M) == 0.
  * n * K < 2^32.  K_eff * 127 < 2^31.  T >= 0 tokens (T == 0 enqueues nothing), T * K_eff < 2^31.
  *
  * Conventions for every call:
@@ -83,6 +98,7 @@ extern "C" {
 
 #define BL_LAYOUT_SPARSE 0
 #define BL_LAYOUT_DENSE2 1
+#define BL_LAYOUT_SPARSE6 2   /* 2:4 re-encoded at 6 bits per group; decode only (see above) */
 #define BL_LAYOUT_VERSION 2
 
 #define BL_DTYPE_F32 0
@@ -90,7 +106,8 @@ extern "C" {
 
 /* Sizes of the packed buffers of an n x K master under (N, M, layout), in bytes, the packed K
  * axis K_eff, and the workspace bytes bitlinear_pack needs.  Any output pointer may be NULL.
- * Host only; enqueues nothing. */
+ * For BL_LAYOUT_SPARSE6 (N:M 2:4 only): codes_bytes is the stream's size, meta_bytes 0, K_eff K,
+ * ws_bytes 0.  Host only; enqueues nothing. */
 int bitlinear_packed_bytes(int64_t n, int64_t K, int N, int M, int layout, size_t* codes_bytes,
                            size_t* meta_bytes, int64_t* K_eff, size_t* ws_bytes);
 
@@ -149,10 +166,22 @@ int act_quant_i8_group(const bl_quant_desc* descs, int64_t count, int x_dtype, i
  * K is the master's in-feature count; (N, M, layout) must be those the weights were packed
  * with, and xq must be on the packed K axis (lifted with lift_M = M for SPARSE 6:8 and 14:16).
  * gamma is the device scalar written by bitlinear_pack.  acc_opt, if not NULL, receives the
- * int32 accumulators [T][n] (4-byte alignment suffices for it). */
+ * int32 accumulators [T][n] (4-byte alignment suffices for it).
+ * BL_LAYOUT_SPARSE6: codes is the stream of bitlinear_transcode6, meta must be NULL, N:M 2:4,
+ * T <= 32 and K <= 16384 (BL_ENOTSUP otherwise); results equal those of the 2:4 SPARSE buffers
+ * the stream was made from, bit for bit. */
 int bitlinear_fwd(const int8_t* xq, const float* x_scale, int64_t T, int64_t K,
                   const uint8_t* codes, const uint8_t* meta, const float* gamma, int N, int M,
                   int layout, int64_t n, float* y, int32_t* acc_opt, void* stream);
+
+/* Re-encode the 2:4 SPARSE packed buffers of an n x K master (codes, meta as bitlinear_pack wrote
+ * them with N:M 2:4) into the SPARSE6 stream out[codes_bytes of bitlinear_packed_bytes(n, K, 2,
+ * 4, BL_LAYOUT_SPARSE6)].  The re-encoding is exact (a group's state is its kept pair and codes);
+ * gamma is unchanged and shared.  Buffers not written by bitlinear_pack (an index pair that is not
+ * ascending, code 11) give an unspecified stream.  out may not overlap codes or meta (BL_EINVAL).
+ * One launch, one thread per three stream dwords. */
+int bitlinear_transcode6(const uint8_t* codes, const uint8_t* meta, int64_t n, int64_t K,
+                         uint8_t* out, void* stream);
 
 /* ---------------------------------------------------------------------------------------------
  * Grouped pack: the bitlinear_pack calls of several masters (a training step re-packs every
@@ -213,6 +242,8 @@ int bitlinear_pack_group(const void* table, const bl_pack_group_plan* plan, void
  * (N, M, layout).  Per projection: 0 <= T <= 32 (T == 0 projections are skipped and may hold NULL
  * token buffers), the bitlinear_fwd shape and alignment rules, acc_opt may be NULL.
  * Projections may share xq / x_scale; their y and acc_opt buffers must not overlap.
+ * BL_LAYOUT_SPARSE6 groups (N:M 2:4, codes = bitlinear_transcode6 streams, meta NULL) run the
+ * 6-bit decode kernel, with no bound on K beyond the shape rules.
  *
  * Use: bitlinear_group_table_bytes sizes a device table, bitlinear_group_build validates every
  * descriptor on the host and writes the table (it synchronizes `stream`: build once, outside any
@@ -262,7 +293,7 @@ int bitlinear_fwd_group(const void* table, int64_t work_items, int N, int M, int
  * quantization launch per activation matrix plus the group launch.
  *
  * Layouts without activation lifting only: BL_LAYOUT_SPARSE with N:M = 2:4, or BL_LAYOUT_DENSE2
- * (BL_ENOTSUP otherwise).  Per projection: 0 <= T <= 32, T * K * 2 < 2^31, x 16-byte aligned,
+ * (BL_ENOTSUP otherwise, SPARSE6 included).  Per projection: 0 <= T <= 32, T * K * 2 < 2^31, x 16-byte aligned,
  * the other rules and the build / launch protocol as for the plain group; projections may share
  * x.  A fused table launched through bitlinear_fwd_group (or a plain one through
  * bitlinear_fwd_group_fused) writes nothing.

@@ -17,5 +17,6 @@ from .bitlinear import (  # noqa: F401
     bitlinear_group_fused_build, bitlinear_group_fused_table_bytes, bitlinear_group_table_bytes,
     bitlinear_pack, bitlinear_packed_bytes, bwd, bwd_workspace_bytes, fwd, lib, pack,
     packed_bytes, bitlinear_pack_noalloc, BlChainLayer, BlChainPlan, Chain, bitlinear_chain_plan,
-    bitlinear_chain_build, bitlinear_fwd_chain,
+    bitlinear_chain_build, bitlinear_fwd_chain, BL_LAYOUT_SPARSE6, bitlinear_transcode6,
+    transcode6,
 )

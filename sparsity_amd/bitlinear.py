@@ -6,9 +6,10 @@ Names mirror the C ABI: ``bitlinear_packed_bytes``, ``bitlinear_pack``, ``bitlin
 ``bitlinear_fwd_group``, ``bitlinear_group_fused_table_bytes``, ``bitlinear_group_fused_build``,
 ``bitlinear_fwd_group_fused``, ``bitlinear_bwd_workspace_bytes``, ``bitlinear_bwd``,
 ``bitlinear_bwd_group_plan``, ``bitlinear_bwd_group_build``, ``bitlinear_bwd_group``,
-``bitlinear_pack_group_plan``, ``bitlinear_pack_group_build``, ``bitlinear_pack_group``.
-``pack`` / ``PackGroup`` / ``act_quant`` / ``fwd`` / ``FwdGroup`` / ``FusedGroup`` / ``bwd`` /
-``BwdGroup`` are convenience
+``bitlinear_pack_group_plan``, ``bitlinear_pack_group_build``, ``bitlinear_pack_group``,
+``bitlinear_transcode6``, the chain and prefill-group calls.
+``pack`` / ``PackGroup`` / ``act_quant`` / ``fwd`` / ``transcode6`` / ``FwdGroup`` / ``FusedGroup``
+/ ``bwd`` / ``BwdGroup`` are convenience
 wrappers that allocate the output tensors with torch on the input's device and enqueue on torch's
 current stream.
 """
@@ -21,6 +22,7 @@ from typing import Optional, Tuple
 BL_OK = 0
 BL_LAYOUT_SPARSE = 0
 BL_LAYOUT_DENSE2 = 1
+BL_LAYOUT_SPARSE6 = 2
 BL_DTYPE_F32 = 0
 BL_DTYPE_BF16 = 1
 BL_BWD_ACCUM_DX = 1
@@ -128,6 +130,7 @@ def lib() -> ctypes.CDLL:
         L.act_quant_i8.argtypes = [vp, i32, i64, i64, i32, vp, vp, vp]
         L.act_quant_i8_group.argtypes = [ctypes.POINTER(BlQuantDesc), i64, i32, i32, vp]
         L.bitlinear_fwd.argtypes = [vp, vp, i64, i64, vp, vp, vp, i32, i32, i32, i64, vp, vp, vp]
+        L.bitlinear_transcode6.argtypes = [vp, vp, i64, i64, vp, vp]
         dp = ctypes.POINTER(BlFwdDesc)
         L.bitlinear_group_table_bytes.argtypes = [dp, i64, i32, i32, i32, ctypes.POINTER(sz),
                                                   ctypes.POINTER(i64)]
@@ -218,6 +221,10 @@ def act_quant_i8_group(descs, x_dtype, lift_M, stream) -> int:
 
 def bitlinear_fwd(xq, x_scale, T, K, codes, meta, gamma, N, M, layout, n, y, acc, stream) -> int:
     return lib().bitlinear_fwd(xq, x_scale, T, K, codes, meta, gamma, N, M, layout, n, y, acc, stream)
+
+
+def bitlinear_transcode6(codes, meta, n, K, out, stream) -> int:
+    return lib().bitlinear_transcode6(codes, meta, n, K, out, stream)
 
 
 def bitlinear_group_table_bytes(descs, N, M, layout):
@@ -465,7 +472,7 @@ def fwd(xq, scale, K: int, codes, meta, gamma, n: int, N: int = 2, M: int = 4,
     if mb:
         _need(meta, torch.uint8, mb, dev, "meta")
     elif meta is not None:
-        raise ValueError("meta: must be None for the dense 2-bit layout")
+        raise ValueError("meta: must be None for a layout without index dwords")
     _need(gamma, torch.float32, 1, dev, "gamma")
     if out is None:
         y = torch.empty((T, n), dtype=torch.float32, device=dev)
@@ -479,6 +486,23 @@ def fwd(xq, scale, K: int, codes, meta, gamma, n: int, N: int = 2, M: int = 4,
                          gamma.data_ptr(), N, M, layout, n, y.data_ptr(), _ptr(acc), _stream()),
            "bitlinear_fwd")
     return (y, acc) if want_acc else y
+
+
+def transcode6(codes, meta, n: int, K: int, out=None):
+    """Re-encode the 2:4 SPARSE packed buffers (codes, meta) of an n x K master into the SPARSE6
+    stream (uint8); the master's gamma is unchanged.  ``out`` may supply the stream buffer."""
+    import torch
+    cb, mb, _, _ = packed_bytes(n, K, 2, 4, BL_LAYOUT_SPARSE)
+    sb, _, _, _ = packed_bytes(n, K, 2, 4, BL_LAYOUT_SPARSE6)
+    dev = codes.device
+    _need(codes, torch.uint8, cb, dev, "codes")
+    _need(meta, torch.uint8, mb, dev, "meta")
+    if out is None:
+        out = torch.empty(sb, dtype=torch.uint8, device=dev)
+    _need(out, torch.uint8, sb, dev, "out")
+    _check(bitlinear_transcode6(codes.data_ptr(), meta.data_ptr(), n, K, out.data_ptr(), _stream()),
+           "bitlinear_transcode6")
+    return out
 
 
 class PackGroup:

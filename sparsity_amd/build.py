@@ -10,7 +10,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libbitlinear.so")
 SOURCES = ["bitlinear_api.hip", "pack.hip", "act_quant.hip", "fwd.hip", "gemv_group.hip", "bwd.hip",
-           "chain.hip"]
+           "chain.hip", "gemv6.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

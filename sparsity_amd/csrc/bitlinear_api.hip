@@ -70,6 +70,18 @@ int check_shape(int64_t n, int64_t K, int N, int M, int layout, int64_t* keff) {
   return BL_OK;
 }
 
+// Shape rules of SPARSE6 (a 2:4 matrix re-encoded for decode): those of 2:4 SPARSE.
+int check_shape6(int64_t n, int64_t K, int N, int M, int64_t* keff) {
+  if (N != 2 || M != 4) return BL_ENOTSUP;
+  return check_shape(n, K, 2, 4, BL_LAYOUT_SPARSE, keff);
+}
+
+// check_shape for every layout bitlinear_fwd and the decode group accept.
+int check_shape_fwd(int64_t n, int64_t K, int N, int M, int layout, int64_t* keff) {
+  return layout == BL_LAYOUT_SPARSE6 ? check_shape6(n, K, N, M, keff)
+                                     : check_shape(n, K, N, M, layout, keff);
+}
+
 int status_of(hipError_t e) { return e == hipSuccess ? BL_OK : BL_EIO; }
 
 // Checks of one act_quant_i8 call (pointers are not looked at when T == 0).
@@ -88,9 +100,10 @@ int check_quant(const void* x, int x_dtype, int64_t T, int64_t K, int lift_M, co
 int check_fwd(const int8_t* xq, const float* x_scale, int64_t T, int64_t K, const uint8_t* codes,
               const uint8_t* meta, const float* gamma, int N, int M, int layout, int64_t n,
               const float* y, const int32_t* acc_opt, int64_t* keff) {
-  const int st = check_shape(n, K, N, M, layout, keff);
+  const int st = check_shape_fwd(n, K, N, M, layout, keff);
   if (st != BL_OK) return st;
   if (T < 0 || T > INT32_MAX || (uint64_t)T * (uint64_t)n >= (1ull << 40)) return BL_EINVAL;
+  if (layout == BL_LAYOUT_SPARSE6 && T > 32) return BL_ENOTSUP;   // a decode format
   if ((uint64_t)T * (uint64_t)*keff >= (1ull << 31)) return BL_EINVAL;  // 32-bit activation offsets
   if (T == 0) return BL_OK;  // nothing is read or written; pointers may be NULL
   if (!aligned16(xq) || !aligned4(x_scale) || !aligned16(codes) || !aligned16(gamma) ||
@@ -668,6 +681,7 @@ int fused_as_plain(const bl_fwd_x_desc* d, int64_t count, int M, int layout,
                    std::vector<bl_fwd_desc>* out) {
   if (!d || count < 1 || count > (1 << 24)) return BL_EINVAL;
   if (layout == BL_LAYOUT_SPARSE && M != 4) return BL_ENOTSUP;
+  if (layout == BL_LAYOUT_SPARSE6) return BL_ENOTSUP;
   out->resize((size_t)count);
   for (int64_t i = 0; i < count; ++i) {
     if (d[i].T < 0 || d[i].K < 1) return BL_EINVAL;
@@ -755,9 +769,17 @@ const char* bitlinear_strerror(int status) {
 int bitlinear_packed_bytes(int64_t n, int64_t K, int N, int M, int layout, size_t* codes_bytes,
                            size_t* meta_bytes, int64_t* K_eff, size_t* ws_bytes) {
   int64_t ke = 0;
-  const int st = check_shape(n, K, N, M, layout, &ke);
+  const int st = check_shape_fwd(n, K, N, M, layout, &ke);
   if (st != BL_OK) return st;
   const uint64_t n_pad = (uint64_t)((n + 31) / 32) * 32;
+  if (layout == BL_LAYOUT_SPARSE6) {
+    // three dwords per lane per (32-row panel, 128-column step pair)
+    if (codes_bytes) *codes_bytes = (size_t)(n_pad / 32 * (uint64_t)((K + 127) / 128) * 64 * 12);
+    if (meta_bytes) *meta_bytes = 0;
+    if (K_eff) *K_eff = ke;
+    if (ws_bytes) *ws_bytes = 0;
+    return BL_OK;
+  }
   const uint64_t slots = layout == BL_LAYOUT_SPARSE ? (uint64_t)ke / 2 : (uint64_t)ke;
   if (codes_bytes) *codes_bytes = (size_t)(n_pad * slots / 4);
   if (meta_bytes) *meta_bytes = layout == BL_LAYOUT_SPARSE ? (size_t)(n_pad * slots / 4) : 0;
@@ -957,8 +979,28 @@ int bitlinear_fwd(const int8_t* xq, const float* x_scale, int64_t T, int64_t K,
   int64_t ke = 0;
   const int st = check_fwd(xq, x_scale, T, K, codes, meta, gamma, N, M, layout, n, y, acc_opt, &ke);
   if (st != BL_OK || T == 0) return st;
+  if (layout == BL_LAYOUT_SPARSE6) {
+    if (K > 128 * 128) return BL_ENOTSUP;   // one projection: at most 16 step pairs per wave
+    return status_of(bl::launch_fwd6(xq, x_scale, T, K, (const uint32_t*)codes, gamma, n, y,
+                                     acc_opt, (hipStream_t)stream));
+  }
   return status_of(bl::launch_fwd(xq, x_scale, T, ke, (const uint32_t*)codes, (const uint32_t*)meta,
                                   gamma, layout, n, y, acc_opt, (hipStream_t)stream));
+}
+
+int bitlinear_transcode6(const uint8_t* codes, const uint8_t* meta, int64_t n, int64_t K,
+                         uint8_t* out, void* stream) {
+  int64_t ke = 0;
+  const int st = check_shape(n, K, 2, 4, BL_LAYOUT_SPARSE, &ke);
+  if (st != BL_OK) return st;
+  if (!aligned16(codes) || !aligned16(meta) || !aligned16(out)) return BL_EINVAL;
+  size_t cb = 0, mb = 0, ob = 0;
+  bitlinear_packed_bytes(n, K, 2, 4, BL_LAYOUT_SPARSE, &cb, &mb, nullptr, nullptr);
+  bitlinear_packed_bytes(n, K, 2, 4, BL_LAYOUT_SPARSE6, &ob, nullptr, nullptr, nullptr);
+  const uintptr_t o = (uintptr_t)out, c = (uintptr_t)codes, m = (uintptr_t)meta;
+  if ((o < c + cb && c < o + ob) || (o < m + mb && m < o + ob)) return BL_EINVAL;
+  return status_of(bl::launch_transcode6((const uint32_t*)codes, (const uint32_t*)meta, n, K,
+                                         (uint32_t*)out, (hipStream_t)stream));
 }
 
 int bitlinear_group_table_bytes(const bl_fwd_desc* descs, int64_t count, int N, int M, int layout,
@@ -973,11 +1015,14 @@ int bitlinear_group_build(const bl_fwd_desc* descs, int64_t count, int N, int M,
 
 int bitlinear_fwd_group(const void* table, int64_t work_items, int N, int M, int layout,
                         void* stream) {
-  const int st = check_nm(N, M, layout);
+  const int st = layout == BL_LAYOUT_SPARSE6 ? (N == 2 && M == 4 ? BL_OK : BL_ENOTSUP)
+                                             : check_nm(N, M, layout);
   if (st != BL_OK) return st;
   if (work_items < 0 || work_items > INT32_MAX) return BL_EINVAL;
   if (work_items == 0) return BL_OK;
   if (!aligned16(table)) return BL_EINVAL;
+  if (layout == BL_LAYOUT_SPARSE6)
+    return status_of(bl::launch_fwd6_group(table, work_items, (hipStream_t)stream));
   return status_of(bl::launch_fwd_group(table, work_items, layout, 0, (hipStream_t)stream));
 }
 

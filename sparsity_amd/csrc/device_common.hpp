@@ -45,6 +45,7 @@ constexpr int pack_cols(int layout, int M) {
 
 constexpr int kLayoutSparse = 0;
 constexpr int kLayoutDense2 = 1;
+constexpr int kLayoutSparse6 = 2;   // 2:4 re-encoded at 6 bits per group (decode only)
 constexpr int kPanel = 32;       // rows per packed panel (the M side of a 32x32 MFMA tile)
 constexpr uint32_t kPadMeta = 0x44444444u;
 

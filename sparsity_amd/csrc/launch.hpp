@@ -74,6 +74,15 @@ struct GroupItem {
 hipError_t launch_fwd_group(const void* table, int64_t items, int layout, int fused,
                             hipStream_t s);
 
+// SPARSE6: re-encoding of 2:4 packed buffers, the single-projection decode (T <= 32, K <= 16384)
+// and the grouped decode over a table built for layout SPARSE6.
+hipError_t launch_transcode6(const uint32_t* codes, const uint32_t* meta, int64_t n, int64_t K,
+                             uint32_t* out, hipStream_t s);
+hipError_t launch_fwd6(const int8_t* xq, const float* xs, int64_t T, int64_t K,
+                       const uint32_t* stream, const float* gamma, int64_t n, float* y,
+                       int32_t* acc, hipStream_t s);
+hipError_t launch_fwd6_group(const void* table, int64_t items, hipStream_t s);
+
 }  // namespace bl
 
 namespace bl {

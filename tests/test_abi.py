@@ -147,6 +147,58 @@ def test_fwd_rejects_before_launch(L):
     assert call(T=0, xq=None, xs=None, y=None) == 0
 
 
+@pytest.mark.parametrize("n,K", [(1, 64), (33, 192), (6912, 2560), (2560, 6912), (45, 384)])
+def test_sparse6_packed_bytes(L, n, K):
+    st, cb, mb, ke, ws = L.bitlinear_packed_bytes(n, K, 2, 4, L.BL_LAYOUT_SPARSE6)
+    assert st == 0 and mb == 0 and ke == K and ws == 0
+    assert cb == 4 * O.packed6_dwords(n, K)[0]
+    # 0.75 of the 2:4 codes + meta once the K axis is whole step pairs
+    _, cb2, mb2, _, _ = L.bitlinear_packed_bytes(n, K, 2, 4, 0)
+    if K % 128 == 0:
+        assert 4 * cb == 3 * (cb2 + mb2)
+    assert L.bitlinear_packed_bytes(n, K, 6, 8, L.BL_LAYOUT_SPARSE6)[0] == -95
+    assert L.bitlinear_packed_bytes(n, K + 32, 2, 4, L.BL_LAYOUT_SPARSE6)[0] == -22
+
+
+def test_sparse6_rejects_before_launch(L):
+    P, S6 = FAKE, L.BL_LAYOUT_SPARSE6
+    ok = dict(xq=P, xs=P, T=4, K=256, codes=P, meta=None, gamma=P, N=2, M=4, layout=S6, n=64, y=P,
+              acc=None)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return L.bitlinear_fwd(a["xq"], a["xs"], a["T"], a["K"], a["codes"], a["meta"], a["gamma"],
+                               a["N"], a["M"], a["layout"], a["n"], a["y"], a["acc"], None)
+    assert call(meta=P) == -22                     # no index dwords
+    assert call(T=33) == -95                       # a decode format
+    assert call(N=6, M=8, K=256) == -95
+    assert call(K=100) == -22
+    assert call(K=16384 + 64) == -95               # one projection: K <= 16384
+    assert call(codes=P + 4) == -22
+    assert call(T=0) == 0
+    # re-encoding: the input follows the 2:4 rules, out may not overlap the inputs
+    tc = L.bitlinear_transcode6
+    assert tc(P, P + (1 << 30), 64, 100, P + (2 << 30), None) == -22
+    assert tc(P, P + (1 << 30), 0, 256, P + (2 << 30), None) == -22
+    assert tc(P + 8, P + (1 << 30), 64, 256, P + (2 << 30), None) == -22
+    assert tc(P, P + (1 << 30), 64, 256, P + 1024, None) == -22     # overlaps codes
+    assert tc(P, P + (1 << 30), 64, 256, P + (1 << 30) - 16, None) == -22   # overlaps meta
+    # decode group: plain tables only
+    arr = (L.BlFwdDesc * 1)(_desc(L, meta=None))
+    st, tb, wi = L.bitlinear_group_table_bytes(arr, 2, 4, S6)
+    assert st == 0 and wi >= 1
+    assert L.bitlinear_group_table_bytes((L.BlFwdDesc * 1)(_desc(L)), 2, 4, S6)[0] == -22
+    assert L.bitlinear_group_table_bytes((L.BlFwdDesc * 1)(_desc(L, meta=None, T=33)), 2, 4,
+                                         S6)[0] == -95
+    assert L.bitlinear_group_table_bytes(arr, 6, 8, S6)[0] == -95
+    assert L.bitlinear_fwd_group(FAKE, 3, 6, 8, S6, None) == -95
+    xarr = (L.BlFwdXDesc * 1)(L.BlFwdXDesc(x=P, T=4, K=256, codes=P, meta=None, gamma=P, n=64,
+                                           y=P + (1 << 34), acc_opt=None))
+    assert L.bitlinear_group_fused_table_bytes(xarr, 2, 4, S6)[0] == -95
+    # the training-side calls do not take the decode format
+    assert L.bitlinear_pack(P, 64, 256, 2, 4, S6, P, None, P, P, 1 << 20, None) == -95
+
+
 def test_product_path_never_imports_oracle():
     pkg = os.path.join(ROOT, "sparsity_amd")
     for dirpath, _, files in os.walk(pkg):
