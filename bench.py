@@ -69,7 +69,8 @@ def parse():
     ap.add_argument("--cpu-baseline-only", action="store_true",
                     help="(internal) print the CPU oracle baseline as JSON and exit; no GPU use")
     ap.add_argument("--profile-pass",
-                    choices=("decode", "prefill", "train", "bwd", "bwdgroup", "fwdgroup"),
+                    choices=("decode", "prefill", "train", "bwd", "bwdgroup", "fwdgroup",
+                             "sparse6"),
                     default=None,
                     help="for hardware-counter runs, no graph and no JSON line.  decode: two eager "
                          "decode steps, then a plain copy of COPY_BYTES (the counters' scale "
@@ -78,7 +79,8 @@ def parse():
                          "backward three times; bwdgroup: the layer set's grouped backward three "
                          "times, then the plain copies; fwdgroup: the layer set's grouped forward "
                          "three times, its seven separate forwards three times, then the plain "
-                         "copies")
+                         "copies; sparse6: the decode workload's SPARSE6 and 2:4 groups twice "
+                         "at every T, then the plain copies")
     return ap.parse_args()
 
 
@@ -412,14 +414,11 @@ def decode_dense_leg(S, torch, D, steps, warmup):
             "vs_sparse_2of4_step": round(ms / D.last_ms_per_step, 3) if D.last_ms_per_step else None}
 
 
-def decode_sparse6_leg(S, torch, D, ref, steps, warmup):
-    """The decode stream on SPARSE6 weights: the 128 packed 2:4 masters re-encoded at 6 bits per
-    4-wide group (0.1875 B per weight against 0.25), same activations and grouped launches.
-    Checked bitwise against the 2:4 step's outputs, graph-captured and timed like the main metric;
-    the group launch of each T is also timed with events beside the 2:4 group's."""
+def _sparse6_groups(S, torch, D):
+    """The decode masters re-encoded as SPARSE6 streams and one SPARSE6 group per T over the
+    decode workload's quantized activations."""
     mats6 = [(n, K, S.transcode6(codes, meta, n, K), gamma)
              for (n, K, codes, meta, gamma) in D.mats]
-    stream_bytes = sum(st.numel() for (_, _, st, _) in mats6)
     groups, ys = {}, {}
     for T in DECODE_T:
         projs = []
@@ -431,6 +430,16 @@ def decode_sparse6_leg(S, torch, D, ref, steps, warmup):
                               y=torch.empty((T, n), dtype=torch.float32, device="cuda")))
         ys[T] = [p["y"] for p in projs]
         groups[T] = S.FwdGroup(projs, 2, 4, S.BL_LAYOUT_SPARSE6)
+    return mats6, groups, ys
+
+
+def decode_sparse6_leg(S, torch, D, ref, steps, warmup):
+    """The decode stream on SPARSE6 weights: the 128 packed 2:4 masters re-encoded at 6 bits per
+    4-wide group (0.1875 B per weight against 0.25), same activations and grouped launches.
+    Checked bitwise against the 2:4 step's outputs, graph-captured and timed like the main metric;
+    the group launch of each T is also timed with events beside the 2:4 group's."""
+    mats6, groups, ys = _sparse6_groups(S, torch, D)
+    stream_bytes = sum(st.numel() for (_, _, st, _) in mats6)
 
     def step(events=None):
         for T in DECODE_T:
@@ -1069,6 +1078,21 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         log(f"profile pass done: 2 decode steps, 2 copies of {COPY_BYTES} bytes")
+        return
+    if args.profile_pass == "sparse6":
+        _, groups6, _ = _sparse6_groups(S, torch, D)
+        for _ in range(2):
+            for T in DECODE_T:
+                D.quantize(S, T)
+                groups6[T]()
+                D.groups[T]()
+        torch.cuda.synchronize()
+        src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(2):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"profile pass done: 2 x (SPARSE6 and 2:4 groups at T = 1, 4, 16), 2 copies")
         return
 
     # eager reference output of one step, then graph capture of the same step

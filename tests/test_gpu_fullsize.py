@@ -240,3 +240,43 @@ def test_train_step_backward_full_size_grouped():
         r, b = sums[K]
         _within(host(dX[K])[toks], r, b, f"dX:{K} sampled tokens")
         print(f"dX:{K}: sampled tokens ok", flush=True)
+
+
+def test_backward_full_size_exact_dw():
+    """dW at the gate projection's full size (8192 tokens, 8640 x 3200) on inputs for which every
+    partial sum is exact in fp32, so dW must equal the oracle bit for bit whatever the summation
+    order: |x| in [0.5, 1] with absmax 1 per token gives q in [64, 127] and X^ = bf16(q / 127)
+    multiples of 2^-8 in [0.5, 1]; dY in {-1, 0, +1}; |dW| * 2^8 <= 8192 * 256 < 2^24.  X^
+    without its bf16 rounding (or rounded otherwise) has 24-bit mantissas and moves the sums off
+    the 2^-8 grid, which the bit-exact comparison catches (checked below on the oracle itself)."""
+    import torch
+    T, n, K = 8192, 8640, 3200
+    g = np.random.default_rng(8192)
+    x = (g.uniform(0.5, 1.0, (T, K)) * g.choice([-1.0, 1.0], (T, K))).astype(np.float32)
+    x[np.arange(T), g.integers(0, K, T)] = 1.0                 # absmax 1 in every token
+    dy_bits = g.choice(np.array([0x3F80, 0xBF80, 0x0000], np.uint16), (T, n), p=[0.3, 0.3, 0.4])
+    dy = np.where(dy_bits == 0x3F80, 1.0, np.where(dy_bits == 0xBF80, -1.0, 0.0))
+    q, sc = O.act_quant(x, 0)
+    assert np.abs(q).min() >= 64
+    xq, s = S.act_quant(dev(x))
+    assert np.array_equal(host(xq), q) and np.array_equal(f32_bits(host(s)), f32_bits(sc))
+    W = (torch.randn((n, K), generator=torch.Generator(device="cuda").manual_seed(5),
+                     device="cuda") * 0.02).contiguous()
+    codes, meta, gamma = S.pack(W, 2, 4)
+    _, dw = S.bwd(_bf16_dev(dy_bits), xq, s, K, codes, meta, gamma, n, want_dx=False)
+    dw = host(dw)
+    xh = O.dequant_act(q, sc).astype(np.float64)
+    rows = np.unique(np.concatenate([[0, n - 1], g.choice(n, 62, replace=False)]))
+    cols = np.unique(np.concatenate([[0, K - 1], g.choice(K, 62, replace=False)]))
+    ref_r = dy[:, rows].T @ xh                                 # exact: integers / 256 below 2^24
+    ref_c = dy.T @ xh[:, cols]
+    assert np.array_equal(ref_r * 256, np.round(ref_r * 256))
+    nbad = int((dw[rows].astype(np.float64) != ref_r).sum())
+    assert nbad == 0, f"{nbad} of the sampled dW rows' entries differ"
+    nbad = int((dw[:, cols].astype(np.float64) != ref_c).sum())
+    assert nbad == 0, f"{nbad} of the sampled dW columns' entries differ"
+    # sensitivity: the same sums over X^ without its bf16 rounding leave the 2^-8 grid
+    x_unrounded = (np.asarray(q, np.float32) * sc[:, None]).astype(np.float64)
+    slip = dy[:, rows[:4]].T @ x_unrounded
+    assert (slip != ref_r[:4]).mean() > 0.99
+    print("full-size dW: sampled rows and columns bit-exact", flush=True)

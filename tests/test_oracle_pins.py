@@ -272,6 +272,35 @@ def test_pack_golden_unit():
     assert np.all(meta[others] == pad)
 
 
+def test_pack_golden_tiling():
+    # two panels, several fragments, SPARSE and DENSE2 (tests/golden/pack_tiling.txt)
+    kv = read_kv("pack_tiling.txt")
+    W = np.zeros((33, 128), dtype=np.float32)
+    for key, v in kv.items():
+        if key.startswith("w "):
+            r, k0 = (int(t) for t in key.split()[1:])
+            W[r, k0:k0 + 4] = [float(t) for t in v]
+    for layout, pre in ((O.LAYOUT_SPARSE, "sparse"), (O.LAYOUT_DENSE2, "dense")):
+        p = O.pack(W, 2, 4, layout)
+        assert float(p["gamma"]) == float(np.float32(9 / (33 * 128)))
+        codes = p["codes"]
+        assert codes.size == int(kv[f"{pre}_dwords"][0])
+        exp_c = {int(k.split()[1]): hexu32(v)[0] for k, v in kv.items()
+                 if k.startswith(f"{pre}_code ")}
+        for d, v in exp_c.items():
+            assert int(codes[d]) == v, (pre, d, hex(int(codes[d])), hex(v))
+        others = np.array([d for d in range(codes.size) if d not in exp_c])
+        assert not codes[others].any()
+        if layout == O.LAYOUT_SPARSE:
+            meta = p["meta"]
+            exp_m = {int(k.split()[1]): hexu32(v)[0] for k, v in kv.items()
+                     if k.startswith("sparse_meta ")}
+            for d, v in exp_m.items():
+                assert int(meta[d]) == v, (d, hex(int(meta[d])), hex(v))
+            others = np.array([d for d in range(meta.size) if d not in exp_m])
+            assert np.all(meta[others] == O.PAD_META)
+
+
 @pytest.mark.parametrize("N,M,layout", [(2, 4, O.LAYOUT_SPARSE), (6, 8, O.LAYOUT_SPARSE),
                                         (14, 16, O.LAYOUT_SPARSE), (2, 4, O.LAYOUT_DENSE2),
                                         (6, 8, O.LAYOUT_DENSE2), (14, 16, O.LAYOUT_DENSE2),
