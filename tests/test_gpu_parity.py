@@ -217,6 +217,15 @@ def test_fwd_gemm_partial_stage(N, M, layout, K):
     _fwd_case(520, K, 300, N, M, layout, seed=K)
 
 
+@pytest.mark.parametrize("N,M,layout,K", [(2, 4, O.LAYOUT_SPARSE, 1600), (2, 4, O.LAYOUT_SPARSE, 1536),
+                                          (2, 4, O.LAYOUT_SPARSE, 832), (6, 8, O.LAYOUT_SPARSE, 1024),
+                                          (2, 4, O.LAYOUT_DENSE2, 800), (14, 16, O.LAYOUT_SPARSE, 768)])
+def test_fwd_gemm_stage_counts(N, M, layout, K):
+    # the large-tile GEMM over odd and even counts of 128-byte K stages, with and without a
+    # partial last stage, ragged rows and tokens
+    _fwd_case(300, K, 257, N, M, layout, seed=K + M)
+
+
 def test_fwd_edge_tokens():
     g = rng(9)
     T, K = 70, 256
