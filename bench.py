@@ -70,7 +70,7 @@ def parse():
                     help="(internal) print the CPU oracle baseline as JSON and exit; no GPU use")
     ap.add_argument("--profile-pass",
                     choices=("decode", "prefill", "train", "bwd", "bwdgroup", "fwdgroup",
-                             "sparse6"),
+                             "sparse6", "windows"),
                     default=None,
                     help="for hardware-counter runs, no graph and no JSON line.  decode: two eager "
                          "decode steps, then a plain copy of COPY_BYTES (the counters' scale "
@@ -80,7 +80,9 @@ def parse():
                          "times, then the plain copies; fwdgroup: the layer set's grouped forward "
                          "three times, its seven separate forwards three times, then the plain "
                          "copies; sparse6: the decode workload's SPARSE6 and 2:4 groups twice "
-                         "at every T, then the plain copies")
+                         "at every T, then the plain copies; windows: the 6:8 leg (window and "
+                         "dense GEMMs, 2048 x 4096 -> 4096) with two timed launches each, then "
+                         "the plain copies")
     return ap.parse_args()
 
 
@@ -1060,6 +1062,16 @@ def main():
         train_step_leg(S, torch, iters=2)
         torch.cuda.synchronize()
         log("profile pass done: training-step layer set")
+        return
+    if args.profile_pass == "windows":
+        windows_leg(S, torch, 6, 8, iters=2)
+        torch.cuda.synchronize()
+        src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(2):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("profile pass done: 6:8 window and dense GEMMs, 2 copies")
         return
     if args.profile_pass == "prefill":
         prefill_leg(S, torch, iters=2)

@@ -130,7 +130,7 @@ int bitlinear_pack(const float* W, int64_t n, int64_t K, int N, int M, int layou
  * library runs on holds its own copy from the first call there until the process ends; the call
  * allocates nothing.  Every call on one GPU shares that copy: calls that may overlap on one GPU
  * (different streams, or different host threads) race and must be serialized by the caller. */
-#define BL_PACK_NOALLOC_WS_BYTES 9472
+#define BL_PACK_NOALLOC_WS_BYTES 42240
 int bitlinear_pack_noalloc(const float* W, int64_t n, int64_t K, int N, int M, int layout,
                            uint8_t* codes, uint8_t* meta, float* gamma, void* stream);
 

@@ -6,13 +6,16 @@
 
 namespace bl {
 
-// Workspace of bitlinear_pack: per-block fp64 partial sums of |W|, the exact fallback's nine
-// accumulator words (one 128-byte line each), then gamma, the ternary threshold, a flag and a
-// counter (256-byte multiple).
+// Workspace of bitlinear_pack: per-block fp64 partial sums of |W|; for the exact fallback, one
+// 128-byte line of word sums per exact-pass block, 8 group arrival counters and one overall
+// counter (a line each); then gamma, the ternary threshold and a flag (256-byte multiple).
 constexpr int kGammaBlocks = 1024;
 constexpr int kGammaThreads = 256;
 constexpr int kExactWords = 9;
-constexpr size_t kPackWsBytes = (kGammaBlocks * sizeof(double) + kExactWords * 128 + 16 + 255) / 256 * 256;
+constexpr int kExactBlocks = 256;     // exact-pass blocks per master (one per CU)
+constexpr int kExactGroups = 8;       // arrival counter groups (block b counts in group b % 8)
+constexpr size_t kPackWsBytes = (kGammaBlocks * sizeof(double) + (size_t)kExactBlocks * 128 +
+                                 (kExactGroups + 1) * 128 + 16 + 255) / 256 * 256;
 
 hipError_t launch_pack(const float* W, int64_t n, int64_t K, int N, int M, int layout,
                        uint32_t* codes, uint32_t* meta, float* gamma, void* ws, hipStream_t s);

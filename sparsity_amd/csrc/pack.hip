@@ -8,14 +8,15 @@
 //
 // Three launches, all on the caller's stream:
 //   1. gamma_partial_kernel   fp64 partial sums of |w| (HBM-bound read of W); it also clears the
-//                             exact accumulator and the block counter of launch 2
+//                             arrival counters of launch 2
 //   2. gamma_exact_kernel     every block sums the partials in one fixed order (all get the same
 //                             bits) and certifies the fp32 rounding of the exact mean with a
 //                             rigorous error bound.  Certified (the common case): block 0 stores
 //                             gamma and the ternary threshold tau, and every block exits.
 //                             Otherwise the blocks sum |W| exactly as integers (24-bit
 //                             significands shifted to a 2^-149 fixed point, kept as carry-free
-//                             32-bit words in 64-bit accumulators) and the last block to finish
+//                             32-bit words in 64-bit accumulators), each block stores its word
+//                             sums in a line of its own, and the last block to arrive sums them,
 //                             rounds the exact mean to fp32 and stores gamma and tau: one extra
 //                             pass over W, once per master
 //   3. pack_kernel            reads tau; mask, codes by |w| >= tau, slots assembled in LDS,
@@ -34,12 +35,16 @@ namespace bl {
 // highest a piece reaches.
 struct PackWs {
   double partial[kGammaBlocks];      // fp64 partial sums of |w|, one per partial-sum block
-  // exact fallback: sum_i words[i][0] * 2^(32 i) units of 2^-149; one 128-byte line per word, so
-  // the blocks' atomics on different words do not queue on one cache line
-  unsigned long long words[kExactWords][16];
+  // exact fallback: block b's word sums (sum_i slot[b][i] * 2^(32 i) units of 2^-149), one
+  // 128-byte line per block, written with plain stores: no two blocks touch one line
+  unsigned long long slot[kExactBlocks][16];
+  // arrival counters, one line each: block b counts in group b % kExactGroups; the last block of
+  // a group counts in done_all (at most kExactBlocks / kExactGroups atomics queue on one line)
+  uint32_t done_grp[kExactGroups][32];
+  uint32_t done_all, pad[31];
   float gamma, tau;                  // gamma and the ternary threshold, read by every pack block
   uint32_t exact_used;               // 1 when the exact fallback decided gamma (diagnostic)
-  uint32_t done;                     // exact fallback: blocks that have added their words
+  uint32_t pad2;
 };
 static_assert(sizeof(PackWs) <= kPackWsBytes, "pack workspace");
 
@@ -74,11 +79,12 @@ __device__ __forceinline__ void gamma_partial_block(const float4* __restrict__ W
   }
 }
 
-// Block 0 also clears the exact accumulator and the block counter: the exact launch may add to
-// them, and this launch has completed before it starts.
+// Block 0 also clears the exact pass's arrival counters: the exact launch counts in them, and
+// this launch has completed before it starts.  (The per-block word slots are overwritten, not
+// added to.)
 __device__ __forceinline__ void clear_exact_state(PackWs* __restrict__ ws, int blk) {
-  if (blk == 0 && threadIdx.x < kExactWords) ws->words[threadIdx.x][0] = 0ull;
-  if (blk == 0 && threadIdx.x == kExactWords) ws->done = 0u;
+  if (blk == 0 && threadIdx.x < kExactGroups) ws->done_grp[threadIdx.x][0] = 0u;
+  if (blk == 0 && threadIdx.x == kExactGroups) ws->done_all = 0u;
 }
 
 __global__ __launch_bounds__(kGammaThreads) void gamma_partial_kernel(const float4* __restrict__ W4,
@@ -114,16 +120,30 @@ __device__ float exact_mean_from_words(const unsigned long long* words, uint64_t
   for (int i = L - 1; i >= 0; --i)
     if (q[i]) { len = 32 * i + (32 - __clz(q[i])); break; }
   const int shift = len > 24 ? len - 24 : 0;
-  auto bit = [&](int pos) -> uint32_t { return (q[pos >> 5] >> (pos & 31)) & 1u; };
-  uint32_t sig = 0;
-  for (int k = 23; k >= 0; --k) sig = (sig << 1) | (shift + k < 32 * L ? bit(shift + k) : 0u);
+  // word w of the quotient (0 past the top), as a select chain over the unrolled digits
+  auto word = [&](int w) -> uint32_t {
+    uint32_t r = 0;
+#pragma unroll
+    for (int i = 0; i < L; ++i) r = i == w ? q[i] : r;
+    return r;
+  };
+  // the 24 significant bits: quotient bits shift .. shift + 23
+  const uint64_t two = (uint64_t)word(shift >> 5) | ((uint64_t)word((shift >> 5) + 1) << 32);
+  const uint32_t sig0 = (uint32_t)(two >> (shift & 31)) & 0xFFFFFFu;
+  uint32_t sig = sig0;
   bool up;
   if (shift == 0) {
     up = (2 * rem > count) || (2 * rem == count && (sig & 1));
   } else {
-    const uint32_t half = bit(shift - 1);
-    bool lower = rem != 0;
-    for (int pos = 0; pos < shift - 1 && !lower; ++pos) lower = bit(pos) != 0;
+    const int hb = shift - 1;                                   // the first bit below sig
+    const uint32_t half = (word(hb >> 5) >> (hb & 31)) & 1u;
+    bool lower = rem != 0;                                      // anything below the half bit
+#pragma unroll
+    for (int i = 0; i < L; ++i) {
+      const int below = hb - 32 * i;                            // bits of word i under hb
+      const uint32_t mask = below >= 32 ? 0xFFFFFFFFu : (below > 0 ? (1u << below) - 1u : 0u);
+      lower = lower || (q[i] & mask) != 0u;
+    }
     up = half && (lower || (sig & 1));
   }
   int sh = shift;
@@ -149,9 +169,7 @@ __device__ float ternary_threshold(float gamma) {
 }
 
 constexpr int kExactThreads = 1024;  // 16 waves: four per SIMD for the rare exact pass
-constexpr int kExactBlocks = 256;    // gamma_exact_kernel: blocks per master (one per CU; each
-                                     // adds its word sums with one atomic per word)
-constexpr int kExactLoads = 2;       // float4 loads in flight per thread in the exact pass
+constexpr int kExactLoads = 2;       // float4 loads per thread per iteration of the exact pass
 
 // Certified fp32 rounding of mean |W| from the fp64 partial sums, computed by a whole block in one
 // fixed order (every block gets the same bits).  Returns 1 and *g when the rigorous error bound of
@@ -218,36 +236,43 @@ __device__ __forceinline__ void gamma_exact_block(const float* __restrict__ W, i
   g_v4f* W4 = (g_v4f*)W;
   const int64_t n4 = count / 4;
   const int64_t stride = (int64_t)nblk * kExactThreads;
-  // kExactLoads float4 loads in flight per thread before any is used; then, per word that some
-  // lane of the wave touches, every element's piece for that word in one select chain
+  // kExactLoads float4 loads per thread per iteration, issued one iteration ahead (the next
+  // iteration's loads fly while this one's elements are summed); then, per word that some lane of
+  // the wave touches, every element's piece for that word in one select chain
   constexpr int U = kExactLoads;
-  constexpr int E = 4 * U;
+  auto load = [&](int64_t b, v4f (&dst)[U]) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t i4 = b + u * stride + threadIdx.x;
+      dst[u] = W4[min(i4, n4 - 1)];
+      if (i4 >= n4) dst[u] = v4f{0.f, 0.f, 0.f, 0.f};   // past the end: adds nothing
+    }
+  };
+  v4f nxt[U];
+  load((int64_t)blk * kExactThreads, nxt);
   for (int64_t base = (int64_t)blk * kExactThreads; base < n4; base += U * stride) {
     v4f v[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t i4 = base + u * stride + threadIdx.x;
-      v[u] = W4[min(i4, n4 - 1)];
-      if (i4 >= n4) v[u] = v4f{0.f, 0.f, 0.f, 0.f};
-    }
+    for (int u = 0; u < U; ++u) v[u] = nxt[u];
+    load(base + U * stride, nxt);
+    constexpr int E = 4 * U;
     uint32_t wd[E], p0[E], p1[E];
-    uint32_t wlo = 0xFFu, whi = 0u;
+    uint32_t wmask = 0u;                  // words this lane's elements touch
 #pragma unroll
     for (int j = 0; j < E; ++j) {
-      const float x = v[j / 4][j % 4];
-      const uint32_t b = __float_as_uint(x) & 0x7FFFFFFFu;
+      const uint32_t b = __float_as_uint(v[j / 4][j % 4]) & 0x7FFFFFFFu;
       const uint32_t e = b >> 23;
       const uint32_t m = (b & 0x7FFFFFu) | (e ? 0x800000u : 0u);
       const uint32_t sh = (e ? e : 1u) - 1u;
-      const uint32_t bs = sh & 31u;
+      const uint64_t piece = (uint64_t)m << (sh & 31u);   // p0 in word sh / 32, p1 in the next
       wd[j] = sh >> 5;
-      p0[j] = m << bs;
-      p1[j] = bs ? (m >> (32u - bs)) : 0u;
-      if (m) { wlo = min(wlo, wd[j]); whi = max(whi, wd[j] + 1u); }
+      p0[j] = (uint32_t)piece;
+      p1[j] = (uint32_t)(piece >> 32);
+      wmask |= m ? 3u << wd[j] : 0u;
     }
 #pragma unroll
     for (int i = 0; i < kExactWords; ++i) {
-      if (__ballot(wlo <= (uint32_t)i && (uint32_t)i <= whi) == 0ull) continue;   // uniform
+      if (__ballot((wmask >> i) & 1u) == 0ull) continue;   // uniform: no lane touches word i
       uint64_t add = 0;
 #pragma unroll
       for (int j = 0; j < E; ++j)
@@ -255,7 +280,7 @@ __device__ __forceinline__ void gamma_exact_block(const float* __restrict__ W, i
       acc[i] += add;
     }
   }
-  // block sums per word, then one 64-bit atomic per word and block
+  // block sums per word into this block's slot (plain stores); then the arrival counters
   __shared__ unsigned long long red[kExactThreads / 64][kExactWords];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
@@ -269,18 +294,46 @@ __device__ __forceinline__ void gamma_exact_block(const float* __restrict__ W, i
   if (threadIdx.x < kExactWords) {
     unsigned long long x = 0ull;
     for (int w = 0; w < kExactThreads / 64; ++w) x += red[w][threadIdx.x];
-    if (x) atomicAdd(&ws->words[threadIdx.x][0], x);
+    ws->slot[blk][threadIdx.x] = x;
   }
+  // Release / acquire at agent scope: the slot stores of every block of a group happen before
+  // its counter reaches the group's size; the last block of a group then counts in done_all,
+  // and the block that completes done_all sees every slot.
   __shared__ int last_sh;
-  __threadfence();
+  __shared__ unsigned long long words_sh[kExactWords];
+  // the barrier completes the slot stores (into this XCD's L2); thread 0's agent-scope release
+  // below then writes them back for the other XCDs -- one L2 write-back per block, not one per
+  // wave (a fence in every thread made this phase longer than the pass over W)
   __syncthreads();
-  if (threadIdx.x == 0) last_sh = atomicAdd(&ws->done, 1u) == (uint32_t)(nblk - 1);
+  if (threadIdx.x == 0) {
+    int last = 0;
+    const int grp = blk % kExactGroups;
+    const uint32_t gsize = (uint32_t)((nblk - 1 - grp) / kExactGroups + 1);
+    if (__hip_atomic_fetch_add(&ws->done_grp[grp][0], 1u, __ATOMIC_ACQ_REL,
+                               __HIP_MEMORY_SCOPE_AGENT) == gsize - 1u) {
+      const uint32_t ngroups = (uint32_t)(nblk < kExactGroups ? nblk : kExactGroups);
+      last = __hip_atomic_fetch_add(&ws->done_all, 1u, __ATOMIC_ACQ_REL,
+                                    __HIP_MEMORY_SCOPE_AGENT) == ngroups - 1u;
+    }
+    last_sh = last;
+  }
   __syncthreads();
+  if (last_sh) {
+    // sum the blocks' slots per word: wave w < kExactWords takes word w (no carry beyond 64 bits:
+    // every word sum stays below count * 2^32 < 2^64)
+    if (wave < kExactWords) {
+      unsigned long long x = 0ull;
+      for (int b = lane; b < nblk; b += 64)
+        x += __hip_atomic_load(&ws->slot[b][wave], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
+      if (lane == 0) words_sh[wave] = x;
+    }
+    __syncthreads();
+  }
   if (last_sh && threadIdx.x == 0) {
-    __threadfence();
     unsigned long long words[kExactWords];
-    for (int i = 0; i < kExactWords; ++i)
-      words[i] = __hip_atomic_load(&ws->words[i][0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (int i = 0; i < kExactWords; ++i) words[i] = words_sh[i];
     const float ge = exact_mean_from_words(words, (uint64_t)count);
     ws->gamma = ge;
     ws->tau = ternary_threshold(ge);
