@@ -53,11 +53,13 @@ __device__ __forceinline__ bool chain_wait(uint32_t* ws, uint32_t target, int64_
       }
     }
     *go_sh = go;
+    // one acquire for the block: it invalidates this CU's vector cache and the XCD's L2 for every
+    // wave, whose later loads the barrier orders after it (a fence in every wave costs as many
+    // invalidations)
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   }
   __syncthreads();
-  const bool go = *go_sh != 0;
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  return go;
+  return *go_sh != 0;
 }
 
 // This block's outputs of the phase are complete (every wave waited for its stores at the
