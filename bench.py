@@ -1193,7 +1193,10 @@ def main():
         "config": {"workload": "decode GEMV 2:4 ternary, FFN up 6912x2560 + down 2560x6912, "
                                "64 distinct pairs (cold cache), T=1,4,16 bf16 N(0,1); per step and "
                                "T: one grouped act_quant launch of the stacked activations + one "
-                               "grouped GEMV launch",
+                               "grouped GEMV launch over the 128 projections, which are "
+                               "independent (each reads its own activations; the dependent "
+                               "form is the decode_chain leg, one launch per projection the "
+                               "decode_single leg)",
                    "tokens": list(DECODE_T), "layer_pairs": N_PAIRS,
                    "packed_weight_bytes_per_pass": D.packed_bytes, "parallelism": "none"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
