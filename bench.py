@@ -697,7 +697,8 @@ def train_step_leg(S, torch, iters=3):
         masters.append(W)
         packed.append(S.pack(W, 2, 4))
         ys.append(torch.empty((T, n), dtype=torch.float32, device="cuda"))
-    ws = torch.empty(S.packed_bytes(3200, 3200)[3], dtype=torch.uint8, device="cuda")
+    ws = torch.empty(max(S.packed_bytes(n, K)[3] for (_, n, K) in TRAIN_LAYERS),
+                     dtype=torch.uint8, device="cuda")
     X = {K: torch.randn((T, K), generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
          for K in (3200, 8640)}
     Q = {K: S.act_quant(X[K]) for K in X}
@@ -714,7 +715,7 @@ def train_step_leg(S, torch, iters=3):
         for W, out in zip(masters, packed):
             S.pack(W, 2, 4, out=out, ws=ws)
 
-    # the same seven packs as one grouped pack (one partial-sum launch, one pack launch)
+    # the same seven packs as one grouped pack (each of the pack's launches once for all seven)
     pgroup = S.PackGroup([dict(W=W, out=p) for W, p in zip(masters, packed)])
 
     def pack_all():

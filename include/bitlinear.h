@@ -114,23 +114,31 @@ int bitlinear_packed_bytes(int64_t n, int64_t K, int N, int M, int layout, size_
 /* Mask + ternarize + pack one fp32 master W[n][K] (row-major, nn.Linear out x in).
  * Writes codes[codes_bytes], meta[meta_bytes] (SPARSE; pass NULL for DENSE2) and gamma[1]
  * (device fp32), all in the packed layout above.  ws is scratch of at least ws_bytes (from
- * bitlinear_packed_bytes, the same for every shape); its contents on entry do not matter.  W is
- * only read.  Three launches: fp64 partial sums of |W|; gamma, certified by a rigorous bound of
- * the fp64 sum, with an exact integer pass over W only when the exact mean lies too close to an
- * fp32 rounding boundary for the bound to decide; the packing itself. */
+ * bitlinear_packed_bytes: a fixed part plus 512 bytes per packing tile of 32 rows x at most 256
+ * columns, 1.6% of W's bytes for 2:4); its contents on entry do not matter.  W is only read.
+ * Five launches, one pass over W in the common case: a share of W (all of a small master, at
+ * least a 32nd of a large one) sampled to estimate gamma, and a band around the threshold that
+ * estimate gives (one small block); the pass that sums |W| in fp64, writes
+ * the mask and meta and every code whose weight lies clear of a narrow band around the
+ * estimate's threshold (the kept weights inside it are listed); gamma, certified by a rigorous
+ * bound of the fp64 sum, with an exact integer pass over W only when the exact mean lies too
+ * close to an fp32 rounding boundary for the bound to decide; a fix-up that sets the listed codes
+ * -- or, if the exact threshold fell outside the band or a tile listed more weights than its
+ * region holds, packs W again.  The results never depend on the sample. */
 int bitlinear_pack(const float* W, int64_t n, int64_t K, int N, int M, int layout, uint8_t* codes,
                    uint8_t* meta, float* gamma, void* ws, size_t ws_bytes, void* stream);
 
 /* For callers that cannot allocate device memory (code under graph capture, tight serving loops,
  * harnesses that forbid allocation): bitlinear_pack without a caller workspace.  Same arguments
  * minus ws / ws_bytes, same shape, alignment and error rules, same results bit for bit.  The
- * workspace is a static device array inside the library, BL_PACK_NOALLOC_WS_BYTES bytes (the
- * workspace of one bitlinear_pack call, which does not depend on n or K, so every shape
- * bitlinear_pack accepts fits; BL_ENOSPC would report a shape that did not).  Each GPU the
+ * workspace is a static device array inside the library, BL_PACK_NOALLOC_WS_BYTES bytes: the
+ * workspace of a bitlinear_pack call on up to 8192 tiles (67 M weights).  A larger master is
+ * packed without the band, in two passes over W, so every shape bitlinear_pack accepts fits
+ * (BL_ENOSPC would report one that did not).  Each GPU the
  * library runs on holds its own copy from the first call there until the process ends; the call
  * allocates nothing.  Every call on one GPU shares that copy: calls that may overlap on one GPU
  * (different streams, or different host threads) race and must be serialized by the caller. */
-#define BL_PACK_NOALLOC_WS_BYTES 42240
+#define BL_PACK_NOALLOC_WS_BYTES 4241664
 int bitlinear_pack_noalloc(const float* W, int64_t n, int64_t K, int N, int M, int layout,
                            uint8_t* codes, uint8_t* meta, float* gamma, void* stream);
 
@@ -186,20 +194,18 @@ int bitlinear_transcode6(const uint8_t* codes, const uint8_t* meta, int64_t n, i
 /* ---------------------------------------------------------------------------------------------
  * Grouped pack: the bitlinear_pack calls of several masters (a training step re-packs every
  * master of a layer set; Sparse-BitNet technical summary, the mask is recomputed at each step) in
- * three launches instead of three per master.
+ * five launches instead of five per master.
  *
- * Each master's gamma, codes and meta are exactly bitlinear_pack's, bit for bit.  One launch
- * takes the partial sums of |W| of every master, one decides every master's gamma (the exact pass
- * over a master runs only where the fp64 bound cannot decide its rounding), and the last masks,
- * ternarizes and packs every tile of every master, the masters read last by the first launch
- * first (they are still in the last-level cache).  All masters share (N, M, layout); each follows bitlinear_pack's shape and
+ * Each master's gamma, codes and meta are exactly bitlinear_pack's, bit for bit: the five
+ * launches are bitlinear_pack's, each over every master (sample, band, pass, gamma, fix-up).  The workspace is the sum of the masters' bitlinear_pack workspaces.  All
+ * masters share (N, M, layout); each follows bitlinear_pack's shape and
  * alignment rules.  Masters may be shared or overlap; outputs (codes, meta, gamma) must not
  * overlap each other or any master (BL_EINVAL).  1 <= count <= 4096.
  *
  * Use: bitlinear_pack_group_plan sizes the table and workspace; bitlinear_pack_group_build writes
  * the table (16-byte aligned device memory, caller-owned) for one workspace (256-byte aligned,
  * caller-owned, contents on entry irrelevant) and synchronizes `stream`: build once, outside any
- * graph capture; bitlinear_pack_group enqueues the three launches (asynchronous, stream-ordered,
+ * graph capture; bitlinear_pack_group enqueues the five launches (asynchronous, stream-ordered,
  * capturable).  The table keeps the descriptors' pointers; masters are read at launch time, so
  * updated masters in the same buffers need no rebuild.  Launches sharing a workspace must be
  * ordered on one stream.  A table of another N:M or layout is ignored (nothing is written).

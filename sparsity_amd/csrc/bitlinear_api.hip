@@ -538,15 +538,28 @@ int plan_bwd_group(const bl_bwd_desc* d, int64_t count, int64_t T, int N, int M,
   return BL_OK;
 }
 
-// Grouped pack: per-master workspace slices of kPackWsBytes rounded to 256 bytes.
-constexpr size_t kPackWsSlice = (bl::kPackWsBytes + 255) / 256 * 256;
+// Pack tiles of a master (32-row panels x pack_cols column tiles) and its workspace bytes: the
+// fixed part and one band region per tile.
+int64_t pack_tiles(int64_t n, int64_t K, int layout, int M) {
+  const int64_t kb = bl::pack_cols(layout, M);
+  return (n + 31) / 32 * ((K + kb - 1) / kb);
+}
+size_t pack_ws_bytes(int64_t n, int64_t K, int layout, int M) {
+  return bl::pack_ws_bytes_for_tiles(pack_tiles(n, K, layout, M));
+}
+// Grouped pack: per-master workspace slices, each rounded to 256 bytes.
+size_t pack_ws_slice(int64_t n, int64_t K, int layout, int M) {
+  return (pack_ws_bytes(n, K, layout, M) + 255) / 256 * 256;
+}
 
 // Validates a grouped pack: every descriptor as bitlinear_pack; no output (codes, meta, gamma)
 // may overlap another output or any master.  Fills the items (ws offsets from `ws`) and returns
 // the pack launch's block count.
 int plan_pack_group(const bl_pack_desc* d, int64_t count, int N, int M, int layout, uint8_t* ws,
-                    std::vector<bl::PackGroupItem>* items, int64_t* pack_blocks) {
+                    std::vector<bl::PackGroupItem>* items, int64_t* pack_blocks,
+                    size_t* ws_bytes) {
   if (!d || count < 1 || count > 4096) return BL_EINVAL;
+  size_t ws_off = 0;
   struct R { uintptr_t lo, hi; bool out; };
   std::vector<R> rs;
   items->assign((size_t)count, bl::PackGroupItem{});
@@ -568,7 +581,8 @@ int plan_pack_group(const bl_pack_desc* d, int64_t count, int N, int M, int layo
     it.codes = (uint32_t*)q.codes;
     it.meta = (uint32_t*)q.meta;
     it.gamma = q.gamma;
-    it.ws = ws + (size_t)i * kPackWsSlice;
+    it.ws = ws + ws_off;
+    ws_off += pack_ws_slice(q.n, q.K, layout, M);
     it.n = (int32_t)q.n;
     it.K = (int32_t)q.K;
     it.k_tiles = (int32_t)((q.K + bl::pack_cols(layout, M) - 1) / bl::pack_cols(layout, M));
@@ -590,6 +604,7 @@ int plan_pack_group(const bl_pack_desc* d, int64_t count, int N, int M, int layo
     if (blocks > INT32_MAX) return BL_EINVAL;
   }
   *pack_blocks = blocks;
+  *ws_bytes = ws_off;
   return BL_OK;
 }
 
@@ -784,7 +799,7 @@ int bitlinear_packed_bytes(int64_t n, int64_t K, int N, int M, int layout, size_
   if (codes_bytes) *codes_bytes = (size_t)(n_pad * slots / 4);
   if (meta_bytes) *meta_bytes = layout == BL_LAYOUT_SPARSE ? (size_t)(n_pad * slots / 4) : 0;
   if (K_eff) *K_eff = ke;
-  if (ws_bytes) *ws_bytes = bl::kPackWsBytes;
+  if (ws_bytes) *ws_bytes = pack_ws_bytes(n, K, layout, M);
   return BL_OK;
 }
 
@@ -795,9 +810,9 @@ int bitlinear_pack(const float* W, int64_t n, int64_t K, int N, int M, int layou
   if (st != BL_OK) return st;
   if (!aligned16(W) || !aligned16(codes) || !aligned16(gamma) || !aligned16(ws)) return BL_EINVAL;
   if (layout == BL_LAYOUT_SPARSE ? !aligned16(meta) : meta != nullptr) return BL_EINVAL;
-  if (ws_bytes < bl::kPackWsBytes) return BL_ENOSPC;
+  if (ws_bytes < pack_ws_bytes(n, K, layout, M)) return BL_ENOSPC;
   return status_of(bl::launch_pack(W, n, K, N, M, layout, (uint32_t*)codes, (uint32_t*)meta, gamma,
-                                   ws, (hipStream_t)stream));
+                                   ws, pack_tiles(n, K, layout, M), (hipStream_t)stream));
 }
 
 int bitlinear_pack_noalloc(const float* W, int64_t n, int64_t K, int N, int M, int layout,
@@ -807,7 +822,8 @@ int bitlinear_pack_noalloc(const float* W, int64_t n, int64_t K, int N, int M, i
   if (st != BL_OK) return st;
   if (!aligned16(W) || !aligned16(codes) || !aligned16(gamma)) return BL_EINVAL;
   if (layout == BL_LAYOUT_SPARSE ? !aligned16(meta) : meta != nullptr) return BL_EINVAL;
-  // the static workspace holds one pack workspace, whose size does not depend on the shape
+  // the static workspace holds the fixed part and band regions for kNoallocTiles tiles; a larger
+  // master is packed without the band (two passes), so every shape fits
   if (bl::kPackWsBytes > bl::pack_noalloc_capacity()) return BL_ENOSPC;
   return status_of(bl::launch_pack_noalloc(W, n, K, N, M, layout, (uint32_t*)codes,
                                            (uint32_t*)meta, gamma, (hipStream_t)stream));
@@ -818,11 +834,12 @@ int bitlinear_pack_group_plan(const bl_pack_desc* descs, int64_t count, int N, i
   if (!plan) return BL_EINVAL;
   std::vector<bl::PackGroupItem> items;
   int64_t blocks = 0;
-  const int st = plan_pack_group(descs, count, N, M, layout, nullptr, &items, &blocks);
+  size_t wsb = 0;
+  const int st = plan_pack_group(descs, count, N, M, layout, nullptr, &items, &blocks, &wsb);
   if (st != BL_OK) return st;
   memset(plan, 0, sizeof *plan);
   plan->table_bytes = sizeof(bl::PackGroupHeader) + (size_t)count * sizeof(bl::PackGroupItem);
-  plan->ws_bytes = (size_t)count * kPackWsSlice;
+  plan->ws_bytes = wsb;
   plan->count = count;
   plan->pack_blocks = blocks;
   plan->N = N;
@@ -837,10 +854,11 @@ int bitlinear_pack_group_build(const bl_pack_desc* descs, int64_t count, int N, 
   if (!ws || ((uintptr_t)ws & 255u) || !aligned16(table)) return BL_EINVAL;
   std::vector<bl::PackGroupItem> items;
   int64_t blocks = 0;
-  const int st = plan_pack_group(descs, count, N, M, layout, (uint8_t*)ws, &items, &blocks);
+  size_t wsb = 0;
+  const int st = plan_pack_group(descs, count, N, M, layout, (uint8_t*)ws, &items, &blocks, &wsb);
   if (st != BL_OK) return st;
   const size_t bytes = sizeof(bl::PackGroupHeader) + (size_t)count * sizeof(bl::PackGroupItem);
-  if (ws_bytes < (size_t)count * kPackWsSlice || table_bytes < bytes) return BL_ENOSPC;
+  if (ws_bytes < wsb || table_bytes < bytes) return BL_ENOSPC;
   std::vector<uint8_t> img(bytes, 0);
   bl::PackGroupHeader hdr;
   memset(&hdr, 0, sizeof hdr);

@@ -6,21 +6,33 @@
 // in each M-group (same summary, Maskering) and (2N-2):2N groups -- 6:8, 14:16 -- are rewritten
 // as N-1 overlapping 2:4 windows (SlideSparse abstract, Sliding Window Decomposition).
 //
-// Three launches, all on the caller's stream:
-//   1. gamma_partial_kernel   fp64 partial sums of |w| (HBM-bound read of W); it also clears the
-//                             arrival counters of launch 2
-//   2. gamma_exact_kernel     every block sums the partials in one fixed order (all get the same
-//                             bits) and certifies the fp32 rounding of the exact mean with a
-//                             rigorous error bound.  Certified (the common case): block 0 stores
-//                             gamma and the ternary threshold tau, and every block exits.
-//                             Otherwise the blocks sum |W| exactly as integers (24-bit
-//                             significands shifted to a 2^-149 fixed point, kept as carry-free
-//                             32-bit words in 64-bit accumulators), each block stores its word
-//                             sums in a line of its own, and the last block to arrive sums them,
-//                             rounds the exact mean to fp32 and stores gamma and tau: one extra
-//                             pass over W, once per master
-//   3. pack_kernel            reads tau; mask, codes by |w| >= tau, slots assembled in LDS,
-//                             coalesced dword stores.
+// Five launches, all on the caller's stream, one HBM pass over W in the common case:
+//   1. gamma_sample_kernel  a fixed share of W (1 segment of 256 bytes in S, S = 1..32 by size)
+//                           spread over the matrix: per-block sums of |w|; block 0 also clears the
+//                           accumulators of launches 3-4
+//   2. band_kernel          one block: the sample's estimate of mean |W| and its standard error
+//                           give a band [tau_lo, tau_hi] that holds the exact threshold tau unless
+//                           the sample misleads
+//   3. pack_spec_kernel     the pass over W: per 32-row tile, the fp64 sums of |w| (added into one
+//                           of kGammaBlocks slots), the mask and meta (final: they do not depend on
+//                           gamma) and the codes against the band -- |w| >= tau_hi codes +-1,
+//                           |w| < tau_lo codes 0, and a kept weight in between codes 0 and is
+//                           listed in the tile's own region of the workspace with its code
+//                           position and |w|
+//   4. gamma_exact_kernel   every block sums the slots in one fixed order and certifies the fp32
+//                           rounding of the exact mean with a rigorous error bound.  Certified
+//                           (the common case): block 0 stores gamma and the ternary threshold tau,
+//                           and every block exits.  Otherwise the blocks sum |W| exactly as
+//                           integers (24-bit significands shifted to a 2^-149 fixed point, kept as
+//                           carry-free 32-bit words in 64-bit accumulators), each block stores its
+//                           word sums in a line of its own, and the last block to arrive rounds
+//                           the exact mean to fp32 and stores gamma and tau
+//   5. pack_fix_kernel      tau inside the band and no region overflowed: the listed codes with
+//                           |w| >= tau are set.  Otherwise (tau outside the band, a tile listed
+//                           more than its region holds, no band) every tile is packed again
+//                           against tau: a second pass over W.
+// The codes therefore follow |w| >= tau for the exact tau whatever the sample says; the sample
+// only decides how much work the fix-up has.
 #include <mutex>
 
 #include "device_common.hpp"
@@ -29,69 +41,75 @@
 
 namespace bl {
 
+static_assert(sizeof(PackWs) <= kPackWsFixed, "pack workspace");
+static_assert(kSampleBlocks <= kGammaThreads, "one sampling block per thread of a pack block");
 
-// The exact fixed-point sum: |w| = m * 2^(max(e,1) - 150) with a 24-bit significand m is
-// m << (max(e,1) - 1) units of 2^-149, at most 24 + 253 bits, so word kExactWords - 1 = 8 is the
-// highest a piece reaches.
-struct PackWs {
-  double partial[kGammaBlocks];      // fp64 partial sums of |w|, one per partial-sum block
-  // exact fallback: block b's word sums (sum_i slot[b][i] * 2^(32 i) units of 2^-149), one
-  // 128-byte line per block, written with plain stores: no two blocks touch one line
-  unsigned long long slot[kExactBlocks][16];
-  // arrival counters, one line each: block b counts in group b % kExactGroups; the last block of
-  // a group counts in done_all (at most kExactBlocks / kExactGroups atomics queue on one line)
-  uint32_t done_grp[kExactGroups][32];
-  uint32_t done_all, pad[31];
-  float gamma, tau;                  // gamma and the ternary threshold, read by every pack block
-  uint32_t exact_used;               // 1 when the exact fallback decided gamma (diagnostic)
-  uint32_t pad2;
-};
-static_assert(sizeof(PackWs) <= kPackWsBytes, "pack workspace");
+// Sampling stride: about 2^19 sampled weights, at least a 32nd of the master, all of a small one.
+__host__ __device__ __forceinline__ int64_t sample_stride(int64_t count) {
+  int64_t S = 1;
+  while (S < 32 && (count >> 19) >= 2 * S) S *= 2;
+  return S;
+}
 
-__device__ __forceinline__ void gamma_partial_block(const float4* __restrict__ W4, int64_t n4,
-                                                    double* __restrict__ partial, int blk) {
-  // Four independent fp64 chains per thread keep four 16-byte loads in flight.  Every |w| still
-  // passes through at most 4 * ceil(n4 / threads) + 2 additions before the wave sum, inside the
-  // depth the finalize step assumes for its error bound.
-  const int64_t stride = (int64_t)kGammaBlocks * kGammaThreads;
-  double a0 = 0.0, a1 = 0.0, a2 = 0.0, a3 = 0.0;
-  int64_t i = (int64_t)blk * kGammaThreads + threadIdx.x;
-  for (; i + 3 * stride < n4; i += 4 * stride) {
-    const float4 v0 = W4[i], v1 = W4[i + stride], v2 = W4[i + 2 * stride], v3 = W4[i + 3 * stride];
-    a0 += fabs((double)v0.x); a0 += fabs((double)v0.y); a0 += fabs((double)v0.z); a0 += fabs((double)v0.w);
-    a1 += fabs((double)v1.x); a1 += fabs((double)v1.y); a1 += fabs((double)v1.z); a1 += fabs((double)v1.w);
-    a2 += fabs((double)v2.x); a2 += fabs((double)v2.y); a2 += fabs((double)v2.z); a2 += fabs((double)v2.w);
-    a3 += fabs((double)v3.x); a3 += fabs((double)v3.y); a3 += fabs((double)v3.z); a3 += fabs((double)v3.w);
+// The sampled segments: 64 floats each, segment j = S j + (7 j mod S) for j < count / (64 S).
+// Each quarter-wave reads one segment per step (lane i: float4 i of it) and a thread keeps the
+// sum s of its |w| and their number c; the block stores the sums of s, s^2, s c, c and c^2 over
+// its threads.  Threads are the sampling units: each one's segments lie far apart in the matrix.
+__device__ __forceinline__ void gamma_sample_block(const float4* __restrict__ W4, int64_t count,
+                                                   PackWs* __restrict__ ws, int blk) {
+  const int64_t S = sample_stride(count);
+  const int64_t ns = count / (64 * S);
+  const int64_t Q = (int64_t)kSampleBlocks * kGammaThreads / 16;   // quarter-waves in the launch
+  const int64_t q0 = ((int64_t)blk * kGammaThreads + threadIdx.x) >> 4;
+  const int l16 = threadIdx.x & 15;
+  double s = 0.0, c = 0.0;
+  for (int64_t j = q0; j < ns; j += 4 * Q) {
+    float4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t jj = min(j + u * Q, ns - 1);
+      v[u] = W4[(S * jj + ((7 * jj) & (S - 1))) * 16 + l16];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (j + u * Q < ns) {
+        s += (fabs((double)v[u].x) + fabs((double)v[u].y)) + (fabs((double)v[u].z) + fabs((double)v[u].w));
+        c += 4.0;
+      }
   }
-  for (; i < n4; i += stride) {
-    const float4 v = W4[i];
-    a0 += fabs((double)v.x); a0 += fabs((double)v.y); a0 += fabs((double)v.z); a0 += fabs((double)v.w);
+  double st[kSampleStats] = {s, s * s, s * c, c, c * c};
+  __shared__ double red[kGammaThreads / 64][kSampleStats];
+#pragma unroll
+  for (int i = 0; i < kSampleStats; ++i) {
+    st[i] = wave_sum_f64(st[i]);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6][i] = st[i];
   }
-  double acc = (a0 + a1) + (a2 + a3);
-  acc = wave_sum_f64(acc);
-  __shared__ double red[kGammaThreads / 64];
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = acc;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    double s = 0.0;
-    for (int w = 0; w < kGammaThreads / 64; ++w) s += red[w];
-    partial[blk] = s;
+  if (threadIdx.x < kSampleStats) {
+    double t = 0.0;
+    for (int w = 0; w < kGammaThreads / 64; ++w) t += red[w][threadIdx.x];
+    ws->sample[threadIdx.x][blk] = t;
   }
 }
 
-// Block 0 also clears the exact pass's arrival counters: the exact launch counts in them, and
-// this launch has completed before it starts.  (The per-block word slots are overwritten, not
-// added to.)
-__device__ __forceinline__ void clear_exact_state(PackWs* __restrict__ ws, int blk) {
-  if (blk == 0 && threadIdx.x < kExactGroups) ws->done_grp[threadIdx.x][0] = 0u;
-  if (blk == 0 && threadIdx.x == kExactGroups) ws->done_all = 0u;
+// Block 0 of the sampling launch clears what launches 3-4 accumulate into: the sum slots, the
+// overflow flag and the exact pass's arrival counters.  (The exact pass's per-block word slots
+// and the tiles' regions are overwritten, not added to.)
+__device__ __forceinline__ void clear_pack_state(PackWs* __restrict__ ws, int blk) {
+  if (blk != 0) return;
+  for (int i = threadIdx.x; i < kGammaBlocks; i += kGammaThreads) ws->partial[i] = 0.0;
+  if (threadIdx.x < kExactGroups) ws->done_grp[threadIdx.x][0] = 0u;
+  if (threadIdx.x == 0) {
+    ws->done_all = 0u;
+    ws->overflow = 0u;
+  }
 }
 
-__global__ __launch_bounds__(kGammaThreads) void gamma_partial_kernel(const float4* __restrict__ W4,
-                                                                      int64_t n4,
-                                                                      PackWs* __restrict__ ws) {
-  clear_exact_state(ws, blockIdx.x);
-  gamma_partial_block(W4, n4, ws->partial, blockIdx.x);
+__global__ __launch_bounds__(kGammaThreads) void gamma_sample_kernel(const float4* __restrict__ W4,
+                                                                     int64_t count,
+                                                                     PackWs* __restrict__ ws) {
+  clear_pack_state(ws, blockIdx.x);
+  gamma_sample_block(W4, count, ws, blockIdx.x);
 }
 
 // Round (sum_i words[i] * 2^(32 i - 149)) / count to the nearest fp32, ties to even, exactly.
@@ -171,11 +189,11 @@ __device__ float ternary_threshold(float gamma) {
 constexpr int kExactThreads = 1024;  // 16 waves: four per SIMD for the rare exact pass
 constexpr int kExactLoads = 2;       // float4 loads per thread per iteration of the exact pass
 
-// Certified fp32 rounding of mean |W| from the fp64 partial sums, computed by a whole block in one
+// Certified fp32 rounding of mean |W| from the fp64 slot sums, computed by a whole block in one
 // fixed order (every block gets the same bits).  Returns 1 and *g when the rigorous error bound of
 // the fp64 sum decides the rounding (or the sum is 0), else 0.
 __device__ __forceinline__ int block_certify(const PackWs* __restrict__ ws, int64_t count,
-                                             float* __restrict__ g) {
+                                             int64_t tiles, float* __restrict__ g) {
   static_assert(kGammaBlocks % kExactThreads == 0, "partials split evenly");
   __shared__ double red_sh[kExactThreads / 64];
   __shared__ float g_sh;
@@ -190,13 +208,13 @@ __device__ __forceinline__ int block_certify(const PackWs* __restrict__ ws, int6
   if (threadIdx.x == 0) {
     double S = 0.0;
     for (int w = 0; w < kExactThreads / 64; ++w) S += red_sh[w];
-    // longest chain of fp64 additions any |w| goes through: the partial kernel's per-thread
-    // chains (at most 4 per float4 it reads, plus 2 to join its four chains), its wave butterfly
-    // (6) and block sum (4), then here the per-thread sum (kGammaBlocks / kExactThreads = 1),
-    // the butterfly (6) and the block sum (kExactThreads / 64 = 16); 64 covers every fixed term
-    const int64_t n4 = count / 4;
-    const int64_t per_thread = (n4 + (int64_t)kGammaBlocks * kGammaThreads - 1) / ((int64_t)kGammaBlocks * kGammaThreads);
-    const double depth = 4.0 * (double)per_thread + 64.0;
+    // longest chain of fp64 additions any |w| goes through: in its pack tile the thread's 32
+    // terms and the wave butterfly (6); its slot's chain (one hardware atomic addition per wave of
+    // each tile that shares the slot, four per tile, counted twice in case the atomic unit rounds
+    // faithfully rather than to nearest); here the per-thread sum (kGammaBlocks / kExactThreads =
+    // 1), the butterfly (6) and the block sum (kExactThreads / 64 = 16).  128 covers every fixed
+    // term.
+    const double depth = 128.0 + 8.0 * (double)((tiles + kGammaBlocks - 1) / kGammaBlocks);
     const double u = 0x1p-53;
     const double err = 2.0 * depth * u * S;  // >= ((1+u)^depth - 1) * S for nonnegative terms
     const double cnt = (double)count;
@@ -212,15 +230,17 @@ __device__ __forceinline__ int block_certify(const PackWs* __restrict__ ws, int6
   return ok_sh;
 }
 
-// The exact sum of |W| over this block's share (float4 i4 = blk * NT + tid, strided by the
-// master's blocks), added to ws->words; the last block to finish rounds the exact mean.
+// gamma for launch 4: certified from the slot sums, or else the exact sum of |W| over this
+// block's share (float4 i4 = blk * NT + tid, strided by the master's blocks), the last block to
+// finish rounding the exact mean.
 // Each element's m << (max(e,1) - 1) is split into 32-bit pieces p0 (word w) and p1 (word w + 1);
 // a lane keeps one 64-bit sum per word, so no carry is taken until the end (every word sum stays
 // below count * 2^32 < 2^64).  Words no lane of the wave touches in an iteration are skipped.
-__device__ __forceinline__ void gamma_exact_block(const float* __restrict__ W, int64_t count, PackWs* __restrict__ ws,
-                                  float* __restrict__ gamma_out, int blk, int nblk) {
+__device__ __forceinline__ void gamma_exact_block(const float* __restrict__ W, int64_t count,
+                                                  int64_t tiles, PackWs* __restrict__ ws,
+                                                  float* __restrict__ gamma_out, int blk, int nblk) {
   float g = 0.f;
-  if (block_certify(ws, count, &g)) {   // uniform across the block and the launch
+  if (block_certify(ws, count, tiles, &g)) {   // uniform across the block and the launch
     if (blk == 0 && threadIdx.x == 0) {
       ws->gamma = g;
       ws->tau = ternary_threshold(g);
@@ -343,25 +363,108 @@ __device__ __forceinline__ void gamma_exact_block(const float* __restrict__ W, i
 }
 
 __global__ __launch_bounds__(kExactThreads) void gamma_exact_kernel(const float* __restrict__ W,
-                                                                    int64_t count,
+                                                                    int64_t count, int64_t tiles,
                                                                     PackWs* __restrict__ ws,
                                                                     float* __restrict__ gamma_out) {
-  gamma_exact_block(W, count, ws, gamma_out, blockIdx.x, gridDim.x);
+  gamma_exact_block(W, count, tiles, ws, gamma_out, blockIdx.x, gridDim.x);
 }
 
-constexpr int kPackWidth = 256;  // LDS width of a pack tile (fp32 columns)
+constexpr int kPackWidth = 256;  // dense columns of a pack tile at most (one float4 per lane)
+
+// fp32 neighbours of a positive fp64 value: the largest fp32 <= x and the smallest fp32 >= x.
+__device__ __forceinline__ float f32_down(double x) {
+  float f = (float)x;
+  if ((double)f > x) f = __int_as_float(__float_as_int(f) - 1);
+  return f;
+}
+__device__ __forceinline__ float f32_up(double x) {
+  float f = (float)x;
+  if ((double)f < x) f = __int_as_float(__float_as_int(f) + 1);
+  return f;
+}
+
+// The band regions: tile t's kTileEntries entries at (uint2) entries[t * kTileEntries + e], each
+// (code position word, |w| bits); unused entries hold kNoEntry, whose NaN never passes |w| >= tau.
+constexpr uint32_t kNoEntryPos = 0xFFFFFFFFu, kNoEntryAbs = 0x7FFFFFFFu;
+__device__ __forceinline__ uint2* ws_entries(PackWs* ws) {
+  return (uint2*)((uint8_t*)ws + pack_ws_entries_off());
+}
+
+// The coding band, from the sampling launch's sums (one block per master, before the pass).  The
+// sample mean mu estimates mean |W|; its standard error comes from the spread of the per-thread
+// sums (ratio estimator).  gamma is taken to lie within mu (1 +- d), d = 6 standard errors +
+// 2^-20, rounded outward to fp32, and the band is the two thresholds of those bounds: whatever
+// gamma turns out to be inside it, a weight below tau_lo codes 0 and one at or above tau_hi codes
+// +-1.  Not usable (band_ok 0, both bounds +inf: every weight codes 0 and nothing is listed, so
+// the fix-up repacks) when the sample is empty, not finite, wider than a quarter of mu, the
+// workspace has no region for every tile, or the code positions do not fit the entries' 27 bits.
+__device__ __forceinline__ void band_block(PackWs* __restrict__ ws, uint64_t code_dwords,
+                                           bool regions) {
+  __shared__ double red[kSampleBlocks / 64][kSampleStats];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (wave < kSampleBlocks / 64) {
+#pragma unroll
+    for (int i = 0; i < kSampleStats; ++i) {
+      const double t = wave_sum_f64(ws->sample[i][threadIdx.x]);
+      if (lane == 0) red[wave][i] = t;
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x != 0) return;
+  double st[kSampleStats];
+#pragma unroll
+  for (int i = 0; i < kSampleStats; ++i) {
+    st[i] = 0.0;
+    for (int w = 0; w < kSampleBlocks / 64; ++w) st[i] += red[w][i];
+  }
+  float lo = __int_as_float(0x7f800000), hi = lo;
+  uint32_t ok = 0u;
+  const double c1 = st[3];
+  const double mu = c1 > 0.0 ? st[0] / c1 : 0.0;
+  // sum over threads of (s - mu c)^2
+  const double v = fmax(st[1] - 2.0 * mu * st[2] + mu * mu * st[4], 0.0);
+  const double d = 6.0 * sqrt(v) / c1 / mu + 0x1p-20;
+  if (regions && c1 > 0.0 && mu > 0.0 && isfinite(mu) && d < 0.25 && code_dwords < (1ull << 27)) {
+    const float glo = f32_down(mu * (1.0 - d)), ghi = f32_up(mu * (1.0 + d));
+    if (glo > 0.f && ghi < 3.0e38f) {
+      lo = ternary_threshold(glo);
+      hi = ternary_threshold(ghi);
+      ok = 1u;
+    }
+  }
+  ws->tau_lo = lo;
+  ws->tau_hi = hi;
+  ws->band_ok = ok;
+}
+
+// Code dwords of a master (32-row panels x packed fragments x 64) and its pack tiles.
+__host__ __device__ __forceinline__ uint64_t pack_code_dwords(int64_t n, int64_t K, int layout, int M) {
+  const int64_t nfrag = layout == kLayoutSparse ? (M == 4 ? K : K / M * (2 * M - 4)) / 64 : K / 32;
+  return (uint64_t)((n + kPanel - 1) / kPanel) * (uint64_t)nfrag * 64u;
+}
+
+__global__ __launch_bounds__(kGammaThreads) void band_kernel(PackWs* __restrict__ ws,
+                                                             uint64_t code_dwords, int regions) {
+  band_block(ws, code_dwords, regions != 0);
+}
 
 // One block packs one 32-row panel x KB dense columns (KB = pack_cols: whole M-groups and whole
-// 32-slot fragments, at most 256).  Phase 1 stages the fp32 tile in LDS with
-// coalesced 1 KB row reads; phase 2 turns each M-group into slot bytes (code | index << 2);
-// phase 3 assembles 16-slot units into code/meta dwords, which land contiguously in the tiled
-// layout (unit v = 32*u + r of the tile is dword base + v).
-template <int LAYOUT, int M>
+// 32-slot fragments, at most 256).  Every lane loads one float4 of eight rows.  M = 4: that
+// float4 is one whole group, masked and coded in registers; otherwise the fp32 tile is staged in
+// LDS and each thread takes whole groups from it.  Either way a group becomes slot bytes
+// (code | index << 2) in LDS, and 16-slot units are assembled into code/meta dwords, which land
+// contiguously in the tiled layout (unit v = 32*u + r of the tile is dword base + v, slot i of it
+// at bits 8 (i % 4) + 2 (i / 4)).
+// SPEC (the one-pass pack): codes against the band; each wave's fp64 sum of |w| goes into slot
+// blk % kGammaBlocks and the tile's band entries into its region.  Otherwise (the fix-up's
+// repack) codes against the exact tau.
+template <int LAYOUT, int M, bool SPEC>
 __device__ __forceinline__ void pack_tile(const float* __restrict__ W, int n, int K, int N,
-                                          int k_tiles, const PackWs* __restrict__ ws,
+                                          int k_tiles, PackWs* __restrict__ ws,
                                           uint32_t* __restrict__ codes,
                                           uint32_t* __restrict__ meta, int blk) {
   constexpr bool SP = LAYOUT == kLayoutSparse;
+  constexpr bool REG = M == 4;                                         // one group per float4
   constexpr int KB = pack_cols(LAYOUT, M);
   constexpr int WS = kPackWidth + 4;                                   // padded fp32 row
   constexpr int NKEEP = M == 4 ? 2 : M - 2;                           // SPARSE: 2:4, (M-2):M
@@ -369,47 +472,61 @@ __device__ __forceinline__ void pack_tile(const float* __restrict__ W, int n, in
   constexpr int SS = SLOTS + 16;                                       // padded slot row
   constexpr int GPR = KB / M;                                          // groups per tile row
   constexpr int UPR = SLOTS / 16;                                      // units per tile row
-  __shared__ __attribute__((aligned(16))) float tile[32 * WS];
+  static_assert(!REG || GPR == 64, "a lane's float4 is group c4 of its rows");
+  __shared__ __attribute__((aligned(16))) float tile[REG ? 1 : 32 * WS];
   __shared__ __attribute__((aligned(16))) uint8_t slots[32 * SS];
+  __shared__ uint2 lst[SPEC ? kTileEntries : 1];
+  __shared__ int nl_sh;
 
   const int P = blk / k_tiles;
   const int kb = blk % k_tiles;
   const int k0 = kb * KB;
   const int r0 = P * kPanel;
   const int kw = min(KB, K - k0);
+  const int nfrag = SP ? (M == 4 ? K : K / M * (2 * M - 4)) / 64 : K / 32;   // fragments per panel
+  const size_t base = ((size_t)P * nfrag + (size_t)kb * (UPR / 2)) * 64;
 
-  // all eight 16-byte tile loads before the first LDS store (addresses clamped into the matrix;
+  // all eight 16-byte tile loads before anything else (addresses clamped into the matrix;
   // out-of-range rows and columns are zeroed after the load)
-  const float tau = ws->tau;
+  const int c4 = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  float4 v[8];
   {
-    const int c4 = threadIdx.x & 63;
-    const bool col_ok = 4 * c4 < kw;
     const int col = k0 + min(4 * c4, kw - 4);
-    float4 v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      v[i] = *(const float4*)(W + (size_t)min(r0 + i * 4 + wv, n - 1) * K + col);
+  }
+  // codes: |w| >= hi is +-1, |w| < lo is 0, between (SPEC only) listed
+  const float lo = SPEC ? ws->tau_lo : ws->tau, hi = SPEC ? ws->tau_hi : ws->tau;
+  const uint32_t band_ok = SPEC ? ws->band_ok : 0u;
+  if (SPEC && threadIdx.x == 0) nl_sh = 0;   // read after the barrier below
+  {
+    const bool col_ok = 4 * c4 < kw;
+    double ts = 0.0;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const int row = i * 4 + (threadIdx.x >> 6);
-      v[i] = *(const float4*)(W + (size_t)min(r0 + row, n - 1) * K + col);
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int row = i * 4 + (threadIdx.x >> 6);
+      const int row = i * 4 + wv;
       if (!(col_ok && r0 + row < n)) v[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-      *(float4*)&tile[row * WS + 4 * c4] = v[i];
+      if constexpr (!REG) *(float4*)&tile[row * WS + 4 * c4] = v[i];
+      if constexpr (SPEC) {
+        ts += fabs((double)v[i].x); ts += fabs((double)v[i].y);
+        ts += fabs((double)v[i].z); ts += fabs((double)v[i].w);
+      }
+    }
+    if constexpr (SPEC) {
+      // each wave adds its sum into the tile's slot; no return value is waited for
+      ts = wave_sum_f64(ts);
+      if (c4 == 0) unsafeAtomicAdd(&ws->partial[blk % kGammaBlocks], ts);
     }
   }
-  __syncthreads();
+  if constexpr (!REG) __syncthreads();
 
   const int nkeep = SP ? NKEEP : N;
-  for (int gid = threadIdx.x; gid < 32 * GPR; gid += 256) {
-    const int row = gid / GPR, g = gid % GPR;
-    float w[M];
+  // One M-group at (row, g) with values w: mask, codes, slot bytes.
+  auto group = [&](int row, int g, const float (&w)[M]) {
     uint32_t a[M];
 #pragma unroll
-    for (int j = 0; j < M; ++j) {
-      w[j] = tile[row * WS + g * M + j];
-      a[j] = __float_as_uint(w[j]) & 0x7FFFFFFFu;
-    }
+    for (int j = 0; j < M; ++j) a[j] = __float_as_uint(w[j]) & 0x7FFFFFFFu;
     uint32_t keep = 0;
 #pragma unroll
     for (int i = 0; i < M; ++i) {
@@ -419,14 +536,26 @@ __device__ __forceinline__ void pack_tile(const float* __restrict__ W, int n, in
         if (j != i) rank += (a[j] > a[i]) || (a[j] == a[i] && j < i);
       if (rank < nkeep) keep |= 1u << i;
     }
-    // 00 = 0, 01 = +1, 10 = -1
-    auto code = [&](int j) -> uint32_t { return fabsf(w[j]) >= tau ? (w[j] < 0.f ? 2u : 1u) : 0u; };
+    // 00 = 0, 01 = +1, 10 = -1.  A kept weight of the band codes 0 here and is listed with its
+    // code position (dword, slot i of the unit, sign) and |w|, for the fix-up.
+    auto code = [&](int j, int sp) -> uint32_t {
+      const float aj = __uint_as_float(a[j]);
+      if (SPEC && aj >= lo && aj < hi) {
+        const int i = sp & 15;
+        const uint32_t x = (uint32_t)(base + 32 * (sp >> 4) + row) |
+                           ((uint32_t)(4 * (i & 3) + (i >> 2)) << 27) | (w[j] < 0.f ? 1u << 31 : 0u);
+        const int e = atomicAdd(&nl_sh, 1);
+        if (e < kTileEntries) lst[e] = make_uint2(x, a[j]);
+        return 0u;
+      }
+      return aj >= hi ? (w[j] < 0.f ? 2u : 1u) : 0u;
+    };
     uint8_t* out = &slots[row * SS];
     if constexpr (SP && M == 4) {
       int s = 0;
 #pragma unroll
       for (int p = 0; p < 4; ++p)
-        if (keep >> p & 1u) { out[2 * g + s] = (uint8_t)(code(p) | (p << 2)); ++s; }
+        if (keep >> p & 1u) { out[2 * g + s] = (uint8_t)(code(p, 2 * g + s) | (p << 2)); ++s; }
     } else if constexpr (SP) {
       // (M-2):M into M/2 - 1 windows covering positions 2w..2w+3: kept positions in ascending
       // order, each to the lowest window that covers it and holds fewer than two (position p
@@ -443,21 +572,35 @@ __device__ __forceinline__ void pack_tile(const float* __restrict__ W, int n, in
         int wdw, slot;
         if (cnt[wlo] < 2) { wdw = wlo; slot = 2 * wlo + cnt[wlo]; ++cnt[wlo]; }
         else { wdw = whi; slot = 2 * whi + cnt[whi]; ++cnt[whi]; }
-        out[NKEEP * g + slot] = (uint8_t)(code(p) | ((p - 2 * wdw) << 2));
+        out[NKEEP * g + slot] = (uint8_t)(code(p, NKEEP * g + slot) | ((p - 2 * wdw) << 2));
       }
     } else {
 #pragma unroll
-      for (int j = 0; j < M; ++j) out[g * M + j] = (uint8_t)((keep >> j & 1u) ? code(j) : 0u);
+      for (int j = 0; j < M; ++j) out[g * M + j] = (uint8_t)((keep >> j & 1u) ? code(j, g * M + j) : 0u);
+    }
+  };
+  if constexpr (REG) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      float w[M];
+      w[0] = v[i].x; w[1] = v[i].y; w[2] = v[i].z; w[3] = v[i].w;
+      group(i * 4 + wv, c4, w);
+    }
+  } else {
+    for (int gid = threadIdx.x; gid < 32 * GPR; gid += 256) {
+      const int row = gid / GPR, g = gid % GPR;
+      float w[M];
+#pragma unroll
+      for (int j = 0; j < M; ++j) w[j] = tile[row * WS + g * M + j];
+      group(row, g, w);
     }
   }
   __syncthreads();
 
   const int valid_slots = SP ? kw * NKEEP / M : kw;
   const int units_valid = valid_slots / 16;
-  const int nfrag = SP ? (M == 4 ? K : K / M * (2 * M - 4)) / 64 : K / 32;   // fragments per panel
-  const size_t base = ((size_t)P * nfrag + (size_t)kb * (UPR / 2)) * 64;
-  for (int v = threadIdx.x; v < 32 * UPR; v += 256) {
-    const int u = v >> 5, r = v & 31;
+  for (int u4 = threadIdx.x; u4 < 32 * UPR; u4 += 256) {
+    const int u = u4 >> 5, r = u4 & 31;
     if (u >= units_valid) continue;
     const uint4 sb = *(const uint4*)&slots[r * SS + 16 * u];
     const uint32_t wd[4] = {sb.x, sb.y, sb.z, sb.w};
@@ -468,52 +611,115 @@ __device__ __forceinline__ void pack_tile(const float* __restrict__ W, int n, in
       cw |= (b & 3u) << (8 * (i & 3) + 2 * (i >> 2));
       mw |= (b >> 2) << (2 * i);
     }
-    codes[base + v] = cw;
-    if constexpr (SP) meta[base + v] = mw;
+    codes[base + u4] = cw;
+    if constexpr (SP) meta[base + u4] = mw;
+  }
+  if constexpr (SPEC) {
+    // the tile's region: its band entries, then kNoEntry (no counter shared between tiles)
+    if (!band_ok) return;
+    const int nl = nl_sh;   // final: every append happened before the barrier above
+    if (nl > kTileEntries && threadIdx.x == 0) ws->overflow = 1u;
+    if (threadIdx.x < kTileEntries)
+      ws_entries(ws)[(size_t)blk * kTileEntries + threadIdx.x] =
+          threadIdx.x < nl && nl <= kTileEntries ? lst[threadIdx.x]
+                                                 : make_uint2(kNoEntryPos, kNoEntryAbs);
   }
 }
 
 template <int LAYOUT, int M>
-__global__ __launch_bounds__(256) void pack_kernel(const float* __restrict__ W, int n, int K, int N,
-                                                   int k_tiles, const PackWs* __restrict__ ws,
-                                                   uint32_t* __restrict__ codes,
-                                                   uint32_t* __restrict__ meta) {
-  pack_tile<LAYOUT, M>(W, n, K, N, k_tiles, ws, codes, meta, blockIdx.x);
+__global__ __launch_bounds__(256, 6) void pack_spec_kernel(const float* __restrict__ W, int n, int K,
+                                                        int N, int k_tiles,
+                                                        PackWs* __restrict__ ws,
+                                                        uint32_t* __restrict__ codes,
+                                                        uint32_t* __restrict__ meta) {
+  pack_tile<LAYOUT, M, true>(W, n, K, N, k_tiles, ws, codes, meta, blockIdx.x);
 }
 
-// ---------------------------------------------------------------------------------------------
-// Grouped pack: the bitlinear_pack calls of several masters in three launches, each tensor's
-// blocks running exactly the single call's arithmetic (so gamma, codes and meta are the same
-// bits).  The partial-sum launch walks the tensors in table order and the pack launch in reverse,
-// so the tensors read last by the first launch -- still in the last-level cache -- are packed
-// first.
-// ---------------------------------------------------------------------------------------------
-__global__ __launch_bounds__(kGammaThreads) void gamma_partial_group_kernel(
-    const uint8_t* __restrict__ table) {
-  const PackGroupHeader* hd = (const PackGroupHeader*)table;
-  if (hd->magic != kPackGroupMagic) return;
-  const int b = blockIdx.x;
-  if (b >= hd->count * kGammaBlocks) return;
-  const PackGroupItem it = ((const PackGroupItem*)(table + sizeof(PackGroupHeader)))[b / kGammaBlocks];
-  clear_exact_state((PackWs*)it.ws, b % kGammaBlocks);
-  gamma_partial_block((const float4*)it.W, (int64_t)it.n * it.K / 4, ((PackWs*)it.ws)->partial,
-                      b % kGammaBlocks);
+// Sets the listed codes with |w| >= tau: entries start, start + stride, ... of the master's
+// tiles * kTileEntries, four loads in flight per thread.
+__device__ __forceinline__ void patch_codes(PackWs* __restrict__ ws, int64_t tiles,
+                                            uint32_t* __restrict__ codes, float tau,
+                                            int64_t start, int64_t stride) {
+  constexpr int U = 4;
+  const uint2* ent = ws_entries(ws);
+  const int64_t total = tiles * kTileEntries;
+  for (int64_t b = start; b < total; b += U * stride) {
+    uint2 e[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      e[u] = b + u * stride < total ? ent[b + u * stride] : make_uint2(kNoEntryPos, kNoEntryAbs);
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (__uint_as_float(e[u].y) >= tau)
+        atomicOr(&codes[e[u].x & 0x7FFFFFFu], ((e[u].x >> 31) ? 2u : 1u) << (2 * ((e[u].x >> 27) & 15u)));
+  }
 }
 
-// kExactBlocks blocks per master, in table order (each exits at once unless its master is flagged).
-__global__ __launch_bounds__(kExactThreads) void gamma_exact_group_kernel(
-    const uint8_t* __restrict__ table) {
-  const PackGroupHeader* hd = (const PackGroupHeader*)table;
-  if (hd->magic != kPackGroupMagic) return;
-  const int b = blockIdx.x;
-  if (b >= hd->count * kExactBlocks) return;
-  const PackGroupItem it = ((const PackGroupItem*)(table + sizeof(PackGroupHeader)))[b / kExactBlocks];
-  gamma_exact_block(it.W, (int64_t)it.n * it.K, (PackWs*)it.ws, it.gamma, b % kExactBlocks,
-                    kExactBlocks);
+// Launch 5 for one master (block blk of nblk): the listed codes are set when tau lies inside the
+// band and no region overflowed; otherwise every tile is packed again (block blk takes tiles blk,
+// blk + nblk, ...).  Uniform across the launch.
+template <int LAYOUT, int M>
+__device__ __forceinline__ void pack_fix_block(const float* __restrict__ W, int n, int K, int N,
+                                               int k_tiles, PackWs* __restrict__ ws,
+                                               uint32_t* __restrict__ codes,
+                                               uint32_t* __restrict__ meta, int blk, int nblk) {
+  const float tau = ws->tau;
+  const bool patch = ws->band_ok && !ws->overflow && ws->tau_lo <= tau && tau <= ws->tau_hi;
+  if (blk == 0 && threadIdx.x == 0) ws->fix_mode = patch ? 0u : 1u;
+  const int64_t tiles = (int64_t)((n + kPanel - 1) / kPanel) * k_tiles;
+  if (patch) {
+    patch_codes(ws, tiles, codes, tau, (int64_t)blk * 256 + threadIdx.x, (int64_t)nblk * 256);
+    return;
+  }
+  for (int64_t t = blk; t < tiles; t += nblk) {
+    __syncthreads();   // the previous tile's LDS reads are done
+    pack_tile<LAYOUT, M, false>(W, n, K, N, k_tiles, ws, codes, meta, (int)t);
+  }
 }
 
 template <int LAYOUT, int M>
-__global__ __launch_bounds__(256) void pack_group_kernel(const uint8_t* __restrict__ table) {
+__global__ __launch_bounds__(256) void pack_fix_kernel(const float* __restrict__ W, int n, int K,
+                                                       int N, int k_tiles, PackWs* __restrict__ ws,
+                                                       uint32_t* __restrict__ codes,
+                                                       uint32_t* __restrict__ meta) {
+  pack_fix_block<LAYOUT, M>(W, n, K, N, k_tiles, ws, codes, meta, blockIdx.x, gridDim.x);
+}
+
+// ---------------------------------------------------------------------------------------------
+// Grouped pack: the bitlinear_pack calls of several masters in five launches, each tensor's
+// blocks running exactly the single call's arithmetic (so gamma, codes and meta are the same
+// bits).  Every master's workspace slice holds a band region per tile of that master.
+// ---------------------------------------------------------------------------------------------
+__device__ __forceinline__ PackGroupItem group_item(const uint8_t* __restrict__ table, int i) {
+  return ((const PackGroupItem*)(table + sizeof(PackGroupHeader)))[i];
+}
+
+__device__ __forceinline__ int64_t item_tiles(const PackGroupItem& it) {
+  return (int64_t)((it.n + kPanel - 1) / kPanel) * it.k_tiles;
+}
+
+// kSampleBlocks blocks per master, in table order.
+__global__ __launch_bounds__(kGammaThreads) void gamma_sample_group_kernel(
+    const uint8_t* __restrict__ table) {
+  const PackGroupHeader* hd = (const PackGroupHeader*)table;
+  if (hd->magic != kPackGroupMagic) return;
+  const int b = blockIdx.x;
+  if (b >= hd->count * kSampleBlocks) return;
+  const PackGroupItem it = group_item(table, b / kSampleBlocks);
+  clear_pack_state((PackWs*)it.ws, b % kSampleBlocks);
+  gamma_sample_block((const float4*)it.W, (int64_t)it.n * it.K, (PackWs*)it.ws, b % kSampleBlocks);
+}
+
+// One block per master (every slice holds a region for each of its master's tiles).
+__global__ __launch_bounds__(kGammaThreads) void band_group_kernel(const uint8_t* __restrict__ table) {
+  const PackGroupHeader* hd = (const PackGroupHeader*)table;
+  if (hd->magic != kPackGroupMagic || (int)blockIdx.x >= hd->count) return;
+  const PackGroupItem it = group_item(table, blockIdx.x);
+  band_block((PackWs*)it.ws, pack_code_dwords(it.n, it.K, hd->layout, hd->M), true);
+}
+
+template <int LAYOUT, int M>
+__global__ __launch_bounds__(256, 6) void pack_group_kernel(const uint8_t* __restrict__ table) {
   const PackGroupHeader* hd = (const PackGroupHeader*)table;
   if (hd->magic != kPackGroupMagic || hd->layout != LAYOUT || hd->M != M) return;
   const int b = blockIdx.x;
@@ -526,25 +732,59 @@ __global__ __launch_bounds__(256) void pack_group_kernel(const uint8_t* __restri
     if (items[hd->count - 1 - mid].block0 <= b) lo = mid; else hi = mid - 1;
   }
   const PackGroupItem it = items[hd->count - 1 - lo];
-  pack_tile<LAYOUT, M>(it.W, it.n, it.K, hd->N, it.k_tiles, (const PackWs*)it.ws, it.codes,
-                       it.meta, b - it.block0);
+  pack_tile<LAYOUT, M, true>(it.W, it.n, it.K, hd->N, it.k_tiles, (PackWs*)it.ws, it.codes,
+                             it.meta, b - it.block0);
+}
+
+// kExactBlocks blocks per master, in table order (each exits at once unless its master is flagged).
+__global__ __launch_bounds__(kExactThreads) void gamma_exact_group_kernel(
+    const uint8_t* __restrict__ table) {
+  const PackGroupHeader* hd = (const PackGroupHeader*)table;
+  if (hd->magic != kPackGroupMagic) return;
+  const int b = blockIdx.x;
+  if (b >= hd->count * kExactBlocks) return;
+  const PackGroupItem it = group_item(table, b / kExactBlocks);
+  gamma_exact_block(it.W, (int64_t)it.n * it.K, item_tiles(it), (PackWs*)it.ws, it.gamma,
+                    b % kExactBlocks, kExactBlocks);
+}
+
+// kFixBlocks blocks per master, in table order.
+template <int LAYOUT, int M>
+__global__ __launch_bounds__(256) void pack_fix_group_kernel(const uint8_t* __restrict__ table) {
+  const PackGroupHeader* hd = (const PackGroupHeader*)table;
+  if (hd->magic != kPackGroupMagic || hd->layout != LAYOUT || hd->M != M) return;
+  const int b = blockIdx.x;
+  if (b >= hd->count * kFixBlocks) return;
+  const PackGroupItem it = group_item(table, b / kFixBlocks);
+  pack_fix_block<LAYOUT, M>(it.W, it.n, it.K, hd->N, it.k_tiles, (PackWs*)it.ws, it.codes,
+                            it.meta, b % kFixBlocks, kFixBlocks);
 }
 
 hipError_t launch_pack(const float* W, int64_t n, int64_t K, int N, int M, int layout,
-                       uint32_t* codes, uint32_t* meta, float* gamma, void* ws_raw, hipStream_t s) {
+                       uint32_t* codes, uint32_t* meta, float* gamma, void* ws_raw,
+                       int64_t tiles_cap, hipStream_t s) {
   PackWs* ws = (PackWs*)ws_raw;
   const int64_t count = n * K;
-  gamma_partial_kernel<<<kGammaBlocks, kGammaThreads, 0, s>>>((const float4*)W, count / 4, ws);
-  gamma_exact_kernel<<<kExactBlocks, kExactThreads, 0, s>>>(W, count, ws, gamma);
   const int panels = (int)((n + kPanel - 1) / kPanel);
   const int k_tiles = (int)((K + pack_cols(layout, M) - 1) / pack_cols(layout, M));
-  const dim3 grid((unsigned)(panels * k_tiles));
-  const bool ok = dispatch_m(M, [&](auto m) {
+  const int64_t tiles = (int64_t)panels * k_tiles;
+  gamma_sample_kernel<<<kSampleBlocks, kGammaThreads, 0, s>>>((const float4*)W, count, ws);
+  band_kernel<<<1, kGammaThreads, 0, s>>>(ws, pack_code_dwords(n, K, layout, M), tiles <= tiles_cap);
+  bool ok = dispatch_m(M, [&](auto m) {
     constexpr int MM = decltype(m)::value;
     if (layout == kLayoutSparse)
-      pack_kernel<kLayoutSparse, MM><<<grid, 256, 0, s>>>(W, (int)n, (int)K, N, k_tiles, ws, codes, meta);
+      pack_spec_kernel<kLayoutSparse, MM><<<(unsigned)tiles, 256, 0, s>>>(W, (int)n, (int)K, N, k_tiles, ws, codes, meta);
     else
-      pack_kernel<kLayoutDense2, MM><<<grid, 256, 0, s>>>(W, (int)n, (int)K, N, k_tiles, ws, codes, nullptr);
+      pack_spec_kernel<kLayoutDense2, MM><<<(unsigned)tiles, 256, 0, s>>>(W, (int)n, (int)K, N, k_tiles, ws, codes, nullptr);
+  });
+  if (!ok) return hipErrorInvalidValue;
+  gamma_exact_kernel<<<kExactBlocks, kExactThreads, 0, s>>>(W, count, tiles, ws, gamma);
+  ok = dispatch_m(M, [&](auto m) {
+    constexpr int MM = decltype(m)::value;
+    if (layout == kLayoutSparse)
+      pack_fix_kernel<kLayoutSparse, MM><<<kFixBlocks, 256, 0, s>>>(W, (int)n, (int)K, N, k_tiles, ws, codes, meta);
+    else
+      pack_fix_kernel<kLayoutDense2, MM><<<kFixBlocks, 256, 0, s>>>(W, (int)n, (int)K, N, k_tiles, ws, codes, nullptr);
   });
   if (!ok) return hipErrorInvalidValue;
   return hipGetLastError();
@@ -556,8 +796,8 @@ hipError_t launch_pack(const float* W, int64_t n, int64_t K, int N, int M, int l
 // device array instead of a caller buffer.  The array holds one pack workspace (kPackWsBytes,
 // the same for every shape); each GPU the library runs on holds its own copy until the process
 // ends, and every call on that GPU shares it, so calls that overlap on one GPU race.  The
-// partial-sum launch clears the state the later launches accumulate into (exact words, block
-// counter), so a call never depends on what the previous one left there.
+// sampling launch clears the state the later launches accumulate into (sum slots, list counters,
+// overflow flag, arrival counters), so a call never depends on what the previous one left there.
 // ---------------------------------------------------------------------------------------------
 static __device__ __align__(256) uint8_t scratch[kPackWsBytes];
 
@@ -593,21 +833,30 @@ hipError_t launch_pack_noalloc(const float* W, int64_t n, int64_t K, int N, int 
   void* ws = nullptr;
   const hipError_t e = scratch_on_current_device(&ws);
   if (e != hipSuccess) return e;
-  return launch_pack(W, n, K, N, M, layout, codes, meta, gamma, ws, s);
+  // band regions for at most kNoallocTiles tiles: a larger master is packed in two passes
+  const int64_t tiles = (n + kPanel - 1) / kPanel * ((K + pack_cols(layout, M) - 1) / pack_cols(layout, M));
+  return launch_pack(W, n, K, N, M, layout, codes, meta, gamma, ws,
+                     tiles <= kNoallocTiles ? tiles : 0, s);
 }
 
 hipError_t launch_pack_group(const void* table, int64_t count, int64_t pack_blocks, int layout,
                              int M, hipStream_t s) {
   const uint8_t* t = (const uint8_t*)table;
-  gamma_partial_group_kernel<<<(unsigned)(count * kGammaBlocks), kGammaThreads, 0, s>>>(t);
-  gamma_exact_group_kernel<<<(unsigned)(count * kExactBlocks), kExactThreads, 0, s>>>(t);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  gamma_sample_group_kernel<<<(unsigned)(count * kSampleBlocks), kGammaThreads, 0, s>>>(t);
+  band_group_kernel<<<(unsigned)count, kGammaThreads, 0, s>>>(t);
   const unsigned g = (unsigned)pack_blocks;
-  const bool ok = dispatch_m(M, [&](auto m) {
+  bool ok = dispatch_m(M, [&](auto m) {
     constexpr int MM = decltype(m)::value;
     if (layout == kLayoutSparse) pack_group_kernel<kLayoutSparse, MM><<<g, 256, 0, s>>>(t);
     else pack_group_kernel<kLayoutDense2, MM><<<g, 256, 0, s>>>(t);
+  });
+  if (!ok) return hipErrorInvalidValue;
+  gamma_exact_group_kernel<<<(unsigned)(count * kExactBlocks), kExactThreads, 0, s>>>(t);
+  const unsigned gf = (unsigned)(count * kFixBlocks);
+  ok = dispatch_m(M, [&](auto m) {
+    constexpr int MM = decltype(m)::value;
+    if (layout == kLayoutSparse) pack_fix_group_kernel<kLayoutSparse, MM><<<gf, 256, 0, s>>>(t);
+    else pack_fix_group_kernel<kLayoutDense2, MM><<<gf, 256, 0, s>>>(t);
   });
   if (!ok) return hipErrorInvalidValue;
   return hipGetLastError();

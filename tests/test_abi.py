@@ -88,7 +88,7 @@ FAKE = 0x7F0000000000   # 16-byte aligned, never dereferenced (validation fails 
 
 def test_pack_rejects_before_launch(L):
     P = FAKE
-    ok = dict(W=P, n=64, K=256, N=2, M=4, layout=0, codes=P, meta=P, gamma=P, ws=P, ws_bytes=1 << 20)
+    ok = dict(W=P, n=64, K=256, N=2, M=4, layout=0, codes=P, meta=P, gamma=P, ws=P, ws_bytes=1 << 24)
 
     def call(**kw):
         a = dict(ok, **kw)
@@ -445,8 +445,10 @@ def test_pack_group_plan_and_rejects_before_launch(L):
     assert st == 0
     assert plan.count == 2 and plan.pack_blocks == 10 * 3 + 2 * 1
     assert plan.table_bytes == 64 + 2 * 64
-    ws1 = L.bitlinear_packed_bytes(300, 640, 2, 4, 0)[4]
-    assert plan.ws_bytes == 2 * ((ws1 + 255) // 256 * 256)
+    up = lambda b: (b + 255) // 256 * 256
+    wa = L.bitlinear_packed_bytes(300, 640, 2, 4, 0)[4]
+    wb = L.bitlinear_packed_bytes(64, 256, 2, 4, 0)[4]
+    assert plan.ws_bytes == up(wa) + up(wb)     # each master's bitlinear_pack workspace
     assert _pplan(L, [_pdesc(L, 0, K=100)])[0] == -22
     assert _pplan(L, [a], N=3)[0] == -95
     assert _pplan(L, [_pdesc(L, 0, W=FAKE + 4)])[0] == -22
