@@ -7,8 +7,8 @@
 // as N-1 overlapping 2:4 windows (SlideSparse abstract, Sliding Window Decomposition).
 //
 // Five launches, all on the caller's stream, one HBM pass over W in the common case:
-//   1. gamma_sample_kernel  a fixed share of W (1 segment of 256 bytes in S, S = 1..32 by size)
-//                           spread over the matrix: per-block sums of |w|; block 0 also clears the
+//   1. gamma_sample_kernel  a fixed share of W (1 chunk of 4 KB in S, S = 1..32 by size) spread
+//                           over the matrix: per-block sums of |w|; block 0 also clears the
 //                           accumulators of launches 3-4
 //   2. band_kernel          one block: the sample's estimate of mean |W| and its standard error
 //                           give a band [tau_lo, tau_hi] that holds the exact threshold tau unless
@@ -51,28 +51,27 @@ __host__ __device__ __forceinline__ int64_t sample_stride(int64_t count) {
   return S;
 }
 
-// The sampled segments: 64 floats each, segment j = S j + (7 j mod S) for j < count / (64 S).
-// Each quarter-wave reads one segment per step (lane i: float4 i of it) and a thread keeps the
-// sum s of its |w| and their number c; the block stores the sums of s, s^2, s c, c and c^2 over
-// its threads.  Threads are the sampling units: each one's segments lie far apart in the matrix.
+// The sampled chunks: 1024 floats (4 KB) each, chunk j = S j + (7 j mod S) for j < count / (1024
+// S), dealt to the blocks round-robin.  Thread t reads float4 t of each of its block's chunks and
+// keeps the sum s of their |w| and their number c; the block stores the sums of s, s^2, s c, c
+// and c^2 over its threads.  Threads are the sampling units: each one's elements lie in chunks
+// far apart in the matrix.
 __device__ __forceinline__ void gamma_sample_block(const float4* __restrict__ W4, int64_t count,
                                                    PackWs* __restrict__ ws, int blk) {
   const int64_t S = sample_stride(count);
-  const int64_t ns = count / (64 * S);
-  const int64_t Q = (int64_t)kSampleBlocks * kGammaThreads / 16;   // quarter-waves in the launch
-  const int64_t q0 = ((int64_t)blk * kGammaThreads + threadIdx.x) >> 4;
-  const int l16 = threadIdx.x & 15;
+  const int64_t ns = count / (1024 * S);
+  constexpr int U = 8;   // chunks in flight per block (a 2^19-weight sample is ~4-8 per block)
   double s = 0.0, c = 0.0;
-  for (int64_t j = q0; j < ns; j += 4 * Q) {
-    float4 v[4];
+  for (int64_t j = blk; j < ns; j += U * kSampleBlocks) {
+    float4 v[U];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int64_t jj = min(j + u * Q, ns - 1);
-      v[u] = W4[(S * jj + ((7 * jj) & (S - 1))) * 16 + l16];
+    for (int u = 0; u < U; ++u) {
+      const int64_t jj = min(j + u * kSampleBlocks, ns - 1);
+      v[u] = W4[(S * jj + ((7 * jj) & (S - 1))) * 256 + threadIdx.x];
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
-      if (j + u * Q < ns) {
+    for (int u = 0; u < U; ++u)
+      if (j + u * kSampleBlocks < ns) {
         s += (fabs((double)v[u].x) + fabs((double)v[u].y)) + (fabs((double)v[u].z) + fabs((double)v[u].w));
         c += 4.0;
       }
@@ -189,66 +188,45 @@ __device__ float ternary_threshold(float gamma) {
 constexpr int kExactThreads = 1024;  // 16 waves: four per SIMD for the rare exact pass
 constexpr int kExactLoads = 2;       // float4 loads per thread per iteration of the exact pass
 
-// Certified fp32 rounding of mean |W| from the fp64 slot sums, computed by a whole block in one
-// fixed order (every block gets the same bits).  Returns 1 and *g when the rigorous error bound of
-// the fp64 sum decides the rounding (or the sum is 0), else 0.
-__device__ __forceinline__ int block_certify(const PackWs* __restrict__ ws, int64_t count,
-                                             int64_t tiles, float* __restrict__ g) {
-  static_assert(kGammaBlocks % kExactThreads == 0, "partials split evenly");
-  __shared__ double red_sh[kExactThreads / 64];
-  __shared__ float g_sh;
-  __shared__ int ok_sh;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+// Certified fp32 rounding of mean |W| from the fp64 slot sums, computed by one wave in one fixed
+// order (every wave that certifies a master gets the same bits).  Returns 1 and *g when the
+// rigorous error bound of the fp64 sum decides the rounding (or the sum is 0), else 0; the result
+// is uniform across the wave.
+__device__ __forceinline__ int wave_certify(const PackWs* __restrict__ ws, int64_t count,
+                                            int64_t tiles, float* __restrict__ g) {
+  static_assert(kGammaBlocks % 64 == 0, "slots split evenly over a wave");
+  const int lane = threadIdx.x & 63;
   double v = 0.0;
 #pragma unroll
-  for (int i = 0; i < kGammaBlocks / kExactThreads; ++i) v += ws->partial[threadIdx.x + i * kExactThreads];
+  for (int i = 0; i < kGammaBlocks / 64; ++i) v += ws->partial[lane + 64 * i];
   v = wave_sum_f64(v);
-  if (lane == 0) red_sh[wave] = v;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    double S = 0.0;
-    for (int w = 0; w < kExactThreads / 64; ++w) S += red_sh[w];
-    // longest chain of fp64 additions any |w| goes through: in its pack tile the thread's 32
-    // terms and the wave butterfly (6); its slot's chain (one hardware atomic addition per wave of
-    // each tile that shares the slot, four per tile, counted twice in case the atomic unit rounds
-    // faithfully rather than to nearest); here the per-thread sum (kGammaBlocks / kExactThreads =
-    // 1), the butterfly (6) and the block sum (kExactThreads / 64 = 16).  128 covers every fixed
-    // term.
-    const double depth = 128.0 + 8.0 * (double)((tiles + kGammaBlocks - 1) / kGammaBlocks);
-    const double u = 0x1p-53;
-    const double err = 2.0 * depth * u * S;  // >= ((1+u)^depth - 1) * S for nonnegative terms
-    const double cnt = (double)count;
-    const double lo = (S - err) / cnt * (1.0 - 4.0 * u);
-    const double hi = (S + err) / cnt * (1.0 + 4.0 * u);
-    const float glo = (float)lo, ghi = (float)hi;
-    if (S == 0.0) { ok_sh = 1; g_sh = 0.f; }
-    else if (glo == ghi) { ok_sh = 1; g_sh = glo; }
-    else ok_sh = 0;
-  }
-  __syncthreads();
-  *g = g_sh;
-  return ok_sh;
+  const double S = __shfl(v, 0, 64);
+  // longest chain of fp64 additions any |w| goes through: in its pack tile the thread's 32
+  // terms and the wave butterfly (6); its slot's chain (one hardware atomic addition per wave of
+  // each tile that shares the slot, four per tile, counted twice in case the atomic unit rounds
+  // faithfully rather than to nearest); here the lane's 16 slots and the butterfly (6).  128
+  // covers every fixed term.
+  const double depth = 128.0 + 8.0 * (double)((tiles + kGammaBlocks - 1) / kGammaBlocks);
+  const double u = 0x1p-53;
+  const double err = 2.0 * depth * u * S;  // >= ((1+u)^depth - 1) * S for nonnegative terms
+  const double cnt = (double)count;
+  const double lo = (S - err) / cnt * (1.0 - 4.0 * u);
+  const double hi = (S + err) / cnt * (1.0 + 4.0 * u);
+  const float glo = (float)lo, ghi = (float)hi;
+  if (S == 0.0) { *g = 0.f; return 1; }
+  if (glo == ghi) { *g = glo; return 1; }
+  return 0;
 }
 
-// gamma for launch 4: certified from the slot sums, or else the exact sum of |W| over this
-// block's share (float4 i4 = blk * NT + tid, strided by the master's blocks), the last block to
-// finish rounding the exact mean.
+// The exact pass of launch 4, for a master whose gamma the bound did not decide: the exact sum of
+// |W| over this block's share (float4 i4 = blk * NT + tid, strided by the launch's blocks), the
+// last block to finish rounding the exact mean.
 // Each element's m << (max(e,1) - 1) is split into 32-bit pieces p0 (word w) and p1 (word w + 1);
 // a lane keeps one 64-bit sum per word, so no carry is taken until the end (every word sum stays
 // below count * 2^32 < 2^64).  Words no lane of the wave touches in an iteration are skipped.
-__device__ __forceinline__ void gamma_exact_block(const float* __restrict__ W, int64_t count,
-                                                  int64_t tiles, PackWs* __restrict__ ws,
-                                                  float* __restrict__ gamma_out, int blk, int nblk) {
-  float g = 0.f;
-  if (block_certify(ws, count, tiles, &g)) {   // uniform across the block and the launch
-    if (blk == 0 && threadIdx.x == 0) {
-      ws->gamma = g;
-      ws->tau = ternary_threshold(g);
-      ws->exact_used = 0u;
-      gamma_out[0] = g;
-    }
-    return;
-  }
+__device__ __forceinline__ void gamma_exact_pass(const float* __restrict__ W, int64_t count,
+                                                 PackWs* __restrict__ ws,
+                                                 float* __restrict__ gamma_out, int blk, int nblk) {
   unsigned long long acc[kExactWords];
 #pragma unroll
   for (int i = 0; i < kExactWords; ++i) acc[i] = 0ull;
@@ -362,11 +340,48 @@ __device__ __forceinline__ void gamma_exact_block(const float* __restrict__ W, i
   }
 }
 
+// Launch 4 over `nm` masters (kExactBlocks blocks): wave w of every block certifies masters w,
+// w + 16, ... (the same bits in every block, so the decisions are uniform), block 0 stores each
+// certified master's gamma and tau, and then all blocks run the exact pass of each master the
+// bound did not decide, in order.  item(m) gives master m's (W, count, tiles, ws, gamma).
+template <typename Item>
+__device__ __forceinline__ void gamma_masters(int nm, Item item) {
+  constexpr int NW = kExactThreads / 64;
+  __shared__ int need_sh[NW];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  for (int m0 = 0; m0 < nm; m0 += NW) {
+    if (m0 + wave < nm) {
+      const float* W; int64_t count, tiles; PackWs* ws; float* gout;
+      item(m0 + wave, &W, &count, &tiles, &ws, &gout);
+      float g = 0.f;
+      const int ok = wave_certify(ws, count, tiles, &g);
+      if (lane == 0) need_sh[wave] = !ok;
+      if (ok && blockIdx.x == 0 && lane == 0) {
+        ws->gamma = g;
+        ws->tau = ternary_threshold(g);
+        ws->exact_used = 0u;
+        gout[0] = g;
+      }
+    }
+    __syncthreads();
+    for (int w = 0; w < NW && m0 + w < nm; ++w) {
+      if (!need_sh[w]) continue;   // uniform
+      const float* W; int64_t count, tiles; PackWs* ws; float* gout;
+      item(m0 + w, &W, &count, &tiles, &ws, &gout);
+      gamma_exact_pass(W, count, ws, gout, blockIdx.x, gridDim.x);
+      __syncthreads();
+    }
+    __syncthreads();
+  }
+}
+
 __global__ __launch_bounds__(kExactThreads) void gamma_exact_kernel(const float* __restrict__ W,
                                                                     int64_t count, int64_t tiles,
                                                                     PackWs* __restrict__ ws,
                                                                     float* __restrict__ gamma_out) {
-  gamma_exact_block(W, count, tiles, ws, gamma_out, blockIdx.x, gridDim.x);
+  gamma_masters(1, [&](int, const float** w, int64_t* c, int64_t* t, PackWs** p, float** g) {
+    *w = W; *c = count; *t = tiles; *p = ws; *g = gamma_out;
+  });
 }
 
 constexpr int kPackWidth = 256;  // dense columns of a pack tile at most (one float4 per lane)
@@ -487,19 +502,24 @@ __device__ __forceinline__ void pack_tile(const float* __restrict__ W, int n, in
   const size_t base = ((size_t)P * nfrag + (size_t)kb * (UPR / 2)) * 64;
 
   // all eight 16-byte tile loads before anything else (addresses clamped into the matrix;
-  // out-of-range rows and columns are zeroed after the load)
+  // out-of-range rows and columns are zeroed after the load); non-temporal: the pass reads each
+  // weight once
   const int c4 = threadIdx.x & 63, wv = threadIdx.x >> 6;
   float4 v[8];
   {
+    typedef float f4v __attribute__((ext_vector_type(4)));
     const int col = k0 + min(4 * c4, kw - 4);
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      v[i] = *(const float4*)(W + (size_t)min(r0 + i * 4 + wv, n - 1) * K + col);
+    for (int i = 0; i < 8; ++i) {
+      const f4v t = __builtin_nontemporal_load(
+          (const f4v*)(W + (size_t)min(r0 + i * 4 + wv, n - 1) * K + col));
+      v[i] = make_float4(t.x, t.y, t.z, t.w);
+    }
   }
   // codes: |w| >= hi is +-1, |w| < lo is 0, between (SPEC only) listed
   const float lo = SPEC ? ws->tau_lo : ws->tau, hi = SPEC ? ws->tau_hi : ws->tau;
   const uint32_t band_ok = SPEC ? ws->band_ok : 0u;
-  if (SPEC && threadIdx.x == 0) nl_sh = 0;   // read after the barrier below
+  if (SPEC && threadIdx.x == 0) nl_sh = 0;
   {
     const bool col_ok = 4 * c4 < kw;
     double ts = 0.0;
@@ -519,7 +539,8 @@ __device__ __forceinline__ void pack_tile(const float* __restrict__ W, int n, in
       if (c4 == 0) unsafeAtomicAdd(&ws->partial[blk % kGammaBlocks], ts);
     }
   }
-  if constexpr (!REG) __syncthreads();
+  // the LDS tile is complete and the entry counter is clear before any group reads or appends
+  if constexpr (!REG || SPEC) __syncthreads();
 
   const int nkeep = SP ? NKEEP : N;
   // One M-group at (row, g) with values w: mask, codes, slot bytes.
@@ -618,11 +639,12 @@ __device__ __forceinline__ void pack_tile(const float* __restrict__ W, int n, in
     // the tile's region: its band entries, then kNoEntry (no counter shared between tiles)
     if (!band_ok) return;
     const int nl = nl_sh;   // final: every append happened before the barrier above
-    if (nl > kTileEntries && threadIdx.x == 0) ws->overflow = 1u;
-    if (threadIdx.x < kTileEntries)
-      ws_entries(ws)[(size_t)blk * kTileEntries + threadIdx.x] =
-          threadIdx.x < nl && nl <= kTileEntries ? lst[threadIdx.x]
-                                                 : make_uint2(kNoEntryPos, kNoEntryAbs);
+    int e = threadIdx.x;
+    asm volatile("" : "+v"(e));   // derive the entry's addresses here, not at the top
+    if (nl > kTileEntries && e == 0) ws->overflow = 1u;
+    if (e < kTileEntries)
+      ws_entries(ws)[(size_t)blk * kTileEntries + e] =
+          e < nl && nl <= kTileEntries ? lst[e] : make_uint2(kNoEntryPos, kNoEntryAbs);
   }
 }
 
@@ -736,16 +758,15 @@ __global__ __launch_bounds__(256, 6) void pack_group_kernel(const uint8_t* __res
                              it.meta, b - it.block0);
 }
 
-// kExactBlocks blocks per master, in table order (each exits at once unless its master is flagged).
+// kExactBlocks blocks for the whole group.
 __global__ __launch_bounds__(kExactThreads) void gamma_exact_group_kernel(
     const uint8_t* __restrict__ table) {
   const PackGroupHeader* hd = (const PackGroupHeader*)table;
   if (hd->magic != kPackGroupMagic) return;
-  const int b = blockIdx.x;
-  if (b >= hd->count * kExactBlocks) return;
-  const PackGroupItem it = group_item(table, b / kExactBlocks);
-  gamma_exact_block(it.W, (int64_t)it.n * it.K, item_tiles(it), (PackWs*)it.ws, it.gamma,
-                    b % kExactBlocks, kExactBlocks);
+  gamma_masters(hd->count, [&](int m, const float** w, int64_t* c, int64_t* t, PackWs** p, float** g) {
+    const PackGroupItem it = group_item(table, m);
+    *w = it.W; *c = (int64_t)it.n * it.K; *t = item_tiles(it); *p = (PackWs*)it.ws; *g = it.gamma;
+  });
 }
 
 // kFixBlocks blocks per master, in table order.
@@ -851,7 +872,7 @@ hipError_t launch_pack_group(const void* table, int64_t count, int64_t pack_bloc
     else pack_group_kernel<kLayoutDense2, MM><<<g, 256, 0, s>>>(t);
   });
   if (!ok) return hipErrorInvalidValue;
-  gamma_exact_group_kernel<<<(unsigned)(count * kExactBlocks), kExactThreads, 0, s>>>(t);
+  gamma_exact_group_kernel<<<kExactBlocks, kExactThreads, 0, s>>>(t);
   const unsigned gf = (unsigned)(count * kFixBlocks);
   ok = dispatch_m(M, [&](auto m) {
     constexpr int MM = decltype(m)::value;

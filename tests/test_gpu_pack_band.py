@@ -6,8 +6,8 @@ gamma is known either sets the listed codes (tau inside the band, list complete)
 tile again.  Whichever path runs, gamma, codes and meta must equal the oracle's bit for bit.  The
 workspace's diagnostic words say which path ran: ordinary masters must take the listed-codes path
 (otherwise the pack would read W twice), and the masters built here to defeat the band -- weights
-crowded at the threshold, a sample that misses the one large segment, a master smaller than one
-sampling segment -- must take the repack path and still be exact.
+crowded at the threshold, a sample that misses the one large piece, a master smaller than one
+sampling chunk -- must take the repack path and still be exact.
 """
 import numpy as np
 import pytest
@@ -83,7 +83,7 @@ def test_weights_crowded_at_the_threshold_overflow_and_repack():
 
 
 def test_sample_that_misses_the_mass_repacks():
-    # tiny weights everywhere but one 256-byte segment of huge ones: the sample either misses it
+    # tiny weights everywhere but one 256-byte piece of huge ones: the sample either misses it
     # (estimate far below gamma) or holds it (estimate far above, standard error huge)
     g = rng(92)
     n, K = 1024, 1024
@@ -93,19 +93,21 @@ def test_sample_that_misses_the_mass_repacks():
     assert _word(ws, FIX_MODE) == 1
 
 
-def test_master_without_a_whole_sampled_segment_repacks():
-    # 32 weights: not one 64-weight sampling segment, so no band (a small master is otherwise
-    # sampled whole)
-    W = master_weights(rng(93), 1, 32)
-    ws = _pack_checked(W, 2, 4, O.LAYOUT_DENSE2)
+@pytest.mark.parametrize("n,K,layout", [(1, 32, O.LAYOUT_DENSE2), (1, 512, O.LAYOUT_SPARSE),
+                                        (7, 128, O.LAYOUT_SPARSE)])
+def test_master_without_a_whole_sampling_chunk_repacks(n, K, layout):
+    # fewer than 1024 weights: not one 4 KB sampling chunk, so no band (a small master is
+    # otherwise sampled whole)
+    W = master_weights(rng(93 + K), n, K)
+    ws = _pack_checked(W, 2, 4, layout)
     assert _word(ws, BAND_OK) == 0
     assert _word(ws, FIX_MODE) == 1
 
 
-@pytest.mark.parametrize("n,K", [(1, 512), (3, 64), (7, 128), (8, 512)])
+@pytest.mark.parametrize("n,K", [(3, 384), (8, 512), (33, 640)])
 def test_small_masters_sampled_whole(n, K):
     # the band follows the sample's standard error: usable from a few thousand weights on; below
-    # that (3 x 64) it may be too wide and the fix-up repacks -- exact either way
+    # that (3 x 384) it may be too wide and the fix-up repacks -- exact either way
     W = master_weights(rng(93 + n), n, K)
     ws = _pack_checked(W)
     if n * K >= 4096:
