@@ -969,7 +969,9 @@ def cpu_baseline(budget_s):
 
     import oracle as O
     from synth import act_normal, rng, to_bf16
-    _cpu_worker_init()
+    t_pack = time.perf_counter()
+    _cpu_worker_init()                                       # the oracle pack of both masters
+    t_pack = time.perf_counter() - t_pack
     pu, pd = _CPU_STATE["p"]
     g = rng(0)
     from synth import master_weights
@@ -977,13 +979,21 @@ def cpu_baseline(budget_s):
     xu, _ = to_bf16(act_normal(g, max(DECODE_T), UP[1]))
     xd, _ = to_bf16(act_normal(g, max(DECODE_T), DOWN[1]))
     packed = 2 * UP[0] * UP[1] // 4
-    # one thread
+    # one thread (the quantization and the GEMV + rescale also timed apart: the stages)
     done_bytes, n_mats, t0 = 0, 0, time.perf_counter()
+    t_q = t_g = 0.0
+    q_bytes = 0
     while True:
         for T in DECODE_T:
             for p, x in ((pu, xu), (pd, xd)):
+                ta = time.perf_counter()
                 q, s = O.act_quant(x[:T])
+                tb = time.perf_counter()
                 O.rescale(O.acc_dense(p["W_eff"], q), p["gamma"], s)
+                tc = time.perf_counter()
+                t_q += tb - ta
+                t_g += tc - tb
+                q_bytes += 3 * q.size + 4 * T          # bf16 read, int8 written, token scales
                 done_bytes += packed
                 n_mats += 1
         if time.perf_counter() - t0 > budget_s / 2:
@@ -1010,8 +1020,17 @@ def cpu_baseline(budget_s):
                 break
         dtm = time.perf_counter() - t0
     multi = done_m / dtm / 1e9
+    pack_bytes = 4 * (UP[0] * UP[1] + DOWN[0] * DOWN[1]) + 2 * packed   # masters read, codes+meta
     return {"value": round(multi, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
             "single_thread_value": round(single, 4),
+            "stages_single_thread": {
+                "pack": {"GBps": round(pack_bytes / t_pack / 1e9, 4), "s": round(t_pack, 2),
+                         "work": "the up and down masters (35.4 M weights): mask, exact gamma, "
+                                 "ternarize, 2:4 pack; 4 B read + 0.25 B written per weight"},
+                "act_quant": {"GBps": round(q_bytes / t_q / 1e9, 4), "s": round(t_q, 4),
+                              "work": f"{n_mats} token blocks (T = 1, 4, 16), bf16 in, int8 out"},
+                "gemv": {"GBps": round(done_bytes / t_g / 1e9, 4), "s": round(t_g, 2),
+                         "work": f"{n_mats} int64 GEMVs + fp64 rescales, packed bytes per s"}},
             "host": _host_description(),
             "sample": f"decode up/down pair at T=1,4,16 (act_quant + int64 GEMV + fp64 rescale per "
                       f"matrix pass): {n_mats} passes on one thread in {dt1:.1f} s, then {n_m} "
