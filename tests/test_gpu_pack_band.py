@@ -140,3 +140,28 @@ def test_group_mixes_both_paths():
     assert _word(ws, slice_bytes + FIX_MODE) == 1
     ref = O.pack(np.asarray(B), 2, 4, O.LAYOUT_SPARSE)
     assert np.array_equal(host(grp.outputs[1][0]).view(np.uint32), ref["codes"])
+
+
+def test_noalloc_beyond_its_band_regions_matches_pack():
+    """bitlinear_pack_noalloc's static workspace holds band regions for 8192 tiles (67 M weights);
+    a larger master is packed there without the band (two passes over W) and must equal
+    bitlinear_pack, which has a region for every tile and takes the one-pass path."""
+    import ctypes
+    import torch
+    n, K = 8224, 8192                     # 257 panels x 32 tiles = 8224 tiles
+    g = torch.Generator(device="cuda")
+    g.manual_seed(95)
+    Wd = (torch.randn((n, K), generator=g, device="cuda") * 0.02).contiguous()
+    cb, mb, _, wsb = S.packed_bytes(n, K)
+    outs = [(torch.full((cb,), 0xAB, dtype=torch.uint8, device="cuda"),
+             torch.full((mb,), 0xAB, dtype=torch.uint8, device="cuda"),
+             torch.full((4,), float("nan"), device="cuda")) for _ in range(2)]
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    c, m, gm = outs[0]
+    assert S.lib().bitlinear_pack_noalloc(Wd.data_ptr(), n, K, 2, 4, O.LAYOUT_SPARSE,
+                                          c.data_ptr(), m.data_ptr(), gm.data_ptr(), stream) == 0
+    ws = torch.full((wsb,), 0x5A, dtype=torch.uint8, device="cuda")
+    c2, m2, g2 = S.pack(Wd, out=outs[1], ws=ws)
+    torch.cuda.synchronize()
+    assert _word(ws, FIX_MODE) == 0 and _word(ws, BAND_OK) == 1
+    assert torch.equal(gm[:1], g2[:1]) and torch.equal(c, c2) and torch.equal(m, m2)
