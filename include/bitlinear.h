@@ -115,7 +115,9 @@ int bitlinear_packed_bytes(int64_t n, int64_t K, int N, int M, int layout, size_
  * Writes codes[codes_bytes], meta[meta_bytes] (SPARSE; pass NULL for DENSE2) and gamma[1]
  * (device fp32), all in the packed layout above.  ws is scratch of at least ws_bytes (from
  * bitlinear_packed_bytes: a fixed part plus 512 bytes per packing tile of 32 rows x at most 256
- * columns, 1.6% of W's bytes for 2:4); its contents on entry do not matter.  W is only read.
+ * columns, 1.6% of W's bytes for 2:4); its contents on entry do not matter, and it must be
+ * ordinary device memory (hipMalloc or a framework allocator on it: the pass adds into it with
+ * device atomics that fine-grained or managed memory does not support).  W is only read.
  * Five launches, one pass over W in the common case: a share of W (all of a small master, at
  * least a 32nd of a large one) sampled to estimate gamma, and a band around the threshold that
  * estimate gives (one small block); the pass that sums |W| in fp64, writes
