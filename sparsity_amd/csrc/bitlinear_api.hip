@@ -16,6 +16,7 @@
 #include "quant_group.hpp"
 #include "device_common.hpp"
 #include "launch.hpp"
+#include "pack_ws.hpp"
 #include "pack_group.hpp"
 
 static_assert(BL_PACK_NOALLOC_WS_BYTES == bl::kPackWsBytes, "header states the static workspace size");

@@ -37,6 +37,7 @@
 
 #include "device_common.hpp"
 #include "launch.hpp"
+#include "pack_ws.hpp"
 #include "pack_group.hpp"
 
 namespace bl {
@@ -649,7 +650,7 @@ __device__ __forceinline__ void pack_tile(const float* __restrict__ W, int n, in
 }
 
 template <int LAYOUT, int M>
-__global__ __launch_bounds__(256, 6) void pack_spec_kernel(const float* __restrict__ W, int n, int K,
+__global__ __launch_bounds__(256, 7) void pack_spec_kernel(const float* __restrict__ W, int n, int K,
                                                         int N, int k_tiles,
                                                         PackWs* __restrict__ ws,
                                                         uint32_t* __restrict__ codes,
@@ -741,7 +742,7 @@ __global__ __launch_bounds__(kGammaThreads) void band_group_kernel(const uint8_t
 }
 
 template <int LAYOUT, int M>
-__global__ __launch_bounds__(256, 6) void pack_group_kernel(const uint8_t* __restrict__ table) {
+__global__ __launch_bounds__(256, 7) void pack_group_kernel(const uint8_t* __restrict__ table) {
   const PackGroupHeader* hd = (const PackGroupHeader*)table;
   if (hd->magic != kPackGroupMagic || hd->layout != LAYOUT || hd->M != M) return;
   const int b = blockIdx.x;

@@ -1,7 +1,8 @@
-// Device table of a grouped pack (bitlinear_pack_group_build writes it, gamma_partial_group_kernel
-// and pack_group_kernel read it): a header, then one item per master in descriptor order.
-// Partial-sum block b serves item b / kGammaBlocks; pack blocks are dealt to the items in reverse
-// order, item count - 1 first, and item i owns pack blocks [block0, block0 + its tile count).
+// Device table of a grouped pack (bitlinear_pack_group_build writes it, the five grouped pack
+// launches read it): a header, then one item per master in descriptor order.  Sampling block b
+// serves item b / kSampleBlocks, band block b item b, fix-up block b item b / kFixBlocks; pass
+// blocks are dealt to the items in reverse order, item count - 1 first, and item i owns pass
+// blocks [block0, block0 + its tile count).
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
