@@ -349,9 +349,10 @@ int bitlinear_fwd_group_fused(const void* table, int64_t work_items, int N, int 
  * once, outside graph capture); bitlinear_fwd_chain enqueues a clear of the workspace (a small
  * kernel) and the cooperative chain launch (64 workgroups, all resident).  The workspace
  * (caller-owned device memory, 16-byte aligned, contents on entry irrelevant) holds the grid
- * barrier's counter, an error word and per-workgroup partial absmax of every layer's input; calls
- * sharing it
- * must be ordered on one stream.  Every wait at the grid barrier is bounded by spin_limit polls
+ * barrier's counter, an error word, per-workgroup partial absmax of every layer's input and
+ * T x 8192 bytes for the int8 input rows of a layer whose fp32 input is larger than 256 KB (such
+ * a layer is quantized in slices by all workgroups, one extra grid barrier, then copied into each
+ * workgroup's LDS); calls sharing it must be ordered on one stream.  Every wait at the grid barrier is bounded by spin_limit polls
  * (<= 0: a default of about a second); a wait that gives up sets the uint32 error word at byte
  * offset 4 of the workspace to nonzero and its block returns, so the launch always ends -- then
  * the outputs are invalid.  Read that word after the launch completes.

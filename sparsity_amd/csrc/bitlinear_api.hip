@@ -734,7 +734,7 @@ int plan_chain(const bl_chain_layer* d, int64_t L, int64_t T, int N, int M, int 
     int64_t ke = 0;
     const int st = check_shape(q.n, q.K, N, M, layout, &ke);
     if (st != BL_OK) return st;
-    if (q.K > 8192) return BL_EINVAL;
+    if (q.K > bl::kChainMaxK) return BL_EINVAL;
     if (l > 0 && q.K != d[l - 1].n) return BL_EINVAL;
     if ((uint64_t)T * q.K * 4 >= (1ull << 31) || (uint64_t)T * q.n * 4 >= (1ull << 31)) return BL_EINVAL;
     if (!aligned16(q.codes) || !aligned16(q.meta) || !aligned4(q.gamma) || !aligned16(q.y))

@@ -15,7 +15,10 @@
 //                first -- they do not depend on the previous layer -- then the block waits at the
 //                grid barrier for layer l - 1, takes the per-token absmax as the max of every
 //                block's slot, forms the token scales (act_quant_i8's expressions), quantizes the
-//                input rows into LDS once (act_quant_i8's expression), and each team runs the
+//                input rows into LDS once (act_quant_i8's expression; for a large input, T x K x 4
+//                bytes above kChainSplitBytes, every block quantizes a slice into an int8 copy in
+//                the workspace and, after one more grid barrier, copies the int8 rows into LDS
+//                instead of reading all of the fp32 rows), and each team runs the
 //                sparse MFMAs, sums its waves' int32 partials in LDS in a fixed order, writes
 //                y = fl32(fl32(acc * gamma) * scale_t) and keeps the max |y| per token; the block
 //                stores its max in its slot for layer l + 1.  With the decode shapes every panel
@@ -23,7 +26,7 @@
 //
 // so every layer's y (and int32 accumulators) are bit-identical to act_quant_i8 on the previous
 // layer's y followed by bitlinear_fwd.  The grid barrier is a counter every block increments
-// once per phase (after a release fence at agent scope, so its outputs are visible on every XCD)
+// once per barrier (after a release fence at agent scope, so its outputs are visible on every XCD)
 // and thread 0 of every block polls (then an acquire fence).  The launch is cooperative
 // (all blocks resident), and every wait is bounded: after spin_limit polls the block raises the
 // workspace's error flag and returns, so a failure ends the kernel instead of hanging it.
@@ -102,6 +105,9 @@ __global__ __launch_bounds__(64 * kChainWaves) void chain_kernel(const uint8_t* 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   // per-block partial max |x| of every layer's input: pmax[(l * G + block) * T + t]
   uint32_t* pmax = ws + kChainWsHead;
+  // int8 input rows of a split layer
+  int8_t* xq = (int8_t*)ws + chain_xq_offset(L, T);
+  uint32_t gen = 0;                              // this block's arrivals so far (the same in every block)
 
   // ---- phase 0: partial per-token absmax of the first layer's input, column slices ----
   {
@@ -125,6 +131,7 @@ __global__ __launch_bounds__(64 * kChainWaves) void chain_kernel(const uint8_t* 
     }
   }
   chain_arrive(ws);
+  gen = 1;
 
   const int tok = lane & 31, h = lane >> 5;
   // layer records are read-only: each is read one layer ahead, before the wait that invalidates
@@ -153,12 +160,20 @@ __global__ __launch_bounds__(64 * kChainWaves) void chain_kernel(const uint8_t* 
     const int P0 = blk * tpb + team, Pstep = G * tpb;
 
     uint32_t c0[kChainMaxSteps], m0[kChainMaxSteps];
+    // Only the 4-step groups that hold this wave's steps (u < cnt) are read, and multiplied
+    // below: the loads a wave has in flight at the barrier stay few (the poll's result returns
+    // after them), and no matrix-core time goes to all-zero steps.
     auto load = [&](int P, uint32_t (&c)[kChainMaxSteps], uint32_t (&m)[kChainMaxSteps]) {
 #pragma unroll
-      for (int u = 0; u < kChainMaxSteps; ++u) {
-        const size_t off = ((size_t)P * NF + min(s_begin + u, NF - 1)) * 64;
-        c[u] = __builtin_nontemporal_load(cbase + off);
-        m[u] = __builtin_nontemporal_load(mbase + off);
+      for (int g = 0; g < kChainMaxSteps / 4; ++g) {
+        if (4 * g >= cnt) break;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int u = 4 * g + v;
+          const size_t off = ((size_t)P * NF + min(s_begin + u, NF - 1)) * 64;
+          c[u] = __builtin_nontemporal_load(cbase + off);
+          m[u] = __builtin_nontemporal_load(mbase + off);
+        }
       }
     };
     // the first panel's weights and gamma before the wait: they do not depend on the previous
@@ -166,22 +181,28 @@ __global__ __launch_bounds__(64 * kChainWaves) void chain_kernel(const uint8_t* 
     if (P0 < npanels) load(P0, c0, m0);
     const float gamma = *(__attribute__((address_space(1))) const float*)Ly.gamma;
 
-    // layer l - 1 (or phase 0) complete: (l + 1) arrivals of every block
-    if (!chain_wait(ws, (uint32_t)(l + 1) * (uint32_t)G, spin_limit, &go_sh)) return;
+    // layer l - 1 (or phase 0) complete: every block has made `gen` arrivals
+    if (!chain_wait(ws, gen * (uint32_t)G, spin_limit, &go_sh)) return;
     // The per-token absmax (max over every block's slot) and the input rows both come from the
     // previous layer: their loads go out together, then the scales are formed and the rows
-    // quantized into LDS (rows t < T, stride K + 16), once for all of the block's panels.
+    // quantized (act_quant_i8's expression) into LDS (rows t < T, stride K + 16), once for all
+    // of the block's panels.  A layer with a large input splits this (kChainSplitBytes): each
+    // block quantizes a 1/G slice of the rows into the workspace's int8 rows, and after one more
+    // grid barrier every block with panels copies the int8 rows into LDS.
     // 8 positions per piece: 8 fp32 (two 16-byte loads) or 8 bf16 (one).
     const bool has_work = blk * tpb < npanels;   // uniform: the block has at least one panel
+    const bool split = (int64_t)T * K * 4 > kChainSplitBytes;   // uniform: the same in every block
     const int ppr = K / 8;                       // pieces per row
-    const int pieces = has_work ? T * ppr : 0;
+    const int per_blk = (T * ppr + G - 1) / G;   // split: pieces per block's slice
+    const int pbase = split ? blk * per_blk : 0;
+    const int pieces = split ? max(0, min(per_blk, T * ppr - pbase)) : has_work ? T * ppr : 0;
     constexpr int U = 2;                         // pieces in flight per thread
     constexpr int NT = 64 * kChainWaves;
     v4i raw[U][2];
     auto issue = [&](int b0) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const int pc = min(b0 + u * NT, pieces - 1);
+        const int pc = pbase + min(b0 + u * NT, pieces - 1);
         const int t = pc / ppr, k = 8 * (pc % ppr);
         const size_t e = (size_t)t * K + k;
         if (l == 0 && X0_BF16) {
@@ -212,36 +233,56 @@ __global__ __launch_bounds__(64 * kChainWaves) void chain_kernel(const uint8_t* 
     }
     __syncthreads();
 
-    if (has_work) {
-      for (int b0 = tid; b0 < pieces; b0 += NT * U) {
-        if (b0 != tid) issue(b0);
+    for (int b0 = tid; b0 < pieces; b0 += NT * U) {
+      if (b0 != tid) issue(b0);
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-          const int pc = b0 + u * NT;
-          if (pc >= pieces) break;
-          const int t = pc / ppr, k = 8 * (pc % ppr);
-          const float sc = tok_s[t];
-          uint32_t out[2];
+      for (int u = 0; u < U; ++u) {
+        const int pc = b0 + u * NT;
+        if (pc >= pieces) break;
+        const int t = (pbase + pc) / ppr, k = 8 * ((pbase + pc) % ppr);
+        const float sc = tok_s[t];
+        uint32_t out[2];
 #pragma unroll
-          for (int d = 0; d < 2; ++d) {
-            float v[4];
-            if (l == 0 && X0_BF16) {
-              const uint32_t w0 = (uint32_t)raw[u][0][2 * d];
-              const uint32_t w1 = (uint32_t)raw[u][0][2 * d + 1];
-              v[0] = __uint_as_float(w0 << 16); v[1] = __uint_as_float(w0 & 0xFFFF0000u);
-              v[2] = __uint_as_float(w1 << 16); v[3] = __uint_as_float(w1 & 0xFFFF0000u);
-            } else {
+        for (int d = 0; d < 2; ++d) {
+          float v[4];
+          if (l == 0 && X0_BF16) {
+            const uint32_t w0 = (uint32_t)raw[u][0][2 * d];
+            const uint32_t w1 = (uint32_t)raw[u][0][2 * d + 1];
+            v[0] = __uint_as_float(w0 << 16); v[1] = __uint_as_float(w0 & 0xFFFF0000u);
+            v[2] = __uint_as_float(w1 << 16); v[3] = __uint_as_float(w1 & 0xFFFF0000u);
+          } else {
 #pragma unroll
-              for (int q = 0; q < 4; ++q) v[q] = __int_as_float(raw[u][d][q]);
-            }
-            out[d] = q8(v[0], sc) | (q8(v[1], sc) << 8) | (q8(v[2], sc) << 16) | (q8(v[3], sc) << 24);
+            for (int q = 0; q < 4; ++q) v[q] = __int_as_float(raw[u][d][q]);
           }
-          *(uint2*)&sm[t * stride + k] = make_uint2(out[0], out[1]);
+          out[d] = q8(v[0], sc) | (q8(v[1], sc) << 8) | (q8(v[2], sc) << 16) | (q8(v[3], sc) << 24);
         }
+        if (split) *(uint2*)(xq + (size_t)t * K + k) = make_uint2(out[0], out[1]);
+        else *(uint2*)&sm[t * stride + k] = make_uint2(out[0], out[1]);
       }
-      __syncthreads();
+    }
+    if (split) {
+      // every slice written: the int8 rows are complete once all blocks arrive
+      chain_arrive(ws);
+      ++gen;
+      if (!chain_wait(ws, gen * (uint32_t)G, spin_limit, &go_sh)) return;
+      if (has_work) {
+        // row t's K bytes in 1 KB pieces, one direct-to-LDS load per wave each (a short last
+        // piece with fewer lanes): no registers hold them, so all of them are in flight at once
+        const int cpr = (K + 1023) / 1024;
+        for (int c = __builtin_amdgcn_readfirstlane(wave); c < T * cpr; c += kChainWaves) {
+          const int t = c / cpr, k0 = (c % cpr) * 1024;
+          const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_offset(sm + t * stride + k0));
+          if (k0 + 16 * lane < K) lds_dma16(xq + (size_t)t * K + k0 + 16 * lane, m0);
+        }
+        __builtin_amdgcn_s_waitcnt(waitcnt_imm(0));
+      }
+    }
+    __syncthreads();
 
-      const int8_t* xr = sm + min(tok, T - 1) * stride + 16 * h;   // dead token lanes: row T - 1
+    if (has_work) {
+      // this lane's B fragment of the wave's first step (dead token lanes: row T - 1); the steps
+      // follow at immediate offsets of 64 bytes
+      const int8_t* xw = sm + min(tok, T - 1) * stride + 16 * h + s_begin * 64;
       // One round: every team multiplies its panel P (P >= npanels: no work, but the team still
       // meets the block at the barriers), the waves' int32 partials are summed in LDS in team
       // order, then y (and acc) and the block's running max |y| per token.
@@ -249,33 +290,59 @@ __global__ __launch_bounds__(64 * kChainWaves) void chain_kernel(const uint8_t* 
         const bool live = P < npanels;
         if (live) {
           v16i acc0 = {}, acc1 = {};
+          // B fragments in a ring of three, read two steps ahead of their MFMA.  Reads past the
+          // wave's last step (at most five steps: the group's rest and the look-ahead) stay inside
+          // the LDS allocation: past the last row they land in the reduction buffer, and they
+          // only ever meet a zero code or no MFMA at all.
+          // Lanes of tokens past T read nothing: their B columns only feed outputs that are
+          // never stored, and the LDS returns data for the live lanes alone.
+          const bool rd = tok < T;
+          int4 blo[3] = {}, bhi[3] = {};
+          if (rd) {
+            blo[0] = *(const int4*)xw;
+            bhi[0] = *(const int4*)(xw + 32);
+            blo[1] = *(const int4*)(xw + 64);
+            bhi[1] = *(const int4*)(xw + 96);
+          }
 #pragma unroll
-          for (int u = 0; u < kChainMaxSteps; ++u) {
-            const int s = min(s_begin + u, NF - 1);
-            const int4 blo = *(const int4*)(xr + s * 64);
-            const int4 bhi = *(const int4*)(xr + s * 64 + 32);
-            if (u & 1) acc1 = mfma_step<true>(u < cnt ? c[u] : 0u, m[u], blo, bhi, acc1);
-            else acc0 = mfma_step<true>(u < cnt ? c[u] : 0u, m[u], blo, bhi, acc0);
+          for (int g = 0; g < kChainMaxSteps / 4; ++g) {
+            if (4 * g >= cnt) break;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+              const int u = 4 * g + v;
+              if (u + 2 < kChainMaxSteps && rd) {
+                blo[(u + 2) % 3] = *(const int4*)(xw + (u + 2) * 64);
+                bhi[(u + 2) % 3] = *(const int4*)(xw + (u + 2) * 64 + 32);
+              }
+              const uint32_t code = u < cnt ? c[u] : 0u;
+              if (u & 1) acc1 = mfma_step<true>(code, m[u], blo[u % 3], bhi[u % 3], acc1);
+              else acc0 = mfma_step<true>(code, m[u], blo[u % 3], bhi[u % 3], acc0);
+            }
           }
           if (tok < T) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) red[(wave * 16 + r) * 64 + lane] = acc0[r] + acc1[r];
+            for (int r = 0; r < 16; ++r) red[(wave * 16 + r) * kChainRedStride + lane] = acc0[r] + acc1[r];
           }
         }
         __syncthreads();
-        // each team's 16 x 64 outputs, by the team's S waves
+        // The team's 32 x T outputs: item j is token j / 32, panel row j % 32, so a wave's store
+        // covers 32 consecutive outputs of a token row.  The accumulator of panel row oo and token
+        // t sits in element r = 4 (oo / 8) + oo % 4 of lane 32 ((oo / 4) % 2) + t.
         if (live) {
-          for (int i = wt * 64 + lane; i < 16 * 64; i += 64 * S) {
-            const int r = i >> 6, l2 = i & 63;
-            const int tk = l2 & 31;
-            const int o = P * kPanel + 8 * (r >> 2) + 4 * (l2 >> 5) + (r & 3);
-            if (tk < T && o < n) {
-              int32_t sum = 0;
-              for (int w = 0; w < S; ++w) sum += red[((team * S + w) * 16 + r) * 64 + l2];
-              const float v = ((float)sum * gamma) * tok_scale[tk];
-              Ly.y[(size_t)tk * n + o] = v;
-              if (Ly.acc) Ly.acc[(size_t)tk * n + o] = sum;
-              atomicMax(&tok_out[tk], __float_as_uint(v) & 0x7FFFFFFFu);
+          for (int j = wt * 64 + lane; j < 32 * T; j += 64 * S) {
+            const int t = j >> 5, oo = j & 31;
+            const int r = ((oo >> 3) << 2) | (oo & 3);
+            const int at = r * kChainRedStride + 32 * ((oo >> 2) & 1) + t;
+            int32_t sum = 0;
+#pragma unroll
+            for (int w = 0; w < kChainWaves; ++w)
+              if (w < S) sum += red[(team * S + w) * 16 * kChainRedStride + at];
+            const int o = P * kPanel + oo;
+            if (o < n) {
+              const float v = ((float)sum * gamma) * tok_scale[t];
+              Ly.y[(size_t)t * n + o] = v;
+              if (Ly.acc) Ly.acc[(size_t)t * n + o] = sum;
+              atomicMax(&tok_out[t], __float_as_uint(v) & 0x7FFFFFFFu);
             }
           }
         }
@@ -294,6 +361,7 @@ __global__ __launch_bounds__(64 * kChainWaves) void chain_kernel(const uint8_t* 
     if (tid < T) pmax[((size_t)(l + 1) * G + blk) * T + tid] = tok_out[tid];
     yin = Ly.y;
     chain_arrive(ws);
+    ++gen;
   }
 }
 

@@ -30,18 +30,34 @@ struct ChainLayer {
 };
 static_assert(sizeof(ChainLayer) == 56, "chain layer record is 56 bytes");
 
-// Workspace (uint32 words): [0] arrivals at the grid barrier (every block adds 1 per phase),
+// Workspace (uint32 words): [0] arrivals at the grid barrier (every block adds 1 per barrier),
 // [1] error flag (a bounded barrier wait gave up), [2..63] unused, then
 // pmax[(L + 1)][kChainBlocks][T]: each block's max |x| bit pattern per token of each layer's
 // input (layer l's input is layer l - 1's y); the layer's absmax is the max over the blocks.
+// Then, from the next 256-byte boundary, xq[T][K]: the int8 input rows of a layer quantized in
+// slices by all blocks (layers whose fp32 input exceeds kChainSplitBytes), sized for the
+// largest K a chain accepts.
 constexpr int kChainWsHead = 64;
+constexpr int kChainMaxK = 8192;
 
+__host__ __device__ inline size_t chain_xq_offset(int64_t L, int64_t T) {
+  return (((size_t)kChainWsHead + (size_t)(L + 1) * kChainBlocks * T) * 4 + 255) / 256 * 256;
+}
 inline size_t chain_ws_bytes(int64_t L, int64_t T) {
-  return ((size_t)kChainWsHead + (size_t)(L + 1) * kChainBlocks * T) * 4;
+  return chain_xq_offset(L, T) + (size_t)T * kChainMaxK;
 }
 
+// A layer whose fp32 input rows (T x K x 4 bytes) exceed this is quantized in two stages: every
+// block quantizes a 1/G slice of the rows into xq, a grid barrier, then every block copies the
+// int8 rows (a quarter of the bytes) into LDS.  Below it every block quantizes the whole input
+// itself, which saves the barrier.
+constexpr int64_t kChainSplitBytes = 256 * 1024;
+
 // Dynamic LDS of a layer: its int8 input rows (T x (K + 16)), then the waves' int32 partials.
-constexpr int64_t kChainRedBytes = (int64_t)kChainWaves * 16 * 64 * 4;
+// A wave's 16 x 64 int32 partials with a row stride of 65 words, so that the reads of 32
+// consecutive panel rows of one token fall on distinct banks.
+constexpr int kChainRedStride = 65;
+constexpr int64_t kChainRedBytes = (int64_t)kChainWaves * 16 * kChainRedStride * 4;
 
 hipError_t launch_chain(const void* table, int64_t L, int64_t T, int smem, const void* x0,
                         int x_is_bf16, void* ws, int64_t spin_limit, hipStream_t s);

@@ -641,9 +641,11 @@ def test_chain_plan_sizes_and_rejects(L):
     assert st == 0
     assert plan.L == 3 and plan.T == 16
     assert plan.table_bytes == (64 + 3 * 56 + 15) // 16 * 16
-    assert plan.ws_bytes == 4 * (64 + 4 * 64 * 16)   # per-workgroup absmax slots, 64 workgroups
+    # per-workgroup absmax slots (64 workgroups), then from a 256-byte boundary the int8 rows of
+    # the largest accepted K
+    assert plan.ws_bytes == (4 * (64 + 4 * 64 * 16) + 255) // 256 * 256 + 16 * 8192
     # the widest layer's int8 input rows, then the eight waves' int32 partials
-    assert plan.smem == 16 * (6912 + 16) + 8 * 16 * 64 * 4
+    assert plan.smem == 16 * (6912 + 16) + 8 * 16 * 65 * 4
     ok = [_cdesc(L, 0, 128, 256), _cdesc(L, 1, 64, 128)]
     assert _cplan(L, ok)[0] == 0
     assert _cplan(L, [_cdesc(L, 0, 128, 256), _cdesc(L, 1, 64, 192)])[0] == -22   # K != prev n

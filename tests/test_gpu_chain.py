@@ -87,6 +87,31 @@ def test_chain_matches_oracle_layer_by_layer(T, dtype):
     _check_against_calls(layers, ch, x0, T)
 
 
+@pytest.mark.parametrize("T,dims", [
+    (32, [(2304, 2112), (128, 2304), (2112, 128), (64, 2112)]),
+    (17, [(256, 3904), (3904, 256), (128, 3904)]),
+])
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_chain_split_input_layers(T, dims, dtype):
+    """Layers whose fp32 input exceeds 256 KB (T x K x 4) take the two-stage input: every block
+    quantizes a slice of the rows into the workspace's int8 rows, then every block copies them
+    into LDS (K not a multiple of 1 KB: a short last piece per row).  Split layers at the start
+    (bf16 or fp32 first input) and after an unsplit one."""
+    import torch
+    g = rng(80 + T)
+    layers = _layers(g, dims)
+    x = act_normal(g, T, dims[0][1])
+    if dtype == "bf16":
+        xh, bits = to_bf16(x)
+        x0 = torch.from_numpy(bits.view(np.int16)).cuda().view(torch.bfloat16)
+    else:
+        xh = x
+        x0 = dev(x)
+    ch = _run_chain(layers, T, x0)
+    _check_against_oracle(layers, ch, xh)
+    _check_against_calls(layers, ch, x0, T)
+
+
 def test_chain_degenerate_rows():
     """A zero input row (absmax 0: q = 0, scale 0, y = 0 all along the chain) and a heavy-tailed
     row next to ordinary ones."""
