@@ -70,7 +70,7 @@ def parse():
                     help="(internal) print the CPU oracle baseline as JSON and exit; no GPU use")
     ap.add_argument("--profile-pass",
                     choices=("decode", "prefill", "train", "bwd", "bwdgroup", "fwdgroup",
-                             "sparse6", "windows"),
+                             "sparse6", "windows", "chain"),
                     default=None,
                     help="for hardware-counter runs, no graph and no JSON line.  decode: two eager "
                          "decode steps, then a plain copy of COPY_BYTES (the counters' scale "
@@ -82,7 +82,8 @@ def parse():
                          "copies; sparse6: the decode workload's SPARSE6 and 2:4 groups twice "
                          "at every T, then the plain copies; windows: the 6:8 leg (window and "
                          "dense GEMMs, 2048 x 4096 -> 4096) with two timed launches each, then "
-                         "the plain copies")
+                         "the plain copies; chain: the 128 decode layers as one dependent chain, "
+                         "two launches at every T")
     return ap.parse_args()
 
 
@@ -1110,6 +1111,16 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         log(f"profile pass done: 2 decode steps, 2 copies of {COPY_BYTES} bytes")
+        return
+    if args.profile_pass == "chain":
+        layers = [dict(codes=c, meta=m, gamma=ga, n=n, K=K) for (n, K, c, m, ga) in D.mats]
+        for T in DECODE_T:
+            ch = S.Chain(layers, T)
+            for _ in range(2):
+                ch(D.x[(T, UP[1])][:T])
+            if ch.error():
+                raise RuntimeError("chain launch reported a barrier timeout")
+        log("profile pass done: 2 chain launches of the 128 decode layers at T = 1, 4, 16")
         return
     if args.profile_pass == "sparse6":
         _, groups6, _ = _sparse6_groups(S, torch, D)
