@@ -527,19 +527,58 @@ __device__ __forceinline__ void big_tile(
     k.template stage<1, false>(main_end + 1, R0, R1);
     k.template stage<2, false>(main_end + 2, R0, R1);
   }
-  __builtin_amdgcn_s_waitcnt(waitcnt_imm(0));   // no load may still be writing LDS when the block ends
+  // No load may still be writing LDS once the ring is reused below or the block ends; after the
+  // barrier no wave reads the ring any more.
+  __builtin_amdgcn_s_waitcnt(waitcnt_imm(0));
+  block_barrier_nofence();
 
   const float gamma = *gamma_p;
   const int lane = k.lane, h = k.h;
   // Lane (token lane % 32) holds rows 8j + 4h + i (i = 0..3) of each 32-row panel: four runs of
-  // four consecutive outputs.  Full panels with 16-byte aligned rows take one 16-byte store per
-  // run; ragged edges fall back to element stores.  The four stores of a token complete one
-  // 128-byte line, which L2 merges; nontemporal stores would send the 32-byte pieces to HBM one by
-  // one (measured 1.7x slower for the whole GEMM).
+  // four consecutive outputs.  Stored as they are, one instruction writes 32-byte pieces of 32
+  // token rows, so the tile's output costs four L2 requests per 128-byte line.  A 32-token group
+  // whose 64 rows and 32 tokens all lie inside y is therefore first written to a wave-private
+  // region of the (now idle) ring, [token][row] with rows padded to 68 floats so that both the
+  // 16-byte writes of 16 tokens and the reads of 16 consecutive row pieces hit distinct banks,
+  // then read back four tokens at a time: each store instruction then writes 256 contiguous bytes
+  // of four token rows.  Other groups (ragged rows or tokens, n not a multiple of 4) store from
+  // the registers: one 16-byte store per run where aligned, else element stores.  Nontemporal
+  // stores would send the pieces to HBM one by one (measured 1.7x slower for the whole GEMM).
   const bool vec_ok = (n & 3) == 0;
+  constexpr int kStgRow = 68;                                  // floats per staged token row
+  static_assert(G::NWAVE * 32 * kStgRow * 4 <= 3 * G::STAGE, "staging fits the ring");
+  static_assert(G::WM * 32 == 64, "staged rows: two panels per wave");
+  float* stg = (float*)(ring + k.wave * (32 * kStgRow * 4));
+  const int orow0 = row0 + k.wm * G::WM * 32;                  // first output row of the wave
 #pragma unroll
   for (int g = 0; g < G::WN; ++g) {
-    const int tk = tok0 + (k.wn * G::WN + g) * 32 + (lane & 31);
+    const int tg0 = tok0 + (k.wn * G::WN + g) * 32;
+    const int tk = tg0 + (lane & 31);
+    if (vec_ok && orow0 + 64 <= n && tg0 + 32 <= T) {
+      const float sc = xs[tk];
+#pragma unroll
+      for (int p = 0; p < G::WM; ++p)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          v4f v;
+          v[0] = ((float)k.acc[p][g][4 * jj + 0] * gamma) * sc;
+          v[1] = ((float)k.acc[p][g][4 * jj + 1] * gamma) * sc;
+          v[2] = ((float)k.acc[p][g][4 * jj + 2] * gamma) * sc;
+          v[3] = ((float)k.acc[p][g][4 * jj + 3] * gamma) * sc;
+          *(v4f*)&stg[(lane & 31) * kStgRow + p * 32 + 8 * jj + 4 * h] = v;
+        }
+      // a wave's LDS accesses complete in order; the clobber keeps the compiler from moving the
+      // reads above the writes (or the next group's writes above these reads)
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+      for (int it = 0; it < 8; ++it) {
+        const int tt = 4 * it + (lane >> 4), r4 = 4 * (lane & 15);
+        const v4f v = *(const v4f*)&stg[tt * kStgRow + r4];
+        *(v4f*)(y + (size_t)(tg0 + tt) * n + orow0 + r4) = v;
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      continue;
+    }
     if (tk >= T) continue;
     const float sc = xs[tk];
     float* yrow = y + (size_t)tk * n;
