@@ -20,6 +20,8 @@
 //                reduced through LDS in a fixed order.
 //   gemm_kernel  prefill: block tile BM rows x BN tokens; B staged in LDS (double buffered),
 //                A loaded per wave straight into registers one step ahead.
+#include <utility>
+
 #include "device_common.hpp"
 #include "gemm_group.hpp"
 #include "launch.hpp"
@@ -258,11 +260,10 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(
 // barely overlap, and these wave tiles measured 8-10% faster than 128 x 64 ones.
 //
 // Operands reach LDS with direct global->LDS loads (global_load_lds_dwordx4: lane l's 16 bytes
-// land at the wave-uniform LDS base + 16*l), so no VGPRs stage them, and a ring of three stage
-// buffers keeps two stages in flight while the third is multiplied.  A stage is KS MFMA K-steps:
-// B = 128 tokens x 128 bytes, A = 8 panels x KS fragments of codes (and of meta).  The three
-// buffers are distinct __shared__ variables and the stage loop is unrolled by three, so every
-// access names its buffer statically.  The loads are inline asm the compiler does not track, so
+// land at the wave-uniform LDS base + 16*l), so no VGPRs stage them, and a ring of NBUF stage
+// buffers keeps NBUF - 1 stages in flight while one is multiplied.  A stage is KS MFMA K-steps: B = 128 tokens x 128
+// bytes, A = 8 panels x KS fragments of codes (and of meta).  The stage loop is unrolled by NBUF,
+// so every access names its buffer statically.  The loads are inline asm the compiler does not track, so
 // each wave waits on its own vmcnt (every stage issues exactly LPS loads per wave) and meets the
 // others at a bare s_barrier (no fence: a fence would also drain the loads meant to stay in
 // flight).  B rows are
@@ -277,9 +278,13 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(
 // Blocks are mapped XCD-major (big_tile_of_block): each XCD owns a slab of token tiles and walks
 // them fastest, so its activations stay in its L2 and every weight panel is fetched once per XCD.
 constexpr int kBigWaves = 4;
+// Three stage buffers (72 KB of LDS) allow two blocks per CU.  A six-deep ring for grids of one
+// tile per CU (one block, 144 KB) measured 7% slower on the 2048-token window GEMM: its unrolled
+// loop needs more registers than the file holds beside the accumulators.
+constexpr int kBigRing = 3;
 constexpr int kBigWaveRows = 4, kBigWaveM = 2, kBigWaveN = 4;
 
-template <int LAYOUT, int NWAVE_, int WR_, int WM_, int WN_>
+template <int LAYOUT, int NWAVE_, int WR_, int WM_, int WN_, int NBUF_ = 3>
 struct BigGemm {
   static constexpr bool SP = LAYOUT == kLayoutSparse;
   static constexpr int KSTEP = SP ? 64 : 32;
@@ -296,10 +301,12 @@ struct BigGemm {
   static constexpr int A_LOADS = A_BYTES / 1024 / NWAVE;
   static constexpr int LPS = B_LOADS + (SP ? 2 : 1) * A_LOADS;   // loads per wave per stage
   static constexpr int STAGE = B_BYTES + A_BYTES;
+  static constexpr int NBUF = NBUF_;                 // stage buffers in the LDS ring
+  static_assert(NBUF >= 3 && (NBUF - 2) * LPS <= 63, "loads in flight fit the vmcnt field");
   static_assert(SK == 128, "stage layout");
   static_assert(A_LOADS >= 1 && A_BYTES % (1024 * NWAVE) == 0, "A stage splits evenly over waves");
 
-  int8_t* ring;                                      // 3 stage buffers in LDS
+  int8_t* ring;                                      // NBUF stage buffers in LDS
   const int8_t* __restrict__ xq;
   const uint32_t* __restrict__ codes;
   const uint32_t* __restrict__ meta;
@@ -404,7 +411,7 @@ struct BigGemm {
     for (int p = 0; p < WM; ++p) {
       __builtin_amdgcn_sched_barrier(0);
       if (p * WN < LPS) issue_one<BUF>(st_refill, p * WN);
-      if (p == 0) read_step(ring + ((BUF + 1) % 3) * STAGE, 0, nxt);
+      if (p == 0) read_step(ring + ((BUF + 1) % NBUF) * STAGE, 0, nxt);
       const v4i ap = expand_codes(live ? r.code[p] : 0u);
 #pragma unroll
       for (int g = 0; g < WN; ++g) {
@@ -428,13 +435,16 @@ struct BigGemm {
 
   // One stage (buffer BUF) as KS pipelined steps: while step j's MFMAs run, step j+1's operands
   // are read from LDS into the other register set.  At the last step the next stage's buffer is
-  // needed, so the wave first waits for its own loads of that stage (at most the LPS loads of the
-  // stage after it stay outstanding) and for its outstanding LDS reads, meets the other waves at a
+  // needed, so the wave first waits for its own loads of that stage (the loads of the NBUF - 2
+  // stages after it stay outstanding) and for its outstanding LDS reads, meets the other waves at a
   // bare s_barrier (after which no wave reads this stage's buffer again), then refills this buffer
-  // with stage st+3 and reads the next stage's first step while the step's MFMAs run.
-  // ALL_LIVE: every step of the stage is real.
+  // with stage st + NBUF and reads the next stage's first step while the step's MFMAs run.
+  // ALL_LIVE: every step of the stage is real.  Stages past the last real one (the padding of the
+  // last group of NBUF) do nothing: every wave skips them alike, and the loads still in flight
+  // into their buffers are drained before the epilogue.
   template <int BUF, bool ALL_LIVE>
   __device__ __forceinline__ void stage(int st, StepRegs& R0, StepRegs& R1) {
+    if (!ALL_LIVE && st >= NS) return;
 #pragma unroll
     for (int j = 0; j < KS; ++j) {
       StepRegs& cur = (j % 2 == 0) ? R0 : R1;
@@ -443,22 +453,33 @@ struct BigGemm {
         read_step(ring + BUF * STAGE, j + 1, nxt);
         mma_step(cur, ALL_LIVE || st * KS + j < NF);
       } else {
-        __builtin_amdgcn_s_waitcnt(waitcnt_imm(LPS, 0));
+        __builtin_amdgcn_s_waitcnt(waitcnt_imm((NBUF - 2) * LPS, 0));
         block_barrier_nofence();
-        mma_step_refill<BUF>(cur, ALL_LIVE || st * KS + j < NF, st + 3, nxt);
+        mma_step_refill<BUF>(cur, ALL_LIVE || st * KS + j < NF, st + NBUF, nxt);
       }
     }
   }
 };
 
 // One 256-row x 128-token output tile at (row0, tok0): the pipelined main loop, then the epilogue.
-template <int LAYOUT, int NWAVE>
+template <class G, int... I>
+__device__ __forceinline__ void big_issue_ring(G& k, std::integer_sequence<int, I...>) {
+  (k.template issue<I>(I), ...);
+}
+template <bool ALL_LIVE, class G, int... I>
+__device__ __forceinline__ void big_stage_group(G& k, int st, typename G::StepRegs& R0,
+                                                typename G::StepRegs& R1,
+                                                std::integer_sequence<int, I...>) {
+  (k.template stage<I, ALL_LIVE>(st + I, R0, R1), ...);
+}
+
+template <int LAYOUT, int NWAVE, int NBUF>
 __device__ __forceinline__ void big_tile(
     int8_t* ring, const int8_t* __restrict__ xq, const float* __restrict__ xs, int T, int Keff,
     const uint32_t* __restrict__ codes, const uint32_t* __restrict__ meta,
     const float* __restrict__ gamma_p, int n, int npanels, float* __restrict__ y,
     int32_t* __restrict__ acc_out, int row0, int tok0) {
-  using G = BigGemm<LAYOUT, NWAVE, kBigWaveRows, kBigWaveM, kBigWaveN>;
+  using G = BigGemm<LAYOUT, NWAVE, kBigWaveRows, kBigWaveM, kBigWaveN, NBUF>;
   G k;
   k.ring = ring;
   k.xq = xq; k.codes = codes; k.meta = meta; k.Keff = Keff;
@@ -504,29 +525,22 @@ __device__ __forceinline__ void big_tile(
 #pragma unroll
     for (int g = 0; g < G::WN; ++g) k.acc[p][g] = v16i{};
 
-  // Groups of three stages (one per ring buffer).  Groups made only of full stages skip the
+  // Groups of NBUF stages (one per ring buffer).  Groups made only of full stages skip the
   // per-step liveness select; the last group, which may hold the partial stage and padding up to
-  // a multiple of 3, keeps it (padded steps have their codes zeroed).  Every stage issues its
-  // refill (clamped to real data), so each wave always has exactly LPS loads per stage in flight.
+  // a multiple of NBUF, keeps it (a partial stage's padded steps have their codes zeroed; whole
+  // padded stages are skipped).  Every real stage issues its refill (clamped to real data), so
+  // each wave always has exactly LPS loads per stage in flight.
   const int full_stages = k.NF / G::KS;
-  const int main_end = full_stages / 3 * 3;
+  const int main_end = full_stages / NBUF * NBUF;
   typename G::StepRegs R0, R1;
-  k.template issue<0>(0);
-  k.template issue<1>(1);
-  k.template issue<2>(2);
-  __builtin_amdgcn_s_waitcnt(waitcnt_imm(2 * G::LPS));   // stage 0 landed (this wave's part)
+  big_issue_ring(k, std::make_integer_sequence<int, NBUF>{});
+  __builtin_amdgcn_s_waitcnt(waitcnt_imm((NBUF - 1) * G::LPS));   // stage 0 landed (this wave's part)
   block_barrier_nofence();
   k.read_step(ring, 0, R0);
-  for (int st = 0; st < main_end; st += 3) {
-    k.template stage<0, true>(st, R0, R1);
-    k.template stage<1, true>(st + 1, R0, R1);
-    k.template stage<2, true>(st + 2, R0, R1);
-  }
-  if (main_end < k.NS) {
-    k.template stage<0, false>(main_end, R0, R1);
-    k.template stage<1, false>(main_end + 1, R0, R1);
-    k.template stage<2, false>(main_end + 2, R0, R1);
-  }
+  for (int st = 0; st < main_end; st += NBUF)
+    big_stage_group<true>(k, st, R0, R1, std::make_integer_sequence<int, NBUF>{});
+  if (main_end < k.NS)
+    big_stage_group<false>(k, main_end, R0, R1, std::make_integer_sequence<int, NBUF>{});
   // No load may still be writing LDS once the ring is reused below or the block ends; after the
   // barrier no wave reads the ring any more.
   __builtin_amdgcn_s_waitcnt(waitcnt_imm(0));
@@ -546,7 +560,7 @@ __device__ __forceinline__ void big_tile(
   // stores would send the pieces to HBM one by one (measured 1.7x slower for the whole GEMM).
   const bool vec_ok = (n & 3) == 0;
   constexpr int kStgRow = 68;                                  // floats per staged token row
-  static_assert(G::NWAVE * 32 * kStgRow * 4 <= 3 * G::STAGE, "staging fits the ring");
+  static_assert(G::NWAVE * 32 * kStgRow * 4 <= NBUF * G::STAGE, "staging fits the ring");
   static_assert(G::WM * 32 == 64, "staged rows: two panels per wave");
   float* stg = (float*)(ring + k.wave * (32 * kStgRow * 4));
   const int orow0 = row0 + k.wm * G::WM * 32;                  // first output row of the wave
@@ -641,17 +655,17 @@ __device__ __forceinline__ void big_tile_of_block(int b, int tiles_m, int tiles_
   *tn = t / tiles_m;
 }
 
-template <int LAYOUT, int NWAVE>
+template <int LAYOUT, int NWAVE, int NBUF>
 __global__ __launch_bounds__(64 * NWAVE, 2) void gemm_big_kernel(
     const int8_t* __restrict__ xq, const float* __restrict__ xs, int T, int Keff,
     const uint32_t* __restrict__ codes, const uint32_t* __restrict__ meta,
     const float* __restrict__ gamma_p, int n, int npanels, float* __restrict__ y,
     int32_t* __restrict__ acc_out, int tiles_m, int tiles) {
-  using G = BigGemm<LAYOUT, NWAVE, kBigWaveRows, kBigWaveM, kBigWaveN>;
-  __shared__ __attribute__((aligned(16))) int8_t ring[3 * G::STAGE];
+  using G = BigGemm<LAYOUT, NWAVE, kBigWaveRows, kBigWaveM, kBigWaveN, NBUF>;
+  __shared__ __attribute__((aligned(16))) int8_t ring[NBUF * G::STAGE];
   int tm, tn;
   big_tile_of_block(blockIdx.x, tiles_m, tiles / tiles_m, &tm, &tn);
-  big_tile<LAYOUT, NWAVE>(ring, xq, xs, T, Keff, codes, meta, gamma_p, n, npanels, y, acc_out,
+  big_tile<LAYOUT, NWAVE, NBUF>(ring, xq, xs, T, Keff, codes, meta, gamma_p, n, npanels, y, acc_out,
                           tm * G::BM, tn * G::BN);
 }
 
@@ -665,14 +679,14 @@ __global__ __launch_bounds__(64 * NWAVE, 2) void gemm_big_kernel(
 template <int LAYOUT>
 __global__ __launch_bounds__(64 * kBigWaves, 2) void gemm_big_group_kernel(
     const uint8_t* __restrict__ table) {
-  using G = BigGemm<LAYOUT, kBigWaves, kBigWaveRows, kBigWaveM, kBigWaveN>;
-  __shared__ __attribute__((aligned(16))) int8_t ring[3 * G::STAGE];
+  using G = BigGemm<LAYOUT, kBigWaves, kBigWaveRows, kBigWaveM, kBigWaveN, kBigRing>;
+  __shared__ __attribute__((aligned(16))) int8_t ring[kBigRing * G::STAGE];
   const GemmGroupHeader* hd = (const GemmGroupHeader*)table;
   if (hd->magic != kGemmGroupMagic || hd->layout != LAYOUT || (int)blockIdx.x >= hd->jobs) return;
   const GemmGroupJob jb = ((const GemmGroupJob*)(table + hd->jobs_off))[blockIdx.x];
   if (jb.proj < 0) return;
   const GemmGroupProj P = ((const GemmGroupProj*)(table + sizeof(GemmGroupHeader)))[jb.proj];
-  big_tile<LAYOUT, kBigWaves>(ring, P.xq, P.xs, P.T, P.Keff, P.codes, P.meta, P.gamma, P.n,
+  big_tile<LAYOUT, kBigWaves, kBigRing>(ring, P.xq, P.xs, P.T, P.Keff, P.codes, P.meta, P.gamma, P.n,
                               P.npanels, P.y, P.acc, jb.tm * G::BM, jb.tn * G::BN);
 }
 
@@ -713,8 +727,8 @@ static hipError_t launch_fwd_layout(const int8_t* xq, const float* xs, int64_t T
     using G = BigGemm<LAYOUT, kBigWaves, kBigWaveRows, kBigWaveM, kBigWaveN>;
     const int tiles_m = (int)((n + G::BM - 1) / G::BM);
     const int tiles = tiles_m * (int)((T + G::BN - 1) / G::BN);
-    gemm_big_kernel<LAYOUT, kBigWaves><<<tiles, 64 * kBigWaves, 0, s>>>(xq, xs, (int)T, (int)Keff, codes, meta, gamma,
-                                                     (int)n, npanels, y, acc, tiles_m, tiles);
+    gemm_big_kernel<LAYOUT, kBigWaves, kBigRing><<<tiles, 64 * kBigWaves, 0, s>>>(
+        xq, xs, (int)T, (int)Keff, codes, meta, gamma, (int)n, npanels, y, acc, tiles_m, tiles);
   } else {
     constexpr int WM = 2, WN = 2, WAM = 2, WAN = 2;
     constexpr int BM = 32 * WM * WAM, BN = 32 * WN * WAN;
