@@ -556,8 +556,10 @@ __device__ __forceinline__ void big_tile(
   // 16-byte writes of 16 tokens and the reads of 16 consecutive row pieces hit distinct banks,
   // then read back four tokens at a time: each store instruction then writes 256 contiguous bytes
   // of four token rows.  Other groups (ragged rows or tokens, n not a multiple of 4) store from
-  // the registers: one 16-byte store per run where aligned, else element stores.  Nontemporal
-  // stores would send the pieces to HBM one by one (measured 1.7x slower for the whole GEMM).
+  // the registers: one 16-byte store per run where aligned, else element stores.  The staged
+  // stores are non-temporal: whole lines that would otherwise evict operand lines from L2 (2-5%
+  // faster); the 32-byte pieces of the register path must merge in L2 first (non-temporal, they
+  // reached HBM one by one: 1.7x slower for the whole GEMM).
   const bool vec_ok = (n & 3) == 0;
   constexpr int kStgRow = 68;                                  // floats per staged token row
   static_assert(G::NWAVE * 32 * kStgRow * 4 <= NBUF * G::STAGE, "staging fits the ring");
@@ -588,7 +590,7 @@ __device__ __forceinline__ void big_tile(
       for (int it = 0; it < 8; ++it) {
         const int tt = 4 * it + (lane >> 4), r4 = 4 * (lane & 15);
         const v4f v = *(const v4f*)&stg[tt * kStgRow + r4];
-        *(v4f*)(y + (size_t)(tg0 + tt) * n + orow0 + r4) = v;
+        __builtin_nontemporal_store(v, (v4f*)(y + (size_t)(tg0 + tt) * n + orow0 + r4));
       }
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
       continue;
