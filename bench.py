@@ -1097,7 +1097,12 @@ def main():
     if args.profile_pass == "prefill":
         prefill_leg(S, torch, iters=2)
         torch.cuda.synchronize()
-        log("profile pass done: prefill GEMM x 5")
+        src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(2):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("profile pass done: prefill GEMM x 5, 2 copies")
         return
     log(f"device {torch.cuda.get_device_name(0)}; packing {2 * N_PAIRS} matrices")
     D = Decode(S, torch)

@@ -615,11 +615,17 @@ size_t gemm_jobs_offset(size_t count) {
 }
 
 // Grouped prefill plan: validates the projections (bitlinear_fwd's rules, T > 128 each), checks
-// that no output overlaps another output or an input, and lays out the jobs.  Each projection's
-// tiles are cut into runs of up to kGemmRun consecutive tile numbers in gemm_big_kernel's own
-// order (row tiles fastest, so neighbouring blocks of a run read the same token tile and the
-// run's weight rows stay in the XCD's L2); runs are dealt longest first to the least-loaded XCD,
-// and block b takes entry b / 8 of XCD b % 8's list.
+// that no output overlaps another output or an input, and lays out the jobs; block b takes entry
+// b / 8 of XCD b % 8's list.
+//   - When every projection's token tiles split evenly over the XCDs, XCD x takes slab x of the
+//     token tiles of every projection, walked as bitlinear_fwd walks it (row tile by row tile,
+//     the slab's token tiles fastest), projection after projection with those that read the
+//     same activations next to each other: the slab's activation rows stay in that XCD's L2
+//     across the projections that share them, and every XCD gets the same work.  On the 3B-alike
+//     layer set at 8192 tokens this halves the bytes fetched past L2 of the run order below.
+//   - Otherwise each projection's tiles are cut into runs of up to kGemmRun consecutive tile
+//     numbers (row tiles fastest, so neighbouring blocks of a run read the same token tile), and
+//     runs are dealt longest first to the least-loaded XCD.
 constexpr int64_t kGemmRun = 64;   // two block slots on each of an XCD's 32 CUs
 
 int plan_gemm_group(const bl_fwd_desc* d, int64_t count, int N, int M, int layout,
@@ -660,26 +666,53 @@ int plan_gemm_group(const bl_fwd_desc* d, int64_t count, int N, int M, int layou
     if (r.out) out_hi = std::max(out_hi, r.hi);
   }
   const int64_t BM = bl::gemm_group_tile_rows(), BN = bl::gemm_group_tile_tokens();
-  struct Run { int32_t proj; int64_t t0, t1, tiles_m, work; };
-  std::vector<Run> runs;
-  for (int64_t i = 0; i < count; ++i) {
-    const bl::GemmGroupProj& r = (*projs)[(size_t)i];
-    const int64_t tm = (r.n + BM - 1) / BM, tiles = tm * ((r.T + BN - 1) / BN);
-    for (int64_t t0 = 0; t0 < tiles; t0 += kGemmRun) {
-      const int64_t t1 = std::min(tiles, t0 + kGemmRun);
-      runs.push_back({(int32_t)i, t0, t1, tm, (t1 - t0) * (int64_t)r.Keff});
-    }
-    if ((int64_t)runs.size() > (int64_t)1 << 24) return BL_EINVAL;
-  }
-  std::stable_sort(runs.begin(), runs.end(),
-                   [](const Run& a, const Run& b) { return a.work > b.work; });
   std::vector<std::vector<bl::GemmGroupJob>> per(bl::kXcds);
-  int64_t load[bl::kXcds] = {};
-  for (const Run& rn : runs) {
-    const int x = (int)(std::min_element(load, load + bl::kXcds) - load);
-    load[x] += rn.work;
-    for (int64_t t = rn.t0; t < rn.t1; ++t)
-      per[x].push_back({rn.proj, (int32_t)(t % rn.tiles_m), (int32_t)(t / rn.tiles_m), 0});
+  bool slabs = true;
+  int64_t total = 0;
+  for (const bl::GemmGroupProj& r : *projs) {
+    const int64_t tn = (r.T + BN - 1) / BN;
+    slabs = slabs && tn % bl::kXcds == 0;
+    total += tn * ((r.n + BM - 1) / BM);
+  }
+  if (slabs && total <= (int64_t)1 << 30) {   // the run order below allows as many tiles
+    std::vector<int64_t> order;   // projections grouped by activation rows, first-seen order
+    std::vector<bool> taken((size_t)count, false);
+    for (int64_t i = 0; i < count; ++i) {
+      if (taken[(size_t)i]) continue;
+      for (int64_t j = i; j < count; ++j)
+        if (!taken[(size_t)j] && (*projs)[(size_t)j].xq == (*projs)[(size_t)i].xq) {
+          taken[(size_t)j] = true;
+          order.push_back(j);
+        }
+    }
+    for (int x = 0; x < bl::kXcds; ++x)
+      for (int64_t i : order) {
+        const bl::GemmGroupProj& r = (*projs)[(size_t)i];
+        const int64_t tm = (r.n + BM - 1) / BM, ntn = (r.T + BN - 1) / BN / bl::kXcds;
+        for (int64_t k = 0; k < tm * ntn; ++k)
+          per[x].push_back({(int32_t)i, (int32_t)(k / ntn), (int32_t)(x * ntn + k % ntn), 0});
+      }
+  } else {
+    struct Run { int32_t proj; int64_t t0, t1, tiles_m, work; };
+    std::vector<Run> runs;
+    for (int64_t i = 0; i < count; ++i) {
+      const bl::GemmGroupProj& r = (*projs)[(size_t)i];
+      const int64_t tm = (r.n + BM - 1) / BM, tiles = tm * ((r.T + BN - 1) / BN);
+      for (int64_t t0 = 0; t0 < tiles; t0 += kGemmRun) {
+        const int64_t t1 = std::min(tiles, t0 + kGemmRun);
+        runs.push_back({(int32_t)i, t0, t1, tm, (t1 - t0) * (int64_t)r.Keff});
+      }
+      if ((int64_t)runs.size() > (int64_t)1 << 24) return BL_EINVAL;
+    }
+    std::stable_sort(runs.begin(), runs.end(),
+                     [](const Run& a, const Run& b) { return a.work > b.work; });
+    int64_t load[bl::kXcds] = {};
+    for (const Run& rn : runs) {
+      const int x = (int)(std::min_element(load, load + bl::kXcds) - load);
+      load[x] += rn.work;
+      for (int64_t t = rn.t0; t < rn.t1; ++t)
+        per[x].push_back({rn.proj, (int32_t)(t % rn.tiles_m), (int32_t)(t / rn.tiles_m), 0});
+    }
   }
   size_t depth = 0;
   for (const auto& v : per) depth = std::max(depth, v.size());

@@ -44,7 +44,7 @@ def _make(n, K, T, N, M, layout, seed, with_acc=True):
     y = torch.full((T, n), float("nan"), dtype=torch.float32, device="cuda")
     acc = torch.full((T, n), -7, dtype=torch.int32, device="cuda") if with_acc else None
     return dict(xq=xq, scale=sc, K=K, codes=codes, meta=meta, gamma=gamma, n=n, y=y, acc=acc,
-                acc_ref=acc_ref, y_ref=O.rescale(acc_ref, ref["gamma"], s), T=T)
+                acc_ref=acc_ref, y_ref=O.rescale(acc_ref, ref["gamma"], s), T=T, q=q, s=s)
 
 
 def _single(p, N, M, layout):
@@ -78,6 +78,36 @@ def test_gemm_group_mixed_shapes(N, M, layout):
         assert np.array_equal(f32_bits(y1), f32_bits(host(p["y"]))), f"{what}: y != bitlinear_fwd"
         if p["acc"] is not None:
             assert np.array_equal(acc1, host(p["acc"])), f"{what}: acc != bitlinear_fwd"
+
+
+@pytest.mark.parametrize("N,M,layout", CASES_NM)
+def test_gemm_group_xcd_slabs(N, M, layout):
+    """Token tiles that split evenly over the 8 XCDs (T a multiple of 8 x 128) take the slab plan:
+    each XCD walks its slab of every projection, projections reading the same activations next
+    to each other (here the first and the third share one xq and are launched apart).  Every
+    output against the oracle and against bitlinear_fwd, bit for bit."""
+    import torch
+    kq = _kq(N, M, layout)
+    a = _make(300, 2 * kq, 1024, N, M, layout, seed=900 + M + 7 * layout)          # ragged rows
+    b = _make(45, kq, 2048, N, M, layout, seed=901 + M + 7 * layout, with_acc=False)
+    W = master_weights(rng(902 + M + 7 * layout), 257, 2 * kq)                      # a 1-row tile
+    ref = O.pack(W, N, M, layout)
+    codes, meta, gamma = S.pack(dev(W), N, M, layout)
+    acc_ref = O.acc_dense(ref["W_eff"], a["q"])
+    c = dict(xq=a["xq"], scale=a["scale"], K=a["K"], codes=codes, meta=meta, gamma=gamma, n=257,
+             y=torch.full((1024, 257), float("nan"), dtype=torch.float32, device="cuda"),
+             acc=torch.full((1024, 257), -7, dtype=torch.int32, device="cuda"), acc_ref=acc_ref,
+             y_ref=O.rescale(acc_ref, ref["gamma"], a["s"]), T=1024)
+    projs = [a, b, c]
+    S.GemmGroup(projs, N, M, layout)()
+    for i, p in enumerate(projs):
+        what = f"projection {i}"
+        if p["acc"] is not None:
+            nbad = int((host(p["acc"]) != p["acc_ref"]).sum())
+            assert nbad == 0, f"{what}: {nbad} accumulators differ from the oracle"
+        assert_y_close(host(p["y"]), p["y_ref"], what=what)
+        y1, acc1 = _single(p, N, M, layout)
+        assert np.array_equal(f32_bits(y1), f32_bits(host(p["y"]))), f"{what}: y != bitlinear_fwd"
 
 
 def test_gemm_group_shared_activations_new_contents_and_graph():
