@@ -388,8 +388,10 @@ int bitlinear_fwd_chain(const void* table, const bl_chain_plan* plan, const void
  * Same operation and descriptors as the grouped decode forward (bl_fwd_desc; BitNet b1.58 page,
  * "The mechanism"), but for 128 < T per projection: y (and acc_opt) are those of bitlinear_fwd
  * for each descriptor, bit for bit.  Every 256-row x 128-token output tile of every projection
- * is one workgroup of the launch, dealt to the XCDs longest first, so the separate launches'
- * partial last waves become one.  All projections share (N, M, layout); each follows
+ * is one workgroup of the launch, so the separate launches' partial last waves become one; when
+ * every projection's token tiles divide by 8 each XCD takes the same eighth of the token tiles
+ * of every projection (projections sharing xq back to back), otherwise runs of tiles are dealt
+ * to the XCDs longest first.  All projections share (N, M, layout); each follows
  * bitlinear_fwd's shape and alignment rules with T > 128 (BL_EINVAL otherwise).  Inputs (xq,
  * x_scale, codes, meta, gamma) may be shared or overlap; outputs (y, acc_opt) may overlap
  * nothing (BL_EINVAL).  1 <= count <= 4096.
