@@ -497,6 +497,23 @@ def _gplan(L, descs, N=2, M=4, layout=0):
     return L.bitlinear_gemm_group_plan((L.BlFwdDesc * len(descs))(*descs), N, M, layout)
 
 
+def test_gemm_group_plan_xcd_slabs(L):
+    """Token tiles that divide by 8 in every projection: each XCD takes the same eighth of every
+    projection's tiles, so the launch holds exactly the tiles (no padding jobs); one projection
+    whose token tiles do not divide by 8 sends the group back to the run plan."""
+    a = _gdesc(L, 0, T=1024, n=300, K=640)     # 2 row tiles x 8 token tiles
+    b = _gdesc(L, 1, T=2048, n=1000, K=256)    # 4 x 16
+    c = _gdesc(L, 2, T=1024, n=45, K=640, xq=a.xq, x_scale=a.x_scale)   # 1 x 8, shares a's rows
+    st, plan = _gplan(L, [a, b, c])
+    assert st == 0
+    assert plan.jobs == 16 + 64 + 8
+    assert plan.table_bytes == (64 + 3 * 72 + 15) // 16 * 16 + 16 * plan.jobs
+    # T = 129 (2 token tiles) does not divide: the run plan pads every XCD to the depth of the
+    # deepest one (a's 16 tiles in one run)
+    st, plan2 = _gplan(L, [a, _gdesc(L, 1, T=129, n=64)])
+    assert st == 0 and plan2.jobs == 8 * 16
+
+
 def test_gemm_group_plan_and_rejects_before_launch(L):
     """256 x 128 output tiles per projection, runs of up to 64 tiles dealt to the least-loaded XCD
     (heaviest tiles first), launch position p * 8 + x; bitlinear_fwd's rules with T > 128; no
